@@ -1,0 +1,389 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each pin compares the oracle with a closed form, a library routine (scipy,
+torch's attention), a brute-force search, or an invariant of the mathematics.
+The planted-mistake tests at the end patch a plausible bug into the oracle and
+show that a pin fails.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special as sps
+import scipy.stats as sst
+import torch
+
+import oracle.zha_oracle as O
+from tree_indexed_sparse_zha_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_cache(N, d, R, seed, seg=8):
+    K, V, ref, Q = W.random_cache(N, d, R, "f32", seed=seed, n_queries=6, segment_len=seg)
+    f = lambda t: t.double().numpy()
+    return f(K), f(V), f(ref), f(Q)
+
+
+# ----------------------------------------------------------------------------
+# pin checks, written as functions so the planted-mistake tests can reuse them
+
+
+def pin_dense_at_p1(o=O, N=203, d=16, R=3, C=4, levels=3, seed=1):
+    """P1: p = 1 keeps every key; the output is torch's dense attention."""
+    K, V, ref, Q = _rand_cache(N, d, R, seed)
+    tree = o.build_tree(K, ref, C, levels, "f64", n_tokens=N)
+    for q in Q:
+        out, lse, idx, recs = o.route_and_attend(q, K, V, tree, ref, C, 1.0, N)
+        assert np.array_equal(idx, np.arange(N))
+        ref_o = torch.nn.functional.scaled_dot_product_attention(
+            torch.tensor(q)[None, None, None], torch.tensor(K)[None, None], torch.tensor(V)[None, None]
+        )[0, 0, 0].numpy()
+        np.testing.assert_allclose(out, ref_o, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, sps.logsumexp(K @ q / math.sqrt(d)), rtol=0, atol=1e-12)
+
+
+def pin_chunk1_exact_logit(o=O, N=37, d=8, R=5, seed=2):
+    """P2: C = 1, one level: the plane score is the exact logit q.k/sqrt(d)."""
+    K, V, ref, Q = _rand_cache(N, d, R, seed)
+    tree = o.build_tree(K, ref, 1, 1, "f64")
+    for q in Q:
+        s = o.plane_scores(q, tree[0], ref)
+        np.testing.assert_allclose(s, K @ q / math.sqrt(d), rtol=0, atol=1e-12)
+
+
+def pin_merge_equals_direct(o=O, N=150, d=8, R=3, C=3, levels=4, seed=3):
+    """P3: every node equals logsumexp / softmax mean over all its keys."""
+    K, V, ref, Q = _rand_cache(N, d, R, seed)
+    tree = o.build_tree(K, ref, C, levels, "f64", n_tokens=N)
+    sizes = o.level_sizes(N, C, levels)
+    for lv in range(1, levels + 1):
+        assert tree[lv - 1].L.shape[0] == sizes[lv - 1]
+        for n in range(sizes[lv - 1]):
+            a, b = o.node_token_range(lv, n, C, N)
+            z = (K[a:b] @ ref.T) / math.sqrt(d)  # [keys, R]
+            L = sps.logsumexp(z, axis=0)
+            w = sps.softmax(z, axis=0)
+            g = w.T @ K[a:b]
+            np.testing.assert_allclose(tree[lv - 1].L[n], L, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(tree[lv - 1].g[n], g, rtol=0, atol=1e-12)
+
+
+def pin_tangent_point(o=O, N=96, d=8, R=4, C=4, levels=3, seed=4):
+    """P4: at q = r_j the score is L_j (planes touch there; others lie below)."""
+    K, V, ref, Q = _rand_cache(N, d, R, seed)
+    tree = o.build_tree(K, ref, C, levels, "f64")
+    for lvl in tree:
+        for j in range(R):
+            s = o.plane_scores(ref[j], lvl, ref)
+            # the max over planes at r_j is exactly L_j (convexity: other planes <= f(r_j) = L_j)
+            np.testing.assert_allclose(s, lvl.L[:, j], rtol=0, atol=1e-12)
+
+
+def pin_gibbs_bound(o=O, N=128, d=8, R=4, C=4, levels=3, seed=5):
+    """P5: every plane, hence the score, is <= the exact log mass of the node."""
+    K, V, ref, Q = _rand_cache(N, d, R, seed)
+    tree = o.build_tree(K, ref, C, levels, "f64")
+    rng = np.random.default_rng(seed)
+    for q in np.concatenate([Q, rng.normal(size=(10, d)) * 2.0]):
+        for lv, lvl in enumerate(tree, start=1):
+            s = o.plane_scores(q, lvl, ref)
+            for n in range(lvl.L.shape[0]):
+                a, b = o.node_token_range(lv, n, C, N)
+                exact = sps.logsumexp(K[a:b] @ q / math.sqrt(d))
+                assert s[n] <= exact + 1e-12
+
+
+def pin_entropy(o=O, N=128, d=8, R=4, C=4, levels=3, seed=6):
+    """P6: c_j is the Shannon entropy of r_j's softmax over the node, in [0, ln|node|]."""
+    K, V, ref, Q = _rand_cache(N, d, R, seed)
+    tree = o.build_tree(K, ref, C, levels, "f64")
+    for lv, lvl in enumerate(tree, start=1):
+        for n in range(lvl.L.shape[0]):
+            a, b = o.node_token_range(lv, n, C, N)
+            z = (K[a:b] @ ref.T) / math.sqrt(d)
+            H = sst.entropy(sps.softmax(z, axis=0), axis=0)
+            np.testing.assert_allclose(lvl.c[n], H, rtol=0, atol=1e-11)
+            assert np.all(lvl.c[n] >= -1e-12) and np.all(lvl.c[n] <= math.log(b - a) + 1e-12)
+
+
+def pin_zero_reference(o=O, N=64, d=8, C=4, levels=3, seed=7):
+    """P7: r = 0 gives uniform weights: c = ln|node|, g = centroid."""
+    K, V, ref, Q = _rand_cache(N, d, 1, seed)
+    ref = np.zeros((1, d))
+    tree = o.build_tree(K, ref, C, levels, "f64")
+    for lv, lvl in enumerate(tree, start=1):
+        for n in range(lvl.L.shape[0]):
+            a, b = o.node_token_range(lv, n, C, N)
+            np.testing.assert_allclose(lvl.c[n, 0], math.log(b - a), atol=1e-12)
+            np.testing.assert_allclose(lvl.g[n, 0], K[a:b].mean(axis=0), atol=1e-12)
+            for q in Q:
+                s = o.plane_scores(q, lvl, ref, [n])[0]
+                np.testing.assert_allclose(s, math.log(b - a) + q @ K[a:b].mean(0) / math.sqrt(d), atol=1e-12)
+
+
+def pin_top_p_invariants(o=O, seed=8):
+    """P8: kept mass >= pM; removing the smallest kept drops below pM; kept >= dropped."""
+    rng = np.random.default_rng(seed)
+    for trial in range(200):
+        n = int(rng.integers(1, 300))
+        s = rng.normal(size=n) * rng.uniform(0.1, 4)
+        if trial % 5 == 0:  # exact ties
+            s = np.round(s, 1)
+        ids = rng.permutation(10 * n)[:n]
+        p = float(rng.uniform(0.05, 0.999))
+        sel = o.top_p_select(ids, s, p)
+        m = np.exp(s - s.max())
+        M = m.sum()
+        kept = sel.kept
+        assert kept.any()
+        assert m[kept].sum() >= p * M * (1 - 1e-12)
+        smallest = np.min(m[kept])
+        assert m[kept].sum() - smallest < p * M * (1 + 1e-12)
+        if (~kept).any():
+            assert m[~kept].max() <= m[kept].min()
+        # ties: among equal scores the lower ids are kept first
+        for v in np.unique(s):
+            eq = s == v
+            if kept[eq].any() and (~kept[eq]).any():
+                assert ids[eq & kept].max() < ids[eq & ~kept].min()
+    # p = 1 keeps everything, even masses that underflow
+    s = np.array([0.0, -800.0, -900.0])
+    assert o.top_p_select(np.arange(3), s, 1.0).kept.all()
+
+
+def pin_brute_force_minimal(o=O, seed=9):
+    """P9: on tiny trees the kept set is the minimum-cardinality set with mass >= pM."""
+    rng = np.random.default_rng(seed)
+    checked = 0
+    for trial in range(40):
+        N = int(rng.integers(8, 65))
+        C, levels, d, R = 2, int(rng.integers(1, 4)), 6, int(rng.integers(1, 4))
+        K, V, ref, Q = _rand_cache(N, d, R, 100 + trial, seg=4)
+        tree = o.build_tree(K, ref, C, levels, "f64")
+        p = float(rng.uniform(0.3, 0.99))
+        for q in Q[:2]:
+            for rec in o.route(q, tree, ref, C, p):
+                sel = rec.sel
+                n = sel.ids.size
+                if n == 0 or n > 16:
+                    continue
+                m = sel.mass
+                target = p * sel.total
+                best = None
+                for k in range(1, n + 1):
+                    sets = [c for c in itertools.combinations(range(n), k) if m[list(c)].sum() >= target]
+                    if sets:
+                        best = k
+                        break
+                assert best == int(sel.kept.sum())
+                # with distinct masses the minimal set of max mass is unique: the kept one
+                top = np.argsort(-m, kind="stable")[:best]
+                if len(np.unique(m)) == n:
+                    assert set(top) == set(np.nonzero(sel.kept)[0])
+                checked += 1
+    assert checked > 50
+
+
+def pin_structure(o=O, N=1000, d=8, R=3, C=4, levels=4, seed=10):
+    """P10: kept nodes lie under kept parents; A holds the sink and the current chunk."""
+    K, V, ref, Q = _rand_cache(N + 3, d, R, seed)
+    for n_tok in (N, N + 3):
+        tree = o.build_tree(K, ref, C, levels, "f64", n_tokens=n_tok)
+        for q in Q:
+            out, lse, idx, recs = o.route_and_attend(q, K, V, tree, ref, C, 0.8, n_tok)
+            for up, down in zip(recs[:-1], recs[1:]):
+                parents = set(up.sel.kept_ids.tolist())
+                assert all(int(x) // C in parents for x in down.sel.ids)
+                assert set(down.sel.kept_ids.tolist()) <= set(down.sel.ids.tolist())
+            assert 0 in idx
+            last = C * ((n_tok - 1) // C)
+            assert set(range(last, n_tok)) <= set(idx.tolist())
+            forced = {0} | set(range(last, n_tok))
+            rest = [i for i in idx.tolist() if i not in forced]
+            chunks = {i // C for i in rest}
+            assert all(set(range(c * C, c * C + C)) <= set(idx.tolist()) for c in chunks)
+
+
+def pin_prefix_stable(o=O, d=8, R=3, C=4, levels=3, seed=11):
+    """P11 (oracle side): nodes complete in a prefix are unchanged when keys are appended."""
+    K, V, ref, Q = _rand_cache(300, d, R, seed)
+    small = o.build_tree(K, ref, C, levels, "f64", n_tokens=170)
+    big = o.build_tree(K, ref, C, levels, "f64", n_tokens=300)
+    for lv in range(1, levels + 1):
+        span = C ** lv
+        n_full = 168 // span  # nodes whose whole span lies in the complete chunks of the prefix
+        np.testing.assert_array_equal(small[lv - 1].L[:n_full], big[lv - 1].L[:n_full])
+        np.testing.assert_array_equal(small[lv - 1].ghat[:n_full], big[lv - 1].ghat[:n_full])
+
+
+def pin_subset_attention(o=O, N=90, d=8, seed=12):
+    """P12: attention over any index set is torch's softmax attention over the gathered keys."""
+    K, V, ref, Q = _rand_cache(N, d, 2, seed)
+    rng = np.random.default_rng(seed)
+    for q in Q:
+        idx = np.sort(rng.choice(N, size=int(rng.integers(1, N)), replace=False))
+        out, lse = o.attend(q, K, V, idx)
+        ref_o = torch.nn.functional.scaled_dot_product_attention(
+            torch.tensor(q)[None, None, None], torch.tensor(K[idx])[None, None], torch.tensor(V[idx])[None, None]
+        )[0, 0, 0].numpy()
+        np.testing.assert_allclose(out, ref_o, rtol=0, atol=1e-12)
+
+
+PINS = [
+    pin_dense_at_p1,
+    pin_chunk1_exact_logit,
+    pin_merge_equals_direct,
+    pin_tangent_point,
+    pin_gibbs_bound,
+    pin_entropy,
+    pin_zero_reference,
+    pin_top_p_invariants,
+    pin_brute_force_minimal,
+    pin_structure,
+    pin_prefix_stable,
+    pin_subset_attention,
+]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(pin):
+    pin()
+
+
+# ----------------------------------------------------------------------------
+# storage rounding and geometry
+
+
+def test_bf16_rounding_matches_torch_on_fp32_inputs():
+    rng = np.random.default_rng(0)
+    x32 = (rng.normal(size=20000) * np.exp(rng.normal(size=20000) * 5)).astype(np.float32)
+    mine = O.round_bf16(x32.astype(np.float64))
+    theirs = torch.tensor(x32).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(mine, theirs)
+
+
+def test_bf16_rounding_single_rounding_from_fp64():
+    # 1 + 2^-8 is the midpoint between 1 and 1 + 2^-7: ties go to the even mantissa (1.0)
+    assert O.round_bf16(np.array([1.0 + 2.0**-8]))[0] == 1.0
+    # just above the midpoint rounds up, even though fp32 would first round it to the midpoint
+    x = 1.0 + 2.0**-8 + 2.0**-40
+    assert O.round_bf16(np.array([x]))[0] == 1.0 + 2.0**-7
+    assert O.round_bf16(np.array([3.0 * 2.0**-8 + 1.0]))[0] == 1.0 + 2.0**-6
+
+
+def test_golden_geometry():
+    gold = json.load(open(os.path.join(GOLDEN, "geometry.json")))
+    for t in gold["trees"]:
+        C, lv = t["chunk"], t["levels"]
+        # a top node spans the tokens of C**levels: one top node per top_span keys
+        sizes = O.level_sizes(t["top_span"], C, lv)
+        assert sizes[-1] == 1 and sizes[0] == t["top_span"] // C
+        assert O.level_sizes(t["top_span"] + C, C, lv)[-1] == 2
+    anim = gold["animation"]
+    C = anim["chunk"]
+    counts = {int(k): v for k, v in anim["nodes_per_level"].items()}
+    assert O.level_sizes(counts[1] * C, C, 3) == [counts[1], counts[2], counts[3]]
+    kept = {int(k): v for k, v in anim["kept"].items()}
+    for lv in (2, 1):
+        cand = O.children(np.array(kept[lv + 1]), C, counts[lv])
+        assert set(kept[lv]) <= set(cand.tolist())
+
+
+def test_workload_geometry():
+    for w in W.WORKLOADS.values():
+        assert w.top_span == w.chunk ** w.levels
+    assert W.WORKLOADS["deep1m"].top_span == 4096
+    assert W.WORKLOADS["wide256k"].top_span == 256
+    assert int(W.WORKLOADS["deep1m"].needle_counts().sum()) == 256
+    assert int(W.WORKLOADS["deep32k"].needle_counts().sum()) == 32
+    assert int(W.WORKLOADS["tiny"].needle_counts().sum()) == 8
+
+
+def test_tiny_workload_routes_needles():
+    """On the tiny workload the oracle finds planted needles through the tree."""
+    w = W.WORKLOADS["tiny"]
+    b = W.make_batch(w)
+    K = b.K[0, 0, : w.n_tokens].double().numpy()
+    V = b.V[0, 0, : w.n_tokens].double().numpy()
+    ref = b.ref[0].double().numpy()
+    tree = O.build_tree(K, ref, w.chunk, w.levels, "f32")
+    found = 0
+    for t in range(w.queries_per_head):
+        q = b.Q[0, 0, 0, t].double().numpy()
+        o, lse, idx, recs = O.route_and_attend(q, K, V, tree, ref, w.chunk, w.p[0], w.n_tokens)
+        assert 0 < idx.size < w.n_tokens
+        for pos in b.needles[0][t]:
+            found += int(pos in set(idx.tolist()))
+    assert found >= 1
+
+
+# ----------------------------------------------------------------------------
+# planted mistakes: each must make at least one pin fail
+
+
+def _fails(pin, monkeypatch, name, bad):
+    with monkeypatch.context() as mp:
+        mp.setattr(O, name, bad)
+        with pytest.raises(AssertionError):
+            pin()
+
+
+def test_planted_score_sign_error_is_caught(monkeypatch):
+    def bad(q, level, ref, ids=None):
+        q = np.asarray(q, float)
+        ids = np.arange(level.L.shape[0]) if ids is None else np.asarray(ids)
+        d = q.shape[-1]
+        planes = level.L[ids] + np.einsum("nrd,rd->nr", level.ghat[ids], q[None] + ref) / math.sqrt(d)
+        return planes.max(1)
+
+    _fails(pin_tangent_point, monkeypatch, "plane_scores", bad)
+
+
+def test_planted_missing_scale_is_caught(monkeypatch):
+    def bad(q, level, ref, ids=None):
+        q = np.asarray(q, float)
+        ids = np.arange(level.L.shape[0]) if ids is None else np.asarray(ids)
+        planes = level.L[ids] + np.einsum("nrd,rd->nr", level.ghat[ids], q[None] - ref)
+        return planes.max(1)
+
+    _fails(pin_chunk1_exact_logit, monkeypatch, "plane_scores", bad)
+
+
+def test_planted_merge_weight_error_is_caught(monkeypatch):
+    orig = O._logsumexp
+
+    def bad_lse(a, axis):  # mean instead of logsumexp
+        return np.mean(a, axis=axis)
+
+    _fails(pin_merge_equals_direct, monkeypatch, "_logsumexp", bad_lse)
+
+
+def test_planted_selection_order_error_is_caught(monkeypatch):
+    orig = O.top_p_select
+
+    def bad(ids, score, p):  # keeps the lowest-scoring candidates first
+        return orig(ids, -np.asarray(score), p)
+
+    _fails(pin_top_p_invariants, monkeypatch, "top_p_select", bad)
+
+
+def test_planted_children_index_error_is_caught(monkeypatch):
+    def bad(ids, chunk, n_below):
+        ids = np.asarray(ids, dtype=np.int64)
+        kids = (ids[:, None] + np.arange(chunk)[None, :]).reshape(-1)
+        return np.unique(kids[kids < n_below])
+
+    _fails(pin_structure, monkeypatch, "children", bad)
+
+
+def test_planted_sink_dropped_is_caught(monkeypatch):
+    orig = O.attend_set
+
+    def bad(kept, n, chunk, sink=True, last_chunk=True):
+        return orig(kept, n, chunk, False, last_chunk)
+
+    _fails(pin_structure, monkeypatch, "attend_set", bad)
