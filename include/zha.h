@@ -1,0 +1,294 @@
+/*
+ * zha.h - C ABI of the ZHA decode hot path on AMD Instinct MI355X (gfx950).
+ *
+ * ZHA (Zyphra Hierarchical Attention) keeps the full KV cache and builds a
+ * tree index over it; a decode query walks the tree top-down with per-level
+ * top-p selection and then runs exact attention over the keys it reached.
+ *
+ * Sources (web pages, cited by title and section):
+ *   MTP = "Zyphra AI Introduces Zyphra Hierarchical Attention (ZHA): A Path to
+ *         True Subquadratic Attention" (MarkTechPost article with its
+ *         explainer widget).
+ *   LC  = "Zyphra Hierarchical Attention" (lesscarbs.net), "What happened?".
+ *
+ * Conventions for every entry point:
+ *   - Every pointer argument named *device* is device memory owned by the
+ *     caller; the library never allocates, frees or retains device memory and
+ *     keeps no global mutable state apart from a thread-local error string.
+ *   - Calls are asynchronous and ordered on the given HIP stream (a
+ *     hipStream_t passed as void*; NULL = the default stream).  No call
+ *     synchronises the host.  Device faults surface at the caller's next
+ *     synchronisation.  NaN/Inf inputs are not sanitised and propagate.
+ *   - All argument checks run on the host before any HIP call; a failed check
+ *     returns a negative zha_status and launches nothing.  zha_last_error()
+ *     then describes the failure.
+ *   - Two calls may run concurrently on different streams when they write to
+ *     distinct buffers.
+ *
+ * Shapes.  B sequences, H KV heads, G query heads per KV head, d head dim,
+ * R reference queries, C chunk size, Lv levels, T queries per query head.
+ * A "cache" is one (sequence, KV head) pair with its own tree; cache index
+ * = b * H + h.  Query index = ((b * H + h) * G + g) * T + t.
+ */
+#ifndef ZHA_H_
+#define ZHA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZHA_VERSION 1
+#define ZHA_MAX_LEVELS 8
+
+/* Status codes returned by every int-returning entry point. */
+enum zha_status {
+  ZHA_OK = 0,
+  ZHA_ERR_NULL = -1,        /* a required pointer is NULL */
+  ZHA_ERR_ARG = -2,         /* bad dimension, p outside (0, 1], T <= 0, n_old mismatch, ... */
+  ZHA_ERR_UNSUPPORTED = -3, /* valid but not implemented (head_dim, chunk, n_ref, dtype) */
+  ZHA_ERR_CAPACITY = -4,    /* tokens beyond capacity, or a buffer too small */
+  ZHA_ERR_ALIGN = -5,       /* a row or base pointer is not 16-byte aligned */
+  ZHA_ERR_HIP = -6          /* a HIP call or launch failed (text in zha_last_error) */
+};
+
+/* Element types of K, V, Q and of the stored mean keys g. */
+enum zha_dtype { ZHA_F32 = 0, ZHA_BF16 = 1 };
+
+/* Flags of zha_attend. */
+enum zha_attend_flags {
+  ZHA_SINK = 1,       /* token 0 is always attended (MTP "How does top-p routing pick tokens?") */
+  ZHA_LAST_CHUNK = 2, /* tokens [C*floor((N-1)/C), N) are always attended (MTP widget step 5) */
+  ZHA_ALL_KEYS = 4    /* ignore the selection: dense attention over all N keys */
+};
+
+/*
+ * Problem configuration.  Supported: head_dim in {64, 128}; n_ref in 1..16;
+ * chunk a power of two in 1..256; levels in 1..ZHA_MAX_LEVELS with
+ * chunk^levels <= 2^24; kv_dtype ZHA_F32 or ZHA_BF16 (g is stored in the same
+ * type); q_per_kv * T <= 1024.  Anything else is ZHA_ERR_UNSUPPORTED.
+ */
+typedef struct zha_config {
+  int32_t batch;           /* B */
+  int32_t n_kv_heads;      /* H */
+  int32_t q_per_kv;        /* G: query heads sharing one KV head (and its tree) */
+  int32_t head_dim;        /* d */
+  int32_t n_ref;           /* R: reference queries per KV head */
+  int32_t chunk;           /* C: keys per level-1 node; children per upper node */
+  int32_t levels;          /* Lv: level 1 = chunks of raw keys, level Lv = top */
+  int32_t kv_dtype;        /* enum zha_dtype */
+  int64_t capacity_tokens; /* largest N the tree buffer must hold */
+} zha_config;
+
+/*
+ * Tree buffer layout (computed by zha_get_tree_layout).  Level l (index l-1)
+ * holds node_cap[l-1] = ceil(node_cap[l-2] / C) nodes per cache, with
+ * node_cap[0] = floor(capacity / C).  Per level, three blocks:
+ *   g: [caches][node_cap][R*d] in kv_dtype.  Within one node the R x d mean
+ *      keys are stored d-chunk-interleaved so that one 64-lane load yields a
+ *      16 x 32 MFMA operand tile: element (j, e) with 16-byte piece
+ *      k = e / E (E = elements per 16 bytes), sub-index e % E, lives at
+ *      element offset ((k / 4) * 4 * R + (k % 4) * R + j) * E + e % E.
+ *   L: [caches][node_cap][R] fp32, log mass L_j of the node.
+ *   c: [caches][node_cap][R] fp32, plane offset c_j = L_j - r_j . g_j / sqrt(d)
+ *      with the stored (rounded) g_j.
+ * Offsets are bytes from the tree base; every block is 256-byte aligned.
+ */
+typedef struct zha_tree_layout {
+  int32_t levels;
+  int32_t reserved;
+  int64_t node_cap[ZHA_MAX_LEVELS];
+  int64_t g_offset[ZHA_MAX_LEVELS];
+  int64_t L_offset[ZHA_MAX_LEVELS];
+  int64_t c_offset[ZHA_MAX_LEVELS];
+  int64_t g_node_bytes; /* R * d * sizeof(kv_dtype) */
+  int64_t total_bytes;  /* size of the caller's tree buffer */
+} zha_tree_layout;
+
+/*
+ * Route output layout (computed by zha_get_route_layout) for n_queries =
+ * B*H*G*T queries.  Per level l (index l-1):
+ *   sel:   [n_queries][words[l-1]] uint32 bitsets, bit n%32 of word n/32 set
+ *          iff node n is kept; starts at sel_offset[l-1] (in uint32 words).
+ *   score: [n_queries][node_cap[l-1]] fp32 plane scores of the candidates,
+ *          -inf for nodes that were not candidates; starts at
+ *          score_offset[l-1] (in floats).
+ *   stats: [n_queries] zha_select_stats; starts at stats_offset[l-1]
+ *          (in records).
+ */
+typedef struct zha_route_layout {
+  int32_t levels;
+  int32_t reserved;
+  int64_t n_queries;
+  int64_t words[ZHA_MAX_LEVELS];
+  int64_t sel_offset[ZHA_MAX_LEVELS];
+  int64_t score_offset[ZHA_MAX_LEVELS];
+  int64_t stats_offset[ZHA_MAX_LEVELS];
+  int64_t sel_words_total;    /* uint32 words of the sel buffer */
+  int64_t score_floats_total; /* floats of the score buffer */
+  int64_t stats_total;        /* records of the stats buffer */
+  int64_t workspace_bytes;    /* scratch zha_route needs */
+} zha_route_layout;
+
+/*
+ * Per (level, query) record of the top-p selection.  Masses are fixed-point
+ * integers m = round(exp(s - max_score) * 2^shift), so sums are exact and
+ * independent of summation order.  A candidate is kept iff its order key is
+ * > cut_key, or == cut_key and its node id < cut_id (ties go to lower ids).
+ */
+typedef struct zha_select_stats {
+  float max_score;     /* largest candidate score */
+  int32_t n_cand;      /* candidates at this level */
+  int32_t n_kept;      /* kept candidates */
+  uint32_t cut_key;    /* order key of the last kept score */
+  int32_t cut_id;      /* tie bound at cut_key (exclusive) */
+  int32_t shift;       /* fixed-point shift of the masses */
+  uint64_t mass_total; /* sum of candidate masses (M) */
+  uint64_t mass_kept;  /* sum of kept masses */
+} zha_select_stats;
+
+/*
+ * Optional per-kernel timing.  When a call receives a non-NULL zha_profile,
+ * it records events[2k] on the stream right before its k-th kernel launch
+ * and events[2k+1] right after it, for k < n_pairs, and reports in n_used
+ * how many kernels it launched and in kernel[k] which kernel each pair
+ * timed (enum zha_kernel_id * 16 + level, level 0 when not per-level).
+ * The events are caller-created hipEvent_t handles; the library only
+ * records them (no allocation, no synchronisation).
+ */
+#define ZHA_PROFILE_MAX 32
+enum zha_kernel_id {
+  ZHA_K_BUILD = 1,   /* tree build over whole top spans */
+  ZHA_K_SCORE = 2,   /* plane scores of one level's candidates */
+  ZHA_K_SELECT = 3,  /* top-p selection of one level */
+  ZHA_K_ATTEND = 4,  /* split-K attention over the routed keys */
+  ZHA_K_COMBINE = 5  /* merge of the split-K partials */
+};
+typedef struct zha_profile {
+  void* events[2 * ZHA_PROFILE_MAX]; /* hipEvent_t */
+  int32_t n_pairs;                    /* event pairs provided (<= ZHA_PROFILE_MAX) */
+  int32_t n_used;                     /* (out) kernels launched by the call */
+  int32_t kernel[ZHA_PROFILE_MAX];    /* (out) id * 16 + level of each timed kernel */
+} zha_profile;
+
+/* ---- information ------------------------------------------------------- */
+
+int zha_version(void);
+/* Static text for a status code. */
+const char* zha_status_string(int status);
+/* Thread-local description of the last failure of this thread ("" if none). */
+const char* zha_last_error(void);
+
+/* ---- sizes and layouts (host only, never touch the GPU) ---------------- */
+
+/* Fills *out for cfg.  Returns ZHA_OK or a validation error. */
+int zha_get_tree_layout(const zha_config* cfg, zha_tree_layout* out);
+/* Fills *out for cfg and T queries per query head. */
+int zha_get_route_layout(const zha_config* cfg, int32_t T, zha_route_layout* out);
+/* Scratch bytes zha_attend / zha_dense_decode need for T queries per head. */
+int64_t zha_attend_workspace_bytes(const zha_config* cfg, int32_t T);
+
+/* ---- the hot path ------------------------------------------------------- */
+
+/*
+ * zha_build - build every tree level for the first n_tokens keys.
+ * Defines (MTP "Building the tree"): keys are cut into contiguous chunks of
+ * C; each chunk is summarised per reference query r_j by its log attention
+ * mass L_j = logsumexp_i (r_j . k_i / sqrt(d)) and the tangent-plane slope
+ * g_j = sum_i softmax_i(r_j . k_i / sqrt(d)) k_i; summaries are merged level
+ * by level: L(P) = logsumexp_c L(c), g(P) = sum_c exp(L(c) - L(P)) g(c).
+ * n_1 = floor(N / C) leaves (a trailing partial chunk is not a node);
+ * n_l = ceil(n_{l-1} / C) (a partial upper node merges the children present).
+ *   K        device, [B][H][capacity][d] kv_dtype addressed by
+ *            k_strides = {batch, head, token} in elements; each token row
+ *            is d contiguous elements, 16-byte aligned.
+ *   ref      device, [H][R][d] fp32 reference queries (bf16-representable
+ *            values when kv_dtype is bf16).
+ *   tree     device, zha_get_tree_layout(cfg).total_bytes bytes; overwritten for
+ *            the nodes that exist at n_tokens.
+ * Errors: NULL pointers, n_tokens < 0 or > capacity, misalignment.
+ */
+int zha_build(const zha_config* cfg, const void* K, const int64_t k_strides[3], int64_t n_tokens,
+              const float* ref, void* tree, zha_profile* prof, void* stream);
+
+/*
+ * zha_append - extend a tree built for n_old tokens to n_old + n_new.
+ * The caller has already written K rows [n_old, n_old + n_new).  Only the
+ * nodes whose key range meets the new tokens are rewritten (new leaves and
+ * the right spine of ancestors); the result is bit-identical to zha_build
+ * over n_old + n_new tokens.  MTP "Building the tree" defines the nodes;
+ * growth in place follows from nodes being functions of their key range.
+ * Errors: as zha_build, plus n_old < 0, n_new < 0, n_old + n_new > capacity.
+ */
+int zha_append(const zha_config* cfg, const void* K, const int64_t k_strides[3], int64_t n_old,
+               int64_t n_new, const float* ref, void* tree, zha_profile* prof, void* stream);
+
+/*
+ * zha_route - top-down top-p routing of B*H*G*T decode queries.
+ * Defines (MTP "Building the tree", "How does top-p routing pick tokens?",
+ * widget "1 . How it works" steps 2-4): a query scores a node by the max
+ * over its reference-query tangent planes,
+ *   s(q, node) = max_j [ L_j + (q - r_j) . g_j / sqrt(d) ]
+ *              = max_j [ c_j + q . g_j / sqrt(d) ];
+ * all top-level nodes are candidates; at each level the estimated masses
+ * exp(s) are renormalised over the query's candidates, the smallest set
+ * holding fraction p is kept (order: score descending, node id ascending;
+ * keep a candidate iff the mass ranked before it is < p * M; p >= 1 keeps
+ * all), and the children of kept nodes become the next candidates, down to
+ * level 1 (raw chunks).
+ *   tree      device, built for n_tokens.
+ *   Q         device, [B][H][G][T][d] kv_dtype with q_strides = {batch,
+ *             kv head, query head, t} in elements; rows contiguous, 16-byte
+ *             aligned.
+ *   p         in (0, 1]; NaN or <= 0 is ZHA_ERR_ARG.
+ *   sel       device, zha_get_route_layout().sel_words_total uint32 (output).
+ *   score     device, zha_get_route_layout().score_floats_total fp32 (output).
+ *   stats     device, zha_get_route_layout().stats_total records (output).
+ *   ws        device scratch of at least workspace_bytes.
+ * Level-1 bits of sel are the routed chunk ids consumed by zha_attend.
+ */
+int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const void* Q,
+              const int64_t q_strides[4], int32_t T, float p, uint32_t* sel, float* score,
+              zha_select_stats* stats, void* ws, int64_t ws_bytes, zha_profile* prof, void* stream);
+
+/*
+ * zha_attend - exact softmax attention over the routed keys.
+ * Defines (MTP widget step 5; "How does top-p routing pick tokens?"):
+ *   A = keys of the level-1 chunks whose bit is set in sel1
+ *       U {0} (ZHA_SINK) U [C*floor((N-1)/C), N) (ZHA_LAST_CHUNK),
+ *   o = sum_{i in A} softmax_i(q . k_i / sqrt(d)) v_i,  lse = logsumexp.
+ * With ZHA_ALL_KEYS, A = all N keys (dense decode).
+ *   Q         as zha_route.
+ *   K, V      device, as zha_build (same kv_strides for both).
+ *   sel1      device, [n_queries][sel1_words] uint32 chunk bitsets (the
+ *             level-1 block of zha_route's sel, or any set); may be NULL
+ *             with ZHA_ALL_KEYS.
+ *   out       device, [n_queries][d] fp32 (output).
+ *   lse       device, [n_queries] fp32 (output, may be NULL).
+ *   ws        device scratch of zha_attend_workspace_bytes(cfg, T).
+ *   prof      optional per-kernel timing (may be NULL), see zha_profile.
+ * Errors: NULL pointers, n_tokens outside [1, capacity], sel1_words <
+ * ceil(floor(n_tokens / C) / 32), workspace too small, misalignment.
+ */
+int zha_attend(const zha_config* cfg, const void* Q, const int64_t q_strides[4], int32_t T,
+               const void* K, const void* V, const int64_t kv_strides[3], int64_t n_tokens,
+               const uint32_t* sel1, int64_t sel1_words, uint32_t flags, float* out, float* lse,
+               void* ws, int64_t ws_bytes, zha_profile* prof, void* stream);
+
+/*
+ * zha_dense_decode - dense flash-decode over all n_tokens keys, the
+ * same-GPU baseline (MTP "How fast is ZHA?" compares against dense
+ * attention).  Equivalent to zha_attend with ZHA_ALL_KEYS and no sel1.
+ */
+int zha_dense_decode(const zha_config* cfg, const void* Q, const int64_t q_strides[4], int32_t T,
+                     const void* K, const void* V, const int64_t kv_strides[3], int64_t n_tokens,
+                     float* out, float* lse, void* ws, int64_t ws_bytes, zha_profile* prof,
+                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZHA_H_ */

@@ -1,0 +1,167 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+entry point, computes layouts, and rejects bad arguments before any HIP call."""
+import ctypes as ct
+import os
+import re
+
+import pytest
+
+from tree_indexed_sparse_zha_amd import zha
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zha.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zha_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return zha.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status(lib):
+    assert zha.version() == 1
+    assert lib.zha_status_string(0) == b"ok"
+    assert lib.zha_status_string(-4).startswith(b"capacity")
+
+
+def cfg_deep(**kw):
+    base = dict(batch=1, n_kv_heads=8, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=6, dtype="bf16", capacity=32768)
+    base.update(kw)
+    return zha.ZhaConfig(**base)
+
+
+def test_tree_layout_sizes():
+    cfg = cfg_deep()
+    tl = zha.tree_layout(cfg)
+    assert tl.levels == 6
+    assert [tl.node_cap[i] for i in range(6)] == [8192, 2048, 512, 128, 32, 8]
+    assert tl.g_node_bytes == 16 * 128 * 2
+    # node = R*d*2 (g) + 4R (L) + 4R (c) = 4224 bytes
+    nodes = sum(tl.node_cap[i] for i in range(6)) * 8
+    assert tl.total_bytes >= nodes * 4224
+    assert tl.total_bytes < nodes * 4224 + 6 * 3 * 256
+    for i in range(6):
+        assert tl.g_offset[i] % 256 == 0 and tl.L_offset[i] % 256 == 0 and tl.c_offset[i] % 256 == 0
+
+
+def test_route_layout_sizes():
+    cfg = cfg_deep()
+    rl = zha.route_layout(cfg, 64)
+    assert rl.n_queries == 8 * 4 * 64
+    assert rl.words[0] == 8192 // 32
+    assert rl.score_floats_total == rl.n_queries * (8192 + 2048 + 512 + 128 + 32 + 8)
+    assert rl.stats_total == 6 * rl.n_queries
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(head_dim=96), zha.ZHA_ERR_UNSUPPORTED),
+        (dict(head_dim=0), zha.ZHA_ERR_ARG),
+        (dict(n_ref=17), zha.ZHA_ERR_UNSUPPORTED),
+        (dict(chunk=3), zha.ZHA_ERR_UNSUPPORTED),
+        (dict(chunk=512, levels=1), zha.ZHA_ERR_UNSUPPORTED),
+        (dict(levels=9), zha.ZHA_ERR_UNSUPPORTED),
+        (dict(chunk=16, levels=7), zha.ZHA_ERR_UNSUPPORTED),  # span 2^28
+        (dict(batch=0), zha.ZHA_ERR_ARG),
+        (dict(capacity=0), zha.ZHA_ERR_ARG),
+        (dict(dtype="f32", head_dim=64, n_ref=4, chunk=4, levels=3), 0),
+    ],
+)
+def test_config_validation(kw, code):
+    cfg = cfg_deep(**kw)
+    if code == 0:
+        zha.tree_layout(cfg)
+        return
+    with pytest.raises(zha.ZhaError) as e:
+        zha.tree_layout(cfg)
+    assert e.value.code == code
+
+
+def _call_route(lib, cfg, **over):
+    a = dict(tree=16, n_tokens=32768, Q=16, qs=zha._i64(1 << 20, 1 << 16, 1 << 12, 128), T=1, p=0.95,
+             sel=16, score=16, stats=16, ws=16, ws_bytes=0)
+    a.update(over)
+    c = cfg.c()
+    return lib.zha_route(ct.byref(c), a["tree"], a["n_tokens"], a["Q"], a["qs"], a["T"], a["p"], a["sel"],
+                         a["score"], a["stats"], a["ws"], a["ws_bytes"], a.get("prof"), None)
+
+
+def test_route_argument_errors(lib):
+    cfg = cfg_deep()
+    # fake but aligned addresses: every case fails validation before any HIP call
+    assert _call_route(lib, cfg, tree=None) == zha.ZHA_ERR_NULL
+    assert _call_route(lib, cfg, Q=8) == zha.ZHA_ERR_ALIGN
+    assert _call_route(lib, cfg, p=0.0) == zha.ZHA_ERR_ARG
+    assert _call_route(lib, cfg, p=float("nan")) == zha.ZHA_ERR_ARG
+    assert _call_route(lib, cfg, p=-0.5) == zha.ZHA_ERR_ARG
+    assert _call_route(lib, cfg, T=0) == zha.ZHA_ERR_ARG
+    assert _call_route(lib, cfg, T=512) == zha.ZHA_ERR_UNSUPPORTED
+    assert _call_route(lib, cfg, n_tokens=32769) == zha.ZHA_ERR_CAPACITY
+    assert b"n_tokens exceeds capacity" in lib.zha_last_error()
+    assert _call_route(lib, cfg, qs=zha._i64(1, 1, 1, 1)) == zha.ZHA_ERR_ALIGN
+    bad = zha.Profile()
+    bad.n_pairs = 40
+    assert _call_route(lib, cfg, prof=ct.byref(bad)) == zha.ZHA_ERR_ARG
+    bad.n_pairs = 1  # events left NULL
+    assert _call_route(lib, cfg, prof=ct.byref(bad)) == zha.ZHA_ERR_NULL
+
+
+def test_build_argument_errors(lib):
+    cfg = cfg_deep()
+    c = cfg.c()
+    ks = zha._i64(8 * 32768 * 128, 32768 * 128, 128)
+    assert lib.zha_build(ct.byref(c), None, ks, 100, 16, 16, None, None) == zha.ZHA_ERR_NULL
+    assert lib.zha_build(ct.byref(c), 16, ks, 40000, 16, 16, None, None) == zha.ZHA_ERR_CAPACITY
+    assert b"exceed capacity" in lib.zha_last_error()
+    assert lib.zha_build(ct.byref(c), 16, ks, -1, 16, 16, None, None) == zha.ZHA_ERR_ARG
+    assert lib.zha_build(ct.byref(c), 16, zha._i64(0, 0, 4), 10, 16, 16, None, None) == zha.ZHA_ERR_ALIGN
+    assert lib.zha_append(ct.byref(c), 16, ks, 30000, 5000, 16, 16, None, None) == zha.ZHA_ERR_CAPACITY
+    assert lib.zha_append(ct.byref(c), 16, ks, -4, 5, 16, 16, None, None) == zha.ZHA_ERR_ARG
+    # no new complete chunk: nothing to do, succeeds without touching the GPU
+    assert lib.zha_append(ct.byref(c), 16, ks, 100, 3, 16, 16, None, None) == zha.ZHA_OK
+
+
+def test_attend_argument_errors(lib):
+    cfg = cfg_deep()
+    c = cfg.c()
+    qs = zha._i64(1 << 20, 1 << 16, 1 << 12, 128)
+    ks = zha._i64(8 * 32768 * 128, 32768 * 128, 128)
+    ws = zha.attend_workspace_bytes(cfg, 1)
+    assert ws > 0
+
+    def call(**o):
+        a = dict(Q=16, T=1, K=16, V=16, n=32768, sel=16, words=256, flags=3, out=16, ws=16, wsb=ws)
+        a.update(o)
+        return lib.zha_attend(ct.byref(c), a["Q"], qs, a["T"], a["K"], a["V"], ks, a["n"], a["sel"], a["words"],
+                              a["flags"], a["out"], None, a["ws"], a["wsb"], None, None)
+
+    assert call(sel=None) == zha.ZHA_ERR_NULL
+    assert call(words=255) == zha.ZHA_ERR_CAPACITY
+    assert call(wsb=ws - 1) == zha.ZHA_ERR_CAPACITY
+    assert call(n=0) == zha.ZHA_ERR_ARG
+    assert call(n=40000) == zha.ZHA_ERR_CAPACITY
+    assert call(flags=8) == zha.ZHA_ERR_ARG
+    assert call(V=24) == zha.ZHA_ERR_ALIGN
+    assert call(out=None) == zha.ZHA_ERR_NULL
+
+
+def test_bit_helpers_roundtrip():
+    import torch
+
+    m = torch.rand(3, 77) < 0.4
+    w = zha.pack_bits(m, 3)
+    assert w.dtype == torch.int32 and w.shape == (3, 3)
+    assert torch.equal(zha.unpack_bits(w, 77), m)

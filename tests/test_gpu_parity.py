@@ -1,0 +1,361 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle.
+
+Every input comes from the seeded generators; the oracle takes CPU copies of
+the very same tensors.  Tolerances: attention outputs within 1e-5 (fp32 K/V)
+or 1e-2 (bf16 K/V, fp32 accumulation) max abs error; selected sets identical
+up to ambiguous nodes (see tests/parity.py); tree fields as documented in
+each test.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.zha_oracle as O
+from tests import parity as PAR
+from tree_indexed_sparse_zha_amd import workloads as W
+from tree_indexed_sparse_zha_amd import zha
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm device")
+    zha.load()
+    torch.manual_seed(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def cfg_of(w: W.Workload, capacity=None, **kw) -> zha.ZhaConfig:
+    d = dict(
+        batch=w.batch, n_kv_heads=w.n_kv_heads, q_per_kv=w.q_per_kv, head_dim=w.head_dim, n_ref=w.n_ref,
+        chunk=w.chunk, levels=w.levels, dtype=w.dtype, capacity=capacity or w.n_tokens,
+    )
+    d.update(kw)
+    return zha.ZhaConfig(**d)
+
+
+def np64(t):
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def random_inputs(cfg: zha.ZhaConfig, T, seed=0, n_tokens=None):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    B, H, G, d = cfg.batch, cfg.n_kv_heads, cfg.q_per_kv, cfg.head_dim
+    cap = cfg.capacity
+    K = torch.randn(B, H, cap, d, generator=g, device="cuda").to(cfg.torch_dtype)
+    V = torch.randn(B, H, cap, d, generator=g, device="cuda").to(cfg.torch_dtype)
+    Q = torch.randn(B, H, G, T, d, generator=g, device="cuda").to(cfg.torch_dtype)
+    ref = (torch.randn(H, cfg.n_ref, d, generator=g, device="cuda") / math.sqrt(d)).to(cfg.torch_dtype).float()
+    return K, V, Q, ref
+
+
+def query_list(cfg, T):
+    return [(b, h, gq, t) for b in range(cfg.batch) for h in range(cfg.n_kv_heads) for gq in range(cfg.q_per_kv) for t in range(T)]
+
+
+# ---------------------------------------------------------------------------
+# attention over given chunk sets
+
+
+ATTEND_CASES = [
+    # name, cfg kwargs, T, n_tokens
+    ("f32-d64-C4", dict(batch=1, n_kv_heads=2, q_per_kv=3, head_dim=64, n_ref=4, chunk=4, levels=3, dtype="f32", capacity=5000), 2, 4999),
+    ("bf16-d128-C4", dict(batch=2, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=6, dtype="bf16", capacity=9000), 1, 8999),
+    ("bf16-d64-C256", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=64, n_ref=16, chunk=256, levels=1, dtype="bf16", capacity=4200), 3, 4133),
+    ("f32-d128-C8", dict(batch=1, n_kv_heads=1, q_per_kv=5, head_dim=128, n_ref=1, chunk=8, levels=4, dtype="f32", capacity=3000), 1, 2997),
+]
+
+
+@pytest.mark.parametrize("name,kw,T,N", ATTEND_CASES, ids=[c[0] for c in ATTEND_CASES])
+@pytest.mark.parametrize("flags", [zha.ZHA_SINK | zha.ZHA_LAST_CHUNK, 0, zha.ZHA_ALL_KEYS])
+def test_attend_matches_oracle(name, kw, T, N, flags):
+    _say(f"attend {name} flags={flags}")
+    cfg = zha.ZhaConfig(**kw)
+    K, V, Q, _ = random_inputs(cfg, T, seed=1)
+    nq = cfg.n_caches * cfg.q_per_kv * T
+    n_chunks = N // cfg.chunk
+    words = (n_chunks + 31) // 32 + 1
+    gsel = torch.Generator(device="cpu")
+    gsel.manual_seed(2)
+    density = torch.rand(nq, 1, generator=gsel) * 0.5
+    mask = torch.rand(nq, n_chunks, generator=gsel) < density
+    mask[0, :] = False  # one query with no routed chunk: only the forced keys
+    sel = zha.pack_bits(mask, words).cuda()
+    out = torch.full((nq, cfg.head_dim), float("nan"), device="cuda")
+    lse = torch.full((nq,), float("nan"), device="cuda")
+    ws = torch.empty(zha.attend_workspace_bytes(cfg, T), dtype=torch.uint8, device="cuda")
+    zha.attend(cfg, Q, T, K, V, N, sel, flags, out, lse, ws)
+    torch.cuda.synchronize()
+    out_c, lse_c = out.cpu().numpy(), lse.cpu().numpy()
+    tol = PAR.OUT_TOL[cfg.dtype]
+    for qi, (b, h, gq, t) in enumerate(query_list(cfg, T)):
+        Kn, Vn = np64(K[b, h, :N]), np64(V[b, h, :N])
+        q = np64(Q[b, h, gq, t])
+        if flags & zha.ZHA_ALL_KEYS:
+            idx = np.arange(N)
+        else:
+            chunks = np.nonzero(mask[qi].numpy())[0]
+            idx = O.attend_set(chunks, N, cfg.chunk, bool(flags & zha.ZHA_SINK), bool(flags & zha.ZHA_LAST_CHUNK))
+        if idx.size == 0:
+            assert np.all(out_c[qi] == 0) and np.isneginf(lse_c[qi])
+            continue
+        o, l = O.attend(q, Kn, Vn, idx)
+        np.testing.assert_allclose(out_c[qi], o, rtol=0, atol=tol, err_msg=f"query {qi}")
+        np.testing.assert_allclose(lse_c[qi], l, rtol=0, atol=tol, err_msg=f"query {qi}")
+
+
+# ---------------------------------------------------------------------------
+# tree build
+
+
+BUILD_CASES = [
+    ("tiny-f32", dict(batch=1, n_kv_heads=1, q_per_kv=1, head_dim=64, n_ref=4, chunk=4, levels=3, dtype="f32", capacity=4096), 4096),
+    ("deep-bf16-ragged", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=6, dtype="bf16", capacity=9000), 8192 + 4 * 37 + 2),
+    ("wide-bf16", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=256, levels=1, dtype="bf16", capacity=3000), 2560 + 100),
+    ("light-bf16", dict(batch=1, n_kv_heads=1, q_per_kv=4, head_dim=128, n_ref=1, chunk=8, levels=4, dtype="bf16", capacity=5000), 4096 + 8 * 5 + 3),
+    ("c32-f32-d64", dict(batch=1, n_kv_heads=1, q_per_kv=1, head_dim=64, n_ref=5, chunk=32, levels=2, dtype="f32", capacity=2200), 2048 + 70),
+    ("c1-f32", dict(batch=1, n_kv_heads=1, q_per_kv=1, head_dim=64, n_ref=3, chunk=1, levels=1, dtype="f32", capacity=300), 300),
+]
+
+
+def _segmented_keys(cfg, seed):
+    """Clustered keys (segments of 64) so that reference softmaxes are not flat."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    B, H, cap, d = cfg.batch, cfg.n_kv_heads, cfg.capacity, cfg.head_dim
+    mu = torch.randn(B, H, (cap + 63) // 64, d, generator=g, device="cuda")
+    idx = torch.arange(cap, device="cuda") // 64
+    K = mu[:, :, idx] + 0.5 * torch.randn(B, H, cap, d, generator=g, device="cuda")
+    ref = torch.randn(H, cfg.n_ref, d, generator=g, device="cuda")  # larger than N(0, I/d): sharper weights
+    return K.to(cfg.torch_dtype), ref.to(cfg.torch_dtype).float()
+
+
+def check_tree(cfg, tree, K, ref, N):
+    sizes = O.level_sizes(N, cfg.chunk, cfg.levels)
+    d = cfg.head_dim
+    for b in range(cfg.batch):
+        for h in range(cfg.n_kv_heads):
+            cache = b * cfg.n_kv_heads + h
+            Kn, rn = np64(K[b, h, :N]), np64(ref[h])
+            to = O.build_tree(Kn, rn, cfg.chunk, cfg.levels, cfg.dtype, n_tokens=N)
+            for lv in range(1, cfg.levels + 1):
+                n = sizes[lv - 1]
+                got = zha.read_level(cfg, tree, lv, n)
+                gg, gL, gc = np64(got["g"][cache]), np64(got["L"][cache]), np64(got["c"][cache])
+                lvl = to[lv - 1]
+                np.testing.assert_allclose(gL, lvl.L, rtol=1e-5, atol=3e-5, err_msg=f"L level {lv}")
+                # c is consistent with the GPU's own stored g ...
+                c_self = gL - np.einsum("nrd,rd->nr", gg, rn) / math.sqrt(d)
+                np.testing.assert_allclose(gc, c_self, rtol=0, atol=3e-5, err_msg=f"c/g level {lv}")
+                # ... and with the oracle's L given that g
+                c_or = lvl.L - np.einsum("nrd,rd->nr", gg, rn) / math.sqrt(d)
+                np.testing.assert_allclose(gc, c_or, rtol=1e-5, atol=5e-5, err_msg=f"c level {lv}")
+                if cfg.dtype == "f32":
+                    scale = np.abs(lvl.g).max() + 1e-30
+                    np.testing.assert_allclose(gg, lvl.g, rtol=0, atol=2e-6 * scale, err_msg=f"g level {lv}")
+                else:
+                    mism = gg != lvl.ghat
+                    frac = mism.mean() if mism.size else 0.0
+                    assert frac <= 1e-3, f"level {lv}: {frac:.2e} of bf16 g differ"
+                    if mism.any():
+                        # A mismatch is a rounding-boundary flip: the GPU's fp32 value and the
+                        # oracle's fp64 value round to neighbouring bf16 numbers.  Allowed: one
+                        # bf16 spacing at the value, plus the fp32 accumulation error of the
+                        # node row (relative 4e-6 of the row's largest element).
+                        row_scale = np.abs(lvl.g).max(axis=2, keepdims=True)
+                        row_scale = np.broadcast_to(row_scale, lvl.g.shape)[mism]
+                        spacing = np.maximum(np.abs(lvl.ghat[mism]), np.abs(gg[mism])) * 2.0**-7
+                        allowed = spacing + 4e-6 * row_scale
+                        dev = np.abs(gg[mism] - lvl.ghat[mism])
+                        bad = dev > allowed
+                        assert not bad.any(), (
+                            f"level {lv}: {int(bad.sum())} g flips beyond one spacing: gpu {gg[mism][bad][:5]} "
+                            f"oracle {lvl.ghat[mism][bad][:5]} exact {lvl.g[mism][bad][:5]}"
+                        )
+
+
+@pytest.mark.parametrize("name,kw,N", BUILD_CASES, ids=[c[0] for c in BUILD_CASES])
+def test_build_matches_oracle(name, kw, N):
+    _say(f"build {name}")
+    cfg = zha.ZhaConfig(**kw)
+    K, ref = _segmented_keys(cfg, 3)
+    tree = zha.alloc_tree(cfg)
+    zha.build(cfg, K, ref, tree, N)
+    torch.cuda.synchronize()
+    check_tree(cfg, tree, K, ref, N)
+
+
+@pytest.mark.parametrize("name,kw,N", BUILD_CASES[:5], ids=[c[0] for c in BUILD_CASES[:5]])
+def test_append_equals_build(name, kw, N):
+    _say(f"append {name}")
+    cfg = zha.ZhaConfig(**kw)
+    K, ref = _segmented_keys(cfg, 4)
+    fresh = zha.alloc_tree(cfg)
+    zha.build(cfg, K, ref, fresh, N)
+    grown = zha.alloc_tree(cfg)
+    grown.fill_(0x7F)
+    steps = [N // 3, 1, 2 * cfg.chunk + 1, 0, N // 4]
+    n = 0
+    zha.build(cfg, K, ref, grown, steps[0])
+    n = steps[0]
+    for s in steps[1:]:
+        zha.append(cfg, K, ref, grown, n, s)
+        n += s
+    zha.append(cfg, K, ref, grown, n, N - n)
+    torch.cuda.synchronize()
+    sizes = O.level_sizes(N, cfg.chunk, cfg.levels)
+    for lv in range(1, cfg.levels + 1):
+        a = zha.read_level(cfg, fresh, lv, sizes[lv - 1])
+        b = zha.read_level(cfg, grown, lv, sizes[lv - 1])
+        for f in ("g", "L", "c"):
+            ba = a[f].contiguous().view(torch.uint8)
+            bb = b[f].contiguous().view(torch.uint8)
+            assert torch.equal(ba, bb), f"{f} level {lv} differs between append and build"
+
+
+# ---------------------------------------------------------------------------
+# routing + attention end to end on the workloads
+
+
+def run_path(cfg, K, V, Q, ref, N, T, p, flags=zha.ZHA_SINK | zha.ZHA_LAST_CHUNK):
+    tree = zha.alloc_tree(cfg)
+    zha.build(cfg, K, ref, tree, N)
+    buf = zha.alloc_route(cfg, T)
+    zha.route(cfg, tree, N, Q, T, p, buf)
+    nq = int(buf.layout.n_queries)
+    out = torch.empty(nq, cfg.head_dim, device="cuda")
+    lse = torch.empty(nq, device="cuda")
+    ws = torch.empty(zha.attend_workspace_bytes(cfg, T), dtype=torch.uint8, device="cuda")
+    zha.attend(cfg, Q, T, K, V, N, zha.level1_sel(buf), flags, out, lse, ws)
+    torch.cuda.synchronize()
+    return tree, buf, out, lse
+
+
+def gpu_levels(cfg, buf, N, qi):
+    """Per level: kept bits [n_l] and score row [n_l] of query qi."""
+    rl = buf.layout
+    sizes = O.level_sizes(N, cfg.chunk, cfg.levels)
+    nq = int(rl.n_queries)
+    bits, scores = {}, {}
+    for lv in range(1, cfg.levels + 1):
+        i = lv - 1
+        w = int(rl.words[i])
+        words = buf.sel[int(rl.sel_offset[i]) + qi * w : int(rl.sel_offset[i]) + (qi + 1) * w]
+        bits[lv] = zha.unpack_bits(words.cpu(), sizes[i]).numpy()
+        cap = zha.tree_layout(cfg).node_cap[i]
+        off = int(rl.score_offset[i]) + qi * cap
+        scores[lv] = buf.score[off : off + sizes[i]].cpu().numpy()
+    return bits, scores
+
+
+ROUTE_WORKLOADS = [
+    ("tiny", None, None, 16),  # all queries of the tiny workload
+    ("deep32k", 2, None, 6),  # 2 of 8 caches, 6 sampled queries each
+    ("wide256k", 2, None, 4),
+]
+
+
+@pytest.mark.parametrize("wname,n_caches_checked,_unused,q_per_cache", ROUTE_WORKLOADS, ids=[r[0] for r in ROUTE_WORKLOADS])
+def test_route_and_attend_match_oracle(wname, n_caches_checked, _unused, q_per_cache):
+    w = W.WORKLOADS[wname]
+    _say(f"route {wname}")
+    cfg = cfg_of(w)
+    batch = W.make_batch(w, device="cuda")
+    N, T, p = w.n_tokens, w.queries_per_head, w.p[0]
+    tree, buf, out, lse = run_path(cfg, batch.K, batch.V, batch.Q, batch.ref, N, T, p)
+    tol = PAR.OUT_TOL[cfg.dtype]
+    QC = cfg.q_per_kv * T
+    caches = list(range(cfg.n_caches))
+    if n_caches_checked:
+        caches = [0, cfg.n_caches - 1][:n_caches_checked]
+    rng = np.random.default_rng(5)
+    out_c, lse_c = out.cpu().numpy(), lse.cpu().numpy()
+    n_same = 0
+    for cache in caches:
+        b, h = divmod(cache, cfg.n_kv_heads)
+        Kn, Vn, rn = np64(batch.K[b, h, :N]), np64(batch.V[b, h, :N]), np64(batch.ref[h])
+        to = O.build_tree(Kn, rn, cfg.chunk, cfg.levels, cfg.dtype, keep_g=False)
+        qis = list(range(QC)) if q_per_cache >= QC else sorted(rng.choice(QC, q_per_cache, replace=False).tolist())
+        for qi_local in qis:
+            gq, t = divmod(qi_local, T)
+            qi = cache * QC + qi_local
+            q = np64(batch.Q[b, h, gq, t])
+            bits, scores = gpu_levels(cfg, buf, N, qi)
+            kept = PAR.gpu_kept_from_bits(bits)
+            PAR.check_route_teacher_forced(q, to, rn, cfg.chunk, p, kept, cfg.dtype, scores)
+            # attention over the GPU's set (R21)
+            idx = O.attend_set(kept[1], N, cfg.chunk, True, True)
+            o, l = O.attend(q, Kn, Vn, idx)
+            np.testing.assert_allclose(out_c[qi], o, rtol=0, atol=tol)
+            np.testing.assert_allclose(lse_c[qi], l, rtol=0, atol=tol)
+            # end to end when the oracle's own routing reaches the same set
+            o2, l2, idx2, _ = O.route_and_attend(q, Kn, Vn, to, rn, cfg.chunk, p, N)
+            if np.array_equal(idx, idx2):
+                n_same += 1
+                np.testing.assert_allclose(out_c[qi], o2, rtol=0, atol=tol)
+    assert n_same >= 1
+
+
+def test_route_stats_consistent():
+    w = W.WORKLOADS["tiny"]
+    cfg = cfg_of(w)
+    batch = W.make_batch(w, device="cuda")
+    N, T, p = w.n_tokens, w.queries_per_head, w.p[0]
+    tree, buf, out, lse = run_path(cfg, batch.K, batch.V, batch.Q, batch.ref, N, T, p)
+    for lv in range(1, cfg.levels + 1):
+        recs = zha.stats_records(buf, lv)
+        for qi, r in enumerate(recs):
+            bits, scores = gpu_levels(cfg, buf, N, qi)
+            assert r.n_kept == int(bits[lv].sum())
+            assert r.n_cand == int(np.isfinite(scores[lv]).sum())
+            assert r.mass_kept >= math.ceil(p * r.mass_total) - 1
+            assert 1 <= r.n_kept <= r.n_cand
+
+
+def test_p1_is_dense():
+    w = W.WORKLOADS["tiny"]
+    cfg = cfg_of(w)
+    batch = W.make_batch(w, device="cuda")
+    N, T = w.n_tokens, w.queries_per_head
+    tree, buf, out, lse = run_path(cfg, batch.K, batch.V, batch.Q, batch.ref, N, T, 1.0)
+    sel1 = zha.unpack_bits(zha.level1_sel(buf).cpu(), N // cfg.chunk)
+    assert bool(sel1.all())
+    dense = torch.empty_like(out)
+    dl = torch.empty_like(lse)
+    ws = torch.empty(zha.attend_workspace_bytes(cfg, T), dtype=torch.uint8, device="cuda")
+    zha.dense_decode(cfg, batch.Q, T, batch.K, batch.V, N, dense, dl, ws)
+    torch.cuda.synchronize()
+    Kn, Vn = np64(batch.K[0, 0, :N]), np64(batch.V[0, 0, :N])
+    for t in range(T):
+        o, l = O.attend(np64(batch.Q[0, 0, 0, t]), Kn, Vn, np.arange(N))
+        np.testing.assert_allclose(out[t].cpu().numpy(), o, atol=1e-5, rtol=0)
+        np.testing.assert_allclose(dense[t].cpu().numpy(), o, atol=1e-5, rtol=0)
+
+
+def test_route_is_deterministic():
+    w = W.WORKLOADS["deep32k"]
+    cfg = cfg_of(w)
+    batch = W.make_batch(w, device="cuda")
+    N, T, p = w.n_tokens, w.queries_per_head, w.p[0]
+    tree, buf, out, lse = run_path(cfg, batch.K, batch.V, batch.Q, batch.ref, N, T, p)
+    sel0, sc0, st0, out0 = buf.sel.clone(), buf.score.clone(), buf.stats.clone(), out.clone()
+    zha.route(cfg, tree, N, batch.Q, T, p, buf)
+    ws = torch.empty(zha.attend_workspace_bytes(cfg, T), dtype=torch.uint8, device="cuda")
+    zha.attend(cfg, batch.Q, T, batch.K, batch.V, N, zha.level1_sel(buf), 3, out, lse, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(sel0, buf.sel)
+    assert torch.equal(sc0.nan_to_num(), buf.score.nan_to_num())
+    assert torch.equal(st0, buf.stats)
+    assert torch.equal(out0, out)

@@ -1,0 +1,416 @@
+// C-ABI entry points of the ZHA decode path: argument checks, layouts and
+// launch geometry.  Every check runs on the host before any HIP call.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "zha_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(ZHA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+int esize(int dtype) { return dtype == ZHA_BF16 ? 2 : 4; }
+
+int check_config(const zha_config* c) {
+  if (!c) return fail(ZHA_ERR_NULL, "cfg is NULL");
+  if (c->batch < 1 || c->n_kv_heads < 1 || c->q_per_kv < 1)
+    return fail(ZHA_ERR_ARG, "batch, n_kv_heads and q_per_kv must be >= 1");
+  if (c->head_dim < 1 || c->n_ref < 1 || c->chunk < 1 || c->levels < 1)
+    return fail(ZHA_ERR_ARG, "head_dim, n_ref, chunk and levels must be >= 1");
+  if (c->capacity_tokens < 1) return fail(ZHA_ERR_ARG, "capacity_tokens must be >= 1");
+  if (c->kv_dtype != ZHA_F32 && c->kv_dtype != ZHA_BF16)
+    return fail(ZHA_ERR_UNSUPPORTED, "kv_dtype %d unsupported", c->kv_dtype);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(ZHA_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", c->head_dim);
+  if (c->n_ref > 16) return fail(ZHA_ERR_UNSUPPORTED, "n_ref %d unsupported (1..16)", c->n_ref);
+  if (!is_pow2(c->chunk) || c->chunk > 256)
+    return fail(ZHA_ERR_UNSUPPORTED, "chunk %d unsupported (power of two <= 256)", c->chunk);
+  if (c->levels > ZHA_MAX_LEVELS)
+    return fail(ZHA_ERR_UNSUPPORTED, "levels %d unsupported (<= %d)", c->levels, ZHA_MAX_LEVELS);
+  int64_t span = 1;
+  for (int l = 0; l < c->levels; ++l) span *= c->chunk;
+  if (span > (int64_t(1) << 24))
+    return fail(ZHA_ERR_UNSUPPORTED, "chunk^levels = %lld exceeds 2^24", (long long)span);
+  if (c->chunk > 16 && c->levels > 4)
+    return fail(ZHA_ERR_UNSUPPORTED, "chunk > 16 supports at most 4 levels");
+  if (c->capacity_tokens > (int64_t(1) << 36)) return fail(ZHA_ERR_UNSUPPORTED, "capacity too large");
+  if ((int64_t)c->batch * c->n_kv_heads > 65535)
+    return fail(ZHA_ERR_UNSUPPORTED, "batch * n_kv_heads must be <= 65535");
+  return ZHA_OK;
+}
+
+int check_T(const zha_config* c, int32_t T) {
+  if (T < 1) return fail(ZHA_ERR_ARG, "T must be >= 1");
+  if ((int64_t)c->q_per_kv * T > 1024) return fail(ZHA_ERR_UNSUPPORTED, "q_per_kv * T must be <= 1024");
+  return ZHA_OK;
+}
+
+int check_ptr16(const void* p, const char* name) {
+  if (!p) return fail(ZHA_ERR_NULL, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p) % 16) return fail(ZHA_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return ZHA_OK;
+}
+
+int check_strides(const int64_t* s, int n, int es, const char* name) {
+  if (!s) return fail(ZHA_ERR_NULL, "%s is NULL", name);
+  for (int i = 0; i < n; ++i) {
+    if (s[i] < 0) return fail(ZHA_ERR_ARG, "%s[%d] is negative", name, i);
+    if ((s[i] * es) % 16) return fail(ZHA_ERR_ALIGN, "%s[%d] * element size is not a multiple of 16", name, i);
+  }
+  return ZHA_OK;
+}
+
+void fill_tree_layout(const zha_config* c, zha_tree_layout* out) {
+  std::memset(out, 0, sizeof(*out));
+  out->levels = c->levels;
+  const int64_t caches = (int64_t)c->batch * c->n_kv_heads;
+  out->g_node_bytes = (int64_t)c->n_ref * c->head_dim * esize(c->kv_dtype);
+  int64_t n = c->capacity_tokens / c->chunk;
+  int64_t off = 0;
+  for (int l = 0; l < c->levels; ++l) {
+    if (l > 0) n = cdiv(n, c->chunk);
+    out->node_cap[l] = n;
+    out->g_offset[l] = off;
+    off = align256(off + caches * n * out->g_node_bytes);
+    out->L_offset[l] = off;
+    off = align256(off + caches * n * c->n_ref * 4);
+    out->c_offset[l] = off;
+    off = align256(off + caches * n * c->n_ref * 4);
+  }
+  out->total_bytes = off > 0 ? off : 256;
+}
+
+void fill_geom(const zha_config* c, const zha_tree_layout& tl, zha::TreeGeom* g) {
+  std::memset(g, 0, sizeof(*g));
+  g->levels = c->levels;
+  g->R = c->n_ref;
+  g->D = c->head_dim;
+  g->C = c->chunk;
+  g->esize = esize(c->kv_dtype);
+  g->H = c->n_kv_heads;
+  g->caches = c->batch * c->n_kv_heads;
+  for (int l = 0; l < c->levels; ++l) {
+    g->node_cap[l] = tl.node_cap[l];
+    g->g_off[l] = tl.g_offset[l];
+    g->L_off[l] = tl.L_offset[l];
+    g->c_off[l] = tl.c_offset[l];
+  }
+  g->span_len[0] = 1;
+  for (int l = 1; l <= c->levels; ++l) g->span_len[l] = g->span_len[l - 1] * c->chunk;
+}
+
+// node counts per level for n tokens
+void level_sizes(const zha_config* c, int64_t n_tokens, int64_t* n) {
+  n[0] = n_tokens / c->chunk;
+  for (int l = 1; l < c->levels; ++l) n[l] = cdiv(n[l - 1], c->chunk);
+}
+
+// Keys per attention workgroup, fixed per configuration (from the capacity) so
+// that the workspace bound holds for every n_tokens: tiles of >= 256 keys and
+// enough workgroups to fill 256 CUs several times at full capacity.
+int64_t attend_tile_keys(const zha_config* c, int32_t T) {
+  const int64_t caches = (int64_t)c->batch * c->n_kv_heads;
+  const int64_t groups = cdiv((int64_t)c->q_per_kv * T, 4);
+  int64_t tk = 256;
+  while (tk < 8192 && caches * groups * cdiv(c->capacity_tokens, tk * 2) >= 2048) tk *= 2;
+  return tk;
+}
+
+int64_t attend_ws(const zha_config* c, int32_t T) {
+  const int64_t nq = (int64_t)c->batch * c->n_kv_heads * c->q_per_kv * T;
+  const int64_t tk = attend_tile_keys(c, T);
+  return align256(nq * cdiv(c->capacity_tokens, tk) * (c->head_dim + 2) * 4);
+}
+
+int check_prof(zha_profile* prof) {
+  if (!prof) return ZHA_OK;
+  if (prof->n_pairs < 0 || prof->n_pairs > ZHA_PROFILE_MAX)
+    return fail(ZHA_ERR_ARG, "prof->n_pairs must be in [0, %d]", ZHA_PROFILE_MAX);
+  for (int i = 0; i < 2 * prof->n_pairs; ++i)
+    if (!prof->events[i]) return fail(ZHA_ERR_NULL, "prof->events[%d] is NULL", i);
+  return ZHA_OK;
+}
+
+int do_build(const zha_config* cfg, const void* K, const int64_t* ks, int64_t n_old, int64_t n_new,
+             const float* ref, void* tree, zha_profile* prof, void* stream, bool append) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if ((rc = check_prof(prof))) return rc;
+  if (prof) prof->n_used = 0;
+  if ((rc = check_ptr16(K, "K"))) return rc;
+  if ((rc = check_strides(ks, 3, esize(cfg->kv_dtype), "k_strides"))) return rc;
+  if ((rc = check_ptr16(ref, "ref"))) return rc;
+  if ((rc = check_ptr16(tree, "tree"))) return rc;
+  if (n_old < 0 || n_new < 0) return fail(ZHA_ERR_ARG, "token counts must be >= 0");
+  if (n_old + n_new > cfg->capacity_tokens)
+    return fail(ZHA_ERR_CAPACITY, "%lld tokens exceed capacity %lld", (long long)(n_old + n_new),
+                (long long)cfg->capacity_tokens);
+  zha_tree_layout tl;
+  fill_tree_layout(cfg, &tl);
+  zha::BuildArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.K = K;
+  a.sb = ks[0];
+  a.sh = ks[1];
+  a.st = ks[2];
+  a.ref = ref;
+  a.tree = static_cast<char*>(tree);
+  fill_geom(cfg, tl, &a.geo);
+  a.n_tokens = n_old + n_new;
+  a.span_tokens = a.geo.span_len[cfg->levels];
+  a.inv_sqrt_d = 1.0f / std::sqrt((float)cfg->head_dim);
+  const int64_t C = cfg->chunk;
+  const int64_t end_c = ((n_old + n_new) / C) * C;  // complete-chunk boundary after the call
+  if (append) {
+    const int64_t old_c = (n_old / C) * C;
+    if (end_c <= old_c) return ZHA_OK;  // no new complete chunk: the tree is unchanged
+    a.first_span = old_c / a.span_tokens;
+    a.n_spans = cdiv(end_c, a.span_tokens) - a.first_span;
+  } else {
+    a.first_span = 0;
+    a.n_spans = cdiv(end_c, a.span_tokens);
+  }
+  if (a.n_spans <= 0) return ZHA_OK;
+  if (a.n_spans > 0x7fffffffll) return fail(ZHA_ERR_UNSUPPORTED, "too many spans");
+  zha::Prof pr{prof, static_cast<hipStream_t>(stream)};
+  hipError_t e = zha::launch_build(a, cfg->kv_dtype, pr);
+  if (e != hipSuccess) return hip_fail(e, "build launch");
+  return ZHA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int zha_version(void) { return ZHA_VERSION; }
+
+const char* zha_status_string(int s) {
+  switch (s) {
+    case ZHA_OK:
+      return "ok";
+    case ZHA_ERR_NULL:
+      return "null pointer";
+    case ZHA_ERR_ARG:
+      return "invalid argument";
+    case ZHA_ERR_UNSUPPORTED:
+      return "unsupported configuration";
+    case ZHA_ERR_CAPACITY:
+      return "capacity exceeded or buffer too small";
+    case ZHA_ERR_ALIGN:
+      return "misaligned pointer or stride";
+    case ZHA_ERR_HIP:
+      return "HIP error";
+    default:
+      return "unknown status";
+  }
+}
+
+const char* zha_last_error(void) { return g_err; }
+
+int zha_get_tree_layout(const zha_config* cfg, zha_tree_layout* out) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!out) return fail(ZHA_ERR_NULL, "out is NULL");
+  fill_tree_layout(cfg, out);
+  return ZHA_OK;
+}
+
+int zha_get_route_layout(const zha_config* cfg, int32_t T, zha_route_layout* out) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if ((rc = check_T(cfg, T))) return rc;
+  if (!out) return fail(ZHA_ERR_NULL, "out is NULL");
+  zha_tree_layout tl;
+  fill_tree_layout(cfg, &tl);
+  std::memset(out, 0, sizeof(*out));
+  out->levels = cfg->levels;
+  out->n_queries = (int64_t)cfg->batch * cfg->n_kv_heads * cfg->q_per_kv * T;
+  int64_t sw = 0, sf = 0, ss = 0;
+  for (int l = 0; l < cfg->levels; ++l) {
+    out->words[l] = cdiv(tl.node_cap[l], 32);
+    out->sel_offset[l] = sw;
+    sw += out->n_queries * out->words[l];
+    out->score_offset[l] = sf;
+    sf += out->n_queries * tl.node_cap[l];
+    out->stats_offset[l] = ss;
+    ss += out->n_queries;
+  }
+  out->sel_words_total = sw > 0 ? sw : 1;
+  out->score_floats_total = sf > 0 ? sf : 1;
+  out->stats_total = ss;
+  out->workspace_bytes = 0;
+  return ZHA_OK;
+}
+
+int64_t zha_attend_workspace_bytes(const zha_config* cfg, int32_t T) {
+  if (check_config(cfg) || check_T(cfg, T)) return -1;
+  return attend_ws(cfg, T);
+}
+
+int zha_build(const zha_config* cfg, const void* K, const int64_t k_strides[3], int64_t n_tokens,
+              const float* ref, void* tree, zha_profile* prof, void* stream) {
+  return do_build(cfg, K, k_strides, 0, n_tokens, ref, tree, prof, stream, false);
+}
+
+int zha_append(const zha_config* cfg, const void* K, const int64_t k_strides[3], int64_t n_old,
+               int64_t n_new, const float* ref, void* tree, zha_profile* prof, void* stream) {
+  return do_build(cfg, K, k_strides, n_old, n_new, ref, tree, prof, stream, true);
+}
+
+int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const void* Q,
+              const int64_t q_strides[4], int32_t T, float p, uint32_t* sel, float* score,
+              zha_select_stats* stats, void* ws, int64_t ws_bytes, zha_profile* prof, void* stream) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if ((rc = check_prof(prof))) return rc;
+  if ((rc = check_T(cfg, T))) return rc;
+  if ((rc = check_ptr16(tree, "tree"))) return rc;
+  if ((rc = check_ptr16(Q, "Q"))) return rc;
+  if ((rc = check_strides(q_strides, 4, esize(cfg->kv_dtype), "q_strides"))) return rc;
+  if ((rc = check_ptr16(sel, "sel"))) return rc;
+  if ((rc = check_ptr16(score, "score"))) return rc;
+  if ((rc = check_ptr16(stats, "stats"))) return rc;
+  if (!(p > 0.0f) || std::isnan(p)) return fail(ZHA_ERR_ARG, "p must be in (0, 1]");
+  if (n_tokens < 0) return fail(ZHA_ERR_ARG, "n_tokens must be >= 0");
+  if (n_tokens > cfg->capacity_tokens) return fail(ZHA_ERR_CAPACITY, "n_tokens exceeds capacity");
+  zha_route_layout rl;
+  zha_get_route_layout(cfg, T, &rl);
+  if (ws_bytes < rl.workspace_bytes) return fail(ZHA_ERR_CAPACITY, "workspace too small");
+  zha_tree_layout tl;
+  fill_tree_layout(cfg, &tl);
+  int64_t n[ZHA_MAX_LEVELS];
+  level_sizes(cfg, n_tokens, n);
+  const int caches = cfg->batch * cfg->n_kv_heads;
+  const float isd = 1.0f / std::sqrt((float)cfg->head_dim);
+  if (prof) prof->n_used = 0;
+  zha::Prof pr{prof, static_cast<hipStream_t>(stream)};
+  for (int l = cfg->levels - 1; l >= 0; --l) {
+    zha::ScoreArgs sa;
+    std::memset(&sa, 0, sizeof(sa));
+    sa.g = static_cast<const char*>(tree) + tl.g_offset[l];
+    sa.c = reinterpret_cast<const float*>(static_cast<const char*>(tree) + tl.c_offset[l]);
+    sa.node_cap = tl.node_cap[l];
+    sa.n_nodes = n[l];
+    sa.R = cfg->n_ref;
+    sa.C = cfg->chunk;
+    sa.D = cfg->head_dim;
+    sa.H = cfg->n_kv_heads;
+    sa.G = cfg->q_per_kv;
+    sa.T = T;
+    sa.QC = cfg->q_per_kv * T;
+    sa.Q = Q;
+    sa.qsb = q_strides[0];
+    sa.qsh = q_strides[1];
+    sa.qsg = q_strides[2];
+    sa.qst = q_strides[3];
+    sa.sel_parent = (l == cfg->levels - 1) ? nullptr : sel + rl.sel_offset[l + 1];
+    sa.parent_words = (l == cfg->levels - 1) ? 0 : rl.words[l + 1];
+    sa.score = score + rl.score_offset[l];
+    sa.inv_sqrt_d = isd;
+    zha::SelectArgs se;
+    std::memset(&se, 0, sizeof(se));
+    se.score = sa.score;
+    se.node_cap = tl.node_cap[l];
+    se.n_nodes = n[l];
+    se.sel = sel + rl.sel_offset[l];
+    se.words = rl.words[l];
+    se.stats = stats + rl.stats_offset[l];
+    se.p = p;
+    se.keep_all = p >= 1.0f;
+    hipError_t e = zha::launch_route_level(sa, se, cfg->kv_dtype, caches, l + 1, pr);
+    if (e != hipSuccess) return hip_fail(e, "route launch");
+  }
+  return ZHA_OK;
+}
+
+int zha_attend(const zha_config* cfg, const void* Q, const int64_t q_strides[4], int32_t T,
+               const void* K, const void* V, const int64_t kv_strides[3], int64_t n_tokens,
+               const uint32_t* sel1, int64_t sel1_words, uint32_t flags, float* out, float* lse,
+               void* ws, int64_t ws_bytes, zha_profile* prof, void* stream) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if ((rc = check_prof(prof))) return rc;
+  if ((rc = check_T(cfg, T))) return rc;
+  const int es = esize(cfg->kv_dtype);
+  if ((rc = check_ptr16(Q, "Q"))) return rc;
+  if ((rc = check_strides(q_strides, 4, es, "q_strides"))) return rc;
+  if ((rc = check_ptr16(K, "K"))) return rc;
+  if ((rc = check_ptr16(V, "V"))) return rc;
+  if ((rc = check_strides(kv_strides, 3, es, "kv_strides"))) return rc;
+  if ((rc = check_ptr16(out, "out"))) return rc;
+  if ((rc = check_ptr16(ws, "ws"))) return rc;
+  if (flags & ~7u) return fail(ZHA_ERR_ARG, "unknown flags 0x%x", flags);
+  if (n_tokens < 1) return fail(ZHA_ERR_ARG, "n_tokens must be >= 1");
+  if (n_tokens > cfg->capacity_tokens) return fail(ZHA_ERR_CAPACITY, "n_tokens exceeds capacity");
+  const int64_t n_chunks = n_tokens / cfg->chunk;
+  if (!(flags & ZHA_ALL_KEYS)) {
+    if (!sel1) return fail(ZHA_ERR_NULL, "sel1 is NULL");
+    if (sel1_words < cdiv(n_chunks, 32)) return fail(ZHA_ERR_CAPACITY, "sel1_words too small");
+  }
+  const int64_t need = attend_ws(cfg, T);
+  if (ws_bytes < need)
+    return fail(ZHA_ERR_CAPACITY, "workspace %lld < %lld bytes", (long long)ws_bytes, (long long)need);
+  zha::AttendArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.Q = Q;
+  a.qsb = q_strides[0];
+  a.qsh = q_strides[1];
+  a.qsg = q_strides[2];
+  a.qst = q_strides[3];
+  a.K = K;
+  a.V = V;
+  a.sb = kv_strides[0];
+  a.sh = kv_strides[1];
+  a.st = kv_strides[2];
+  a.H = cfg->n_kv_heads;
+  a.G = cfg->q_per_kv;
+  a.T = T;
+  a.QC = cfg->q_per_kv * T;
+  a.C = cfg->chunk;
+  a.D = cfg->head_dim;
+  a.n_tokens = n_tokens;
+  a.n_chunks = n_chunks;
+  a.sel1 = (flags & ZHA_ALL_KEYS) ? nullptr : sel1;
+  a.sel_words = sel1_words;
+  a.flags = flags;
+  a.tile_keys = attend_tile_keys(cfg, T);
+  a.n_tiles = cdiv(n_tokens, a.tile_keys);
+  a.partial = static_cast<float*>(ws);
+  a.out = out;
+  a.lse = lse;
+  a.inv_sqrt_d = 1.0f / std::sqrt((float)cfg->head_dim);
+  if (prof) prof->n_used = 0;
+  zha::Prof pr{prof, static_cast<hipStream_t>(stream)};
+  hipError_t e = zha::launch_attend(a, cfg->kv_dtype, cfg->batch * cfg->n_kv_heads, pr);
+  if (e != hipSuccess) return hip_fail(e, "attend launch");
+  return ZHA_OK;
+}
+
+int zha_dense_decode(const zha_config* cfg, const void* Q, const int64_t q_strides[4], int32_t T,
+                     const void* K, const void* V, const int64_t kv_strides[3], int64_t n_tokens,
+                     float* out, float* lse, void* ws, int64_t ws_bytes, zha_profile* prof,
+                     void* stream) {
+  return zha_attend(cfg, Q, q_strides, T, K, V, kv_strides, n_tokens, nullptr, 0, ZHA_ALL_KEYS, out,
+                    lse, ws, ws_bytes, prof, stream);
+}
+
+}  // extern "C"

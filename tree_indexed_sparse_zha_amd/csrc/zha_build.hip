@@ -1,0 +1,300 @@
+// Tree build for ZHA (levels 1..Lv) on gfx950.
+//
+// Defines (MTP = "Zyphra AI Introduces Zyphra Hierarchical Attention (ZHA):
+// A Path to True Subquadratic Attention", section "Building the tree"):
+// contiguous chunks of C keys are summarised per reference query r_j by
+//   L_j = logsumexp_i z_ji,  g_j = sum_i softmax_i(z_j) k_i,  z_ji = r_j.k_i/sqrt(d),
+// and summaries are merged level by level,
+//   L_j(P) = logsumexp_c L_j(c),  g_j(P) = sum_c exp(L_j(c) - L_j(P)) g_j(c).
+// Stored: g rounded once to the KV dtype, L, and c_j = L_j - r_j.g_j/sqrt(d)
+// with the rounded g.
+//
+// Design.  One 64-lane wave owns one top span (C^Lv tokens) of one cache and
+// streams it in blocks of 16 keys.  Lane (j = lane % 16, dg = lane / 16) owns
+// reference query j and a quarter of the head dimension (the 16-byte pieces
+// dg, dg+4, dg+8, ... of a row), so all merges of g are lane-local fp32
+// arithmetic and only the two dot products over d (r.k on MFMA, r.g for c)
+// cross lanes.  Open nodes of every level above the leaves are kept as fp32
+// flash-style accumulators (running max, mass, weighted sum) in registers;
+// a node is written once, when its last child arrives, in the d-interleaved
+// layout the routing MFMA reads directly (one coalesced 1 KiB store per
+// 16-byte piece group).  Since a wave rebuilds whole top spans and nothing
+// else, a rebuild of the spans touched by appended tokens reproduces a fresh
+// build bit for bit.
+#include "zha_device.h"
+#include "zha_internal.h"
+
+namespace zha {
+namespace {
+
+constexpr int kKeysPerBlock = 16;
+
+__device__ __forceinline__ void absorb(float& am, float& as, float* aacc, bool& used, float mc,
+                                       float sc, const float* gc, int nv) {
+  // Fold a child with mass sc*exp(mc) and mass-weighted key sum gc*exp(mc)
+  // into an open node.
+  if (!used) {
+    am = mc;
+    as = sc;
+    for (int v = 0; v < nv; ++v) aacc[v] = gc[v];
+    used = true;
+    return;
+  }
+  const float mn = fmaxf(am, mc);
+  const float fa = __expf(am - mn), fc = __expf(mc - mn);
+  as = as * fa + sc * fc;
+  for (int v = 0; v < nv; ++v) aacc[v] = aacc[v] * fa + gc[v] * fc;
+  am = mn;
+}
+
+template <typename T, int D, int NA, bool LEAF_ACC>
+__global__ __launch_bounds__(64) void k_build_span(BuildArgs A) {
+  constexpr int E = Elem<T>::per16;
+  constexpr int PIECES = D / E;
+  constexpr int NS = PIECES / 4;  // 16-byte pieces per lane
+  constexpr int NV = NS * E;      // fp32 values per lane = D / 4
+  constexpr int KB = kKeysPerBlock;
+  constexpr int NAR = NA > 0 ? NA : 1;
+
+  const int lane = threadIdx.x;
+  const int j = lane & 15, dg = lane >> 4;
+  const TreeGeom& geo = A.geo;
+  const int R = geo.R, C = geo.C;
+  const int cache = blockIdx.y;
+  const int b = cache / geo.H, h = cache % geo.H;
+  const int64_t span = A.first_span + blockIdx.x;
+  const int64_t ncomplete = (A.n_tokens / C) * C;
+  const int64_t t0 = span * A.span_tokens;
+  const int64_t t1 = min(t0 + A.span_tokens, ncomplete);
+  if (t0 >= t1) return;
+  const float isd = A.inv_sqrt_d;
+
+  // reference query j, this lane's quarter of d
+  float rj[NV];
+  {
+    const float* rp = A.ref + ((int64_t)h * R + (j < R ? j : 0)) * D;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int e = 0; e < E; ++e) rj[s * E + e] = (j < R) ? rp[(4 * s + dg) * E + e] : 0.f;
+  }
+
+  __shared__ uint4 Ks[KB * PIECES];
+  __shared__ float zs[16][KB + 1];
+
+  const T* Kc = reinterpret_cast<const T*>(A.K) + (int64_t)b * A.sb + (int64_t)h * A.sh;
+
+  // open nodes above the leaves (or of the leaves themselves when C > 16)
+  float am[NAR], as[NAR], aacc[NAR][NV];
+  bool used[NAR];
+#pragma unroll
+  for (int a = 0; a < NAR; ++a) used[a] = false;
+
+  auto emit = [&](int lvl, int64_t node, float L, const float* g) {
+    float gr[NV];
+    uint4 pk[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) pk[s] = pack(&g[s * E], &gr[s * E], T());
+    float dot = 0.f;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) dot += rj[v] * gr[v];
+    dot += __shfl_xor(dot, 16);
+    dot += __shfl_xor(dot, 32);
+    const float c = L - dot * isd;
+    const int64_t nidx = (int64_t)cache * geo.node_cap[lvl - 1] + node;
+    if (j < R) {
+      char* gb = A.tree + geo.g_off[lvl - 1] + nidx * ((int64_t)R * D * Elem<T>::size);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) st16(gb + ((int64_t)(s * 4 + dg) * R + j) * 16, pk[s]);
+      if (dg == 0) {
+        reinterpret_cast<float*>(A.tree + geo.L_off[lvl - 1])[nidx * R + j] = L;
+        reinterpret_cast<float*>(A.tree + geo.c_off[lvl - 1])[nidx * R + j] = c;
+      }
+    }
+  };
+
+  auto load_block = [&](int64_t pos, int nk, uint4* regs) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int pi = lane + 64 * u;
+      const int key = pi / PIECES, pc = pi % PIECES;
+      regs[u] = key < nk ? ld16(Kc + (pos + key) * A.st + pc * E) : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  // bf16: reference rows as MFMA A operands (exact: ref holds bf16 values)
+  bf16x8 afr[NS];
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      float rr[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rr[e] = rj[s * 8 + e];
+      float dummy[8];
+      afr[s] = as_bf16x8(pack(rr, dummy, bf16_t()));
+    }
+  }
+
+  uint4 pre[NS];
+  int64_t pos = t0;
+  int nk = (int)min<int64_t>(KB, t1 - pos);
+  load_block(pos, nk, pre);
+  const int seg = C < KB ? C : KB;
+
+  while (pos < t1) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) Ks[lane + 64 * u] = pre[u];
+    __syncthreads();
+    const int64_t npos = pos + nk;
+    const int nnk = (int)min<int64_t>(KB, t1 - npos);
+    if (npos < t1) load_block(npos, nnk, pre);
+
+    // z[j][i] = r_j . k_i / sqrt(d) for the 16 keys of the block
+    if constexpr (sizeof(T) == 2) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const uint4 kb = Ks[(lane & 15) * PIECES + 4 * s + (lane >> 4)];
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[s], as_bf16x8(kb), acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zs[4 * (lane >> 4) + i][lane & 15] = acc[i] * isd;
+    } else {
+      for (int i = 0; i < KB; ++i) {
+        float part = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          float kv[E];
+          unpack(Ks[i * PIECES + 4 * s + dg], kv, T());
+#pragma unroll
+          for (int e = 0; e < E; ++e) part += rj[s * E + e] * kv[e];
+        }
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+        if (dg == 0) zs[j][i] = part * isd;
+      }
+    }
+    __syncthreads();
+
+    // leaf segments of this block: seg keys each (a whole leaf when C <= 16)
+    for (int sg = 0; sg < nk; sg += seg) {
+      float m = kNegInf;
+      for (int i = 0; i < seg; ++i) m = fmaxf(m, zs[j][sg + i]);
+      float ssum = 0.f;
+      float acc[NV];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) acc[v] = 0.f;
+      for (int i = 0; i < seg; ++i) {
+        const float e = __expf(zs[j][sg + i] - m);
+        ssum += e;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          float kv[E];
+          unpack(Ks[(sg + i) * PIECES + 4 * s + dg], kv, T());
+#pragma unroll
+          for (int x = 0; x < E; ++x) acc[s * E + x] += e * kv[x];
+        }
+      }
+      if constexpr (!LEAF_ACC) {
+        const float L = m + __logf(ssum);
+        const float inv = 1.f / ssum;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[v] *= inv;
+        emit(1, (pos + sg) / C, L, acc);
+        if constexpr (NA > 0) absorb(am[0], as[0], aacc[0], used[0], L, 1.f, acc, NV);
+      } else {
+        absorb(am[0], as[0], aacc[0], used[0], m, ssum, acc, NV);
+      }
+      // close every node whose span ends after this segment, bottom-up
+      // (with C < 16 several levels can close inside one block)
+      const int64_t end = pos + sg + seg;
+      const int64_t rel = end - t0;
+#pragma unroll
+      for (int a = 0; a < NA; ++a) {
+        const int lvl = a + (LEAF_ACC ? 1 : 2);
+        const int64_t sp = geo.span_len[lvl];
+        if (used[a] && (rel % sp) == 0) {
+          const float L = am[a] + __logf(as[a]);
+          const float inv = 1.f / as[a];
+          float g[NV];
+#pragma unroll
+          for (int v = 0; v < NV; ++v) g[v] = aacc[a][v] * inv;
+          emit(lvl, (end - sp) / sp, L, g);
+          if (a + 1 < NA) absorb(am[a + 1], as[a + 1], aacc[a + 1], used[a + 1], L, 1.f, g, NV);
+          used[a] = false;
+        }
+      }
+    }
+    pos = npos;
+    nk = nnk;
+    __syncthreads();
+  }
+
+  // end of the data inside this span: close the partial nodes, bottom-up
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
+    const int lvl = a + (LEAF_ACC ? 1 : 2);
+    const int64_t sp = geo.span_len[lvl];
+    if (used[a]) {
+      const float L = am[a] + __logf(as[a]);
+      const float inv = 1.f / as[a];
+      float g[NV];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) g[v] = aacc[a][v] * inv;
+      emit(lvl, (pos - 1) / sp, L, g);
+      if (a + 1 < NA) absorb(am[a + 1], as[a + 1], aacc[a + 1], used[a + 1], L, 1.f, g, NV);
+      used[a] = false;
+    }
+  }
+}
+
+#define ZHA_CASE(LEAF, N)                                                            \
+  case N:                                                                            \
+    hipLaunchKernelGGL((k_build_span<T, D, N, LEAF>), grid, dim3(64), 0, s, a);      \
+    return hipGetLastError();
+
+template <typename T, int D>
+hipError_t dispatch_leaf(const BuildArgs& a, dim3 grid, hipStream_t s) {
+  if (a.geo.C > kKeysPerBlock) {
+    // leaves span several blocks: an open node per level, leaves included
+    switch (a.geo.levels) {
+      ZHA_CASE(true, 1)
+      ZHA_CASE(true, 2)
+      ZHA_CASE(true, 3)
+      ZHA_CASE(true, 4)
+      default:
+        return hipErrorInvalidValue;
+    }
+  }
+  switch (a.geo.levels - 1) {
+    ZHA_CASE(false, 0)
+    ZHA_CASE(false, 1)
+    ZHA_CASE(false, 2)
+    ZHA_CASE(false, 3)
+    ZHA_CASE(false, 4)
+    ZHA_CASE(false, 5)
+    ZHA_CASE(false, 6)
+    ZHA_CASE(false, 7)
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+#undef ZHA_CASE
+
+}  // namespace
+
+hipError_t launch_build(const BuildArgs& a, int dtype, Prof& prof) {
+  if (a.n_spans <= 0 || a.geo.caches <= 0) return hipSuccess;
+  dim3 grid((unsigned)a.n_spans, (unsigned)a.geo.caches);
+  hipStream_t s = prof.s;
+  hipError_t e;
+  prof.begin(ZHA_K_BUILD, 0);
+  if (dtype == 1)
+    e = a.geo.D == 128 ? dispatch_leaf<bf16_t, 128>(a, grid, s) : dispatch_leaf<bf16_t, 64>(a, grid, s);
+  else
+    e = a.geo.D == 128 ? dispatch_leaf<float, 128>(a, grid, s) : dispatch_leaf<float, 64>(a, grid, s);
+  prof.end();
+  return e;
+}
+
+}  // namespace zha

@@ -1,0 +1,99 @@
+// Device helpers shared by the ZHA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace zha {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+struct bf16_t {
+  uint16_t bits;
+};
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+  static constexpr int size = 4;
+  static constexpr int per16 = 4;  // elements per 16-byte piece
+};
+template <>
+struct Elem<bf16_t> {
+  static constexpr int size = 2;
+  static constexpr int per16 = 8;
+};
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// Unpack one 16-byte piece into fp32 values.
+__device__ __forceinline__ void unpack(const uint4& v, float* out, bf16_t) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void unpack(const uint4& v, float* out, float) {
+  out[0] = __uint_as_float(v.x);
+  out[1] = __uint_as_float(v.y);
+  out[2] = __uint_as_float(v.z);
+  out[3] = __uint_as_float(v.w);
+}
+
+// Round fp32 to bf16 (round to nearest even, hardware conversion).
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  __bf16 b = (__bf16)x;
+  return (uint32_t)__builtin_bit_cast(uint16_t, b);
+}
+
+// Pack fp32 values of one piece, rounding to the storage type; also returns
+// the rounded values as fp32 in `rounded`.
+__device__ __forceinline__ uint4 pack(const float* x, float* rounded, bf16_t) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t lo = bf16_bits(x[2 * i]), hi = bf16_bits(x[2 * i + 1]);
+    w[i] = lo | (hi << 16);
+    rounded[2 * i] = __uint_as_float(lo << 16);
+    rounded[2 * i + 1] = __uint_as_float(hi << 16);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+__device__ __forceinline__ uint4 pack(const float* x, float* rounded, float) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rounded[i] = x[i];
+  return make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                    __float_as_uint(x[3]));
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Monotone map of a float to uint32: larger float -> larger key (-inf lowest
+// of the non-NaN values).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int from, int to) {
+  for (int o = from; o < to; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_xor(float v, int from, int to) {
+  for (int o = from; o < to; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+}  // namespace zha

@@ -1,0 +1,111 @@
+// Internal launch interface between the C-ABI layer (zha_api.cpp) and the
+// HIP kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/zha.h"
+
+namespace zha {
+
+// Records the caller's timing events around each kernel launch (zha_profile).
+struct Prof {
+  zha_profile* p;
+  hipStream_t s;
+  void begin(int id, int level) {
+    if (p && p->n_used < p->n_pairs) {
+      hipEventRecord(static_cast<hipEvent_t>(p->events[2 * p->n_used]), s);
+      p->kernel[p->n_used] = id * 16 + level;
+    }
+  }
+  void end() {
+    if (!p) return;
+    if (p->n_used < p->n_pairs) hipEventRecord(static_cast<hipEvent_t>(p->events[2 * p->n_used + 1]), s);
+    ++p->n_used;
+  }
+};
+
+constexpr int kMaxLevels = 8;
+
+// Tree geometry for one call.  Offsets are bytes from the tree base.
+struct TreeGeom {
+  int levels;
+  int R;
+  int D;
+  int C;
+  int esize;  // bytes per K/V/g element (2 = bf16, 4 = fp32)
+  int H;
+  int caches;
+  int64_t node_cap[kMaxLevels];
+  int64_t g_off[kMaxLevels];
+  int64_t L_off[kMaxLevels];
+  int64_t c_off[kMaxLevels];
+  int64_t span_len[kMaxLevels + 1];  // span_len[l] = C^l tokens covered by a level-l node
+};
+
+struct BuildArgs {
+  const void* K;
+  int64_t sb, sh, st;  // K strides in elements (batch, head, token)
+  const float* ref;    // [H][R][D]
+  char* tree;
+  TreeGeom geo;
+  int64_t n_tokens;    // tree is built for this many tokens
+  int64_t first_span;  // first top span to rebuild
+  int64_t n_spans;     // number of spans to rebuild
+  int64_t span_tokens; // tokens per top span = C^levels
+  float inv_sqrt_d;
+};
+
+struct ScoreArgs {
+  const char* g;         // level base of g
+  const float* c;        // level base of c
+  int64_t node_cap;      // nodes per cache at this level
+  int64_t n_nodes;       // valid nodes per cache at this level
+  int R, C, D, H, G, T, QC;  // QC = G * T queries per cache
+  const void* Q;
+  int64_t qsb, qsh, qsg, qst;
+  const uint32_t* sel_parent;  // parent level bitsets or nullptr (top level)
+  int64_t parent_words;        // words per query row of sel_parent
+  float* score;                // [n_queries][node_cap] for this level
+  float inv_sqrt_d;
+};
+
+struct SelectArgs {
+  const float* score;  // [n_queries][node_cap]
+  int64_t node_cap;
+  int64_t n_nodes;
+  uint32_t* sel;       // [n_queries][words]
+  int64_t words;
+  void* stats;         // zha_select_stats[n_queries]
+  float p;
+  int keep_all;
+};
+
+struct AttendArgs {
+  const void* Q;
+  int64_t qsb, qsh, qsg, qst;
+  const void* K;
+  const void* V;
+  int64_t sb, sh, st;
+  int H, G, T, QC, C, D;
+  int64_t n_tokens;
+  int64_t n_chunks;  // floor(n_tokens / C): chunks that can carry a selection bit
+  const uint32_t* sel1;
+  int64_t sel_words;
+  uint32_t flags;
+  int64_t tile_keys;  // keys per workgroup
+  int64_t n_tiles;
+  float* partial;     // [n_queries][n_tiles][D + 2]
+  float* out;
+  float* lse;
+  float inv_sqrt_d;
+};
+
+hipError_t launch_build(const BuildArgs& a, int dtype, Prof& prof);
+hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dtype, int n_caches,
+                              int level, Prof& prof);
+hipError_t launch_attend(const AttendArgs& a, int dtype, int n_caches, Prof& prof);
+
+}  // namespace zha
