@@ -1,0 +1,349 @@
+#!/usr/bin/env python3
+"""Routed ZHA decode on one MI355X: queries/s and HBM roofline.
+
+One step = one decode step of the whole hot path on the 1M-token deep-tree
+workload (8 sequences x 8 KV heads x 4 query heads, d = 128, bf16 K/V,
+chunk 4, 6 levels, 16 reference queries, p = 0.95):
+  zha_append  (4,096 new tokens per sequence: new leaves + ancestors)
+  zha_route   (256 decode queries, 6 levels of score + top-p select)
+  zha_attend  (exact attention over the routed keys, sink, current chunk)
+Inputs are seeded synthetic data already resident in HBM.  Prints one JSON
+line (rank 0).  ``--gpus`` above 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+from tree_indexed_sparse_zha_amd import workloads as W
+from tree_indexed_sparse_zha_amd import zha
+
+HBM_PEAK_GBS = 8000.0
+FLAGS = zha.ZHA_SINK | zha.ZHA_LAST_CHUNK
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cfg_of(w: W.Workload, capacity: int) -> zha.ZhaConfig:
+    return zha.ZhaConfig(
+        w.batch, w.n_kv_heads, w.q_per_kv, w.head_dim, w.n_ref, w.chunk, w.levels, w.dtype, capacity
+    )
+
+
+def level_sizes(n, C, L):
+    return zha.level_sizes(n, C, L)
+
+
+def unpack_level(cfg, buf, lv, n_nodes):
+    rl = buf.layout
+    i = lv - 1
+    nq, w = int(rl.n_queries), int(rl.words[i])
+    off = int(rl.sel_offset[i])
+    return zha.unpack_bits(buf.sel[off : off + nq * w].view(nq, w), n_nodes)
+
+
+def selection_bytes(cfg: zha.ZhaConfig, buf, n_tokens: int, T: int):
+    """Algorithmic bytes of one route + attend from the selection it made.
+
+    route, per cache and level: |union over the cache's queries of the
+    candidates| x (R*d*2 bytes of g + 4R bytes of c); attend, per cache:
+    |union over the cache's queries of the attended keys| x 2*d*2 bytes of
+    K and V.  Also returns per-query selected share and per-level counts.
+    """
+    C, Lv, R, d = cfg.chunk, cfg.levels, cfg.n_ref, cfg.head_dim
+    sizes = level_sizes(n_tokens, C, Lv)
+    caches, QC = cfg.n_caches, cfg.q_per_kv * T
+    node_bytes = R * d * cfg.esize + 4 * R
+    per_level = {}
+    kept_prev = None
+    for lv in range(Lv, 0, -1):
+        n = sizes[lv - 1]
+        if lv == Lv:
+            cand = torch.ones(caches * QC, n, dtype=torch.bool, device="cuda")
+        else:
+            cand = kept_prev.repeat_interleave(C, dim=1)[:, :n]
+        kept = unpack_level(cfg, buf, lv, n)
+        union = cand.view(caches, QC, n).any(dim=1).sum().item()
+        per_level[lv] = dict(
+            nodes=n,
+            cand_per_query=float(cand.sum().item()) / (caches * QC),
+            kept_per_query=float(kept.sum().item()) / (caches * QC),
+            union_cand_per_cache=union / caches,
+            alg_bytes=union * node_bytes,
+        )
+        kept_prev = kept
+    # attended keys: kept chunks + sink + current chunk
+    kept1 = kept_prev
+    n1 = sizes[0]
+    keys = kept1.repeat_interleave(C, dim=1)
+    if keys.shape[1] < n_tokens:
+        keys = torch.nn.functional.pad(keys, (0, n_tokens - keys.shape[1]))
+    keys[:, 0] = True
+    keys[:, C * ((n_tokens - 1) // C) : n_tokens] = True
+    phi = keys.sum(dim=1).float() / n_tokens
+    union_keys = keys.view(caches, QC, n_tokens).any(dim=1).sum().item()
+    attend_bytes = union_keys * 2 * d * cfg.esize
+    del keys
+    return per_level, attend_bytes, phi.mean().item(), phi.min().item(), phi.max().item(), union_keys / caches
+
+
+def cpu_baseline(w: W.Workload, batch, n0: int, p: float, T: int):
+    """Time the CPU oracle on one cache (sequence 0, KV head 0): one decode
+    step = build of the appended top span + route and attend of its G*T
+    queries.  The oracle's full tree build for the initial tokens is done
+    first and not counted."""
+    import oracle.zha_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    A = w.append_tokens
+    n1 = n0 + A
+    K = batch.K[0, 0, :n1].to(torch.float64).cpu().numpy()
+    V = batch.V[0, 0, :n1].to(torch.float64).cpu().numpy()
+    ref = batch.ref[0].to(torch.float64).cpu().numpy()
+    Q = batch.Q[0, 0].to(torch.float64).cpu().numpy()  # [G, T, d]
+    t0 = time.time()
+    tree = O.build_tree(K, ref, w.chunk, w.levels, w.dtype, n_tokens=n1, keep_g=False)
+    t_build_full = time.time() - t0
+    # the step: the appended span's nodes, then route + attend of the cache's queries
+    t0 = time.time()
+    O.build_tree(K[n0:n1], ref, w.chunk, w.levels, w.dtype, keep_g=False)
+    for g in range(w.q_per_kv):
+        for t in range(T):
+            O.route_and_attend(Q[g, t], K, V, tree, ref, w.chunk, p, n1)
+    t_step = time.time() - t0
+    nq = w.q_per_kv * T
+    return {
+        "value": nq / t_step,
+        "unit": "queries/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": (
+            f"one cache (sequence 0, KV head 0) of the same workload at {n1} tokens: build of the "
+            f"appended {A}-token top span + route and attend of its {nq} queries, fp64 numpy "
+            f"({t_step:.1f} s; the oracle's initial full tree build, {t_build_full:.1f} s, not counted); "
+            f"BLAS threads {blas_threads}, other numpy work single-threaded; host "
+            f"{platform.processor() or platform.machine()} with {len(os.sched_getaffinity(0))} usable cores"
+        ),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=8)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="deep1m")
+    ap.add_argument("--p", type=float, default=None, help="top-p (default: the workload's first p)")
+    ap.add_argument("--tokens", type=int, default=None, help="override the context length (sweeps)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(
+            "bench.py measures the single-GPU path only; --gpus above 1 is not supported by this build "
+            "(the per-GPU share at real shape is what one GPU can show).",
+            file=sys.stderr,
+        )
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(2)
+    zha.load()
+    w = W.WORKLOADS[args.workload]
+    if args.tokens:
+        w = w.with_tokens(args.tokens)
+    p = args.p if args.p is not None else w.p[0]
+    T = w.queries_per_head
+    A = w.append_tokens
+    n_steps = args.warmup + args.steps
+    N0 = w.n_tokens
+    capacity = N0 + n_steps * A
+    cfg = cfg_of(w, capacity)
+    torch.cuda.set_device(0)
+    log(f"workload {w.name}: N={N0} caches={cfg.n_caches} p={p} capacity={capacity}")
+
+    t0 = time.time()
+    batch = W.make_batch(w, device="cuda", capacity=capacity, append_steps=n_steps)
+    torch.cuda.synchronize()
+    log(f"generated inputs in {time.time() - t0:.1f}s")
+    K, V, Q, ref = batch.K, batch.V, batch.Q, batch.ref
+    tree = zha.alloc_tree(cfg)
+    buf = zha.alloc_route(cfg, T)
+    nq = int(buf.layout.n_queries)
+    out = torch.empty(nq, cfg.head_dim, device="cuda")
+    lse = torch.empty(nq, device="cuda")
+    ws = torch.empty(zha.attend_workspace_bytes(cfg, T), dtype=torch.uint8, device="cuda")
+    log(
+        f"tree {tree.numel() / 1e9:.1f} GB, K+V {2 * K.numel() * K.element_size() / 1e9:.1f} GB, "
+        f"scores {buf.score.numel() * 4 / 1e9:.2f} GB"
+    )
+
+    # tree build over the initial context (reported separately)
+    ev_build = zha.HipEvents(1)
+    zha.build(cfg, K, ref, tree, N0, ev=ev_build)
+    torch.cuda.synchronize()
+    zha.build(cfg, K, ref, tree, N0, ev=ev_build)
+    torch.cuda.synchronize()
+    build_ms = ev_build.elapsed_ms()[0][2]
+    log(f"build {build_ms:.2f} ms")
+
+    ev_app = [zha.HipEvents(1) for _ in range(n_steps)]
+    ev_route = [zha.HipEvents(2 * cfg.levels) for _ in range(n_steps)]
+    ev_att = [zha.HipEvents(2) for _ in range(n_steps)]
+
+    def step(s):
+        n_old = N0 + s * A
+        zha.append(cfg, K, ref, tree, n_old, A, ev=ev_app[s])
+        n = n_old + A
+        zha.route(cfg, tree, n, Q, T, p, buf, ev=ev_route[s])
+        zha.attend(cfg, Q, T, K, V, n, zha.level1_sel(buf), FLAGS, out, lse, ws, ev=ev_att[s])
+        return n
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(args.warmup, n_steps):
+        n_final = step(s)
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    value = nq / (ms_per_step / 1e3)
+    log(f"{ms_per_step:.3f} ms/step -> {value:.1f} queries/s")
+
+    # per-kernel times over the timed steps
+    kt = {}
+    for s in range(args.warmup, n_steps):
+        for evs in (ev_app[s], ev_route[s], ev_att[s]):
+            for kid, lvl, ms in evs.elapsed_ms():
+                key = f"{zha.KERNEL_NAMES[kid]}" + (f"_L{lvl}" if lvl else "")
+                kt.setdefault(key, []).append(ms)
+    kmean = {k: float(np.mean(v)) for k, v in kt.items()}
+    route_ms = sum(v for k, v in kmean.items() if k.startswith(("score", "select")))
+    attend_ms = kmean.get("attend", 0.0) + kmean.get("combine", 0.0)
+    append_ms = kmean.get("build", 0.0)
+
+    # algorithmic bytes from the last step's selection
+    per_level, attend_bytes, phi, phi_min, phi_max, ukeys = selection_bytes(cfg, buf, n_final, T)
+    route_bytes = sum(v["alg_bytes"] for v in per_level.values())
+    tree_bytes_per_token = sum(
+        cfg.n_ref * (cfg.head_dim * cfg.esize + 8) / (cfg.chunk**l) for l in range(1, cfg.levels + 1)
+    )
+    append_bytes = cfg.n_caches * A * (cfg.head_dim * cfg.esize + tree_bytes_per_token)
+    alg = {"attend": attend_bytes, "build": append_bytes}
+    for lv, v in per_level.items():
+        alg[f"score_L{lv}"] = v["alg_bytes"]
+        alg[f"select_L{lv}"] = nq * v["nodes"] * 4  # one read of the score row per query
+    dom = max(kmean, key=kmean.get)
+    dom_bytes = alg.get(dom)
+    roofline = {
+        "kernel": dom,
+        "bound": "hbm",
+        "achieved": round(dom_bytes / (kmean[dom] / 1e3) / 1e9, 1) if dom_bytes else None,
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(dom_bytes / (kmean[dom] / 1e3) / 1e9 / HBM_PEAK_GBS, 4) if dom_bytes else None,
+        "traffic": None,
+        "alg_bytes_per_launch": dom_bytes,
+        "avg_launch_ms": round(kmean[dom], 4),
+    }
+    ra_ms = route_ms + attend_ms
+    ra_gbs = (route_bytes + attend_bytes) / (ra_ms / 1e3) / 1e9 if ra_ms > 0 else None
+
+    dense = None
+    if not args.no_dense:
+        ev_d = zha.HipEvents(2)
+        times = []
+        for r in range(4):
+            zha.dense_decode(cfg, Q, T, K, V, n_final, out, lse, ev=ev_d, ws=ws)
+            torch.cuda.synchronize()
+            if r:
+                times.append(sum(ms for _, _, ms in ev_d.elapsed_ms()))
+        dms = float(np.mean(times))
+        dbytes = cfg.n_caches * n_final * 2 * cfg.head_dim * cfg.esize
+        dense = {
+            "ms": round(dms, 4),
+            "queries_per_s": round(nq / (dms / 1e3), 1),
+            "GB_s": round(dbytes / (dms / 1e3) / 1e9, 1),
+            "frac_of_peak": round(dbytes / (dms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "route_plus_attend_over_dense": round(ra_ms / dms, 3),
+        }
+        log(f"dense {dms:.3f} ms")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(w, batch, n_final - A, p, T)
+        log(f"cpu baseline {cpu['value']:.3f} queries/s")
+
+    res = {
+        "metric": "routed decode queries/s + HBM GB/s (% of peak) at 1M ctx, deep tree",
+        "value": round(value, 2),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "n_tokens": N0,
+            "batch": w.batch,
+            "kv_heads": w.n_kv_heads,
+            "q_per_kv": w.q_per_kv,
+            "head_dim": w.head_dim,
+            "chunk": w.chunk,
+            "levels": w.levels,
+            "n_ref": w.n_ref,
+            "p": p,
+            "append_tokens_per_step": A,
+            "queries_per_step": nq,
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "route_attend": {
+            "ms": round(ra_ms, 4),
+            "alg_GB": round((route_bytes + attend_bytes) / 1e9, 3),
+            "GB_s": round(ra_gbs, 1) if ra_gbs else None,
+            "frac_of_peak": round(ra_gbs / HBM_PEAK_GBS, 4) if ra_gbs else None,
+        },
+        "append_ms": round(append_ms, 4),
+        "kernel_ms": {k: round(v, 4) for k, v in sorted(kmean.items())},
+        "alg_bytes": {k: int(v) for k, v in alg.items()},
+        "selected_share": {"mean": round(phi, 4), "min": round(phi_min, 4), "max": round(phi_max, 4)},
+        "levels": {str(k): {kk: round(vv, 2) for kk, vv in v.items()} for k, v in sorted(per_level.items())},
+        "build": {
+            "ms": round(build_ms, 3),
+            "tokens_per_s": round(w.batch * N0 / (build_ms / 1e3), 1),
+            "token_heads_per_s": round(cfg.n_caches * N0 / (build_ms / 1e3), 1),
+            "GB_s": round(cfg.n_caches * N0 * (cfg.head_dim * cfg.esize + tree_bytes_per_token) / (build_ms / 1e3) / 1e9, 1),
+        },
+        "dense": dense,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
