@@ -34,9 +34,9 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def cfg_of(w: W.Workload, capacity: int) -> zha.ZhaConfig:
+def cfg_of(w: W.Workload, capacity: int, leaf_form: str) -> zha.ZhaConfig:
     return zha.ZhaConfig(
-        w.batch, w.n_kv_heads, w.q_per_kv, w.head_dim, w.n_ref, w.chunk, w.levels, w.dtype, capacity
+        w.batch, w.n_kv_heads, w.q_per_kv, w.head_dim, w.n_ref, w.chunk, w.levels, w.dtype, capacity, leaf_form
     )
 
 
@@ -64,6 +64,7 @@ def selection_bytes(cfg: zha.ZhaConfig, buf, n_tokens: int, T: int):
     sizes = level_sizes(n_tokens, C, Lv)
     caches, QC = cfg.n_caches, cfg.q_per_kv * T
     node_bytes = R * d * cfg.esize + 4 * R
+    leaf_bytes = C * d * cfg.esize + R * C * 4 + 4 * R if cfg.leaf_form == "weights" else node_bytes
     per_level = {}
     kept_prev = None
     for lv in range(Lv, 0, -1):
@@ -79,7 +80,7 @@ def selection_bytes(cfg: zha.ZhaConfig, buf, n_tokens: int, T: int):
             cand_per_query=float(cand.sum().item()) / (caches * QC),
             kept_per_query=float(kept.sum().item()) / (caches * QC),
             union_cand_per_cache=union / caches,
-            alg_bytes=union * node_bytes,
+            alg_bytes=union * (leaf_bytes if lv == 1 else node_bytes),
         )
         kept_prev = kept
     # attended keys: kept chunks + sink + current chunk
@@ -150,6 +151,8 @@ def main():
     ap.add_argument("--workload", default="deep1m")
     ap.add_argument("--p", type=float, default=None, help="top-p (default: the workload's first p)")
     ap.add_argument("--tokens", type=int, default=None, help="override the context length (sweeps)")
+    ap.add_argument("--leaf-form", default="weights", choices=["weights", "mean"],
+                    help="level-1 storage: softmax weights scored from raw keys (default) or mean keys")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     args = ap.parse_args()
@@ -173,7 +176,9 @@ def main():
     n_steps = args.warmup + args.steps
     N0 = w.n_tokens
     capacity = N0 + n_steps * A
-    cfg = cfg_of(w, capacity)
+    if args.leaf_form == "weights" and w.chunk not in (4, 8, 16):
+        args.leaf_form = "mean"
+    cfg = cfg_of(w, capacity, args.leaf_form)
     torch.cuda.set_device(0)
     log(f"workload {w.name}: N={N0} caches={cfg.n_caches} p={p} capacity={capacity}")
 
@@ -210,7 +215,7 @@ def main():
         n_old = N0 + s * A
         zha.append(cfg, K, ref, tree, n_old, A, ev=ev_app[s])
         n = n_old + A
-        zha.route(cfg, tree, n, Q, T, p, buf, ev=ev_route[s])
+        zha.route(cfg, tree, n, Q, T, p, buf, ev=ev_route[s], K=K)
         zha.attend(cfg, Q, T, K, V, n, zha.level1_sel(buf), FLAGS, out, lse, ws, ev=ev_att[s])
         return n
 
@@ -245,8 +250,8 @@ def main():
     per_level, attend_bytes, phi, phi_min, phi_max, ukeys = selection_bytes(cfg, buf, n_final, T)
     route_bytes = sum(v["alg_bytes"] for v in per_level.values())
     tree_bytes_per_token = sum(
-        cfg.n_ref * (cfg.head_dim * cfg.esize + 8) / (cfg.chunk**l) for l in range(1, cfg.levels + 1)
-    )
+        cfg.n_ref * (cfg.head_dim * cfg.esize + 8) / (cfg.chunk**l) for l in range(2, cfg.levels + 1)
+    ) + (cfg.n_ref * (4 * cfg.chunk + 8) if cfg.leaf_form == "weights" else cfg.n_ref * (cfg.head_dim * cfg.esize + 8)) / cfg.chunk
     append_bytes = cfg.n_caches * A * (cfg.head_dim * cfg.esize + tree_bytes_per_token)
     alg = {"attend": attend_bytes, "build": append_bytes}
     for lv, v in per_level.items():
@@ -319,6 +324,7 @@ def main():
             "n_ref": w.n_ref,
             "p": p,
             "append_tokens_per_step": A,
+            "leaf_form": cfg.leaf_form,
             "queries_per_step": nq,
         },
         "roofline": roofline,

@@ -57,6 +57,21 @@ enum zha_status {
 /* Element types of K, V, Q and of the stored mean keys g. */
 enum zha_dtype { ZHA_F32 = 0, ZHA_BF16 = 1 };
 
+/*
+ * Storage form of level-1 nodes.
+ *   ZHA_LEAF_MEAN: like every other level, the node stores its mean keys
+ *     g_j (kv_dtype), L_j and c_j = L_j - r_j . g_j / sqrt(d).
+ *   ZHA_LEAF_WEIGHTS: the node stores the softmax weights of its own C keys,
+ *     w_ji = exp(z_ji - L_j) ([R][C] fp32), L_j and c_j = L_j - sum_i w_ji z_ji.
+ *     Since g_j = sum_i w_ji k_i, the tangent-plane score of a level-1 node is
+ *     computed from the raw keys as max_j [c_j + sum_i w_ji q . k_i / sqrt(d)]
+ *     (the same plane with g_j unrounded).  A level-1 node then occupies
+ *     R*(4C+8) bytes instead of R*(d*esize+8), and routing reads the chunk's
+ *     C*d key elements instead of R*d mean-key elements.  Supported with bf16
+ *     and chunk in {4, 8, 16}.  Levels >= 2 are the same in both forms.
+ */
+enum zha_leaf_form { ZHA_LEAF_MEAN = 0, ZHA_LEAF_WEIGHTS = 1 };
+
 /* Flags of zha_attend. */
 enum zha_attend_flags {
   ZHA_SINK = 1,       /* token 0 is always attended (MTP "How does top-p routing pick tokens?") */
@@ -79,6 +94,7 @@ typedef struct zha_config {
   int32_t chunk;           /* C: keys per level-1 node; children per upper node */
   int32_t levels;          /* Lv: level 1 = chunks of raw keys, level Lv = top */
   int32_t kv_dtype;        /* enum zha_dtype */
+  int32_t leaf_form;       /* enum zha_leaf_form */
   int64_t capacity_tokens; /* largest N the tree buffer must hold */
 } zha_config;
 
@@ -86,7 +102,9 @@ typedef struct zha_config {
  * Tree buffer layout (computed by zha_get_tree_layout).  Level l (index l-1)
  * holds node_cap[l-1] = ceil(node_cap[l-2] / C) nodes per cache, with
  * node_cap[0] = floor(capacity / C).  Per level, three blocks:
- *   g: [caches][node_cap][R*d] in kv_dtype.  Within one node the R x d mean
+ *   g: [caches][node_cap][g_bytes / element size]: for level 1 in the
+ *      weights form, w as [R][C] fp32; otherwise R x d mean keys in kv_dtype.
+ *      Within one node the R x d mean
  *      keys are stored d-chunk-interleaved so that one 64-lane load yields a
  *      16 x 32 MFMA operand tile: element (j, e) with 16-byte piece
  *      k = e / E (E = elements per 16 bytes), sub-index e % E, lives at
@@ -103,7 +121,7 @@ typedef struct zha_tree_layout {
   int64_t g_offset[ZHA_MAX_LEVELS];
   int64_t L_offset[ZHA_MAX_LEVELS];
   int64_t c_offset[ZHA_MAX_LEVELS];
-  int64_t g_node_bytes; /* R * d * sizeof(kv_dtype) */
+  int64_t g_bytes[ZHA_MAX_LEVELS]; /* bytes of one node's g (or w) block, per level */
   int64_t total_bytes;  /* size of the caller's tree buffer */
 } zha_tree_layout;
 
@@ -112,9 +130,10 @@ typedef struct zha_tree_layout {
  * B*H*G*T queries.  Per level l (index l-1):
  *   sel:   [n_queries][words[l-1]] uint32 bitsets, bit n%32 of word n/32 set
  *          iff node n is kept; starts at sel_offset[l-1] (in uint32 words).
- *   score: [n_queries][node_cap[l-1]] fp32 plane scores of the candidates,
- *          -inf for nodes that were not candidates; starts at
- *          score_offset[l-1] (in floats).
+ *   score: [n_queries][score_stride[l-1]] fp32 plane scores of the
+ *          candidates (entries >= the level's node count are unused), -inf
+ *          for nodes that were not candidates; starts at score_offset[l-1]
+ *          (in floats); score_stride = node_cap rounded up to 4.
  *   stats: [n_queries] zha_select_stats; starts at stats_offset[l-1]
  *          (in records).
  */
@@ -125,6 +144,7 @@ typedef struct zha_route_layout {
   int64_t words[ZHA_MAX_LEVELS];
   int64_t sel_offset[ZHA_MAX_LEVELS];
   int64_t score_offset[ZHA_MAX_LEVELS];
+  int64_t score_stride[ZHA_MAX_LEVELS];
   int64_t stats_offset[ZHA_MAX_LEVELS];
   int64_t sel_words_total;    /* uint32 words of the sel buffer */
   int64_t score_floats_total; /* floats of the score buffer */
@@ -243,6 +263,8 @@ int zha_append(const zha_config* cfg, const void* K, const int64_t k_strides[3],
  *             kv head, query head, t} in elements; rows contiguous, 16-byte
  *             aligned.
  *   p         in (0, 1]; NaN or <= 0 is ZHA_ERR_ARG.
+ *   K         device keys as zha_build (read by level-1 scoring in the
+ *             weights form; may be NULL, with k_strides, in the mean form).
  *   sel       device, zha_get_route_layout().sel_words_total uint32 (output).
  *   score     device, zha_get_route_layout().score_floats_total fp32 (output).
  *   stats     device, zha_get_route_layout().stats_total records (output).
@@ -250,7 +272,8 @@ int zha_append(const zha_config* cfg, const void* K, const int64_t k_strides[3],
  * Level-1 bits of sel are the routed chunk ids consumed by zha_attend.
  */
 int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const void* Q,
-              const int64_t q_strides[4], int32_t T, float p, uint32_t* sel, float* score,
+              const int64_t q_strides[4], int32_t T, float p, const void* K,
+              const int64_t k_strides[3], uint32_t* sel, float* score,
               zha_select_stats* stats, void* ws, int64_t ws_bytes, zha_profile* prof, void* stream);
 
 /*

@@ -187,12 +187,16 @@ def build_tree(
     n_tokens: Optional[int] = None,
     keep_g: bool = True,
     block: int = 8192,
+    leaf_dtype: Optional[str] = None,
 ) -> List[Level]:
     """Build every level for keys K[:n_tokens] (fp64 [N, d]) and ref [R, d].
 
     Returns levels[0] = level 1 (chunks) ... levels[-1] = top level.  Nodes
     are processed in batches of ``block`` only to bound memory; each node's
-    arithmetic is the per-node definition above.
+    arithmetic is the per-node definition above.  ``g_dtype`` is the storage
+    precision of g; ``leaf_dtype`` (default: g_dtype) that of level 1 alone,
+    "f64" when level-1 planes are evaluated from the chunk's own keys so that
+    g is never rounded there.
     """
     K = np.asarray(K, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
@@ -212,7 +216,7 @@ def build_tree(
         w = np.exp(z - L[:, :, None])
         L1[a:b] = L
         g1[a:b] = np.einsum("nrc,ncd->nrd", w, keys)
-    out.append(_finish(L1, g1, ref, g_dtype, True))
+    out.append(_finish(L1, g1, ref, leaf_dtype or g_dtype, True))
     # upper levels from the unrounded children
     for lv in range(1, levels):
         n = sizes[lv]

@@ -34,7 +34,7 @@ def eps_score(dtype: str, q: np.ndarray, level) -> float:
     bound allows two flips of the largest |q_i| and |g| of the level, plus
     the fp32 term.
     """
-    if dtype == "f32":
+    if dtype in ("f32", "f64"):
         return 5e-5
     d = q.shape[-1]
     gmax = float(np.abs(level.ghat).max()) if level.ghat.size else 0.0
@@ -51,7 +51,8 @@ class LevelReport:
     max_score_err: float
 
 
-def check_route_teacher_forced(q, tree, ref, chunk, p, gpu_kept: Dict[int, np.ndarray], dtype, gpu_score=None):
+def check_route_teacher_forced(q, tree, ref, chunk, p, gpu_kept: Dict[int, np.ndarray], dtype, gpu_score=None,
+                               leaf_dtype=None):
     """Returns per-level reports; raises AssertionError on an unexplained difference.
 
     gpu_kept[level] = sorted kept node ids of the GPU; gpu_score[level] =
@@ -68,7 +69,7 @@ def check_route_teacher_forced(q, tree, ref, chunk, p, gpu_kept: Dict[int, np.nd
         gk = np.asarray(gpu_kept[lv], dtype=np.int64)
         assert set(gk.tolist()) <= set(cand.tolist()), f"level {lv}: GPU kept a non-candidate"
         s = O.plane_scores(q, tree[lv - 1], ref, cand)
-        eps = eps_score(dtype, q, tree[lv - 1])
+        eps = eps_score(leaf_dtype if (lv == 1 and leaf_dtype) else dtype, q, tree[lv - 1])
         err = 0.0
         if gpu_score is not None and cand.size:
             gs = np.asarray(gpu_score[lv], dtype=np.float64)[cand]

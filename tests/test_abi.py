@@ -47,13 +47,22 @@ def test_tree_layout_sizes():
     tl = zha.tree_layout(cfg)
     assert tl.levels == 6
     assert [tl.node_cap[i] for i in range(6)] == [8192, 2048, 512, 128, 32, 8]
-    assert tl.g_node_bytes == 16 * 128 * 2
+    assert all(tl.g_bytes[i] == 16 * 128 * 2 for i in range(6))
     # node = R*d*2 (g) + 4R (L) + 4R (c) = 4224 bytes
     nodes = sum(tl.node_cap[i] for i in range(6)) * 8
     assert tl.total_bytes >= nodes * 4224
     assert tl.total_bytes < nodes * 4224 + 6 * 3 * 256
     for i in range(6):
         assert tl.g_offset[i] % 256 == 0 and tl.L_offset[i] % 256 == 0 and tl.c_offset[i] % 256 == 0
+
+
+def test_tree_layout_weights_form():
+    cfg = cfg_deep(leaf_form="weights")
+    tl = zha.tree_layout(cfg)
+    assert tl.g_bytes[0] == 16 * 4 * 4
+    assert all(tl.g_bytes[i] == 16 * 128 * 2 for i in range(1, 6))
+    mean = zha.tree_layout(cfg_deep())
+    assert tl.total_bytes < mean.total_bytes * 0.35
 
 
 def test_route_layout_sizes():
@@ -63,6 +72,11 @@ def test_route_layout_sizes():
     assert rl.words[0] == 8192 // 32
     assert rl.score_floats_total == rl.n_queries * (8192 + 2048 + 512 + 128 + 32 + 8)
     assert rl.stats_total == 6 * rl.n_queries
+    assert [rl.score_stride[i] for i in range(6)] == [8192, 2048, 512, 128, 32, 8]
+    assert rl.workspace_bytes >= 6 * rl.n_queries * 16
+    odd = zha.route_layout(cfg_deep(capacity=32768 + 4 * 4096 * 3 + 4), 1)
+    for i in range(6):
+        assert odd.score_stride[i] % 4 == 0 and odd.score_stride[i] >= zha.tree_layout(cfg_deep(capacity=32768 + 4 * 4096 * 3 + 4)).node_cap[i]
 
 
 @pytest.mark.parametrize(
@@ -78,6 +92,11 @@ def test_route_layout_sizes():
         (dict(batch=0), zha.ZHA_ERR_ARG),
         (dict(capacity=0), zha.ZHA_ERR_ARG),
         (dict(dtype="f32", head_dim=64, n_ref=4, chunk=4, levels=3), 0),
+        (dict(leaf_form="weights"), 0),
+        (dict(leaf_form="weights", chunk=8, levels=4), 0),
+        (dict(leaf_form="weights", dtype="f32"), zha.ZHA_ERR_UNSUPPORTED),
+        (dict(leaf_form="weights", chunk=256, levels=1), zha.ZHA_ERR_UNSUPPORTED),
+        (dict(leaf_form="weights", chunk=2, levels=6), zha.ZHA_ERR_UNSUPPORTED),
     ],
 )
 def test_config_validation(kw, code):
@@ -92,10 +111,10 @@ def test_config_validation(kw, code):
 
 def _call_route(lib, cfg, **over):
     a = dict(tree=16, n_tokens=32768, Q=16, qs=zha._i64(1 << 20, 1 << 16, 1 << 12, 128), T=1, p=0.95,
-             sel=16, score=16, stats=16, ws=16, ws_bytes=0)
+             K=None, ks=None, sel=16, score=16, stats=16, ws=16, ws_bytes=0)
     a.update(over)
     c = cfg.c()
-    return lib.zha_route(ct.byref(c), a["tree"], a["n_tokens"], a["Q"], a["qs"], a["T"], a["p"], a["sel"],
+    return lib.zha_route(ct.byref(c), a["tree"], a["n_tokens"], a["Q"], a["qs"], a["T"], a["p"], a["K"], a["ks"], a["sel"],
                          a["score"], a["stats"], a["ws"], a["ws_bytes"], a.get("prof"), None)
 
 
@@ -112,6 +131,13 @@ def test_route_argument_errors(lib):
     assert _call_route(lib, cfg, n_tokens=32769) == zha.ZHA_ERR_CAPACITY
     assert b"n_tokens exceeds capacity" in lib.zha_last_error()
     assert _call_route(lib, cfg, qs=zha._i64(1, 1, 1, 1)) == zha.ZHA_ERR_ALIGN
+    assert _call_route(lib, cfg, ws_bytes=0) == zha.ZHA_ERR_CAPACITY
+    assert b"workspace" in lib.zha_last_error()
+    assert _call_route(lib, cfg, ws=None, ws_bytes=1 << 20) == zha.ZHA_ERR_NULL
+    # the leaf weights form scores level 1 from the keys: K is required
+    cw = cfg_deep(leaf_form="weights")
+    assert _call_route(lib, cw, ws_bytes=1 << 20) == zha.ZHA_ERR_NULL
+    assert b"K" in lib.zha_last_error()
     bad = zha.Profile()
     bad.n_pairs = 40
     assert _call_route(lib, cfg, prof=ct.byref(bad)) == zha.ZHA_ERR_ARG

@@ -13,6 +13,8 @@ import numpy as np
 import pytest
 import torch
 
+import scipy.special as sps
+
 import oracle.zha_oracle as O
 from tests import parity as PAR
 from tree_indexed_sparse_zha_amd import workloads as W
@@ -127,7 +129,11 @@ BUILD_CASES = [
     ("light-bf16", dict(batch=1, n_kv_heads=1, q_per_kv=4, head_dim=128, n_ref=1, chunk=8, levels=4, dtype="bf16", capacity=5000), 4096 + 8 * 5 + 3),
     ("c32-f32-d64", dict(batch=1, n_kv_heads=1, q_per_kv=1, head_dim=64, n_ref=5, chunk=32, levels=2, dtype="f32", capacity=2200), 2048 + 70),
     ("c1-f32", dict(batch=1, n_kv_heads=1, q_per_kv=1, head_dim=64, n_ref=3, chunk=1, levels=1, dtype="f32", capacity=300), 300),
+    ("deep-bf16-weights", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=6, dtype="bf16", capacity=9000, leaf_form="weights"), 8192 + 4 * 37 + 2),
+    ("light-bf16-weights", dict(batch=1, n_kv_heads=1, q_per_kv=4, head_dim=128, n_ref=1, chunk=8, levels=4, dtype="bf16", capacity=5000, leaf_form="weights"), 4096 + 8 * 5 + 3),
+    ("c16-bf16-d64-weights", dict(batch=2, n_kv_heads=1, q_per_kv=2, head_dim=64, n_ref=7, chunk=16, levels=2, dtype="bf16", capacity=3000, leaf_form="weights"), 2048 + 16 * 9 + 5),
 ]
+APPEND_CASES = BUILD_CASES[:5] + BUILD_CASES[6:]
 
 
 def _segmented_keys(cfg, seed):
@@ -149,12 +155,21 @@ def check_tree(cfg, tree, K, ref, N):
         for h in range(cfg.n_kv_heads):
             cache = b * cfg.n_kv_heads + h
             Kn, rn = np64(K[b, h, :N]), np64(ref[h])
-            to = O.build_tree(Kn, rn, cfg.chunk, cfg.levels, cfg.dtype, n_tokens=N)
+            weights = cfg.leaf_form == "weights"
+            to = O.build_tree(Kn, rn, cfg.chunk, cfg.levels, cfg.dtype, n_tokens=N, leaf_dtype="f64" if weights else None)
             for lv in range(1, cfg.levels + 1):
                 n = sizes[lv - 1]
                 got = zha.read_level(cfg, tree, lv, n)
-                gg, gL, gc = np64(got["g"][cache]), np64(got["L"][cache]), np64(got["c"][cache])
                 lvl = to[lv - 1]
+                if lv == 1 and weights:
+                    # w is the softmax of r_j . k_i / sqrt(d) over the chunk (scipy), c = L - sum w z
+                    gw, gL, gc = np64(got["w"][cache]), np64(got["L"][cache]), np64(got["c"][cache])
+                    z = np.einsum("ncd,rd->nrc", Kn[: n * cfg.chunk].reshape(n, cfg.chunk, d), rn) / math.sqrt(d)
+                    np.testing.assert_allclose(gw, sps.softmax(z, axis=2), rtol=0, atol=2e-6, err_msg="w level 1")
+                    np.testing.assert_allclose(gL, lvl.L, rtol=1e-5, atol=3e-5, err_msg="L level 1")
+                    np.testing.assert_allclose(gc, lvl.c, rtol=1e-5, atol=3e-5, err_msg="c level 1")
+                    continue
+                gg, gL, gc = np64(got["g"][cache]), np64(got["L"][cache]), np64(got["c"][cache])
                 np.testing.assert_allclose(gL, lvl.L, rtol=1e-5, atol=3e-5, err_msg=f"L level {lv}")
                 # c is consistent with the GPU's own stored g ...
                 c_self = gL - np.einsum("nrd,rd->nr", gg, rn) / math.sqrt(d)
@@ -197,7 +212,7 @@ def test_build_matches_oracle(name, kw, N):
     check_tree(cfg, tree, K, ref, N)
 
 
-@pytest.mark.parametrize("name,kw,N", BUILD_CASES[:5], ids=[c[0] for c in BUILD_CASES[:5]])
+@pytest.mark.parametrize("name,kw,N", APPEND_CASES, ids=[c[0] for c in APPEND_CASES])
 def test_append_equals_build(name, kw, N):
     _say(f"append {name}")
     cfg = zha.ZhaConfig(**kw)
@@ -219,7 +234,7 @@ def test_append_equals_build(name, kw, N):
     for lv in range(1, cfg.levels + 1):
         a = zha.read_level(cfg, fresh, lv, sizes[lv - 1])
         b = zha.read_level(cfg, grown, lv, sizes[lv - 1])
-        for f in ("g", "L", "c"):
+        for f in a:
             ba = a[f].contiguous().view(torch.uint8)
             bb = b[f].contiguous().view(torch.uint8)
             assert torch.equal(ba, bb), f"{f} level {lv} differs between append and build"
@@ -233,7 +248,7 @@ def run_path(cfg, K, V, Q, ref, N, T, p, flags=zha.ZHA_SINK | zha.ZHA_LAST_CHUNK
     tree = zha.alloc_tree(cfg)
     zha.build(cfg, K, ref, tree, N)
     buf = zha.alloc_route(cfg, T)
-    zha.route(cfg, tree, N, Q, T, p, buf)
+    zha.route(cfg, tree, N, Q, T, p, buf, K=K)
     nq = int(buf.layout.n_queries)
     out = torch.empty(nq, cfg.head_dim, device="cuda")
     lse = torch.empty(nq, device="cuda")
@@ -254,24 +269,27 @@ def gpu_levels(cfg, buf, N, qi):
         w = int(rl.words[i])
         words = buf.sel[int(rl.sel_offset[i]) + qi * w : int(rl.sel_offset[i]) + (qi + 1) * w]
         bits[lv] = zha.unpack_bits(words.cpu(), sizes[i]).numpy()
-        cap = zha.tree_layout(cfg).node_cap[i]
+        cap = int(rl.score_stride[i])
         off = int(rl.score_offset[i]) + qi * cap
         scores[lv] = buf.score[off : off + sizes[i]].cpu().numpy()
     return bits, scores
 
 
 ROUTE_WORKLOADS = [
-    ("tiny", None, None, 16),  # all queries of the tiny workload
-    ("deep32k", 2, None, 6),  # 2 of 8 caches, 6 sampled queries each
-    ("wide256k", 2, None, 4),
+    ("tiny", None, "mean", 16),  # all queries of the tiny workload
+    ("deep32k", 2, "mean", 6),  # 2 of 8 caches, 6 sampled queries each
+    ("deep32k", 2, "weights", 6),
+    ("wide256k", 2, "mean", 4),
 ]
 
 
-@pytest.mark.parametrize("wname,n_caches_checked,_unused,q_per_cache", ROUTE_WORKLOADS, ids=[r[0] for r in ROUTE_WORKLOADS])
-def test_route_and_attend_match_oracle(wname, n_caches_checked, _unused, q_per_cache):
+@pytest.mark.parametrize(
+    "wname,n_caches_checked,leaf_form,q_per_cache", ROUTE_WORKLOADS, ids=[f"{r[0]}-{r[2]}" for r in ROUTE_WORKLOADS]
+)
+def test_route_and_attend_match_oracle(wname, n_caches_checked, leaf_form, q_per_cache):
     w = W.WORKLOADS[wname]
-    _say(f"route {wname}")
-    cfg = cfg_of(w)
+    _say(f"route {wname} {leaf_form}")
+    cfg = cfg_of(w, leaf_form=leaf_form)
     batch = W.make_batch(w, device="cuda")
     N, T, p = w.n_tokens, w.queries_per_head, w.p[0]
     tree, buf, out, lse = run_path(cfg, batch.K, batch.V, batch.Q, batch.ref, N, T, p)
@@ -286,7 +304,8 @@ def test_route_and_attend_match_oracle(wname, n_caches_checked, _unused, q_per_c
     for cache in caches:
         b, h = divmod(cache, cfg.n_kv_heads)
         Kn, Vn, rn = np64(batch.K[b, h, :N]), np64(batch.V[b, h, :N]), np64(batch.ref[h])
-        to = O.build_tree(Kn, rn, cfg.chunk, cfg.levels, cfg.dtype, keep_g=False)
+        leaf_dtype = "f64" if leaf_form == "weights" else None
+        to = O.build_tree(Kn, rn, cfg.chunk, cfg.levels, cfg.dtype, keep_g=False, leaf_dtype=leaf_dtype)
         qis = list(range(QC)) if q_per_cache >= QC else sorted(rng.choice(QC, q_per_cache, replace=False).tolist())
         for qi_local in qis:
             gq, t = divmod(qi_local, T)
@@ -294,7 +313,7 @@ def test_route_and_attend_match_oracle(wname, n_caches_checked, _unused, q_per_c
             q = np64(batch.Q[b, h, gq, t])
             bits, scores = gpu_levels(cfg, buf, N, qi)
             kept = PAR.gpu_kept_from_bits(bits)
-            PAR.check_route_teacher_forced(q, to, rn, cfg.chunk, p, kept, cfg.dtype, scores)
+            PAR.check_route_teacher_forced(q, to, rn, cfg.chunk, p, kept, cfg.dtype, scores, leaf_dtype=leaf_dtype)
             # attention over the GPU's set (R21)
             idx = O.attend_set(kept[1], N, cfg.chunk, True, True)
             o, l = O.attend(q, Kn, Vn, idx)
@@ -344,14 +363,15 @@ def test_p1_is_dense():
         np.testing.assert_allclose(dense[t].cpu().numpy(), o, atol=1e-5, rtol=0)
 
 
-def test_route_is_deterministic():
+@pytest.mark.parametrize("leaf_form", ["mean", "weights"])
+def test_route_is_deterministic(leaf_form):
     w = W.WORKLOADS["deep32k"]
-    cfg = cfg_of(w)
+    cfg = cfg_of(w, leaf_form=leaf_form)
     batch = W.make_batch(w, device="cuda")
     N, T, p = w.n_tokens, w.queries_per_head, w.p[0]
     tree, buf, out, lse = run_path(cfg, batch.K, batch.V, batch.Q, batch.ref, N, T, p)
     sel0, sc0, st0, out0 = buf.sel.clone(), buf.score.clone(), buf.stats.clone(), out.clone()
-    zha.route(cfg, tree, N, batch.Q, T, p, buf)
+    zha.route(cfg, tree, N, batch.Q, T, p, buf, K=batch.K)
     ws = torch.empty(zha.attend_workspace_bytes(cfg, T), dtype=torch.uint8, device="cuda")
     zha.attend(cfg, batch.Q, T, batch.K, batch.V, N, zha.level1_sel(buf), 3, out, lse, ws)
     torch.cuda.synchronize()

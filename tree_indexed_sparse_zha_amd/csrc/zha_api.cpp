@@ -39,6 +39,11 @@ int check_config(const zha_config* c) {
   if (c->capacity_tokens < 1) return fail(ZHA_ERR_ARG, "capacity_tokens must be >= 1");
   if (c->kv_dtype != ZHA_F32 && c->kv_dtype != ZHA_BF16)
     return fail(ZHA_ERR_UNSUPPORTED, "kv_dtype %d unsupported", c->kv_dtype);
+  if (c->leaf_form != ZHA_LEAF_MEAN && c->leaf_form != ZHA_LEAF_WEIGHTS)
+    return fail(ZHA_ERR_ARG, "leaf_form %d unknown", c->leaf_form);
+  if (c->leaf_form == ZHA_LEAF_WEIGHTS &&
+      (c->kv_dtype != ZHA_BF16 || (c->chunk != 4 && c->chunk != 8 && c->chunk != 16)))
+    return fail(ZHA_ERR_UNSUPPORTED, "the leaf weights form needs bf16 and chunk 4, 8 or 16");
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(ZHA_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", c->head_dim);
   if (c->n_ref > 16) return fail(ZHA_ERR_UNSUPPORTED, "n_ref %d unsupported (1..16)", c->n_ref);
@@ -83,14 +88,16 @@ void fill_tree_layout(const zha_config* c, zha_tree_layout* out) {
   std::memset(out, 0, sizeof(*out));
   out->levels = c->levels;
   const int64_t caches = (int64_t)c->batch * c->n_kv_heads;
-  out->g_node_bytes = (int64_t)c->n_ref * c->head_dim * esize(c->kv_dtype);
   int64_t n = c->capacity_tokens / c->chunk;
   int64_t off = 0;
   for (int l = 0; l < c->levels; ++l) {
     if (l > 0) n = cdiv(n, c->chunk);
+    out->g_bytes[l] = (l == 0 && c->leaf_form == ZHA_LEAF_WEIGHTS)
+                          ? (int64_t)c->n_ref * c->chunk * 4
+                          : (int64_t)c->n_ref * c->head_dim * esize(c->kv_dtype);
     out->node_cap[l] = n;
     out->g_offset[l] = off;
-    off = align256(off + caches * n * out->g_node_bytes);
+    off = align256(off + caches * n * out->g_bytes[l]);
     out->L_offset[l] = off;
     off = align256(off + caches * n * c->n_ref * 4);
     out->c_offset[l] = off;
@@ -108,6 +115,7 @@ void fill_geom(const zha_config* c, const zha_tree_layout& tl, zha::TreeGeom* g)
   g->esize = esize(c->kv_dtype);
   g->H = c->n_kv_heads;
   g->caches = c->batch * c->n_kv_heads;
+  g->leaf_weights = c->leaf_form == ZHA_LEAF_WEIGHTS;
   for (int l = 0; l < c->levels; ++l) {
     g->node_cap[l] = tl.node_cap[l];
     g->g_off[l] = tl.g_offset[l];
@@ -250,14 +258,16 @@ int zha_get_route_layout(const zha_config* cfg, int32_t T, zha_route_layout* out
     out->sel_offset[l] = sw;
     sw += out->n_queries * out->words[l];
     out->score_offset[l] = sf;
-    sf += out->n_queries * tl.node_cap[l];
+    out->score_stride[l] = (tl.node_cap[l] + 3) / 4 * 4;
+    sf += out->n_queries * out->score_stride[l];
     out->stats_offset[l] = ss;
     ss += out->n_queries;
   }
   out->sel_words_total = sw > 0 ? sw : 1;
   out->score_floats_total = sf > 0 ? sf : 1;
   out->stats_total = ss;
-  out->workspace_bytes = 0;
+  // per level and query: candidate key range and count, filled by the score kernel
+  out->workspace_bytes = align256((int64_t)cfg->levels * out->n_queries * 16);
   return ZHA_OK;
 }
 
@@ -277,7 +287,8 @@ int zha_append(const zha_config* cfg, const void* K, const int64_t k_strides[3],
 }
 
 int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const void* Q,
-              const int64_t q_strides[4], int32_t T, float p, uint32_t* sel, float* score,
+              const int64_t q_strides[4], int32_t T, float p, const void* K,
+              const int64_t k_strides[3], uint32_t* sel, float* score,
               zha_select_stats* stats, void* ws, int64_t ws_bytes, zha_profile* prof, void* stream) {
   int rc = check_config(cfg);
   if (rc) return rc;
@@ -286,6 +297,11 @@ int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const v
   if ((rc = check_ptr16(tree, "tree"))) return rc;
   if ((rc = check_ptr16(Q, "Q"))) return rc;
   if ((rc = check_strides(q_strides, 4, esize(cfg->kv_dtype), "q_strides"))) return rc;
+  const bool leafw = cfg->leaf_form == ZHA_LEAF_WEIGHTS;
+  if (leafw) {
+    if ((rc = check_ptr16(K, "K"))) return rc;
+    if ((rc = check_strides(k_strides, 3, esize(cfg->kv_dtype), "k_strides"))) return rc;
+  }
   if ((rc = check_ptr16(sel, "sel"))) return rc;
   if ((rc = check_ptr16(score, "score"))) return rc;
   if ((rc = check_ptr16(stats, "stats"))) return rc;
@@ -294,6 +310,7 @@ int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const v
   if (n_tokens > cfg->capacity_tokens) return fail(ZHA_ERR_CAPACITY, "n_tokens exceeds capacity");
   zha_route_layout rl;
   zha_get_route_layout(cfg, T, &rl);
+  if ((rc = check_ptr16(ws, "ws"))) return rc;
   if (ws_bytes < rl.workspace_bytes) return fail(ZHA_ERR_CAPACITY, "workspace too small");
   zha_tree_layout tl;
   fill_tree_layout(cfg, &tl);
@@ -303,6 +320,11 @@ int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const v
   const float isd = 1.0f / std::sqrt((float)cfg->head_dim);
   if (prof) prof->n_used = 0;
   zha::Prof pr{prof, static_cast<hipStream_t>(stream)};
+  uint32_t* keyrange = static_cast<uint32_t*>(ws);
+  {
+    hipError_t e = zha::launch_route_init(keyrange, (int64_t)cfg->levels * rl.n_queries, pr);
+    if (e != hipSuccess) return hip_fail(e, "route init launch");
+  }
   for (int l = cfg->levels - 1; l >= 0; --l) {
     zha::ScoreArgs sa;
     std::memset(&sa, 0, sizeof(sa));
@@ -325,11 +347,21 @@ int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const v
     sa.sel_parent = (l == cfg->levels - 1) ? nullptr : sel + rl.sel_offset[l + 1];
     sa.parent_words = (l == cfg->levels - 1) ? 0 : rl.words[l + 1];
     sa.score = score + rl.score_offset[l];
+    sa.score_stride = rl.score_stride[l];
+    sa.keyrange = keyrange + (int64_t)l * rl.n_queries * 4;
     sa.inv_sqrt_d = isd;
+    sa.leaf_weights = leafw && l == 0;
+    if (sa.leaf_weights) {
+      sa.K = K;
+      sa.ksb = k_strides[0];
+      sa.ksh = k_strides[1];
+      sa.kst = k_strides[2];
+    }
     zha::SelectArgs se;
     std::memset(&se, 0, sizeof(se));
     se.score = sa.score;
-    se.node_cap = tl.node_cap[l];
+    se.score_stride = sa.score_stride;
+    se.keyrange = sa.keyrange;
     se.n_nodes = n[l];
     se.sel = sel + rl.sel_offset[l];
     se.words = rl.words[l];

@@ -204,6 +204,260 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(AttendArgs A) {
   }
 }
 
+// bf16 path: compacted quads, QK^T on MFMA, PV in fp32 FMA.
+//
+// Phase 1: every thread tests 8 consecutive 4-key quads of the tile against
+// the routed chunk bits of the group's queries (plus sink / current chunk)
+// and the non-empty quads are compacted, in key order, into an LDS list with
+// a 4-bit key mask per query.  Phase 2: each wave takes groups of four list
+// entries (16 keys); K rows go straight into the A operand of
+// v_mfma_f32_16x16x32_bf16 (queries are the B operand), so one MFMA chain
+// yields the 16 x 16 logits.  The softmax weights leave the MFMA layout
+// through a 1 KiB LDS slot per wave and meet V, which is loaded with fully
+// coalesced 16-byte rows and accumulated in fp32.  The next group's K and V
+// are in flight while the current one is computed.
+constexpr int kTileQuadsMax = 2048;  // 8192 keys
+
+template <int D, int QG>
+__global__ __launch_bounds__(kAttThreads) void k_attend_mfma(AttendArgs A) {
+  constexpr int PIECES = D / 8;    // 16-byte pieces per row
+  constexpr int NS = D / 32;       // MFMA k-steps
+  constexpr int NVL = PIECES / 4;  // V loads per lane per 16-key group
+  constexpr int QPT = kTileQuadsMax / kAttThreads;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cache = blockIdx.y;
+  const int qg0 = blockIdx.z * QG;
+  const int nq = min(QG, A.QC - qg0);
+  const int64_t tile = blockIdx.x;
+  const int b = cache / A.H, h = cache % A.H;
+  const int64_t k_lo = tile * A.tile_keys;
+  const int64_t k_hi = min(A.n_tokens, k_lo + A.tile_keys);
+  const int nquads = (int)((k_hi - k_lo + 3) / 4);
+  const bool all = A.flags & 4u, sink = A.flags & 1u, last = A.flags & 2u;
+  const int64_t last_start = (int64_t)A.C * ((A.n_tokens - 1) / A.C);
+
+  __shared__ uint16_t e_quad[kTileQuadsMax];
+  __shared__ unsigned long long e_mask[kTileQuadsMax];
+  __shared__ int scan[kAttThreads];
+  __shared__ float p_lds[4][16][16];  // [wave][key in group][query]
+  __shared__ float sc_lds[4][16];
+  __shared__ float red[4][QG][D + 2];
+
+  // ---- phase 1: per-quad selection masks, compacted in key order
+  unsigned long long qmask[QPT];
+  int cnt = 0;
+  {
+    const uint32_t* srow[QG];
+#pragma unroll
+    for (int u = 0; u < QG; ++u)
+      srow[u] = A.sel1 ? A.sel1 + ((int64_t)cache * A.QC + qg0 + (u < nq ? u : 0)) * A.sel_words : nullptr;
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int qd = tid * QPT + i;
+      unsigned long long msk = 0ull;
+      if (qd < nquads) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int64_t key = k_lo + 4 * qd + kk;
+          if (key >= k_hi) break;
+          const bool forced = all || (sink && key == 0) || (last && key >= last_start);
+          const int64_t chunk = key / A.C;
+          const bool has_chunk = !all && chunk < A.n_chunks;
+#pragma unroll
+          for (int u = 0; u < QG; ++u) {
+            if (u >= nq) break;
+            bool s = forced;
+            if (!s && has_chunk) s = (srow[u][chunk >> 5] >> (chunk & 31)) & 1u;
+            if (s) msk |= 1ull << (u * 4 + kk);
+          }
+        }
+      }
+      qmask[i] = msk;
+      cnt += msk != 0ull;
+    }
+  }
+  scan[tid] = cnt;
+  __syncthreads();
+  for (int off = 1; off < kAttThreads; off <<= 1) {
+    const int add = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  const int n_ent = scan[kAttThreads - 1];
+  {
+    int pos = scan[tid] - cnt;
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      if (qmask[i]) {
+        e_quad[pos] = (uint16_t)(tid * QPT + i);
+        e_mask[pos] = qmask[i];
+        ++pos;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 2
+  const int r16 = lane & 15, kg = lane >> 4;
+  bf16x8 bq[NS];
+  {
+    const int qi = qg0 + r16;
+    if (r16 < nq) {
+      const int gq = qi / A.T, t = qi % A.T;
+      const bf16_t* qp = reinterpret_cast<const bf16_t*>(A.Q) + (int64_t)b * A.qsb + (int64_t)h * A.qsh +
+                         (int64_t)gq * A.qsg + (int64_t)t * A.qst;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) bq[s] = as_bf16x8(ld16(qp + (4 * s + kg) * 8));
+    } else {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) bq[s] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    }
+  }
+  const bf16_t* Kc = reinterpret_cast<const bf16_t*>(A.K) + (int64_t)b * A.sb + (int64_t)h * A.sh;
+  const bf16_t* Vc = reinterpret_cast<const bf16_t*>(A.V) + (int64_t)b * A.sb + (int64_t)h * A.sh;
+
+  const int n_groups = (n_ent + 3) / 4;
+  auto load_group = [&](int g, uint4* kf, uint4* vf) {
+    {
+      const int e = 4 * g + (r16 >> 2);
+      const int64_t key = e < n_ent ? k_lo + 4 * (int64_t)e_quad[e] + (r16 & 3) : k_hi;
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        kf[s] = key < k_hi ? ld16(Kc + key * A.st + (4 * s + kg) * 8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < NVL; ++u) {
+      const int pi = lane + 64 * u;
+      const int kq = pi / PIECES, pc = pi % PIECES;
+      const int e = 4 * g + (kq >> 2);
+      const int64_t key = e < n_ent ? k_lo + 4 * (int64_t)e_quad[e] + (kq & 3) : k_hi;
+      vf[u] = key < k_hi ? ld16(Vc + key * A.st + pc * 8) : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  float m = kNegInf, l = 0.f;  // softmax state of query r16 (MFMA layout)
+  float acc[QG][8];            // V accumulators of piece (lane % PIECES) (FMA layout)
+#pragma unroll
+  for (int u = 0; u < QG; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[u][e] = 0.f;
+
+  uint4 kf[NS], vf[NVL], kn[NS], vn[NVL];
+  if (wave < n_groups) load_group(wave, kf, vf);
+  const int rounds = (n_groups + 3) / 4;
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int g = rd * 4 + wave;
+    const bool live = g < n_groups;
+    if (g + 4 < n_groups) load_group(g + 4, kn, vn);
+    if (live) {
+      f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[s]), bq[s], z, 0, 0, 0);
+      // lane: keys 4*kg + i of the group (entry 4g + kg), query r16
+      const int e = 4 * g + kg;
+      const unsigned long long msk = (e < n_ent && r16 < QG) ? e_mask[e] >> (r16 * 4) : 0ull;
+      float zz[4];
+      float mb = kNegInf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        zz[i] = ((msk >> i) & 1ull) ? z[i] * A.inv_sqrt_d : kNegInf;
+        mb = fmaxf(mb, zz[i]);
+      }
+      mb = fmaxf(mb, __shfl_xor(mb, 16));
+      mb = fmaxf(mb, __shfl_xor(mb, 32));
+      const float mn = fmaxf(m, mb);
+      float sc = 1.f, ps = 0.f;
+      float pz[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pz[i] = 0.f;
+      if (mn != kNegInf) {
+        sc = __expf(m - mn);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pz[i] = __expf(zz[i] - mn);
+          ps += pz[i];
+        }
+      }
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);
+      l = l * sc + ps;
+      m = mn;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p_lds[wave][4 * kg + i][r16] = pz[i];
+      if (kg == 0) sc_lds[wave][r16] = sc;
+    }
+    __syncthreads();
+    if (live) {
+      float scq[QG];
+#pragma unroll
+      for (int u = 0; u < QG; ++u) scq[u] = sc_lds[wave][u];
+#pragma unroll
+      for (int u = 0; u < QG; ++u)
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc[u][x] *= scq[u];
+#pragma unroll
+      for (int v = 0; v < NVL; ++v) {
+        const int kq = (lane + 64 * v) / PIECES;
+        float vv[8];
+        unpack(vf[v], vv, bf16_t());
+#pragma unroll
+        for (int u = 0; u < QG; ++u) {
+          const float pw = p_lds[wave][kq][u];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) acc[u][x] += pw * vv[x];
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kf[s] = kn[s];
+#pragma unroll
+    for (int v = 0; v < NVL; ++v) vf[v] = vn[v];
+  }
+
+  // lanes sharing a piece hold partial V sums of different keys: add them
+#pragma unroll
+  for (int off = PIECES; off < 64; off <<= 1)
+#pragma unroll
+    for (int u = 0; u < QG; ++u)
+#pragma unroll
+      for (int x = 0; x < 8; ++x) acc[u][x] += __shfl_xor(acc[u][x], off);
+  if (lane < PIECES) {
+#pragma unroll
+    for (int u = 0; u < QG; ++u)
+#pragma unroll
+      for (int x = 0; x < 8; ++x) red[wave][u][lane * 8 + x] = acc[u][x];
+  }
+  if (kg == 0 && r16 < QG) {
+    red[wave][r16][D] = m;
+    red[wave][r16][D + 1] = l;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < QG * D; idx += kAttThreads) {
+    const int u = idx / D, d = idx % D;
+    if (u >= nq) continue;
+    float mm = kNegInf;
+    for (int w = 0; w < 4; ++w) mm = fmaxf(mm, red[w][u][D]);
+    float ll = 0.f, o = 0.f;
+    if (mm != kNegInf) {
+      for (int w = 0; w < 4; ++w) {
+        const float mw = red[w][u][D];
+        if (mw == kNegInf) continue;
+        const float f = __expf(mw - mm);
+        ll += red[w][u][D + 1] * f;
+        o += red[w][u][d] * f;
+      }
+    }
+    float* part = A.partial + (((int64_t)cache * A.QC + qg0 + u) * A.n_tiles + tile) * (D + 2);
+    if (d == 0) {
+      part[0] = mm;
+      part[1] = ll;
+    }
+    part[2 + d] = o;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(D) void k_combine(AttendArgs A) {
   const int64_t q = blockIdx.x;
@@ -225,19 +479,36 @@ __global__ __launch_bounds__(D) void k_combine(AttendArgs A) {
   if (d == 0 && A.lse) A.lse[q] = L > 0.f ? M + __logf(L) : kNegInf;
 }
 
+template <int D, int QG>
+void launch_mfma(const AttendArgs& a, int n_caches, hipStream_t s) {
+  dim3 grid((unsigned)a.n_tiles, (unsigned)n_caches, (unsigned)((a.QC + QG - 1) / QG));
+  hipLaunchKernelGGL((k_attend_mfma<D, QG>), grid, dim3(kAttThreads), 0, s, a);
+}
+
+template <int D>
+void launch_mfma_qg(const AttendArgs& a, int n_caches, hipStream_t s) {
+  if (a.QC <= 4)
+    launch_mfma<D, 4>(a, n_caches, s);
+  else if (a.QC <= 8)
+    launch_mfma<D, 8>(a, n_caches, s);
+  else
+    launch_mfma<D, 16>(a, n_caches, s);
+}
+
 }  // namespace
 
 hipError_t launch_attend(const AttendArgs& a, int dtype, int n_caches, Prof& prof) {
   const int64_t n_queries = (int64_t)n_caches * a.QC;
   hipStream_t s = prof.s;
-  dim3 grid((unsigned)a.n_tiles, (unsigned)n_caches, (unsigned)((a.QC + kQG - 1) / kQG));
+  if (a.tile_keys > 4 * kTileQuadsMax || a.tile_keys % 256) return hipErrorInvalidValue;
   prof.begin(ZHA_K_ATTEND, 0);
   if (dtype == 1) {
     if (a.D == 128)
-      hipLaunchKernelGGL((k_attend<bf16_t, 128>), grid, dim3(kAttThreads), 0, s, a);
+      launch_mfma_qg<128>(a, n_caches, s);
     else
-      hipLaunchKernelGGL((k_attend<bf16_t, 64>), grid, dim3(kAttThreads), 0, s, a);
+      launch_mfma_qg<64>(a, n_caches, s);
   } else {
+    dim3 grid((unsigned)a.n_tiles, (unsigned)n_caches, (unsigned)((a.QC + kQG - 1) / kQG));
     if (a.D == 128)
       hipLaunchKernelGGL((k_attend<float, 128>), grid, dim3(kAttThreads), 0, s, a);
     else

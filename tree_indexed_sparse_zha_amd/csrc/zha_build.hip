@@ -200,7 +200,29 @@ __global__ __launch_bounds__(64) void k_build_span(BuildArgs A) {
         const float inv = 1.f / ssum;
 #pragma unroll
         for (int v = 0; v < NV; ++v) acc[v] *= inv;
-        emit(1, (pos + sg) / C, L, acc);
+        if (geo.leaf_weights) {
+          // weights form: w_ji = exp(z_ji - L_j) and c_j = L_j - sum_i w_ji z_ji
+          // (= L_j - r_j . g_j / sqrt(d) with the unrounded g_j = sum_i w_ji k_i)
+          const int64_t nidx = (int64_t)cache * geo.node_cap[0] + (pos + sg) / C;
+          float wz = 0.f;
+          float* wb = reinterpret_cast<float*>(A.tree + geo.g_off[0]) + (nidx * R + j) * C;
+          for (int i0 = 0; i0 < seg; i0 += 4) {
+            float wv[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              const float z = zs[j][sg + i0 + x];
+              wv[x] = __expf(z - m) * inv;
+              wz += wv[x] * z;
+            }
+            if (j < R && dg == 0) *reinterpret_cast<float4*>(wb + i0) = make_float4(wv[0], wv[1], wv[2], wv[3]);
+          }
+          if (j < R && dg == 0) {
+            reinterpret_cast<float*>(A.tree + geo.L_off[0])[nidx * R + j] = L;
+            reinterpret_cast<float*>(A.tree + geo.c_off[0])[nidx * R + j] = L - wz;
+          }
+        } else {
+          emit(1, (pos + sg) / C, L, acc);
+        }
         if constexpr (NA > 0) absorb(am[0], as[0], aacc[0], used[0], L, 1.f, acc, NV);
       } else {
         absorb(am[0], as[0], aacc[0], used[0], m, ssum, acc, NV);

@@ -16,13 +16,13 @@ struct Prof {
   hipStream_t s;
   void begin(int id, int level) {
     if (p && p->n_used < p->n_pairs) {
-      hipEventRecord(static_cast<hipEvent_t>(p->events[2 * p->n_used]), s);
+      (void)hipEventRecord(static_cast<hipEvent_t>(p->events[2 * p->n_used]), s);
       p->kernel[p->n_used] = id * 16 + level;
     }
   }
   void end() {
     if (!p) return;
-    if (p->n_used < p->n_pairs) hipEventRecord(static_cast<hipEvent_t>(p->events[2 * p->n_used + 1]), s);
+    if (p->n_used < p->n_pairs) (void)hipEventRecord(static_cast<hipEvent_t>(p->events[2 * p->n_used + 1]), s);
     ++p->n_used;
   }
 };
@@ -38,6 +38,7 @@ struct TreeGeom {
   int esize;  // bytes per K/V/g element (2 = bf16, 4 = fp32)
   int H;
   int caches;
+  int leaf_weights;  // level 1 stores softmax weights instead of mean keys
   int64_t node_cap[kMaxLevels];
   int64_t g_off[kMaxLevels];
   int64_t L_off[kMaxLevels];
@@ -68,13 +69,19 @@ struct ScoreArgs {
   int64_t qsb, qsh, qsg, qst;
   const uint32_t* sel_parent;  // parent level bitsets or nullptr (top level)
   int64_t parent_words;        // words per query row of sel_parent
-  float* score;                // [n_queries][node_cap] for this level
+  float* score;                // [n_queries][score_stride] for this level
+  int64_t score_stride;
+  uint32_t* keyrange;          // [n_queries][4]: max key, min key, candidate count, 0
   float inv_sqrt_d;
+  int leaf_weights;            // level 1 in the weights form: g holds w [R][C] fp32
+  const void* K;               // keys (weights form only)
+  int64_t ksb, ksh, kst;
 };
 
 struct SelectArgs {
-  const float* score;  // [n_queries][node_cap]
-  int64_t node_cap;
+  const float* score;  // [n_queries][score_stride]
+  int64_t score_stride;
+  const uint32_t* keyrange;  // written by the score kernel of the same level
   int64_t n_nodes;
   uint32_t* sel;       // [n_queries][words]
   int64_t words;
@@ -104,6 +111,7 @@ struct AttendArgs {
 };
 
 hipError_t launch_build(const BuildArgs& a, int dtype, Prof& prof);
+hipError_t launch_route_init(uint32_t* keyrange, int64_t n, Prof& prof);
 hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dtype, int n_caches,
                               int level, Prof& prof);
 hipError_t launch_attend(const AttendArgs& a, int dtype, int n_caches, Prof& prof);

@@ -21,10 +21,11 @@
 //
 // Select design.  One workgroup per query.  Masses are fixed-point integers
 // round(exp(s - max) * 2^shift) so every sum is exact and order-independent
-// (deterministic without float atomics).  The cut is found by a three-pass
-// radix select on the order key of the score (11 + 11 + 10 bits) over
-// mass-weighted histograms in LDS, then ties at the cut key are resolved by
-// node id.  The kept set is written as a bitset.
+// (deterministic without float atomics).  The cut is found by a radix select
+// on the order key of the score (digits of up to 11 bits below the
+// candidates' common key prefix) over mass-weighted histograms in LDS, then
+// ties at the cut key are resolved by node id.  The kept set is written as a
+// bitset.
 #include <climits>
 
 #include "zha_device.h"
@@ -44,6 +45,33 @@ struct SelStats {  // mirrors zha_select_stats
   unsigned long long mass_kept;
 };
 static_assert(sizeof(SelStats) == 40, "stats layout");
+
+// Folds one wave's candidates (flag c, key k per lane) into a query's
+// [max key, min key, count] record.
+__device__ __forceinline__ void publish_range(uint32_t* kr, bool c, uint32_t k) {
+  const unsigned long long bal = __ballot(c);
+  if (bal == 0ull) return;
+  uint32_t kmax = c ? k : 0u, kmin = c ? k : 0xffffffffu;
+  for (int o = 1; o < 64; o <<= 1) {
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    atomicMax(&kr[0], kmax);
+    atomicMin(&kr[1], kmin);
+    atomicAdd(&kr[2], (uint32_t)__popcll(bal));
+  }
+}
+
+__global__ void k_route_init(uint32_t* kr, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    kr[4 * i + 0] = 0u;
+    kr[4 * i + 1] = 0xffffffffu;
+    kr[4 * i + 2] = 0u;
+    kr[4 * i + 3] = 0u;
+  }
+}
 
 // ---------------------------------------------------------------------------
 // score, bf16, MFMA
@@ -132,7 +160,153 @@ __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs A) {
   for (int idx = tid; idx < nq * TILE; idx += 256) {
     const int q = idx / TILE, x = idx % TILE;
     const int64_t mm = n0 + x;
-    if (mm < A.n_nodes) A.score[((int64_t)cache * A.QC + qg0 + q) * A.node_cap + mm] = sc[q][x];
+    if (mm < A.n_nodes) A.score[((int64_t)cache * A.QC + qg0 + q) * A.score_stride + mm] = sc[q][x];
+  }
+  // candidate key range and count of this tile, per query (integer atomics)
+  for (int q = wave; q < nq; q += 4) {
+    const float v = sc[q][lane];
+    const bool c = n0 + lane < A.n_nodes && v > kNegInf;
+    publish_range(A.keyrange + ((int64_t)cache * A.QC + qg0 + q) * 4, c, order_key(v));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// score of level-1 nodes in the weights form (bf16, C in {4, 8, 16})
+//
+// s(q, chunk) = max_j [ c_j + sum_i w_ji (q . k_i) / sqrt(d) ]: the chunk's
+// raw keys go through the MFMA (A = 16 keys, B = up to 16 queries) exactly
+// as in attention, then each lane (plane j, 4 keys) folds its four logits
+// with its four weights and the planes are maxed over 16 lanes.  A tile is
+// 256 keys; every wave takes 4 groups of 16 keys and skips the groups none of
+// whose chunks is a candidate of any query.
+
+template <int D, int C>
+__global__ __launch_bounds__(256) void k_score_leafw(ScoreArgs A) {
+  constexpr int NS = D / 32;
+  constexpr int KT = 256;       // keys per tile
+  constexpr int NCH = KT / C;   // chunks per tile
+  constexpr int CPG = 16 / C;   // chunks per 16-key group
+  constexpr int GPW = 4;        // groups per wave
+  constexpr int PARTS = C / 4;  // lanes (of 4 keys) per chunk
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cache = blockIdx.y;
+  const int qg0 = blockIdx.z * 16;
+  const int nq = min(16, A.QC - qg0);
+  const int64_t k0 = (int64_t)blockIdx.x * KT;
+  const int64_t m0 = k0 / C;
+  const int R = A.R;
+  const int qn = lane & 15, kg = lane >> 4;
+  const int64_t n_keys = A.n_nodes * C;  // keys of complete chunks
+  __shared__ float sc[16][NCH + 1];
+  __shared__ float zl[4][16][17];  // [wave][query][key of group]
+
+  bf16x8 bq[NS];
+  {
+    const int qi = qg0 + qn;
+    if (qn < nq) {
+      const int b = cache / A.H, h = cache % A.H, gq = qi / A.T, t = qi % A.T;
+      const bf16_t* qp = reinterpret_cast<const bf16_t*>(A.Q) + (int64_t)b * A.qsb +
+                         (int64_t)h * A.qsh + (int64_t)gq * A.qsg + (int64_t)t * A.qst;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) bq[s] = as_bf16x8(ld16(qp + (4 * s + kg) * 8));
+    } else {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) bq[s] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    }
+  }
+  const int b = cache / A.H, h = cache % A.H;
+  const bf16_t* Kc = reinterpret_cast<const bf16_t*>(A.K) + (int64_t)b * A.ksb + (int64_t)h * A.ksh;
+  const float* wcache = reinterpret_cast<const float*>(A.g) + (int64_t)cache * A.node_cap * R * C;
+  const float* ccache = A.c + (int64_t)cache * A.node_cap * R;
+  const uint32_t* prow =
+      A.sel_parent ? A.sel_parent + ((int64_t)cache * A.QC + qg0 + qn) * A.parent_words : nullptr;
+
+  // candidate flags of every chunk of this wave's groups, one ballot each:
+  // bit q of cmask[gi][cc] = chunk cc of group gi is a candidate of query q
+  unsigned long long cmask[GPW][CPG];
+  bool gany[GPW];
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
+    gany[gi] = false;
+#pragma unroll
+    for (int cc = 0; cc < CPG; ++cc) {
+      const int64_t m = m0 + (wave * GPW + gi) * CPG + cc;
+      bool ok = m < A.n_nodes && qn < nq;
+      if (ok && prow) {
+        const int64_t par = m / A.C;
+        ok = (prow[par >> 5] >> (par & 31)) & 1u;
+      }
+      cmask[gi][cc] = __ballot(ok && kg == 0);
+      gany[gi] = gany[gi] || cmask[gi][cc] != 0ull;
+    }
+  }
+  // all loads of the wave up front: K rows (MFMA A operand), weights, offsets
+  const int j = qn, ccl = kg / PARTS, part = kg % PARTS;  // lane role after the MFMA
+  uint4 kf[GPW][NS];
+  float4 wv[GPW];
+  float cj[GPW];
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
+    const int g = wave * GPW + gi;
+    const int64_t key = k0 + g * 16 + qn;
+    const int64_t m = m0 + g * CPG + ccl;
+    const bool live = gany[gi];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      kf[gi][s] = live && key < n_keys ? ld16(Kc + key * A.kst + (4 * s + kg) * 8) : make_uint4(0, 0, 0, 0);
+    const bool wok = live && m < A.n_nodes && j < R;
+    wv[gi] = wok ? *reinterpret_cast<const float4*>(wcache + (m * R + j) * C + part * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    cj[gi] = wok ? ccache[m * R + j] : kNegInf;
+  }
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
+    const int g = wave * GPW + gi;
+    if (!gany[gi]) {
+      if (lane < 16)
+#pragma unroll
+        for (int cc = 0; cc < CPG; ++cc) sc[qn][g * CPG + cc] = kNegInf;
+      continue;
+    }
+    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[gi][s]), bq[s], z, 0, 0, 0);
+    // lane holds the logits of keys 4*kg .. 4*kg+3 of the group for query qn
+#pragma unroll
+    for (int i = 0; i < 4; ++i) zl[wave][qn][4 * kg + i] = z[i] * A.inv_sqrt_d;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // lane (plane j, 4-key part kg of chunk ccl): planes folded, then maxed over j
+    unsigned long long cm = 0ull;
+#pragma unroll
+    for (int cc = 0; cc < CPG; ++cc)
+      if (cc == ccl) cm = cmask[gi][cc];
+    for (int q = 0; q < nq; ++q) {
+      const float4 zq = *reinterpret_cast<const float4*>(&zl[wave][q][4 * kg]);
+      float v = wv[gi].x * zq.x + wv[gi].y * zq.y + wv[gi].z * zq.z + wv[gi].w * zq.w;
+#pragma unroll
+      for (int o = 16; o < 16 * PARTS; o <<= 1) v += __shfl_xor(v, o);
+      v += cj[gi];  // -inf for planes j >= R
+      v = wave_max_xor(v, 1, 16);
+      if (j == 0 && part == 0) sc[q][g * CPG + ccl] = ((cm >> q) & 1ull) ? v : kNegInf;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  __syncthreads();
+  for (int idx = tid; idx < nq * NCH; idx += 256) {
+    const int q = idx / NCH, x = idx % NCH;
+    const int64_t mm = m0 + x;
+    if (mm < A.n_nodes) A.score[((int64_t)cache * A.QC + qg0 + q) * A.score_stride + mm] = sc[q][x];
+  }
+  for (int q = wave; q < nq; q += 4) {
+    for (int x0 = 0; x0 < NCH; x0 += 64) {
+      const int x = x0 + lane;
+      const float v = x < NCH ? sc[q][x] : kNegInf;
+      const bool c = x < NCH && m0 + x < A.n_nodes && v > kNegInf;
+      publish_range(A.keyrange + ((int64_t)cache * A.QC + qg0 + q) * 4, c, order_key(v));
+    }
   }
 }
 
@@ -185,14 +359,22 @@ __global__ __launch_bounds__(256) void k_score_generic(ScoreArgs A) {
       v = j < R ? cj + part * A.inv_sqrt_d : kNegInf;
       v = wave_max_xor(v, 1, 16);
     }
-    if (lane == 0) A.score[qg * A.node_cap + m] = v;
+    if (lane == 0) {
+      A.score[qg * A.score_stride + m] = v;
+      if (v > kNegInf) {
+        uint32_t* kr = A.keyrange + qg * 4;
+        atomicMax(&kr[0], order_key(v));
+        atomicMin(&kr[1], order_key(v));
+        atomicAdd(&kr[2], 1u);
+      }
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // select
 
-constexpr int kSelThreads = 256;
+constexpr int kSelThreads = 1024;
 
 __device__ __forceinline__ unsigned long long fixed_mass(float s, float mx, double scale) {
   return (unsigned long long)llrint((double)expf(s - mx) * scale);
@@ -215,79 +397,83 @@ __device__ unsigned long long block_sum_u64(unsigned long long v, unsigned long 
 // Finds the bin b (scanning from the highest bin down) whose mass interval
 // (above, above + hist[b]] contains P, where `above` starts at *A_io and
 // accumulates the bins above b.  Returns b and updates *A_io to the mass
-// strictly above bin b.
+// strictly above bin b.  nbins is a power of two.
 __device__ int find_bin(const unsigned long long* hist, int nbins, unsigned long long P,
                         unsigned long long* A_io, unsigned long long* red, int* sh_bin,
                         unsigned long long* sh_above) {
   const int tid = threadIdx.x;
-  const int per = nbins / kSelThreads;
-  // thread t owns bins [t*per, (t+1)*per); suffix sums over threads
+  const int per = nbins >= kSelThreads ? nbins / kSelThreads : 1;
+  const int b0 = tid * per;
+  const int nb = b0 < nbins ? per : 0;
   unsigned long long mine = 0;
-  for (int i = 0; i < per; ++i) mine += hist[tid * per + i];
+  for (int i = 0; i < nb; ++i) mine += hist[b0 + i];
   red[tid] = mine;
   __syncthreads();
-  // inclusive suffix scan (Hillis-Steele) over 256 values
+  // inclusive suffix scan (Hillis-Steele) over the threads' sums
   for (int off = 1; off < kSelThreads; off <<= 1) {
-    unsigned long long add = (tid + off < kSelThreads) ? red[tid + off] : 0ull;
+    const unsigned long long add = (tid + off < kSelThreads) ? red[tid + off] : 0ull;
     __syncthreads();
     red[tid] += add;
     __syncthreads();
   }
-  unsigned long long cum = *A_io + (red[tid] - mine);  // mass of bins above this thread's range
+  unsigned long long cum = *A_io + (red[tid] - mine);  // mass of the bins above this thread's range
   if (tid == 0) *sh_bin = -1;
   __syncthreads();
-  for (int i = per - 1; i >= 0; --i) {
-    const int bin = tid * per + i;
-    const unsigned long long h = hist[bin];
+  for (int i = nb - 1; i >= 0; --i) {
+    const unsigned long long h = hist[b0 + i];
     if (cum < P && P <= cum + h) {
-      *sh_bin = bin;
+      *sh_bin = b0 + i;
       *sh_above = cum;
     }
     cum += h;
   }
   __syncthreads();
   const int b = *sh_bin;
-  *A_io = *sh_above;
+  if (b >= 0) *A_io = *sh_above;
   __syncthreads();
   return b;
 }
 
+// Radix select on the order key.  Candidate keys share their bits above the
+// highest bit where the largest and smallest key differ, so the digits
+// (11 bits at most, from the top down) start below that common prefix: every
+// histogram then spreads over the candidates' actual range instead of piling
+// into the few bins a narrow score range occupies.
 __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs A) {
   const int tid = threadIdx.x;
   const int64_t q = blockIdx.x;
-  const float* row = A.score + q * A.node_cap;
+  const float* row = A.score + q * A.score_stride;  // 16-byte aligned rows
+  const float4* row4 = reinterpret_cast<const float4*>(row);
   const int64_t n = A.n_nodes;
+  const int64_t n4 = (n + 3) / 4;
   uint32_t* srow = A.sel + q * A.words;
   SelStats* st = reinterpret_cast<SelStats*>(A.stats) + q;
   const int64_t nwords = (n + 31) / 32;
 
   __shared__ unsigned long long hist[2048];
   __shared__ unsigned long long red[kSelThreads];
-  __shared__ float redf[kSelThreads];
   __shared__ int sh_bin;
   __shared__ unsigned long long sh_above;
   __shared__ int sh_cut;
 
-  // pass 0: max score and candidate count
-  float mx = kNegInf;
-  unsigned long long cnt = 0;
-  for (int64_t i = tid; i < n; i += kSelThreads) {
-    const float s = row[i];
-    if (s > kNegInf) {
-      ++cnt;
-      mx = fmaxf(mx, s);
+  // Visits every candidate score of the row (index, score, key): float4
+  // loads, two in flight per thread.
+  auto for_each = [&](auto&& fn) {
+    for (int64_t b = tid; b < n4; b += 2 * kSelThreads) {
+      const float4 v0 = row4[b];
+      const float4 v1 = b + kSelThreads < n4 ? row4[b + kSelThreads] : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+      const float a[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int64_t i = (c < 4 ? b : b + kSelThreads) * 4 + (c & 3);
+        if (i < n && a[c] > kNegInf) fn(i, a[c], order_key(a[c]));
+      }
     }
-  }
-  redf[tid] = mx;
-  __syncthreads();
-  for (int off = kSelThreads / 2; off > 0; off >>= 1) {
-    if (tid < off) redf[tid] = fmaxf(redf[tid], redf[tid + off]);
-    __syncthreads();
-  }
-  mx = redf[0];
-  __syncthreads();
-  const unsigned long long ncand = block_sum_u64(cnt, red);
+  };
 
+  const uint32_t* kr = A.keyrange + q * 4;
+  const uint32_t kmax = kr[0], kmin = kr[1];
+  const unsigned long long ncand = kr[2];
   if (ncand == 0) {
     for (int64_t w = tid; w < nwords; w += kSelThreads) srow[w] = 0u;
     if (tid == 0) {
@@ -296,65 +482,62 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs A) {
     }
     return;
   }
+  const float mx = key_to_float(kmax);
   int lg = 0;
   while ((1ll << lg) < n) ++lg;
   const int shift = 62 - lg;
   const double scale = ldexp(1.0, shift);
 
-  // pass 1: total mass and histogram of the top 11 key bits
-  for (int i = tid; i < 2048; i += kSelThreads) hist[i] = 0ull;
-  __syncthreads();
-  unsigned long long part = 0;
-  for (int64_t i = tid; i < n; i += kSelThreads) {
-    const float s = row[i];
-    if (s > kNegInf) {
-      const unsigned long long mm = fixed_mass(s, mx, scale);
-      part += mm;
-      atomicAdd(&hist[order_key(s) >> 21], mm);
-    }
-  }
-  __syncthreads();
-  const unsigned long long M = block_sum_u64(part, red);
-
+  // digit passes; the first one also sums the total mass M
+  const int hb = kmax == kmin ? 0 : 32 - __clz(kmax ^ kmin);  // low bits that differ
+  uint32_t want = hb >= 32 ? 0u : (kmax >> hb);              // bits above the current digit
+  int lo = hb;
+  unsigned long long M = 0, P = 0, above = 0, h_tau = 0;
+  bool first = true;
   uint32_t tau = 0u;
   int cut_id = INT_MAX;
+  do {
+    const int w = lo < 11 ? lo : 11;
+    const int nb = 1 << w;
+    const int top = lo;  // bits [top, 32) must equal `want`
+    lo -= w;
+    for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0ull;
+    __syncthreads();
+    unsigned long long part = 0;
+    const bool fst = first;
+    for_each([&](int64_t i, float s, uint32_t k) {
+      const bool match = top >= 32 || (k >> top) == want;
+      if (!fst && !match) return;
+      const unsigned long long mm = fixed_mass(s, mx, scale);
+      if (fst) part += mm;
+      if (match && w > 0) atomicAdd(&hist[(k >> lo) & (uint32_t)(nb - 1)], mm);
+    });
+    __syncthreads();
+    if (first) {
+      M = block_sum_u64(part, red);
+      first = false;
+      if (A.keep_all) break;
+      P = (unsigned long long)ceil((double)A.p * (double)M);
+      if (P < 1ull) P = 1ull;
+      if (P > M) P = M;
+      if (w == 0) {  // every candidate has the same key
+        want = kmax;
+        h_tau = M;
+        break;
+      }
+    }
+    const int bsel = find_bin(hist, nb, P, &above, red, &sh_bin, &sh_above);
+    want = (w >= 32 ? 0u : (want << w)) | (uint32_t)bsel;
+    h_tau = hist[bsel];
+    __syncthreads();
+  } while (lo > 0);
+
   if (!A.keep_all) {
-    unsigned long long P = (unsigned long long)ceil((double)A.p * (double)M);
-    if (P < 1ull) P = 1ull;
-    if (P > M) P = M;
-    unsigned long long above = 0ull;
-    const int b1 = find_bin(hist, 2048, P, &above, red, &sh_bin, &sh_above);
-    // pass 2: next 11 bits inside bin b1
-    for (int i = tid; i < 2048; i += kSelThreads) hist[i] = 0ull;
-    __syncthreads();
-    for (int64_t i = tid; i < n; i += kSelThreads) {
-      const float s = row[i];
-      if (s > kNegInf) {
-        const uint32_t k = order_key(s);
-        if ((int)(k >> 21) == b1) atomicAdd(&hist[(k >> 10) & 2047u], fixed_mass(s, mx, scale));
-      }
-    }
-    __syncthreads();
-    const int b2 = find_bin(hist, 2048, P, &above, red, &sh_bin, &sh_above);
-    // pass 3: last 10 bits
-    const uint32_t hi22 = ((uint32_t)b1 << 11) | (uint32_t)b2;
-    for (int i = tid; i < 2048; i += kSelThreads) hist[i] = 0ull;
-    __syncthreads();
-    for (int64_t i = tid; i < n; i += kSelThreads) {
-      const float s = row[i];
-      if (s > kNegInf) {
-        const uint32_t k = order_key(s);
-        if ((k >> 10) == hi22) atomicAdd(&hist[k & 1023u], fixed_mass(s, mx, scale));
-      }
-    }
-    __syncthreads();
-    const int b3 = find_bin(hist, 1024, P, &above, red, &sh_bin, &sh_above);
-    tau = (hi22 << 10) | (uint32_t)b3;
+    tau = want;
     // ties at tau all carry the same mass
     const unsigned long long m_tau = fixed_mass(key_to_float(tau), mx, scale);
-    const unsigned long long n_tau = hist[b3] / m_tau;
-    const unsigned long long k_tie = (P - above + m_tau - 1ull) / m_tau;
-    __syncthreads();
+    const unsigned long long n_tau = m_tau ? h_tau / m_tau : 0ull;
+    const unsigned long long k_tie = m_tau ? (P - above + m_tau - 1ull) / m_tau : n_tau;
     if (k_tie < n_tau) {
       // the k_tie-th smallest id among the ties is the last one kept
       unsigned long long need = k_tie;
@@ -379,19 +562,30 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs A) {
     }
   }
 
-  // pass 5: bitset of kept candidates
+  // bitset of kept candidates: one word (8 float4 loads) per thread step
   unsigned long long kept = 0, kmass = 0;
   for (int64_t w = tid; w < nwords; w += kSelThreads) {
     uint32_t bits = 0u;
-    for (int bb = 0; bb < 32; ++bb) {
-      const int64_t i = w * 32 + bb;
-      if (i >= n) break;
-      const float s = row[i];
-      if (s > kNegInf) {
-        const uint32_t k = order_key(s);
-        if (k > tau || (k == tau && i < (int64_t)cut_id)) {
-          bits |= 1u << bb;
-          kmass += fixed_mass(s, mx, scale);
+    float4 v[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int64_t b4 = w * 8 + c;
+      v[c] = b4 < n4 ? row4[b4] : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float a[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int bb = c * 4 + e;
+        const int64_t i = w * 32 + bb;
+        const float s = a[e];
+        if (i < n && s > kNegInf) {
+          const uint32_t k = order_key(s);
+          if (k > tau || (k == tau && i < (int64_t)cut_id)) {
+            bits |= 1u << bb;
+            kmass += fixed_mass(s, mx, scale);
+          }
         }
       }
     }
@@ -416,13 +610,32 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs A) {
 
 }  // namespace
 
+hipError_t launch_route_init(uint32_t* keyrange, int64_t n, Prof& prof) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_route_init, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, prof.s, keyrange, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dtype, int n_caches,
                               int level, Prof& prof) {
   const int64_t n_queries = (int64_t)n_caches * sa.QC;
   hipStream_t s = prof.s;
   if (sa.n_nodes > 0) {
     prof.begin(ZHA_K_SCORE, level);
-    if (dtype == 1) {
+    if (sa.leaf_weights) {
+      dim3 grid((unsigned)((sa.n_nodes * sa.C + 255) / 256), (unsigned)n_caches, (unsigned)((sa.QC + 15) / 16));
+#define ZHA_LW(DD, CC) hipLaunchKernelGGL((k_score_leafw<DD, CC>), grid, dim3(256), 0, s, sa)
+      if (sa.D == 128) {
+        if (sa.C == 4) ZHA_LW(128, 4);
+        else if (sa.C == 8) ZHA_LW(128, 8);
+        else ZHA_LW(128, 16);
+      } else {
+        if (sa.C == 4) ZHA_LW(64, 4);
+        else if (sa.C == 8) ZHA_LW(64, 8);
+        else ZHA_LW(64, 16);
+      }
+#undef ZHA_LW
+    } else if (dtype == 1) {
       dim3 grid((unsigned)((sa.n_nodes + 63) / 64), (unsigned)n_caches, (unsigned)((sa.QC + 15) / 16));
       if (sa.D == 128)
         hipLaunchKernelGGL(k_score_bf16<128>, grid, dim3(256), 0, s, sa);

@@ -118,7 +118,7 @@ WORKLOADS: Dict[str, Workload] = {
         Workload(1, "deep32k", 1, 8, 4, 128, "bf16", 32768, 4, 6, 16, (0.95,), 64, 512, 1, 0),
         Workload(2, "wide256k", 4, 8, 4, 128, "bf16", 262144, 256, 1, 16, (0.95,), 1, 4096, 1, 64),
         Workload(
-            3, "deep1m", 8, 8, 4, 128, "bf16", 1048576, 4, 6, 16, (0.9, 0.95, 0.99), 1, 1024, 1, 127,
+            3, "deep1m", 8, 8, 4, 128, "bf16", 1048576, 4, 6, 16, (0.95, 0.9, 0.99), 1, 1024, 1, 127,
             append_tokens=4096,
         ),
         Workload(4, "deep10m", 2, 2, 4, 128, "bf16", 10485760, 4, 6, 16, (0.95,), 1, 10240, 1, 127),

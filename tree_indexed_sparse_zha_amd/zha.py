@@ -28,6 +28,7 @@ ZHA_OK, ZHA_ERR_NULL, ZHA_ERR_ARG, ZHA_ERR_UNSUPPORTED, ZHA_ERR_CAPACITY, ZHA_ER
 )
 ZHA_F32, ZHA_BF16 = 0, 1
 ZHA_SINK, ZHA_LAST_CHUNK, ZHA_ALL_KEYS = 1, 2, 4
+ZHA_LEAF_MEAN, ZHA_LEAF_WEIGHTS = 0, 1
 MAX_LEVELS = 8
 
 
@@ -47,6 +48,7 @@ class Config(ct.Structure):
         ("chunk", ct.c_int32),
         ("levels", ct.c_int32),
         ("kv_dtype", ct.c_int32),
+        ("leaf_form", ct.c_int32),
         ("capacity_tokens", ct.c_int64),
     ]
 
@@ -59,7 +61,7 @@ class TreeLayout(ct.Structure):
         ("g_offset", ct.c_int64 * MAX_LEVELS),
         ("L_offset", ct.c_int64 * MAX_LEVELS),
         ("c_offset", ct.c_int64 * MAX_LEVELS),
-        ("g_node_bytes", ct.c_int64),
+        ("g_bytes", ct.c_int64 * MAX_LEVELS),
         ("total_bytes", ct.c_int64),
     ]
 
@@ -72,6 +74,7 @@ class RouteLayout(ct.Structure):
         ("words", ct.c_int64 * MAX_LEVELS),
         ("sel_offset", ct.c_int64 * MAX_LEVELS),
         ("score_offset", ct.c_int64 * MAX_LEVELS),
+        ("score_stride", ct.c_int64 * MAX_LEVELS),
         ("stats_offset", ct.c_int64 * MAX_LEVELS),
         ("sel_words_total", ct.c_int64),
         ("score_floats_total", ct.c_int64),
@@ -169,7 +172,7 @@ def load(path: str = LIB_PATH) -> ct.CDLL:
         "zha_attend_workspace_bytes": (I64, [cfgp, I32]),
         "zha_build": (ct.c_int, [cfgp, P, i64p, I64, P, P, P, P]),
         "zha_append": (ct.c_int, [cfgp, P, i64p, I64, I64, P, P, P, P]),
-        "zha_route": (ct.c_int, [cfgp, P, I64, P, i64p, I32, F, P, P, P, P, I64, P, P]),
+        "zha_route": (ct.c_int, [cfgp, P, I64, P, i64p, I32, F, P, i64p, P, P, P, P, I64, P, P]),
         "zha_attend": (ct.c_int, [cfgp, P, i64p, I32, P, P, i64p, I64, P, I64, ct.c_uint32, P, P, P, I64, P, P]),
         "zha_dense_decode": (ct.c_int, [cfgp, P, i64p, I32, P, P, i64p, I64, P, P, P, I64, P, P]),
     }
@@ -217,6 +220,7 @@ class ZhaConfig:
     levels: int
     dtype: str  # "f32" | "bf16"
     capacity: int
+    leaf_form: str = "mean"  # "mean" | "weights"
 
     def c(self) -> Config:
         return Config(
@@ -228,6 +232,7 @@ class ZhaConfig:
             self.chunk,
             self.levels,
             ZHA_BF16 if self.dtype == "bf16" else ZHA_F32,
+            ZHA_LEAF_WEIGHTS if self.leaf_form == "weights" else ZHA_LEAF_MEAN,
             self.capacity,
         )
 
@@ -316,9 +321,10 @@ def alloc_route(cfg: ZhaConfig, T: int, device="cuda") -> RouteBuffers:
 
 
 def route(cfg: ZhaConfig, tree: torch.Tensor, n_tokens: int, Q: torch.Tensor, T: int, p: float, buf: RouteBuffers,
-          ev=None):
+          ev=None, K: Optional[torch.Tensor] = None):
     c = cfg.c()
     qs = _i64(*_elem_strides(Q, 4))
+    ks = _i64(*_elem_strides(K, 3)) if K is not None else None
     _check(
         load().zha_route(
             ct.byref(c),
@@ -328,6 +334,8 @@ def route(cfg: ZhaConfig, tree: torch.Tensor, n_tokens: int, Q: torch.Tensor, T:
             qs,
             int(T),
             float(p),
+            _ptr(K),
+            ks,
             _ptr(buf.sel),
             _ptr(buf.score),
             _ptr(buf.stats),
@@ -418,13 +426,17 @@ def read_level(cfg: ZhaConfig, tree: torch.Tensor, level: int, n_nodes: Optional
     R, d, E = cfg.n_ref, cfg.head_dim, 16 // cfg.esize
     caches = cfg.n_caches
     gb = int(tl.g_offset[i])
+    Lb, cb = int(tl.L_offset[i]), int(tl.c_offset[i])
+    L = tree[Lb : Lb + caches * cap * R * 4].view(torch.float32).view(caches, cap, R)[:, :n]
+    c = tree[cb : cb + caches * cap * R * 4].view(torch.float32).view(caches, cap, R)[:, :n]
+    if level == 1 and cfg.leaf_form == "weights":
+        C = cfg.chunk
+        w = tree[gb : gb + caches * cap * R * C * 4].view(torch.float32).view(caches, cap, R, C)[:, :n]
+        return {"w": w, "L": L, "c": c}
     graw = tree[gb : gb + caches * cap * R * d * cfg.esize].view(cfg.torch_dtype).view(caches, cap, -1)[:, :n]
     pieces = d // E
     # element offset ((k//4)*4*R + (k%4)*R + j)*E + e  ->  [k//4][k%4][j][e]
     g = graw.reshape(caches, n, pieces // 4, 4, R, E).permute(0, 1, 4, 2, 3, 5).reshape(caches, n, R, d)
-    Lb, cb = int(tl.L_offset[i]), int(tl.c_offset[i])
-    L = tree[Lb : Lb + caches * cap * R * 4].view(torch.float32).view(caches, cap, R)[:, :n]
-    c = tree[cb : cb + caches * cap * R * 4].view(torch.float32).view(caches, cap, R)[:, :n]
     return {"g": g, "L": L, "c": c}
 
 
@@ -443,6 +455,14 @@ def pack_bits(mask: torch.Tensor, words: int) -> torch.Tensor:
     w = (m << torch.arange(32, device=m.device)).sum(-1)
     w = torch.where(w >= 2**31, w - 2**32, w)
     return w.to(torch.int32)
+
+
+def level_scores(buf: RouteBuffers, level: int) -> torch.Tensor:
+    """Score rows of a level, [n_queries, score_stride] (a view into buf.score)."""
+    rl = buf.layout
+    nq, st = int(rl.n_queries), int(rl.score_stride[level - 1])
+    off = int(rl.score_offset[level - 1])
+    return buf.score[off : off + nq * st].view(nq, st)
 
 
 def stats_records(buf: RouteBuffers, level: int) -> List[SelectStats]:
