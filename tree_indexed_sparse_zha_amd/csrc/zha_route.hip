@@ -80,6 +80,7 @@ template <int D>
 __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs A) {
   constexpr int NS = D / 32;  // MFMA k-steps of 32 bf16
   constexpr int TILE = 64;
+  constexpr int NB = 4;       // nodes per batch
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cache = blockIdx.y;
   const int qg0 = blockIdx.z * 16;
@@ -106,44 +107,67 @@ __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs A) {
   const int64_t gnode = (int64_t)R * D * 2;
   const char* gcache = A.g + (int64_t)cache * A.node_cap * gnode;
   const float* ccache = A.c + (int64_t)cache * A.node_cap * R;
-  const uint32_t* prow =
-      A.sel_parent ? A.sel_parent + ((int64_t)cache * A.QC + qg0 + qn) * A.parent_words : nullptr;
   const int jrow = lane & 15;
 
-  for (int u = 0; u < 16; u += 4) {
-    bool cand[4], any[4];
-    int64_t m[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      m[k] = n0 + wave * 16 + u + k;
-      bool ok = m[k] < A.n_nodes && qn < nq;
-      if (ok && prow) {
-        const int64_t par = m[k] / A.C;
-        ok = (prow[par >> 5] >> (par & 31)) & 1u;
-      }
-      cand[k] = ok;
-      any[k] = __ballot(ok) != 0;
-    }
-    uint4 af[4][NS];
-    float cv[4][4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (any[k]) {
-        const char* gn = gcache + m[k] * gnode;
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-          af[k][s] = jrow < R ? ld16(gn + ((int64_t)(4 * s + kg) * R + jrow) * 16) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int jj = 4 * kg + i;
-          cv[k][i] = jj < R ? ccache[m[k] * R + jj] : kNegInf;
+  // candidate bits of this wave's 16 nodes for query qn (their 16 / C parents
+  // lie in one bitset word), then per-node "any query"
+  uint32_t mybits = 0u;
+  if (qn < nq) {
+    const int64_t nb0 = n0 + wave * 16;
+    const int64_t nvalid = A.n_nodes - nb0 < 16 ? (A.n_nodes - nb0 > 0 ? A.n_nodes - nb0 : 0) : 16;
+    const uint32_t valid = (uint32_t)((1ull << nvalid) - 1ull);
+    if (A.sel_parent) {
+      if (A.C >= 16) {
+        // every node of the wave has one of at most two parents; test each node
+        for (int u = 0; u < 16; ++u) {
+          const int64_t par = (nb0 + u) / A.C;
+          const uint32_t w = A.sel_parent[((int64_t)cache * A.QC + qg0 + qn) * A.parent_words + (par >> 5)];
+          if ((w >> (par & 31)) & 1u) mybits |= 1u << u;
         }
+      } else {
+        const int64_t p0 = nb0 / A.C;
+        const uint32_t word =
+            A.sel_parent[((int64_t)cache * A.QC + qg0 + qn) * A.parent_words + (p0 >> 5)] >> (p0 & 31);
+        for (int pi = 0; pi < 16 / A.C; ++pi)
+          if ((word >> pi) & 1u) mybits |= ((1u << A.C) - 1u) << (pi * A.C);
+      }
+      mybits &= valid;
+    } else {
+      mybits = valid;
+    }
+  }
+  uint32_t anybits = mybits;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) anybits |= (uint32_t)__shfl_xor((int)anybits, o);
+
+  auto load_batch = [&](int u0, uint4 (*af)[NS], float (*cv)[4]) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int u = u0 + k;
+      const int64_t m = n0 + wave * 16 + u;
+      const bool live = (anybits >> u) & 1u;
+      const char* gn = gcache + m * gnode;
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        af[k][s] = live && jrow < R ? ld16(gn + ((int64_t)(4 * s + kg) * R + jrow) * 16) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int jj = 4 * kg + i;
+        cv[k][i] = live && jj < R ? ccache[m * R + jj] : kNegInf;
       }
     }
+  };
+
+  uint4 af[NB][NS], an[NB][NS];
+  float cv[NB][4], cn[NB][4];
+  load_batch(0, af, cv);
+  for (int u0 = 0; u0 < 16; u0 += NB) {
+    if (u0 + NB < 16) load_batch(u0 + NB, an, cn);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < NB; ++k) {
+      const int u = u0 + k;
       float v = kNegInf;
-      if (any[k]) {
+      if ((anybits >> u) & 1u) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < NS; ++s)
@@ -153,7 +177,14 @@ __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs A) {
         v = fmaxf(v, __shfl_xor(v, 16));
         v = fmaxf(v, __shfl_xor(v, 32));
       }
-      if (lane < 16) sc[qn][wave * 16 + u + k] = cand[k] ? v : kNegInf;
+      if (lane < 16) sc[qn][wave * 16 + u] = ((mybits >> u) & 1u) ? v : kNegInf;
+    }
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) af[k][s] = an[k][s];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cv[k][i] = cn[k][i];
     }
   }
   __syncthreads();
@@ -175,19 +206,21 @@ __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs A) {
 //
 // s(q, chunk) = max_j [ c_j + sum_i w_ji (q . k_i) / sqrt(d) ]: the chunk's
 // raw keys go through the MFMA (A = 16 keys, B = up to 16 queries) exactly
-// as in attention, then each lane (plane j, 4 keys) folds its four logits
-// with its four weights and the planes are maxed over 16 lanes.  A tile is
-// 256 keys; every wave takes 4 groups of 16 keys and skips the groups none of
-// whose chunks is a candidate of any query.
+// as in attention; the MFMA leaves, in each lane, the logits of 4 keys for
+// one query, and the lane folds them with the weights of all R planes of
+// their chunk (staged once per tile in LDS and read as broadcasts) and takes
+// the max itself, so no lane exchange is needed when C = 4.  A tile is 256
+// keys; each wave owns 4 groups of 16 keys and skips groups none of whose
+// chunks is a candidate of any query; weights are staged only for candidate
+// chunks.
 
 template <int D, int C>
 __global__ __launch_bounds__(256) void k_score_leafw(ScoreArgs A) {
   constexpr int NS = D / 32;
   constexpr int KT = 256;       // keys per tile
-  constexpr int NCH = KT / C;   // chunks per tile
-  constexpr int CPG = 16 / C;   // chunks per 16-key group
-  constexpr int GPW = 4;        // groups per wave
-  constexpr int PARTS = C / 4;  // lanes (of 4 keys) per chunk
+  constexpr int NCH = KT / C;   // chunks per tile (<= 64)
+  constexpr int GPW = 4;        // groups of 16 keys per wave
+  constexpr int PARTS = C / 4;  // 4-key lane parts per chunk
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cache = blockIdx.y;
   const int qg0 = blockIdx.z * 16;
@@ -198,7 +231,8 @@ __global__ __launch_bounds__(256) void k_score_leafw(ScoreArgs A) {
   const int qn = lane & 15, kg = lane >> 4;
   const int64_t n_keys = A.n_nodes * C;  // keys of complete chunks
   __shared__ float sc[16][NCH + 1];
-  __shared__ float zl[4][16][17];  // [wave][query][key of group]
+  __shared__ float4 wl[NCH][16][PARTS];  // w of chunk x, plane j, 4-key part
+  __shared__ float cl[NCH][16];
 
   bf16x8 bq[NS];
   {
@@ -218,81 +252,98 @@ __global__ __launch_bounds__(256) void k_score_leafw(ScoreArgs A) {
   const bf16_t* Kc = reinterpret_cast<const bf16_t*>(A.K) + (int64_t)b * A.ksb + (int64_t)h * A.ksh;
   const float* wcache = reinterpret_cast<const float*>(A.g) + (int64_t)cache * A.node_cap * R * C;
   const float* ccache = A.c + (int64_t)cache * A.node_cap * R;
-  const uint32_t* prow =
-      A.sel_parent ? A.sel_parent + ((int64_t)cache * A.QC + qg0 + qn) * A.parent_words : nullptr;
 
-  // candidate flags of every chunk of this wave's groups, one ballot each:
-  // bit q of cmask[gi][cc] = chunk cc of group gi is a candidate of query q
-  unsigned long long cmask[GPW][CPG];
-  bool gany[GPW];
+  // candidate bits of the tile's chunks for query qn (bit x = chunk m0 + x).
+  // The tile's NCH chunks have NCH / C parents, which lie in one bitset word.
+  unsigned long long mybits = 0ull;
+  if (qn < nq) {
+    const int64_t nvalid = A.n_nodes - m0 < NCH ? A.n_nodes - m0 : NCH;
+    const unsigned long long valid = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1ull);
+    if (A.sel_parent) {
+      const int64_t p0 = m0 / C;
+      const uint32_t word =
+          A.sel_parent[((int64_t)cache * A.QC + qg0 + qn) * A.parent_words + (p0 >> 5)] >> (p0 & 31);
 #pragma unroll
-  for (int gi = 0; gi < GPW; ++gi) {
-    gany[gi] = false;
-#pragma unroll
-    for (int cc = 0; cc < CPG; ++cc) {
-      const int64_t m = m0 + (wave * GPW + gi) * CPG + cc;
-      bool ok = m < A.n_nodes && qn < nq;
-      if (ok && prow) {
-        const int64_t par = m / A.C;
-        ok = (prow[par >> 5] >> (par & 31)) & 1u;
-      }
-      cmask[gi][cc] = __ballot(ok && kg == 0);
-      gany[gi] = gany[gi] || cmask[gi][cc] != 0ull;
+      for (int pi = 0; pi < NCH / C; ++pi)
+        if ((word >> pi) & 1u) mybits |= ((1ull << C) - 1ull) << (pi * C);
+      mybits &= valid;
+    } else {
+      mybits = valid;
     }
   }
-  // all loads of the wave up front: K rows (MFMA A operand), weights, offsets
-  const int j = qn, ccl = kg / PARTS, part = kg % PARTS;  // lane role after the MFMA
+  // chunks that are a candidate of some query (same value in every lane)
+  unsigned long long anybits = mybits;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) anybits |= __shfl_xor(anybits, o);
+
+  // stage w and c of the candidate chunks: all loads first, then the stores
+  {
+    constexpr int ITEMS = NCH * 16 / 256;
+    float4 wst[ITEMS][PARTS];
+    float cst[ITEMS];
+#pragma unroll
+    for (int r = 0; r < ITEMS; ++r) {
+      const int it = tid + 256 * r;
+      const int x = it / 16, j = it % 16;
+      const int64_t m = m0 + x;
+      const bool ok = ((anybits >> x) & 1ull) && j < R;
+      const float4* src = reinterpret_cast<const float4*>(wcache + (m * R + j) * C);
+#pragma unroll
+      for (int pp = 0; pp < PARTS; ++pp) wst[r][pp] = ok ? src[pp] : make_float4(0.f, 0.f, 0.f, 0.f);
+      cst[r] = ok ? ccache[m * R + j] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < ITEMS; ++r) {
+      const int it = tid + 256 * r;
+      const int x = it / 16, j = it % 16;
+#pragma unroll
+      for (int pp = 0; pp < PARTS; ++pp) wl[x][j][pp] = wst[r][pp];
+      cl[x][j] = cst[r];
+    }
+  }
+  // K rows of this wave's live groups (A operand: row qn = key, k-group kg)
   uint4 kf[GPW][NS];
-  float4 wv[GPW];
-  float cj[GPW];
+  bool live[GPW];
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
     const int g = wave * GPW + gi;
+    const unsigned long long gmask = ((1ull << (16 / C)) - 1ull) << (g * 16 / C);
+    live[gi] = (anybits & gmask) != 0ull;
     const int64_t key = k0 + g * 16 + qn;
-    const int64_t m = m0 + g * CPG + ccl;
-    const bool live = gany[gi];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-      kf[gi][s] = live && key < n_keys ? ld16(Kc + key * A.kst + (4 * s + kg) * 8) : make_uint4(0, 0, 0, 0);
-    const bool wok = live && m < A.n_nodes && j < R;
-    wv[gi] = wok ? *reinterpret_cast<const float4*>(wcache + (m * R + j) * C + part * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-    cj[gi] = wok ? ccache[m * R + j] : kNegInf;
+      kf[gi][s] = live[gi] && key < n_keys ? ld16(Kc + key * A.kst + (4 * s + kg) * 8) : make_uint4(0, 0, 0, 0);
   }
+  __syncthreads();
+
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
     const int g = wave * GPW + gi;
-    if (!gany[gi]) {
-      if (lane < 16)
-#pragma unroll
-        for (int cc = 0; cc < CPG; ++cc) sc[qn][g * CPG + cc] = kNegInf;
+    const int x = (g * 16 + 4 * kg) / C;  // chunk (within the tile) of this lane's 4 keys
+    const int part = kg % PARTS;
+    if (!live[gi]) {
+      if (part == 0 && qn < 16) sc[qn][x] = kNegInf;
       continue;
     }
     f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < NS; ++s) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[gi][s]), bq[s], z, 0, 0, 0);
-    // lane holds the logits of keys 4*kg .. 4*kg+3 of the group for query qn
+    float zz[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) zl[wave][qn][4 * kg + i] = z[i] * A.inv_sqrt_d;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // lane (plane j, 4-key part kg of chunk ccl): planes folded, then maxed over j
-    unsigned long long cm = 0ull;
-#pragma unroll
-    for (int cc = 0; cc < CPG; ++cc)
-      if (cc == ccl) cm = cmask[gi][cc];
-    for (int q = 0; q < nq; ++q) {
-      const float4 zq = *reinterpret_cast<const float4*>(&zl[wave][q][4 * kg]);
-      float v = wv[gi].x * zq.x + wv[gi].y * zq.y + wv[gi].z * zq.z + wv[gi].w * zq.w;
+    for (int i = 0; i < 4; ++i) zz[i] = z[i] * A.inv_sqrt_d;
+    const bool xc = (anybits >> x) & 1ull;
+    float best = kNegInf;
+    for (int j = 0; j < R; ++j) {
+      float v = 0.f;
+      if (xc) {
+        const float4 wv = wl[x][j][part];
+        v = wv.x * zz[0] + wv.y * zz[1] + wv.z * zz[2] + wv.w * zz[3];
+      }
 #pragma unroll
       for (int o = 16; o < 16 * PARTS; o <<= 1) v += __shfl_xor(v, o);
-      v += cj[gi];  // -inf for planes j >= R
-      v = wave_max_xor(v, 1, 16);
-      if (j == 0 && part == 0) sc[q][g * CPG + ccl] = ((cm >> q) & 1ull) ? v : kNegInf;
+      if (xc) best = fmaxf(best, cl[x][j] + v);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (part == 0) sc[qn][x] = ((mybits >> x) & 1ull) ? best : kNegInf;
   }
   __syncthreads();
   for (int idx = tid; idx < nq * NCH; idx += 256) {
@@ -301,12 +352,9 @@ __global__ __launch_bounds__(256) void k_score_leafw(ScoreArgs A) {
     if (mm < A.n_nodes) A.score[((int64_t)cache * A.QC + qg0 + q) * A.score_stride + mm] = sc[q][x];
   }
   for (int q = wave; q < nq; q += 4) {
-    for (int x0 = 0; x0 < NCH; x0 += 64) {
-      const int x = x0 + lane;
-      const float v = x < NCH ? sc[q][x] : kNegInf;
-      const bool c = x < NCH && m0 + x < A.n_nodes && v > kNegInf;
-      publish_range(A.keyrange + ((int64_t)cache * A.QC + qg0 + q) * 4, c, order_key(v));
-    }
+    const float v = lane < NCH ? sc[q][lane] : kNegInf;
+    const bool c = lane < NCH && m0 + lane < A.n_nodes && v > kNegInf;
+    publish_range(A.keyrange + ((int64_t)cache * A.QC + qg0 + q) * 4, c, order_key(v));
   }
 }
 
