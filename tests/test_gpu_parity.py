@@ -129,11 +129,12 @@ BUILD_CASES = [
     ("light-bf16", dict(batch=1, n_kv_heads=1, q_per_kv=4, head_dim=128, n_ref=1, chunk=8, levels=4, dtype="bf16", capacity=5000), 4096 + 8 * 5 + 3),
     ("c32-f32-d64", dict(batch=1, n_kv_heads=1, q_per_kv=1, head_dim=64, n_ref=5, chunk=32, levels=2, dtype="f32", capacity=2200), 2048 + 70),
     ("c1-f32", dict(batch=1, n_kv_heads=1, q_per_kv=1, head_dim=64, n_ref=3, chunk=1, levels=1, dtype="f32", capacity=300), 300),
+    ("c2-f32-5lv", dict(batch=1, n_kv_heads=2, q_per_kv=1, head_dim=128, n_ref=3, chunk=2, levels=5, dtype="f32", capacity=1000), 32 * 7 + 2 * 5 + 1),
     ("deep-bf16-weights", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=6, dtype="bf16", capacity=9000, leaf_form="weights"), 8192 + 4 * 37 + 2),
     ("light-bf16-weights", dict(batch=1, n_kv_heads=1, q_per_kv=4, head_dim=128, n_ref=1, chunk=8, levels=4, dtype="bf16", capacity=5000, leaf_form="weights"), 4096 + 8 * 5 + 3),
     ("c16-bf16-d64-weights", dict(batch=2, n_kv_heads=1, q_per_kv=2, head_dim=64, n_ref=7, chunk=16, levels=2, dtype="bf16", capacity=3000, leaf_form="weights"), 2048 + 16 * 9 + 5),
 ]
-APPEND_CASES = BUILD_CASES[:5] + BUILD_CASES[6:]
+APPEND_CASES = [c for c in BUILD_CASES if c[0] != "c1-f32"]
 
 
 def _segmented_keys(cfg, seed):

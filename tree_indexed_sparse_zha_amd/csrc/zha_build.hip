@@ -9,8 +9,8 @@
 // Stored: g rounded once to the KV dtype, L, and c_j = L_j - r_j.g_j/sqrt(d)
 // with the rounded g.
 //
-// Design.  One 64-lane wave owns one top span (C^Lv tokens) of one cache and
-// streams it in blocks of 16 keys.  Lane (j = lane % 16, dg = lane / 16) owns
+// Design.  One workgroup owns one top span (C^Lv tokens) of one cache; each of
+// its W waves streams a share of it in blocks of 16 keys.  Lane (j = lane % 16, dg = lane / 16) owns
 // reference query j and a quarter of the head dimension (the 16-byte pieces
 // dg, dg+4, dg+8, ... of a row), so all merges of g are lane-local fp32
 // arithmetic and only the two dot products over d (r.k on MFMA, r.g for c)
@@ -47,8 +47,19 @@ __device__ __forceinline__ void absorb(float& am, float& as, float* aacc, bool& 
   am = mn;
 }
 
-template <typename T, int D, int NA, bool LEAF_ACC>
-__global__ __launch_bounds__(64) void k_build_span(BuildArgs A) {
+// Wave-scope barrier for LDS regions private to one wave.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// W > 1: the workgroup's W waves share one top span (W divides C), wave w
+// streaming the w-th W-th of it, i.e. C / W whole children of the top node;
+// their open top-level accumulators are merged in LDS, in wave order, by
+// wave 0.
+template <typename T, int D, int NA, bool LEAF_ACC, int W>
+__global__ __launch_bounds__(64 * W) void k_build_span(BuildArgs A) {
   constexpr int E = Elem<T>::per16;
   constexpr int PIECES = D / E;
   constexpr int NS = PIECES / 4;  // 16-byte pieces per lane
@@ -56,7 +67,8 @@ __global__ __launch_bounds__(64) void k_build_span(BuildArgs A) {
   constexpr int KB = kKeysPerBlock;
   constexpr int NAR = NA > 0 ? NA : 1;
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int j = lane & 15, dg = lane >> 4;
   const TreeGeom& geo = A.geo;
   const int R = geo.R, C = geo.C;
@@ -64,9 +76,13 @@ __global__ __launch_bounds__(64) void k_build_span(BuildArgs A) {
   const int b = cache / geo.H, h = cache % geo.H;
   const int64_t span = A.first_span + blockIdx.x;
   const int64_t ncomplete = (A.n_tokens / C) * C;
-  const int64_t t0 = span * A.span_tokens;
-  const int64_t t1 = min(t0 + A.span_tokens, ncomplete);
-  if (t0 >= t1) return;
+  const int64_t t0 = span * A.span_tokens;  // span start: every node boundary is relative to it
+  const int64_t tend = min(t0 + A.span_tokens, ncomplete);
+  if (t0 >= tend) return;  // uniform over the workgroup
+  // this wave's share of the span
+  const int64_t sub = A.span_tokens / W;
+  const int64_t w0 = t0 + wave * sub;
+  const int64_t t1 = min(w0 + sub, tend);
   const float isd = A.inv_sqrt_d;
 
   // reference query j, this lane's quarter of d
@@ -79,8 +95,10 @@ __global__ __launch_bounds__(64) void k_build_span(BuildArgs A) {
       for (int e = 0; e < E; ++e) rj[s * E + e] = (j < R) ? rp[(4 * s + dg) * E + e] : 0.f;
   }
 
-  __shared__ uint4 Ks[KB * PIECES];
-  __shared__ float zs[16][KB + 1];
+  __shared__ uint4 Ks_all[W][KB * PIECES];
+  __shared__ float zs_all[W][16][KB + 1];
+  uint4* Ks = Ks_all[wave];
+  float (*zs)[KB + 1] = zs_all[wave];
 
   const T* Kc = reinterpret_cast<const T*>(A.K) + (int64_t)b * A.sb + (int64_t)h * A.sh;
 
@@ -136,15 +154,15 @@ __global__ __launch_bounds__(64) void k_build_span(BuildArgs A) {
   }
 
   uint4 pre[NS];
-  int64_t pos = t0;
+  int64_t pos = w0;
   int nk = (int)min<int64_t>(KB, t1 - pos);
-  load_block(pos, nk, pre);
+  if (pos < t1) load_block(pos, nk, pre);
   const int seg = C < KB ? C : KB;
 
   while (pos < t1) {
 #pragma unroll
     for (int u = 0; u < NS; ++u) Ks[lane + 64 * u] = pre[u];
-    __syncthreads();
+    wave_sync();
     const int64_t npos = pos + nk;
     const int nnk = (int)min<int64_t>(KB, t1 - npos);
     if (npos < t1) load_block(npos, nnk, pre);
@@ -174,7 +192,7 @@ __global__ __launch_bounds__(64) void k_build_span(BuildArgs A) {
         if (dg == 0) zs[j][i] = part * isd;
       }
     }
-    __syncthreads();
+    wave_sync();
 
     // leaf segments of this block: seg keys each (a whole leaf when C <= 16)
     for (int sg = 0; sg < nk; sg += seg) {
@@ -235,7 +253,7 @@ __global__ __launch_bounds__(64) void k_build_span(BuildArgs A) {
       for (int a = 0; a < NA; ++a) {
         const int lvl = a + (LEAF_ACC ? 1 : 2);
         const int64_t sp = geo.span_len[lvl];
-        if (used[a] && (rel % sp) == 0) {
+        if (used[a] && (rel % sp) == 0 && !(W > 1 && a == NA - 1)) {
           const float L = am[a] + __logf(as[a]);
           const float inv = 1.f / as[a];
           float g[NV];
@@ -249,12 +267,14 @@ __global__ __launch_bounds__(64) void k_build_span(BuildArgs A) {
     }
     pos = npos;
     nk = nnk;
-    __syncthreads();
+    wave_sync();
   }
 
-  // end of the data inside this span: close the partial nodes, bottom-up
+  // end of the data inside this wave's share: close the partial nodes,
+  // bottom-up (with W > 1 the top accumulator is merged across waves below)
 #pragma unroll
   for (int a = 0; a < NA; ++a) {
+    if (W > 1 && a == NA - 1) break;
     const int lvl = a + (LEAF_ACC ? 1 : 2);
     const int64_t sp = geo.span_len[lvl];
     if (used[a]) {
@@ -268,40 +288,81 @@ __global__ __launch_bounds__(64) void k_build_span(BuildArgs A) {
       used[a] = false;
     }
   }
+  if constexpr (W > 1 && NA > 0) {
+    __shared__ float dep_m[W][64], dep_s[W][64], dep_g[W][NV][64];
+    __shared__ int dep_used[W];
+    const int top = NA - 1;
+    dep_m[wave][lane] = am[top];
+    dep_s[wave][lane] = as[top];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) dep_g[wave][v][lane] = aacc[top][v];
+    if (lane == 0) dep_used[wave] = used[top] ? 1 : 0;
+    __syncthreads();
+    if (wave == 0) {
+      float mm = 0.f, ss = 0.f, gg[NV];
+      bool u = false;
+      for (int w = 0; w < W; ++w) {
+        if (!dep_used[w]) continue;
+        float gc[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) gc[v] = dep_g[w][v][lane];
+        absorb(mm, ss, gg, u, dep_m[w][lane], dep_s[w][lane], gc, NV);
+      }
+      if (u) {
+        const int lvl = top + (LEAF_ACC ? 1 : 2);
+        const float L = mm + __logf(ss);
+        const float inv = 1.f / ss;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) gg[v] *= inv;
+        emit(lvl, t0 / geo.span_len[lvl], L, gg);
+      }
+    }
+  }
 }
 
-#define ZHA_CASE(LEAF, N)                                                            \
-  case N:                                                                            \
-    hipLaunchKernelGGL((k_build_span<T, D, N, LEAF>), grid, dim3(64), 0, s, a);      \
-    return hipGetLastError();
+// Waves per top span: W = min(C, 4) when the top node has children built by
+// the waves (C <= 16 and at least 2 levels); W divides C, so a wave's share
+// is a whole number of the top node's children.
+template <typename T, int D, int NA, bool LEAF>
+hipError_t launch_na(const BuildArgs& a, dim3 grid, hipStream_t s) {
+  if constexpr (!LEAF && NA >= 1) {
+    if (a.geo.C >= 4) {
+      hipLaunchKernelGGL((k_build_span<T, D, NA, LEAF, 4>), grid, dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
+    if (a.geo.C == 2) {
+      hipLaunchKernelGGL((k_build_span<T, D, NA, LEAF, 2>), grid, dim3(128), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((k_build_span<T, D, NA, LEAF, 1>), grid, dim3(64), 0, s, a);
+  return hipGetLastError();
+}
 
 template <typename T, int D>
 hipError_t dispatch_leaf(const BuildArgs& a, dim3 grid, hipStream_t s) {
   if (a.geo.C > kKeysPerBlock) {
     // leaves span several blocks: an open node per level, leaves included
     switch (a.geo.levels) {
-      ZHA_CASE(true, 1)
-      ZHA_CASE(true, 2)
-      ZHA_CASE(true, 3)
-      ZHA_CASE(true, 4)
-      default:
-        return hipErrorInvalidValue;
+      case 1: return launch_na<T, D, 1, true>(a, grid, s);
+      case 2: return launch_na<T, D, 2, true>(a, grid, s);
+      case 3: return launch_na<T, D, 3, true>(a, grid, s);
+      case 4: return launch_na<T, D, 4, true>(a, grid, s);
+      default: return hipErrorInvalidValue;
     }
   }
   switch (a.geo.levels - 1) {
-    ZHA_CASE(false, 0)
-    ZHA_CASE(false, 1)
-    ZHA_CASE(false, 2)
-    ZHA_CASE(false, 3)
-    ZHA_CASE(false, 4)
-    ZHA_CASE(false, 5)
-    ZHA_CASE(false, 6)
-    ZHA_CASE(false, 7)
-    default:
-      return hipErrorInvalidValue;
+    case 0: return launch_na<T, D, 0, false>(a, grid, s);
+    case 1: return launch_na<T, D, 1, false>(a, grid, s);
+    case 2: return launch_na<T, D, 2, false>(a, grid, s);
+    case 3: return launch_na<T, D, 3, false>(a, grid, s);
+    case 4: return launch_na<T, D, 4, false>(a, grid, s);
+    case 5: return launch_na<T, D, 5, false>(a, grid, s);
+    case 6: return launch_na<T, D, 6, false>(a, grid, s);
+    case 7: return launch_na<T, D, 7, false>(a, grid, s);
+    default: return hipErrorInvalidValue;
   }
 }
-#undef ZHA_CASE
 
 }  // namespace
 
