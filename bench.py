@@ -72,19 +72,25 @@ def unpack_level(cfg, buf, lv, n_nodes):
     return zha.unpack_bits(buf.sel[off : off + nq * w].view(nq, w), n_nodes)
 
 
-def selection_bytes(cfg: zha.ZhaConfig, buf, n_tokens: int, T: int):
+def selection_bytes(cfg: zha.ZhaConfig, buf, n_tokens: int, T: int, logits: bool = False):
     """Algorithmic bytes of one route + attend from the selection it made.
 
     route, per cache and level: |union over the cache's queries of the
-    candidates| x (R*d*2 bytes of g + 4R bytes of c); attend, per cache:
-    |union over the cache's queries of the attended keys| x 2*d*2 bytes of
-    K and V.  Also returns per-query selected share and per-level counts.
+    candidates| x (R*d*2 bytes of g + 4R bytes of c), or at level 1 in the
+    weights form x (C*d*2 bytes of keys + 4RC of weights + 4R of c, plus
+    4*min(QC,16) bytes of logits written per key when they are kept);
+    attend, per cache: |union over the cache's queries of the attended keys|
+    x (d*2 bytes of V + d*2 bytes of K, or 4*min(QC,16) bytes of cached
+    logits).  Also returns per-query selected share and per-level counts.
     """
     C, Lv, R, d = cfg.chunk, cfg.levels, cfg.n_ref, cfg.head_dim
     sizes = level_sizes(n_tokens, C, Lv)
     caches, QC = cfg.n_caches, cfg.q_per_kv * T
     node_bytes = R * d * cfg.esize + 4 * R
+    QW = min(QC, 16)
     leaf_bytes = C * d * cfg.esize + R * C * 4 + 4 * R if cfg.leaf_form == "weights" else node_bytes
+    if logits:
+        leaf_bytes += C * QW * 4
     per_level = {}
     kept_prev = None
     for lv in range(Lv, 0, -1):
@@ -113,7 +119,7 @@ def selection_bytes(cfg: zha.ZhaConfig, buf, n_tokens: int, T: int):
     keys[:, C * ((n_tokens - 1) // C) : n_tokens] = True
     phi = keys.sum(dim=1).float() / n_tokens
     union_keys = keys.view(caches, QC, n_tokens).any(dim=1).sum().item()
-    attend_bytes = union_keys * 2 * d * cfg.esize
+    attend_bytes = union_keys * (d * cfg.esize + (QW * 4 if logits else d * cfg.esize))
     del keys
     return per_level, attend_bytes, phi.mean().item(), phi.min().item(), phi.max().item(), union_keys / caches
 
@@ -173,6 +179,8 @@ def main():
     ap.add_argument("--tokens", type=int, default=None, help="override the context length (sweeps)")
     ap.add_argument("--leaf-form", default="weights", choices=["weights", "mean"],
                     help="level-1 storage: softmax weights scored from raw keys (default) or mean keys")
+    ap.add_argument("--no-logits", action="store_true",
+                    help="attention recomputes every logit from K instead of reading the route's level-1 logits")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     args = ap.parse_args()
@@ -208,7 +216,7 @@ def main():
     log(f"generated inputs in {time.time() - t0:.1f}s")
     K, V, Q, ref = batch.K, batch.V, batch.Q, batch.ref
     tree = zha.alloc_tree(cfg)
-    buf = zha.alloc_route(cfg, T)
+    buf = zha.alloc_route(cfg, T, logits=not args.no_logits)
     nq = int(buf.layout.n_queries)
     out = torch.empty(nq, cfg.head_dim, device="cuda")
     lse = torch.empty(nq, device="cuda")
@@ -236,7 +244,7 @@ def main():
         zha.append(cfg, K, ref, tree, n_old, A, ev=ev_app[s])
         n = n_old + A
         zha.route(cfg, tree, n, Q, T, p, buf, ev=ev_route[s], K=K)
-        zha.attend(cfg, Q, T, K, V, n, zha.level1_sel(buf), FLAGS, out, lse, ws, ev=ev_att[s])
+        zha.attend(cfg, Q, T, K, V, n, zha.level1_sel(buf), FLAGS, out, lse, ws, ev=ev_att[s], logits=buf.logits)
         return n
 
     for s in range(args.warmup):
@@ -267,7 +275,9 @@ def main():
     append_ms = kmean.get("build", 0.0)
 
     # algorithmic bytes from the last step's selection
-    per_level, attend_bytes, phi, phi_min, phi_max, ukeys = selection_bytes(cfg, buf, n_final, T)
+    per_level, attend_bytes, phi, phi_min, phi_max, ukeys = selection_bytes(
+        cfg, buf, n_final, T, logits=buf.logits is not None
+    )
     route_bytes = sum(v["alg_bytes"] for v in per_level.values())
     tree_bytes_per_token = sum(
         cfg.n_ref * (cfg.head_dim * cfg.esize + 8) / (cfg.chunk**l) for l in range(2, cfg.levels + 1)
@@ -345,6 +355,7 @@ def main():
             "p": p,
             "append_tokens_per_step": A,
             "leaf_form": cfg.leaf_form,
+            "cached_logits": buf.logits is not None,
             "queries_per_step": nq,
         },
         "roofline": roofline,

@@ -136,6 +136,11 @@ typedef struct zha_tree_layout {
  *          (in floats); score_stride = node_cap rounded up to 4.
  *   stats: [n_queries] zha_select_stats; starts at stats_offset[l-1]
  *          (in records).
+ * Optional logits (leaf-weights form only): level-1 scoring computes
+ * q . k_i / sqrt(d) for every key of every candidate chunk; zha_route can
+ * keep them in a [caches][ceil(QC/16)][capacity/4][min(QC,16)][4] fp32 buffer
+ * (4-key quads; QC = G*T queries per cache) so that zha_attend reads 16 bytes
+ * per query and quad instead of the keys.
  */
 typedef struct zha_route_layout {
   int32_t levels;
@@ -150,6 +155,7 @@ typedef struct zha_route_layout {
   int64_t score_floats_total; /* floats of the score buffer */
   int64_t stats_total;        /* records of the stats buffer */
   int64_t workspace_bytes;    /* scratch zha_route needs */
+  int64_t logits_floats;      /* floats of the optional logits buffer (weights form), else 0 */
 } zha_route_layout;
 
 /*
@@ -268,13 +274,16 @@ int zha_append(const zha_config* cfg, const void* K, const int64_t k_strides[3],
  *   sel       device, zha_get_route_layout().sel_words_total uint32 (output).
  *   score     device, zha_get_route_layout().score_floats_total fp32 (output).
  *   stats     device, zha_get_route_layout().stats_total records (output).
+ *   logits    device, zha_get_route_layout().logits_floats fp32 (optional
+ *             output, NULL to skip; leaf-weights form only).
  *   ws        device scratch of at least workspace_bytes.
  * Level-1 bits of sel are the routed chunk ids consumed by zha_attend.
  */
 int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const void* Q,
               const int64_t q_strides[4], int32_t T, float p, const void* K,
               const int64_t k_strides[3], uint32_t* sel, float* score,
-              zha_select_stats* stats, void* ws, int64_t ws_bytes, zha_profile* prof, void* stream);
+              zha_select_stats* stats, float* logits, void* ws, int64_t ws_bytes,
+              zha_profile* prof, void* stream);
 
 /*
  * zha_attend - exact softmax attention over the routed keys.
@@ -288,6 +297,10 @@ int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const v
  *   sel1      device, [n_queries][sel1_words] uint32 chunk bitsets (the
  *             level-1 block of zha_route's sel, or any set); may be NULL
  *             with ZHA_ALL_KEYS.
+ *   logits    device, optional (NULL = compute every logit from K): the
+ *             logits zha_route wrote for the same Q, K and n_tokens with
+ *             sel1 = its level-1 selection.  Quads holding a routed chunk
+ *             read their logits there; other quads (forced keys only) use K.
  *   out       device, [n_queries][d] fp32 (output).
  *   lse       device, [n_queries] fp32 (output, may be NULL).
  *   ws        device scratch of zha_attend_workspace_bytes(cfg, T).
@@ -297,8 +310,9 @@ int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const v
  */
 int zha_attend(const zha_config* cfg, const void* Q, const int64_t q_strides[4], int32_t T,
                const void* K, const void* V, const int64_t kv_strides[3], int64_t n_tokens,
-               const uint32_t* sel1, int64_t sel1_words, uint32_t flags, float* out, float* lse,
-               void* ws, int64_t ws_bytes, zha_profile* prof, void* stream);
+               const uint32_t* sel1, int64_t sel1_words, const float* logits, uint32_t flags,
+               float* out, float* lse, void* ws, int64_t ws_bytes, zha_profile* prof,
+               void* stream);
 
 /*
  * zha_dense_decode - dense flash-decode over all n_tokens keys, the

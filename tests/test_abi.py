@@ -65,6 +65,15 @@ def test_tree_layout_weights_form():
     assert tl.total_bytes < mean.total_bytes * 0.35
 
 
+def test_route_layout_logits():
+    assert zha.route_layout(cfg_deep(), 1).logits_floats == 0
+    rl = zha.route_layout(cfg_deep(leaf_form="weights"), 1)
+    # caches x ceil(QC/16) x quads x min(QC, 16) x 4 (QC = 4 queries per cache)
+    assert rl.logits_floats == 8 * 1 * (32768 // 4) * 4 * 4
+    rl = zha.route_layout(cfg_deep(leaf_form="weights"), 8)  # QC = 32: two groups of 16
+    assert rl.logits_floats == 8 * 2 * (32768 // 4) * 16 * 4
+
+
 def test_route_layout_sizes():
     cfg = cfg_deep()
     rl = zha.route_layout(cfg, 64)
@@ -115,7 +124,7 @@ def _call_route(lib, cfg, **over):
     a.update(over)
     c = cfg.c()
     return lib.zha_route(ct.byref(c), a["tree"], a["n_tokens"], a["Q"], a["qs"], a["T"], a["p"], a["K"], a["ks"], a["sel"],
-                         a["score"], a["stats"], a["ws"], a["ws_bytes"], a.get("prof"), None)
+                         a["score"], a["stats"], a.get("logits"), a["ws"], a["ws_bytes"], a.get("prof"), None)
 
 
 def test_route_argument_errors(lib):
@@ -138,6 +147,8 @@ def test_route_argument_errors(lib):
     cw = cfg_deep(leaf_form="weights")
     assert _call_route(lib, cw, ws_bytes=1 << 20) == zha.ZHA_ERR_NULL
     assert b"K" in lib.zha_last_error()
+    assert _call_route(lib, cfg, logits=16, ws_bytes=1 << 20) == zha.ZHA_ERR_ARG
+    assert _call_route(lib, cw, K=16, ks=zha._i64(0, 0, 128), logits=8, ws_bytes=1 << 20) == zha.ZHA_ERR_ALIGN
     bad = zha.Profile()
     bad.n_pairs = 40
     assert _call_route(lib, cfg, prof=ct.byref(bad)) == zha.ZHA_ERR_ARG
@@ -172,7 +183,7 @@ def test_attend_argument_errors(lib):
         a = dict(Q=16, T=1, K=16, V=16, n=32768, sel=16, words=256, flags=3, out=16, ws=16, wsb=ws)
         a.update(o)
         return lib.zha_attend(ct.byref(c), a["Q"], qs, a["T"], a["K"], a["V"], ks, a["n"], a["sel"], a["words"],
-                              a["flags"], a["out"], None, a["ws"], a["wsb"], None, None)
+                              a.get("logits"), a["flags"], a["out"], None, a["ws"], a["wsb"], None, None)
 
     assert call(sel=None) == zha.ZHA_ERR_NULL
     assert call(words=255) == zha.ZHA_ERR_CAPACITY
@@ -182,6 +193,8 @@ def test_attend_argument_errors(lib):
     assert call(flags=8) == zha.ZHA_ERR_ARG
     assert call(V=24) == zha.ZHA_ERR_ALIGN
     assert call(out=None) == zha.ZHA_ERR_NULL
+    assert call(logits=16) == zha.ZHA_ERR_ARG  # logits need the weights form
+    assert b"weights" in lib.zha_last_error()
 
 
 def test_bit_helpers_roundtrip():

@@ -61,19 +61,21 @@ def _levels(cfg, buf, N, qi):
 
 
 def _run_step(cfg, b, N0, A, T, p):
-    """The bench's step: build over N0, append A, route, attend."""
+    """The bench's step: build over N0, append A, route (keeping the level-1
+    logits), attend (reading them)."""
     tree = zha.alloc_tree(cfg)
     zha.build(cfg, b.K, b.ref, tree, N0)
     if A:
         zha.append(cfg, b.K, b.ref, tree, N0, A)
     N = N0 + A
-    buf = zha.alloc_route(cfg, T)
+    buf = zha.alloc_route(cfg, T, logits=True)
     zha.route(cfg, tree, N, b.Q, T, p, buf, K=b.K)
     nq = int(buf.layout.n_queries)
     out = torch.empty(nq, cfg.head_dim, device="cuda")
     lse = torch.empty(nq, device="cuda")
     ws = torch.empty(zha.attend_workspace_bytes(cfg, T), dtype=torch.uint8, device="cuda")
-    zha.attend(cfg, b.Q, T, b.K, b.V, N, zha.level1_sel(buf), zha.ZHA_SINK | zha.ZHA_LAST_CHUNK, out, lse, ws)
+    zha.attend(cfg, b.Q, T, b.K, b.V, N, zha.level1_sel(buf), zha.ZHA_SINK | zha.ZHA_LAST_CHUNK, out, lse, ws,
+               logits=buf.logits)
     torch.cuda.synchronize()
     return tree, buf, out, lse
 

@@ -246,15 +246,25 @@ def test_append_equals_build(name, kw, N):
 
 
 def run_path(cfg, K, V, Q, ref, N, T, p, flags=zha.ZHA_SINK | zha.ZHA_LAST_CHUNK):
+    """build + route + attend.  In the weights form the route also keeps the
+    level-1 logits and attention runs twice, with and without them: the
+    logits come from the same MFMA as attention's own, so the outputs must be
+    bit-identical."""
     tree = zha.alloc_tree(cfg)
     zha.build(cfg, K, ref, tree, N)
-    buf = zha.alloc_route(cfg, T)
+    buf = zha.alloc_route(cfg, T, logits=cfg.leaf_form == "weights")
     zha.route(cfg, tree, N, Q, T, p, buf, K=K)
     nq = int(buf.layout.n_queries)
     out = torch.empty(nq, cfg.head_dim, device="cuda")
     lse = torch.empty(nq, device="cuda")
     ws = torch.empty(zha.attend_workspace_bytes(cfg, T), dtype=torch.uint8, device="cuda")
     zha.attend(cfg, Q, T, K, V, N, zha.level1_sel(buf), flags, out, lse, ws)
+    if buf.logits is not None:
+        out2, lse2 = torch.empty_like(out), torch.empty_like(lse)
+        zha.attend(cfg, Q, T, K, V, N, zha.level1_sel(buf), flags, out2, lse2, ws, logits=buf.logits)
+        torch.cuda.synchronize()
+        assert torch.equal(out, out2), float((out - out2).abs().max())
+        assert torch.equal(lse, lse2)
     torch.cuda.synchronize()
     return tree, buf, out, lse
 

@@ -268,6 +268,11 @@ int zha_get_route_layout(const zha_config* cfg, int32_t T, zha_route_layout* out
   out->stats_total = ss;
   // per level and query: candidate key range and count, filled by the score kernel
   out->workspace_bytes = align256((int64_t)cfg->levels * out->n_queries * 16);
+  if (cfg->leaf_form == ZHA_LEAF_WEIGHTS) {
+    const int64_t QC = (int64_t)cfg->q_per_kv * T;
+    out->logits_floats = (int64_t)cfg->batch * cfg->n_kv_heads * cdiv(QC, 16) *
+                         (tl.node_cap[0] * cfg->chunk / 4) * (QC < 16 ? QC : 16) * 4;
+  }
   return ZHA_OK;
 }
 
@@ -289,7 +294,8 @@ int zha_append(const zha_config* cfg, const void* K, const int64_t k_strides[3],
 int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const void* Q,
               const int64_t q_strides[4], int32_t T, float p, const void* K,
               const int64_t k_strides[3], uint32_t* sel, float* score,
-              zha_select_stats* stats, void* ws, int64_t ws_bytes, zha_profile* prof, void* stream) {
+              zha_select_stats* stats, float* logits, void* ws, int64_t ws_bytes,
+              zha_profile* prof, void* stream) {
   int rc = check_config(cfg);
   if (rc) return rc;
   if ((rc = check_prof(prof))) return rc;
@@ -301,6 +307,10 @@ int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const v
   if (leafw) {
     if ((rc = check_ptr16(K, "K"))) return rc;
     if ((rc = check_strides(k_strides, 3, esize(cfg->kv_dtype), "k_strides"))) return rc;
+  }
+  if (logits) {
+    if (!leafw) return fail(ZHA_ERR_ARG, "logits need the leaf weights form");
+    if ((rc = check_ptr16(logits, "logits"))) return rc;
   }
   if ((rc = check_ptr16(sel, "sel"))) return rc;
   if ((rc = check_ptr16(score, "score"))) return rc;
@@ -356,6 +366,9 @@ int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const v
       sa.ksb = k_strides[0];
       sa.ksh = k_strides[1];
       sa.kst = k_strides[2];
+      sa.logits = logits;
+      sa.nquads = tl.node_cap[0] * cfg->chunk / 4;
+      sa.QW = sa.QC < 16 ? sa.QC : 16;
     }
     zha::SelectArgs se;
     std::memset(&se, 0, sizeof(se));
@@ -376,8 +389,9 @@ int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const v
 
 int zha_attend(const zha_config* cfg, const void* Q, const int64_t q_strides[4], int32_t T,
                const void* K, const void* V, const int64_t kv_strides[3], int64_t n_tokens,
-               const uint32_t* sel1, int64_t sel1_words, uint32_t flags, float* out, float* lse,
-               void* ws, int64_t ws_bytes, zha_profile* prof, void* stream) {
+               const uint32_t* sel1, int64_t sel1_words, const float* logits, uint32_t flags,
+               float* out, float* lse, void* ws, int64_t ws_bytes, zha_profile* prof,
+               void* stream) {
   int rc = check_config(cfg);
   if (rc) return rc;
   if ((rc = check_prof(prof))) return rc;
@@ -394,6 +408,11 @@ int zha_attend(const zha_config* cfg, const void* Q, const int64_t q_strides[4],
   if (n_tokens < 1) return fail(ZHA_ERR_ARG, "n_tokens must be >= 1");
   if (n_tokens > cfg->capacity_tokens) return fail(ZHA_ERR_CAPACITY, "n_tokens exceeds capacity");
   const int64_t n_chunks = n_tokens / cfg->chunk;
+  if (logits) {
+    if (cfg->leaf_form != ZHA_LEAF_WEIGHTS) return fail(ZHA_ERR_ARG, "logits need the leaf weights form");
+    if (flags & ZHA_ALL_KEYS) return fail(ZHA_ERR_ARG, "logits cannot be used with ZHA_ALL_KEYS");
+    if ((rc = check_ptr16(logits, "logits"))) return rc;
+  }
   if (!(flags & ZHA_ALL_KEYS)) {
     if (!sel1) return fail(ZHA_ERR_NULL, "sel1 is NULL");
     if (sel1_words < cdiv(n_chunks, 32)) return fail(ZHA_ERR_CAPACITY, "sel1_words too small");
@@ -427,6 +446,13 @@ int zha_attend(const zha_config* cfg, const void* Q, const int64_t q_strides[4],
   a.tile_keys = attend_tile_keys(cfg, T);
   a.n_tiles = cdiv(n_tokens, a.tile_keys);
   a.partial = static_cast<float*>(ws);
+  a.logits = logits;
+  if (logits) {
+    zha_tree_layout tl;
+    fill_tree_layout(cfg, &tl);
+    a.nquads = tl.node_cap[0] * cfg->chunk / 4;
+    a.QW = a.QC < 16 ? a.QC : 16;
+  }
   a.out = out;
   a.lse = lse;
   a.inv_sqrt_d = 1.0f / std::sqrt((float)cfg->head_dim);
@@ -441,8 +467,8 @@ int zha_dense_decode(const zha_config* cfg, const void* Q, const int64_t q_strid
                      const void* K, const void* V, const int64_t kv_strides[3], int64_t n_tokens,
                      float* out, float* lse, void* ws, int64_t ws_bytes, zha_profile* prof,
                      void* stream) {
-  return zha_attend(cfg, Q, q_strides, T, K, V, kv_strides, n_tokens, nullptr, 0, ZHA_ALL_KEYS, out,
-                    lse, ws, ws_bytes, prof, stream);
+  return zha_attend(cfg, Q, q_strides, T, K, V, kv_strides, n_tokens, nullptr, 0, nullptr, ZHA_ALL_KEYS,
+                    out, lse, ws, ws_bytes, prof, stream);
 }
 
 }  // extern "C"

@@ -23,6 +23,13 @@ namespace zha {
 namespace {
 
 constexpr int kAttThreads = 256;
+
+// Wave-scope barrier for LDS regions private to one wave.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 constexpr int kQG = 4;  // queries per workgroup
 constexpr int kU = 4;   // wave steps per batch
 
@@ -232,7 +239,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_mfma(AttendArgs A) {
   const int b = cache / A.H, h = cache % A.H;
   const int64_t k_lo = tile * A.tile_keys;
   const int64_t k_hi = min(A.n_tokens, k_lo + A.tile_keys);
-  const int nquads = (int)((k_hi - k_lo + 3) / 4);
+  const int nquads = (int)((k_hi - k_lo + 3) / 4);  // quads of this tile
   const bool all = A.flags & 4u, sink = A.flags & 1u, last = A.flags & 2u;
   const int64_t last_start = (int64_t)A.C * ((A.n_tokens - 1) / A.C);
 
@@ -243,9 +250,12 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_mfma(AttendArgs A) {
   __shared__ float sc_lds[4][16];
   __shared__ float red[4][QG][D + 2];
 
-  // ---- phase 1: per-quad selection masks, compacted in key order
+  // ---- phase 1: per-quad selection masks, compacted in key order; with a
+  // logits buffer, quads holding a routed chunk come first (their logits are
+  // cached), then the quads holding forced keys only
   unsigned long long qmask[QPT];
-  int cnt = 0;
+  uint32_t qrouted = 0u;
+  int cnt = 0;  // routed count in the low 16 bits, forced-only count above
   {
     const uint32_t* srow[QG];
 #pragma unroll
@@ -255,6 +265,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_mfma(AttendArgs A) {
     for (int i = 0; i < QPT; ++i) {
       const int qd = tid * QPT + i;
       unsigned long long msk = 0ull;
+      bool routed = false;
       if (qd < nquads) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -266,14 +277,17 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_mfma(AttendArgs A) {
 #pragma unroll
           for (int u = 0; u < QG; ++u) {
             if (u >= nq) break;
-            bool s = forced;
-            if (!s && has_chunk) s = (srow[u][chunk >> 5] >> (chunk & 31)) & 1u;
-            if (s) msk |= 1ull << (u * 4 + kk);
+            bool bit = false;
+            if (has_chunk) bit = (srow[u][chunk >> 5] >> (chunk & 31)) & 1u;
+            routed = routed || bit;
+            if (forced || bit) msk |= 1ull << (u * 4 + kk);
           }
         }
       }
       qmask[i] = msk;
-      cnt += msk != 0ull;
+      const bool r = routed && A.logits != nullptr;
+      if (r) qrouted |= 1u << i;
+      if (msk) cnt += r ? 1 : (1 << 16);
     }
   }
   scan[tid] = cnt;
@@ -284,15 +298,17 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_mfma(AttendArgs A) {
     scan[tid] += add;
     __syncthreads();
   }
-  const int n_ent = scan[kAttThreads - 1];
+  const int n_r = scan[kAttThreads - 1] & 0xffff;
+  const int n_ent = n_r + (scan[kAttThreads - 1] >> 16);
   {
-    int pos = scan[tid] - cnt;
+    int pos_r = (scan[tid] - cnt) & 0xffff;
+    int pos_f = n_r + ((scan[tid] - cnt) >> 16);
 #pragma unroll
     for (int i = 0; i < QPT; ++i) {
       if (qmask[i]) {
+        const int pos = ((qrouted >> i) & 1u) ? pos_r++ : pos_f++;
         e_quad[pos] = (uint16_t)(tid * QPT + i);
         e_mask[pos] = qmask[i];
-        ++pos;
       }
     }
   }
@@ -318,23 +334,37 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_mfma(AttendArgs A) {
   const bf16_t* Vc = reinterpret_cast<const bf16_t*>(A.V) + (int64_t)b * A.sb + (int64_t)h * A.sh;
 
   const int n_groups = (n_ent + 3) / 4;
-  auto load_group = [&](int g, uint4* kf, uint4* vf) {
-    {
-      const int e = 4 * g + (r16 >> 2);
-      const int64_t key = e < n_ent ? k_lo + 4 * (int64_t)e_quad[e] + (r16 & 3) : k_hi;
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-        kf[s] = key < k_hi ? ld16(Kc + key * A.st + (4 * s + kg) * 8) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < NVL; ++u) {
-      const int pi = lane + 64 * u;
-      const int kq = pi / PIECES, pc = pi % PIECES;
-      const int e = 4 * g + (kq >> 2);
-      const int64_t key = e < n_ent ? k_lo + 4 * (int64_t)e_quad[e] + (kq & 3) : k_hi;
-      vf[u] = key < k_hi ? ld16(Vc + key * A.st + pc * 8) : make_uint4(0, 0, 0, 0);
-    }
-  };
+  // groups whose valid entries all hold a routed chunk read cached logits
+  auto cached = [&](int g) { return min(4 * g + 3, n_ent - 1) < n_r; };
+  const float* lbase =
+      A.logits ? A.logits + (((int64_t)cache * ((A.QC + 15) / 16) + (qg0 + r16) / 16) * A.nquads) * A.QW * 4 : nullptr;
+  // Loads of one 16-key group into the register arrays KA (K rows, A
+  // operand, when the logits are computed here), VA (V rows, FMA layout)
+  // and LG (the 4 cached logits of entry 4g + kg for query r16).  Every
+  // slot is assigned on every path so the arrays stay in registers.
+#define ZHA_LOAD_GROUP(g, KA, VA, LG)                                                        \
+  do {                                                                                       \
+    const bool cg_ = cached(g);                                                              \
+    {                                                                                        \
+      const int e_ = 4 * (g) + kg;                                                           \
+      const bool ok_ = cg_ && e_ < n_ent && r16 < nq;                                        \
+      const int64_t quad_ = (k_lo >> 2) + (ok_ ? (int64_t)e_quad[e_] : 0);                   \
+      LG = ok_ ? ld16(lbase + (quad_ * A.QW + (qg0 + r16) % 16) * 4) : make_uint4(0, 0, 0, 0); \
+    }                                                                                        \
+    {                                                                                        \
+      const int e_ = 4 * (g) + (r16 >> 2);                                                   \
+      const int64_t key_ = (!cg_ && e_ < n_ent) ? k_lo + 4 * (int64_t)e_quad[e_] + (r16 & 3) : k_hi; \
+      _Pragma("unroll") for (int s_ = 0; s_ < NS; ++s_) KA[s_] =                             \
+          key_ < k_hi ? ld16(Kc + key_ * A.st + (4 * s_ + kg) * 8) : make_uint4(0, 0, 0, 0); \
+    }                                                                                        \
+    _Pragma("unroll") for (int u_ = 0; u_ < NVL; ++u_) {                                     \
+      const int pi_ = lane + 64 * u_;                                                        \
+      const int kq_ = pi_ / PIECES, pc_ = pi_ % PIECES;                                      \
+      const int e_ = 4 * (g) + (kq_ >> 2);                                                   \
+      const int64_t key_ = e_ < n_ent ? k_lo + 4 * (int64_t)e_quad[e_] + (kq_ & 3) : k_hi;   \
+      VA[u_] = key_ < k_hi ? ld16(Vc + key_ * A.st + pc_ * 8) : make_uint4(0, 0, 0, 0);      \
+    }                                                                                        \
+  } while (0)
 
   float m = kNegInf, l = 0.f;  // softmax state of query r16 (MFMA layout)
   float acc[QG][8];            // V accumulators of piece (lane % PIECES) (FMA layout)
@@ -343,25 +373,35 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_mfma(AttendArgs A) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[u][e] = 0.f;
 
-  uint4 kf[NS], vf[NVL], kn[NS], vn[NVL];
-  if (wave < n_groups) load_group(wave, kf, vf);
-  const int rounds = (n_groups + 3) / 4;
-  for (int rd = 0; rd < rounds; ++rd) {
-    const int g = rd * 4 + wave;
-    const bool live = g < n_groups;
-    if (g + 4 < n_groups) load_group(g + 4, kn, vn);
-    if (live) {
-      f32x4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < NS; ++s) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[s]), bq[s], z, 0, 0, 0);
+  // each wave walks its own groups (g = wave, wave + 4, ...); the LDS slots
+  // it exchanges through are its own, so only wave-scope barriers are needed
+  uint4 kf[NS], vf[NVL], lf, kn[NS], vn[NVL], ln;
+  if (wave < n_groups) ZHA_LOAD_GROUP(wave, kf, vf, lf);
+  for (int g = wave; g < n_groups; g += 4) {
+    if (g + 4 < n_groups) ZHA_LOAD_GROUP(g + 4, kn, vn, ln);
+    {
       // lane: keys 4*kg + i of the group (entry 4g + kg), query r16
+      float zl[4];
+      if (cached(g)) {
+        const uint4 c = lf;
+        zl[0] = __uint_as_float(c.x);
+        zl[1] = __uint_as_float(c.y);
+        zl[2] = __uint_as_float(c.z);
+        zl[3] = __uint_as_float(c.w);
+      } else {
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NS; ++s) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[s]), bq[s], z, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zl[i] = z[i] * A.inv_sqrt_d;
+      }
       const int e = 4 * g + kg;
       const unsigned long long msk = (e < n_ent && r16 < QG) ? e_mask[e] >> (r16 * 4) : 0ull;
       float zz[4];
       float mb = kNegInf;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        zz[i] = ((msk >> i) & 1ull) ? z[i] * A.inv_sqrt_d : kNegInf;
+        zz[i] = ((msk >> i) & 1ull) ? zl[i] : kNegInf;
         mb = fmaxf(mb, zz[i]);
       }
       mb = fmaxf(mb, __shfl_xor(mb, 16));
@@ -387,8 +427,8 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_mfma(AttendArgs A) {
       for (int i = 0; i < 4; ++i) p_lds[wave][4 * kg + i][r16] = pz[i];
       if (kg == 0) sc_lds[wave][r16] = sc;
     }
-    __syncthreads();
-    if (live) {
+    wave_sync();
+    {
       float scq[QG];
 #pragma unroll
       for (int u = 0; u < QG; ++u) scq[u] = sc_lds[wave][u];
@@ -409,12 +449,14 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_mfma(AttendArgs A) {
         }
       }
     }
-    __syncthreads();
+    wave_sync();
 #pragma unroll
     for (int s = 0; s < NS; ++s) kf[s] = kn[s];
 #pragma unroll
     for (int v = 0; v < NVL; ++v) vf[v] = vn[v];
+    lf = ln;
   }
+#undef ZHA_LOAD_GROUP
 
   // lanes sharing a piece hold partial V sums of different keys: add them
 #pragma unroll

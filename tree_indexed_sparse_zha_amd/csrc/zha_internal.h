@@ -76,6 +76,9 @@ struct ScoreArgs {
   int leaf_weights;            // level 1 in the weights form: g holds w [R][C] fp32
   const void* K;               // keys (weights form only)
   int64_t ksb, ksh, kst;
+  float* logits;               // optional [caches][ceil(QC/16)][nquads][QW][4] (weights form)
+  int64_t nquads;              // 4-key quads per cache in the logits buffer
+  int QW;                      // min(QC, 16)
 };
 
 struct SelectArgs {
@@ -105,6 +108,9 @@ struct AttendArgs {
   int64_t tile_keys;  // keys per workgroup
   int64_t n_tiles;
   float* partial;     // [n_queries][n_tiles][D + 2]
+  const float* logits;  // optional, see ScoreArgs
+  int64_t nquads;
+  int QW;
   float* out;
   float* lse;
   float inv_sqrt_d;

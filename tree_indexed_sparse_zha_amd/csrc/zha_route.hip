@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs A) {
 // chunks is a candidate of any query; weights are staged only for candidate
 // chunks.
 
-template <int D, int C>
+template <int D, int C, int RT>  // RT: R as a compile-time constant, 0 = runtime
 __global__ __launch_bounds__(256) void k_score_leafw(ScoreArgs A) {
   constexpr int NS = D / 32;
   constexpr int KT = 256;       // keys per tile
@@ -331,17 +331,23 @@ __global__ __launch_bounds__(256) void k_score_leafw(ScoreArgs A) {
     float zz[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) zz[i] = z[i] * A.inv_sqrt_d;
-    const bool xc = (anybits >> x) & 1ull;
+    const int64_t quad = (k0 + g * 16) / 4 + kg;
+    if (A.logits && qn < nq && quad < A.nquads) {
+      // keep the attention logits of these 4 keys for query qn (zha_attend reads them)
+      float* lp = A.logits + ((((int64_t)cache * gridDim.z + blockIdx.z) * A.nquads + quad) * A.QW + qn) * 4;
+      *reinterpret_cast<float4*>(lp) = make_float4(zz[0], zz[1], zz[2], zz[3]);
+    }
+    // fold the 4 logits with every plane of the chunk (rows of chunks that
+    // are no candidate hold stale LDS data; their result is discarded below)
     float best = kNegInf;
-    for (int j = 0; j < R; ++j) {
-      float v = 0.f;
-      if (xc) {
-        const float4 wv = wl[x][j][part];
-        v = wv.x * zz[0] + wv.y * zz[1] + wv.z * zz[2] + wv.w * zz[3];
-      }
+    const int RR = RT > 0 ? RT : R;
+#pragma unroll 4
+    for (int jj = 0; jj < RR; ++jj) {
+      const float4 wv = wl[x][jj][part];
+      float v = wv.x * zz[0] + wv.y * zz[1] + wv.z * zz[2] + wv.w * zz[3];
 #pragma unroll
       for (int o = 16; o < 16 * PARTS; o <<= 1) v += __shfl_xor(v, o);
-      if (xc) best = fmaxf(best, cl[x][j] + v);
+      best = fmaxf(best, cl[x][jj] + v);
     }
     if (part == 0) sc[qn][x] = ((mybits >> x) & 1ull) ? best : kNegInf;
   }
@@ -672,7 +678,15 @@ hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dty
     prof.begin(ZHA_K_SCORE, level);
     if (sa.leaf_weights) {
       dim3 grid((unsigned)((sa.n_nodes * sa.C + 255) / 256), (unsigned)n_caches, (unsigned)((sa.QC + 15) / 16));
-#define ZHA_LW(DD, CC) hipLaunchKernelGGL((k_score_leafw<DD, CC>), grid, dim3(256), 0, s, sa)
+#define ZHA_LW(DD, CC)                                                              \
+  do {                                                                              \
+    if (sa.R == 16)                                                                 \
+      hipLaunchKernelGGL((k_score_leafw<DD, CC, 16>), grid, dim3(256), 0, s, sa);   \
+    else if (sa.R == 1)                                                             \
+      hipLaunchKernelGGL((k_score_leafw<DD, CC, 1>), grid, dim3(256), 0, s, sa);    \
+    else                                                                            \
+      hipLaunchKernelGGL((k_score_leafw<DD, CC, 0>), grid, dim3(256), 0, s, sa);    \
+  } while (0)
       if (sa.D == 128) {
         if (sa.C == 4) ZHA_LW(128, 4);
         else if (sa.C == 8) ZHA_LW(128, 8);

@@ -80,6 +80,7 @@ class RouteLayout(ct.Structure):
         ("score_floats_total", ct.c_int64),
         ("stats_total", ct.c_int64),
         ("workspace_bytes", ct.c_int64),
+        ("logits_floats", ct.c_int64),
     ]
 
 
@@ -172,8 +173,8 @@ def load(path: str = LIB_PATH) -> ct.CDLL:
         "zha_attend_workspace_bytes": (I64, [cfgp, I32]),
         "zha_build": (ct.c_int, [cfgp, P, i64p, I64, P, P, P, P]),
         "zha_append": (ct.c_int, [cfgp, P, i64p, I64, I64, P, P, P, P]),
-        "zha_route": (ct.c_int, [cfgp, P, I64, P, i64p, I32, F, P, i64p, P, P, P, P, I64, P, P]),
-        "zha_attend": (ct.c_int, [cfgp, P, i64p, I32, P, P, i64p, I64, P, I64, ct.c_uint32, P, P, P, I64, P, P]),
+        "zha_route": (ct.c_int, [cfgp, P, I64, P, i64p, I32, F, P, i64p, P, P, P, P, P, I64, P, P]),
+        "zha_attend": (ct.c_int, [cfgp, P, i64p, I32, P, P, i64p, I64, P, I64, P, ct.c_uint32, P, P, P, I64, P, P]),
         "zha_dense_decode": (ct.c_int, [cfgp, P, i64p, I32, P, P, i64p, I64, P, P, P, I64, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -307,16 +308,23 @@ class RouteBuffers:
     stats: torch.Tensor  # uint8 [n_records * 40]
     ws: torch.Tensor
     layout: RouteLayout
+    logits: Optional[torch.Tensor] = None  # level-1 attention logits (weights form)
 
 
-def alloc_route(cfg: ZhaConfig, T: int, device="cuda") -> RouteBuffers:
+def alloc_route(cfg: ZhaConfig, T: int, device="cuda", logits: bool = False) -> RouteBuffers:
+    """Route outputs; ``logits`` also allocates the level-1 logits buffer
+    (leaf-weights form) that zha_attend can read instead of the keys."""
     rl = route_layout(cfg, T)
+    lg = None
+    if logits and int(rl.logits_floats) > 0:
+        lg = torch.empty(int(rl.logits_floats), dtype=torch.float32, device=device)
     return RouteBuffers(
         sel=torch.zeros(int(rl.sel_words_total), dtype=torch.int32, device=device),
         score=torch.empty(int(rl.score_floats_total), dtype=torch.float32, device=device),
         stats=torch.zeros(max(1, int(rl.stats_total)) * STATS_BYTES, dtype=torch.uint8, device=device),
         ws=torch.empty(max(256, int(rl.workspace_bytes)), dtype=torch.uint8, device=device),
         layout=rl,
+        logits=lg,
     )
 
 
@@ -339,6 +347,7 @@ def route(cfg: ZhaConfig, tree: torch.Tensor, n_tokens: int, Q: torch.Tensor, T:
             _ptr(buf.sel),
             _ptr(buf.score),
             _ptr(buf.stats),
+            _ptr(buf.logits),
             _ptr(buf.ws),
             int(buf.ws.numel()),
             _prof(ev),
@@ -368,6 +377,7 @@ def attend(
     lse: Optional[torch.Tensor],
     ws: torch.Tensor,
     ev=None,
+    logits: Optional[torch.Tensor] = None,
 ):
     c = cfg.c()
     qs = _i64(*_elem_strides(Q, 4))
@@ -387,6 +397,7 @@ def attend(
             int(n_tokens),
             _ptr(sel1),
             words,
+            _ptr(logits),
             int(flags),
             _ptr(out),
             _ptr(lse),
