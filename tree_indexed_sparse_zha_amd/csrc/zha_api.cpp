@@ -242,6 +242,18 @@ int zha_get_tree_layout(const zha_config* cfg, zha_tree_layout* out) {
   return ZHA_OK;
 }
 
+// Key-range slots of every level: offsets (in uint32 units) into the route
+// workspace when `off` is given; returns the bytes needed.
+static int64_t kr_total(const zha_config* cfg, const zha_tree_layout& tl, int64_t n_queries, int64_t* off) {
+  int64_t words = 0;
+  for (int l = 0; l < cfg->levels; ++l) {
+    const bool lw = cfg->leaf_form == ZHA_LEAF_WEIGHTS && l == 0;
+    if (off) off[l] = words;
+    words += n_queries * zha::route_kr_slots(cfg->kv_dtype, lw, tl.node_cap[l], cfg->chunk) * 4;
+  }
+  return words * 4;
+}
+
 int zha_get_route_layout(const zha_config* cfg, int32_t T, zha_route_layout* out) {
   int rc = check_config(cfg);
   if (rc) return rc;
@@ -266,8 +278,9 @@ int zha_get_route_layout(const zha_config* cfg, int32_t T, zha_route_layout* out
   out->sel_words_total = sw > 0 ? sw : 1;
   out->score_floats_total = sf > 0 ? sf : 1;
   out->stats_total = ss;
-  // per level and query: candidate key range and count, filled by the score kernel
-  out->workspace_bytes = align256((int64_t)cfg->levels * out->n_queries * 16);
+  // per level, query and score tile: candidate key range and count, written
+  // by the score kernel and reduced by the select kernel
+  out->workspace_bytes = align256(kr_total(cfg, tl, out->n_queries, nullptr));
   if (cfg->leaf_form == ZHA_LEAF_WEIGHTS) {
     const int64_t QC = (int64_t)cfg->q_per_kv * T;
     out->logits_floats = (int64_t)cfg->batch * cfg->n_kv_heads * cdiv(QC, 16) *
@@ -331,8 +344,11 @@ int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const v
   if (prof) prof->n_used = 0;
   zha::Prof pr{prof, static_cast<hipStream_t>(stream)};
   uint32_t* keyrange = static_cast<uint32_t*>(ws);
-  {
-    hipError_t e = zha::launch_route_init(keyrange, (int64_t)cfg->levels * rl.n_queries, pr);
+  int64_t kr_off[ZHA_MAX_LEVELS];
+  const int64_t kr_bytes = kr_total(cfg, tl, rl.n_queries, kr_off);
+  if (cfg->kv_dtype != ZHA_BF16) {
+    // the fp32 score kernel accumulates its single slot per query with atomics
+    hipError_t e = zha::launch_route_init(keyrange, kr_bytes / 16, pr);
     if (e != hipSuccess) return hip_fail(e, "route init launch");
   }
   for (int l = cfg->levels - 1; l >= 0; --l) {
@@ -358,7 +374,8 @@ int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const v
     sa.parent_words = (l == cfg->levels - 1) ? 0 : rl.words[l + 1];
     sa.score = score + rl.score_offset[l];
     sa.score_stride = rl.score_stride[l];
-    sa.keyrange = keyrange + (int64_t)l * rl.n_queries * 4;
+    sa.keyrange = keyrange + kr_off[l];
+    sa.kr_slots = zha::route_kr_slots(cfg->kv_dtype, leafw && l == 0, tl.node_cap[l], cfg->chunk);
     sa.inv_sqrt_d = isd;
     sa.leaf_weights = leafw && l == 0;
     if (sa.leaf_weights) {
@@ -375,6 +392,7 @@ int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const v
     se.score = sa.score;
     se.score_stride = sa.score_stride;
     se.keyrange = sa.keyrange;
+    se.kr_slots = sa.kr_slots;
     se.n_nodes = n[l];
     se.sel = sel + rl.sel_offset[l];
     se.words = rl.words[l];

@@ -24,12 +24,6 @@ namespace {
 
 constexpr int kAttThreads = 256;
 
-// Wave-scope barrier for LDS regions private to one wave.
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 constexpr int kQG = 4;  // queries per workgroup
 constexpr int kU = 4;   // wave steps per batch
 
@@ -500,6 +494,255 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_mfma(AttendArgs A) {
   }
 }
 
+// bf16 path with the route's cached level-1 logits: V streaming only.
+//
+// Phase 1 compacts the selected quads as above (routed quads first, then the
+// at most 5 quads that hold forced keys only: the sink's quad and the
+// current chunk, which lies inside one tile).  The logits of those few are
+// computed once into LDS.  Phase 2: lanes are (quad of the step, key of the
+// quad, 16-byte piece of the row); each wave takes every 4th step, with up
+// to 8 steps of V (one coalesced 1 KiB load per quad for d = 128) and their
+// cached logits in flight at once (fewer for larger query groups, whose
+// accumulators take the registers), and keeps a per-lane online softmax
+// (one rescale per batch) in fp32.  No LDS traffic or barrier in the loop.
+constexpr int kMaxForcedQuads = 8;
+
+template <int D, int QG>
+__global__ __launch_bounds__(kAttThreads) void k_attend_cached(AttendArgs A) {
+  constexpr int PIECES = D / 8;   // 16-byte pieces per row
+  constexpr int LPQ = 4 * PIECES; // lanes per quad
+  constexpr int EPS = 64 / LPQ;   // quads per wave step
+  constexpr int QPT = kTileQuadsMax / kAttThreads;
+  constexpr int kU2 = QG <= 4 ? 8 : QG <= 8 ? 4 : 2;  // steps in flight
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cache = blockIdx.y;
+  const int qg0 = blockIdx.z * QG;
+  const int nq = min(QG, A.QC - qg0);
+  const int64_t tile = blockIdx.x;
+  const int b = cache / A.H, h = cache % A.H;
+  const int64_t k_lo = tile * A.tile_keys;
+  const int64_t k_hi = min(A.n_tokens, k_lo + A.tile_keys);
+  const int nquads = (int)((k_hi - k_lo + 3) / 4);
+  const bool sink = A.flags & 1u, last = A.flags & 2u;
+  const int64_t last_start = (int64_t)A.C * ((A.n_tokens - 1) / A.C);
+
+  __shared__ uint16_t e_quad[kTileQuadsMax];
+  __shared__ unsigned long long e_mask[kTileQuadsMax];
+  __shared__ int scan[kAttThreads];
+  __shared__ float f_log[kMaxForcedQuads][QG][4];
+  __shared__ float red[4][QG][D + 2];
+
+  // ---- phase 1
+  unsigned long long qmask[QPT];
+  uint32_t qrouted = 0u;
+  int cnt = 0;  // routed count in the low 16 bits, forced-only count above
+  {
+    const uint32_t* srow[QG];
+#pragma unroll
+    for (int u = 0; u < QG; ++u)
+      srow[u] = A.sel1 + ((int64_t)cache * A.QC + qg0 + (u < nq ? u : 0)) * A.sel_words;
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int qd = tid * QPT + i;
+      unsigned long long msk = 0ull;
+      bool routed = false;
+      if (qd < nquads) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int64_t key = k_lo + 4 * qd + kk;
+          if (key >= k_hi) break;
+          const bool forced = (sink && key == 0) || (last && key >= last_start);
+          const int64_t chunk = key / A.C;
+          const bool has_chunk = chunk < A.n_chunks;
+#pragma unroll
+          for (int u = 0; u < QG; ++u) {
+            if (u >= nq) break;
+            bool bit = false;
+            if (has_chunk) bit = (srow[u][chunk >> 5] >> (chunk & 31)) & 1u;
+            routed = routed || bit;
+            if (forced || bit) msk |= 1ull << (u * 4 + kk);
+          }
+        }
+      }
+      qmask[i] = msk;
+      if (routed) qrouted |= 1u << i;
+      if (msk) cnt += routed ? 1 : (1 << 16);
+    }
+  }
+  scan[tid] = cnt;
+  __syncthreads();
+  for (int off = 1; off < kAttThreads; off <<= 1) {
+    const int add = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  const int n_r = scan[kAttThreads - 1] & 0xffff;
+  const int n_f = min(scan[kAttThreads - 1] >> 16, kMaxForcedQuads);
+  const int n_ent = n_r + n_f;
+  {
+    int pos_r = (scan[tid] - cnt) & 0xffff;
+    int pos_f = n_r + ((scan[tid] - cnt) >> 16);
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      if (qmask[i]) {
+        const int pos = ((qrouted >> i) & 1u) ? pos_r++ : pos_f++;
+        if (pos < n_ent) {
+          e_quad[pos] = (uint16_t)(tid * QPT + i);
+          e_mask[pos] = qmask[i];
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  const bf16_t* Kc = reinterpret_cast<const bf16_t*>(A.K) + (int64_t)b * A.sb + (int64_t)h * A.sh;
+  const bf16_t* Vc = reinterpret_cast<const bf16_t*>(A.V) + (int64_t)b * A.sb + (int64_t)h * A.sh;
+
+  // ---- phase 1b: logits of the forced-only quads (one thread per key and query)
+  if (n_f) {
+    for (int idx = tid; idx < n_f * 4 * QG; idx += kAttThreads) {
+      const int f = idx / (4 * QG), kk = (idx / QG) % 4, u = idx % QG;
+      const int64_t key = k_lo + 4 * (int64_t)e_quad[n_r + f] + kk;
+      float z = kNegInf;
+      if (u < nq && key < k_hi) {
+        const int qi = qg0 + u;
+        const bf16_t* qp = reinterpret_cast<const bf16_t*>(A.Q) + (int64_t)b * A.qsb + (int64_t)h * A.qsh +
+                           (int64_t)(qi / A.T) * A.qsg + (int64_t)(qi % A.T) * A.qst;
+        const bf16_t* kp = Kc + key * A.st;
+        float dot = 0.f;
+#pragma unroll
+        for (int pc = 0; pc < PIECES; ++pc) {
+          float kv[8], qv[8];
+          unpack(ld16(kp + pc * 8), kv, bf16_t());
+          unpack(ld16(qp + pc * 8), qv, bf16_t());
+#pragma unroll
+          for (int x = 0; x < 8; ++x) dot += kv[x] * qv[x];
+        }
+        z = dot * A.inv_sqrt_d;
+      }
+      f_log[f][u][kk] = z;
+    }
+    __syncthreads();
+  }
+
+  // ---- phase 2
+  const int qs = lane / LPQ, kk = (lane % LPQ) / PIECES, pc = lane % PIECES;
+  const float* lbase = A.logits + ((int64_t)cache * ((A.QC + 15) / 16) + qg0 / 16) * A.nquads * A.QW * 4;
+  const int qoff = qg0 % 16;
+  float m[QG], lsum[QG], acc[QG][8];
+#pragma unroll
+  for (int u = 0; u < QG; ++u) {
+    m[u] = kNegInf;
+    lsum[u] = 0.f;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) acc[u][x] = 0.f;
+  }
+  constexpr int STRIDE = 4 * EPS;
+  for (int e0 = wave * EPS + qs; e0 < n_ent; e0 += STRIDE * kU2) {
+    uint4 vr[kU2];
+    float z[kU2][QG];
+#pragma unroll
+    for (int t = 0; t < kU2; ++t) {
+      const int e = e0 + t * STRIDE;
+      const bool ok = e < n_ent;
+      const int quad = ok ? e_quad[e] : 0;
+      const unsigned long long msk = ok ? e_mask[e] >> kk : 0ull;
+      const int64_t key = k_lo + 4 * (int64_t)quad + kk;
+      vr[t] = (ok && key < k_hi) ? ld16(Vc + key * A.st + pc * 8) : make_uint4(0, 0, 0, 0);
+      if (e < n_r) {
+        const float* lp = lbase + (((k_lo >> 2) + quad) * A.QW + qoff) * 4 + kk;
+#pragma unroll
+        for (int u = 0; u < QG; ++u) z[t][u] = ((msk >> (4 * u)) & 1ull) ? lp[4 * u] : kNegInf;
+      } else {
+#pragma unroll
+        for (int u = 0; u < QG; ++u) z[t][u] = ((msk >> (4 * u)) & 1ull) ? f_log[ok ? e - n_r : 0][u][kk] : kNegInf;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < QG; ++u) {
+      float bm = z[0][u];
+#pragma unroll
+      for (int t = 1; t < kU2; ++t) bm = fmaxf(bm, z[t][u]);
+      const float mn = fmaxf(m[u], bm);
+      if (mn > m[u]) {
+        const float sc = __expf(m[u] - mn);
+        lsum[u] *= sc;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc[u][x] *= sc;
+        m[u] = mn;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kU2; ++t) {
+      float vv[8];
+      unpack(vr[t], vv, bf16_t());
+#pragma unroll
+      for (int u = 0; u < QG; ++u) {
+        const float pw = z[t][u] == kNegInf ? 0.f : __expf(z[t][u] - m[u]);
+        lsum[u] += pw;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc[u][x] += pw * vv[x];
+      }
+    }
+  }
+
+  // merge the lanes that share a piece (different keys): common max, then sums
+#pragma unroll
+  for (int u = 0; u < QG; ++u) {
+    const float mw = wave_max_xor(m[u], PIECES, 64);
+    const float f = mw == kNegInf ? 0.f : __expf(m[u] - mw);
+    lsum[u] *= f;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) acc[u][x] *= f;
+    m[u] = mw;
+  }
+#pragma unroll
+  for (int off = PIECES; off < 64; off <<= 1)
+#pragma unroll
+    for (int u = 0; u < QG; ++u) {
+      lsum[u] += __shfl_xor(lsum[u], off);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) acc[u][x] += __shfl_xor(acc[u][x], off);
+    }
+  if (lane < PIECES) {
+#pragma unroll
+    for (int u = 0; u < QG; ++u)
+#pragma unroll
+      for (int x = 0; x < 8; ++x) red[wave][u][lane * 8 + x] = acc[u][x];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int u = 0; u < QG; ++u) {
+      red[wave][u][D] = m[u];
+      red[wave][u][D + 1] = lsum[u];
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < QG * D; idx += kAttThreads) {
+    const int u = idx / D, d = idx % D;
+    if (u >= nq) continue;
+    float mm = kNegInf;
+    for (int w = 0; w < 4; ++w) mm = fmaxf(mm, red[w][u][D]);
+    float ll = 0.f, o = 0.f;
+    if (mm != kNegInf) {
+      for (int w = 0; w < 4; ++w) {
+        const float mw = red[w][u][D];
+        if (mw == kNegInf) continue;
+        const float f = __expf(mw - mm);
+        ll += red[w][u][D + 1] * f;
+        o += red[w][u][d] * f;
+      }
+    }
+    float* part = A.partial + (((int64_t)cache * A.QC + qg0 + u) * A.n_tiles + tile) * (D + 2);
+    if (d == 0) {
+      part[0] = mm;
+      part[1] = ll;
+    }
+    part[2 + d] = o;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(D) void k_combine(AttendArgs A) {
   const int64_t q = blockIdx.x;
@@ -527,8 +770,23 @@ void launch_mfma(const AttendArgs& a, int n_caches, hipStream_t s) {
   hipLaunchKernelGGL((k_attend_mfma<D, QG>), grid, dim3(kAttThreads), 0, s, a);
 }
 
+template <int D, int QG>
+void launch_cached(const AttendArgs& a, int n_caches, hipStream_t s) {
+  dim3 grid((unsigned)a.n_tiles, (unsigned)n_caches, (unsigned)((a.QC + QG - 1) / QG));
+  hipLaunchKernelGGL((k_attend_cached<D, QG>), grid, dim3(kAttThreads), 0, s, a);
+}
+
 template <int D>
 void launch_mfma_qg(const AttendArgs& a, int n_caches, hipStream_t s) {
+  if (a.logits) {
+    if (a.QC <= 4)
+      launch_cached<D, 4>(a, n_caches, s);
+    else if (a.QC <= 8)
+      launch_cached<D, 8>(a, n_caches, s);
+    else
+      launch_cached<D, 16>(a, n_caches, s);
+    return;
+  }
   if (a.QC <= 4)
     launch_mfma<D, 4>(a, n_caches, s);
   else if (a.QC <= 8)

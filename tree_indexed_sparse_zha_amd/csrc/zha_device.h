@@ -28,6 +28,29 @@ struct Elem<bf16_t> {
 };
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Raw buffer loads: the base is wave-uniform, offsets are bytes, and a load
+// at an offset past `bytes` returns zeros (no branch, no fault), so masked
+// loads need no control flow.  kOffNone is such an offset.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOffNone = 0x80000000u;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // base and size are wave-uniform by contract: take lane 0's so that they
+  // live in scalar registers whatever the compiler proved
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 bld16(rsrc_t r, uint32_t off) {
+  typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+  const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ float bld4f(rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 
 // Unpack one 16-byte piece into fp32 values.
@@ -95,5 +118,12 @@ __device__ __forceinline__ float wave_sum_xor(float v, int from, int to) {
 }
 
 constexpr float kNegInf = -__builtin_huge_valf();
+
+// Wave-scope barrier for LDS regions private to one wave.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 }  // namespace zha

@@ -71,7 +71,8 @@ struct ScoreArgs {
   int64_t parent_words;        // words per query row of sel_parent
   float* score;                // [n_queries][score_stride] for this level
   int64_t score_stride;
-  uint32_t* keyrange;          // [n_queries][4]: max key, min key, candidate count, 0
+  uint32_t* keyrange;          // [n_queries][kr_slots][4]: max key, min key, candidate count, 0
+  int64_t kr_slots;            // slots per query: one per score tile (plain stores), or 1 (atomics)
   float inv_sqrt_d;
   int leaf_weights;            // level 1 in the weights form: g holds w [R][C] fp32
   const void* K;               // keys (weights form only)
@@ -85,6 +86,8 @@ struct SelectArgs {
   const float* score;  // [n_queries][score_stride]
   int64_t score_stride;
   const uint32_t* keyrange;  // written by the score kernel of the same level
+  int64_t kr_slots;          // slot stride per query
+  int64_t kr_used;           // slots the score kernel wrote (its tile count, or 1)
   int64_t n_nodes;
   uint32_t* sel;       // [n_queries][words]
   int64_t words;
@@ -118,6 +121,9 @@ struct AttendArgs {
 
 hipError_t launch_build(const BuildArgs& a, int dtype, Prof& prof);
 hipError_t launch_route_init(uint32_t* keyrange, int64_t n, Prof& prof);
+// key-range slots per query of one level's score kernel, for a level of
+// `node_cap` nodes: one per tile for the bf16 kernels, 1 for the fp32 one
+int64_t route_kr_slots(int dtype, bool leaf_weights, int64_t node_cap, int C);
 hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dtype, int n_caches,
                               int level, Prof& prof);
 hipError_t launch_attend(const AttendArgs& a, int dtype, int n_caches, Prof& prof);

@@ -48,19 +48,21 @@ static_assert(sizeof(SelStats) == 40, "stats layout");
 
 // Folds one wave's candidates (flag c, key k per lane) into a query's
 // [max key, min key, count] record.
-__device__ __forceinline__ void publish_range(uint32_t* kr, bool c, uint32_t k) {
+// Candidate key range and count of one score tile for one query, reduced
+// over the wave's lanes and stored (plain store, no atomics) into the
+// tile's slot; the select kernel reduces the slots.  Every tile writes its
+// slot, also when it has no candidate (max 0, min ~0, count 0).
+__device__ __forceinline__ void publish_range(uint32_t* slot, bool c, uint32_t k) {
   const unsigned long long bal = __ballot(c);
-  if (bal == 0ull) return;
   uint32_t kmax = c ? k : 0u, kmin = c ? k : 0xffffffffu;
-  for (int o = 1; o < 64; o <<= 1) {
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+  if (bal != 0ull) {
+    for (int o = 1; o < 64; o <<= 1) {
+      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+    }
   }
-  if ((threadIdx.x & 63) == 0) {
-    atomicMax(&kr[0], kmax);
-    atomicMin(&kr[1], kmin);
-    atomicAdd(&kr[2], (uint32_t)__popcll(bal));
-  }
+  if ((threadIdx.x & 63) == 0)
+    *reinterpret_cast<uint4*>(slot) = make_uint4(kmax, kmin, (uint32_t)__popcll(bal), 0u);
 }
 
 __global__ void k_route_init(uint32_t* kr, int64_t n) {
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs A) {
   for (int q = wave; q < nq; q += 4) {
     const float v = sc[q][lane];
     const bool c = n0 + lane < A.n_nodes && v > kNegInf;
-    publish_range(A.keyrange + ((int64_t)cache * A.QC + qg0 + q) * 4, c, order_key(v));
+    publish_range(A.keyrange + (((int64_t)cache * A.QC + qg0 + q) * A.kr_slots + blockIdx.x) * 4, c, order_key(v));
   }
 }
 
@@ -214,8 +216,12 @@ __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs A) {
 // chunks is a candidate of any query; weights are staged only for candidate
 // chunks.
 
-template <int D, int C, int RT>  // RT: R as a compile-time constant, 0 = runtime
-__global__ __launch_bounds__(256) void k_score_leafw(ScoreArgs A) {
+// RT: R as a compile-time constant (0 = runtime).  Q4: at most 4 queries per
+// cache; the MFMA then fills only 4 of its 16 query columns, so the logits
+// go through LDS and the plane fold runs with lanes = (chunk, part, query),
+// every lane busy.
+template <int D, int C, int RT, bool Q4>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_score_leafw(ScoreArgs A) {
   constexpr int NS = D / 32;
   constexpr int KT = 256;       // keys per tile
   constexpr int NCH = KT / C;   // chunks per tile (<= 64)
@@ -230,9 +236,12 @@ __global__ __launch_bounds__(256) void k_score_leafw(ScoreArgs A) {
   const int R = A.R;
   const int qn = lane & 15, kg = lane >> 4;
   const int64_t n_keys = A.n_nodes * C;  // keys of complete chunks
+  constexpr int WROW = 16 * PARTS + 1;  // padded: chunks start on different banks
   __shared__ float sc[16][NCH + 1];
-  __shared__ float4 wl[NCH][16][PARTS];  // w of chunk x, plane j, 4-key part
-  __shared__ float cl[NCH][16];
+  __shared__ float4 wl[NCH][WROW];  // w of chunk x, plane j, 4-key part at [x][j * PARTS + part]
+  __shared__ float cl[NCH][17];
+  __shared__ float4 zl[Q4 ? 4 : 1][16][4];  // Q4: [wave][quad of the wave][query] logits
+  __shared__ unsigned long long mbl[16];    // candidate bits per query
 
   bf16x8 bq[NS];
   {
@@ -276,32 +285,31 @@ __global__ __launch_bounds__(256) void k_score_leafw(ScoreArgs A) {
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) anybits |= __shfl_xor(anybits, o);
 
-  // stage w and c of the candidate chunks: all loads first, then the stores
-  {
-    constexpr int ITEMS = NCH * 16 / 256;
-    float4 wst[ITEMS][PARTS];
-    float cst[ITEMS];
+  // All loads of the tile are issued together as buffer loads (masked rows
+  // read zeros): w and c of the candidate chunks first, then the K rows of
+  // this wave's live groups; only the w/c loads are waited for before the
+  // LDS stores, the K loads stay in flight across the barrier.
+  const int64_t n_valid = min((int64_t)NCH, A.n_nodes - m0);  // chunks of this tile (>= 1)
+  const rsrc_t wr = make_rsrc(wcache + m0 * R * C, (uint32_t)(n_valid * R * C * 4));
+  const rsrc_t cr = make_rsrc(ccache + m0 * R, (uint32_t)(n_valid * R * 4));
+  const int64_t rows = min((int64_t)KT, n_keys - k0);  // keys of complete chunks in this tile
+  const rsrc_t kr = make_rsrc(Kc + k0 * A.kst, (uint32_t)((rows - 1) * A.kst * 2 + D * 2));
+  constexpr int ITEMS = NCH * 16 / 256;
+  float4 wst[ITEMS][PARTS];
+  float cst[ITEMS];
 #pragma unroll
-    for (int r = 0; r < ITEMS; ++r) {
-      const int it = tid + 256 * r;
-      const int x = it / 16, j = it % 16;
-      const int64_t m = m0 + x;
-      const bool ok = ((anybits >> x) & 1ull) && j < R;
-      const float4* src = reinterpret_cast<const float4*>(wcache + (m * R + j) * C);
+  for (int r = 0; r < ITEMS; ++r) {
+    const int it = tid + 256 * r;
+    const int x = it / 16, j = it % 16;
+    const bool ok = ((anybits >> x) & 1ull) && j < R;
+    const uint32_t wo = ok ? (uint32_t)((x * R + j) * C * 4) : kOffNone;
 #pragma unroll
-      for (int pp = 0; pp < PARTS; ++pp) wst[r][pp] = ok ? src[pp] : make_float4(0.f, 0.f, 0.f, 0.f);
-      cst[r] = ok ? ccache[m * R + j] : 0.f;
+    for (int pp = 0; pp < PARTS; ++pp) {
+      const uint4 v = bld16(wr, wo + pp * 16);
+      wst[r][pp] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
     }
-#pragma unroll
-    for (int r = 0; r < ITEMS; ++r) {
-      const int it = tid + 256 * r;
-      const int x = it / 16, j = it % 16;
-#pragma unroll
-      for (int pp = 0; pp < PARTS; ++pp) wl[x][j][pp] = wst[r][pp];
-      cl[x][j] = cst[r];
-    }
+    cst[r] = bld4f(cr, ok ? (uint32_t)((x * R + j) * 4) : kOffNone);
   }
-  // K rows of this wave's live groups (A operand: row qn = key, k-group kg)
   uint4 kf[GPW][NS];
   bool live[GPW];
 #pragma unroll
@@ -309,20 +317,30 @@ __global__ __launch_bounds__(256) void k_score_leafw(ScoreArgs A) {
     const int g = wave * GPW + gi;
     const unsigned long long gmask = ((1ull << (16 / C)) - 1ull) << (g * 16 / C);
     live[gi] = (anybits & gmask) != 0ull;
-    const int64_t key = k0 + g * 16 + qn;
+    const uint32_t ko = live[gi] ? (uint32_t)((g * 16 + qn) * A.kst * 2) : kOffNone;
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-      kf[gi][s] = live[gi] && key < n_keys ? ld16(Kc + key * A.kst + (4 * s + kg) * 8) : make_uint4(0, 0, 0, 0);
+    for (int s = 0; s < NS; ++s) kf[gi][s] = bld16(kr, ko + (4 * s + kg) * 16);
   }
+#pragma unroll
+  for (int r = 0; r < ITEMS; ++r) {
+    const int it = tid + 256 * r;
+    const int x = it / 16, j = it % 16;
+#pragma unroll
+    for (int pp = 0; pp < PARTS; ++pp) wl[x][j * PARTS + pp] = wst[r][pp];
+    cl[x][j] = cst[r];
+  }
+  if (tid < 16) mbl[tid] = mybits;  // lanes 0..15: kg 0, query qn = tid
   __syncthreads();
 
+  const int RR = RT > 0 ? RT : R;
+  constexpr int UNR = RT <= 0 ? 1 : RT < 4 ? RT : 4;  // plane loop unroll
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
     const int g = wave * GPW + gi;
     const int x = (g * 16 + 4 * kg) / C;  // chunk (within the tile) of this lane's 4 keys
     const int part = kg % PARTS;
     if (!live[gi]) {
-      if (part == 0 && qn < 16) sc[qn][x] = kNegInf;
+      if (!Q4 && part == 0) sc[qn][x] = kNegInf;
       continue;
     }
     f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -337,19 +355,40 @@ __global__ __launch_bounds__(256) void k_score_leafw(ScoreArgs A) {
       float* lp = A.logits + ((((int64_t)cache * gridDim.z + blockIdx.z) * A.nquads + quad) * A.QW + qn) * 4;
       *reinterpret_cast<float4*>(lp) = make_float4(zz[0], zz[1], zz[2], zz[3]);
     }
-    // fold the 4 logits with every plane of the chunk (rows of chunks that
-    // are no candidate hold stale LDS data; their result is discarded below)
-    float best = kNegInf;
-    const int RR = RT > 0 ? RT : R;
-#pragma unroll 4
-    for (int jj = 0; jj < RR; ++jj) {
-      const float4 wv = wl[x][jj][part];
-      float v = wv.x * zz[0] + wv.y * zz[1] + wv.z * zz[2] + wv.w * zz[3];
+    if constexpr (Q4) {
+      if (qn < 4) zl[wave][gi * 4 + kg][qn] = make_float4(zz[0], zz[1], zz[2], zz[3]);
+    } else {
+      // fold the 4 logits with every plane of the chunk (rows of chunks that
+      // are no candidate hold stale LDS data; their result is discarded below)
+      float best = kNegInf;
+#pragma unroll UNR
+      for (int jj = 0; jj < RR; ++jj) {
+        const float4 wv = wl[x][jj * PARTS + part];
+        float v = wv.x * zz[0] + wv.y * zz[1] + wv.z * zz[2] + wv.w * zz[3];
 #pragma unroll
-      for (int o = 16; o < 16 * PARTS; o <<= 1) v += __shfl_xor(v, o);
+        for (int o = 16; o < 16 * PARTS; o <<= 1) v += __shfl_xor(v, o);
+        best = fmaxf(best, cl[x][jj] + v);
+      }
+      if (part == 0) sc[qn][x] = ((mybits >> x) & 1ull) ? best : kNegInf;
+    }
+  }
+  if constexpr (Q4) {
+    // lanes (query u, part, chunk cx) over the wave's 64 / C chunks; quads of
+    // dead groups hold stale LDS data, discarded by the candidate bit
+    wave_sync();
+    const int u = lane & 3, part = (lane >> 2) % PARTS, cx = lane / (4 * PARTS);
+    const int x = wave * (64 / C) + cx;
+    const float4 zv = zl[wave][cx * PARTS + part][u];
+    float best = kNegInf;
+#pragma unroll UNR
+    for (int jj = 0; jj < RR; ++jj) {
+      const float4 wv = wl[x][jj * PARTS + part];
+      float v = wv.x * zv.x + wv.y * zv.y + wv.z * zv.z + wv.w * zv.w;
+#pragma unroll
+      for (int o = 4; o < 4 * PARTS; o <<= 1) v += __shfl_xor(v, o);
       best = fmaxf(best, cl[x][jj] + v);
     }
-    if (part == 0) sc[qn][x] = ((mybits >> x) & 1ull) ? best : kNegInf;
+    if (part == 0 && u < nq) sc[u][x] = ((mbl[u] >> x) & 1ull) ? best : kNegInf;
   }
   __syncthreads();
   for (int idx = tid; idx < nq * NCH; idx += 256) {
@@ -360,7 +399,7 @@ __global__ __launch_bounds__(256) void k_score_leafw(ScoreArgs A) {
   for (int q = wave; q < nq; q += 4) {
     const float v = lane < NCH ? sc[q][lane] : kNegInf;
     const bool c = lane < NCH && m0 + lane < A.n_nodes && v > kNegInf;
-    publish_range(A.keyrange + ((int64_t)cache * A.QC + qg0 + q) * 4, c, order_key(v));
+    publish_range(A.keyrange + (((int64_t)cache * A.QC + qg0 + q) * A.kr_slots + blockIdx.x) * 4, c, order_key(v));
   }
 }
 
@@ -416,7 +455,7 @@ __global__ __launch_bounds__(256) void k_score_generic(ScoreArgs A) {
     if (lane == 0) {
       A.score[qg * A.score_stride + m] = v;
       if (v > kNegInf) {
-        uint32_t* kr = A.keyrange + qg * 4;
+        uint32_t* kr = A.keyrange + qg * A.kr_slots * 4;
         atomicMax(&kr[0], order_key(v));
         atomicMin(&kr[1], order_key(v));
         atomicAdd(&kr[2], 1u);
@@ -525,9 +564,39 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs A) {
     }
   };
 
-  const uint32_t* kr = A.keyrange + q * 4;
-  const uint32_t kmax = kr[0], kmin = kr[1];
-  const unsigned long long ncand = kr[2];
+  // candidate key range and count: reduce the score tiles' slots
+  uint32_t kmax = 0u, kmin = 0xffffffffu;
+  unsigned long long ncand = 0ull;
+  {
+    const uint4* kr = reinterpret_cast<const uint4*>(A.keyrange) + q * A.kr_slots;
+    for (int64_t i = tid; i < A.kr_used; i += kSelThreads) {
+      const uint4 v = kr[i];
+      kmax = max(kmax, v.x);
+      kmin = min(kmin, v.y);
+      ncand += v.z;
+    }
+    for (int o = 1; o < 64; o <<= 1) {
+      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+      ncand += __shfl_xor(ncand, o);
+    }
+    __shared__ uint32_t rmax[kSelThreads / 64], rmin[kSelThreads / 64];
+    __shared__ unsigned long long rcnt[kSelThreads / 64];
+    if ((tid & 63) == 0) {
+      rmax[tid >> 6] = kmax;
+      rmin[tid >> 6] = kmin;
+      rcnt[tid >> 6] = ncand;
+    }
+    __syncthreads();
+    kmax = 0u;
+    kmin = 0xffffffffu;
+    ncand = 0ull;
+    for (int w = 0; w < kSelThreads / 64; ++w) {
+      kmax = max(kmax, rmax[w]);
+      kmin = min(kmin, rmin[w]);
+      ncand += rcnt[w];
+    }
+  }
   if (ncand == 0) {
     for (int64_t w = tid; w < nwords; w += kSelThreads) srow[w] = 0u;
     if (tid == 0) {
@@ -664,6 +733,12 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs A) {
 
 }  // namespace
 
+int64_t route_kr_slots(int dtype, bool leaf_weights, int64_t node_cap, int C) {
+  if (leaf_weights) return (node_cap * C + 255) / 256;  // k_score_leafw: 256-key tiles
+  if (dtype == 1) return (node_cap + 63) / 64;          // k_score_bf16: 64-node tiles
+  return 1;                                             // k_score_generic: atomics
+}
+
 hipError_t launch_route_init(uint32_t* keyrange, int64_t n, Prof& prof) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_route_init, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, prof.s, keyrange, n);
@@ -678,14 +753,21 @@ hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dty
     prof.begin(ZHA_K_SCORE, level);
     if (sa.leaf_weights) {
       dim3 grid((unsigned)((sa.n_nodes * sa.C + 255) / 256), (unsigned)n_caches, (unsigned)((sa.QC + 15) / 16));
-#define ZHA_LW(DD, CC)                                                              \
-  do {                                                                              \
-    if (sa.R == 16)                                                                 \
-      hipLaunchKernelGGL((k_score_leafw<DD, CC, 16>), grid, dim3(256), 0, s, sa);   \
-    else if (sa.R == 1)                                                             \
-      hipLaunchKernelGGL((k_score_leafw<DD, CC, 1>), grid, dim3(256), 0, s, sa);    \
-    else                                                                            \
-      hipLaunchKernelGGL((k_score_leafw<DD, CC, 0>), grid, dim3(256), 0, s, sa);    \
+#define ZHA_LW_Q(DD, CC, QQ)                                                            \
+  do {                                                                                  \
+    if (sa.R == 16)                                                                     \
+      hipLaunchKernelGGL((k_score_leafw<DD, CC, 16, QQ>), grid, dim3(256), 0, s, sa);   \
+    else if (sa.R == 1)                                                                 \
+      hipLaunchKernelGGL((k_score_leafw<DD, CC, 1, QQ>), grid, dim3(256), 0, s, sa);    \
+    else                                                                                \
+      hipLaunchKernelGGL((k_score_leafw<DD, CC, 0, QQ>), grid, dim3(256), 0, s, sa);    \
+  } while (0)
+#define ZHA_LW(DD, CC)               \
+  do {                               \
+    if (sa.QC <= 4)                  \
+      ZHA_LW_Q(DD, CC, true);        \
+    else                             \
+      ZHA_LW_Q(DD, CC, false);       \
   } while (0)
       if (sa.D == 128) {
         if (sa.C == 4) ZHA_LW(128, 4);
@@ -697,6 +779,7 @@ hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dty
         else ZHA_LW(64, 16);
       }
 #undef ZHA_LW
+#undef ZHA_LW_Q
     } else if (dtype == 1) {
       dim3 grid((unsigned)((sa.n_nodes + 63) / 64), (unsigned)n_caches, (unsigned)((sa.QC + 15) / 16));
       if (sa.D == 128)
@@ -714,8 +797,17 @@ hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dty
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  SelectArgs sel = se;
+  if (sa.n_nodes <= 0)
+    sel.kr_used = 0;
+  else if (sa.leaf_weights)
+    sel.kr_used = (sa.n_nodes * sa.C + 255) / 256;
+  else if (dtype == 1)
+    sel.kr_used = (sa.n_nodes + 63) / 64;
+  else
+    sel.kr_used = 1;
   prof.begin(ZHA_K_SELECT, level);
-  hipLaunchKernelGGL(k_select, dim3((unsigned)n_queries), dim3(kSelThreads), 0, s, se);
+  hipLaunchKernelGGL(k_select, dim3((unsigned)n_queries), dim3(kSelThreads), 0, s, sel);
   prof.end();
   return hipGetLastError();
 }
