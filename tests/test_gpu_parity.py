@@ -128,6 +128,8 @@ CACHED_CASES = [
     ("qg8-d64-C8", dict(batch=1, n_kv_heads=2, q_per_kv=3, head_dim=64, n_ref=4, chunk=8, levels=3, capacity=6000), 2, 5995, 0.7),
     ("qg16-d128-C16", dict(batch=1, n_kv_heads=1, q_per_kv=4, head_dim=128, n_ref=2, chunk=16, levels=2, capacity=5000), 5, 4992, 0.95),
     ("qg4-d64-C4-p1", dict(batch=1, n_kv_heads=1, q_per_kv=2, head_dim=64, n_ref=3, chunk=4, levels=3, capacity=2100), 1, 2051, 1.0),
+    ("qg4-d128-C8", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=8, levels=3, capacity=7000), 1, 6999, 0.9),
+    ("qg4-d64-C16-R1", dict(batch=1, n_kv_heads=1, q_per_kv=3, head_dim=64, n_ref=1, chunk=16, levels=2, capacity=5000), 1, 4990, 0.8),
 ]
 
 
@@ -150,6 +152,18 @@ def test_attend_cached_logits_matches_oracle(name, kw, T, N, p, flags):
     out_c, lse_c = out.cpu().numpy(), lse.cpu().numpy()
     tol = PAR.OUT_TOL[cfg.dtype]
     n_chunks = N // cfg.chunk
+    if flags == zha.ZHA_SINK | zha.ZHA_LAST_CHUNK:
+        # the routing itself (level-1 scores from raw keys and weights), teacher-forced
+        QC = cfg.q_per_kv * T
+        for cache in sorted({0, cfg.n_caches - 1}):
+            b, h = divmod(cache, cfg.n_kv_heads)
+            Kn, rn = np64(K[b, h, :N]), np64(ref[h])
+            to = O.build_tree(Kn, rn, cfg.chunk, cfg.levels, cfg.dtype, keep_g=False, leaf_dtype="f64")
+            for ql in range(QC):
+                bits, scores = gpu_levels(cfg, buf, N, cache * QC + ql)
+                q = np64(Q[b, h, ql // T, ql % T])
+                PAR.check_route_teacher_forced(q, to, rn, cfg.chunk, p, PAR.gpu_kept_from_bits(bits), cfg.dtype,
+                                               scores, leaf_dtype="f64")
     for qi, (b, h, gq, t) in enumerate(query_list(cfg, T)):
         bits, _ = gpu_levels(cfg, buf, N, qi)
         chunks = np.nonzero(bits[1][:n_chunks])[0]

@@ -205,85 +205,60 @@ __global__ __launch_bounds__(kAttThreads) void k_attend(AttendArgs A) {
   }
 }
 
-// bf16 path: compacted quads, QK^T on MFMA, PV in fp32 FMA.
-//
-// Phase 1: every thread tests 8 consecutive 4-key quads of the tile against
-// the routed chunk bits of the group's queries (plus sink / current chunk)
-// and the non-empty quads are compacted, in key order, into an LDS list with
-// a 4-bit key mask per query.  Phase 2: each wave takes groups of four list
-// entries (16 keys); K rows go straight into the A operand of
-// v_mfma_f32_16x16x32_bf16 (queries are the B operand), so one MFMA chain
-// yields the 16 x 16 logits.  The softmax weights leave the MFMA layout
-// through a 1 KiB LDS slot per wave and meet V, which is loaded with fully
-// coalesced 16-byte rows and accumulated in fp32.  The next group's K and V
-// are in flight while the current one is computed.
-constexpr int kTileQuadsMax = 2048;  // 8192 keys
+constexpr int kTileQuadsMax = 2048;                // 8192 keys
+constexpr int kQPT = kTileQuadsMax / kAttThreads;  // quads per thread in phase 1 (32 keys)
 
-template <int D, int QG>
-__global__ __launch_bounds__(kAttThreads) void k_attend_mfma(AttendArgs A) {
-  constexpr int PIECES = D / 8;    // 16-byte pieces per row
-  constexpr int NS = D / 32;       // MFMA k-steps
-  constexpr int NVL = PIECES / 4;  // V loads per lane per 16-key group
-  constexpr int QPT = kTileQuadsMax / kAttThreads;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int cache = blockIdx.y;
-  const int qg0 = blockIdx.z * QG;
-  const int nq = min(QG, A.QC - qg0);
-  const int64_t tile = blockIdx.x;
-  const int b = cache / A.H, h = cache % A.H;
-  const int64_t k_lo = tile * A.tile_keys;
-  const int64_t k_hi = min(A.n_tokens, k_lo + A.tile_keys);
-  const int nquads = (int)((k_hi - k_lo + 3) / 4);  // quads of this tile
+// Phase 1 of the bf16 kernels.  Thread `tid` covers the 8 quads (32 keys)
+// starting at k_lo + 32 tid.  Bit 4u + kk of qmask[i] marks key kk of quad i
+// as attended by query u of the group (a routed chunk or a forced key); bit i
+// of *routed marks quads that hold a routed chunk of some query.  The 32 keys
+// start on a multiple of 32 and C is a power of two, so the bits of their
+// chunks lie in one selection word per query: one load per query.
+template <int QG>
+__device__ __forceinline__ void quad_masks(const AttendArgs& A, int cache, int qg0, int nq, int64_t k_lo,
+                                           int64_t k_hi, int tid, unsigned long long* qmask,
+                                           uint32_t* routed) {
   const bool all = A.flags & 4u, sink = A.flags & 1u, last = A.flags & 2u;
   const int64_t last_start = (int64_t)A.C * ((A.n_tokens - 1) / A.C);
-
-  __shared__ uint16_t e_quad[kTileQuadsMax];
-  __shared__ unsigned long long e_mask[kTileQuadsMax];
-  __shared__ int scan[kAttThreads];
-  __shared__ float p_lds[4][16][16];  // [wave][key in group][query]
-  __shared__ float sc_lds[4][16];
-  __shared__ float red[4][QG][D + 2];
-
-  // ---- phase 1: per-quad selection masks, compacted in key order; with a
-  // logits buffer, quads holding a routed chunk come first (their logits are
-  // cached), then the quads holding forced keys only
-  unsigned long long qmask[QPT];
-  uint32_t qrouted = 0u;
-  int cnt = 0;  // routed count in the low 16 bits, forced-only count above
-  {
-    const uint32_t* srow[QG];
+  const int64_t key0 = k_lo + 32 * (int64_t)tid;
+  const int lc = __builtin_ctz((unsigned)A.C);
+  const int64_t c0 = key0 >> lc;
+  const bool rd = !all && A.sel1 != nullptr && key0 < k_hi && c0 < A.n_chunks;
+  const uint32_t* wp = A.sel1 + ((int64_t)cache * A.QC + qg0) * A.sel_words + (c0 >> 5);
+  uint32_t wq[QG];
 #pragma unroll
-    for (int u = 0; u < QG; ++u)
-      srow[u] = A.sel1 ? A.sel1 + ((int64_t)cache * A.QC + qg0 + (u < nq ? u : 0)) * A.sel_words : nullptr;
+  for (int u = 0; u < QG; ++u) wq[u] = (rd && u < nq) ? wp[(int64_t)u * A.sel_words] : 0u;
+  const int sh = (int)(c0 & 31);
+  const uint32_t qall = (1u << nq) - 1u;  // nq <= 16
+  uint32_t rt = 0u;
 #pragma unroll
-    for (int i = 0; i < QPT; ++i) {
-      const int qd = tid * QPT + i;
-      unsigned long long msk = 0ull;
-      bool routed = false;
-      if (qd < nquads) {
+  for (int i = 0; i < kQPT; ++i) {
+    unsigned long long msk = 0ull;
+    uint32_t qany = 0u;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int64_t key = k_lo + 4 * qd + kk;
-          if (key >= k_hi) break;
-          const bool forced = all || (sink && key == 0) || (last && key >= last_start);
-          const int64_t chunk = key / A.C;
-          const bool has_chunk = !all && chunk < A.n_chunks;
+    for (int kk = 0; kk < 4; ++kk) {
+      const int64_t key = key0 + 4 * i + kk;
+      const bool in = key < k_hi;
+      const bool forced = in && (all || (sink && key == 0) || (last && key >= last_start));
+      const int j = (4 * i + kk) >> lc;  // chunk of this key, counted from c0
+      uint32_t qb = 0u;                  // bit u: query u routes this key's chunk
 #pragma unroll
-          for (int u = 0; u < QG; ++u) {
-            if (u >= nq) break;
-            bool bit = false;
-            if (has_chunk) bit = (srow[u][chunk >> 5] >> (chunk & 31)) & 1u;
-            routed = routed || bit;
-            if (forced || bit) msk |= 1ull << (u * 4 + kk);
-          }
-        }
-      }
-      qmask[i] = msk;
-      const bool r = routed && A.logits != nullptr;
-      if (r) qrouted |= 1u << i;
-      if (msk) cnt += r ? 1 : (1 << 16);
+      for (int u = 0; u < QG; ++u) qb |= ((wq[u] >> (sh + j)) & 1u) << u;
+      if (!in || c0 + j >= A.n_chunks) qb = 0u;
+      qany |= qb;
+      const uint32_t qs = forced ? qall : qb;
+#pragma unroll
+      for (int u = 0; u < QG; ++u) msk |= (unsigned long long)((qs >> u) & 1u) << (4 * u + kk);
     }
+    qmask[i] = msk;
+    if (qany) rt |= 1u << i;
   }
+  *routed = rt;
+}
+
+// Exclusive scan of `cnt` over the workgroup (256 threads); returns the total.
+__device__ __forceinline__ int block_scan_excl(int cnt, int* scan, int* excl) {
+  const int tid = threadIdx.x;
   scan[tid] = cnt;
   __syncthreads();
   for (int off = 1; off < kAttThreads; off <<= 1) {
@@ -292,17 +267,119 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_mfma(AttendArgs A) {
     scan[tid] += add;
     __syncthreads();
   }
-  const int n_r = scan[kAttThreads - 1] & 0xffff;
-  const int n_ent = n_r + (scan[kAttThreads - 1] >> 16);
-  {
-    int pos_r = (scan[tid] - cnt) & 0xffff;
-    int pos_f = n_r + ((scan[tid] - cnt) >> 16);
+  *excl = scan[tid] - cnt;
+  return scan[kAttThreads - 1];
+}
+
+// Combines the 4 waves' (max, sum, weighted V sum) per query and writes the
+// workgroup's partial result for the tile.
+template <int D, int QG>
+__device__ __forceinline__ void write_partial(const AttendArgs& A, float (*red)[QG][D + 2], int cache, int qg0,
+                                              int nq, int64_t tile) {
+  for (int idx = threadIdx.x; idx < QG * D; idx += kAttThreads) {
+    const int u = idx / D, d = idx % D;
+    if (u >= nq) continue;
+    float mm = kNegInf;
+    for (int w = 0; w < 4; ++w) mm = fmaxf(mm, red[w][u][D]);
+    float ll = 0.f, o = 0.f;
+    if (mm != kNegInf) {
+      for (int w = 0; w < 4; ++w) {
+        const float mw = red[w][u][D];
+        if (mw == kNegInf) continue;
+        const float f = __expf(mw - mm);
+        ll += red[w][u][D + 1] * f;
+        o += red[w][u][d] * f;
+      }
+    }
+    float* part = A.partial + (((int64_t)cache * A.QC + qg0 + u) * A.n_tiles + tile) * (D + 2);
+    if (d == 0) {
+      part[0] = mm;
+      part[1] = ll;
+    }
+    part[2 + d] = o;
+  }
+}
+
+// One batch of T steps of the streaming kernel for this lane's key: rescale
+// the running state once to the batch max, then accumulate exp(z - max) * v.
+template <int T, int QG>
+__device__ __forceinline__ void absorb(const uint4 (&vv4)[T], const float (&z)[T][QG], float (&m)[QG],
+                                       float (&lsum)[QG], float (&acc)[QG][8]) {
 #pragma unroll
-    for (int i = 0; i < QPT; ++i) {
+  for (int u = 0; u < QG; ++u) {
+    float bm = z[0][u];
+#pragma unroll
+    for (int t = 1; t < T; ++t) bm = fmaxf(bm, z[t][u]);
+    const float mn = fmaxf(m[u], bm);
+    if (mn > m[u]) {
+      const float sc = __expf(m[u] - mn);
+      lsum[u] *= sc;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) acc[u][x] *= sc;
+      m[u] = mn;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    float vv[8];
+    unpack(vv4[t], vv, bf16_t());
+#pragma unroll
+    for (int u = 0; u < QG; ++u) {
+      const float pw = z[t][u] == kNegInf ? 0.f : __expf(z[t][u] - m[u]);
+      lsum[u] += pw;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) acc[u][x] += pw * vv[x];
+    }
+  }
+}
+
+// bf16 path without cached logits: compacted quads, QK^T on MFMA, PV in fp32
+// FMA.  The non-empty quads are compacted, in key order, into an LDS list
+// with a 4-bit key mask per query.  Each wave takes groups of four list
+// entries (16 keys); K rows go straight into the A operand of
+// v_mfma_f32_16x16x32_bf16 (queries are the B operand), so one MFMA chain
+// yields the 16 x 16 logits.  The softmax weights leave the MFMA layout
+// through a 1 KiB LDS slot per wave and meet V, which is loaded with fully
+// coalesced 16-byte rows and accumulated in fp32.  The next group's K and V
+// are in flight while the current one is computed.
+template <int D, int QG>
+__global__ __launch_bounds__(kAttThreads) void k_attend_mfma(AttendArgs A) {
+  constexpr int PIECES = D / 8;    // 16-byte pieces per row
+  constexpr int NS = D / 32;       // MFMA k-steps
+  constexpr int NVL = PIECES / 4;  // V loads per lane per 16-key group
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cache = blockIdx.y;
+  const int qg0 = blockIdx.z * QG;
+  const int nq = min(QG, A.QC - qg0);
+  const int64_t tile = blockIdx.x;
+  const int b = cache / A.H, h = cache % A.H;
+  const int64_t k_lo = tile * A.tile_keys;
+  const int64_t k_hi = min(A.n_tokens, k_lo + A.tile_keys);
+
+  __shared__ uint16_t e_quad[kTileQuadsMax];
+  __shared__ unsigned long long e_mask[kTileQuadsMax];
+  __shared__ int scan[kAttThreads];
+  __shared__ float p_lds[4][16][16];  // [wave][key in group][query]
+  __shared__ float sc_lds[4][16];
+  __shared__ float red[4][QG][D + 2];
+
+  // ---- phase 1
+  int n_ent;
+  {
+    unsigned long long qmask[kQPT];
+    uint32_t routed;
+    quad_masks<QG>(A, cache, qg0, nq, k_lo, k_hi, tid, qmask, &routed);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < kQPT; ++i) cnt += qmask[i] != 0ull;
+    int pos;
+    n_ent = block_scan_excl(cnt, scan, &pos);
+#pragma unroll
+    for (int i = 0; i < kQPT; ++i) {
       if (qmask[i]) {
-        const int pos = ((qrouted >> i) & 1u) ? pos_r++ : pos_f++;
-        e_quad[pos] = (uint16_t)(tid * QPT + i);
+        e_quad[pos] = (uint16_t)(tid * kQPT + i);
         e_mask[pos] = qmask[i];
+        ++pos;
       }
     }
   }
@@ -326,38 +403,29 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_mfma(AttendArgs A) {
   }
   const bf16_t* Kc = reinterpret_cast<const bf16_t*>(A.K) + (int64_t)b * A.sb + (int64_t)h * A.sh;
   const bf16_t* Vc = reinterpret_cast<const bf16_t*>(A.V) + (int64_t)b * A.sb + (int64_t)h * A.sh;
+  // this tile's rows; offsets past the last key read zeros
+  const uint32_t tile_bytes = (uint32_t)((k_hi - k_lo - 1) * A.st * 2 + D * 2);
+  const rsrc_t kr = make_rsrc(Kc + k_lo * A.st, tile_bytes);
+  const rsrc_t vr = make_rsrc(Vc + k_lo * A.st, tile_bytes);
+  const uint32_t row_bytes = (uint32_t)(A.st * 2);
 
   const int n_groups = (n_ent + 3) / 4;
-  // groups whose valid entries all hold a routed chunk read cached logits
-  auto cached = [&](int g) { return min(4 * g + 3, n_ent - 1) < n_r; };
-  const float* lbase =
-      A.logits ? A.logits + (((int64_t)cache * ((A.QC + 15) / 16) + (qg0 + r16) / 16) * A.nquads) * A.QW * 4 : nullptr;
-  // Loads of one 16-key group into the register arrays KA (K rows, A
-  // operand, when the logits are computed here), VA (V rows, FMA layout)
-  // and LG (the 4 cached logits of entry 4g + kg for query r16).  Every
-  // slot is assigned on every path so the arrays stay in registers.
-#define ZHA_LOAD_GROUP(g, KA, VA, LG)                                                        \
-  do {                                                                                       \
-    const bool cg_ = cached(g);                                                              \
-    {                                                                                        \
-      const int e_ = 4 * (g) + kg;                                                           \
-      const bool ok_ = cg_ && e_ < n_ent && r16 < nq;                                        \
-      const int64_t quad_ = (k_lo >> 2) + (ok_ ? (int64_t)e_quad[e_] : 0);                   \
-      LG = ok_ ? ld16(lbase + (quad_ * A.QW + (qg0 + r16) % 16) * 4) : make_uint4(0, 0, 0, 0); \
-    }                                                                                        \
-    {                                                                                        \
-      const int e_ = 4 * (g) + (r16 >> 2);                                                   \
-      const int64_t key_ = (!cg_ && e_ < n_ent) ? k_lo + 4 * (int64_t)e_quad[e_] + (r16 & 3) : k_hi; \
-      _Pragma("unroll") for (int s_ = 0; s_ < NS; ++s_) KA[s_] =                             \
-          key_ < k_hi ? ld16(Kc + key_ * A.st + (4 * s_ + kg) * 8) : make_uint4(0, 0, 0, 0); \
-    }                                                                                        \
-    _Pragma("unroll") for (int u_ = 0; u_ < NVL; ++u_) {                                     \
-      const int pi_ = lane + 64 * u_;                                                        \
-      const int kq_ = pi_ / PIECES, pc_ = pi_ % PIECES;                                      \
-      const int e_ = 4 * (g) + (kq_ >> 2);                                                   \
-      const int64_t key_ = e_ < n_ent ? k_lo + 4 * (int64_t)e_quad[e_] + (kq_ & 3) : k_hi;   \
-      VA[u_] = key_ < k_hi ? ld16(Vc + key_ * A.st + pc_ * 8) : make_uint4(0, 0, 0, 0);      \
-    }                                                                                        \
+  // Loads of one 16-key group into KA (K rows, A operand) and VA (V rows,
+  // FMA layout).
+#define ZHA_LOAD_GROUP(g, KA, VA)                                                                 \
+  do {                                                                                            \
+    {                                                                                             \
+      const int e_ = 4 * (g) + (r16 >> 2);                                                        \
+      const uint32_t ro_ = e_ < n_ent ? (4u * e_quad[e_] + (r16 & 3)) * row_bytes : kOffNone;     \
+      _Pragma("unroll") for (int s_ = 0; s_ < NS; ++s_) KA[s_] = bld16(kr, ro_ + (4 * s_ + kg) * 16); \
+    }                                                                                             \
+    _Pragma("unroll") for (int u_ = 0; u_ < NVL; ++u_) {                                          \
+      const int pi_ = lane + 64 * u_;                                                             \
+      const int kq_ = pi_ / PIECES, pc_ = pi_ % PIECES;                                           \
+      const int e_ = 4 * (g) + (kq_ >> 2);                                                        \
+      const uint32_t ro_ = e_ < n_ent ? (4u * e_quad[e_] + (kq_ & 3)) * row_bytes : kOffNone;     \
+      VA[u_] = bld16(vr, ro_ + pc_ * 16);                                                         \
+    }                                                                                             \
   } while (0)
 
   float m = kNegInf, l = 0.f;  // softmax state of query r16 (MFMA layout)
@@ -369,33 +437,22 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_mfma(AttendArgs A) {
 
   // each wave walks its own groups (g = wave, wave + 4, ...); the LDS slots
   // it exchanges through are its own, so only wave-scope barriers are needed
-  uint4 kf[NS], vf[NVL], lf, kn[NS], vn[NVL], ln;
-  if (wave < n_groups) ZHA_LOAD_GROUP(wave, kf, vf, lf);
+  uint4 kf[NS], vf[NVL], kn[NS], vn[NVL];
+  if (wave < n_groups) ZHA_LOAD_GROUP(wave, kf, vf);
   for (int g = wave; g < n_groups; g += 4) {
-    if (g + 4 < n_groups) ZHA_LOAD_GROUP(g + 4, kn, vn, ln);
+    if (g + 4 < n_groups) ZHA_LOAD_GROUP(g + 4, kn, vn);
     {
       // lane: keys 4*kg + i of the group (entry 4g + kg), query r16
-      float zl[4];
-      if (cached(g)) {
-        const uint4 c = lf;
-        zl[0] = __uint_as_float(c.x);
-        zl[1] = __uint_as_float(c.y);
-        zl[2] = __uint_as_float(c.z);
-        zl[3] = __uint_as_float(c.w);
-      } else {
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < NS; ++s) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[s]), bq[s], z, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) zl[i] = z[i] * A.inv_sqrt_d;
-      }
+      for (int s = 0; s < NS; ++s) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[s]), bq[s], z, 0, 0, 0);
       const int e = 4 * g + kg;
       const unsigned long long msk = (e < n_ent && r16 < QG) ? e_mask[e] >> (r16 * 4) : 0ull;
       float zz[4];
       float mb = kNegInf;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        zz[i] = ((msk >> i) & 1ull) ? zl[i] : kNegInf;
+        zz[i] = ((msk >> i) & 1ull) ? z[i] * A.inv_sqrt_d : kNegInf;
         mb = fmaxf(mb, zz[i]);
       }
       mb = fmaxf(mb, __shfl_xor(mb, 16));
@@ -448,7 +505,6 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_mfma(AttendArgs A) {
     for (int s = 0; s < NS; ++s) kf[s] = kn[s];
 #pragma unroll
     for (int v = 0; v < NVL; ++v) vf[v] = vn[v];
-    lf = ln;
   }
 #undef ZHA_LOAD_GROUP
 
@@ -470,41 +526,20 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_mfma(AttendArgs A) {
     red[wave][r16][D + 1] = l;
   }
   __syncthreads();
-  for (int idx = tid; idx < QG * D; idx += kAttThreads) {
-    const int u = idx / D, d = idx % D;
-    if (u >= nq) continue;
-    float mm = kNegInf;
-    for (int w = 0; w < 4; ++w) mm = fmaxf(mm, red[w][u][D]);
-    float ll = 0.f, o = 0.f;
-    if (mm != kNegInf) {
-      for (int w = 0; w < 4; ++w) {
-        const float mw = red[w][u][D];
-        if (mw == kNegInf) continue;
-        const float f = __expf(mw - mm);
-        ll += red[w][u][D + 1] * f;
-        o += red[w][u][d] * f;
-      }
-    }
-    float* part = A.partial + (((int64_t)cache * A.QC + qg0 + u) * A.n_tiles + tile) * (D + 2);
-    if (d == 0) {
-      part[0] = mm;
-      part[1] = ll;
-    }
-    part[2 + d] = o;
-  }
+  write_partial<D, QG>(A, red, cache, qg0, nq, tile);
 }
 
 // bf16 path with the route's cached level-1 logits: V streaming only.
 //
-// Phase 1 compacts the selected quads as above (routed quads first, then the
-// at most 5 quads that hold forced keys only: the sink's quad and the
-// current chunk, which lies inside one tile).  The logits of those few are
-// computed once into LDS.  Phase 2: lanes are (quad of the step, key of the
-// quad, 16-byte piece of the row); each wave takes every 4th step, with up
-// to 8 steps of V (one coalesced 1 KiB load per quad for d = 128) and their
-// cached logits in flight at once (fewer for larger query groups, whose
-// accumulators take the registers), and keeps a per-lane online softmax
-// (one rescale per batch) in fp32.  No LDS traffic or barrier in the loop.
+// Phase 1 compacts the selected quads as above, routed quads first, then the
+// at most 5 quads that hold forced keys only (the sink's quad and the current
+// chunk, which lies inside one tile); the logits of those few are computed
+// once into LDS.  Phase 2: lanes are (quad of the step, key of the quad,
+// 16-byte piece of the row); each wave takes every 4th step, with up to 8
+// steps of V (one coalesced 1 KiB load per quad for d = 128) and their cached
+// logits in flight at once (fewer for larger query groups, whose accumulators
+// take the registers), and keeps a per-lane online softmax (one rescale per
+// batch) in fp32.  No LDS traffic or barrier in the loop.
 constexpr int kMaxForcedQuads = 8;
 
 template <int D, int QG>
@@ -512,8 +547,8 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_cached(AttendArgs A) {
   constexpr int PIECES = D / 8;   // 16-byte pieces per row
   constexpr int LPQ = 4 * PIECES; // lanes per quad
   constexpr int EPS = 64 / LPQ;   // quads per wave step
-  constexpr int QPT = kTileQuadsMax / kAttThreads;
-  constexpr int kU2 = QG <= 4 ? 8 : QG <= 8 ? 4 : 2;  // steps in flight
+  constexpr int U = QG <= 4 ? 8 : QG <= 8 ? 4 : 2;  // steps in flight
+  constexpr int STRIDE = 4 * EPS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cache = blockIdx.y;
   const int qg0 = blockIdx.z * QG;
@@ -522,9 +557,6 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_cached(AttendArgs A) {
   const int b = cache / A.H, h = cache % A.H;
   const int64_t k_lo = tile * A.tile_keys;
   const int64_t k_hi = min(A.n_tokens, k_lo + A.tile_keys);
-  const int nquads = (int)((k_hi - k_lo + 3) / 4);
-  const bool sink = A.flags & 1u, last = A.flags & 2u;
-  const int64_t last_start = (int64_t)A.C * ((A.n_tokens - 1) / A.C);
 
   __shared__ uint16_t e_quad[kTileQuadsMax];
   __shared__ unsigned long long e_mask[kTileQuadsMax];
@@ -533,62 +565,26 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_cached(AttendArgs A) {
   __shared__ float red[4][QG][D + 2];
 
   // ---- phase 1
-  unsigned long long qmask[QPT];
-  uint32_t qrouted = 0u;
-  int cnt = 0;  // routed count in the low 16 bits, forced-only count above
+  int n_r, n_f;
   {
-    const uint32_t* srow[QG];
+    unsigned long long qmask[kQPT];
+    uint32_t routed;
+    quad_masks<QG>(A, cache, qg0, nq, k_lo, k_hi, tid, qmask, &routed);
+    int cnt = 0;  // routed count in the low 16 bits, forced-only count above
 #pragma unroll
-    for (int u = 0; u < QG; ++u)
-      srow[u] = A.sel1 + ((int64_t)cache * A.QC + qg0 + (u < nq ? u : 0)) * A.sel_words;
+    for (int i = 0; i < kQPT; ++i)
+      if (qmask[i]) cnt += ((routed >> i) & 1u) ? 1 : (1 << 16);
+    int excl;
+    const int tot = block_scan_excl(cnt, scan, &excl);
+    n_r = tot & 0xffff;
+    n_f = min(tot >> 16, kMaxForcedQuads);
+    int pos_r = excl & 0xffff, pos_f = n_r + (excl >> 16);
 #pragma unroll
-    for (int i = 0; i < QPT; ++i) {
-      const int qd = tid * QPT + i;
-      unsigned long long msk = 0ull;
-      bool routed = false;
-      if (qd < nquads) {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int64_t key = k_lo + 4 * qd + kk;
-          if (key >= k_hi) break;
-          const bool forced = (sink && key == 0) || (last && key >= last_start);
-          const int64_t chunk = key / A.C;
-          const bool has_chunk = chunk < A.n_chunks;
-#pragma unroll
-          for (int u = 0; u < QG; ++u) {
-            if (u >= nq) break;
-            bool bit = false;
-            if (has_chunk) bit = (srow[u][chunk >> 5] >> (chunk & 31)) & 1u;
-            routed = routed || bit;
-            if (forced || bit) msk |= 1ull << (u * 4 + kk);
-          }
-        }
-      }
-      qmask[i] = msk;
-      if (routed) qrouted |= 1u << i;
-      if (msk) cnt += routed ? 1 : (1 << 16);
-    }
-  }
-  scan[tid] = cnt;
-  __syncthreads();
-  for (int off = 1; off < kAttThreads; off <<= 1) {
-    const int add = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += add;
-    __syncthreads();
-  }
-  const int n_r = scan[kAttThreads - 1] & 0xffff;
-  const int n_f = min(scan[kAttThreads - 1] >> 16, kMaxForcedQuads);
-  const int n_ent = n_r + n_f;
-  {
-    int pos_r = (scan[tid] - cnt) & 0xffff;
-    int pos_f = n_r + ((scan[tid] - cnt) >> 16);
-#pragma unroll
-    for (int i = 0; i < QPT; ++i) {
+    for (int i = 0; i < kQPT; ++i) {
       if (qmask[i]) {
-        const int pos = ((qrouted >> i) & 1u) ? pos_r++ : pos_f++;
-        if (pos < n_ent) {
-          e_quad[pos] = (uint16_t)(tid * QPT + i);
+        const int pos = ((routed >> i) & 1u) ? pos_r++ : pos_f++;
+        if (pos < n_r + n_f) {
+          e_quad[pos] = (uint16_t)(tid * kQPT + i);
           e_mask[pos] = qmask[i];
         }
       }
@@ -628,8 +624,13 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_cached(AttendArgs A) {
 
   // ---- phase 2
   const int qs = lane / LPQ, kk = (lane % LPQ) / PIECES, pc = lane % PIECES;
-  const float* lbase = A.logits + ((int64_t)cache * ((A.QC + 15) / 16) + qg0 / 16) * A.nquads * A.QW * 4;
-  const int qoff = qg0 % 16;
+  const uint32_t row_bytes = (uint32_t)(A.st * 2);
+  const rsrc_t vr = make_rsrc(Vc + k_lo * A.st, (uint32_t)((k_hi - k_lo - 1) * A.st * 2 + D * 2));
+  // this tile's cached logits: [quad][QW][4] fp32
+  const int nqt = (int)((k_hi - k_lo + 3) / 4);
+  const float* ltile = A.logits + (((int64_t)cache * ((A.QC + 15) / 16) + qg0 / 16) * A.nquads + (k_lo >> 2)) * A.QW * 4;
+  const rsrc_t lr = make_rsrc(ltile, (uint32_t)(nqt * A.QW * 16));
+  const uint32_t lq = (uint32_t)(qg0 % 16) * 16 + kk * 4;  // byte offset of (query 0 of the group, key kk)
   float m[QG], lsum[QG], acc[QG][8];
 #pragma unroll
   for (int u = 0; u < QG; ++u) {
@@ -638,53 +639,36 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_cached(AttendArgs A) {
 #pragma unroll
     for (int x = 0; x < 8; ++x) acc[u][x] = 0.f;
   }
-  constexpr int STRIDE = 4 * EPS;
-  for (int e0 = wave * EPS + qs; e0 < n_ent; e0 += STRIDE * kU2) {
-    uint4 vr[kU2];
-    float z[kU2][QG];
+  // routed quads: V and cached logits by buffer loads (unselected read nothing)
+  for (int e0 = wave * EPS + qs; e0 < n_r; e0 += STRIDE * U) {
+    uint4 vv4[U];
+    float z[U][QG];
 #pragma unroll
-    for (int t = 0; t < kU2; ++t) {
+    for (int t = 0; t < U; ++t) {
       const int e = e0 + t * STRIDE;
-      const bool ok = e < n_ent;
-      const int quad = ok ? e_quad[e] : 0;
+      const bool ok = e < n_r;
+      const uint32_t quad = ok ? e_quad[e] : 0u;
       const unsigned long long msk = ok ? e_mask[e] >> kk : 0ull;
-      const int64_t key = k_lo + 4 * (int64_t)quad + kk;
-      vr[t] = (ok && key < k_hi) ? ld16(Vc + key * A.st + pc * 8) : make_uint4(0, 0, 0, 0);
-      if (e < n_r) {
-        const float* lp = lbase + (((k_lo >> 2) + quad) * A.QW + qoff) * 4 + kk;
-#pragma unroll
-        for (int u = 0; u < QG; ++u) z[t][u] = ((msk >> (4 * u)) & 1ull) ? lp[4 * u] : kNegInf;
-      } else {
-#pragma unroll
-        for (int u = 0; u < QG; ++u) z[t][u] = ((msk >> (4 * u)) & 1ull) ? f_log[ok ? e - n_r : 0][u][kk] : kNegInf;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < QG; ++u) {
-      float bm = z[0][u];
-#pragma unroll
-      for (int t = 1; t < kU2; ++t) bm = fmaxf(bm, z[t][u]);
-      const float mn = fmaxf(m[u], bm);
-      if (mn > m[u]) {
-        const float sc = __expf(m[u] - mn);
-        lsum[u] *= sc;
-#pragma unroll
-        for (int x = 0; x < 8; ++x) acc[u][x] *= sc;
-        m[u] = mn;
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < kU2; ++t) {
-      float vv[8];
-      unpack(vr[t], vv, bf16_t());
+      vv4[t] = bld16(vr, ok ? (4u * quad + kk) * row_bytes + pc * 16 : kOffNone);
 #pragma unroll
       for (int u = 0; u < QG; ++u) {
-        const float pw = z[t][u] == kNegInf ? 0.f : __expf(z[t][u] - m[u]);
-        lsum[u] += pw;
-#pragma unroll
-        for (int x = 0; x < 8; ++x) acc[u][x] += pw * vv[x];
+        const bool sel = (msk >> (4 * u)) & 1ull;
+        const float lz = bld4f(lr, sel ? quad * (uint32_t)A.QW * 16 + lq + u * 16 : kOffNone);
+        z[t][u] = sel ? lz : kNegInf;
       }
     }
+    absorb<U, QG>(vv4, z, m, lsum, acc);
+  }
+  // forced-only quads: logits from LDS
+  for (int f0 = wave * EPS + qs; f0 < n_f; f0 += STRIDE) {
+    uint4 vv4[1];
+    float z[1][QG];
+    const uint32_t quad = e_quad[n_r + f0];
+    const unsigned long long msk = e_mask[n_r + f0] >> kk;
+    vv4[0] = bld16(vr, (4u * quad + kk) * row_bytes + pc * 16);
+#pragma unroll
+    for (int u = 0; u < QG; ++u) z[0][u] = ((msk >> (4 * u)) & 1ull) ? f_log[f0][u][kk] : kNegInf;
+    absorb<1, QG>(vv4, z, m, lsum, acc);
   }
 
   // merge the lanes that share a piece (different keys): common max, then sums
@@ -719,28 +703,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_cached(AttendArgs A) {
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < QG * D; idx += kAttThreads) {
-    const int u = idx / D, d = idx % D;
-    if (u >= nq) continue;
-    float mm = kNegInf;
-    for (int w = 0; w < 4; ++w) mm = fmaxf(mm, red[w][u][D]);
-    float ll = 0.f, o = 0.f;
-    if (mm != kNegInf) {
-      for (int w = 0; w < 4; ++w) {
-        const float mw = red[w][u][D];
-        if (mw == kNegInf) continue;
-        const float f = __expf(mw - mm);
-        ll += red[w][u][D + 1] * f;
-        o += red[w][u][d] * f;
-      }
-    }
-    float* part = A.partial + (((int64_t)cache * A.QC + qg0 + u) * A.n_tiles + tile) * (D + 2);
-    if (d == 0) {
-      part[0] = mm;
-      part[1] = ll;
-    }
-    part[2 + d] = o;
-  }
+  write_partial<D, QG>(A, red, cache, qg0, nq, tile);
 }
 
 template <int D>
