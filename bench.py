@@ -87,7 +87,7 @@ def selection_bytes(cfg: zha.ZhaConfig, buf, n_tokens: int, T: int, logits: bool
     sizes = level_sizes(n_tokens, C, Lv)
     caches, QC = cfg.n_caches, cfg.q_per_kv * T
     node_bytes = R * d * cfg.esize + 4 * R
-    QW = min(QC, 16)
+    QW = min(QC, 16)  # useful logits per key (rows are padded to 4 in memory)
     leaf_bytes = C * d * cfg.esize + R * C * 4 + 4 * R if cfg.leaf_form == "weights" else node_bytes
     if logits:
         leaf_bytes += C * QW * 4

@@ -138,9 +138,10 @@ typedef struct zha_tree_layout {
  *          (in records).
  * Optional logits (leaf-weights form only): level-1 scoring computes
  * q . k_i / sqrt(d) for every key of every candidate chunk; zha_route can
- * keep them in a [caches][ceil(QC/16)][capacity/4][min(QC,16)][4] fp32 buffer
- * (4-key quads; QC = G*T queries per cache) so that zha_attend reads 16 bytes
- * per query and quad instead of the keys.
+ * keep them in a [caches][ceil(QC/16)][capacity/4][4][QW] fp32 buffer (4-key
+ * quads, 4 keys, QW = min(QC rounded up to 4, 16) queries; QC = G*T queries
+ * per cache; rows beyond QC unused) so that zha_attend reads 16 bytes per key
+ * and query instead of the keys.
  */
 typedef struct zha_route_layout {
   int32_t levels;

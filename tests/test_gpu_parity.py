@@ -308,9 +308,9 @@ def check_cached_logits(cfg, buf, K, Q, N, T, n_queries=3, max_chunks=48):
     q.k / sqrt(d) in fp64 (products of bf16 values are exact in fp32; the
     only error is the fp32 accumulation)."""
     QC = cfg.q_per_kv * T
-    QB, QW = (QC + 15) // 16, min(QC, 16)
+    QB, QW = (QC + 15) // 16, min((QC + 3) // 4 * 4, 16)
     nquads = buf.logits.numel() // (cfg.n_caches * QB * QW * 4)
-    lg = buf.logits.view(cfg.n_caches, QB, nquads, QW, 4)
+    lg = buf.logits.view(cfg.n_caches, QB, nquads, 4, QW)
     rng = np.random.default_rng(11)
     d = cfg.head_dim
     for cache in sorted({0, cfg.n_caches - 1}):
@@ -322,7 +322,7 @@ def check_cached_logits(cfg, buf, K, Q, N, T, n_queries=3, max_chunks=48):
             kept = kept[rng.permutation(kept.size)[:max_chunks]]
             keys = (kept[:, None] * cfg.chunk + np.arange(cfg.chunk)[None, :]).reshape(-1)
             kt = torch.as_tensor(keys, device=lg.device)
-            got = lg[cache, int(ql) // 16, kt // 4, int(ql) % 16, kt % 4].double().cpu().numpy()
+            got = lg[cache, int(ql) // 16, kt // 4, kt % 4, int(ql) % 16].double().cpu().numpy()
             q = np64(Q[bb, h, int(ql) // T, int(ql) % T])
             Kk = np64(K[bb, h, kt])
             ref = Kk @ q / math.sqrt(d)

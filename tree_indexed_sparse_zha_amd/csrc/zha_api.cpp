@@ -242,6 +242,9 @@ int zha_get_tree_layout(const zha_config* cfg, zha_tree_layout* out) {
   return ZHA_OK;
 }
 
+// Queries per row of the logits buffer: QC rounded up to 4, at most 16.
+static int logits_row(int64_t QC) { return QC >= 16 ? 16 : (int)((QC + 3) / 4 * 4); }
+
 // Key-range slots of every level: offsets (in uint32 units) into the route
 // workspace when `off` is given; returns the bytes needed.
 static int64_t kr_total(const zha_config* cfg, const zha_tree_layout& tl, int64_t n_queries, int64_t* off) {
@@ -284,7 +287,7 @@ int zha_get_route_layout(const zha_config* cfg, int32_t T, zha_route_layout* out
   if (cfg->leaf_form == ZHA_LEAF_WEIGHTS) {
     const int64_t QC = (int64_t)cfg->q_per_kv * T;
     out->logits_floats = (int64_t)cfg->batch * cfg->n_kv_heads * cdiv(QC, 16) *
-                         (tl.node_cap[0] * cfg->chunk / 4) * (QC < 16 ? QC : 16) * 4;
+                         (tl.node_cap[0] * cfg->chunk / 4) * 4 * logits_row(QC);
   }
   return ZHA_OK;
 }
@@ -385,7 +388,7 @@ int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const v
       sa.kst = k_strides[2];
       sa.logits = logits;
       sa.nquads = tl.node_cap[0] * cfg->chunk / 4;
-      sa.QW = sa.QC < 16 ? sa.QC : 16;
+      sa.QW = logits_row(sa.QC);
     }
     zha::SelectArgs se;
     std::memset(&se, 0, sizeof(se));
@@ -469,7 +472,7 @@ int zha_attend(const zha_config* cfg, const void* Q, const int64_t q_strides[4],
     zha_tree_layout tl;
     fill_tree_layout(cfg, &tl);
     a.nquads = tl.node_cap[0] * cfg->chunk / 4;
-    a.QW = a.QC < 16 ? a.QC : 16;
+    a.QW = logits_row(a.QC);
   }
   a.out = out;
   a.lse = lse;

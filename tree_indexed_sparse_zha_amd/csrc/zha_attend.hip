@@ -417,7 +417,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_mfma(AttendArgs A) {
     {                                                                                             \
       const int e_ = 4 * (g) + (r16 >> 2);                                                        \
       const uint32_t ro_ = e_ < n_ent ? (4u * e_quad[e_] + (r16 & 3)) * row_bytes : kOffNone;     \
-      _Pragma("unroll") for (int s_ = 0; s_ < NS; ++s_) KA[s_] = bld16(kr, ro_ + (4 * s_ + kg) * 16); \
+      _Pragma("unroll") for (int s_ = 0; s_ < NS; ++s_) KA[s_] = bld16<0>(kr, ro_ + (4 * s_ + kg) * 16); \
     }                                                                                             \
     _Pragma("unroll") for (int u_ = 0; u_ < NVL; ++u_) {                                          \
       const int pi_ = lane + 64 * u_;                                                             \
@@ -630,7 +630,9 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_cached(AttendArgs A) {
   const int nqt = (int)((k_hi - k_lo + 3) / 4);
   const float* ltile = A.logits + (((int64_t)cache * ((A.QC + 15) / 16) + qg0 / 16) * A.nquads + (k_lo >> 2)) * A.QW * 4;
   const rsrc_t lr = make_rsrc(ltile, (uint32_t)(nqt * A.QW * 16));
-  const uint32_t lq = (uint32_t)(qg0 % 16) * 16 + kk * 4;  // byte offset of (query 0 of the group, key kk)
+  // byte offset of (key kk, query 0 of the group) within a quad's row; the
+  // group's QG queries are contiguous there (QG <= QW, qg0 % 16 + QG <= QW)
+  const uint32_t lq = (uint32_t)(kk * A.QW + qg0 % 16) * 4;
   float m[QG], lsum[QG], acc[QG][8];
 #pragma unroll
   for (int u = 0; u < QG; ++u) {
@@ -650,11 +652,13 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_cached(AttendArgs A) {
       const uint32_t quad = ok ? e_quad[e] : 0u;
       const unsigned long long msk = ok ? e_mask[e] >> kk : 0ull;
       vv4[t] = bld16(vr, ok ? (4u * quad + kk) * row_bytes + pc * 16 : kOffNone);
+      // the logits of key kk for the group's queries, 4 per 16-byte load
 #pragma unroll
-      for (int u = 0; u < QG; ++u) {
-        const bool sel = (msk >> (4 * u)) & 1ull;
-        const float lz = bld4f(lr, sel ? quad * (uint32_t)A.QW * 16 + lq + u * 16 : kOffNone);
-        z[t][u] = sel ? lz : kNegInf;
+      for (int v = 0; v < QG / 4; ++v) {
+        const uint4 lz = bld16<0>(lr, ok ? quad * (uint32_t)A.QW * 16 + lq + v * 16 : kOffNone);
+        const float l4[4] = {__uint_as_float(lz.x), __uint_as_float(lz.y), __uint_as_float(lz.z), __uint_as_float(lz.w)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[t][4 * v + i] = ((msk >> (4 * (4 * v + i))) & 1ull) ? l4[i] : kNegInf;
       }
     }
     absorb<U, QG>(vv4, z, m, lsum, acc);

@@ -77,9 +77,9 @@ struct ScoreArgs {
   int leaf_weights;            // level 1 in the weights form: g holds w [R][C] fp32
   const void* K;               // keys (weights form only)
   int64_t ksb, ksh, kst;
-  float* logits;               // optional [caches][ceil(QC/16)][nquads][QW][4] (weights form)
+  float* logits;               // optional [caches][ceil(QC/16)][nquads][4][QW] (weights form)
   int64_t nquads;              // 4-key quads per cache in the logits buffer
-  int QW;                      // min(QC, 16)
+  int QW;                      // queries per logits row: min(QC rounded up to 4, 16)
 };
 
 struct SelectArgs {

@@ -319,7 +319,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     live[gi] = (anybits & gmask) != 0ull;
     const uint32_t ko = live[gi] ? (uint32_t)((g * 16 + qn) * A.kst * 2) : kOffNone;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) kf[gi][s] = bld16(kr, ko + (4 * s + kg) * 16);
+    for (int s = 0; s < NS; ++s) kf[gi][s] = bld16<0>(kr, ko + (4 * s + kg) * 16);
   }
 #pragma unroll
   for (int r = 0; r < ITEMS; ++r) {
@@ -351,9 +351,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     for (int i = 0; i < 4; ++i) zz[i] = z[i] * A.inv_sqrt_d;
     const int64_t quad = (k0 + g * 16) / 4 + kg;
     if (A.logits && qn < nq && quad < A.nquads) {
-      // keep the attention logits of these 4 keys for query qn (zha_attend reads them)
-      float* lp = A.logits + ((((int64_t)cache * gridDim.z + blockIdx.z) * A.nquads + quad) * A.QW + qn) * 4;
-      *reinterpret_cast<float4*>(lp) = make_float4(zz[0], zz[1], zz[2], zz[3]);
+      // keep the attention logits of these 4 keys for query qn (zha_attend
+      // reads them): row [quad][key][query], queries innermost
+      float* lp = A.logits + (((int64_t)cache * gridDim.z + blockIdx.z) * A.nquads + quad) * 4 * A.QW + qn;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lp[i * A.QW] = zz[i];
     }
     if constexpr (Q4) {
       if (qn < 4) zl[wave][gi * 4 + kg][qn] = make_float4(zz[0], zz[1], zz[2], zz[3]);
