@@ -44,10 +44,13 @@ def recorded_traffic(kernel: str, workload: str, leaf_form: str, p: float):
     k = rec.get("kernels", {}).get(kernel)
     if not k:
         return None
-    src = k["source"]
-    with open(os.path.join(ROOT, "tree_indexed_sparse_zha_amd", "csrc", src), "rb") as f:
-        h = hashlib.sha256(f.read()).hexdigest()[:16]
-    return k["bytes"] if h == rec["sources"].get(src) else None
+    # the kernel's own source and the device headers every kernel includes
+    for src in (k["source"], "zha_device.h", "zha_internal.h"):
+        with open(os.path.join(ROOT, "tree_indexed_sparse_zha_amd", "csrc", src), "rb") as f:
+            h = hashlib.sha256(f.read()).hexdigest()[:16]
+        if h != rec["sources"].get(src):
+            return None
+    return k["bytes"]
 
 
 def log(msg):
