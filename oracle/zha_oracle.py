@@ -33,7 +33,9 @@ What is computed, for one cache (one sequence x one KV head):
     L_j(P) = logsumexp_c L_j(c),   g_j(P) = sum_c exp(L_j(c) - L_j(P)) g_j(c),
   which is exactly the statistic of all descendant keys.
 * Storage.  g is stored in the KV dtype (rounded once, round-to-nearest-even,
-  from the unrounded merge value); L in fp32-or-better; the plane offset
+  from the unrounded merge value), or, in the low-precision router variant
+  (MTP TL;DR "FP4 router"; read here as FP8 E4M3), per row j as a
+  power-of-two scale times E4M3 values; L in fp32-or-better; the plane offset
   c_j = L_j - r_j . ghat_j / sqrt(d) makes c_j + q . ghat_j / sqrt(d) equal the
   tangent plane written with the stored ghat.
 * Score (MTP "Building the tree": the max over the planes approximates the
@@ -91,9 +93,46 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return out
 
 
+def round_e4m3(x: np.ndarray) -> np.ndarray:
+    """Round fp64 values to the nearest OCP FP8 E4M3 value (ties to even), as fp64.
+
+    E4M3: 1 sign, 4 exponent (bias 7) and 3 mantissa bits; normal values
+    (1 + m/8) * 2**(e-7) for e = 1..15 (largest 448), subnormals m * 2**-9.
+    In every binade [2**E, 2**(E+1)) the spacing is 2**(E-3); below 2**-6 it
+    stays 2**-9.  Inputs must satisfy |x| <= 448 (callers scale first).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    if np.any(a > 448.0):
+        raise ValueError("round_e4m3: |x| > 448")
+    _, e = np.frexp(a)  # a = f * 2**e, 0.5 <= f < 1, so a lies in [2**(e-1), 2**e)
+    quantum = np.ldexp(1.0, np.maximum(e - 1, -6) - 3)
+    return np.copysign(np.rint(a / quantum) * quantum, x)  # np.rint: half to even
+
+
+def fp8_row_scale(g: np.ndarray) -> np.ndarray:
+    """Power-of-two scale 2**s per row (last axis) with max|row| / 2**s in (128, 256].
+
+    s = ceil(log2 max|row|) - 8; a row whose max is below 2**-126 gets 1.
+    """
+    m = np.max(np.abs(np.asarray(g, dtype=np.float64)), axis=-1)
+    f, e = np.frexp(m)  # m = f * 2**e, 0.5 <= f < 1
+    ceil_log2 = np.where(f == 0.5, e - 1, e)
+    s = np.where(m < 2.0**-126, 0, ceil_log2 - 8)
+    return np.ldexp(1.0, s)
+
+
+def round_fp8_rows(g: np.ndarray):
+    """(ghat, scale): each row of g (last axis) stored as scale * E4M3(g / scale)."""
+    scale = fp8_row_scale(g)
+    return scale[..., None] * round_e4m3(np.asarray(g, dtype=np.float64) / scale[..., None]), scale
+
+
 def round_storage(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return round_bf16(x)
+    if dtype == "fp8":
+        return round_fp8_rows(x)[0]
     if dtype == "f32":
         return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
     if dtype == "f64":
@@ -140,6 +179,7 @@ class Level:
     g: Optional[np.ndarray]  # [n, R, d] unrounded softmax-weighted mean key
     ghat: np.ndarray  # [n, R, d] stored (rounded) g
     c: np.ndarray  # [n, R] plane offset L - r . ghat / sqrt(d)
+    scale: Optional[np.ndarray] = None  # [n, R] row scales of fp8 storage
 
 
 def _logsumexp(a: np.ndarray, axis: int) -> np.ndarray:
@@ -171,11 +211,15 @@ def _finish(L, g, ref, g_dtype, keep_g, block=8192):
     d = ref.shape[-1]
     ghat = np.empty_like(g)
     c = np.empty_like(L)
+    scale = np.empty_like(L) if g_dtype == "fp8" else None
     for a in range(0, L.shape[0], block):
         b = min(L.shape[0], a + block)
-        ghat[a:b] = round_storage(g[a:b], g_dtype)
+        if g_dtype == "fp8":
+            ghat[a:b], scale[a:b] = round_fp8_rows(g[a:b])
+        else:
+            ghat[a:b] = round_storage(g[a:b], g_dtype)
         c[a:b] = L[a:b] - np.einsum("nrd,rd->nr", ghat[a:b], ref) / math.sqrt(d)
-    return Level(L=L, g=g if keep_g else None, ghat=ghat, c=c)
+    return Level(L=L, g=g if keep_g else None, ghat=ghat, c=c, scale=scale)
 
 
 def build_tree(

@@ -8,8 +8,8 @@ differ must be ambiguous:
     [prefix_excl, prefix_incl] / M interval, widened by 1e-4, contains p; or
   * its oracle score is within eps_score of the score of the oracle's last
     kept node (an order swap caused by rounding of near-equal scores).
-eps_score (below) is 5e-5 when g is stored in fp32; with bf16 storage it
-bounds two rounding flips of g at the level's largest magnitudes.
+eps_score (below) is 5e-5 when g is stored in fp32; with bf16 or fp8 storage
+it bounds two rounding flips of g at the level's largest magnitudes.
 """
 from __future__ import annotations
 
@@ -38,7 +38,9 @@ def eps_score(dtype: str, q: np.ndarray, level) -> float:
         return 5e-5
     d = q.shape[-1]
     gmax = float(np.abs(level.ghat).max()) if level.ghat.size else 0.0
-    return 2.0 * (float(np.abs(q).max()) + 1.0) * gmax * 2.0**-7 / np.sqrt(d) + 5e-5
+    # relative spacing of the stored format: bf16 2^-7, fp8 E4M3 2^-3
+    rel = 2.0**-3 if dtype == "fp8" else 2.0**-7
+    return 2.0 * (float(np.abs(q).max()) + 1.0) * gmax * rel / np.sqrt(d) + 5e-5
 
 
 @dataclasses.dataclass

@@ -275,6 +275,83 @@ def test_bf16_rounding_single_rounding_from_fp64():
     assert O.round_bf16(np.array([3.0 * 2.0**-8 + 1.0]))[0] == 1.0 + 2.0**-6
 
 
+def _e4m3_table():
+    """All finite E4M3 values by code, from the bit layout alone: sign, 4
+    exponent bits (bias 7), 3 mantissa bits; exponent 0 is subnormal; code
+    0x7F / 0xFF (exponent 15, mantissa 7) is NaN."""
+    vals = {}
+    for code in range(256):
+        sgn = -1.0 if code & 0x80 else 1.0
+        e, m = (code >> 3) & 15, code & 7
+        if e == 15 and m == 7:
+            continue
+        vals[code] = sgn * (m / 8.0 * 2.0**-6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return vals
+
+
+def _e4m3_brute(x):
+    """Nearest E4M3 value by exhaustive search; ties go to the even code."""
+    table = _e4m3_table()
+    best = min(table.items(), key=lambda kv: (abs(kv[1] - x), kv[0] & 1, kv[0]))
+    return best[1]
+
+
+def test_e4m3_rounding_matches_brute_force():
+    table = _e4m3_table()
+    pos = sorted(set(abs(v) for v in table.values()))
+    assert max(pos) == 448.0 and min(v for v in pos if v > 0) == 2.0**-9 and len(pos) == 127
+    xs = [0.0]
+    for a, b in zip(pos[:-1], pos[1:]):
+        mid = 0.5 * (a + b)
+        xs += [a, mid, np.nextafter(mid, 0.0), np.nextafter(mid, 1e9)]
+    rng = np.random.default_rng(3)
+    xs += list(rng.uniform(-448, 448, 3000)) + list(rng.normal(0, 0.02, 2000))
+    xs = np.array(xs + [-v for v in xs])
+    got = O.round_e4m3(xs)
+    want = np.array([_e4m3_brute(float(x)) for x in xs])
+    np.testing.assert_array_equal(np.abs(got), np.abs(want))
+    assert np.all((got == 0) | (np.sign(got) == np.sign(xs)))
+
+
+def test_fp8_rows_scale_and_error():
+    rng = np.random.default_rng(4)
+    g = rng.normal(size=(50, 16, 64)) * np.exp(rng.normal(size=(50, 16, 1)) * 3)
+    g[0, 0] = 0.0
+    g[1, 1, :] = 0.0
+    g[1, 1, 5] = 2.0**-3  # max exactly a power of two: row max maps to 256
+    ghat, scale = O.round_fp8_rows(g)
+    m = np.abs(g).max(axis=-1)
+    nz = m > 0
+    r = m[nz] / scale[nz]
+    assert np.all((r > 128) & (r <= 256))
+    assert scale[0, 0] == 1.0 and np.all(ghat[0, 0] == 0)
+    assert ghat[1, 1, 5] == 2.0**-3 and scale[1, 1] == 2.0**-11
+    assert np.all(np.log2(scale) == np.round(np.log2(scale)))
+    # each element is within half a spacing of its exact value (spacing 2^-3
+    # relative in a binade, 2^-9 * scale below the normal range)
+    spacing = np.maximum(2.0 ** (np.floor(np.log2(np.maximum(np.abs(g) / scale[..., None], 2.0**-6))) - 3), 2.0**-9)
+    assert np.all(np.abs(ghat - g) <= 0.5 * spacing * scale[..., None] * (1 + 1e-12))
+
+
+def test_fp8_tree_keeps_tangent_point():
+    """With fp8 storage plane j still passes through (r_j, L_j): c absorbs the
+    rounding of g.  The other planes are no longer exact tangents, so the max
+    at r_j is >= L_j, by at most the rounding's reach."""
+    K, V, ref, Q = _rand_cache(256, 16, 4, 11)
+    d = ref.shape[1]
+    tree = O.build_tree(K, ref, 4, 3, "fp8")
+    for lvl in tree:
+        assert lvl.scale is not None
+        np.testing.assert_array_equal(lvl.ghat, O.round_fp8_rows(lvl.g)[0])
+        for j in range(4):
+            plane_j = lvl.c[:, j] + lvl.ghat[:, j] @ ref[j] / math.sqrt(d)
+            np.testing.assert_allclose(plane_j, lvl.L[:, j], rtol=0, atol=1e-12)
+            s = O.plane_scores(ref[j], lvl, ref)
+            assert np.all(s >= lvl.L[:, j] - 1e-12)
+            reach = np.abs(ref[j] - ref).sum(axis=1).max() * np.abs(lvl.ghat - lvl.g).max() / math.sqrt(d)
+            assert np.all(s - lvl.L[:, j] <= reach + 1e-12)
+
+
 def test_golden_geometry():
     gold = json.load(open(os.path.join(GOLDEN, "geometry.json")))
     for t in gold["trees"]:
