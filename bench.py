@@ -57,9 +57,10 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def cfg_of(w: W.Workload, capacity: int, leaf_form: str) -> zha.ZhaConfig:
+def cfg_of(w: W.Workload, capacity: int, leaf_form: str, g_dtype: str = "kv") -> zha.ZhaConfig:
     return zha.ZhaConfig(
-        w.batch, w.n_kv_heads, w.q_per_kv, w.head_dim, w.n_ref, w.chunk, w.levels, w.dtype, capacity, leaf_form
+        w.batch, w.n_kv_heads, w.q_per_kv, w.head_dim, w.n_ref, w.chunk, w.levels, w.dtype, capacity, leaf_form,
+        g_dtype,
     )
 
 
@@ -79,7 +80,8 @@ def selection_bytes(cfg: zha.ZhaConfig, buf, n_tokens: int, T: int, logits: bool
     """Algorithmic bytes of one route + attend from the selection it made.
 
     route, per cache and level: |union over the cache's queries of the
-    candidates| x (R*d*2 bytes of g + 4R bytes of c), or at level 1 in the
+    candidates| x (R*d*2 bytes of g + 4R bytes of c; fp8 g: R*d + 8R with the
+    row scales), or at level 1 in the
     weights form x (C*d*2 bytes of keys + 4RC of weights + 4R of c, plus
     4*min(QC,16) bytes of logits written per key when they are kept);
     attend, per cache: |union over the cache's queries of the attended keys|
@@ -89,7 +91,8 @@ def selection_bytes(cfg: zha.ZhaConfig, buf, n_tokens: int, T: int, logits: bool
     C, Lv, R, d = cfg.chunk, cfg.levels, cfg.n_ref, cfg.head_dim
     sizes = level_sizes(n_tokens, C, Lv)
     caches, QC = cfg.n_caches, cfg.q_per_kv * T
-    node_bytes = R * d * cfg.esize + 4 * R
+    gsize = 1 if cfg.g_dtype == "fp8" else cfg.esize  # bytes per stored g element
+    node_bytes = R * d * gsize + 4 * R * (2 if cfg.g_dtype == "fp8" else 1)  # g, c (+ row scales)
     QW = min(QC, 16)  # useful logits per key (rows are padded to 4 in memory)
     leaf_bytes = C * d * cfg.esize + R * C * 4 + 4 * R if cfg.leaf_form == "weights" else node_bytes
     if logits:
@@ -182,6 +185,8 @@ def main():
     ap.add_argument("--tokens", type=int, default=None, help="override the context length (sweeps)")
     ap.add_argument("--leaf-form", default="weights", choices=["weights", "mean"],
                     help="level-1 storage: softmax weights scored from raw keys (default) or mean keys")
+    ap.add_argument("--g-dtype", default="kv", choices=["kv", "fp8"],
+                    help="storage of the mean keys g: the KV dtype (default) or FP8 E4M3 with row scales")
     ap.add_argument("--no-logits", action="store_true",
                     help="attention recomputes every logit from K instead of reading the route's level-1 logits")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -209,7 +214,7 @@ def main():
     capacity = N0 + n_steps * A
     if args.leaf_form == "weights" and w.chunk not in (4, 8, 16):
         args.leaf_form = "mean"
-    cfg = cfg_of(w, capacity, args.leaf_form)
+    cfg = cfg_of(w, capacity, args.leaf_form, args.g_dtype)
     torch.cuda.set_device(0)
     log(f"workload {w.name}: N={N0} caches={cfg.n_caches} p={p} capacity={capacity}")
 
@@ -282,9 +287,11 @@ def main():
         cfg, buf, n_final, T, logits=buf.logits is not None
     )
     route_bytes = sum(v["alg_bytes"] for v in per_level.values())
-    tree_bytes_per_token = sum(
-        cfg.n_ref * (cfg.head_dim * cfg.esize + 8) / (cfg.chunk**l) for l in range(2, cfg.levels + 1)
-    ) + (cfg.n_ref * (4 * cfg.chunk + 8) if cfg.leaf_form == "weights" else cfg.n_ref * (cfg.head_dim * cfg.esize + 8)) / cfg.chunk
+    g8 = cfg.g_dtype == "fp8"
+    mean_node = cfg.n_ref * (cfg.head_dim * (1 if g8 else cfg.esize) + (12 if g8 else 8))  # g, L, c (+ scales)
+    tree_bytes_per_token = sum(mean_node / (cfg.chunk**l) for l in range(2, cfg.levels + 1)) + (
+        cfg.n_ref * (4 * cfg.chunk + 8) if cfg.leaf_form == "weights" else mean_node
+    ) / cfg.chunk
     append_bytes = cfg.n_caches * A * (cfg.head_dim * cfg.esize + tree_bytes_per_token)
     alg = {"attend": attend_bytes, "build": append_bytes}
     for lv, v in per_level.items():
@@ -358,6 +365,7 @@ def main():
             "p": p,
             "append_tokens_per_step": A,
             "leaf_form": cfg.leaf_form,
+            "g_dtype": cfg.g_dtype,
             "cached_logits": buf.logits is not None,
             "queries_per_step": nq,
         },

@@ -72,6 +72,19 @@ enum zha_dtype { ZHA_F32 = 0, ZHA_BF16 = 1 };
  */
 enum zha_leaf_form { ZHA_LEAF_MEAN = 0, ZHA_LEAF_WEIGHTS = 1 };
 
+/*
+ * Storage of the mean keys g of the levels that store them (every level but
+ * level 1 in the weights form).
+ *   ZHA_G_KV: kv_dtype.
+ *   ZHA_G_FP8: the low-precision router variant (MTP TL;DR, "FP4 router"),
+ *     read as OCP FP8 E4M3 with one power-of-two scale per node and
+ *     reference query: row j is stored as s_j * e4m3(g_j / s_j), rounded to
+ *     nearest even, with s_j = 2^(ceil(log2 max_e |g_je|) - 8) (1 for a zero
+ *     row) in the tree's scale block; c_j uses the stored values.  Halves
+ *     the bytes routing reads per node.  Needs kv_dtype ZHA_BF16.
+ */
+enum zha_g_dtype { ZHA_G_KV = 0, ZHA_G_FP8 = 2 };
+
 /* Flags of zha_attend. */
 enum zha_attend_flags {
   ZHA_SINK = 1,       /* token 0 is always attended (MTP "How does top-p routing pick tokens?") */
@@ -95,6 +108,7 @@ typedef struct zha_config {
   int32_t levels;          /* Lv: level 1 = chunks of raw keys, level Lv = top */
   int32_t kv_dtype;        /* enum zha_dtype */
   int32_t leaf_form;       /* enum zha_leaf_form */
+  int32_t g_dtype;         /* enum zha_g_dtype (0 = ZHA_G_KV) */
   int64_t capacity_tokens; /* largest N the tree buffer must hold */
 } zha_config;
 
@@ -112,6 +126,11 @@ typedef struct zha_config {
  *   L: [caches][node_cap][R] fp32, log mass L_j of the node.
  *   c: [caches][node_cap][R] fp32, plane offset c_j = L_j - r_j . g_j / sqrt(d)
  *      with the stored (rounded) g_j.
+ * With g_dtype ZHA_G_FP8 the levels that store mean keys hold R x d E4M3
+ * bytes per node: element (j, e) with MFMA step s = e / 32 and k-group
+ * kg = (e % 32) / 8 lives at byte ((s / 2) * 4 * R + kg * R + j) * 16 +
+ * (s % 2) * 8 + e % 8 (one 16-byte load yields two MFMA steps), and a fourth
+ * block s: [caches][node_cap][R] fp32 holds the row scales (s_offset).
  * Offsets are bytes from the tree base; every block is 256-byte aligned.
  */
 typedef struct zha_tree_layout {
@@ -123,6 +142,7 @@ typedef struct zha_tree_layout {
   int64_t c_offset[ZHA_MAX_LEVELS];
   int64_t g_bytes[ZHA_MAX_LEVELS]; /* bytes of one node's g (or w) block, per level */
   int64_t total_bytes;  /* size of the caller's tree buffer */
+  int64_t s_offset[ZHA_MAX_LEVELS]; /* fp8 row scales per level, or -1 */
 } zha_tree_layout;
 
 /*

@@ -65,10 +65,24 @@ def test_tree_layout_weights_form():
     assert tl.total_bytes < mean.total_bytes * 0.35
 
 
+def test_tree_layout_fp8():
+    for leaf_form in ("mean", "weights"):
+        tl = zha.tree_layout(cfg_deep(leaf_form=leaf_form, g_dtype="fp8"))
+        kv = zha.tree_layout(cfg_deep(leaf_form=leaf_form))
+        for i in range(6):
+            weights = leaf_form == "weights" and i == 0
+            assert tl.g_bytes[i] == (16 * 4 * 4 if weights else 16 * 128)
+            assert (tl.s_offset[i] == -1) if weights else (tl.s_offset[i] % 256 == 0 and tl.s_offset[i] > tl.c_offset[i])
+            assert kv.s_offset[i] == -1
+        assert all(tl.s_offset[i] == -1 for i in range(6, zha.MAX_LEVELS))
+        # fp8 nodes: R*d (g) + 3 * 4R (L, c, scale) bytes
+        assert tl.total_bytes < kv.total_bytes
+
+
 def test_route_layout_logits():
     assert zha.route_layout(cfg_deep(), 1).logits_floats == 0
     rl = zha.route_layout(cfg_deep(leaf_form="weights"), 1)
-    # caches x ceil(QC/16) x quads x min(QC, 16) x 4 (QC = 4 queries per cache)
+    # caches x ceil(QC/16) x quads x 4 keys x QW (QW = QC rounded up to 4, at most 16; QC = 4 here)
     assert rl.logits_floats == 8 * 1 * (32768 // 4) * 4 * 4
     rl = zha.route_layout(cfg_deep(leaf_form="weights"), 8)  # QC = 32: two groups of 16
     assert rl.logits_floats == 8 * 2 * (32768 // 4) * 16 * 4
@@ -106,6 +120,9 @@ def test_route_layout_sizes():
         (dict(leaf_form="weights", dtype="f32"), zha.ZHA_ERR_UNSUPPORTED),
         (dict(leaf_form="weights", chunk=256, levels=1), zha.ZHA_ERR_UNSUPPORTED),
         (dict(leaf_form="weights", chunk=2, levels=6), zha.ZHA_ERR_UNSUPPORTED),
+        (dict(g_dtype="fp8"), 0),
+        (dict(g_dtype="fp8", leaf_form="weights"), 0),
+        (dict(g_dtype="fp8", dtype="f32", head_dim=64, n_ref=4, chunk=4, levels=3), zha.ZHA_ERR_UNSUPPORTED),
     ],
 )
 def test_config_validation(kw, code):

@@ -191,6 +191,9 @@ BUILD_CASES = [
     ("deep-bf16-weights", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=6, dtype="bf16", capacity=9000, leaf_form="weights"), 8192 + 4 * 37 + 2),
     ("light-bf16-weights", dict(batch=1, n_kv_heads=1, q_per_kv=4, head_dim=128, n_ref=1, chunk=8, levels=4, dtype="bf16", capacity=5000, leaf_form="weights"), 4096 + 8 * 5 + 3),
     ("c16-bf16-d64-weights", dict(batch=2, n_kv_heads=1, q_per_kv=2, head_dim=64, n_ref=7, chunk=16, levels=2, dtype="bf16", capacity=3000, leaf_form="weights"), 2048 + 16 * 9 + 5),
+    ("deep-bf16-fp8", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=6, dtype="bf16", capacity=9000, g_dtype="fp8"), 8192 + 4 * 37 + 2),
+    ("deep-bf16-weights-fp8", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=6, dtype="bf16", capacity=9000, leaf_form="weights", g_dtype="fp8"), 8192 + 4 * 37 + 2),
+    ("c8-bf16-d64-fp8", dict(batch=1, n_kv_heads=1, q_per_kv=2, head_dim=64, n_ref=5, chunk=8, levels=3, dtype="bf16", capacity=5000, g_dtype="fp8"), 4096 + 8 * 7 + 3),
 ]
 APPEND_CASES = [c for c in BUILD_CASES if c[0] != "c1-f32"]
 
@@ -215,7 +218,8 @@ def check_tree(cfg, tree, K, ref, N):
             cache = b * cfg.n_kv_heads + h
             Kn, rn = np64(K[b, h, :N]), np64(ref[h])
             weights = cfg.leaf_form == "weights"
-            to = O.build_tree(Kn, rn, cfg.chunk, cfg.levels, cfg.dtype, n_tokens=N, leaf_dtype="f64" if weights else None)
+            gd = "fp8" if cfg.g_dtype == "fp8" else cfg.dtype
+            to = O.build_tree(Kn, rn, cfg.chunk, cfg.levels, gd, n_tokens=N, leaf_dtype="f64" if weights else None)
             for lv in range(1, cfg.levels + 1):
                 n = sizes[lv - 1]
                 got = zha.read_level(cfg, tree, lv, n)
@@ -239,6 +243,8 @@ def check_tree(cfg, tree, K, ref, N):
                 if cfg.dtype == "f32":
                     scale = np.abs(lvl.g).max() + 1e-30
                     np.testing.assert_allclose(gg, lvl.g, rtol=0, atol=2e-6 * scale, err_msg=f"g level {lv}")
+                elif cfg.g_dtype == "fp8":
+                    check_fp8_level(lv, np64(got["g"][cache]), np64(got["scale"][cache]), lvl)
                 else:
                     mism = gg != lvl.ghat
                     frac = mism.mean() if mism.size else 0.0
@@ -258,6 +264,31 @@ def check_tree(cfg, tree, K, ref, N):
                             f"level {lv}: {int(bad.sum())} g flips beyond one spacing: gpu {gg[mism][bad][:5]} "
                             f"oracle {lvl.ghat[mism][bad][:5]} exact {lvl.g[mism][bad][:5]}"
                         )
+
+
+def check_fp8_level(lv, gg, gs, lvl):
+    """fp8 rows: the GPU's power-of-two scale equals the oracle's except where
+    the row max sits at a power of two (fp32 and fp64 may then pick
+    neighbouring exponents); codes differ only at rounding boundaries, by one
+    E4M3 spacing, on at most 1e-3 of the elements."""
+    m = np.abs(lvl.g).max(axis=-1)
+    f, _ = np.frexp(np.maximum(m, 1e-300))
+    near_pow2 = np.abs(f - 0.5) < 1e-5
+    same = gs == lvl.scale
+    assert np.all(same | near_pow2), f"level {lv}: {int((~same & ~near_pow2).sum())} row scales differ"
+    assert np.all(np.log2(gs) == np.round(np.log2(gs)))
+    a, b = gg[same], lvl.ghat[same]
+    sc = np.broadcast_to(gs[..., None], gg.shape)[same]
+    mism = a != b
+    frac = mism.mean() if mism.size else 0.0
+    assert frac <= 1e-3, f"level {lv}: {frac:.2e} of fp8 g differ"
+    if mism.any():
+        row = np.broadcast_to(np.abs(lvl.g).max(axis=-1, keepdims=True), lvl.g.shape)[same][mism]
+        x = np.maximum(np.abs(a[mism]), np.abs(b[mism])) / sc[mism]
+        spacing = np.maximum(2.0 ** (np.floor(np.log2(np.maximum(x, 2.0**-6))) - 3), 2.0**-9) * sc[mism]
+        dev = np.abs(a[mism] - b[mism])
+        bad = dev > spacing + 4e-6 * row
+        assert not bad.any(), f"level {lv}: {int(bad.sum())} fp8 flips beyond one spacing"
 
 
 @pytest.mark.parametrize("name,kw,N", BUILD_CASES, ids=[c[0] for c in BUILD_CASES])
@@ -376,20 +407,24 @@ def gpu_levels(cfg, buf, N, qi):
 
 
 ROUTE_WORKLOADS = [
-    ("tiny", None, "mean", 16),  # all queries of the tiny workload
-    ("deep32k", 2, "mean", 6),  # 2 of 8 caches, 6 sampled queries each
-    ("deep32k", 2, "weights", 6),
-    ("wide256k", 2, "mean", 4),
+    ("tiny", None, "mean", 16, "kv"),  # all queries of the tiny workload
+    ("deep32k", 2, "mean", 6, "kv"),  # 2 of 8 caches, 6 sampled queries each
+    ("deep32k", 2, "weights", 6, "kv"),
+    ("wide256k", 2, "mean", 4, "kv"),
+    ("deep32k", 2, "weights", 6, "fp8"),
+    ("deep32k", 1, "mean", 6, "fp8"),
 ]
 
 
 @pytest.mark.parametrize(
-    "wname,n_caches_checked,leaf_form,q_per_cache", ROUTE_WORKLOADS, ids=[f"{r[0]}-{r[2]}" for r in ROUTE_WORKLOADS]
+    "wname,n_caches_checked,leaf_form,q_per_cache,g_dtype",
+    ROUTE_WORKLOADS,
+    ids=[f"{r[0]}-{r[2]}" + ("-fp8" if r[4] == "fp8" else "") for r in ROUTE_WORKLOADS],
 )
-def test_route_and_attend_match_oracle(wname, n_caches_checked, leaf_form, q_per_cache):
+def test_route_and_attend_match_oracle(wname, n_caches_checked, leaf_form, q_per_cache, g_dtype):
     w = W.WORKLOADS[wname]
-    _say(f"route {wname} {leaf_form}")
-    cfg = cfg_of(w, leaf_form=leaf_form)
+    _say(f"route {wname} {leaf_form} {g_dtype}")
+    cfg = cfg_of(w, leaf_form=leaf_form, g_dtype=g_dtype)
     batch = W.make_batch(w, device="cuda")
     N, T, p = w.n_tokens, w.queries_per_head, w.p[0]
     tree, buf, out, lse = run_path(cfg, batch.K, batch.V, batch.Q, batch.ref, N, T, p)
@@ -405,7 +440,8 @@ def test_route_and_attend_match_oracle(wname, n_caches_checked, leaf_form, q_per
         b, h = divmod(cache, cfg.n_kv_heads)
         Kn, Vn, rn = np64(batch.K[b, h, :N]), np64(batch.V[b, h, :N]), np64(batch.ref[h])
         leaf_dtype = "f64" if leaf_form == "weights" else None
-        to = O.build_tree(Kn, rn, cfg.chunk, cfg.levels, cfg.dtype, keep_g=False, leaf_dtype=leaf_dtype)
+        gd = "fp8" if g_dtype == "fp8" else cfg.dtype
+        to = O.build_tree(Kn, rn, cfg.chunk, cfg.levels, gd, keep_g=False, leaf_dtype=leaf_dtype)
         qis = list(range(QC)) if q_per_cache >= QC else sorted(rng.choice(QC, q_per_cache, replace=False).tolist())
         for qi_local in qis:
             gq, t = divmod(qi_local, T)
@@ -413,7 +449,7 @@ def test_route_and_attend_match_oracle(wname, n_caches_checked, leaf_form, q_per
             q = np64(batch.Q[b, h, gq, t])
             bits, scores = gpu_levels(cfg, buf, N, qi)
             kept = PAR.gpu_kept_from_bits(bits)
-            PAR.check_route_teacher_forced(q, to, rn, cfg.chunk, p, kept, cfg.dtype, scores, leaf_dtype=leaf_dtype)
+            PAR.check_route_teacher_forced(q, to, rn, cfg.chunk, p, kept, gd, scores, leaf_dtype=leaf_dtype)
             # attention over the GPU's set (R21)
             idx = O.attend_set(kept[1], N, cfg.chunk, True, True)
             o, l = O.attend(q, Kn, Vn, idx)

@@ -44,6 +44,10 @@ int check_config(const zha_config* c) {
   if (c->leaf_form == ZHA_LEAF_WEIGHTS &&
       (c->kv_dtype != ZHA_BF16 || (c->chunk != 4 && c->chunk != 8 && c->chunk != 16)))
     return fail(ZHA_ERR_UNSUPPORTED, "the leaf weights form needs bf16 and chunk 4, 8 or 16");
+  if (c->g_dtype != ZHA_G_KV && c->g_dtype != ZHA_G_FP8)
+    return fail(ZHA_ERR_ARG, "g_dtype %d unknown", c->g_dtype);
+  if (c->g_dtype == ZHA_G_FP8 && c->kv_dtype != ZHA_BF16)
+    return fail(ZHA_ERR_UNSUPPORTED, "fp8 g needs bf16 keys");
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(ZHA_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", c->head_dim);
   if (c->n_ref > 16) return fail(ZHA_ERR_UNSUPPORTED, "n_ref %d unsupported (1..16)", c->n_ref);
@@ -92,9 +96,10 @@ void fill_tree_layout(const zha_config* c, zha_tree_layout* out) {
   int64_t off = 0;
   for (int l = 0; l < c->levels; ++l) {
     if (l > 0) n = cdiv(n, c->chunk);
-    out->g_bytes[l] = (l == 0 && c->leaf_form == ZHA_LEAF_WEIGHTS)
-                          ? (int64_t)c->n_ref * c->chunk * 4
-                          : (int64_t)c->n_ref * c->head_dim * esize(c->kv_dtype);
+    const bool weights = l == 0 && c->leaf_form == ZHA_LEAF_WEIGHTS;
+    const bool fp8 = !weights && c->g_dtype == ZHA_G_FP8;
+    out->g_bytes[l] = weights ? (int64_t)c->n_ref * c->chunk * 4
+                              : (int64_t)c->n_ref * c->head_dim * (fp8 ? 1 : esize(c->kv_dtype));
     out->node_cap[l] = n;
     out->g_offset[l] = off;
     off = align256(off + caches * n * out->g_bytes[l]);
@@ -102,7 +107,13 @@ void fill_tree_layout(const zha_config* c, zha_tree_layout* out) {
     off = align256(off + caches * n * c->n_ref * 4);
     out->c_offset[l] = off;
     off = align256(off + caches * n * c->n_ref * 4);
+    out->s_offset[l] = -1;
+    if (fp8) {
+      out->s_offset[l] = off;
+      off = align256(off + caches * n * c->n_ref * 4);
+    }
   }
+  for (int l = c->levels; l < ZHA_MAX_LEVELS; ++l) out->s_offset[l] = -1;
   out->total_bytes = off > 0 ? off : 256;
 }
 
@@ -121,6 +132,8 @@ void fill_geom(const zha_config* c, const zha_tree_layout& tl, zha::TreeGeom* g)
     g->g_off[l] = tl.g_offset[l];
     g->L_off[l] = tl.L_offset[l];
     g->c_off[l] = tl.c_offset[l];
+    g->s_off[l] = tl.s_offset[l];
+    if (tl.s_offset[l] >= 0) g->g8 |= 1u << l;
   }
   g->span_len[0] = 1;
   for (int l = 1; l <= c->levels; ++l) g->span_len[l] = g->span_len[l - 1] * c->chunk;
@@ -359,6 +372,9 @@ int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const v
     std::memset(&sa, 0, sizeof(sa));
     sa.g = static_cast<const char*>(tree) + tl.g_offset[l];
     sa.c = reinterpret_cast<const float*>(static_cast<const char*>(tree) + tl.c_offset[l]);
+    sa.gscale = tl.s_offset[l] >= 0
+                    ? reinterpret_cast<const float*>(static_cast<const char*>(tree) + tl.s_offset[l])
+                    : nullptr;
     sa.node_cap = tl.node_cap[l];
     sa.n_nodes = n[l];
     sa.R = cfg->n_ref;

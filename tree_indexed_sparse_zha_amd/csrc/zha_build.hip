@@ -47,13 +47,6 @@ __device__ __forceinline__ void absorb(float& am, float& as, float* aacc, bool& 
   am = mn;
 }
 
-// Wave-scope barrier for LDS regions private to one wave.
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // W > 1: the workgroup's W waves share one top span (W divides C), wave w
 // streaming the w-th W-th of it, i.e. C / W whole children of the top node;
 // their open top-level accumulators are merged in LDS, in wave order, by
@@ -109,7 +102,55 @@ __global__ __launch_bounds__(64 * W) void k_build_span(BuildArgs A) {
   for (int a = 0; a < NAR; ++a) used[a] = false;
 
   auto emit = [&](int lvl, int64_t node, float L, const float* g) {
+    const int64_t nidx = (int64_t)cache * geo.node_cap[lvl - 1] + node;
     float gr[NV];
+    if constexpr (sizeof(T) == 2 && NS % 2 == 0) {
+      if ((geo.g8 >> (lvl - 1)) & 1u) {
+        // fp8 E4M3 with a power-of-two scale per row j: 2^e, e = ceil(log2 max|g_j|) - 8
+        float mx = 0.f;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) mx = fmaxf(mx, fabsf(g[v]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const uint32_t mb = __float_as_uint(mx);
+        const int ex = (int)(mb >> 23) & 255;
+        const int e = ex == 0 ? 0 : ((mb & 0x7fffffu) == 0u ? ex - 127 : ex - 126) - 8;
+        const float scl = ldexpf(1.f, e);
+        uint32_t w8[NV / 4];  // 4 E4M3 codes per word, hardware round to nearest even
+#pragma unroll
+        for (int k = 0; k < NV / 4; ++k) {
+          const float a0 = ldexpf(g[4 * k], -e), a1 = ldexpf(g[4 * k + 1], -e);
+          const float a2 = ldexpf(g[4 * k + 2], -e), a3 = ldexpf(g[4 * k + 3], -e);
+          const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+          w8[k] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, lo, true);
+          gr[4 * k + 0] = __builtin_amdgcn_cvt_f32_fp8((int)w8[k], 0) * scl;
+          gr[4 * k + 1] = __builtin_amdgcn_cvt_f32_fp8((int)w8[k], 1) * scl;
+          gr[4 * k + 2] = __builtin_amdgcn_cvt_f32_fp8((int)w8[k], 2) * scl;
+          gr[4 * k + 3] = __builtin_amdgcn_cvt_f32_fp8((int)w8[k], 3) * scl;
+        }
+        float dot = 0.f;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) dot += rj[v] * gr[v];
+        dot += __shfl_xor(dot, 16);
+        dot += __shfl_xor(dot, 32);
+        const float c = L - dot * isd;
+        if (j < R) {
+          // this lane's 8-value pieces s = 0..NS-1 are MFMA steps s, k-group dg;
+          // steps 2P and 2P+1 share one 16-byte slot
+          char* gb = A.tree + geo.g_off[lvl - 1] + nidx * ((int64_t)R * D);
+#pragma unroll
+          for (int P = 0; P < NS / 2; ++P)
+            st16(gb + ((int64_t)(P * 4 + dg) * R + j) * 16,
+                 make_uint4(w8[4 * P], w8[4 * P + 1], w8[4 * P + 2], w8[4 * P + 3]));
+          if (dg == 0) {
+            reinterpret_cast<float*>(A.tree + geo.L_off[lvl - 1])[nidx * R + j] = L;
+            reinterpret_cast<float*>(A.tree + geo.c_off[lvl - 1])[nidx * R + j] = c;
+            reinterpret_cast<float*>(A.tree + geo.s_off[lvl - 1])[nidx * R + j] = scl;
+          }
+        }
+        return;
+      }
+    }
     uint4 pk[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) pk[s] = pack(&g[s * E], &gr[s * E], T());
@@ -119,7 +160,6 @@ __global__ __launch_bounds__(64 * W) void k_build_span(BuildArgs A) {
     dot += __shfl_xor(dot, 16);
     dot += __shfl_xor(dot, 32);
     const float c = L - dot * isd;
-    const int64_t nidx = (int64_t)cache * geo.node_cap[lvl - 1] + node;
     if (j < R) {
       char* gb = A.tree + geo.g_off[lvl - 1] + nidx * ((int64_t)R * D * Elem<T>::size);
 #pragma unroll

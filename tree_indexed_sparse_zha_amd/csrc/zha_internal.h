@@ -43,6 +43,8 @@ struct TreeGeom {
   int64_t g_off[kMaxLevels];
   int64_t L_off[kMaxLevels];
   int64_t c_off[kMaxLevels];
+  int64_t s_off[kMaxLevels];  // fp8 row scales per level, or -1
+  uint32_t g8;                // bit l-1: level l stores g as fp8 E4M3 with row scales
   int64_t span_len[kMaxLevels + 1];  // span_len[l] = C^l tokens covered by a level-l node
 };
 
@@ -62,6 +64,7 @@ struct BuildArgs {
 struct ScoreArgs {
   const char* g;         // level base of g
   const float* c;        // level base of c
+  const float* gscale;   // level base of the fp8 row scales, or nullptr (g in the KV dtype)
   int64_t node_cap;      // nodes per cache at this level
   int64_t n_nodes;       // valid nodes per cache at this level
   int R, C, D, H, G, T, QC;  // QC = G * T queries per cache

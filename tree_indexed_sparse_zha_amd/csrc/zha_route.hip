@@ -78,7 +78,10 @@ __global__ void k_route_init(uint32_t* kr, int64_t n) {
 // ---------------------------------------------------------------------------
 // score, bf16, MFMA
 
-template <int D>
+// G8: g stored as fp8 E4M3 with a power-of-two scale per row; each 16-byte
+// load holds two MFMA steps, converted to bf16 with the row's scale applied
+// (exact: E4M3 values times powers of two are bf16 values).
+template <int D, bool G8>
 __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs A) {
   constexpr int NS = D / 32;  // MFMA k-steps of 32 bf16
   constexpr int TILE = 64;
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs A) {
       for (int s = 0; s < NS; ++s) bq[s] = as_bf16x8(make_uint4(0, 0, 0, 0));
     }
   }
-  const int64_t gnode = (int64_t)R * D * 2;
+  const int64_t gnode = (int64_t)R * D * (G8 ? 1 : 2);
   const char* gcache = A.g + (int64_t)cache * A.node_cap * gnode;
   const float* ccache = A.c + (int64_t)cache * A.node_cap * R;
   const int jrow = lane & 15;
@@ -142,7 +145,10 @@ __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs A) {
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) anybits |= (uint32_t)__shfl_xor((int)anybits, o);
 
-  auto load_batch = [&](int u0, uint4 (*af)[NS], float (*cv)[4]) {
+  // raw 16-byte loads per node and lane: NS pieces (bf16) or NS / 2 (fp8)
+  constexpr int NL = G8 ? NS / 2 : NS;
+  const float* scache = G8 ? A.gscale + (int64_t)cache * A.node_cap * R : nullptr;
+  auto load_batch = [&](int u0, uint4 (*af)[NL], float (*cv)[4], float* sv) {
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
       const int u = u0 + k;
@@ -150,8 +156,9 @@ __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs A) {
       const bool live = (anybits >> u) & 1u;
       const char* gn = gcache + m * gnode;
 #pragma unroll
-      for (int s = 0; s < NS; ++s)
+      for (int s = 0; s < NL; ++s)
         af[k][s] = live && jrow < R ? ld16(gn + ((int64_t)(4 * s + kg) * R + jrow) * 16) : make_uint4(0, 0, 0, 0);
+      if constexpr (G8) sv[k] = live && jrow < R ? scache[m * R + jrow] : 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int jj = 4 * kg + i;
@@ -160,11 +167,12 @@ __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs A) {
     }
   };
 
-  uint4 af[NB][NS], an[NB][NS];
+  uint4 af[NB][NL], an[NB][NL];
   float cv[NB][4], cn[NB][4];
-  load_batch(0, af, cv);
+  float sv[NB], sn[NB];
+  load_batch(0, af, cv, sv);
   for (int u0 = 0; u0 < 16; u0 += NB) {
-    if (u0 + NB < 16) load_batch(u0 + NB, an, cn);
+    if (u0 + NB < 16) load_batch(u0 + NB, an, cn, sn);
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
       const int u = u0 + k;
@@ -172,8 +180,21 @@ __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs A) {
       if ((anybits >> u) & 1u) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af[k][s]), bq[s], acc, 0, 0, 0);
+        for (int s = 0; s < NS; ++s) {
+          uint4 op;
+          if constexpr (G8) {
+            // 8 E4M3 codes of step s (words x, y or z, w of the pair's slot) -> bf16 x scale
+            const uint32_t w0 = (s & 1) ? af[k][s / 2].z : af[k][s / 2].x;
+            const uint32_t w1 = (s & 1) ? af[k][s / 2].w : af[k][s / 2].y;
+            op.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, sv[k], false));
+            op.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, sv[k], true));
+            op.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, sv[k], false));
+            op.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, sv[k], true));
+          } else {
+            op = af[k][s];
+          }
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(op), bq[s], acc, 0, 0, 0);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) v = fmaxf(v, cv[k][i] + acc[i] * A.inv_sqrt_d);
         v = fmaxf(v, __shfl_xor(v, 16));
@@ -184,9 +205,10 @@ __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs A) {
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
 #pragma unroll
-      for (int s = 0; s < NS; ++s) af[k][s] = an[k][s];
+      for (int s = 0; s < NL; ++s) af[k][s] = an[k][s];
 #pragma unroll
       for (int i = 0; i < 4; ++i) cv[k][i] = cn[k][i];
+      sv[k] = sn[k];
     }
   }
   __syncthreads();
@@ -784,10 +806,16 @@ hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dty
 #undef ZHA_LW_Q
     } else if (dtype == 1) {
       dim3 grid((unsigned)((sa.n_nodes + 63) / 64), (unsigned)n_caches, (unsigned)((sa.QC + 15) / 16));
-      if (sa.D == 128)
-        hipLaunchKernelGGL(k_score_bf16<128>, grid, dim3(256), 0, s, sa);
-      else
-        hipLaunchKernelGGL(k_score_bf16<64>, grid, dim3(256), 0, s, sa);
+      if (sa.gscale) {
+        if (sa.D == 128)
+          hipLaunchKernelGGL((k_score_bf16<128, true>), grid, dim3(256), 0, s, sa);
+        else
+          hipLaunchKernelGGL((k_score_bf16<64, true>), grid, dim3(256), 0, s, sa);
+      } else if (sa.D == 128) {
+        hipLaunchKernelGGL((k_score_bf16<128, false>), grid, dim3(256), 0, s, sa);
+      } else {
+        hipLaunchKernelGGL((k_score_bf16<64, false>), grid, dim3(256), 0, s, sa);
+      }
     } else {
       dim3 grid((unsigned)((sa.n_nodes + 3) / 4), (unsigned)n_caches);
       if (sa.D == 128)

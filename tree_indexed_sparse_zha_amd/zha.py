@@ -29,6 +29,7 @@ ZHA_OK, ZHA_ERR_NULL, ZHA_ERR_ARG, ZHA_ERR_UNSUPPORTED, ZHA_ERR_CAPACITY, ZHA_ER
 ZHA_F32, ZHA_BF16 = 0, 1
 ZHA_SINK, ZHA_LAST_CHUNK, ZHA_ALL_KEYS = 1, 2, 4
 ZHA_LEAF_MEAN, ZHA_LEAF_WEIGHTS = 0, 1
+ZHA_G_KV, ZHA_G_FP8 = 0, 2
 MAX_LEVELS = 8
 
 
@@ -49,6 +50,7 @@ class Config(ct.Structure):
         ("levels", ct.c_int32),
         ("kv_dtype", ct.c_int32),
         ("leaf_form", ct.c_int32),
+        ("g_dtype", ct.c_int32),
         ("capacity_tokens", ct.c_int64),
     ]
 
@@ -63,6 +65,7 @@ class TreeLayout(ct.Structure):
         ("c_offset", ct.c_int64 * MAX_LEVELS),
         ("g_bytes", ct.c_int64 * MAX_LEVELS),
         ("total_bytes", ct.c_int64),
+        ("s_offset", ct.c_int64 * MAX_LEVELS),
     ]
 
 
@@ -222,6 +225,7 @@ class ZhaConfig:
     dtype: str  # "f32" | "bf16"
     capacity: int
     leaf_form: str = "mean"  # "mean" | "weights"
+    g_dtype: str = "kv"  # "kv" (g in the KV dtype) | "fp8" (E4M3 with row scales)
 
     def c(self) -> Config:
         return Config(
@@ -234,6 +238,7 @@ class ZhaConfig:
             self.levels,
             ZHA_BF16 if self.dtype == "bf16" else ZHA_F32,
             ZHA_LEAF_WEIGHTS if self.leaf_form == "weights" else ZHA_LEAF_MEAN,
+            ZHA_G_FP8 if self.g_dtype == "fp8" else ZHA_G_KV,
             self.capacity,
         )
 
@@ -428,7 +433,9 @@ def dense_decode(cfg, Q, T, K, V, n_tokens, out, lse, ws, ev=None):
 def read_level(cfg: ZhaConfig, tree: torch.Tensor, level: int, n_nodes: Optional[int] = None) -> Dict[str, torch.Tensor]:
     """Level ``level`` (1 = chunks) as logical tensors on the tree's device.
 
-    Returns g [caches, n, R, d] (storage dtype), L and c [caches, n, R] fp32.
+    Returns g [caches, n, R, d] (storage dtype; fp8 levels: the decoded
+    values times their row scale, fp32, plus "scale" [caches, n, R]), L and c
+    [caches, n, R] fp32; level 1 in the weights form returns w instead of g.
     """
     tl = tree_layout(cfg)
     i = level - 1
@@ -444,6 +451,14 @@ def read_level(cfg: ZhaConfig, tree: torch.Tensor, level: int, n_nodes: Optional
         C = cfg.chunk
         w = tree[gb : gb + caches * cap * R * C * 4].view(torch.float32).view(caches, cap, R, C)[:, :n]
         return {"w": w, "L": L, "c": c}
+    sb = int(tl.s_offset[i])
+    if sb >= 0:
+        # E4M3 byte of (j, e) with step s = e // 32, k-group kg = (e % 32) // 8 at
+        # ((s // 2) * 4 * R + kg * R + j) * 16 + (s % 2) * 8 + e % 8
+        raw = tree[gb : gb + caches * cap * R * d].view(torch.float8_e4m3fn).view(caches, cap, -1)[:, :n]
+        vals = raw.float().reshape(caches, n, d // 64, 4, R, 2, 8).permute(0, 1, 4, 2, 5, 3, 6).reshape(caches, n, R, d)
+        scale = tree[sb : sb + caches * cap * R * 4].view(torch.float32).view(caches, cap, R)[:, :n]
+        return {"g": vals * scale.unsqueeze(-1), "scale": scale, "L": L, "c": c}
     graw = tree[gb : gb + caches * cap * R * d * cfg.esize].view(cfg.torch_dtype).view(caches, cap, -1)[:, :n]
     pieces = d // E
     # element offset ((k//4)*4*R + (k%4)*R + j)*E + e  ->  [k//4][k%4][j][e]
