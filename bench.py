@@ -76,7 +76,7 @@ def unpack_level(cfg, buf, lv, n_nodes):
     return zha.unpack_bits(buf.sel[off : off + nq * w].view(nq, w), n_nodes)
 
 
-def selection_bytes(cfg: zha.ZhaConfig, buf, n_tokens: int, T: int, logits: bool = False):
+def selection_bytes(cfg: zha.ZhaConfig, buf, n_tokens: int, T: int, logits: bool = False, top: int = 0):
     """Algorithmic bytes of one route + attend from the selection it made.
 
     route, per cache and level: |union over the cache's queries of the
@@ -99,9 +99,10 @@ def selection_bytes(cfg: zha.ZhaConfig, buf, n_tokens: int, T: int, logits: bool
         leaf_bytes += C * QW * 4
     per_level = {}
     kept_prev = None
-    for lv in range(Lv, 0, -1):
+    top = top or Lv  # routing starts here; the levels above are not read
+    for lv in range(top, 0, -1):
         n = sizes[lv - 1]
-        if lv == Lv:
+        if lv == top:
             cand = torch.ones(caches * QC, n, dtype=torch.bool, device="cuda")
         else:
             cand = kept_prev.repeat_interleave(C, dim=1)[:, :n]
@@ -185,6 +186,9 @@ def main():
     ap.add_argument("--tokens", type=int, default=None, help="override the context length (sweeps)")
     ap.add_argument("--leaf-form", default="weights", choices=["weights", "mean"],
                     help="level-1 storage: softmax weights scored from raw keys (default) or mean keys")
+    ap.add_argument("--p-levels", default=None,
+                    help="depth-aware schedule: comma-separated p per level, level 1 first (overrides --p)")
+    ap.add_argument("--top-level", type=int, default=0, help="level routing starts from (0 = the tree's top)")
     ap.add_argument("--g-dtype", default="kv", choices=["kv", "fp8"],
                     help="storage of the mean keys g: the KV dtype (default) or FP8 E4M3 with row scales")
     ap.add_argument("--no-logits", action="store_true",
@@ -207,6 +211,7 @@ def main():
     if args.tokens:
         w = w.with_tokens(args.tokens)
     p = args.p if args.p is not None else w.p[0]
+    p_levels = [float(x) for x in args.p_levels.split(",")] if args.p_levels else None
     T = w.queries_per_head
     A = w.append_tokens
     n_steps = args.warmup + args.steps
@@ -251,7 +256,11 @@ def main():
         n_old = N0 + s * A
         zha.append(cfg, K, ref, tree, n_old, A, ev=ev_app[s])
         n = n_old + A
-        zha.route(cfg, tree, n, Q, T, p, buf, ev=ev_route[s], K=K)
+        if p_levels is not None or args.top_level:
+            zha.route_levels(cfg, tree, n, Q, T, p_levels or [p] * cfg.levels, buf, top_level=args.top_level,
+                             ev=ev_route[s], K=K)
+        else:
+            zha.route(cfg, tree, n, Q, T, p, buf, ev=ev_route[s], K=K)
         zha.attend(cfg, Q, T, K, V, n, zha.level1_sel(buf), FLAGS, out, lse, ws, ev=ev_att[s], logits=buf.logits)
         return n
 
@@ -284,7 +293,7 @@ def main():
 
     # algorithmic bytes from the last step's selection
     per_level, attend_bytes, phi, phi_min, phi_max, ukeys = selection_bytes(
-        cfg, buf, n_final, T, logits=buf.logits is not None
+        cfg, buf, n_final, T, logits=buf.logits is not None, top=args.top_level
     )
     route_bytes = sum(v["alg_bytes"] for v in per_level.values())
     g8 = cfg.g_dtype == "fp8"
@@ -306,7 +315,8 @@ def main():
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(dom_bytes / (kmean[dom] / 1e3) / 1e9 / HBM_PEAK_GBS, 4) if dom_bytes else None,
-        "traffic": recorded_traffic(dom, w.name, cfg.leaf_form, p),
+        "traffic": recorded_traffic(dom, w.name, cfg.leaf_form, p)
+        if (p_levels is None and not args.top_level and cfg.g_dtype == "kv" and not args.tokens) else None,
         "alg_bytes_per_launch": dom_bytes,
         "avg_launch_ms": round(kmean[dom], 4),
     }
@@ -362,7 +372,8 @@ def main():
             "chunk": w.chunk,
             "levels": w.levels,
             "n_ref": w.n_ref,
-            "p": p,
+            "p": p_levels if p_levels is not None else p,
+            "top_level": args.top_level or w.levels,
             "append_tokens_per_step": A,
             "leaf_form": cfg.leaf_form,
             "g_dtype": cfg.g_dtype,

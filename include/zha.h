@@ -307,6 +307,27 @@ int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const v
               zha_profile* prof, void* stream);
 
 /*
+ * zha_route_levels - zha_route with a depth-aware schedule.
+ * Defines (MTP widget "5 . Caveats": top-p must scale with depth, a fixed
+ * per-level p shrinks the coverage of deeper trees; the pages' summary of
+ * the method: the tree depth can grow iteratively): the same routing, with
+ *   p_levels  host, cfg->levels floats; p_levels[l-1] is the fraction kept at
+ *             level l, each in (0, 1] (>= 1 keeps all; NaN or <= 0 is
+ *             ZHA_ERR_ARG);
+ *   top_level the level routing starts from: all its nodes are candidates
+ *             and the levels above it are neither read nor written (their
+ *             blocks of sel, score and stats keep their contents); 0 means
+ *             cfg->levels, otherwise 1..cfg->levels.
+ * Every other argument, output and error is as zha_route, which equals
+ * zha_route_levels with p at every level and top_level 0.
+ */
+int zha_route_levels(const zha_config* cfg, const void* tree, int64_t n_tokens, const void* Q,
+                     const int64_t q_strides[4], int32_t T, const float* p_levels, int32_t top_level,
+                     const void* K, const int64_t k_strides[3], uint32_t* sel, float* score,
+                     zha_select_stats* stats, float* logits, void* ws, int64_t ws_bytes,
+                     zha_profile* prof, void* stream);
+
+/*
  * zha_attend - exact softmax attention over the routed keys.
  * Defines (MTP widget step 5; "How does top-p routing pick tokens?"):
  *   A = keys of the level-1 chunks whose bit is set in sel1

@@ -354,15 +354,47 @@ class RouteLevel:
     sel: Selection
 
 
-def route(q: np.ndarray, tree: List[Level], ref: np.ndarray, chunk: int, p: float) -> List[RouteLevel]:
-    """Top-down routing of one query; returns records from the top level down."""
+def level_p(p, levels: int) -> List[float]:
+    """p per level (index l-1 for level l) from a scalar or a per-level sequence."""
+    if np.ndim(p) == 0:
+        return [float(p)] * levels
+    p = [float(x) for x in p]
+    if len(p) != levels:
+        raise ValueError("one p per level")
+    return p
+
+
+def depth_schedule(coverage: float, depth: int) -> List[float]:
+    """Per-level p whose product is ``coverage``: p_l = coverage ** (1 / depth).
+
+    MTP widget "5 . Caveats" ("Top-p must scale with depth"): with the same p
+    at every level the mass kept down to the leaves shrinks roughly like
+    p ** depth; spreading a target coverage over the routed levels keeps it
+    independent of the depth.
+    """
+    return [float(coverage) ** (1.0 / depth)] * depth
+
+
+def route(q: np.ndarray, tree: List[Level], ref: np.ndarray, chunk: int, p, top: Optional[int] = None) -> List[RouteLevel]:
+    """Top-down routing of one query; returns records from the start level down.
+
+    ``p`` is a scalar or one value per level (index l-1 for level l).  ``top``
+    (default: the tree's top level) is the level routing starts from: every
+    node of that level is a candidate and the levels above it are not used,
+    so the routing depth can follow the context length (MTP "depth can grow
+    iteratively").
+    """
     levels = len(tree)
-    cand = np.arange(tree[-1].L.shape[0], dtype=np.int64)
+    top = levels if top is None else top
+    if not 1 <= top <= levels:
+        raise ValueError("top must be in 1..levels")
+    pl = level_p(p, levels)
+    cand = np.arange(tree[top - 1].L.shape[0], dtype=np.int64)
     out: List[RouteLevel] = []
-    for lv in range(levels, 0, -1):
+    for lv in range(top, 0, -1):
         lvl = tree[lv - 1]
         s = plane_scores(q, lvl, ref, cand)
-        sel = top_p_select(cand, s, p)
+        sel = top_p_select(cand, s, pl[lv - 1])
         out.append(RouteLevel(lv, sel))
         if lv > 1:
             cand = children(sel.kept_ids, chunk, tree[lv - 2].L.shape[0])
@@ -403,9 +435,9 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, key_idx: np.ndarray):
     return (w @ v) / l, float(m + math.log(l))
 
 
-def route_and_attend(q, K, V, tree, ref, chunk, p, n_tokens, sink=True, last_chunk=True):
+def route_and_attend(q, K, V, tree, ref, chunk, p, n_tokens, sink=True, last_chunk=True, top=None):
     """Full decode path for one query: (o, lse, key set, route records)."""
-    recs = route(q, tree, ref, chunk, p)
+    recs = route(q, tree, ref, chunk, p, top)
     kept = recs[-1].sel.kept_ids
     idx = attend_set(kept, n_tokens, chunk, sink, last_chunk)
     o, lse = attend(q, K, V, idx)

@@ -54,17 +54,22 @@ class LevelReport:
 
 
 def check_route_teacher_forced(q, tree, ref, chunk, p, gpu_kept: Dict[int, np.ndarray], dtype, gpu_score=None,
-                               leaf_dtype=None):
+                               leaf_dtype=None, top=None):
     """Returns per-level reports; raises AssertionError on an unexplained difference.
 
     gpu_kept[level] = sorted kept node ids of the GPU; gpu_score[level] =
-    the GPU's score row for that level (or None).
+    the GPU's score row for that level (or None).  p is a scalar or one
+    value per level (index l-1 for level l); routing starts at ``top``
+    (default: the top level).
     """
     levels = len(tree)
+    top = levels if top is None else top
+    pl = O.level_p(p, levels)
     reports: List[LevelReport] = []
-    for lv in range(levels, 0, -1):
+    for lv in range(top, 0, -1):
+        p = pl[lv - 1]
         n_lv = tree[lv - 1].L.shape[0]
-        if lv == levels:
+        if lv == top:
             cand = np.arange(n_lv, dtype=np.int64)
         else:
             cand = O.children(gpu_kept[lv + 1], chunk, n_lv)

@@ -144,6 +144,29 @@ def _call_route(lib, cfg, **over):
                          a["score"], a["stats"], a.get("logits"), a["ws"], a["ws_bytes"], a.get("prof"), None)
 
 
+def _call_route_levels(lib, cfg, pl, top=0, **over):
+    a = dict(tree=16, n_tokens=32768, Q=16, qs=zha._i64(1 << 20, 1 << 16, 1 << 12, 128), T=1,
+             K=None, ks=None, sel=16, score=16, stats=16, ws=16, ws_bytes=1 << 30)
+    a.update(over)
+    c = cfg.c()
+    arr = None if pl is None else (ct.c_float * len(pl))(*pl)
+    return lib.zha_route_levels(ct.byref(c), a["tree"], a["n_tokens"], a["Q"], a["qs"], a["T"], arr, top, a["K"],
+                                a["ks"], a["sel"], a["score"], a["stats"], None, a["ws"], a["ws_bytes"], None, None)
+
+
+def test_route_levels_argument_errors(lib):
+    cfg = cfg_deep()
+    assert _call_route_levels(lib, cfg, None) == zha.ZHA_ERR_NULL
+    assert b"p_levels" in lib.zha_last_error()
+    assert _call_route_levels(lib, cfg, [0.9] * 5 + [0.0]) == zha.ZHA_ERR_ARG
+    assert b"level 6" in lib.zha_last_error()
+    assert _call_route_levels(lib, cfg, [float("nan")] + [0.9] * 5) == zha.ZHA_ERR_ARG
+    assert _call_route_levels(lib, cfg, [0.9] * 6, top=7) == zha.ZHA_ERR_ARG
+    assert _call_route_levels(lib, cfg, [0.9] * 6, top=-1) == zha.ZHA_ERR_ARG
+    # valid schedules pass validation and reach the capacity check
+    assert _call_route_levels(lib, cfg, [0.9] * 6, top=3, n_tokens=32769) == zha.ZHA_ERR_CAPACITY
+
+
 def test_route_argument_errors(lib):
     cfg = cfg_deep()
     # fake but aligned addresses: every case fails validation before any HIP call

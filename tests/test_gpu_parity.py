@@ -499,6 +499,44 @@ def test_p1_is_dense():
         np.testing.assert_allclose(dense[t].cpu().numpy(), o, atol=1e-5, rtol=0)
 
 
+def test_route_levels_schedule_and_start_level():
+    """zha_route_levels: a depth-aware schedule and a lower start level,
+    teacher-forced against the oracle; keep-all at the top equals starting
+    one level lower, bit for bit."""
+    w = W.WORKLOADS["deep32k"]
+    cfg = cfg_of(w, leaf_form="weights")
+    batch = W.make_batch(w, device="cuda")
+    N, T, L = w.n_tokens, w.queries_per_head, w.levels
+    _say("route_levels deep32k")
+    tree = zha.alloc_tree(cfg)
+    zha.build(cfg, batch.K, batch.ref, tree, N)
+    QC = cfg.q_per_kv * T
+    cache = cfg.n_caches - 1
+    b, h = divmod(cache, cfg.n_kv_heads)
+    Kn, rn = np64(batch.K[b, h, :N]), np64(batch.ref[h])
+    to = O.build_tree(Kn, rn, cfg.chunk, L, cfg.dtype, keep_g=False, leaf_dtype="f64")
+    sched = O.depth_schedule(0.8, L)
+    for pl, top in ((sched, 0), ([0.9, 0.95, 0.97, 0.99, 1.0, 1.0], 4), ([0.5] * L, 1)):
+        buf = zha.alloc_route(cfg, T)
+        zha.route_levels(cfg, tree, N, batch.Q, T, pl, buf, top_level=top, K=batch.K)
+        torch.cuda.synchronize()
+        for ql in (0, QC // 2, QC - 1):
+            bits, scores = gpu_levels(cfg, buf, N, cache * QC + ql)
+            t = top or L
+            kept = PAR.gpu_kept_from_bits({lv: bits[lv] for lv in range(1, t + 1)})
+            q = np64(batch.Q[b, h, ql // T, ql % T])
+            PAR.check_route_teacher_forced(q, to, rn, cfg.chunk, pl, kept, cfg.dtype,
+                                           {lv: scores[lv] for lv in range(1, t + 1)}, leaf_dtype="f64", top=t)
+    a, c = zha.alloc_route(cfg, T), zha.alloc_route(cfg, T)
+    zha.route_levels(cfg, tree, N, batch.Q, T, [0.9] * (L - 1) + [1.0], a, K=batch.K)
+    zha.route_levels(cfg, tree, N, batch.Q, T, [0.9] * L, c, top_level=L - 1, K=batch.K)
+    torch.cuda.synchronize()
+    rl = a.layout
+    for lv in range(1, L):
+        o, n = int(rl.sel_offset[lv - 1]), int(rl.words[lv - 1]) * int(rl.n_queries)
+        assert torch.equal(a.sel[o : o + n], c.sel[o : o + n]), f"level {lv}"
+
+
 @pytest.mark.parametrize("leaf_form", ["mean", "weights"])
 def test_route_is_deterministic(leaf_form):
     w = W.WORKLOADS["deep32k"]

@@ -275,6 +275,37 @@ def test_bf16_rounding_single_rounding_from_fp64():
     assert O.round_bf16(np.array([3.0 * 2.0**-8 + 1.0]))[0] == 1.0 + 2.0**-6
 
 
+def test_per_level_p_and_start_level():
+    """Depth-aware routing: p per level (index l-1 for level l) and a start
+    level.  Keeping everything at the top makes every node one level down a
+    candidate, which is routing from that level; a small p at the top only,
+    with 1 below, keeps exactly the descendants of the kept top nodes."""
+    K, V, ref, Q = _rand_cache(1024, 16, 4, 21)
+    C, L = 4, 4
+    tree = O.build_tree(K, ref, C, L, "f64")
+    for q in Q:
+        a = O.route(q, tree, ref, C, [0.9] * (L - 1) + [1.0])
+        b = O.route(q, tree, ref, C, 0.9, top=L - 1)
+        assert len(b) == L - 1
+        for ra, rb in zip(a[1:], b):
+            assert ra.level == rb.level
+            np.testing.assert_array_equal(ra.sel.kept_ids, rb.sel.kept_ids)
+        c = O.route(q, tree, ref, C, [1.0] * (L - 1) + [0.3])
+        top_kept = c[0].sel.kept_ids
+        assert 0 < top_kept.size < tree[-1].L.shape[0]
+        desc = top_kept
+        for lv in range(L - 1, 0, -1):
+            desc = O.children(desc, C, tree[lv - 1].L.shape[0])
+        np.testing.assert_array_equal(c[-1].sel.kept_ids, desc)
+        # a scalar p is the same p at every level
+        d1 = O.route(q, tree, ref, C, 0.8)
+        d2 = O.route(q, tree, ref, C, [0.8] * L)
+        for x, y in zip(d1, d2):
+            np.testing.assert_array_equal(x.sel.kept_ids, y.sel.kept_ids)
+    sched = O.depth_schedule(0.9, 6)
+    assert len(sched) == 6 and abs(np.prod(sched) - 0.9) < 1e-12
+
+
 def _e4m3_table():
     """All finite E4M3 values by code, from the bit layout alone: sign, 4
     exponent bits (bias 7), 3 mantissa bits; exponent 0 is subnormal; code

@@ -320,11 +320,10 @@ int zha_append(const zha_config* cfg, const void* K, const int64_t k_strides[3],
   return do_build(cfg, K, k_strides, n_old, n_new, ref, tree, prof, stream, true);
 }
 
-int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const void* Q,
-              const int64_t q_strides[4], int32_t T, float p, const void* K,
-              const int64_t k_strides[3], uint32_t* sel, float* score,
-              zha_select_stats* stats, float* logits, void* ws, int64_t ws_bytes,
-              zha_profile* prof, void* stream) {
+static int do_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const void* Q,
+                    const int64_t q_strides[4], int32_t T, const float* pl, int32_t top_level, const void* K,
+                    const int64_t k_strides[3], uint32_t* sel, float* score, zha_select_stats* stats,
+                    float* logits, void* ws, int64_t ws_bytes, zha_profile* prof, void* stream) {
   int rc = check_config(cfg);
   if (rc) return rc;
   if ((rc = check_prof(prof))) return rc;
@@ -344,7 +343,12 @@ int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const v
   if ((rc = check_ptr16(sel, "sel"))) return rc;
   if ((rc = check_ptr16(score, "score"))) return rc;
   if ((rc = check_ptr16(stats, "stats"))) return rc;
-  if (!(p > 0.0f) || std::isnan(p)) return fail(ZHA_ERR_ARG, "p must be in (0, 1]");
+  if (!pl) return fail(ZHA_ERR_NULL, "p_levels is NULL");
+  for (int l = 0; l < cfg->levels; ++l)
+    if (!(pl[l] > 0.0f) || std::isnan(pl[l])) return fail(ZHA_ERR_ARG, "p of level %d must be in (0, 1]", l + 1);
+  if (top_level < 0 || top_level > cfg->levels)
+    return fail(ZHA_ERR_ARG, "top_level %d outside 0..%d", top_level, cfg->levels);
+  const int top = top_level == 0 ? cfg->levels : top_level;
   if (n_tokens < 0) return fail(ZHA_ERR_ARG, "n_tokens must be >= 0");
   if (n_tokens > cfg->capacity_tokens) return fail(ZHA_ERR_CAPACITY, "n_tokens exceeds capacity");
   zha_route_layout rl;
@@ -367,7 +371,7 @@ int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const v
     hipError_t e = zha::launch_route_init(keyrange, kr_bytes / 16, pr);
     if (e != hipSuccess) return hip_fail(e, "route init launch");
   }
-  for (int l = cfg->levels - 1; l >= 0; --l) {
+  for (int l = top - 1; l >= 0; --l) {
     zha::ScoreArgs sa;
     std::memset(&sa, 0, sizeof(sa));
     sa.g = static_cast<const char*>(tree) + tl.g_offset[l];
@@ -389,8 +393,8 @@ int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const v
     sa.qsh = q_strides[1];
     sa.qsg = q_strides[2];
     sa.qst = q_strides[3];
-    sa.sel_parent = (l == cfg->levels - 1) ? nullptr : sel + rl.sel_offset[l + 1];
-    sa.parent_words = (l == cfg->levels - 1) ? 0 : rl.words[l + 1];
+    sa.sel_parent = (l == top - 1) ? nullptr : sel + rl.sel_offset[l + 1];
+    sa.parent_words = (l == top - 1) ? 0 : rl.words[l + 1];
     sa.score = score + rl.score_offset[l];
     sa.score_stride = rl.score_stride[l];
     sa.keyrange = keyrange + kr_off[l];
@@ -416,12 +420,32 @@ int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const v
     se.sel = sel + rl.sel_offset[l];
     se.words = rl.words[l];
     se.stats = stats + rl.stats_offset[l];
-    se.p = p;
-    se.keep_all = p >= 1.0f;
+    se.p = pl[l];
+    se.keep_all = pl[l] >= 1.0f;
     hipError_t e = zha::launch_route_level(sa, se, cfg->kv_dtype, caches, l + 1, pr);
     if (e != hipSuccess) return hip_fail(e, "route launch");
   }
   return ZHA_OK;
+}
+
+int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const void* Q,
+              const int64_t q_strides[4], int32_t T, float p, const void* K,
+              const int64_t k_strides[3], uint32_t* sel, float* score,
+              zha_select_stats* stats, float* logits, void* ws, int64_t ws_bytes,
+              zha_profile* prof, void* stream) {
+  float pl[ZHA_MAX_LEVELS];
+  for (int l = 0; l < ZHA_MAX_LEVELS; ++l) pl[l] = p;
+  return do_route(cfg, tree, n_tokens, Q, q_strides, T, pl, 0, K, k_strides, sel, score, stats, logits, ws,
+                  ws_bytes, prof, stream);
+}
+
+int zha_route_levels(const zha_config* cfg, const void* tree, int64_t n_tokens, const void* Q,
+                     const int64_t q_strides[4], int32_t T, const float* p_levels, int32_t top_level,
+                     const void* K, const int64_t k_strides[3], uint32_t* sel, float* score,
+                     zha_select_stats* stats, float* logits, void* ws, int64_t ws_bytes,
+                     zha_profile* prof, void* stream) {
+  return do_route(cfg, tree, n_tokens, Q, q_strides, T, p_levels, top_level, K, k_strides, sel, score, stats,
+                  logits, ws, ws_bytes, prof, stream);
 }
 
 int zha_attend(const zha_config* cfg, const void* Q, const int64_t q_strides[4], int32_t T,

@@ -177,6 +177,7 @@ def load(path: str = LIB_PATH) -> ct.CDLL:
         "zha_build": (ct.c_int, [cfgp, P, i64p, I64, P, P, P, P]),
         "zha_append": (ct.c_int, [cfgp, P, i64p, I64, I64, P, P, P, P]),
         "zha_route": (ct.c_int, [cfgp, P, I64, P, i64p, I32, F, P, i64p, P, P, P, P, P, I64, P, P]),
+        "zha_route_levels": (ct.c_int, [cfgp, P, I64, P, i64p, I32, ct.POINTER(F), I32, P, i64p, P, P, P, P, P, I64, P, P]),
         "zha_attend": (ct.c_int, [cfgp, P, i64p, I32, P, P, i64p, I64, P, I64, P, ct.c_uint32, P, P, P, I64, P, P]),
         "zha_dense_decode": (ct.c_int, [cfgp, P, i64p, I32, P, P, i64p, I64, P, P, P, I64, P, P]),
     }
@@ -357,6 +358,23 @@ def route(cfg: ZhaConfig, tree: torch.Tensor, n_tokens: int, Q: torch.Tensor, T:
             int(buf.ws.numel()),
             _prof(ev),
             _stream(Q),
+        )
+    )
+
+
+def route_levels(cfg: ZhaConfig, tree: torch.Tensor, n_tokens: int, Q: torch.Tensor, T: int, p_levels,
+                 buf: RouteBuffers, top_level: int = 0, ev=None, K: Optional[torch.Tensor] = None):
+    """zha_route_levels: p_levels[l-1] is the fraction kept at level l;
+    routing starts at top_level (0 = the tree's top)."""
+    c = cfg.c()
+    qs = _i64(*_elem_strides(Q, 4))
+    ks = _i64(*_elem_strides(K, 3)) if K is not None else None
+    pl = (ct.c_float * max(1, len(p_levels)))(*[float(x) for x in p_levels])
+    _check(
+        load().zha_route_levels(
+            ct.byref(c), _ptr(tree), int(n_tokens), _ptr(Q), qs, int(T), pl, int(top_level), _ptr(K), ks,
+            _ptr(buf.sel), _ptr(buf.score), _ptr(buf.stats), _ptr(buf.logits), _ptr(buf.ws), int(buf.ws.numel()),
+            _prof(ev), _stream(Q),
         )
     )
 
