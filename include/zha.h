@@ -89,7 +89,10 @@ enum zha_g_dtype { ZHA_G_KV = 0, ZHA_G_FP8 = 2 };
 enum zha_attend_flags {
   ZHA_SINK = 1,       /* token 0 is always attended (MTP "How does top-p routing pick tokens?") */
   ZHA_LAST_CHUNK = 2, /* tokens [C*floor((N-1)/C), N) are always attended (MTP widget step 5) */
-  ZHA_ALL_KEYS = 4    /* ignore the selection: dense attention over all N keys */
+  ZHA_ALL_KEYS = 4,   /* ignore the selection: dense attention over all N keys */
+  ZHA_CAUSAL = 8      /* prefill block: query t of each head sits at position
+                         N - T + t and sees keys [0, N - T + t] only; the current
+                         chunk and the sink are taken relative to it (bf16) */
 };
 
 /*
@@ -305,6 +308,47 @@ int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const v
               const int64_t k_strides[3], uint32_t* sel, float* score,
               zha_select_stats* stats, float* logits, void* ws, int64_t ws_bytes,
               zha_profile* prof, void* stream);
+
+/*
+ * Chunked prefill (causal).  A block of T consecutive positions
+ * [N - T, N) of every sequence is processed at once: query t of a head sits
+ * at position N - T + t and decodes against the tree of its own prefix of
+ * N - T + t + 1 tokens (the pages' sub-quadratic claim is about this
+ * regime, MTP TL;DR).  Complete nodes of that prefix tree are nodes of the
+ * tree built over N tokens; the one node per level >= 2 that straddles the
+ * query's position is partial and merges the children that exist (R11).
+ * zha_build_spine stores those partial nodes for every prefix state of the
+ * block; zha_route_prefill routes each query on its prefix tree; zha_attend
+ * with ZHA_CAUSAL attends each query over its own keys.  bf16 keys only.
+ */
+/* Bytes of the spine buffer for blocks of up to T positions (-1 on bad cfg/T). */
+int64_t zha_spine_bytes(const zha_config* cfg, int32_t T);
+
+/*
+ * zha_build_spine - the partial nodes of the prefix trees of a block.
+ *   K, k_strides, ref   as zha_build; keys [0, n_tokens) are read.
+ *   n_tokens, T         the block is positions [n_tokens - T, n_tokens).
+ *   spine               device, zha_spine_bytes(cfg, T) bytes (output):
+ *                       for each state k (complete chunks of a prefix) and
+ *                       level >= 2 whose node holding chunk k-1 is partial,
+ *                       that node (g in the tree's storage and layout, L, c,
+ *                       scale).
+ * Errors: as zha_build, plus T outside [1, n_tokens], kv_dtype not bf16.
+ */
+int zha_build_spine(const zha_config* cfg, const void* K, const int64_t k_strides[3], int64_t n_tokens,
+                    int32_t T, const float* ref, void* spine, zha_profile* prof, void* stream);
+
+/*
+ * zha_route_prefill - zha_route for a prefill block: query t of each head
+ * routes on the tree of its prefix of n_tokens - T + t + 1 tokens (complete
+ * nodes from tree, built over n_tokens; the partial ones from spine, built
+ * by zha_build_spine for the same n_tokens and T).  Score rows hold -inf
+ * beyond each query's prefix; outputs, workspace and errors as zha_route.
+ */
+int zha_route_prefill(const zha_config* cfg, const void* tree, const void* spine, int64_t n_tokens,
+                      const void* Q, const int64_t q_strides[4], int32_t T, float p, const void* K,
+                      const int64_t k_strides[3], uint32_t* sel, float* score, zha_select_stats* stats,
+                      float* logits, void* ws, int64_t ws_bytes, zha_profile* prof, void* stream);
 
 /*
  * zha_route_levels - zha_route with a depth-aware schedule.

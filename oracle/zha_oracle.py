@@ -442,3 +442,31 @@ def route_and_attend(q, K, V, tree, ref, chunk, p, n_tokens, sink=True, last_chu
     idx = attend_set(kept, n_tokens, chunk, sink, last_chunk)
     o, lse = attend(q, K, V, idx)
     return o, lse, idx, recs
+
+
+# ---------------------------------------------------------------------------
+# chunked prefill (causal)
+
+
+def prefill_query(q, K, V, ref, chunk, levels, p, position, g_dtype="f64", leaf_dtype=None,
+                  sink=True, last_chunk=True, top=None):
+    """One prefill query at ``position`` t, causal: it sees tokens [0, t].
+
+    The plain reading of routing under a causal limit (the pages' claim of
+    sub-quadratic cost is about this regime, MTP TL;DR): the query decodes
+    against the tree of its own prefix of t + 1 tokens.  Complete nodes of
+    that tree are those of any longer tree (a node is a function of its key
+    range); a node straddling t is partial and merges the children that
+    exist, as the trailing node of any tree does.  Returns
+    (o, lse, key set, route records, tree).
+    """
+    n = position + 1
+    tree = build_tree(np.asarray(K[:n]), ref, chunk, levels, g_dtype, n_tokens=n, keep_g=False,
+                      leaf_dtype=leaf_dtype)
+    if level_sizes(n, chunk, levels)[0] == 0:
+        idx = attend_set(np.zeros(0, np.int64), n, chunk, sink, last_chunk)
+        o, lse = attend(q, K, V, idx)
+        return o, lse, idx, [], tree
+    o, lse, idx, recs = route_and_attend(q, np.asarray(K[:n]), np.asarray(V[:n]), tree, ref, chunk, p, n,
+                                         sink, last_chunk, top)
+    return o, lse, idx, recs, tree

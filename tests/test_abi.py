@@ -167,6 +167,29 @@ def test_route_levels_argument_errors(lib):
     assert _call_route_levels(lib, cfg, [0.9] * 6, top=3, n_tokens=32769) == zha.ZHA_ERR_CAPACITY
 
 
+def test_prefill_argument_errors(lib):
+    cfg = cfg_deep()
+    c = cfg.c()
+    assert zha.spine_bytes(cfg, 64) > 0
+    # a spine record per (state, level >= 2): states = T / C + 2
+    rec = (16 * 128 * 2 + 12 * 16 + 15) // 16 * 16
+    assert zha.spine_bytes(cfg, 64) >= 8 * (64 // 4 + 2) * 5 * rec
+    ks = zha._i64(1 << 22, 1 << 19, 128)
+    # T beyond n_tokens, NULL spine, f32 keys
+    assert lib.zha_build_spine(ct.byref(c), 16, ks, 100, 200, 16, 16, None, None) == zha.ZHA_ERR_ARG
+    assert lib.zha_build_spine(ct.byref(c), 16, ks, 1000, 64, 16, None, None, None) == zha.ZHA_ERR_NULL
+    cf = cfg_deep(dtype="f32", head_dim=64, n_ref=4, chunk=4, levels=3).c()
+    assert lib.zha_build_spine(ct.byref(cf), 16, zha._i64(1 << 20, 1 << 16, 64), 1000, 64, 16, 16, None,
+                               None) == zha.ZHA_ERR_UNSUPPORTED
+    qs = zha._i64(1 << 20, 1 << 16, 1 << 12, 128)
+    args = (16, 16, 1000, 16, qs, 64, 0.9, None, None, 16, 16, 16, None, 16, 1 << 30, None, None)
+    # missing spine with an upper level is an error before any launch
+    bad = (16, None) + args[2:]
+    assert lib.zha_route_prefill(ct.byref(c), *bad) == zha.ZHA_ERR_NULL
+    big = (16, 16, 40) + args[3:]  # T = 64 > n_tokens = 40
+    assert lib.zha_route_prefill(ct.byref(c), *big) == zha.ZHA_ERR_ARG
+
+
 def test_route_argument_errors(lib):
     cfg = cfg_deep()
     # fake but aligned addresses: every case fails validation before any HIP call
@@ -230,7 +253,8 @@ def test_attend_argument_errors(lib):
     assert call(wsb=ws - 1) == zha.ZHA_ERR_CAPACITY
     assert call(n=0) == zha.ZHA_ERR_ARG
     assert call(n=40000) == zha.ZHA_ERR_CAPACITY
-    assert call(flags=8) == zha.ZHA_ERR_ARG
+    assert call(flags=16) == zha.ZHA_ERR_ARG
+    assert call(flags=8 | 3, T=2, n=1) == zha.ZHA_ERR_ARG  # causal block longer than the context
     assert call(V=24) == zha.ZHA_ERR_ALIGN
     assert call(out=None) == zha.ZHA_ERR_NULL
     assert call(logits=16) == zha.ZHA_ERR_ARG  # logits need the weights form

@@ -306,6 +306,33 @@ def test_per_level_p_and_start_level():
     assert len(sched) == 6 and abs(np.prod(sched) - 0.9) < 1e-12
 
 
+def test_prefill_is_decode_of_the_prefix():
+    """Chunked prefill, causal: the query at position t routes on the tree of
+    tokens [0, t] and never attends a later key; at the last position it is
+    the decode query; the tree's straddling (partial) nodes are the direct
+    statistics of the keys they hold; complete nodes equal the full tree's."""
+    K, V, ref, Q = _rand_cache(700, 16, 3, 31)
+    C, L, p = 4, 3, 0.9
+    full = O.build_tree(K, ref, C, L, "f64", n_tokens=700)
+    for t in (0, 2, 3, 4, 63, 64, 65, 130, 255, 256, 450, 699):
+        q = Q[t % len(Q)]
+        o, lse, idx, recs, tree = O.prefill_query(q, K, V, ref, C, L, p, t)
+        assert idx.max() <= t and 0 in idx and t in idx
+        if t == 699:
+            o2, l2, idx2, _ = O.route_and_attend(q, K, V, full, ref, C, p, 700)
+            np.testing.assert_array_equal(idx, idx2)
+        sizes = O.level_sizes(t + 1, C, L)
+        for lv in range(1, L + 1):
+            n = sizes[lv - 1]
+            for m in range(n):
+                a, b = O.node_token_range(lv, m, C, t + 1)
+                Lx, gx = O.node_stats_direct(K, ref, a, b)
+                np.testing.assert_allclose(tree[lv - 1].L[m], Lx, rtol=0, atol=1e-12)
+                complete = b - a == C**lv
+                if complete:
+                    np.testing.assert_allclose(tree[lv - 1].L[m], full[lv - 1].L[m], rtol=0, atol=1e-12)
+
+
 def _e4m3_table():
     """All finite E4M3 values by code, from the bit layout alone: sign, 4
     exponent bits (bias 7), 3 mantissa bits; exponent 0 is subnormal; code

@@ -320,10 +320,20 @@ int zha_append(const zha_config* cfg, const void* K, const int64_t k_strides[3],
   return do_build(cfg, K, k_strides, n_old, n_new, ref, tree, prof, stream, true);
 }
 
+// Prefill spine geometry for blocks of up to T query positions: snapshot
+// states k (complete chunks of a query's prefix) per cache, and bytes per
+// record (one node: g block, then L, c and scale, R fp32 each).
+static int64_t spine_states(const zha_config* c, int32_t T) { return (int64_t)T / c->chunk + 2; }
+static int64_t spine_rec_bytes(const zha_config* c) {
+  const int64_t g = (int64_t)c->n_ref * c->head_dim * (c->g_dtype == ZHA_G_FP8 ? 1 : esize(c->kv_dtype));
+  return (g + 12 * c->n_ref + 15) / 16 * 16;
+}
+
 static int do_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const void* Q,
                     const int64_t q_strides[4], int32_t T, const float* pl, int32_t top_level, const void* K,
                     const int64_t k_strides[3], uint32_t* sel, float* score, zha_select_stats* stats,
-                    float* logits, void* ws, int64_t ws_bytes, zha_profile* prof, void* stream) {
+                    float* logits, void* ws, int64_t ws_bytes, zha_profile* prof, void* stream,
+                    bool prefill = false, const void* spine = nullptr) {
   int rc = check_config(cfg);
   if (rc) return rc;
   if ((rc = check_prof(prof))) return rc;
@@ -351,6 +361,11 @@ static int do_route(const zha_config* cfg, const void* tree, int64_t n_tokens, c
   const int top = top_level == 0 ? cfg->levels : top_level;
   if (n_tokens < 0) return fail(ZHA_ERR_ARG, "n_tokens must be >= 0");
   if (n_tokens > cfg->capacity_tokens) return fail(ZHA_ERR_CAPACITY, "n_tokens exceeds capacity");
+  if (prefill) {
+    if (cfg->levels >= 2 && (rc = check_ptr16(spine, "spine"))) return rc;
+    if (cfg->kv_dtype != ZHA_BF16) return fail(ZHA_ERR_UNSUPPORTED, "prefill routing needs bf16 keys");
+    if (T > n_tokens) return fail(ZHA_ERR_ARG, "T = %d positions exceed n_tokens", T);
+  }
   zha_route_layout rl;
   zha_get_route_layout(cfg, T, &rl);
   if ((rc = check_ptr16(ws, "ws"))) return rc;
@@ -400,6 +415,19 @@ static int do_route(const zha_config* cfg, const void* tree, int64_t n_tokens, c
     sa.keyrange = keyrange + kr_off[l];
     sa.kr_slots = zha::route_kr_slots(cfg->kv_dtype, leafw && l == 0, tl.node_cap[l], cfg->chunk);
     sa.inv_sqrt_d = isd;
+    sa.causal_n0 = prefill ? n_tokens - T : -1;
+    sa.lvl_chunks = 1;
+    for (int i = 0; i < l; ++i) sa.lvl_chunks *= cfg->chunk;
+    sa.levels = cfg->levels;
+    sa.level = l + 1;
+    sa.top = top;
+    sa.n_queries = rl.n_queries;
+    if (prefill && spine) {
+      sa.spine = static_cast<const char*>(spine);
+      sa.spine_k0 = (n_tokens - T + 1) / cfg->chunk;
+      sa.spine_states = spine_states(cfg, T);
+      sa.spine_rec = spine_rec_bytes(cfg);
+    }
     sa.leaf_weights = leafw && l == 0;
     if (sa.leaf_weights) {
       sa.K = K;
@@ -439,6 +467,68 @@ int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const v
                   ws_bytes, prof, stream);
 }
 
+int64_t zha_spine_bytes(const zha_config* cfg, int32_t T) {
+  if (check_config(cfg) || check_T(cfg, T)) return -1;
+  if (cfg->levels < 2) return 256;
+  return align256((int64_t)cfg->batch * cfg->n_kv_heads * spine_states(cfg, T) * (cfg->levels - 1) *
+                  spine_rec_bytes(cfg));
+}
+
+int zha_build_spine(const zha_config* cfg, const void* K, const int64_t k_strides[3], int64_t n_tokens,
+                    int32_t T, const float* ref, void* spine, zha_profile* prof, void* stream) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if ((rc = check_T(cfg, T))) return rc;
+  if ((rc = check_prof(prof))) return rc;
+  if (prof) prof->n_used = 0;
+  if (cfg->kv_dtype != ZHA_BF16) return fail(ZHA_ERR_UNSUPPORTED, "prefill needs bf16 keys");
+  if ((rc = check_ptr16(K, "K"))) return rc;
+  if ((rc = check_strides(k_strides, 3, esize(cfg->kv_dtype), "k_strides"))) return rc;
+  if ((rc = check_ptr16(ref, "ref"))) return rc;
+  if ((rc = check_ptr16(spine, "spine"))) return rc;
+  if (n_tokens < T || n_tokens < 1) return fail(ZHA_ERR_ARG, "need 1 <= T <= n_tokens");
+  if (n_tokens > cfg->capacity_tokens) return fail(ZHA_ERR_CAPACITY, "n_tokens exceeds capacity");
+  if (cfg->levels < 2) return ZHA_OK;  // no node above the chunks: no spine
+  zha_tree_layout tl;
+  fill_tree_layout(cfg, &tl);
+  zha::BuildArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.K = K;
+  a.sb = k_strides[0];
+  a.sh = k_strides[1];
+  a.st = k_strides[2];
+  a.ref = ref;
+  a.tree = nullptr;
+  fill_geom(cfg, tl, &a.geo);
+  a.n_tokens = n_tokens;
+  a.span_tokens = a.geo.span_len[cfg->levels];
+  a.inv_sqrt_d = 1.0f / std::sqrt((float)cfg->head_dim);
+  a.spine = static_cast<char*>(spine);
+  a.spine_k0 = (n_tokens - T + 1) / cfg->chunk;
+  a.spine_states = spine_states(cfg, T);
+  a.spine_rec = spine_rec_bytes(cfg);
+  // states k0 .. k_end (complete chunks of n_tokens): the spans holding chunks k0-1 .. k_end-1
+  const int64_t k_end = n_tokens / cfg->chunk;
+  if (k_end < 1 || k_end < a.spine_k0) return ZHA_OK;
+  const int64_t c_first = a.spine_k0 > 0 ? a.spine_k0 - 1 : 0;
+  a.first_span = c_first * cfg->chunk / a.span_tokens;
+  a.n_spans = (k_end - 1) * cfg->chunk / a.span_tokens - a.first_span + 1;
+  zha::Prof pr{prof, static_cast<hipStream_t>(stream)};
+  hipError_t e = zha::launch_build(a, cfg->kv_dtype, pr);
+  if (e != hipSuccess) return hip_fail(e, "spine launch");
+  return ZHA_OK;
+}
+
+int zha_route_prefill(const zha_config* cfg, const void* tree, const void* spine, int64_t n_tokens,
+                      const void* Q, const int64_t q_strides[4], int32_t T, float p, const void* K,
+                      const int64_t k_strides[3], uint32_t* sel, float* score, zha_select_stats* stats,
+                      float* logits, void* ws, int64_t ws_bytes, zha_profile* prof, void* stream) {
+  float pl[ZHA_MAX_LEVELS];
+  for (int l = 0; l < ZHA_MAX_LEVELS; ++l) pl[l] = p;
+  return do_route(cfg, tree, n_tokens, Q, q_strides, T, pl, 0, K, k_strides, sel, score, stats, logits, ws,
+                  ws_bytes, prof, stream, true, spine);
+}
+
 int zha_route_levels(const zha_config* cfg, const void* tree, int64_t n_tokens, const void* Q,
                      const int64_t q_strides[4], int32_t T, const float* p_levels, int32_t top_level,
                      const void* K, const int64_t k_strides[3], uint32_t* sel, float* score,
@@ -465,8 +555,12 @@ int zha_attend(const zha_config* cfg, const void* Q, const int64_t q_strides[4],
   if ((rc = check_strides(kv_strides, 3, es, "kv_strides"))) return rc;
   if ((rc = check_ptr16(out, "out"))) return rc;
   if ((rc = check_ptr16(ws, "ws"))) return rc;
-  if (flags & ~7u) return fail(ZHA_ERR_ARG, "unknown flags 0x%x", flags);
+  if (flags & ~15u) return fail(ZHA_ERR_ARG, "unknown flags 0x%x", flags);
   if (n_tokens < 1) return fail(ZHA_ERR_ARG, "n_tokens must be >= 1");
+  if (flags & ZHA_CAUSAL) {
+    if (cfg->kv_dtype != ZHA_BF16) return fail(ZHA_ERR_UNSUPPORTED, "causal attention needs bf16 keys");
+    if (T > n_tokens) return fail(ZHA_ERR_ARG, "T = %d positions exceed n_tokens", T);
+  }
   if (n_tokens > cfg->capacity_tokens) return fail(ZHA_ERR_CAPACITY, "n_tokens exceeds capacity");
   const int64_t n_chunks = n_tokens / cfg->chunk;
   if (logits) {
@@ -507,6 +601,7 @@ int zha_attend(const zha_config* cfg, const void* Q, const int64_t q_strides[4],
   a.tile_keys = attend_tile_keys(cfg, T);
   a.n_tiles = cdiv(n_tokens, a.tile_keys);
   a.partial = static_cast<float*>(ws);
+  a.causal_n0 = (flags & ZHA_CAUSAL) ? n_tokens - T : -1;
   a.logits = logits;
   if (logits) {
     zha_tree_layout tl;

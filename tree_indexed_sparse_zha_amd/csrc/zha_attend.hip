@@ -230,6 +230,12 @@ __device__ __forceinline__ void quad_masks(const AttendArgs& A, int cache, int q
   for (int u = 0; u < QG; ++u) wq[u] = (rd && u < nq) ? wp[(int64_t)u * A.sel_words] : 0u;
   const int sh = (int)(c0 & 31);
   const uint32_t qall = (1u << nq) - 1u;  // nq <= 16
+  // prefill (causal): query u sits at position pos[u], sees keys <= pos[u]
+  // and its own current chunk [C floor(pos[u] / C), pos[u]]
+  const bool causal = A.causal_n0 >= 0;
+  int64_t pos[QG];
+#pragma unroll
+  for (int u = 0; u < QG; ++u) pos[u] = causal ? A.causal_n0 + (qg0 + (u < nq ? u : 0)) % A.T : A.n_tokens - 1;
   uint32_t rt = 0u;
 #pragma unroll
   for (int i = 0; i < kQPT; ++i) {
@@ -239,14 +245,27 @@ __device__ __forceinline__ void quad_masks(const AttendArgs& A, int cache, int q
     for (int kk = 0; kk < 4; ++kk) {
       const int64_t key = key0 + 4 * i + kk;
       const bool in = key < k_hi;
-      const bool forced = in && (all || (sink && key == 0) || (last && key >= last_start));
       const int j = (4 * i + kk) >> lc;  // chunk of this key, counted from c0
       uint32_t qb = 0u;                  // bit u: query u routes this key's chunk
 #pragma unroll
       for (int u = 0; u < QG; ++u) qb |= ((wq[u] >> (sh + j)) & 1u) << u;
       if (!in || c0 + j >= A.n_chunks) qb = 0u;
+      uint32_t qs;
+      if (!causal) {
+        const bool forced = in && (all || (sink && key == 0) || (last && key >= last_start));
+        qs = forced ? qall : qb;
+      } else {
+        uint32_t vis = 0u, fq = 0u;
+#pragma unroll
+        for (int u = 0; u < QG; ++u) {
+          const bool v = in && u < nq && key <= pos[u];
+          vis |= (uint32_t)v << u;
+          fq |= (uint32_t)(v && (all || (sink && key == 0) || (last && key >= (int64_t)A.C * (pos[u] / A.C)))) << u;
+        }
+        qb &= vis;
+        qs = fq | qb;
+      }
       qany |= qb;
-      const uint32_t qs = forced ? qall : qb;
 #pragma unroll
       for (int u = 0; u < QG; ++u) msk |= (unsigned long long)((qs >> u) & 1u) << (4 * u + kk);
     }
@@ -532,15 +551,16 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_mfma(AttendArgs A) {
 // bf16 path with the route's cached level-1 logits: V streaming only.
 //
 // Phase 1 compacts the selected quads as above, routed quads first, then the
-// at most 5 quads that hold forced keys only (the sink's quad and the current
-// chunk, which lies inside one tile); the logits of those few are computed
-// once into LDS.  Phase 2: lanes are (quad of the step, key of the quad,
+// few quads that hold forced keys only (the sink's quad and the current
+// chunk, which lies inside one tile: at most 5 quads; in a prefill block the
+// group's queries have up to 3 current chunks, at most 13 quads); the logits
+// of those few are computed once into LDS.  Phase 2: lanes are (quad of the step, key of the quad,
 // 16-byte piece of the row); each wave takes every 4th step, with up to 8
 // steps of V (one coalesced 1 KiB load per quad for d = 128) and their cached
 // logits in flight at once (fewer for larger query groups, whose accumulators
 // take the registers), and keeps a per-lane online softmax (one rescale per
 // batch) in fp32.  No LDS traffic or barrier in the loop.
-constexpr int kMaxForcedQuads = 8;
+constexpr int kMaxForcedQuads = 16;
 
 template <int D, int QG>
 __global__ __launch_bounds__(kAttThreads) void k_attend_cached(AttendArgs A) {

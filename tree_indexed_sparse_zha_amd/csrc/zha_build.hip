@@ -101,11 +101,13 @@ __global__ __launch_bounds__(64 * W) void k_build_span(BuildArgs A) {
 #pragma unroll
   for (int a = 0; a < NAR; ++a) used[a] = false;
 
-  auto emit = [&](int lvl, int64_t node, float L, const float* g) {
-    const int64_t nidx = (int64_t)cache * geo.node_cap[lvl - 1] + node;
+  // Writes one node: g rounded to its storage (kv dtype, or fp8 with a row
+  // scale), L and c = L - r.g/sqrt(d) with the stored g, at the given
+  // destinations (a tree level, or a prefill spine record).
+  auto emit_at = [&](bool fp8, char* gb, float* Ld, float* cd, float* sd, float L, const float* g) {
     float gr[NV];
     if constexpr (sizeof(T) == 2 && NS % 2 == 0) {
-      if ((geo.g8 >> (lvl - 1)) & 1u) {
+      if (fp8) {
         // fp8 E4M3 with a power-of-two scale per row j: 2^e, e = ceil(log2 max|g_j|) - 8
         float mx = 0.f;
 #pragma unroll
@@ -137,15 +139,14 @@ __global__ __launch_bounds__(64 * W) void k_build_span(BuildArgs A) {
         if (j < R) {
           // this lane's 8-value pieces s = 0..NS-1 are MFMA steps s, k-group dg;
           // steps 2P and 2P+1 share one 16-byte slot
-          char* gb = A.tree + geo.g_off[lvl - 1] + nidx * ((int64_t)R * D);
 #pragma unroll
           for (int P = 0; P < NS / 2; ++P)
             st16(gb + ((int64_t)(P * 4 + dg) * R + j) * 16,
                  make_uint4(w8[4 * P], w8[4 * P + 1], w8[4 * P + 2], w8[4 * P + 3]));
           if (dg == 0) {
-            reinterpret_cast<float*>(A.tree + geo.L_off[lvl - 1])[nidx * R + j] = L;
-            reinterpret_cast<float*>(A.tree + geo.c_off[lvl - 1])[nidx * R + j] = c;
-            reinterpret_cast<float*>(A.tree + geo.s_off[lvl - 1])[nidx * R + j] = scl;
+            Ld[j] = L;
+            cd[j] = c;
+            sd[j] = scl;
           }
         }
         return;
@@ -161,14 +162,31 @@ __global__ __launch_bounds__(64 * W) void k_build_span(BuildArgs A) {
     dot += __shfl_xor(dot, 32);
     const float c = L - dot * isd;
     if (j < R) {
-      char* gb = A.tree + geo.g_off[lvl - 1] + nidx * ((int64_t)R * D * Elem<T>::size);
 #pragma unroll
       for (int s = 0; s < NS; ++s) st16(gb + ((int64_t)(s * 4 + dg) * R + j) * 16, pk[s]);
       if (dg == 0) {
-        reinterpret_cast<float*>(A.tree + geo.L_off[lvl - 1])[nidx * R + j] = L;
-        reinterpret_cast<float*>(A.tree + geo.c_off[lvl - 1])[nidx * R + j] = c;
+        Ld[j] = L;
+        cd[j] = c;
       }
     }
+  };
+  auto emit = [&](int lvl, int64_t node, float L, const float* g) {
+    if (A.spine) return;  // spine pass: the tree is already built
+    const bool fp8 = (geo.g8 >> (lvl - 1)) & 1u;
+    const int64_t nidx = (int64_t)cache * geo.node_cap[lvl - 1] + node;
+    const int64_t gnode = (int64_t)R * D * (fp8 ? 1 : Elem<T>::size);
+    float* Lb = reinterpret_cast<float*>(A.tree + geo.L_off[lvl - 1]) + nidx * R;
+    float* cb = reinterpret_cast<float*>(A.tree + geo.c_off[lvl - 1]) + nidx * R;
+    float* sb = fp8 ? reinterpret_cast<float*>(A.tree + geo.s_off[lvl - 1]) + nidx * R : nullptr;
+    emit_at(fp8, A.tree + geo.g_off[lvl - 1] + nidx * gnode, Lb, cb, sb, L, g);
+  };
+  // spine record of (state k, level lvl): g block, then L, c, scale
+  auto emit_spine = [&](int64_t k, int lvl, float L, const float* g) {
+    const bool fp8 = (geo.g8 >> (lvl - 1)) & 1u;
+    char* rec = A.spine + spine_record(cache, k, lvl, A.spine_k0, A.spine_states, geo.levels, A.spine_rec);
+    const int64_t gbytes = (int64_t)R * D * (fp8 ? 1 : Elem<T>::size);
+    float* f = reinterpret_cast<float*>(rec + gbytes);
+    emit_at(fp8, rec, f, f + R, f + 2 * R, L, g);
   };
 
   auto load_block = [&](int64_t pos, int nk, uint4* regs) {
@@ -259,6 +277,7 @@ __global__ __launch_bounds__(64 * W) void k_build_span(BuildArgs A) {
 #pragma unroll
         for (int v = 0; v < NV; ++v) acc[v] *= inv;
         if (geo.leaf_weights) {
+          if (!A.spine) {
           // weights form: w_ji = exp(z_ji - L_j) and c_j = L_j - sum_i w_ji z_ji
           // (= L_j - r_j . g_j / sqrt(d) with the unrounded g_j = sum_i w_ji k_i)
           const int64_t nidx = (int64_t)cache * geo.node_cap[0] + (pos + sg) / C;
@@ -277,6 +296,7 @@ __global__ __launch_bounds__(64 * W) void k_build_span(BuildArgs A) {
           if (j < R && dg == 0) {
             reinterpret_cast<float*>(A.tree + geo.L_off[0])[nidx * R + j] = L;
             reinterpret_cast<float*>(A.tree + geo.c_off[0])[nidx * R + j] = L - wz;
+          }
           }
         } else {
           emit(1, (pos + sg) / C, L, acc);
@@ -302,6 +322,29 @@ __global__ __launch_bounds__(64 * W) void k_build_span(BuildArgs A) {
           emit(lvl, (end - sp) / sp, L, g);
           if (a + 1 < NA) absorb(am[a + 1], as[a + 1], aacc[a + 1], used[a + 1], L, 1.f, g, NV);
           used[a] = false;
+        }
+      }
+      // prefill spine: after chunk k-1, the partial node of each level >= 2
+      // holding it merges that level's open accumulator with every open one
+      // below it (its partial descendants)
+      if (A.spine && (end % C) == 0) {
+        const int64_t k = end / C;
+        if (k >= A.spine_k0 && k < A.spine_k0 + A.spine_states) {
+          float sm = 0.f, ss = 0.f, sgc[NV];
+          bool su = false;
+#pragma unroll
+          for (int a = 0; a < NA; ++a) {
+            const int lvl = a + (LEAF_ACC ? 1 : 2);
+            if (used[a]) absorb(sm, ss, sgc, su, am[a], as[a], aacc[a], NV);
+            if (lvl >= 2 && su && (k % (geo.span_len[lvl] / C)) != 0) {
+              const float L = sm + __logf(ss);
+              const float inv = 1.f / ss;
+              float g[NV];
+#pragma unroll
+              for (int v = 0; v < NV; ++v) g[v] = sgc[v] * inv;
+              emit_spine(k, lvl, L, g);
+            }
+          }
         }
       }
     }
@@ -365,6 +408,11 @@ __global__ __launch_bounds__(64 * W) void k_build_span(BuildArgs A) {
 // is a whole number of the top node's children.
 template <typename T, int D, int NA, bool LEAF>
 hipError_t launch_na(const BuildArgs& a, dim3 grid, hipStream_t s) {
+  if (a.spine) {
+    // the spine needs the accumulators in key order: one wave per span
+    hipLaunchKernelGGL((k_build_span<T, D, NA, LEAF, 1>), grid, dim3(64), 0, s, a);
+    return hipGetLastError();
+  }
   if constexpr (!LEAF && NA >= 1) {
     if (a.geo.C >= 4) {
       hipLaunchKernelGGL((k_build_span<T, D, NA, LEAF, 4>), grid, dim3(256), 0, s, a);

@@ -59,7 +59,21 @@ struct BuildArgs {
   int64_t n_spans;     // number of spans to rebuild
   int64_t span_tokens; // tokens per top span = C^levels
   float inv_sqrt_d;
+  // prefill spine (nullptr: normal build).  With a spine the kernel writes
+  // no tree node; after every chunk it completes it stores, for each
+  // snapshot state k (complete chunks) in [spine_k0, spine_k0 + spine_states),
+  // the partial node of every level >= 2 that holds chunk k-1.
+  char* spine;
+  int64_t spine_k0;
+  int64_t spine_states;
+  int64_t spine_rec;   // bytes per record: g block, then L, c, scale (R fp32 each)
 };
+
+// Byte offset of the spine record of (cache, state k, level lvl >= 2).
+__host__ __device__ inline int64_t spine_record(int64_t cache, int64_t k, int lvl, int64_t k0, int64_t states,
+                                                int levels, int64_t rec) {
+  return ((cache * states + (k - k0)) * (levels - 1) + (lvl - 2)) * rec;
+}
 
 struct ScoreArgs {
   const char* g;         // level base of g
@@ -80,6 +94,13 @@ struct ScoreArgs {
   int leaf_weights;            // level 1 in the weights form: g holds w [R][C] fp32
   const void* K;               // keys (weights form only)
   int64_t ksb, ksh, kst;
+  int64_t causal_n0;           // prefill: query t of a head sits at position causal_n0 + t; -1 = decode
+  int64_t lvl_chunks;          // chunks under one node of this level (C^(l-1))
+  const char* spine;           // prefill spine records (levels >= 2), or nullptr
+  int64_t spine_k0, spine_states, spine_rec;
+  int levels, level, top;      // tree depth, this level, routing start level
+  int64_t kr_spine_slot;       // key-range slot of the spine score (prefill)
+  int64_t n_queries;           // caches * QC
   float* logits;               // optional [caches][ceil(QC/16)][nquads][4][QW] (weights form)
   int64_t nquads;              // 4-key quads per cache in the logits buffer
   int QW;                      // queries per logits row: min(QC rounded up to 4, 16)
@@ -114,6 +135,7 @@ struct AttendArgs {
   int64_t tile_keys;  // keys per workgroup
   int64_t n_tiles;
   float* partial;     // [n_queries][n_tiles][D + 2]
+  int64_t causal_n0;    // prefill: query t of a head sees keys [0, causal_n0 + t]; -1 = decode
   const float* logits;  // optional, see ScoreArgs
   int64_t nquads;
   int QW;

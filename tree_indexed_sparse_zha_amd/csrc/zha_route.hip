@@ -65,6 +65,16 @@ __device__ __forceinline__ void publish_range(uint32_t* slot, bool c, uint32_t k
     *reinterpret_cast<uint4*>(slot) = make_uint4(kmax, kmin, (uint32_t)__popcll(bal), 0u);
 }
 
+// Prefill (causal): query qi of a cache (qi = head * T + t) sits at position
+// n0 + t and routes on the tree of its first n0 + t + 1 tokens, whose level-l
+// nodes are the complete nodes below its horizon plus one partial node (the
+// spine).  Complete nodes of this level visible to it (all: decode).
+__device__ __forceinline__ int64_t causal_horizon(const ScoreArgs& A, int qi) {
+  if (A.causal_n0 < 0) return INT64_MAX;
+  const int64_t k = (A.causal_n0 + qi % A.T + 1) / A.C;  // complete chunks
+  return k / A.lvl_chunks;
+}
+
 __global__ void k_route_init(uint32_t* kr, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) {
@@ -140,6 +150,9 @@ __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs A) {
     } else {
       mybits = valid;
     }
+    // prefill: nodes at or beyond the query's horizon are not its complete nodes
+    const int64_t hz = causal_horizon(A, qg0 + qn) - nb0;
+    if (hz < 16) mybits &= hz > 0 ? (1u << hz) - 1u : 0u;
   }
   uint32_t anybits = mybits;
 #pragma unroll
@@ -301,6 +314,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     } else {
       mybits = valid;
     }
+    // prefill: only the complete chunks below the query's horizon
+    const int64_t hz = causal_horizon(A, qg0 + qn) - m0;
+    if (hz < 64) mybits &= hz > 0 ? (1ull << hz) - 1ull : 0ull;
   }
   // chunks that are a candidate of some query (same value in every lane)
   unsigned long long anybits = mybits;
@@ -424,6 +440,74 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     const float v = lane < NCH ? sc[q][lane] : kNegInf;
     const bool c = lane < NCH && m0 + lane < A.n_nodes && v > kNegInf;
     publish_range(A.keyrange + (((int64_t)cache * A.QC + qg0 + q) * A.kr_slots + blockIdx.x) * 4, c, order_key(v));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// prefill spine score (bf16 keys, levels >= 2): one wave per query scores the
+// partial node of its own prefix tree at this level, from the spine record of
+// its state, when the node is a candidate (top level, or its parent, the
+// partial node one level up, was kept).  Lane (j, dg): reference query j,
+// the 16-byte pieces dg, dg + 4, ... of d (the node layout of the tree).
+
+template <int D, bool G8>
+__global__ __launch_bounds__(256) void k_score_spine(ScoreArgs A) {
+  constexpr int NS = D / 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t q = (int64_t)blockIdx.x * 4 + wave;
+  if (q >= A.n_queries) return;  // uniform per wave
+  const int cache = (int)(q / A.QC), qi = (int)(q % A.QC);
+  const int64_t k = (A.causal_n0 + qi % A.T + 1) / A.C;  // complete chunks of the prefix
+  const int64_t sid = k / A.lvl_chunks;                   // the partial node's id
+  uint32_t* slot = A.keyrange + (q * A.kr_slots + A.kr_spine_slot) * 4;
+  bool cand = (k % A.lvl_chunks) != 0 && k >= A.spine_k0 && k < A.spine_k0 + A.spine_states;
+  if (cand && A.level < A.top) {
+    const int64_t par = sid / A.C;
+    cand = (A.sel_parent[q * A.parent_words + (par >> 5)] >> (par & 31)) & 1u;
+  }
+  if (!cand) {
+    if (lane == 0) *reinterpret_cast<uint4*>(slot) = make_uint4(0u, 0xffffffffu, 0u, 0u);
+    return;
+  }
+  const int R = A.R, j = lane & 15, dg = lane >> 4;
+  const char* rec = A.spine + spine_record(cache, k, A.level, A.spine_k0, A.spine_states, A.levels, A.spine_rec);
+  const float* f = reinterpret_cast<const float*>(rec + (int64_t)R * D * (G8 ? 1 : 2));
+  const int b = cache / A.H, h = cache % A.H;
+  const bf16_t* qp = reinterpret_cast<const bf16_t*>(A.Q) + (int64_t)b * A.qsb + (int64_t)h * A.qsh +
+                     (int64_t)(qi / A.T) * A.qsg + (int64_t)(qi % A.T) * A.qst;
+  float dot = 0.f;
+  if (j < R) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      float qv[8], gv[8];
+      unpack(ld16(qp + (4 * s + dg) * 8), qv, bf16_t());
+      if constexpr (G8) {
+        const uint4 w = ld16(rec + ((int64_t)((s / 2) * 4 + dg) * R + j) * 16);
+        const uint32_t w0 = (s & 1) ? w.z : w.x, w1 = (s & 1) ? w.w : w.y;
+        const float sc = f[2 * R + j];
+        gv[0] = __builtin_amdgcn_cvt_f32_fp8((int)w0, 0) * sc;
+        gv[1] = __builtin_amdgcn_cvt_f32_fp8((int)w0, 1) * sc;
+        gv[2] = __builtin_amdgcn_cvt_f32_fp8((int)w0, 2) * sc;
+        gv[3] = __builtin_amdgcn_cvt_f32_fp8((int)w0, 3) * sc;
+        gv[4] = __builtin_amdgcn_cvt_f32_fp8((int)w1, 0) * sc;
+        gv[5] = __builtin_amdgcn_cvt_f32_fp8((int)w1, 1) * sc;
+        gv[6] = __builtin_amdgcn_cvt_f32_fp8((int)w1, 2) * sc;
+        gv[7] = __builtin_amdgcn_cvt_f32_fp8((int)w1, 3) * sc;
+      } else {
+        unpack(ld16(rec + ((int64_t)(4 * s + dg) / 4 * 4 * R + (int64_t)((4 * s + dg) % 4) * R + j) * 16), gv,
+               bf16_t());
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot += qv[e] * gv[e];
+    }
+  }
+  dot += __shfl_xor(dot, 16);
+  dot += __shfl_xor(dot, 32);
+  float v = j < R ? f[R + j] + dot * A.inv_sqrt_d : kNegInf;
+  v = wave_max_xor(v, 1, 16);
+  if (lane == 0) {
+    A.score[q * A.score_stride + sid] = v;
+    *reinterpret_cast<uint4*>(slot) = make_uint4(order_key(v), order_key(v), 1u, 0u);
   }
 }
 
@@ -758,9 +842,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs A) {
 }  // namespace
 
 int64_t route_kr_slots(int dtype, bool leaf_weights, int64_t node_cap, int C) {
-  if (leaf_weights) return (node_cap * C + 255) / 256;  // k_score_leafw: 256-key tiles
-  if (dtype == 1) return (node_cap + 63) / 64;          // k_score_bf16: 64-node tiles
-  return 1;                                             // k_score_generic: atomics
+  // one slot per score tile, plus one for the prefill spine score
+  if (leaf_weights) return (node_cap * C + 255) / 256 + 1;  // k_score_leafw: 256-key tiles
+  if (dtype == 1) return (node_cap + 63) / 64 + 1;          // k_score_bf16: 64-node tiles
+  return 1;                                                 // k_score_generic: atomics
 }
 
 hipError_t launch_route_init(uint32_t* keyrange, int64_t n, Prof& prof) {
@@ -836,6 +921,23 @@ hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dty
     sel.kr_used = (sa.n_nodes + 63) / 64;
   else
     sel.kr_used = 1;
+  if (sa.spine && level >= 2 && sa.n_nodes > 0) {
+    // prefill: each query's partial node of this level, scored from the spine
+    ScoreArgs sp = sa;
+    sp.kr_spine_slot = sel.kr_used;
+    const dim3 g((unsigned)((sa.n_queries + 3) / 4));
+    if (sa.gscale) {
+      if (sa.D == 128)
+        hipLaunchKernelGGL((k_score_spine<128, true>), g, dim3(256), 0, s, sp);
+      else
+        hipLaunchKernelGGL((k_score_spine<64, true>), g, dim3(256), 0, s, sp);
+    } else if (sa.D == 128) {
+      hipLaunchKernelGGL((k_score_spine<128, false>), g, dim3(256), 0, s, sp);
+    } else {
+      hipLaunchKernelGGL((k_score_spine<64, false>), g, dim3(256), 0, s, sp);
+    }
+    sel.kr_used += 1;
+  }
   prof.begin(ZHA_K_SELECT, level);
   hipLaunchKernelGGL(k_select, dim3((unsigned)n_queries), dim3(kSelThreads), 0, s, sel);
   prof.end();

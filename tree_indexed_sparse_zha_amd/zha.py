@@ -27,7 +27,7 @@ ZHA_OK, ZHA_ERR_NULL, ZHA_ERR_ARG, ZHA_ERR_UNSUPPORTED, ZHA_ERR_CAPACITY, ZHA_ER
     -6,
 )
 ZHA_F32, ZHA_BF16 = 0, 1
-ZHA_SINK, ZHA_LAST_CHUNK, ZHA_ALL_KEYS = 1, 2, 4
+ZHA_SINK, ZHA_LAST_CHUNK, ZHA_ALL_KEYS, ZHA_CAUSAL = 1, 2, 4, 8
 ZHA_LEAF_MEAN, ZHA_LEAF_WEIGHTS = 0, 1
 ZHA_G_KV, ZHA_G_FP8 = 0, 2
 MAX_LEVELS = 8
@@ -178,6 +178,9 @@ def load(path: str = LIB_PATH) -> ct.CDLL:
         "zha_append": (ct.c_int, [cfgp, P, i64p, I64, I64, P, P, P, P]),
         "zha_route": (ct.c_int, [cfgp, P, I64, P, i64p, I32, F, P, i64p, P, P, P, P, P, I64, P, P]),
         "zha_route_levels": (ct.c_int, [cfgp, P, I64, P, i64p, I32, ct.POINTER(F), I32, P, i64p, P, P, P, P, P, I64, P, P]),
+        "zha_spine_bytes": (I64, [cfgp, I32]),
+        "zha_build_spine": (ct.c_int, [cfgp, P, i64p, I64, I32, P, P, P, P]),
+        "zha_route_prefill": (ct.c_int, [cfgp, P, P, I64, P, i64p, I32, F, P, i64p, P, P, P, P, P, I64, P, P]),
         "zha_attend": (ct.c_int, [cfgp, P, i64p, I32, P, P, i64p, I64, P, I64, P, ct.c_uint32, P, P, P, I64, P, P]),
         "zha_dense_decode": (ct.c_int, [cfgp, P, i64p, I32, P, P, i64p, I64, P, P, P, I64, P, P]),
     }
@@ -373,6 +376,42 @@ def route_levels(cfg: ZhaConfig, tree: torch.Tensor, n_tokens: int, Q: torch.Ten
     _check(
         load().zha_route_levels(
             ct.byref(c), _ptr(tree), int(n_tokens), _ptr(Q), qs, int(T), pl, int(top_level), _ptr(K), ks,
+            _ptr(buf.sel), _ptr(buf.score), _ptr(buf.stats), _ptr(buf.logits), _ptr(buf.ws), int(buf.ws.numel()),
+            _prof(ev), _stream(Q),
+        )
+    )
+
+
+def spine_bytes(cfg: ZhaConfig, T: int) -> int:
+    c = cfg.c()
+    n = load().zha_spine_bytes(ct.byref(c), int(T))
+    if n < 0:
+        _check(ZHA_ERR_ARG)
+    return int(n)
+
+
+def alloc_spine(cfg: ZhaConfig, T: int, device="cuda") -> torch.Tensor:
+    return torch.empty(spine_bytes(cfg, T), dtype=torch.uint8, device=device)
+
+
+def build_spine(cfg: ZhaConfig, K: torch.Tensor, ref: torch.Tensor, spine: torch.Tensor, n_tokens: int, T: int,
+                ev=None):
+    """zha_build_spine: partial nodes of the prefix trees of positions [n_tokens - T, n_tokens)."""
+    c = cfg.c()
+    ks = _i64(*_elem_strides(K, 3))
+    _check(load().zha_build_spine(ct.byref(c), _ptr(K), ks, int(n_tokens), int(T), _ptr(ref), _ptr(spine),
+                                  _prof(ev), _stream(K)))
+
+
+def route_prefill(cfg: ZhaConfig, tree: torch.Tensor, spine: Optional[torch.Tensor], n_tokens: int, Q: torch.Tensor,
+                  T: int, p: float, buf: RouteBuffers, ev=None, K: Optional[torch.Tensor] = None):
+    """zha_route_prefill: query t of each head routes on its prefix of n_tokens - T + t + 1 tokens."""
+    c = cfg.c()
+    qs = _i64(*_elem_strides(Q, 4))
+    ks = _i64(*_elem_strides(K, 3)) if K is not None else None
+    _check(
+        load().zha_route_prefill(
+            ct.byref(c), _ptr(tree), _ptr(spine), int(n_tokens), _ptr(Q), qs, int(T), float(p), _ptr(K), ks,
             _ptr(buf.sel), _ptr(buf.score), _ptr(buf.stats), _ptr(buf.logits), _ptr(buf.ws), int(buf.ws.numel()),
             _prof(ev), _stream(Q),
         )
