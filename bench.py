@@ -193,6 +193,9 @@ def main():
                     help="storage of the mean keys g: the KV dtype (default) or FP8 E4M3 with row scales")
     ap.add_argument("--no-logits", action="store_true",
                     help="attention recomputes every logit from K instead of reading the route's level-1 logits")
+    ap.add_argument("--prefill", type=int, default=0,
+                    help="chunked-prefill mode: each step appends a block of this many positions per sequence and "
+                         "routes + attends all of them causally (prints its own JSON line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     args = ap.parse_args()
@@ -210,6 +213,8 @@ def main():
     w = W.WORKLOADS[args.workload]
     if args.tokens:
         w = w.with_tokens(args.tokens)
+    if args.prefill:
+        return prefill_main(args, w)
     p = args.p if args.p is not None else w.p[0]
     p_levels = [float(x) for x in args.p_levels.split(",")] if args.p_levels else None
     T = w.queries_per_head
@@ -400,6 +405,116 @@ def main():
             "GB_s": round(cfg.n_caches * N0 * (cfg.head_dim * cfg.esize + tree_bytes_per_token) / (build_ms / 1e3) / 1e9, 1),
         },
         "dense": dense,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def prefill_main(args, w):
+    """Chunked prefill: per step, append a block of P positions to every
+    sequence, build the block's spine, route all its queries on their prefix
+    trees and attend causally; against the same-GPU dense causal attention of
+    the block."""
+    P = args.prefill
+    p = args.p if args.p is not None else w.p[0]
+    n_steps = args.warmup + args.steps
+    N0 = w.n_tokens
+    # the appended positions hold the workload's appended segments (zeros when it has none)
+    app = -(-n_steps * P // w.append_tokens) if w.append_tokens else 0
+    capacity = N0 + max(n_steps * P, app * w.append_tokens)
+    leaf_form = args.leaf_form if w.chunk in (4, 8, 16) else "mean"
+    cfg = cfg_of(w, capacity, leaf_form, args.g_dtype)
+    if cfg.q_per_kv * P > 1024:
+        print("--prefill: q_per_kv * block must be <= 1024", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    log(f"prefill {w.name}: N0={N0} block={P} caches={cfg.n_caches} p={p}")
+    batch = W.make_batch(w, device="cuda", capacity=capacity, append_steps=app)
+    K, V, ref = batch.K, batch.V, batch.ref
+    # the block's queries: synthetic, seeded; K/V of the appended positions stay those of the generator
+    gq = torch.Generator(device="cuda")
+    gq.manual_seed(12345)
+    Q = torch.randn(cfg.batch, cfg.n_kv_heads, cfg.q_per_kv, P, cfg.head_dim, generator=gq, device="cuda").to(
+        cfg.torch_dtype)
+    tree = zha.alloc_tree(cfg)
+    spine = zha.alloc_spine(cfg, P)
+    # the cached level-1 logits grow with queries x context: keep them only while they stay small
+    keep_logits = cfg.leaf_form == "weights" and zha.route_layout(cfg, P).logits_floats * 4 <= (8 << 30)
+    buf = zha.alloc_route(cfg, P, logits=keep_logits)
+    nq = int(buf.layout.n_queries)
+    out = torch.empty(nq, cfg.head_dim, device="cuda")
+    lse = torch.empty(nq, device="cuda")
+    ws = torch.empty(zha.attend_workspace_bytes(cfg, P), dtype=torch.uint8, device="cuda")
+    zha.build(cfg, K, ref, tree, N0)
+    torch.cuda.synchronize()
+    flags = FLAGS | zha.ZHA_CAUSAL
+    ev = [[zha.HipEvents(2 * cfg.levels + 4) for _ in range(4)] for _ in range(n_steps)]
+
+    def step(s):
+        n_old = N0 + s * P
+        n = n_old + P
+        zha.append(cfg, K, ref, tree, n_old, P, ev=ev[s][0])
+        zha.build_spine(cfg, K, ref, spine, n, P, ev=ev[s][1])
+        zha.route_prefill(cfg, tree, spine, n, Q, P, p, buf, ev=ev[s][2], K=K)
+        zha.attend(cfg, Q, P, K, V, n, zha.level1_sel(buf), flags, out, lse, ws, ev=ev[s][3], logits=buf.logits)
+        return n
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for s in range(args.warmup, n_steps):
+        n_final = step(s)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    parts = {}
+    for s in range(args.warmup, n_steps):
+        for name, e in zip(("append", "spine", "route", "attend"), ev[s]):
+            parts.setdefault(name, []).append(sum(x[2] for x in e.elapsed_ms()))
+    parts = {k: round(float(np.mean(v)), 4) for k, v in parts.items()}
+    dense_ms = None
+    if not args.no_dense:
+        ev_d = zha.HipEvents(2)
+        times = []
+        for r in range(4):
+            zha.attend(cfg, Q, P, K, V, n_final, None, zha.ZHA_ALL_KEYS | zha.ZHA_CAUSAL, out, lse, ws, ev=ev_d)
+            torch.cuda.synchronize()
+            if r:
+                times.append(sum(x[2] for x in ev_d.elapsed_ms()))
+        dense_ms = round(float(np.mean(times)), 4)
+    tokens = cfg.batch * P
+    res = {
+        "metric": "chunked prefill tokens/s (routed, causal)",
+        "value": round(tokens / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name + "-prefill",
+            "context_at_block_end": n_final,
+            "block_positions": P,
+            "batch": w.batch,
+            "kv_heads": w.n_kv_heads,
+            "q_per_kv": w.q_per_kv,
+            "chunk": w.chunk,
+            "levels": w.levels,
+            "n_ref": w.n_ref,
+            "p": p,
+            "leaf_form": cfg.leaf_form,
+            "g_dtype": cfg.g_dtype,
+            "cached_logits": keep_logits,
+        },
+        "stage_ms": parts,
+        "dense_causal_attend_ms": dense_ms,
+        "routed_over_dense": round((parts["spine"] + parts["route"] + parts["attend"]) / dense_ms, 3) if dense_ms else None,
     }
     print(json.dumps(res), flush=True)
 
