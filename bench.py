@@ -253,7 +253,7 @@ def main():
     build_ms = ev_build.elapsed_ms()[0][2]
     log(f"build {build_ms:.2f} ms")
 
-    ev_app = [zha.HipEvents(1) for _ in range(n_steps)]
+    ev_app = [zha.HipEvents(2) for _ in range(n_steps)]  # the split append launches two kernels
     ev_route = [zha.HipEvents(2 * cfg.levels) for _ in range(n_steps)]
     ev_att = [zha.HipEvents(2) for _ in range(n_steps)]
 
@@ -287,10 +287,13 @@ def main():
     # per-kernel times over the timed steps
     kt = {}
     for s in range(args.warmup, n_steps):
+        per_step = {}  # a stage may launch several kernels (the split append launches two)
         for evs in (ev_app[s], ev_route[s], ev_att[s]):
             for kid, lvl, ms in evs.elapsed_ms():
                 key = f"{zha.KERNEL_NAMES[kid]}" + (f"_L{lvl}" if lvl else "")
-                kt.setdefault(key, []).append(ms)
+                per_step[key] = per_step.get(key, 0.0) + ms
+        for key, ms in per_step.items():
+            kt.setdefault(key, []).append(ms)
     kmean = {k: float(np.mean(v)) for k, v in kt.items()}
     route_ms = sum(v for k, v in kmean.items() if k.startswith(("score", "select")))
     attend_ms = kmean.get("attend", 0.0) + kmean.get("combine", 0.0)

@@ -146,6 +146,9 @@ typedef struct zha_tree_layout {
   int64_t g_bytes[ZHA_MAX_LEVELS]; /* bytes of one node's g (or w) block, per level */
   int64_t total_bytes;  /* size of the caller's tree buffer */
   int64_t s_offset[ZHA_MAX_LEVELS]; /* fp8 row scales per level, or -1 */
+  int64_t scratch_offset; /* fp32 children of up to 2 top nodes per cache, used by
+                             zha_append to split its spans over more workgroups;
+                             -1 when the geometry does not split */
 } zha_tree_layout;
 
 /*

@@ -50,8 +50,11 @@ def test_tree_layout_sizes():
     assert all(tl.g_bytes[i] == 16 * 128 * 2 for i in range(6))
     # node = R*d*2 (g) + 4R (L) + 4R (c) = 4224 bytes
     nodes = sum(tl.node_cap[i] for i in range(6)) * 8
-    assert tl.total_bytes >= nodes * 4224
-    assert tl.total_bytes < nodes * 4224 + 6 * 3 * 256
+    # plus the append scratch: fp32 children of 2 top nodes per cache
+    scratch = 8 * 2 * 4 * 16 * (128 + 2) * 4
+    assert tl.scratch_offset >= 0 and tl.scratch_offset % 256 == 0
+    assert tl.total_bytes >= nodes * 4224 + scratch
+    assert tl.total_bytes < nodes * 4224 + scratch + 7 * 3 * 256
     for i in range(6):
         assert tl.g_offset[i] % 256 == 0 and tl.L_offset[i] % 256 == 0 and tl.c_offset[i] % 256 == 0
 

@@ -88,6 +88,10 @@ int check_strides(const int64_t* s, int n, int es, const char* name) {
   return ZHA_OK;
 }
 
+// Appends split each top span over its C children when the top has at least
+// two levels below it and C is in 4..16 (the sub-span pass uses 4 waves).
+static bool split_top(const zha_config* c) { return c->levels >= 3 && c->chunk >= 4 && c->chunk <= 16; }
+
 void fill_tree_layout(const zha_config* c, zha_tree_layout* out) {
   std::memset(out, 0, sizeof(*out));
   out->levels = c->levels;
@@ -114,6 +118,11 @@ void fill_tree_layout(const zha_config* c, zha_tree_layout* out) {
     }
   }
   for (int l = c->levels; l < ZHA_MAX_LEVELS; ++l) out->s_offset[l] = -1;
+  out->scratch_offset = -1;
+  if (split_top(c)) {
+    out->scratch_offset = off;
+    off = align256(off + caches * 2 * c->chunk * (int64_t)c->n_ref * (c->head_dim + 2) * 4);
+  }
   out->total_bytes = off > 0 ? off : 256;
 }
 
@@ -213,6 +222,26 @@ int do_build(const zha_config* cfg, const void* K, const int64_t* ks, int64_t n_
   if (a.n_spans <= 0) return ZHA_OK;
   if (a.n_spans > 0x7fffffffll) return fail(ZHA_ERR_UNSUPPORTED, "too many spans");
   zha::Prof pr{prof, static_cast<hipStream_t>(stream)};
+  a.top_level = cfg->levels;
+  if (append && a.n_spans <= 2 && tl.scratch_offset >= 0) {
+    // few spans: build their children in parallel, then merge the top nodes
+    zha::BuildArgs s1 = a;
+    s1.top_level = cfg->levels - 1;
+    s1.span_tokens = a.span_tokens / C;
+    s1.first_span = a.first_span * C;
+    s1.n_spans = a.n_spans * C;
+    s1.top_scratch = reinterpret_cast<float*>(static_cast<char*>(tree) + tl.scratch_offset);
+    s1.scratch_span0 = a.first_span;
+    hipError_t e = zha::launch_build(s1, cfg->kv_dtype, pr);
+    if (e != hipSuccess) return hip_fail(e, "build launch");
+    zha::BuildArgs s2 = a;
+    s2.merge_top = 1;
+    s2.top_scratch = s1.top_scratch;
+    s2.scratch_span0 = a.first_span;
+    e = zha::launch_build(s2, cfg->kv_dtype, pr);
+    if (e != hipSuccess) return hip_fail(e, "build launch");
+    return ZHA_OK;
+  }
   hipError_t e = zha::launch_build(a, cfg->kv_dtype, pr);
   if (e != hipSuccess) return hip_fail(e, "build launch");
   return ZHA_OK;
@@ -507,6 +536,7 @@ int zha_build_spine(const zha_config* cfg, const void* K, const int64_t k_stride
   a.spine_k0 = (n_tokens - T + 1) / cfg->chunk;
   a.spine_states = spine_states(cfg, T);
   a.spine_rec = spine_rec_bytes(cfg);
+  a.top_level = cfg->levels;
   // states k0 .. k_end (complete chunks of n_tokens): the spans holding chunks k0-1 .. k_end-1
   const int64_t k_end = n_tokens / cfg->chunk;
   if (k_end < 1 || k_end < a.spine_k0) return ZHA_OK;

@@ -189,6 +189,42 @@ __global__ __launch_bounds__(64 * W) void k_build_span(BuildArgs A) {
     emit_at(fp8, rec, f, f + R, f + 2 * R, L, g);
   };
 
+  // merge pass of a split top span: fold the fp32 children the sub-span pass
+  // stored into the top node with the unsplit build's association: the 4
+  // waves of a span each fold their C / 4 children in order, then wave 0
+  // folds the waves' results in order
+  const int64_t rec_floats = (int64_t)R * (D + 2);
+  if (A.merge_top) {
+    float mm = 0.f, ss = 0.f, gg[NV];
+    bool u = false;
+    const int64_t sub_tokens = A.span_tokens / C;
+    const int per = C / 4;
+    for (int w = 0; w < 4; ++w) {
+      float wm = 0.f, wsum = 0.f, wg[NV];
+      bool wu = false;
+      for (int c = w * per; c < (w + 1) * per; ++c) {
+        if (t0 + c * sub_tokens >= tend) break;
+        const float* rec = A.top_scratch + (((int64_t)cache * 2 + (span - A.scratch_span0)) * C + c) * rec_floats;
+        const int jj = j < R ? j : 0;
+        float gc[NV];
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+          for (int e = 0; e < E; ++e) gc[s * E + e] = rec[2 * R + (int64_t)jj * D + (4 * s + dg) * E + e];
+        absorb(wm, wsum, wg, wu, rec[jj], rec[R + jj], gc, NV);
+      }
+      if (wu) absorb(mm, ss, gg, u, wm, wsum, wg, NV);
+    }
+    if (u) {
+      const float L = mm + __logf(ss);
+      const float inv = 1.f / ss;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) gg[v] *= inv;
+      emit(geo.levels, span, L, gg);
+    }
+    return;
+  }
+
   auto load_block = [&](int64_t pos, int nk, uint4* regs) {
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
@@ -398,6 +434,25 @@ __global__ __launch_bounds__(64 * W) void k_build_span(BuildArgs A) {
 #pragma unroll
         for (int v = 0; v < NV; ++v) gg[v] *= inv;
         emit(lvl, t0 / geo.span_len[lvl], L, gg);
+        if (A.top_scratch) {
+          // sub-span pass: this node is a child of a split top node.  Keep
+          // it in fp32 exactly as a top-level accumulator holds a single
+          // child (max L, mass 1, mean g), so that the merge pass repeats
+          // the unsplit build's arithmetic bit for bit.
+          const int64_t top_span = t0 / (A.span_tokens * C);
+          float* rec = A.top_scratch +
+                       (((int64_t)cache * 2 + (top_span - A.scratch_span0)) * C + (t0 / A.span_tokens) % C) * rec_floats;
+          if (j < R) {
+            if (dg == 0) {
+              rec[j] = L;
+              rec[R + j] = 1.f;
+            }
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+              for (int e = 0; e < E; ++e) rec[2 * R + (int64_t)j * D + (4 * s + dg) * E + e] = gg[s * E + e];
+          }
+        }
       }
     }
   }
@@ -408,7 +463,7 @@ __global__ __launch_bounds__(64 * W) void k_build_span(BuildArgs A) {
 // is a whole number of the top node's children.
 template <typename T, int D, int NA, bool LEAF>
 hipError_t launch_na(const BuildArgs& a, dim3 grid, hipStream_t s) {
-  if (a.spine) {
+  if (a.spine || a.merge_top) {
     // the spine needs the accumulators in key order: one wave per span
     hipLaunchKernelGGL((k_build_span<T, D, NA, LEAF, 1>), grid, dim3(64), 0, s, a);
     return hipGetLastError();
@@ -431,7 +486,7 @@ template <typename T, int D>
 hipError_t dispatch_leaf(const BuildArgs& a, dim3 grid, hipStream_t s) {
   if (a.geo.C > kKeysPerBlock) {
     // leaves span several blocks: an open node per level, leaves included
-    switch (a.geo.levels) {
+    switch (a.top_level) {
       case 1: return launch_na<T, D, 1, true>(a, grid, s);
       case 2: return launch_na<T, D, 2, true>(a, grid, s);
       case 3: return launch_na<T, D, 3, true>(a, grid, s);
@@ -439,7 +494,7 @@ hipError_t dispatch_leaf(const BuildArgs& a, dim3 grid, hipStream_t s) {
       default: return hipErrorInvalidValue;
     }
   }
-  switch (a.geo.levels - 1) {
+  switch (a.top_level - 1) {
     case 0: return launch_na<T, D, 0, false>(a, grid, s);
     case 1: return launch_na<T, D, 1, false>(a, grid, s);
     case 2: return launch_na<T, D, 2, false>(a, grid, s);

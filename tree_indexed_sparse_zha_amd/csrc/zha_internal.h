@@ -67,6 +67,14 @@ struct BuildArgs {
   int64_t spine_k0;
   int64_t spine_states;
   int64_t spine_rec;   // bytes per record: g block, then L, c, scale (R fp32 each)
+  // split top spans (appends touching at most 2 spans): the sub-span pass
+  // builds the top node's children (top_level = levels - 1) and also stores
+  // them as fp32 (m, s, weighted sum) in top_scratch; the merge pass
+  // (merge_top) folds them into the top node.
+  int top_level;       // level of the launch's top node
+  float* top_scratch;  // [caches][2 spans][C children][R][D + 2] fp32, or nullptr
+  int64_t scratch_span0;
+  int merge_top;
 };
 
 // Byte offset of the spine record of (cache, state k, level lvl >= 2).

@@ -66,6 +66,7 @@ class TreeLayout(ct.Structure):
         ("g_bytes", ct.c_int64 * MAX_LEVELS),
         ("total_bytes", ct.c_int64),
         ("s_offset", ct.c_int64 * MAX_LEVELS),
+        ("scratch_offset", ct.c_int64),
     ]
 
 
