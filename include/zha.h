@@ -168,6 +168,11 @@ typedef struct zha_tree_layout {
  * quads, 4 keys, QW = min(QC rounded up to 4, 16) queries; QC = G*T queries
  * per cache; rows beyond QC unused) so that zha_attend reads 16 bytes per key
  * and query instead of the keys.
+ * Scratch: zha_route accepts any ws_bytes >= workspace_min_bytes (per level
+ * and query, the score tiles' candidate key ranges).  With ws_bytes >=
+ * workspace_bytes it may also spread the selection of a level with few
+ * queries and many candidates over several workgroups per query (same
+ * result, bit for bit).
  */
 typedef struct zha_route_layout {
   int32_t levels;
@@ -181,8 +186,9 @@ typedef struct zha_route_layout {
   int64_t sel_words_total;    /* uint32 words of the sel buffer */
   int64_t score_floats_total; /* floats of the score buffer */
   int64_t stats_total;        /* records of the stats buffer */
-  int64_t workspace_bytes;    /* scratch zha_route needs */
+  int64_t workspace_bytes;    /* scratch that enables every select form (see below) */
   int64_t logits_floats;      /* floats of the optional logits buffer (weights form), else 0 */
+  int64_t workspace_min_bytes; /* smallest scratch zha_route accepts */
 } zha_route_layout;
 
 /*
@@ -303,7 +309,8 @@ int zha_append(const zha_config* cfg, const void* K, const int64_t k_strides[3],
  *   stats     device, zha_get_route_layout().stats_total records (output).
  *   logits    device, zha_get_route_layout().logits_floats fp32 (optional
  *             output, NULL to skip; leaf-weights form only).
- *   ws        device scratch of at least workspace_bytes.
+ *   ws        device scratch of at least workspace_min_bytes (ws_bytes
+ *             >= workspace_bytes enables the split selection).
  * Level-1 bits of sel are the routed chunk ids consumed by zha_attend.
  */
 int zha_route(const zha_config* cfg, const void* tree, int64_t n_tokens, const void* Q,

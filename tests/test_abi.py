@@ -91,6 +91,22 @@ def test_route_layout_logits():
     assert rl.logits_floats == 8 * 2 * (32768 // 4) * 16 * 4
 
 
+def test_route_workspace_split_select():
+    """Few queries over many candidates: the full workspace adds, after the
+    key-range slots, one 128-byte state per query and one slot of 2,056
+    64-bit words per (query, segment), segments of >= 32,768 candidates and
+    at most 2,048 workgroups per level, at most 64 queries."""
+    cfg = cfg_deep(capacity=1 << 20, batch=1)  # 8 caches x 4 query heads, T = 1: 32 queries
+    rl = zha.route_layout(cfg, 1)
+    assert rl.n_queries == 32
+    S = min(2048 // 32, (1 << 18) // 32768)  # level 1: 262,144 chunks -> 8 segments
+    split = 32 * 128 + 32 * S * 2056 * 8
+    assert rl.workspace_bytes == rl.workspace_min_bytes + (split + 255) // 256 * 256
+    assert rl.workspace_min_bytes % 256 == 0
+    many = zha.route_layout(cfg, 4)  # 128 queries: one workgroup per query
+    assert many.workspace_bytes == many.workspace_min_bytes
+
+
 def test_route_layout_sizes():
     cfg = cfg_deep()
     rl = zha.route_layout(cfg, 64)
@@ -99,7 +115,9 @@ def test_route_layout_sizes():
     assert rl.score_floats_total == rl.n_queries * (8192 + 2048 + 512 + 128 + 32 + 8)
     assert rl.stats_total == 6 * rl.n_queries
     assert [rl.score_stride[i] for i in range(6)] == [8192, 2048, 512, 128, 32, 8]
-    assert rl.workspace_bytes >= 6 * rl.n_queries * 16
+    assert rl.workspace_min_bytes >= 6 * rl.n_queries * 16
+    # 2,048 queries: every level keeps one select workgroup per query
+    assert rl.workspace_bytes == rl.workspace_min_bytes
     odd = zha.route_layout(cfg_deep(capacity=32768 + 4 * 4096 * 3 + 4), 1)
     for i in range(6):
         assert odd.score_stride[i] % 4 == 0 and odd.score_stride[i] >= zha.tree_layout(cfg_deep(capacity=32768 + 4 * 4096 * 3 + 4)).node_cap[i]

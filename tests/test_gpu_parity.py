@@ -553,3 +553,73 @@ def test_route_is_deterministic(leaf_form):
     assert torch.equal(sc0.nan_to_num(), buf.score.nan_to_num())
     assert torch.equal(st0, buf.stats)
     assert torch.equal(out0, out)
+
+
+SPLIT_CASES = [
+    # name, leaf form, n_tokens, p, keys repeat with period 4096 (exact score ties)
+    ("weights-ragged", "weights", (1 << 19) - 1003, 0.95, False),
+    ("weights-keep-all", "weights", 1 << 19, 1.0, False),
+    ("mean-ties", "mean", 1 << 19, 0.9, True),
+    ("mean-ties-small-p", "mean", (1 << 19) - 64, 0.05, True),
+]
+
+
+@pytest.mark.parametrize("name,leaf_form,N,p,repeat", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_split_select_is_bit_identical(name, leaf_form, N, p, repeat):
+    """With few queries and many candidates a level's selection may run
+    split over several workgroups per query; it must reach exactly what the
+    one-workgroup kernel reaches on the same score rows (bits, statistics)."""
+    _say(f"split select {name}")
+    cap = 1 << 19
+    cfg = zha.ZhaConfig(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=5, dtype="bf16",
+                        capacity=cap, leaf_form=leaf_form)
+    T = 1
+    rl = zha.route_layout(cfg, T)
+    assert int(rl.workspace_bytes) > int(rl.workspace_min_bytes)
+    K = torch.empty(1, 2, cap, 128, dtype=torch.bfloat16)
+    Q = torch.empty(1, 2, 4, T, 128, dtype=torch.bfloat16)
+    ref = torch.empty(2, 16, 128)
+    for h in range(2):
+        k, _, r, q = W.random_cache(cap, 128, 16, "bf16", seed=71 + h, n_queries=4, segment_len=16)
+        if repeat:
+            k = k[:4096].repeat(cap // 4096, 1)
+        q[::2] = (1.5 * k[[777, 300001]].float()).to(torch.bfloat16)  # two needle queries per head
+        K[0, h], ref[h], Q[0, h, :, 0] = k, r, q
+    K, Q, ref = K.cuda(), Q.cuda(), ref.cuda()
+    tree = zha.alloc_tree(cfg)
+    zha.build(cfg, K, ref, tree, N)
+    weights = leaf_form == "weights"
+    bufs = []
+    for split in (True, False):
+        buf = zha.alloc_route(cfg, T, logits=weights, split_select=split)
+        zha.route(cfg, tree, N, Q, T, p, buf, K=K)
+        bufs.append(buf)
+    torch.cuda.synchronize()
+    sizes = O.level_sizes(N, cfg.chunk, cfg.levels)
+    n_cut = 0
+    for lv in range(1, cfg.levels + 1):
+        i = lv - 1
+        nw, st = int(rl.words[i]), int(rl.score_stride[i])
+        for qi in range(int(rl.n_queries)):
+            rows = []
+            for b in bufs:
+                w0 = int(rl.sel_offset[i]) + qi * nw
+                s0 = int(rl.score_offset[i]) + qi * st
+                rows.append((b.sel[w0 : w0 + nw].cpu(), b.score[s0 : s0 + sizes[i]].cpu()))
+            assert torch.equal(rows[0][1].view(torch.int32), rows[1][1].view(torch.int32)), (lv, qi, "scores")
+            assert torch.equal(rows[0][0], rows[1][0]), (lv, qi, "bits")
+            # the kept set is a prefix of the candidates ordered by score
+            # descending, then id ascending (ties at the cut go to lower ids)
+            sc = rows[0][1].numpy()
+            kept = zha.unpack_bits(rows[0][0], sizes[i]).numpy()
+            cand = np.nonzero(np.isfinite(sc))[0]
+            order = cand[np.lexsort((cand, -sc[cand]))]
+            ks = kept[order].astype(np.int8)
+            assert not kept[np.isinf(sc)].any(), (lv, qi, "kept a non-candidate")
+            assert ks.sum() >= 1 and np.all(ks[: ks.sum()] == 1), (lv, qi, "kept set is not a prefix")
+        ra, rb = zha.stats_records(bufs[0], lv), zha.stats_records(bufs[1], lv)
+        for qi, (a, b) in enumerate(zip(ra, rb)):
+            assert bytes(a) == bytes(b), (lv, qi, "stats")
+            n_cut += a.cut_id != 2**31 - 1
+    if repeat and p < 1.0:
+        assert n_cut > 0, "no level split its ties at the cut"

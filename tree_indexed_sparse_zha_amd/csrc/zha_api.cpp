@@ -325,7 +325,10 @@ int zha_get_route_layout(const zha_config* cfg, int32_t T, zha_route_layout* out
   out->stats_total = ss;
   // per level, query and score tile: candidate key range and count, written
   // by the score kernel and reduced by the select kernel
-  out->workspace_bytes = align256(kr_total(cfg, tl, out->n_queries, nullptr));
+  // (the select kernels' split form uses the bytes after them)
+  out->workspace_min_bytes = align256(kr_total(cfg, tl, out->n_queries, nullptr));
+  out->workspace_bytes =
+      out->workspace_min_bytes + align256(zha::select_split_bytes(out->n_queries, tl.node_cap[0]));
   if (cfg->leaf_form == ZHA_LEAF_WEIGHTS) {
     const int64_t QC = (int64_t)cfg->q_per_kv * T;
     out->logits_floats = (int64_t)cfg->batch * cfg->n_kv_heads * cdiv(QC, 16) *
@@ -398,7 +401,7 @@ static int do_route(const zha_config* cfg, const void* tree, int64_t n_tokens, c
   zha_route_layout rl;
   zha_get_route_layout(cfg, T, &rl);
   if ((rc = check_ptr16(ws, "ws"))) return rc;
-  if (ws_bytes < rl.workspace_bytes) return fail(ZHA_ERR_CAPACITY, "workspace too small");
+  if (ws_bytes < rl.workspace_min_bytes) return fail(ZHA_ERR_CAPACITY, "workspace too small");
   zha_tree_layout tl;
   fill_tree_layout(cfg, &tl);
   int64_t n[ZHA_MAX_LEVELS];
@@ -410,6 +413,9 @@ static int do_route(const zha_config* cfg, const void* tree, int64_t n_tokens, c
   uint32_t* keyrange = static_cast<uint32_t*>(ws);
   int64_t kr_off[ZHA_MAX_LEVELS];
   const int64_t kr_bytes = kr_total(cfg, tl, rl.n_queries, kr_off);
+  void* split = rl.workspace_bytes > rl.workspace_min_bytes && ws_bytes >= rl.workspace_bytes
+                    ? static_cast<void*>(static_cast<char*>(ws) + rl.workspace_min_bytes)
+                    : nullptr;
   if (cfg->kv_dtype != ZHA_BF16) {
     // the fp32 score kernel accumulates its single slot per query with atomics
     hipError_t e = zha::launch_route_init(keyrange, kr_bytes / 16, pr);
@@ -479,6 +485,7 @@ static int do_route(const zha_config* cfg, const void* tree, int64_t n_tokens, c
     se.stats = stats + rl.stats_offset[l];
     se.p = pl[l];
     se.keep_all = pl[l] >= 1.0f;
+    se.split = split;
     hipError_t e = zha::launch_route_level(sa, se, cfg->kv_dtype, caches, l + 1, pr);
     if (e != hipSuccess) return hip_fail(e, "route launch");
   }

@@ -730,24 +730,63 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_cached(AttendArgs A) {
   write_partial<D, QG>(A, red, cache, qg0, nq, tile);
 }
 
-template <int D>
-__global__ __launch_bounds__(D) void k_combine(AttendArgs A) {
+// Merges the per-tile partial results of one query: S slices of D threads,
+// slice s folding tiles s, s + S, ... with a running max (two tiles in flight
+// per step), then slice 0 merging the S slice states in slice order, so the
+// result does not depend on timing.
+template <int D, int S>
+__global__ __launch_bounds__(D * S) void k_combine(AttendArgs A) {
   const int64_t q = blockIdx.x;
-  const int d = threadIdx.x;
-  const float* base = A.partial + q * A.n_tiles * (D + 2);
+  const int d = threadIdx.x % D, sl = threadIdx.x / D;
+  const int64_t nt = A.n_tiles;
+  const float* base = A.partial + q * nt * (D + 2);
+  float m = kNegInf, l = 0.f, o = 0.f;
+  auto fold = [&](float mt, float lt, float ot) {
+    if (mt == kNegInf) return;
+    if (mt > m) {
+      const float f = __expf(m - mt);  // 0 while m is -inf
+      l = l * f + lt;
+      o = o * f + ot;
+      m = mt;
+    } else {
+      const float f = __expf(mt - m);
+      l += f * lt;
+      o += f * ot;
+    }
+  };
+  int64_t t = sl;
+  for (; t + S < nt; t += 2 * S) {
+    const float* a = base + t * (D + 2);
+    const float* b = a + S * (D + 2);
+    const float ma = a[0], la = a[1], oa = a[2 + d];
+    const float mb = b[0], lb = b[1], ob = b[2 + d];
+    fold(ma, la, oa);
+    fold(mb, lb, ob);
+  }
+  if (t < nt) {
+    const float* a = base + t * (D + 2);
+    fold(a[0], a[1], a[2 + d]);
+  }
+  __shared__ float sm[S], sls[S], so[S][D];
+  if (d == 0) {
+    sm[sl] = m;
+    sls[sl] = l;
+  }
+  so[sl][d] = o;
+  __syncthreads();
+  if (sl != 0) return;
   float M = kNegInf;
-  for (int64_t t = 0; t < A.n_tiles; ++t) M = fmaxf(M, base[t * (D + 2)]);
-  float L = 0.f, o = 0.f;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, sm[s]);
+  float L = 0.f, O = 0.f;
   if (M != kNegInf) {
-    for (int64_t t = 0; t < A.n_tiles; ++t) {
-      const float mt = base[t * (D + 2)];
-      if (mt == kNegInf) continue;
-      const float f = __expf(mt - M);
-      L += f * base[t * (D + 2) + 1];
-      o += f * base[t * (D + 2) + 2 + d];
+    for (int s = 0; s < S; ++s) {
+      if (sm[s] == kNegInf) continue;
+      const float f = __expf(sm[s] - M);
+      L += f * sls[s];
+      O += f * so[s][d];
     }
   }
-  A.out[q * D + d] = L > 0.f ? o / L : 0.f;
+  A.out[q * D + d] = L > 0.f ? O / L : 0.f;
   if (d == 0 && A.lse) A.lse[q] = L > 0.f ? M + __logf(L) : kNegInf;
 }
 
@@ -806,9 +845,9 @@ hipError_t launch_attend(const AttendArgs& a, int dtype, int n_caches, Prof& pro
   if (e != hipSuccess) return e;
   prof.begin(ZHA_K_COMBINE, 0);
   if (a.D == 128)
-    hipLaunchKernelGGL(k_combine<128>, dim3((unsigned)n_queries), dim3(128), 0, s, a);
+    hipLaunchKernelGGL((k_combine<128, 8>), dim3((unsigned)n_queries), dim3(1024), 0, s, a);
   else
-    hipLaunchKernelGGL(k_combine<64>, dim3((unsigned)n_queries), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((k_combine<64, 16>), dim3((unsigned)n_queries), dim3(1024), 0, s, a);
   prof.end();
   return hipGetLastError();
 }

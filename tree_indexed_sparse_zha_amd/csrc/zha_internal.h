@@ -126,7 +126,21 @@ struct SelectArgs {
   void* stats;         // zha_select_stats[n_queries]
   float p;
   int keep_all;
+  void* split;      // split-select workspace (select_split_bytes), or null
+  int64_t split_S;  // workgroups per query in the split form (set at launch)
 };
+
+// Split select: per query a state record, and per (query, segment) a slot of
+// 2048 histogram bins plus five words; used for at most kSelSplitQueries
+// queries when at least two segments of kSelSplitNodes candidates each fit
+// within kSelSplitBlocks workgroups.
+constexpr int64_t kSelStateBytes = 128;
+constexpr int64_t kSelSlotU64 = 2056;
+constexpr int64_t kSelSplitBlocks = 2048;
+constexpr int64_t kSelSplitNodes = 32768;
+constexpr int64_t kSelSplitQueries = 64;
+int select_segments(int64_t n_queries, int64_t n_nodes);
+int64_t select_split_bytes(int64_t n_queries, int64_t max_nodes);
 
 struct AttendArgs {
   const void* Q;

@@ -19,13 +19,16 @@
 // and v_mfma_f32_16x16x32_bf16 yields all R x 16 plane dot products.  Nodes
 // whose parent no query kept are skipped without touching their bytes.
 //
-// Select design.  One workgroup per query.  Masses are fixed-point integers
+// Select design.  One workgroup per query, or, for levels with few queries
+// and many candidates, a chain of kernels that spreads each query's row over
+// several workgroups with the same arithmetic.  Masses are fixed-point integers
 // round(exp(s - max) * 2^shift) so every sum is exact and order-independent
 // (deterministic without float atomics).  The cut is found by a radix select
 // on the order key of the score (digits of up to 11 bits below the
 // candidates' common key prefix) over mass-weighted histograms in LDS, then
 // ties at the cut key are resolved by node id.  The kept set is written as a
 // bitset.
+#include <algorithm>
 #include <climits>
 
 #include "zha_device.h"
@@ -46,8 +49,6 @@ struct SelStats {  // mirrors zha_select_stats
 };
 static_assert(sizeof(SelStats) == 40, "stats layout");
 
-// Folds one wave's candidates (flag c, key k per lane) into a query's
-// [max key, min key, count] record.
 // Candidate key range and count of one score tile for one query, reduced
 // over the wave's lanes and stored (plain store, no atomics) into the
 // tile's slot; the select kernel reduces the slots.  Every tile writes its
@@ -639,163 +640,195 @@ __device__ int find_bin(const unsigned long long* hist, int nbins, unsigned long
 // highest bit where the largest and smallest key differ, so the digits
 // (11 bits at most, from the top down) start below that common prefix: every
 // histogram then spreads over the candidates' actual range instead of piling
-// into the few bins a narrow score range occupies.
-__global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs A) {
+// into the few bins a narrow score range occupies.  The steps below serve
+// both the one-workgroup-per-query kernel and the split form, where S
+// workgroups share a query's row.
+
+// Candidate key range and count of query q, from the score tiles' slots.
+__device__ void reduce_slots(const SelectArgs& A, int64_t q, uint32_t* kmax_o, uint32_t* kmin_o,
+                             unsigned long long* n_o) {
   const int tid = threadIdx.x;
-  const int64_t q = blockIdx.x;
-  const float* row = A.score + q * A.score_stride;  // 16-byte aligned rows
-  const float4* row4 = reinterpret_cast<const float4*>(row);
-  const int64_t n = A.n_nodes;
-  const int64_t n4 = (n + 3) / 4;
-  uint32_t* srow = A.sel + q * A.words;
-  SelStats* st = reinterpret_cast<SelStats*>(A.stats) + q;
-  const int64_t nwords = (n + 31) / 32;
-
-  __shared__ unsigned long long hist[2048];
-  __shared__ unsigned long long red[kSelThreads];
-  __shared__ int sh_bin;
-  __shared__ unsigned long long sh_above;
-  __shared__ int sh_cut;
-
-  // Visits every candidate score of the row (index, score, key): float4
-  // loads, two in flight per thread.
-  auto for_each = [&](auto&& fn) {
-    for (int64_t b = tid; b < n4; b += 2 * kSelThreads) {
-      const float4 v0 = row4[b];
-      const float4 v1 = b + kSelThreads < n4 ? row4[b + kSelThreads] : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
-      const float a[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int64_t i = (c < 4 ? b : b + kSelThreads) * 4 + (c & 3);
-        if (i < n && a[c] > kNegInf) fn(i, a[c], order_key(a[c]));
-      }
-    }
-  };
-
-  // candidate key range and count: reduce the score tiles' slots
   uint32_t kmax = 0u, kmin = 0xffffffffu;
   unsigned long long ncand = 0ull;
-  {
-    const uint4* kr = reinterpret_cast<const uint4*>(A.keyrange) + q * A.kr_slots;
-    for (int64_t i = tid; i < A.kr_used; i += kSelThreads) {
-      const uint4 v = kr[i];
-      kmax = max(kmax, v.x);
-      kmin = min(kmin, v.y);
-      ncand += v.z;
-    }
-    for (int o = 1; o < 64; o <<= 1) {
-      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
-      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
-      ncand += __shfl_xor(ncand, o);
-    }
-    __shared__ uint32_t rmax[kSelThreads / 64], rmin[kSelThreads / 64];
-    __shared__ unsigned long long rcnt[kSelThreads / 64];
-    if ((tid & 63) == 0) {
-      rmax[tid >> 6] = kmax;
-      rmin[tid >> 6] = kmin;
-      rcnt[tid >> 6] = ncand;
-    }
-    __syncthreads();
-    kmax = 0u;
-    kmin = 0xffffffffu;
-    ncand = 0ull;
-    for (int w = 0; w < kSelThreads / 64; ++w) {
-      kmax = max(kmax, rmax[w]);
-      kmin = min(kmin, rmin[w]);
-      ncand += rcnt[w];
-    }
+  const uint4* kr = reinterpret_cast<const uint4*>(A.keyrange) + q * A.kr_slots;
+  for (int64_t i = tid; i < A.kr_used; i += kSelThreads) {
+    const uint4 v = kr[i];
+    kmax = max(kmax, v.x);
+    kmin = min(kmin, v.y);
+    ncand += v.z;
   }
-  if (ncand == 0) {
-    for (int64_t w = tid; w < nwords; w += kSelThreads) srow[w] = 0u;
-    if (tid == 0) {
-      SelStats s0 = {kNegInf, 0, 0, 0u, 0, 0, 0ull, 0ull};
-      *st = s0;
-    }
-    return;
+  for (int o = 1; o < 64; o <<= 1) {
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+    ncand += __shfl_xor(ncand, o);
   }
-  const float mx = key_to_float(kmax);
+  __shared__ uint32_t rmax[kSelThreads / 64], rmin[kSelThreads / 64];
+  __shared__ unsigned long long rcnt[kSelThreads / 64];
+  if ((tid & 63) == 0) {
+    rmax[tid >> 6] = kmax;
+    rmin[tid >> 6] = kmin;
+    rcnt[tid >> 6] = ncand;
+  }
+  __syncthreads();
+  kmax = 0u;
+  kmin = 0xffffffffu;
+  ncand = 0ull;
+  for (int w = 0; w < kSelThreads / 64; ++w) {
+    kmax = max(kmax, rmax[w]);
+    kmin = min(kmin, rmin[w]);
+    ncand += rcnt[w];
+  }
+  __syncthreads();
+  *kmax_o = kmax;
+  *kmin_o = kmin;
+  *n_o = ncand;
+}
+
+// Fixed-point setting of a row of n candidates (masses below 2^62 / n, so
+// the total fits in 63 bits) and the start of the digit passes.
+struct SelSetup {
+  double scale;
+  float mx;
+  int shift;
+  uint32_t want;  // key bits above the first digit
+  int lo;         // the first digit ends at bit lo
+};
+__device__ SelSetup sel_setup(uint32_t kmax, uint32_t kmin, int64_t n) {
+  SelSetup s;
+  s.mx = key_to_float(kmax);
   int lg = 0;
   while ((1ll << lg) < n) ++lg;
-  const int shift = 62 - lg;
-  const double scale = ldexp(1.0, shift);
-
-  // digit passes; the first one also sums the total mass M
+  s.shift = 62 - lg;
+  s.scale = ldexp(1.0, s.shift);
   const int hb = kmax == kmin ? 0 : 32 - __clz(kmax ^ kmin);  // low bits that differ
-  uint32_t want = hb >= 32 ? 0u : (kmax >> hb);              // bits above the current digit
-  int lo = hb;
-  unsigned long long M = 0, P = 0, above = 0, h_tau = 0;
-  bool first = true;
-  uint32_t tau = 0u;
-  int cut_id = INT_MAX;
-  do {
-    const int w = lo < 11 ? lo : 11;
-    const int nb = 1 << w;
-    const int top = lo;  // bits [top, 32) must equal `want`
-    lo -= w;
-    for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0ull;
-    __syncthreads();
-    unsigned long long part = 0;
-    const bool fst = first;
-    for_each([&](int64_t i, float s, uint32_t k) {
-      const bool match = top >= 32 || (k >> top) == want;
-      if (!fst && !match) return;
-      const unsigned long long mm = fixed_mass(s, mx, scale);
-      if (fst) part += mm;
-      if (match && w > 0) atomicAdd(&hist[(k >> lo) & (uint32_t)(nb - 1)], mm);
-    });
-    __syncthreads();
-    if (first) {
-      M = block_sum_u64(part, red);
-      first = false;
-      if (A.keep_all) break;
-      P = (unsigned long long)ceil((double)A.p * (double)M);
-      if (P < 1ull) P = 1ull;
-      if (P > M) P = M;
-      if (w == 0) {  // every candidate has the same key
-        want = kmax;
-        h_tau = M;
-        break;
-      }
-    }
-    const int bsel = find_bin(hist, nb, P, &above, red, &sh_bin, &sh_above);
-    want = (w >= 32 ? 0u : (want << w)) | (uint32_t)bsel;
-    h_tau = hist[bsel];
-    __syncthreads();
-  } while (lo > 0);
+  s.want = hb >= 32 ? 0u : (kmax >> hb);
+  s.lo = hb;
+  return s;
+}
 
-  if (!A.keep_all) {
-    tau = want;
-    // ties at tau all carry the same mass
-    const unsigned long long m_tau = fixed_mass(key_to_float(tau), mx, scale);
-    const unsigned long long n_tau = m_tau ? h_tau / m_tau : 0ull;
-    const unsigned long long k_tie = m_tau ? (P - above + m_tau - 1ull) / m_tau : n_tau;
-    if (k_tie < n_tau) {
-      // the k_tie-th smallest id among the ties is the last one kept
-      unsigned long long need = k_tie;
-      if (tid == 0) sh_cut = INT_MAX;
-      __syncthreads();
-      for (int64_t base = 0; base < n; base += kSelThreads) {
-        const int64_t i = base + tid;
-        const bool tie = i < n && row[i] > kNegInf && order_key(row[i]) == tau;
-        const int c = __syncthreads_count(tie);
-        if ((unsigned long long)c >= need) {
-          red[tid] = tie ? 1ull : 0ull;
-          __syncthreads();
-          unsigned long long before = 0;
-          for (int t = 0; t < tid; ++t) before += red[t];
-          if (tie && before + 1ull == need) sh_cut = (int)(i + 1);
-          __syncthreads();
-          break;
-        }
-        need -= (unsigned long long)c;
-      }
-      cut_id = sh_cut;
+// Visits every candidate score of float4 range [b0, b1) of a row (index,
+// score, key): float4 loads, two in flight per thread.
+template <typename F>
+__device__ __forceinline__ void visit_row(const float4* row4, int64_t n, int64_t b0, int64_t b1, F&& fn) {
+  for (int64_t b = b0 + threadIdx.x; b < b1; b += 2 * kSelThreads) {
+    const float4 v0 = row4[b];
+    const float4 v1 = b + kSelThreads < b1 ? row4[b + kSelThreads] : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+    const float a[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int64_t i = (c < 4 ? b : b + kSelThreads) * 4 + (c & 3);
+      if (i < n && a[c] > kNegInf) fn(i, a[c], order_key(a[c]));
     }
   }
+}
 
-  // bitset of kept candidates: one word (8 float4 loads) per thread step
-  unsigned long long kept = 0, kmass = 0;
-  for (int64_t w = tid; w < nwords; w += kSelThreads) {
+// One digit pass over float4 range [b0, b1): adds into the LDS histogram
+// `hist` the mass of each candidate whose key bits [top, 32) equal `want`,
+// binned by its bits [lo, lo + w); on the first pass returns this thread's
+// share of the total mass of every candidate.
+__device__ unsigned long long digit_pass(const float4* row4, int64_t n, int64_t b0, int64_t b1, bool first,
+                                         int top, int lo, int w, uint32_t want, float mx, double scale,
+                                         unsigned long long* hist) {
+  unsigned long long part = 0;
+  const uint32_t mask = (uint32_t)((1 << w) - 1);
+  visit_row(row4, n, b0, b1, [&](int64_t, float s, uint32_t k) {
+    const bool match = top >= 32 || (k >> top) == want;
+    if (!first && !match) return;
+    const unsigned long long mm = fixed_mass(s, mx, scale);
+    if (first) part += mm;
+    if (match && w > 0) atomicAdd(&hist[(k >> lo) & mask], mm);
+  });
+  return part;
+}
+
+// With the cut key tau found (mass `above` strictly above it, h_tau at it):
+// ties at tau all carry the same mass; returns how many of them are kept
+// (the smallest ids) when only some are needed to reach P, else 0 (all
+// kept).
+__device__ __forceinline__ unsigned long long ties_needed(uint32_t tau, unsigned long long P,
+                                                          unsigned long long above, unsigned long long h_tau,
+                                                          float mx, double scale) {
+  const unsigned long long m_tau = fixed_mass(key_to_float(tau), mx, scale);
+  const unsigned long long n_tau = m_tau ? h_tau / m_tau : 0ull;
+  const unsigned long long k_tie = m_tau ? (P - above + m_tau - 1ull) / m_tau : n_tau;
+  return k_tie < n_tau ? k_tie : 0ull;
+}
+
+// Is candidate i of the row a tie at key tau?
+__device__ __forceinline__ bool is_tie(const float* row, int64_t i, int64_t i1, uint32_t tau) {
+  if (i >= i1) return false;
+  const float s = row[i];
+  return s > kNegInf && order_key(s) == tau;
+}
+
+// Ties at tau in [i0, i1) of a row, counted by the workgroup.
+__device__ unsigned long long count_ties(const float* row, int64_t i0, int64_t i1, uint32_t tau,
+                                         unsigned long long* red) {
+  unsigned long long c = 0;
+  for (int64_t i = i0 + threadIdx.x; i < i1; i += kSelThreads) c += is_tie(row, i, i1, tau) ? 1ull : 0ull;
+  return block_sum_u64(c, red);
+}
+
+// One past the id of the need-th tie at tau (need >= 1) in [i0, i1), or
+// INT_MAX when the range holds fewer.  The range is walked in steps of 8
+// consecutive candidates per thread; the step that reaches `need` is
+// resolved with a workgroup prefix sum of the threads' tie counts.
+__device__ int tie_find(const float* row, int64_t i0, int64_t i1, uint32_t tau, unsigned long long need) {
+  constexpr int PER = 8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ int sh_cut;
+  __shared__ uint32_t wsum[kSelThreads / 64];
+  if (tid == 0) sh_cut = INT_MAX;
+  __syncthreads();
+  for (int64_t base = i0; base < i1; base += (int64_t)kSelThreads * PER) {
+    const int64_t a = base + (int64_t)tid * PER;
+    uint32_t bits = 0u;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) bits |= is_tie(row, a + e, i1, tau) ? 1u << e : 0u;
+    const uint32_t c = __popc(bits);
+    uint32_t x = c;  // inclusive prefix over the wave
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    uint64_t before = x - c, total = 0;
+    for (int w = 0; w < kSelThreads / 64; ++w) {
+      const uint32_t v = wsum[w];
+      if (w < wave) before += v;
+      total += v;
+    }
+    if (total >= need) {
+      if (before < need && need <= before + c) {
+        uint32_t left = (uint32_t)(need - before);  // the left-th set bit of this thread's mask
+        for (int e = 0; e < PER; ++e)
+          if ((bits >> e) & 1u) {
+            if (--left == 0u) {
+              sh_cut = (int)(a + e + 1);
+              break;
+            }
+          }
+      }
+      __syncthreads();
+      break;
+    }
+    need -= total;
+    __syncthreads();  // wsum is rewritten by the next step
+  }
+  const int cut = sh_cut;
+  __syncthreads();
+  return cut;
+}
+
+// Bitset words [w0, w1) of the kept candidates (key above tau, or at tau
+// with id below cut_id): one word (8 float4 loads) per thread step; adds this
+// thread's kept count and kept mass.
+__device__ void write_bits(const float4* row4, int64_t n, int64_t w0, int64_t w1, uint32_t tau, int cut_id,
+                           float mx, double scale, uint32_t* srow, unsigned long long* kept,
+                           unsigned long long* kmass) {
+  const int64_t n4 = (n + 3) / 4;
+  for (int64_t w = w0 + threadIdx.x; w < w1; w += kSelThreads) {
     uint32_t bits = 0u;
     float4 v[8];
 #pragma unroll
@@ -815,14 +848,99 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs A) {
           const uint32_t k = order_key(s);
           if (k > tau || (k == tau && i < (int64_t)cut_id)) {
             bits |= 1u << bb;
-            kmass += fixed_mass(s, mx, scale);
+            *kmass += fixed_mass(s, mx, scale);
           }
         }
       }
     }
     srow[w] = bits;
-    kept += __popc(bits);
+    *kept += __popc(bits);
   }
+}
+
+__device__ __forceinline__ unsigned long long p_target(float p, unsigned long long M) {
+  unsigned long long P = (unsigned long long)ceil((double)p * (double)M);
+  if (P < 1ull) P = 1ull;
+  if (P > M) P = M;
+  return P;
+}
+
+// One workgroup per query.
+__global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs A) {
+  const int tid = threadIdx.x;
+  const int64_t q = blockIdx.x;
+  const float* row = A.score + q * A.score_stride;  // 16-byte aligned rows
+  const float4* row4 = reinterpret_cast<const float4*>(row);
+  const int64_t n = A.n_nodes;
+  const int64_t n4 = (n + 3) / 4;
+  uint32_t* srow = A.sel + q * A.words;
+  SelStats* st = reinterpret_cast<SelStats*>(A.stats) + q;
+  const int64_t nwords = (n + 31) / 32;
+
+  __shared__ unsigned long long hist[2048];
+  __shared__ unsigned long long red[kSelThreads];
+  __shared__ int sh_bin;
+  __shared__ unsigned long long sh_above;
+
+  uint32_t kmax, kmin;
+  unsigned long long ncand;
+  reduce_slots(A, q, &kmax, &kmin, &ncand);
+  if (ncand == 0) {
+    for (int64_t w = tid; w < nwords; w += kSelThreads) srow[w] = 0u;
+    if (tid == 0) {
+      SelStats s0 = {kNegInf, 0, 0, 0u, 0, 0, 0ull, 0ull};
+      *st = s0;
+    }
+    return;
+  }
+  const SelSetup su = sel_setup(kmax, kmin, n);
+  const float mx = su.mx;
+  const double scale = su.scale;
+
+  // digit passes; the first one also sums the total mass M
+  uint32_t want = su.want;
+  int lo = su.lo;
+  unsigned long long M = 0, P = 0, above = 0, h_tau = 0;
+  bool first = true;
+  uint32_t tau = 0u;
+  int cut_id = INT_MAX;
+  bool found = false;
+  do {
+    const int w = lo < 11 ? lo : 11;
+    const int nb = 1 << w;
+    const int top = lo;  // bits [top, 32) must equal `want`
+    lo -= w;
+    for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0ull;
+    __syncthreads();
+    const unsigned long long part = digit_pass(row4, n, 0, n4, first, top, lo, w, want, mx, scale, hist);
+    __syncthreads();
+    if (first) {
+      M = block_sum_u64(part, red);
+      first = false;
+      if (A.keep_all) break;
+      P = p_target(A.p, M);
+      if (w == 0) {  // every candidate has the same key
+        want = kmax;
+        h_tau = M;
+        found = true;
+        break;
+      }
+    }
+    const int bsel = find_bin(hist, nb, P, &above, red, &sh_bin, &sh_above);
+    want = (w >= 32 ? 0u : (want << w)) | (uint32_t)bsel;
+    h_tau = hist[bsel];
+    __syncthreads();
+    found = lo == 0;
+  } while (!found);
+
+  if (!A.keep_all) {
+    tau = want;
+    const unsigned long long need = ties_needed(tau, P, above, h_tau, mx, scale);
+    if (need) cut_id = tie_find(row, 0, n, tau, need);
+  }
+
+  unsigned long long kept = 0, kmass = 0;
+  write_bits(row4, n, 0, nwords, tau, cut_id, mx, scale, srow, &kept, &kmass);
   const unsigned long long nk = block_sum_u64(kept, red);
   const unsigned long long km = block_sum_u64(kmass, red);
   if (tid == 0) {
@@ -832,14 +950,274 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs A) {
     s1.n_kept = (int32_t)nk;
     s1.cut_key = tau;
     s1.cut_id = cut_id;
-    s1.shift = shift;
+    s1.shift = su.shift;
     s1.mass_total = M;
     s1.mass_kept = km;
     *st = s1;
   }
 }
 
+// Split form: S workgroups per query, each on its share of the row's words,
+// for levels with few queries and many candidates.  The per-query state and
+// the segments' histograms live in the route workspace; a chain of kernels
+// (set-up; per digit a histogram kernel over the segments and a find kernel
+// per query; the ties at the cut key counted per segment; the bitset over
+// the segments, where the segment holding the last kept tie finds it; the
+// statistics) takes the same steps as k_select and reaches bit-identical
+// results, since every sum is of integers.
+struct SelState {
+  double scale;
+  unsigned long long ncand, M, P, above, h_tau;
+  float mx;
+  int32_t shift;
+  unsigned long long need_tie;  // ties at tau to keep (smallest ids first), 0: all
+  uint32_t kmax, want, tau;
+  int32_t lo, first, phase;  // phase 0: digit passes, 1: cut key known, 2: no candidate
+};
+static_assert(sizeof(SelState) <= kSelStateBytes, "select state size");
+
+__device__ __forceinline__ SelState* sel_state(const SelectArgs& A, int64_t q) {
+  return reinterpret_cast<SelState*>(static_cast<char*>(A.split) + q * kSelStateBytes);
+}
+// Segment slot of (query, segment): histogram bins, then the first pass's
+// mass, the kept count, the kept mass, the ties at the cut key and the
+// segment's cut id.
+constexpr int kSlotM = 2048, kSlotKept = 2049, kSlotKMass = 2050, kSlotTies = 2051, kSlotCut = 2052;
+__device__ __forceinline__ unsigned long long* sel_slot(const SelectArgs& A, int64_t n_queries, int64_t q,
+                                                         int64_t s) {
+  return reinterpret_cast<unsigned long long*>(static_cast<char*>(A.split) + n_queries * kSelStateBytes) +
+         (q * A.split_S + s) * kSelSlotU64;
+}
+__device__ __forceinline__ void segment_words(const SelectArgs& A, int64_t s, int64_t* w0, int64_t* w1) {
+  const int64_t nwords = (A.n_nodes + 31) / 32;
+  const int64_t per = (nwords + A.split_S - 1) / A.split_S;
+  *w0 = min(s * per, nwords);
+  *w1 = min(*w0 + per, nwords);
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_select_setup(SelectArgs A) {
+  const int64_t q = blockIdx.x;
+  uint32_t kmax, kmin;
+  unsigned long long ncand;
+  reduce_slots(A, q, &kmax, &kmin, &ncand);
+  if (threadIdx.x != 0) return;
+  SelState s;
+  s.scale = 0.0;
+  s.ncand = ncand;
+  s.M = s.P = s.above = s.h_tau = 0ull;
+  s.mx = kNegInf;
+  s.shift = 0;
+  s.kmax = kmax;
+  s.want = 0u;
+  s.tau = 0u;
+  s.need_tie = 0ull;
+  s.lo = 0;
+  s.first = 1;
+  s.phase = ncand == 0 ? 2 : 0;
+  if (ncand != 0) {
+    const SelSetup su = sel_setup(kmax, kmin, A.n_nodes);
+    s.scale = su.scale;
+    s.mx = su.mx;
+    s.shift = su.shift;
+    s.want = su.want;
+    s.lo = su.lo;
+  }
+  *sel_state(A, q) = s;
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_select_hist(SelectArgs A) {
+  const int64_t seg = blockIdx.x, q = blockIdx.y;
+  const SelState s = *sel_state(A, q);
+  if (s.phase != 0) return;
+  __shared__ unsigned long long hist[2048];
+  __shared__ unsigned long long red[kSelThreads];
+  const int w = s.lo < 11 ? s.lo : 11;
+  const int nb = 1 << w;
+  const int64_t n = A.n_nodes;
+  const float4* row4 = reinterpret_cast<const float4*>(A.score + q * A.score_stride);
+  int64_t w0, w1;
+  segment_words(A, seg, &w0, &w1);
+  const int64_t b1 = min(w1 * 8, (n + 3) / 4);
+  for (int i = threadIdx.x; i < nb; i += kSelThreads) hist[i] = 0ull;
+  __syncthreads();
+  const unsigned long long part =
+      digit_pass(row4, n, w0 * 8, b1, s.first != 0, s.lo, s.lo - w, w, s.want, s.mx, s.scale, hist);
+  __syncthreads();
+  unsigned long long* out = sel_slot(A, gridDim.y, q, seg);
+  if (w > 0)
+    for (int i = threadIdx.x; i < nb; i += kSelThreads) out[i] = hist[i];
+  if (s.first) {
+    const unsigned long long m = block_sum_u64(part, red);
+    if (threadIdx.x == 0) out[kSlotM] = m;
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_select_find(SelectArgs A, int64_t n_queries) {
+  const int tid = threadIdx.x;
+  const int64_t q = blockIdx.x;
+  SelState s = *sel_state(A, q);
+  if (s.phase != 0) return;
+  __shared__ unsigned long long hist[2048];
+  __shared__ unsigned long long red[kSelThreads];
+  __shared__ int sh_bin;
+  __shared__ unsigned long long sh_above;
+  const int w = s.lo < 11 ? s.lo : 11;
+  const int nb = 1 << w;
+  bool found = false;
+  if (s.first) {
+    unsigned long long part = 0;
+    for (int64_t g = tid; g < A.split_S; g += kSelThreads) part += sel_slot(A, n_queries, q, g)[kSlotM];
+    s.M = block_sum_u64(part, red);
+    s.first = 0;
+    if (A.keep_all) {
+      s.phase = 1;
+      if (tid == 0) *sel_state(A, q) = s;
+      return;
+    }
+    s.P = p_target(A.p, s.M);
+    if (w == 0) {  // every candidate has the same key
+      s.want = s.kmax;
+      s.h_tau = s.M;
+      found = true;
+    }
+  }
+  if (!found) {
+    // bin i summed over the segments, 8 loads in flight per thread
+    const unsigned long long* slots = sel_slot(A, n_queries, q, 0);
+    const int64_t S = A.split_S;
+    for (int i = tid; i < nb; i += kSelThreads) {
+      unsigned long long h = 0;
+      int64_t g = 0;
+      for (; g + 8 <= S; g += 8) {
+        unsigned long long v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = slots[(g + u) * kSelSlotU64 + i];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) h += v[u];
+      }
+      for (; g < S; ++g) h += slots[g * kSelSlotU64 + i];
+      hist[i] = h;
+    }
+    __syncthreads();
+    const int bsel = find_bin(hist, nb, s.P, &s.above, red, &sh_bin, &sh_above);
+    s.want = (w >= 32 ? 0u : (s.want << w)) | (uint32_t)bsel;
+    s.h_tau = hist[bsel];
+    s.lo -= w;
+    __syncthreads();
+    found = s.lo == 0;
+  }
+  if (found) {
+    s.tau = s.want;
+    s.need_tie = ties_needed(s.tau, s.P, s.above, s.h_tau, s.mx, s.scale);
+    s.phase = 1;
+  }
+  if (tid == 0) *sel_state(A, q) = s;
+}
+
+// Ties at the cut key per segment, when only some of them are kept.
+__global__ __launch_bounds__(kSelThreads) void k_select_ties(SelectArgs A) {
+  const int64_t seg = blockIdx.x, q = blockIdx.y;
+  const SelState s = *sel_state(A, q);
+  if (s.phase != 1 || s.need_tie == 0ull) return;
+  __shared__ unsigned long long red[kSelThreads];
+  int64_t w0, w1;
+  segment_words(A, seg, &w0, &w1);
+  const unsigned long long c =
+      count_ties(A.score + q * A.score_stride, w0 * 32, min(w1 * 32, A.n_nodes), s.tau, red);
+  if (threadIdx.x == 0) sel_slot(A, gridDim.y, q, seg)[kSlotTies] = c;
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_select_bits(SelectArgs A) {
+  const int64_t seg = blockIdx.x, q = blockIdx.y;
+  const SelState s = *sel_state(A, q);
+  __shared__ unsigned long long red[kSelThreads];
+  int64_t w0, w1;
+  segment_words(A, seg, &w0, &w1);
+  uint32_t* srow = A.sel + q * A.words;
+  if (s.phase == 2) {
+    for (int64_t w = w0 + threadIdx.x; w < w1; w += kSelThreads) srow[w] = 0u;
+    return;
+  }
+  const float* row = A.score + q * A.score_stride;
+  unsigned long long* out = sel_slot(A, gridDim.y, q, seg);
+  // ties at the cut key kept in this segment: all while the segments before
+  // hold fewer than need_tie, none after; the segment that holds the
+  // need_tie-th one cuts inside and records its cut id
+  int cut = INT_MAX, cut_rec = INT_MAX;
+  if (s.phase == 1 && s.need_tie) {
+    unsigned long long before = 0;
+    for (int64_t g = threadIdx.x; g < seg; g += kSelThreads) before += sel_slot(A, gridDim.y, q, g)[kSlotTies];
+    before = block_sum_u64(before, red);
+    const unsigned long long mine = out[kSlotTies];
+    if (before >= s.need_tie) {
+      cut = 0;
+    } else if (s.need_tie - before <= mine) {
+      cut = tie_find(row, w0 * 32, min(w1 * 32, A.n_nodes), s.tau, s.need_tie - before);
+      cut_rec = cut;
+    }
+  }
+  unsigned long long kept = 0, kmass = 0;
+  write_bits(reinterpret_cast<const float4*>(row), A.n_nodes, w0, w1, A.keep_all ? 0u : s.tau, cut, s.mx, s.scale,
+             srow, &kept, &kmass);
+  const unsigned long long nk = block_sum_u64(kept, red);
+  const unsigned long long km = block_sum_u64(kmass, red);
+  if (threadIdx.x == 0) {
+    out[kSlotKept] = nk;
+    out[kSlotKMass] = km;
+    out[kSlotCut] = (unsigned long long)(uint32_t)cut_rec;
+  }
+}
+
+__global__ __launch_bounds__(64) void k_select_stats(SelectArgs A, int64_t n_queries) {
+  const int64_t q = blockIdx.x;
+  const SelState s = *sel_state(A, q);
+  SelStats* st = reinterpret_cast<SelStats*>(A.stats) + q;
+  if (s.phase == 2) {
+    if (threadIdx.x == 0) {
+      SelStats s0 = {kNegInf, 0, 0, 0u, 0, 0, 0ull, 0ull};
+      *st = s0;
+    }
+    return;
+  }
+  unsigned long long nk = 0, km = 0, cut = INT_MAX;
+  for (int64_t g = threadIdx.x; g < A.split_S; g += 64) {
+    const unsigned long long* slot = sel_slot(A, n_queries, q, g);
+    nk += slot[kSlotKept];
+    km += slot[kSlotKMass];
+    cut = min(cut, slot[kSlotCut]);  // at most one segment cuts inside its ties
+  }
+  for (int o = 1; o < 64; o <<= 1) {
+    nk += __shfl_xor(nk, o);
+    km += __shfl_xor(km, o);
+    cut = min(cut, (unsigned long long)__shfl_xor(cut, o));
+  }
+  if (threadIdx.x == 0) {
+    SelStats s1;
+    s1.max_score = s.mx;
+    s1.n_cand = (int32_t)s.ncand;
+    s1.n_kept = (int32_t)nk;
+    s1.cut_key = A.keep_all ? 0u : s.tau;
+    s1.cut_id = (int32_t)cut;
+    s1.shift = s.shift;
+    s1.mass_total = s.M;
+    s1.mass_kept = km;
+    *st = s1;
+  }
+}
+
 }  // namespace
+
+int select_segments(int64_t n_queries, int64_t n_nodes) {
+  if (n_queries <= 0 || n_queries > kSelSplitQueries) return 1;
+  const int64_t s = std::min<int64_t>(kSelSplitBlocks / n_queries, n_nodes / kSelSplitNodes);
+  return s >= 2 ? (int)std::min<int64_t>(s, 256) : 1;
+}
+
+int64_t select_split_bytes(int64_t n_queries, int64_t max_nodes) {
+  const int S = select_segments(n_queries, max_nodes);
+  if (S < 2) return 0;
+  return n_queries * kSelStateBytes + n_queries * S * kSelSlotU64 * 8;
+}
 
 int64_t route_kr_slots(int dtype, bool leaf_weights, int64_t node_cap, int C) {
   // one slot per score tile, plus one for the prefill spine score
@@ -939,7 +1317,20 @@ hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dty
     sel.kr_used += 1;
   }
   prof.begin(ZHA_K_SELECT, level);
-  hipLaunchKernelGGL(k_select, dim3((unsigned)n_queries), dim3(kSelThreads), 0, s, sel);
+  sel.split_S = sel.split ? select_segments(n_queries, sel.n_nodes) : 1;
+  if (sel.split_S < 2) {
+    hipLaunchKernelGGL(k_select, dim3((unsigned)n_queries), dim3(kSelThreads), 0, s, sel);
+  } else {
+    const dim3 segs((unsigned)sel.split_S, (unsigned)n_queries);
+    hipLaunchKernelGGL(k_select_setup, dim3((unsigned)n_queries), dim3(kSelThreads), 0, s, sel);
+    for (int pass = 0; pass < 3; ++pass) {  // 11-bit digits cover the 32-bit key in 3 passes
+      hipLaunchKernelGGL(k_select_hist, segs, dim3(kSelThreads), 0, s, sel);
+      hipLaunchKernelGGL(k_select_find, dim3((unsigned)n_queries), dim3(kSelThreads), 0, s, sel, n_queries);
+    }
+    hipLaunchKernelGGL(k_select_ties, segs, dim3(kSelThreads), 0, s, sel);
+    hipLaunchKernelGGL(k_select_bits, segs, dim3(kSelThreads), 0, s, sel);
+    hipLaunchKernelGGL(k_select_stats, dim3((unsigned)n_queries), dim3(64), 0, s, sel, n_queries);
+  }
   prof.end();
   return hipGetLastError();
 }

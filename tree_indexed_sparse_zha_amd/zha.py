@@ -85,6 +85,7 @@ class RouteLayout(ct.Structure):
         ("stats_total", ct.c_int64),
         ("workspace_bytes", ct.c_int64),
         ("logits_floats", ct.c_int64),
+        ("workspace_min_bytes", ct.c_int64),
     ]
 
 
@@ -321,10 +322,13 @@ class RouteBuffers:
     logits: Optional[torch.Tensor] = None  # level-1 attention logits (weights form)
 
 
-def alloc_route(cfg: ZhaConfig, T: int, device="cuda", logits: bool = False) -> RouteBuffers:
+def alloc_route(cfg: ZhaConfig, T: int, device="cuda", logits: bool = False, split_select: bool = True) -> RouteBuffers:
     """Route outputs; ``logits`` also allocates the level-1 logits buffer
-    (leaf-weights form) that zha_attend can read instead of the keys."""
+    (leaf-weights form) that zha_attend can read instead of the keys;
+    ``split_select=False`` gives the smallest workspace, which keeps every
+    level's selection at one workgroup per query."""
     rl = route_layout(cfg, T)
+    ws_bytes = int(rl.workspace_bytes) if split_select else int(rl.workspace_min_bytes)
     lg = None
     if logits and int(rl.logits_floats) > 0:
         lg = torch.empty(int(rl.logits_floats), dtype=torch.float32, device=device)
@@ -332,7 +336,7 @@ def alloc_route(cfg: ZhaConfig, T: int, device="cuda", logits: bool = False) -> 
         sel=torch.zeros(int(rl.sel_words_total), dtype=torch.int32, device=device),
         score=torch.empty(int(rl.score_floats_total), dtype=torch.float32, device=device),
         stats=torch.zeros(max(1, int(rl.stats_total)) * STATS_BYTES, dtype=torch.uint8, device=device),
-        ws=torch.empty(max(256, int(rl.workspace_bytes)), dtype=torch.uint8, device=device),
+        ws=torch.empty(max(256, ws_bytes), dtype=torch.uint8, device=device),
         layout=rl,
         logits=lg,
     )
