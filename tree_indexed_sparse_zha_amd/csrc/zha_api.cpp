@@ -180,6 +180,14 @@ int check_prof(zha_profile* prof) {
   return ZHA_OK;
 }
 
+// Trees built by k_build_mf: bf16 keys, chunk 4, leaf-weights form, g in
+// bf16, 3 or more levels (level-2 nodes from their 16 keys on the matrix
+// cores), R <= 16.
+static bool build_mf(const zha_config* c) {
+  return c->kv_dtype == ZHA_BF16 && c->chunk == 4 && c->leaf_form == ZHA_LEAF_WEIGHTS && c->g_dtype == ZHA_G_KV &&
+         c->levels >= 3 && c->levels <= 8 && c->n_ref <= 16;
+}
+
 int do_build(const zha_config* cfg, const void* K, const int64_t* ks, int64_t n_old, int64_t n_new,
              const float* ref, void* tree, zha_profile* prof, void* stream, bool append) {
   int rc = check_config(cfg);
@@ -223,7 +231,9 @@ int do_build(const zha_config* cfg, const void* K, const int64_t* ks, int64_t n_
   if (a.n_spans > 0x7fffffffll) return fail(ZHA_ERR_UNSUPPORTED, "too many spans");
   zha::Prof pr{prof, static_cast<hipStream_t>(stream)};
   a.top_level = cfg->levels;
-  if (append && a.n_spans <= 2 && tl.scratch_offset >= 0) {
+  a.mf = build_mf(cfg);
+  // the split's sub-span pass needs >= 3 levels of its own on the matrix-core path
+  if (append && a.n_spans <= 2 && tl.scratch_offset >= 0 && (!a.mf || cfg->levels >= 4)) {
     // few spans: build their children in parallel, then merge the top nodes
     zha::BuildArgs s1 = a;
     s1.top_level = cfg->levels - 1;

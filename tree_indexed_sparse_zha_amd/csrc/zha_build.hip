@@ -40,10 +40,11 @@ __device__ __forceinline__ void absorb(float& am, float& as, float* aacc, bool& 
     used = true;
     return;
   }
+  // explicit fused forms: every kernel that folds nodes rounds alike
   const float mn = fmaxf(am, mc);
   const float fa = __expf(am - mn), fc = __expf(mc - mn);
-  as = as * fa + sc * fc;
-  for (int v = 0; v < nv; ++v) aacc[v] = aacc[v] * fa + gc[v] * fc;
+  as = fmaf(as, fa, sc * fc);
+  for (int v = 0; v < nv; ++v) aacc[v] = fmaf(aacc[v], fa, gc[v] * fc);
   am = mn;
 }
 
@@ -458,6 +459,363 @@ __global__ __launch_bounds__(64 * W) void k_build_span(BuildArgs A) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core build (bf16 keys, C = 4, leaf-weights form, g in bf16, >= 3
+// levels).  Same node definitions as k_build_span, different work split:
+//
+//  * The 4 waves of a workgroup take the 4 level-2 nodes (16 keys each) of a
+//    64-key round of the span, in order.  A level-2 node is computed straight
+//    from its 16 keys: the weights P_ji = exp(z_ji - max_i z_ji) of the
+//    16 x 16 (plane, key) logits are the B operand and the keys the A operand
+//    of v_mfma_f32_16x16x4_f32, so g_j = (sum_i P_ji k_i) / (sum_i P_ji) is an
+//    fp32 matrix product (4 MFMAs of K = 4 keys per 16 values of d) instead
+//    of a VALU loop.  Lane (j, g) of a wave owns the 4 keys of leaf g for the
+//    leaf weights, supplies them as the K = 4 slice of the product, and
+//    receives d = 16b + 4g + i (b < D/16, i < 4) of g_j.
+//  * The level-3 node of the round is the ordered merge of those 4 fp32
+//    level-2 nodes (LSE of L, mass-weighted mean of g), and levels above
+//    fold their children in order in flash-style accumulators, as in
+//    k_build_span.  Above level 2 the 256 lanes of the workgroup split the
+//    R x D values of a node: lane (j, g) of wave w owns the D/16 values of d
+//    starting at (4w + g) D/16, so each lane keeps D/16 values per open level
+//    instead of D/4.  The dot r_j . g_j that c needs is summed over the
+//    waves in LDS, in wave order.
+//
+// Every node of level >= 3 is the in-order fold of its children's
+// (L, mass 1, fp32 mean g); the append split (sub-span pass, then the top
+// node from the stored fp32 children) therefore reproduces a fresh build bit
+// for bit when both of its passes also run here.
+template <int D, int NU>
+__global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
+  constexpr int PIECES = D / 8;  // 16-byte pieces of a bf16 key row
+  constexpr int NS = PIECES / 4;  // pieces per lane when staging K; z MFMA steps
+  constexpr int NB = D / 16;      // 16-wide d blocks of the level-2 product
+  constexpr int VPL = D / 16;     // values of d per lane above level 2
+  constexpr int KB = 16;
+  constexpr int KROW = PIECES + 1;  // padded LDS key row (uint4)
+  constexpr int GROW = D + 4;       // padded LDS child row (floats)
+  constexpr int NUR = NU > 0 ? NU : 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane & 15, g = lane >> 4;
+  const TreeGeom& geo = A.geo;
+  const int R = geo.R;
+  const int cache = blockIdx.y;
+  const int b = cache / geo.H, h = cache % geo.H;
+  const int64_t span = A.first_span + blockIdx.x;
+  const int64_t t0 = span * A.span_tokens;
+  const int64_t tend = min(t0 + A.span_tokens, (A.n_tokens / 4) * 4);
+  if (t0 >= tend) return;  // uniform over the workgroup
+  const float isd = A.inv_sqrt_d;
+  const int top = A.top_level;
+  const int d0 = VPL * (4 * wave + g);  // this lane's first d above level 2
+
+  __shared__ uint4 Ks[4][KB * KROW];
+  __shared__ float zs[4][16][KB + 1];
+  __shared__ float chG[4][16][GROW];
+  __shared__ float chL[4][16];
+  __shared__ float refL[16][GROW];
+  __shared__ float dotp[kMaxLevels][4][16];
+
+  for (int i = threadIdx.x; i < 16 * D; i += 256) {
+    const int jr = i / D, d = i % D;
+    refL[jr][d] = jr < R ? A.ref[((int64_t)h * R + jr) * D + d] : 0.f;
+  }
+  __syncthreads();
+  float rp[VPL];
+#pragma unroll
+  for (int e = 0; e < VPL; ++e) rp[e] = refL[j][d0 + e];
+
+  // node writers above level 2: this lane's D/16 values of g (rounded to
+  // bf16), the wave's share of r . g into dotp[slot]; L and c are stored by
+  // finish() once every wave's share is in
+  auto put_node = [&](int lvl, int64_t node, float L, const float* gv, int slot) {
+    uint32_t wd[VPL / 2];
+    float gr[VPL];
+#pragma unroll
+    for (int e = 0; e < VPL / 2; ++e) {
+      const uint32_t lo = bf16_bits(gv[2 * e]), hi = bf16_bits(gv[2 * e + 1]);
+      wd[e] = lo | (hi << 16);
+      gr[2 * e] = __uint_as_float(lo << 16);
+      gr[2 * e + 1] = __uint_as_float(hi << 16);
+    }
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) dot = fmaf(rp[e], gr[e], dot);
+    dot += __shfl_xor(dot, 16);
+    dot += __shfl_xor(dot, 32);
+    if (g == 0) dotp[slot][wave][j] = dot;
+    if (j < R) {
+      const int64_t nidx = (int64_t)cache * geo.node_cap[lvl - 1] + node;
+      char* gb = A.tree + geo.g_off[lvl - 1] + nidx * R * D * 2 + ((int64_t)(d0 / 8) * R + j) * 16 + (d0 % 8) * 2;
+      if constexpr (VPL == 8)
+        st16(gb, make_uint4(wd[0], wd[1], wd[2], wd[3]));
+      else
+        *reinterpret_cast<uint2*>(gb) = make_uint2(wd[0], wd[1]);
+      if (lvl == top && A.top_scratch && !A.merge_top) {
+        // sub-span pass: the top node is a child of a split top node; keep it
+        // in fp32 as (L, mass 1, mean g) for the merge pass
+        const int64_t top_span = t0 / (A.span_tokens * 4);
+        float* rec = A.top_scratch +
+                     (((int64_t)cache * 2 + (top_span - A.scratch_span0)) * 4 + (t0 / A.span_tokens) % 4) *
+                         ((int64_t)R * (D + 2));
+#pragma unroll
+        for (int e = 0; e < VPL; ++e) rec[2 * R + (int64_t)j * D + d0 + e] = gv[e];
+        if (wave == 0 && g == 0) {
+          rec[j] = L;
+          rec[R + j] = 1.f;
+        }
+      }
+    }
+  };
+  auto finish = [&](int lvl, int64_t node, float L, int slot) {
+    if (wave == 0 && g == 0 && j < R) {
+      const float dot = ((dotp[slot][0][j] + dotp[slot][1][j]) + dotp[slot][2][j]) + dotp[slot][3][j];
+      const int64_t nidx = (int64_t)cache * geo.node_cap[lvl - 1] + node;
+      reinterpret_cast<float*>(A.tree + geo.L_off[lvl - 1])[nidx * R + j] = L;
+      reinterpret_cast<float*>(A.tree + geo.c_off[lvl - 1])[nidx * R + j] = L - dot * isd;
+    }
+  };
+
+  if (A.merge_top) {
+    // merge pass of a split top span: fold the 4 stored fp32 children in order
+    const int64_t sub_tokens = A.span_tokens / 4;
+    const int jj = j < R ? j : 0;
+    float mm = 0.f, ss = 0.f, gg[VPL];
+    bool u = false;
+    for (int c = 0; c < 4; ++c) {
+      if (t0 + c * sub_tokens >= tend) break;
+      const float* rec = A.top_scratch +
+                         (((int64_t)cache * 2 + (span - A.scratch_span0)) * 4 + c) * ((int64_t)R * (D + 2));
+      float gc[VPL];
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) gc[e] = rec[2 * R + (int64_t)jj * D + d0 + e];
+      absorb(mm, ss, gg, u, rec[jj], rec[R + jj], gc, VPL);
+    }
+    const float L = mm + __logf(ss);
+    const float inv = 1.f / ss;
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) gg[e] *= inv;
+    put_node(top, span, L, gg, 0);
+    __syncthreads();
+    finish(top, span, L, 0);
+    return;
+  }
+
+  // reference rows as bf16 MFMA A operands of the logits (exact: ref holds
+  // bf16 values)
+  bf16x8 afr[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    float rr[8], dummy[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rr[e] = refL[j][(4 * s + g) * 8 + e];
+    afr[s] = as_bf16x8(pack(rr, dummy, bf16_t()));
+  }
+
+  const bf16_t* Kc = reinterpret_cast<const bf16_t*>(A.K) + (int64_t)b * A.sb + (int64_t)h * A.sh;
+  const int64_t nkeys = tend - t0;
+  const int64_t nrounds = (nkeys + 63) / 64;
+  auto block_keys = [&](int64_t r) -> int {
+    const int64_t s0 = 64 * r + 16 * wave;
+    return (int)max<int64_t>(0, min<int64_t>(16, nkeys - s0));
+  };
+  auto load_block = [&](int64_t pos, int nk, uint4* regs) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int pi = lane + 64 * u;
+      const int key = pi / PIECES, pc = pi % PIECES;
+      regs[u] = key < nk ? ld16(Kc + (pos + key) * A.st + pc * 8) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  uint4 pre[NS];
+  {
+    const int nk0 = block_keys(0);
+    if (nk0 > 0) load_block(t0 + 16 * wave, nk0, pre);
+  }
+  const uint16_t* Ks16 = reinterpret_cast<const uint16_t*>(Ks[wave]);
+
+  // open accumulators of levels 4 .. 3 + NU
+  float um[NUR], us[NUR], ua[NUR][VPL];
+  bool uu[NUR];
+#pragma unroll
+  for (int a = 0; a < NUR; ++a) uu[a] = false;
+
+  for (int64_t r = 0; r < nrounds; ++r) {
+    const int nk = block_keys(r);
+    const int64_t kb0 = t0 + 64 * r + 16 * wave;  // this wave's level-2 node
+    if (nk > 0) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        const int pi = lane + 64 * u;
+        Ks[wave][(pi / PIECES) * KROW + pi % PIECES] = pre[u];
+      }
+    }
+    wave_sync();
+    {
+      const int nnk = block_keys(r + 1);
+      if (nnk > 0) load_block(kb0 + 64, nnk, pre);
+    }
+    if (nk > 0) {
+      // z[j][i] = r_j . k_i / sqrt(d)
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[s], as_bf16x8(Ks[wave][(lane & 15) * KROW + 4 * s + g]),
+                                                      acc, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zs[wave][4 * g + i][lane & 15] = acc[i] * isd;
+      wave_sync();
+
+      // leaf g of this lane: keys 4g .. 4g+3 of the block
+      const bool leaf = 4 * g < nk;
+      float z[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) z[s] = zs[wave][j][4 * g + s];
+      const float m1 = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+      float e[4], s1 = 0.f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        e[s] = __expf(z[s] - m1);
+        s1 += e[s];
+      }
+      if (leaf && j < R) {
+        // weights form: w_ji = exp(z_ji - L_j), c_j = L_j - sum_i w_ji z_ji
+        const float L1 = m1 + __logf(s1);
+        const float inv1 = 1.f / s1;
+        float wv[4], wz = 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          wv[s] = e[s] * inv1;
+          wz += wv[s] * z[s];
+        }
+        const int64_t nidx = (int64_t)cache * geo.node_cap[0] + kb0 / 4 + g;
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(A.tree + geo.g_off[0]) + (nidx * R + j) * 4) =
+            make_float4(wv[0], wv[1], wv[2], wv[3]);
+        reinterpret_cast<float*>(A.tree + geo.L_off[0])[nidx * R + j] = L1;
+        reinterpret_cast<float*>(A.tree + geo.c_off[0])[nidx * R + j] = L1 - wz;
+      }
+
+      // level-2 node: weights relative to the block max over its keys
+      float m2 = leaf ? m1 : kNegInf;
+      m2 = fmaxf(m2, __shfl_xor(m2, 16));
+      m2 = fmaxf(m2, __shfl_xor(m2, 32));
+      float P[4], ps = 0.f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        P[s] = leaf ? __expf(z[s] - m2) : 0.f;
+        ps += P[s];
+      }
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);
+      const float L2 = m2 + __logf(ps);
+      const float inv2 = 1.f / ps;
+      // g^T[d][j] = sum over keys k[key][d] P[j][key]: A = keys (row d = 16b +
+      // lane % 16, k = key 4g + s), B = P (k = key 4g + s, column j)
+      f32x4 G[NB];
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) {
+        G[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int d = 16 * blk + (lane & 15);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const float kv = __uint_as_float((uint32_t)Ks16[((4 * g + s) * KROW + d / 8) * 8 + d % 8] << 16);
+          G[blk] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, P[s], G[blk], 0, 0, 0);
+        }
+      }
+      // emit the level-2 node (lane: d = 16b + 4g + i of plane j) and keep
+      // its fp32 form for the level-3 merge
+      float dot = 0.f;
+      uint2 pk[NB];
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) {
+        float gv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gv[i] = G[blk][i] * inv2;
+        *reinterpret_cast<float4*>(&chG[wave][j][16 * blk + 4 * g]) = make_float4(gv[0], gv[1], gv[2], gv[3]);
+        const float4 rv = *reinterpret_cast<const float4*>(&refL[j][16 * blk + 4 * g]);
+        const uint32_t b0 = bf16_bits(gv[0]), b1 = bf16_bits(gv[1]), b2 = bf16_bits(gv[2]), b3 = bf16_bits(gv[3]);
+        pk[blk] = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+        dot = fmaf(rv.x, __uint_as_float(b0 << 16), dot);
+        dot = fmaf(rv.y, __uint_as_float(b1 << 16), dot);
+        dot = fmaf(rv.z, __uint_as_float(b2 << 16), dot);
+        dot = fmaf(rv.w, __uint_as_float(b3 << 16), dot);
+      }
+      dot += __shfl_xor(dot, 16);
+      dot += __shfl_xor(dot, 32);
+      if (g == 0) chL[wave][j] = L2;
+      if (j < R) {
+        const int64_t nidx = (int64_t)cache * geo.node_cap[1] + kb0 / 16;
+        char* gb = A.tree + geo.g_off[1] + nidx * R * D * 2;
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk)
+          *reinterpret_cast<uint2*>(gb + ((int64_t)(2 * blk + g / 2) * R + j) * 16 + (g % 2) * 8) = pk[blk];
+        if (g == 0) {
+          reinterpret_cast<float*>(A.tree + geo.L_off[1])[nidx * R + j] = L2;
+          reinterpret_cast<float*>(A.tree + geo.c_off[1])[nidx * R + j] = L2 - dot * isd;
+        }
+      }
+    }
+    __syncthreads();  // the round's level-2 nodes are in LDS
+
+    // level-3 node of the round: ordered fold of its level-2 children
+    const int nch = (int)min<int64_t>(4, (nkeys - 64 * r + 15) / 16);
+    float m3 = 0.f, s3 = 0.f, a3[VPL];
+    bool u3 = false;
+    for (int c = 0; c < nch; ++c) {
+      float gc[VPL];
+#pragma unroll
+      for (int e = 0; e < VPL; e += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(&chG[c][j][d0 + e]);
+        gc[e] = v.x;
+        gc[e + 1] = v.y;
+        gc[e + 2] = v.z;
+        gc[e + 3] = v.w;
+      }
+      absorb(m3, s3, a3, u3, chL[c][j], 1.f, gc, VPL);
+    }
+    const float L3 = m3 + __logf(s3);
+    {
+      const float inv = 1.f / s3;
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) a3[e] *= inv;
+    }
+    const int64_t rel = min<int64_t>(64 * (r + 1), nkeys);
+    const int64_t end = t0 + rel;
+    const bool last = rel == nkeys;
+    put_node(3, (t0 + 64 * r) / 64, L3, a3, 0);
+    float pL[NUR];
+    int64_t pnode[NUR];
+    bool pend[NUR];
+#pragma unroll
+    for (int a = 0; a < NUR; ++a) pend[a] = false;
+    if constexpr (NU > 0) absorb(um[0], us[0], ua[0], uu[0], L3, 1.f, a3, VPL);
+    // close every level >= 4 whose span ends here, bottom-up
+#pragma unroll
+    for (int a = 0; a < NU; ++a) {
+      const int lvl = 4 + a;
+      const int64_t sp = geo.span_len[lvl];
+      if (uu[a] && ((rel % sp) == 0 || last)) {
+        const float L = um[a] + __logf(us[a]);
+        const float inv = 1.f / us[a];
+        float gv[VPL];
+#pragma unroll
+        for (int e = 0; e < VPL; ++e) gv[e] = ua[a][e] * inv;
+        put_node(lvl, (end - 1) / sp, L, gv, a + 1);
+        pend[a] = true;
+        pL[a] = L;
+        pnode[a] = (end - 1) / sp;
+        if (a + 1 < NU) absorb(um[a + 1], us[a + 1], ua[a + 1], uu[a + 1], L, 1.f, gv, VPL);
+        uu[a] = false;
+      }
+    }
+    __syncthreads();  // every wave's share of r . g is in
+    finish(3, (t0 + 64 * r) / 64, L3, 0);
+#pragma unroll
+    for (int a = 0; a < NU; ++a)
+      if (pend[a]) finish(4 + a, pnode[a], pL[a], a + 1);
+  }
+}
+
 // Waves per top span: W = min(C, 4) when the top node has children built by
 // the waves (C <= 16 and at least 2 levels); W divides C, so a wave's share
 // is a whole number of the top node's children.
@@ -507,6 +865,21 @@ hipError_t dispatch_leaf(const BuildArgs& a, dim3 grid, hipStream_t s) {
   }
 }
 
+template <int D>
+hipError_t dispatch_mf(const BuildArgs& a, dim3 grid, hipStream_t s) {
+  const int nu = a.merge_top ? 0 : a.top_level - 3;
+  switch (nu) {
+    case 0: hipLaunchKernelGGL((k_build_mf<D, 0>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_build_mf<D, 1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_build_mf<D, 2>), grid, dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_build_mf<D, 3>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_build_mf<D, 4>), grid, dim3(256), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((k_build_mf<D, 5>), grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_build(const BuildArgs& a, int dtype, Prof& prof) {
@@ -515,7 +888,9 @@ hipError_t launch_build(const BuildArgs& a, int dtype, Prof& prof) {
   hipStream_t s = prof.s;
   hipError_t e;
   prof.begin(ZHA_K_BUILD, 0);
-  if (dtype == 1)
+  if (a.mf && !a.spine) {
+    e = a.geo.D == 128 ? dispatch_mf<128>(a, grid, s) : dispatch_mf<64>(a, grid, s);
+  } else if (dtype == 1)
     e = a.geo.D == 128 ? dispatch_leaf<bf16_t, 128>(a, grid, s) : dispatch_leaf<bf16_t, 64>(a, grid, s);
   else
     e = a.geo.D == 128 ? dispatch_leaf<float, 128>(a, grid, s) : dispatch_leaf<float, 64>(a, grid, s);

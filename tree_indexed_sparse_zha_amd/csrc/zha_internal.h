@@ -75,6 +75,7 @@ struct BuildArgs {
   float* top_scratch;  // [caches][2 spans][C children][R][D + 2] fp32, or nullptr
   int64_t scratch_span0;
   int merge_top;
+  int mf;  // matrix-core build (k_build_mf) for the tree; the spine keeps k_build_span
 };
 
 // Byte offset of the spine record of (cache, state k, level lvl >= 2).
