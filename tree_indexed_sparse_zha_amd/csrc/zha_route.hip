@@ -389,7 +389,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 #pragma unroll
     for (int i = 0; i < 4; ++i) zz[i] = z[i] * A.inv_sqrt_d;
     const int64_t quad = (k0 + g * 16) / 4 + kg;
-    if (A.logits && qn < nq && quad < A.nquads) {
+    if (!Q4 && A.logits && qn < nq && quad < A.nquads) {
       // keep the attention logits of these 4 keys for query qn (zha_attend
       // reads them): row [quad][key][query], queries innermost
       float* lp = A.logits + (((int64_t)cache * gridDim.z + blockIdx.z) * A.nquads + quad) * 4 * A.QW + qn;
@@ -417,6 +417,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     // lanes (query u, part, chunk cx) over the wave's 64 / C chunks; quads of
     // dead groups hold stale LDS data, discarded by the candidate bit
     wave_sync();
+    if (A.logits) {
+      // the wave's 16 quads as rows [quad][key][query]: lane (quad qq, key
+      // kk) gathers the 4 queries' logits of its key and stores them as one
+      // 16-byte piece, so the wave writes 1 KiB with one coalesced store
+      // (quads of groups without a candidate are not written)
+      const int qq = lane >> 2, kk = lane & 3;
+      const unsigned long long gm = ((1ull << (16 / C)) - 1ull) << ((wave * GPW + (qq >> 2)) * 16 / C);
+      const int64_t quad = (k0 + wave * 64) / 4 + qq;
+      if ((anybits & gm) != 0ull && quad < A.nquads) {
+        const float* zr = reinterpret_cast<const float*>(&zl[wave][qq][0]);
+        *reinterpret_cast<float4*>(A.logits + ((((int64_t)cache * gridDim.z + blockIdx.z) * A.nquads + quad) * 4 + kk) * 4) =
+            make_float4(zr[kk], zr[4 + kk], zr[8 + kk], zr[12 + kk]);
+      }
+    }
     const int u = lane & 3, part = (lane >> 2) % PARTS, cx = lane / (4 * PARTS);
     const int x = wave * (64 / C) + cx;
     const float4 zv = zl[wave][cx * PARTS + part][u];
