@@ -194,6 +194,12 @@ BUILD_CASES = [
     ("deep-bf16-fp8", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=6, dtype="bf16", capacity=9000, g_dtype="fp8"), 8192 + 4 * 37 + 2),
     ("deep-bf16-weights-fp8", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=6, dtype="bf16", capacity=9000, leaf_form="weights", g_dtype="fp8"), 8192 + 4 * 37 + 2),
     ("c8-bf16-d64-fp8", dict(batch=1, n_kv_heads=1, q_per_kv=2, head_dim=64, n_ref=5, chunk=8, levels=3, dtype="bf16", capacity=5000, g_dtype="fp8"), 4096 + 8 * 7 + 3),
+    # matrix-core build (bf16, chunk 4, weights form): d = 64 with 3 levels (no level above the round's),
+    # 4 levels (one open level, append split), 8 levels (five open levels, a partial second top span)
+    ("mf-d64-r5-l3", dict(batch=2, n_kv_heads=1, q_per_kv=2, head_dim=64, n_ref=5, chunk=4, levels=3, dtype="bf16", capacity=3000, leaf_form="weights"), 2048 + 4 * 37 + 2),
+    ("mf-d128-r7-l4", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=7, chunk=4, levels=4, dtype="bf16", capacity=5000, leaf_form="weights"), 4096 + 64 * 3 + 16 * 2 + 4 * 3 + 1),
+    ("mf-mean-d64-r16-l4", dict(batch=1, n_kv_heads=2, q_per_kv=2, head_dim=64, n_ref=16, chunk=4, levels=4, dtype="bf16", capacity=5000), 4096 + 64 * 2 + 4 * 5 + 3),
+    ("mf-d128-r3-l8", dict(batch=1, n_kv_heads=1, q_per_kv=1, head_dim=128, n_ref=3, chunk=4, levels=8, dtype="bf16", capacity=70000, leaf_form="weights"), 65536 + 4 * 100 + 1),
 ]
 APPEND_CASES = [c for c in BUILD_CASES if c[0] != "c1-f32"]
 
@@ -247,8 +253,9 @@ def check_tree(cfg, tree, K, ref, N):
                     check_fp8_level(lv, np64(got["g"][cache]), np64(got["scale"][cache]), lvl)
                 else:
                     mism = gg != lvl.ghat
-                    frac = mism.mean() if mism.size else 0.0
-                    assert frac <= 1e-3, f"level {lv}: {frac:.2e} of bf16 g differ"
+                    # at most 1e-3 of the values, and never fewer than 2 allowed (a level of a few
+                    # hundred values, such as an 8-level tree's top, may hold one boundary flip)
+                    assert mism.sum() <= max(2, 1e-3 * mism.size), f"level {lv}: {int(mism.sum())} of {mism.size} bf16 g differ"
                     if mism.any():
                         # A mismatch is a rounding-boundary flip: the GPU's fp32 value and the
                         # oracle's fp64 value round to neighbouring bf16 numbers.  Allowed: one

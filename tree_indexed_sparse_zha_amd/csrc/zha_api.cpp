@@ -180,12 +180,11 @@ int check_prof(zha_profile* prof) {
   return ZHA_OK;
 }
 
-// Trees built by k_build_mf: bf16 keys, chunk 4, leaf-weights form, g in
-// bf16, 3 or more levels (level-2 nodes from their 16 keys on the matrix
-// cores), R <= 16.
+// Trees built by k_build_mf: bf16 keys, chunk 4, g in bf16, 3 or more
+// levels (level-2 nodes from their 16 keys on the matrix cores), R <= 16.
 static bool build_mf(const zha_config* c) {
-  return c->kv_dtype == ZHA_BF16 && c->chunk == 4 && c->leaf_form == ZHA_LEAF_WEIGHTS && c->g_dtype == ZHA_G_KV &&
-         c->levels >= 3 && c->levels <= 8 && c->n_ref <= 16;
+  return c->kv_dtype == ZHA_BF16 && c->chunk == 4 && c->g_dtype == ZHA_G_KV && c->levels >= 3 && c->levels <= 8 &&
+         c->n_ref <= 16;
 }
 
 int do_build(const zha_config* cfg, const void* K, const int64_t* ks, int64_t n_old, int64_t n_new,

@@ -460,8 +460,7 @@ __global__ __launch_bounds__(64 * W) void k_build_span(BuildArgs A) {
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core build (bf16 keys, C = 4, leaf-weights form, g in bf16, >= 3
-// levels).  Same node definitions as k_build_span, different work split:
+// Matrix-core build (bf16 keys, C = 4, g in bf16, >= 3 levels).  Same node definitions as k_build_span, different work split:
 //
 //  * The 4 waves of a workgroup take the 4 level-2 nodes (16 keys each) of a
 //    64-key round of the span, in order.  A level-2 node is computed straight
@@ -470,8 +469,9 @@ __global__ __launch_bounds__(64 * W) void k_build_span(BuildArgs A) {
 //    of v_mfma_f32_16x16x4_f32, so g_j = (sum_i P_ji k_i) / (sum_i P_ji) is an
 //    fp32 matrix product (4 MFMAs of K = 4 keys per 16 values of d) instead
 //    of a VALU loop.  Lane (j, g) of a wave owns the 4 keys of leaf g for the
-//    leaf weights, supplies them as the K = 4 slice of the product, and
-//    receives d = 16b + 4g + i (b < D/16, i < 4) of g_j.
+//    leaf statistics, supplies them as the K = 4 slice of the product, and
+//    receives d = 16b + 4g + i (b < D/16, i < 4) of g_j.  In the mean form
+//    each leaf's g is one more such product over its own 4 keys.
 //  * The level-3 node of the round is the ordered merge of those 4 fp32
 //    level-2 nodes (LSE of L, mass-weighted mean of g), and levels above
 //    fold their children in order in flash-style accumulators, as in
@@ -678,7 +678,49 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
         e[s] = __expf(z[s] - m1);
         s1 += e[s];
       }
-      if (leaf && j < R) {
+      if (!geo.leaf_weights) {
+        // mean form: leaf l's g_j = sum_i w_ji k_i over its 4 keys is one
+        // fp32 MFMA per 16 values of d (K = the leaf's keys; lane (j, g)
+        // supplies key 4l + g, whose weight it recomputes from leaf l's max
+        // and sum, shuffled from lane (j, l))
+        const float L1 = m1 + __logf(s1);
+        const float inv1 = 1.f / s1;
+#pragma unroll
+        for (int l = 0; l < 4; ++l) {
+          if (4 * l >= nk) break;  // uniform: leaves are complete
+          const int src = (lane & 15) + 16 * l;
+          const float ml = __shfl(m1, src), il = __shfl(inv1, src), Ll = __shfl(L1, src);
+          const float wb = __expf(zs[wave][j][4 * l + g] - ml) * il;
+          float dot = 0.f;
+          uint2 pk[NB];
+#pragma unroll
+          for (int blk = 0; blk < NB; ++blk) {
+            const int d = 16 * blk + (lane & 15);
+            const float kv = __uint_as_float((uint32_t)Ks16[((4 * l + g) * KROW + d / 8) * 8 + d % 8] << 16);
+            const f32x4 Gl = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, wb, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            const float4 rv = *reinterpret_cast<const float4*>(&refL[j][16 * blk + 4 * g]);
+            const uint32_t b0 = bf16_bits(Gl[0]), b1 = bf16_bits(Gl[1]), b2 = bf16_bits(Gl[2]), b3 = bf16_bits(Gl[3]);
+            pk[blk] = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+            dot = fmaf(rv.x, __uint_as_float(b0 << 16), dot);
+            dot = fmaf(rv.y, __uint_as_float(b1 << 16), dot);
+            dot = fmaf(rv.z, __uint_as_float(b2 << 16), dot);
+            dot = fmaf(rv.w, __uint_as_float(b3 << 16), dot);
+          }
+          dot += __shfl_xor(dot, 16);
+          dot += __shfl_xor(dot, 32);
+          if (j < R) {
+            const int64_t nidx = (int64_t)cache * geo.node_cap[0] + kb0 / 4 + l;
+            char* gb = A.tree + geo.g_off[0] + nidx * R * D * 2;
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk)
+              *reinterpret_cast<uint2*>(gb + ((int64_t)(2 * blk + g / 2) * R + j) * 16 + (g % 2) * 8) = pk[blk];
+            if (g == 0) {
+              reinterpret_cast<float*>(A.tree + geo.L_off[0])[nidx * R + j] = Ll;
+              reinterpret_cast<float*>(A.tree + geo.c_off[0])[nidx * R + j] = Ll - dot * isd;
+            }
+          }
+        }
+      } else if (leaf && j < R) {
         // weights form: w_ji = exp(z_ji - L_j), c_j = L_j - sum_i w_ji z_ji
         const float L1 = m1 + __logf(s1);
         const float inv1 = 1.f / s1;
