@@ -199,6 +199,8 @@ BUILD_CASES = [
     ("mf-d64-r5-l3", dict(batch=2, n_kv_heads=1, q_per_kv=2, head_dim=64, n_ref=5, chunk=4, levels=3, dtype="bf16", capacity=3000, leaf_form="weights"), 2048 + 4 * 37 + 2),
     ("mf-d128-r7-l4", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=7, chunk=4, levels=4, dtype="bf16", capacity=5000, leaf_form="weights"), 4096 + 64 * 3 + 16 * 2 + 4 * 3 + 1),
     ("mf-mean-d64-r16-l4", dict(batch=1, n_kv_heads=2, q_per_kv=2, head_dim=64, n_ref=16, chunk=4, levels=4, dtype="bf16", capacity=5000), 4096 + 64 * 2 + 4 * 5 + 3),
+    ("mf-c8-d64-r16-l2", dict(batch=1, n_kv_heads=2, q_per_kv=2, head_dim=64, n_ref=16, chunk=8, levels=2, dtype="bf16", capacity=3000, leaf_form="weights"), 2048 + 64 + 8 * 3 + 5),
+    ("mf-c8-mean-d128-r5-l5", dict(batch=1, n_kv_heads=1, q_per_kv=4, head_dim=128, n_ref=5, chunk=8, levels=5, dtype="bf16", capacity=40000), 32768 + 8 * 100 + 3),
     ("mf-d128-r3-l8", dict(batch=1, n_kv_heads=1, q_per_kv=1, head_dim=128, n_ref=3, chunk=4, levels=8, dtype="bf16", capacity=70000, leaf_form="weights"), 65536 + 4 * 100 + 1),
 ]
 APPEND_CASES = [c for c in BUILD_CASES if c[0] != "c1-f32"]

@@ -180,11 +180,14 @@ int check_prof(zha_profile* prof) {
   return ZHA_OK;
 }
 
-// Trees built by k_build_mf: bf16 keys, chunk 4, g in bf16, 3 or more
-// levels (level-2 nodes from their 16 keys on the matrix cores), R <= 16.
+// Trees built by k_build_mf: bf16 keys, g in bf16, R <= 16, and a 64-key
+// round's node at a level of the tree: chunk 4 with 3..8 levels (the round's
+// node is level 3) or chunk 8 with 2..7 levels (level 2).
 static bool build_mf(const zha_config* c) {
-  return c->kv_dtype == ZHA_BF16 && c->chunk == 4 && c->g_dtype == ZHA_G_KV && c->levels >= 3 && c->levels <= 8 &&
-         c->n_ref <= 16;
+  if (c->kv_dtype != ZHA_BF16 || c->g_dtype != ZHA_G_KV || c->n_ref > 16) return false;
+  if (c->chunk == 4) return c->levels >= 3 && c->levels <= 8;
+  if (c->chunk == 8) return c->levels >= 2 && c->levels <= 7;
+  return false;
 }
 
 int do_build(const zha_config* cfg, const void* K, const int64_t* ks, int64_t n_old, int64_t n_new,
@@ -231,8 +234,9 @@ int do_build(const zha_config* cfg, const void* K, const int64_t* ks, int64_t n_
   zha::Prof pr{prof, static_cast<hipStream_t>(stream)};
   a.top_level = cfg->levels;
   a.mf = build_mf(cfg);
-  // the split's sub-span pass needs >= 3 levels of its own on the matrix-core path
-  if (append && a.n_spans <= 2 && tl.scratch_offset >= 0 && (!a.mf || cfg->levels >= 4)) {
+  // on the matrix-core path the split's sub-span pass must itself reach the
+  // round's level (3 for chunk 4, 2 for chunk 8)
+  if (append && a.n_spans <= 2 && tl.scratch_offset >= 0 && (!a.mf || cfg->levels >= (C == 4 ? 4 : 3))) {
     // few spans: build their children in parallel, then merge the top nodes
     zha::BuildArgs s1 = a;
     s1.top_level = cfg->levels - 1;

@@ -485,8 +485,11 @@ __global__ __launch_bounds__(64 * W) void k_build_span(BuildArgs A) {
 // (L, mass 1, fp32 mean g); the append split (sub-span pass, then the top
 // node from the stored fp32 children) therefore reproduces a fresh build bit
 // for bit when both of its passes also run here.
-template <int D, int NU>
+template <int D, int NU, int C>
 __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
+  static_assert(C == 4 || C == 8, "chunk of 4 or 8 keys");
+  constexpr int RL = C == 4 ? 3 : 2;  // level of a round's node (64 keys)
+  constexpr int LPL = C / 4;          // lanes of one plane sharing a leaf
   constexpr int PIECES = D / 8;  // 16-byte pieces of a bf16 key row
   constexpr int NS = PIECES / 4;  // pieces per lane when staging K; z MFMA steps
   constexpr int NB = D / 16;      // 16-wide d blocks of the level-2 product
@@ -503,7 +506,7 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
   const int b = cache / geo.H, h = cache % geo.H;
   const int64_t span = A.first_span + blockIdx.x;
   const int64_t t0 = span * A.span_tokens;
-  const int64_t tend = min(t0 + A.span_tokens, (A.n_tokens / 4) * 4);
+  const int64_t tend = min(t0 + A.span_tokens, (A.n_tokens / C) * C);
   if (t0 >= tend) return;  // uniform over the workgroup
   const float isd = A.inv_sqrt_d;
   const int top = A.top_level;
@@ -554,9 +557,9 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
       if (lvl == top && A.top_scratch && !A.merge_top) {
         // sub-span pass: the top node is a child of a split top node; keep it
         // in fp32 as (L, mass 1, mean g) for the merge pass
-        const int64_t top_span = t0 / (A.span_tokens * 4);
+        const int64_t top_span = t0 / (A.span_tokens * C);
         float* rec = A.top_scratch +
-                     (((int64_t)cache * 2 + (top_span - A.scratch_span0)) * 4 + (t0 / A.span_tokens) % 4) *
+                     (((int64_t)cache * 2 + (top_span - A.scratch_span0)) * C + (t0 / A.span_tokens) % C) *
                          ((int64_t)R * (D + 2));
 #pragma unroll
         for (int e = 0; e < VPL; ++e) rec[2 * R + (int64_t)j * D + d0 + e] = gv[e];
@@ -577,15 +580,15 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
   };
 
   if (A.merge_top) {
-    // merge pass of a split top span: fold the 4 stored fp32 children in order
-    const int64_t sub_tokens = A.span_tokens / 4;
+    // merge pass of a split top span: fold the C stored fp32 children in order
+    const int64_t sub_tokens = A.span_tokens / C;
     const int jj = j < R ? j : 0;
     float mm = 0.f, ss = 0.f, gg[VPL];
     bool u = false;
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < C; ++c) {
       if (t0 + c * sub_tokens >= tend) break;
       const float* rec = A.top_scratch +
-                         (((int64_t)cache * 2 + (span - A.scratch_span0)) * 4 + c) * ((int64_t)R * (D + 2));
+                         (((int64_t)cache * 2 + (span - A.scratch_span0)) * C + c) * ((int64_t)R * (D + 2));
       float gc[VPL];
 #pragma unroll
       for (int e = 0; e < VPL; ++e) gc[e] = rec[2 * R + (int64_t)jj * D + d0 + e];
@@ -634,7 +637,7 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
   }
   const uint16_t* Ks16 = reinterpret_cast<const uint16_t*>(Ks[wave]);
 
-  // open accumulators of levels 4 .. 3 + NU
+  // open accumulators of levels RL + 1 .. RL + NU
   float um[NUR], us[NUR], ua[NUR][VPL];
   bool uu[NUR];
 #pragma unroll
@@ -642,7 +645,7 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
 
   for (int64_t r = 0; r < nrounds; ++r) {
     const int nk = block_keys(r);
-    const int64_t kb0 = t0 + 64 * r + 16 * wave;  // this wave's level-2 node
+    const int64_t kb0 = t0 + 64 * r + 16 * wave;  // this wave's 16-key block
     if (nk > 0) {
 #pragma unroll
       for (int u = 0; u < NS; ++u) {
@@ -666,38 +669,48 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
       for (int i = 0; i < 4; ++i) zs[wave][4 * g + i][lane & 15] = acc[i] * isd;
       wave_sync();
 
-      // leaf g of this lane: keys 4g .. 4g+3 of the block
+      // this lane's keys 4g .. 4g+3 of the block: leaf g (C = 4), or half of
+      // leaf g / 2 (C = 8, statistics shared with lane g ^ 1)
       const bool leaf = 4 * g < nk;
       float z[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) z[s] = zs[wave][j][4 * g + s];
-      const float m1 = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+      float m1 = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+      if constexpr (C == 8) m1 = fmaxf(m1, __shfl_xor(m1, 16));
       float e[4], s1 = 0.f;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         e[s] = __expf(z[s] - m1);
         s1 += e[s];
       }
+      if constexpr (C == 8) s1 += __shfl_xor(s1, 16);
       if (!geo.leaf_weights) {
-        // mean form: leaf l's g_j = sum_i w_ji k_i over its 4 keys is one
-        // fp32 MFMA per 16 values of d (K = the leaf's keys; lane (j, g)
-        // supplies key 4l + g, whose weight it recomputes from leaf l's max
-        // and sum, shuffled from lane (j, l))
+        // mean form: leaf l's g_j = sum_i w_ji k_i over its C keys is C / 4
+        // fp32 MFMAs per 16 values of d (K = 4 of the leaf's keys; lane (j, g)
+        // supplies keys Cl + 4s + g, whose weights it recomputes from leaf
+        // l's max and sum, shuffled from a lane of that leaf)
         const float L1 = m1 + __logf(s1);
         const float inv1 = 1.f / s1;
 #pragma unroll
-        for (int l = 0; l < 4; ++l) {
-          if (4 * l >= nk) break;  // uniform: leaves are complete
-          const int src = (lane & 15) + 16 * l;
+        for (int l = 0; l < 16 / C; ++l) {
+          if (C * l >= nk) break;  // uniform: leaves are complete
+          const int src = (lane & 15) + 16 * (l * LPL);
           const float ml = __shfl(m1, src), il = __shfl(inv1, src), Ll = __shfl(L1, src);
-          const float wb = __expf(zs[wave][j][4 * l + g] - ml) * il;
+          float wb[LPL];
+#pragma unroll
+          for (int s = 0; s < LPL; ++s) wb[s] = __expf(zs[wave][j][C * l + 4 * s + g] - ml) * il;
           float dot = 0.f;
           uint2 pk[NB];
 #pragma unroll
           for (int blk = 0; blk < NB; ++blk) {
             const int d = 16 * blk + (lane & 15);
-            const float kv = __uint_as_float((uint32_t)Ks16[((4 * l + g) * KROW + d / 8) * 8 + d % 8] << 16);
-            const f32x4 Gl = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, wb, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            f32x4 Gl = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < LPL; ++s) {
+              const float kv =
+                  __uint_as_float((uint32_t)Ks16[((C * l + 4 * s + g) * KROW + d / 8) * 8 + d % 8] << 16);
+              Gl = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, wb[s], Gl, 0, 0, 0);
+            }
             const float4 rv = *reinterpret_cast<const float4*>(&refL[j][16 * blk + 4 * g]);
             const uint32_t b0 = bf16_bits(Gl[0]), b1 = bf16_bits(Gl[1]), b2 = bf16_bits(Gl[2]), b3 = bf16_bits(Gl[3]);
             pk[blk] = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
@@ -709,7 +722,7 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
           dot += __shfl_xor(dot, 16);
           dot += __shfl_xor(dot, 32);
           if (j < R) {
-            const int64_t nidx = (int64_t)cache * geo.node_cap[0] + kb0 / 4 + l;
+            const int64_t nidx = (int64_t)cache * geo.node_cap[0] + kb0 / C + l;
             char* gb = A.tree + geo.g_off[0] + nidx * R * D * 2;
 #pragma unroll
             for (int blk = 0; blk < NB; ++blk)
@@ -720,7 +733,7 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
             }
           }
         }
-      } else if (leaf && j < R) {
+      } else {
         // weights form: w_ji = exp(z_ji - L_j), c_j = L_j - sum_i w_ji z_ji
         const float L1 = m1 + __logf(s1);
         const float inv1 = 1.f / s1;
@@ -730,14 +743,20 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
           wv[s] = e[s] * inv1;
           wz += wv[s] * z[s];
         }
-        const int64_t nidx = (int64_t)cache * geo.node_cap[0] + kb0 / 4 + g;
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(A.tree + geo.g_off[0]) + (nidx * R + j) * 4) =
-            make_float4(wv[0], wv[1], wv[2], wv[3]);
-        reinterpret_cast<float*>(A.tree + geo.L_off[0])[nidx * R + j] = L1;
-        reinterpret_cast<float*>(A.tree + geo.c_off[0])[nidx * R + j] = L1 - wz;
+        if constexpr (C == 8) wz += __shfl_xor(wz, 16);
+        if (leaf && j < R) {
+          const int64_t nidx = (int64_t)cache * geo.node_cap[0] + kb0 / C + g / LPL;
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(A.tree + geo.g_off[0]) + (nidx * R + j) * C +
+                                     4 * (g % LPL)) = make_float4(wv[0], wv[1], wv[2], wv[3]);
+          if (g % LPL == 0) {
+            reinterpret_cast<float*>(A.tree + geo.L_off[0])[nidx * R + j] = L1;
+            reinterpret_cast<float*>(A.tree + geo.c_off[0])[nidx * R + j] = L1 - wz;
+          }
+        }
       }
 
-      // level-2 node: weights relative to the block max over its keys
+      // the block's 16 keys: the level-2 node (C = 4) or a quarter of the
+      // round's level-2 node (C = 8); weights relative to the block max
       float m2 = leaf ? m1 : kNegInf;
       m2 = fmaxf(m2, __shfl_xor(m2, 16));
       m2 = fmaxf(m2, __shfl_xor(m2, 32));
@@ -764,8 +783,8 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
           G[blk] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, P[s], G[blk], 0, 0, 0);
         }
       }
-      // emit the level-2 node (lane: d = 16b + 4g + i of plane j) and keep
-      // its fp32 form for the level-3 merge
+      // keep the fp32 form (L, mean g) for the round's node and, when C = 4,
+      // emit it as the level-2 node (lane: d = 16b + 4g + i of plane j)
       float dot = 0.f;
       uint2 pk[NB];
 #pragma unroll
@@ -785,7 +804,7 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
       dot += __shfl_xor(dot, 16);
       dot += __shfl_xor(dot, 32);
       if (g == 0) chL[wave][j] = L2;
-      if (j < R) {
+      if (C == 4 && j < R) {
         const int64_t nidx = (int64_t)cache * geo.node_cap[1] + kb0 / 16;
         char* gb = A.tree + geo.g_off[1] + nidx * R * D * 2;
 #pragma unroll
@@ -797,9 +816,10 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
         }
       }
     }
-    __syncthreads();  // the round's level-2 nodes are in LDS
+    __syncthreads();  // the round's four 16-key parts are in LDS
 
-    // level-3 node of the round: ordered fold of its level-2 children
+    // the round's node (level 3 when C = 4, level 2 when C = 8): ordered fold
+    // of its four 16-key parts
     const int nch = (int)min<int64_t>(4, (nkeys - 64 * r + 15) / 16);
     float m3 = 0.f, s3 = 0.f, a3[VPL];
     bool u3 = false;
@@ -824,17 +844,17 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
     const int64_t rel = min<int64_t>(64 * (r + 1), nkeys);
     const int64_t end = t0 + rel;
     const bool last = rel == nkeys;
-    put_node(3, (t0 + 64 * r) / 64, L3, a3, 0);
+    put_node(RL, (t0 + 64 * r) / 64, L3, a3, 0);
     float pL[NUR];
     int64_t pnode[NUR];
     bool pend[NUR];
 #pragma unroll
     for (int a = 0; a < NUR; ++a) pend[a] = false;
     if constexpr (NU > 0) absorb(um[0], us[0], ua[0], uu[0], L3, 1.f, a3, VPL);
-    // close every level >= 4 whose span ends here, bottom-up
+    // close every level above the round's whose span ends here, bottom-up
 #pragma unroll
     for (int a = 0; a < NU; ++a) {
-      const int lvl = 4 + a;
+      const int lvl = RL + 1 + a;
       const int64_t sp = geo.span_len[lvl];
       if (uu[a] && ((rel % sp) == 0 || last)) {
         const float L = um[a] + __logf(us[a]);
@@ -851,10 +871,10 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
       }
     }
     __syncthreads();  // every wave's share of r . g is in
-    finish(3, (t0 + 64 * r) / 64, L3, 0);
+    finish(RL, (t0 + 64 * r) / 64, L3, 0);
 #pragma unroll
     for (int a = 0; a < NU; ++a)
-      if (pend[a]) finish(4 + a, pnode[a], pL[a], a + 1);
+      if (pend[a]) finish(RL + 1 + a, pnode[a], pL[a], a + 1);
   }
 }
 
@@ -907,19 +927,26 @@ hipError_t dispatch_leaf(const BuildArgs& a, dim3 grid, hipStream_t s) {
   }
 }
 
-template <int D>
-hipError_t dispatch_mf(const BuildArgs& a, dim3 grid, hipStream_t s) {
-  const int nu = a.merge_top ? 0 : a.top_level - 3;
+template <int D, int C>
+hipError_t dispatch_mf_c(const BuildArgs& a, dim3 grid, hipStream_t s) {
+  const int nu = a.merge_top ? 0 : a.top_level - (C == 4 ? 3 : 2);
   switch (nu) {
-    case 0: hipLaunchKernelGGL((k_build_mf<D, 0>), grid, dim3(256), 0, s, a); break;
-    case 1: hipLaunchKernelGGL((k_build_mf<D, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_build_mf<D, 2>), grid, dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_build_mf<D, 3>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_build_mf<D, 4>), grid, dim3(256), 0, s, a); break;
-    case 5: hipLaunchKernelGGL((k_build_mf<D, 5>), grid, dim3(256), 0, s, a); break;
+    case 0: hipLaunchKernelGGL((k_build_mf<D, 0, C>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_build_mf<D, 1, C>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_build_mf<D, 2, C>), grid, dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_build_mf<D, 3, C>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_build_mf<D, 4, C>), grid, dim3(256), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((k_build_mf<D, 5, C>), grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t dispatch_mf(const BuildArgs& a, dim3 grid, hipStream_t s) {
+  if (a.geo.C == 8) return dispatch_mf_c<D, 8>(a, grid, s);
+  if (a.geo.C == 4) return dispatch_mf_c<D, 4>(a, grid, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
