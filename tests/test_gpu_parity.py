@@ -632,3 +632,58 @@ def test_split_select_is_bit_identical(name, leaf_form, N, p, repeat):
             n_cut += a.cut_id != 2**31 - 1
     if repeat and p < 1.0:
         assert n_cut > 0, "no level split its ties at the cut"
+
+
+SMALL_CASES = [
+    # name, cfg kwargs (capacity 300), token counts: below one chunk, one chunk, one 16-key block,
+    # one 64-key round, ragged rounds, several top nodes
+    ("mf-weights-C4", dict(batch=1, n_kv_heads=2, q_per_kv=2, head_dim=64, n_ref=4, chunk=4, levels=3, dtype="bf16",
+                           leaf_form="weights"), [1, 3, 4, 5, 16, 63, 64, 65, 257]),
+    ("mf-mean-C8", dict(batch=1, n_kv_heads=1, q_per_kv=3, head_dim=128, n_ref=1, chunk=8, levels=2, dtype="bf16"),
+     [7, 8, 9, 64, 65, 200]),
+    ("f32-C4", dict(batch=1, n_kv_heads=1, q_per_kv=2, head_dim=64, n_ref=3, chunk=4, levels=3, dtype="f32"), [1, 4, 65, 299]),
+]
+
+
+@pytest.mark.parametrize("name,kw,sizes", SMALL_CASES, ids=[c[0] for c in SMALL_CASES])
+def test_small_and_degenerate_token_counts(name, kw, sizes):
+    """Build, route and attend at token counts around the chunk, block, round
+    and top-node boundaries, down to fewer tokens than one chunk (no node at
+    all: attention over the forced keys alone)."""
+    _say(f"small token counts {name}")
+    cfg = zha.ZhaConfig(capacity=300, **kw)
+    K, V, Q, ref = random_inputs(cfg, 1, seed=9)
+    weights = cfg.leaf_form == "weights"
+    leaf_dtype = "f64" if weights else None
+    tol = PAR.OUT_TOL[cfg.dtype]
+    p = 0.9
+    for N in sizes:
+        tree = zha.alloc_tree(cfg)
+        zha.build(cfg, K, ref, tree, N)
+        buf = zha.alloc_route(cfg, 1, logits=weights)
+        zha.route(cfg, tree, N, Q, 1, p, buf, K=K)
+        nq = int(buf.layout.n_queries)
+        out = torch.full((nq, cfg.head_dim), float("nan"), device="cuda")
+        lse = torch.full((nq,), float("nan"), device="cuda")
+        ws = torch.empty(zha.attend_workspace_bytes(cfg, 1), dtype=torch.uint8, device="cuda")
+        zha.attend(cfg, Q, 1, K, V, N, zha.level1_sel(buf), zha.ZHA_SINK | zha.ZHA_LAST_CHUNK, out, lse, ws,
+                   logits=buf.logits)
+        torch.cuda.synchronize()
+        if N >= cfg.chunk:
+            check_tree(cfg, tree, K, ref, N)
+        out_c, lse_c = out.cpu().numpy(), lse.cpu().numpy()
+        for qi, (b, h, gq, t) in enumerate(query_list(cfg, 1)):
+            Kn, Vn, rn = np64(K[b, h, :N]), np64(V[b, h, :N]), np64(ref[h])
+            q = np64(Q[b, h, gq, t])
+            bits, scores = gpu_levels(cfg, buf, N, qi)
+            kept = PAR.gpu_kept_from_bits(bits)
+            if N >= cfg.chunk:
+                gd = cfg.dtype
+                to = O.build_tree(Kn, rn, cfg.chunk, cfg.levels, gd, keep_g=False, leaf_dtype=leaf_dtype)
+                PAR.check_route_teacher_forced(q, to, rn, cfg.chunk, p, kept, gd, scores, leaf_dtype=leaf_dtype)
+            else:
+                assert all(k.size == 0 for k in kept.values()), f"N={N}: a node kept with no complete chunk"
+            idx = O.attend_set(kept[1], N, cfg.chunk, True, True)
+            o, l = O.attend(q, Kn, Vn, idx)
+            np.testing.assert_allclose(out_c[qi], o, rtol=0, atol=tol, err_msg=f"N={N} query {qi}")
+            np.testing.assert_allclose(lse_c[qi], l, rtol=0, atol=tol, err_msg=f"N={N} query {qi}")
