@@ -687,3 +687,61 @@ def test_small_and_degenerate_token_counts(name, kw, sizes):
             o, l = O.attend(q, Kn, Vn, idx)
             np.testing.assert_allclose(out_c[qi], o, rtol=0, atol=tol, err_msg=f"N={N} query {qi}")
             np.testing.assert_allclose(lse_c[qi], l, rtol=0, atol=tol, err_msg=f"N={N} query {qi}")
+
+
+WAVE_CASES = [
+    # name, n_tokens, p, keys repeat with period 512 (exact score ties)
+    ("ragged", 4096 + 4 * 37 + 3, 0.9, False),
+    ("keep-all", 4096, 1.0, False),
+    ("ties", 4096, 0.9, True),
+    ("ties-small-p", 4096 + 64, 0.05, True),
+]
+
+
+@pytest.mark.parametrize("name,N,p,repeat", WAVE_CASES, ids=[c[0] for c in WAVE_CASES])
+def test_wave_select_is_bit_identical(name, N, p, repeat):
+    """Rows of at most 2,048 candidates at levels with 64 or more queries are
+    selected by one wave per query; the same queries routed among fewer
+    queries (one workgroup per query) must give the same bits and statistics
+    on the same score rows."""
+    _say(f"wave select {name}")
+    cap = 4096 + 256
+    cfg = zha.ZhaConfig(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=4, dtype="bf16",
+                        capacity=cap)
+    K = torch.empty(1, 2, cap, 128, dtype=torch.bfloat16)
+    ref = torch.empty(2, 16, 128)
+    Q16 = torch.empty(1, 2, 4, 16, 128, dtype=torch.bfloat16)
+    for h in range(2):
+        k, _, r, q = W.random_cache(cap, 128, 16, "bf16", seed=31 + h, n_queries=64, segment_len=16)
+        if repeat:
+            k = k[:512].repeat(cap // 512 + 1, 1)[:cap]
+        q[::3] = (1.5 * k[(torch.arange(q.shape[0])[::3] * 61) % N].float()).to(torch.bfloat16)
+        K[0, h], ref[h], Q16[0, h] = k, r, q.view(4, 16, 128)
+    Q1 = Q16[:, :, :, :1].contiguous()
+    K, ref, Q1, Q16 = K.cuda(), ref.cuda(), Q1.cuda(), Q16.cuda()
+    tree = zha.alloc_tree(cfg)
+    zha.build(cfg, K, ref, tree, N)
+    b1 = zha.alloc_route(cfg, 1)
+    zha.route(cfg, tree, N, Q1, 1, p, b1, K=K)
+    b16 = zha.alloc_route(cfg, 16)
+    zha.route(cfg, tree, N, Q16, 16, p, b16, K=K)
+    torch.cuda.synchronize()
+    assert int(b16.layout.n_queries) >= 64
+    sizes = O.level_sizes(N, cfg.chunk, cfg.levels)
+    n_cut = 0
+    for lv in range(1, cfg.levels + 1):
+        assert sizes[lv - 1] <= 2048
+        s1 = zha.stats_records(b1, lv)
+        s16 = zha.stats_records(b16, lv)
+        for cache in range(cfg.n_caches):
+            for gq in range(cfg.q_per_kv):
+                qa = cache * cfg.q_per_kv + gq          # T = 1
+                qb = (cache * cfg.q_per_kv + gq) * 16   # T = 16, t = 0
+                ba, sa = gpu_levels(cfg, b1, N, qa)
+                bb, sb = gpu_levels(cfg, b16, N, qb)
+                assert np.array_equal(sa[lv].view(np.int32), sb[lv].view(np.int32)), (lv, qa, "scores")
+                assert np.array_equal(ba[lv], bb[lv]), (lv, qa, "bits")
+                assert bytes(s1[qa]) == bytes(s16[qb]), (lv, qa, "stats")
+                n_cut += s1[qa].cut_id != 2**31 - 1
+    if repeat and p < 1.0:
+        assert n_cut > 0, "no level split its ties at the cut"

@@ -971,6 +971,214 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs A) {
   }
 }
 
+// Wave form: one wave per query for rows of at most kWaveRow candidates
+// (lane l holds candidates 32l .. 32l + 31 in registers, and later writes
+// bitset word l).  Same fixed-point masses and the same cut as k_select;
+// the radix digits are 8 bits wide (a 256-bin histogram per wave in LDS),
+// which changes the number of passes, not the key found: each pass narrows
+// to the one bin whose mass interval holds P, and the last pass ends at the
+// exact cut key.
+constexpr int kWaveRow = 2048;
+// levels with fewer queries keep one workgroup per query (no gain from
+// finer work items there)
+constexpr int64_t kWaveQueries = 64;
+
+__global__ __launch_bounds__(256) void k_select_wave(SelectArgs A, int64_t n_queries) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t q = (int64_t)blockIdx.x * 4 + wave;
+  if (q >= n_queries) return;  // uniform per wave; nothing below synchronises waves
+  __shared__ unsigned long long hist_all[4][256];
+  unsigned long long* hist = hist_all[wave];
+  const int64_t n = A.n_nodes;
+  const int64_t n4 = (n + 3) / 4;
+  const float4* row4 = reinterpret_cast<const float4*>(A.score + q * A.score_stride);
+  uint32_t* srow = A.sel + q * A.words;
+  SelStats* st = reinterpret_cast<SelStats*>(A.stats) + q;
+  const int64_t nwords = (n + 31) / 32;
+
+  float v[32];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int64_t b4 = 8 * (int64_t)lane + c;
+    const float4 f = b4 < n4 ? row4[b4] : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+    v[4 * c] = f.x;
+    v[4 * c + 1] = f.y;
+    v[4 * c + 2] = f.z;
+    v[4 * c + 3] = f.w;
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i)
+    if (32 * (int64_t)lane + i >= n) v[i] = kNegInf;
+
+  // candidate key range and count from the score tiles' slots
+  uint32_t kmax = 0u, kmin = 0xffffffffu;
+  unsigned long long ncand = 0ull;
+  {
+    const uint4* kr = reinterpret_cast<const uint4*>(A.keyrange) + q * A.kr_slots;
+    for (int64_t i = lane; i < A.kr_used; i += 64) {
+      const uint4 s = kr[i];
+      kmax = max(kmax, s.x);
+      kmin = min(kmin, s.y);
+      ncand += s.z;
+    }
+    for (int o = 1; o < 64; o <<= 1) {
+      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+      ncand += __shfl_xor(ncand, o);
+    }
+  }
+  if (ncand == 0) {
+    if (lane < nwords) srow[lane] = 0u;
+    if (lane == 0) {
+      SelStats s0 = {kNegInf, 0, 0, 0u, 0, 0, 0ull, 0ull};
+      *st = s0;
+    }
+    return;
+  }
+  const SelSetup su = sel_setup(kmax, kmin, n);
+  const float mx = su.mx;
+  const double scale = su.scale;
+  auto wsum = [](unsigned long long x) {
+    for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o);
+    return x;
+  };
+
+  uint32_t want = su.want;
+  int lo = su.lo;
+  unsigned long long M = 0, P = 0, above = 0, h_tau = 0;
+  bool first = true, found = false;
+  do {
+    const int w = lo < 8 ? lo : 8;
+    const int nb = 1 << w;
+    const int top = lo;
+    lo -= w;
+    for (int i = lane; i < nb; i += 64) hist[i] = 0ull;
+    wave_sync();
+    unsigned long long part = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float s = v[i];
+      if (s > kNegInf) {
+        const uint32_t k = order_key(s);
+        const bool match = top >= 32 || (k >> top) == want;
+        if (first || match) {
+          const unsigned long long mm = fixed_mass(s, mx, scale);
+          if (first) part += mm;
+          if (match && w > 0) atomicAdd(&hist[(k >> lo) & (uint32_t)(nb - 1)], mm);
+        }
+      }
+    }
+    wave_sync();
+    if (first) {
+      M = wsum(part);
+      first = false;
+      if (A.keep_all) break;
+      P = p_target(A.p, M);
+      if (w == 0) {  // every candidate has the same key
+        want = kmax;
+        h_tau = M;
+        found = true;
+        break;
+      }
+    }
+    // the bin, scanning from the top, whose mass interval holds P: each lane
+    // sums nb / 64 bins (or one), an inclusive suffix sum over the lanes
+    // gives the mass above each lane's bins
+    const int per = nb >= 64 ? nb / 64 : 1;
+    const int b0 = lane * per;
+    const int cnt = b0 < nb ? per : 0;
+    unsigned long long mine = 0;
+    for (int i = 0; i < cnt; ++i) mine += hist[b0 + i];
+    unsigned long long suf = mine;
+    for (int o = 1; o < 64; o <<= 1) {
+      const unsigned long long t = __shfl_down(suf, o);
+      if (lane + o < 64) suf += t;
+    }
+    unsigned long long cum = above + (suf - mine);
+    int bin = -1;
+    unsigned long long bin_above = 0;
+    for (int i = cnt - 1; i >= 0; --i) {
+      const unsigned long long hv = hist[b0 + i];
+      if (bin < 0 && cum < P && P <= cum + hv) {
+        bin = b0 + i;
+        bin_above = cum;
+      }
+      cum += hv;
+    }
+    const unsigned long long ball = __ballot(bin >= 0);
+    const int src = ball ? __ffsll((long long)ball) - 1 : 0;
+    const int bsel = __shfl(bin, src);
+    if (ball) above = __shfl(bin_above, src);
+    want = (w >= 32 ? 0u : (want << w)) | (uint32_t)bsel;
+    h_tau = hist[bsel & (nb - 1)];
+    wave_sync();
+    found = lo == 0;
+  } while (!found);
+
+  uint32_t tau = 0u;
+  int cut_id = INT_MAX;
+  if (!A.keep_all) {
+    tau = want;
+    const unsigned long long need = ties_needed(tau, P, above, h_tau, mx, scale);
+    if (need) {
+      // the need-th tie in id order: lanes hold consecutive ids
+      uint32_t tb = 0u;
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        if (v[i] > kNegInf && order_key(v[i]) == tau) tb |= 1u << i;
+      const unsigned long long c = __popc(tb);
+      unsigned long long pre = c;
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long t = __shfl_up(pre, o);
+        if (lane >= o) pre += t;
+      }
+      const unsigned long long before = pre - c;
+      int cut = -1;
+      if (before < need && need <= before + c) {
+        uint32_t left = (uint32_t)(need - before);
+        for (int i = 0; i < 32; ++i)
+          if ((tb >> i) & 1u) {
+            if (--left == 0u) {
+              cut = 32 * lane + i + 1;
+              break;
+            }
+          }
+      }
+      const unsigned long long ball = __ballot(cut >= 0);
+      if (ball) cut_id = __shfl(cut, __ffsll((long long)ball) - 1);
+    }
+  }
+
+  uint32_t bits = 0u;
+  unsigned long long kmass = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float s = v[i];
+    if (s > kNegInf) {
+      const uint32_t k = order_key(s);
+      if (k > tau || (k == tau && 32 * lane + i < cut_id)) {
+        bits |= 1u << i;
+        kmass += fixed_mass(s, mx, scale);
+      }
+    }
+  }
+  if (lane < nwords) srow[lane] = bits;
+  const unsigned long long nk = wsum((unsigned long long)__popc(bits));
+  const unsigned long long km = wsum(kmass);
+  if (lane == 0) {
+    SelStats s1;
+    s1.max_score = mx;
+    s1.n_cand = (int32_t)ncand;
+    s1.n_kept = (int32_t)nk;
+    s1.cut_key = tau;
+    s1.cut_id = cut_id;
+    s1.shift = su.shift;
+    s1.mass_total = M;
+    s1.mass_kept = km;
+    *st = s1;
+  }
+}
+
 // Split form: S workgroups per query, each on its share of the row's words,
 // for levels with few queries and many candidates.  The per-query state and
 // the segments' histograms live in the route workspace; a chain of kernels
@@ -1332,7 +1540,9 @@ hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dty
   }
   prof.begin(ZHA_K_SELECT, level);
   sel.split_S = sel.split ? select_segments(n_queries, sel.n_nodes) : 1;
-  if (sel.split_S < 2) {
+  if (sel.split_S < 2 && sel.n_nodes <= kWaveRow && n_queries >= kWaveQueries) {
+    hipLaunchKernelGGL(k_select_wave, dim3((unsigned)((n_queries + 3) / 4)), dim3(256), 0, s, sel, n_queries);
+  } else if (sel.split_S < 2) {
     hipLaunchKernelGGL(k_select, dim3((unsigned)n_queries), dim3(kSelThreads), 0, s, sel);
   } else {
     const dim3 segs((unsigned)sel.split_S, (unsigned)n_queries);
