@@ -8,7 +8,7 @@ chunk 4, 6 levels, 16 reference queries, p = 0.95):
   zha_route   (256 decode queries, 6 levels of score + top-p select)
   zha_attend  (exact attention over the routed keys, sink, current chunk)
 Inputs are seeded synthetic data already resident in HBM.  Prints one JSON
-line (rank 0).  ``--gpus`` above 1 is refused: this build runs on one GPU.
+line (rank 0).  ``--gpus`` above 1 is refused: the library runs on one GPU.
 """
 from __future__ import annotations
 
@@ -201,7 +201,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(
-            "bench.py measures the single-GPU path only; --gpus above 1 is not supported by this build "
+            "bench.py measures the single-GPU path only; --gpus above 1 is not supported "
             "(the per-GPU share at real shape is what one GPU can show).",
             file=sys.stderr,
         )

@@ -51,7 +51,7 @@ What is computed, for one cache (one sequence x one KV head):
   exact softmax attention over the keys of the kept level-1 chunks, plus
   token 0 (the attention sink) and the current chunk.
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
   R3  smallest set: order candidates by (score desc, node id asc) and keep
       rank i iff the mass of the ranks before it is < p * M.  This prefix is a
       minimum-cardinality set with mass >= p * M (checked by brute force).
