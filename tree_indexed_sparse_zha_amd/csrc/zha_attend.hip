@@ -730,6 +730,275 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_cached(AttendArgs A) {
   write_partial<D, QG>(A, red, cache, qg0, nq, tile);
 }
 
+// Groups of 16 queries (QC > 8): the P V product on the matrix cores.  The
+// q.k MFMA (or the cached logits) leaves in lane (query r, key group g) the
+// logits of keys 4g .. 4g+3 of a 16-key group for query r, which is the A
+// operand layout of v_mfma_f32_16x16x16_bf16 for P (rows = queries, k =
+// keys); the group's V rows are staged in LDS and read as the B operand
+// (k = keys, columns = 16 values of d).  P is split into three bf16 terms
+// (hi + mid + lo, exact to about 2^-26 relative), so the product keeps fp32
+// accuracy.  The output rows (4 queries x 16 values of d per lane and block)
+// are rescaled per query when the running max moves, as in the FMA kernels.
+// Phase 1 is the one of k_attend_cached (CACHED: routed quads read the
+// route's logits, forced-only quads get theirs computed once) or of
+// k_attend_mfma (logits from K on the fly).
+typedef short short4v __attribute__((ext_vector_type(4)));
+
+template <int D, bool CACHED>
+__global__ __launch_bounds__(kAttThreads) void k_attend_pv16(AttendArgs A) {
+  constexpr int QG = 16;
+  constexpr int PIECES = D / 8;     // 16-byte pieces per row
+  constexpr int NS = D / 32;        // q.k MFMA k-steps
+  constexpr int NVL = PIECES / 4;   // V loads per lane per 16-key group
+  constexpr int NB = D / 16;        // output blocks of 16 values of d
+  constexpr int VROW = D + 8;       // padded LDS V row (bf16 elements)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cache = blockIdx.y;
+  const int qg0 = blockIdx.z * QG;
+  const int nq = min(QG, A.QC - qg0);
+  const int64_t tile = blockIdx.x;
+  const int b = cache / A.H, h = cache % A.H;
+  const int64_t k_lo = tile * A.tile_keys;
+  const int64_t k_hi = min(A.n_tokens, k_lo + A.tile_keys);
+
+  __shared__ uint16_t e_quad[kTileQuadsMax];
+  __shared__ unsigned long long e_mask[kTileQuadsMax];
+  __shared__ int scan[kAttThreads];
+  __shared__ float f_log[CACHED ? kMaxForcedQuads : 1][QG][4];
+  __shared__ uint16_t vs[4][16 * VROW];
+  __shared__ float red[4][QG][D + 2];
+
+  // ---- phase 1: the tile's quads with a key some query attends, routed
+  // quads first (CACHED) or in key order
+  int n_r, n_ent;
+  {
+    unsigned long long qmask[kQPT];
+    uint32_t routed;
+    quad_masks<QG>(A, cache, qg0, nq, k_lo, k_hi, tid, qmask, &routed);
+    if constexpr (CACHED) {
+      int cnt = 0;  // routed count in the low 16 bits, forced-only count above
+#pragma unroll
+      for (int i = 0; i < kQPT; ++i)
+        if (qmask[i]) cnt += ((routed >> i) & 1u) ? 1 : (1 << 16);
+      int excl;
+      const int tot = block_scan_excl(cnt, scan, &excl);
+      n_r = tot & 0xffff;
+      n_ent = n_r + min(tot >> 16, kMaxForcedQuads);
+      int pos_r = excl & 0xffff, pos_f = n_r + (excl >> 16);
+#pragma unroll
+      for (int i = 0; i < kQPT; ++i) {
+        if (qmask[i]) {
+          const int pos = ((routed >> i) & 1u) ? pos_r++ : pos_f++;
+          if (pos < n_ent) {
+            e_quad[pos] = (uint16_t)(tid * kQPT + i);
+            e_mask[pos] = qmask[i];
+          }
+        }
+      }
+    } else {
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < kQPT; ++i) cnt += qmask[i] != 0ull;
+      int pos;
+      n_ent = block_scan_excl(cnt, scan, &pos);
+      n_r = n_ent;
+#pragma unroll
+      for (int i = 0; i < kQPT; ++i) {
+        if (qmask[i]) {
+          e_quad[pos] = (uint16_t)(tid * kQPT + i);
+          e_mask[pos] = qmask[i];
+          ++pos;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  const bf16_t* Kc = reinterpret_cast<const bf16_t*>(A.K) + (int64_t)b * A.sb + (int64_t)h * A.sh;
+  const bf16_t* Vc = reinterpret_cast<const bf16_t*>(A.V) + (int64_t)b * A.sb + (int64_t)h * A.sh;
+  const int n_f = n_ent - n_r;
+  if (CACHED && n_f) {
+    // logits of the forced-only quads (one thread per key and query)
+    for (int idx = tid; idx < n_f * 4 * QG; idx += kAttThreads) {
+      const int f = idx / (4 * QG), kk = (idx / QG) % 4, u = idx % QG;
+      const int64_t key = k_lo + 4 * (int64_t)e_quad[n_r + f] + kk;
+      float z = kNegInf;
+      if (u < nq && key < k_hi) {
+        const int qi = qg0 + u;
+        const bf16_t* qp = reinterpret_cast<const bf16_t*>(A.Q) + (int64_t)b * A.qsb + (int64_t)h * A.qsh +
+                           (int64_t)(qi / A.T) * A.qsg + (int64_t)(qi % A.T) * A.qst;
+        const bf16_t* kp = Kc + key * A.st;
+        float dot = 0.f;
+#pragma unroll
+        for (int pc = 0; pc < PIECES; ++pc) {
+          float kv[8], qv[8];
+          unpack(ld16(kp + pc * 8), kv, bf16_t());
+          unpack(ld16(qp + pc * 8), qv, bf16_t());
+#pragma unroll
+          for (int x = 0; x < 8; ++x) dot += kv[x] * qv[x];
+        }
+        z = dot * A.inv_sqrt_d;
+      }
+      f_log[CACHED ? f : 0][u][kk] = z;
+    }
+    __syncthreads();
+  }
+
+  // ---- phase 2
+  const int r16 = lane & 15, kg = lane >> 4;
+  bf16x8 bq[CACHED ? 1 : NS];
+  if constexpr (!CACHED) {
+    const int qi = qg0 + r16;
+    if (r16 < nq) {
+      const bf16_t* qp = reinterpret_cast<const bf16_t*>(A.Q) + (int64_t)b * A.qsb + (int64_t)h * A.qsh +
+                         (int64_t)(qi / A.T) * A.qsg + (int64_t)(qi % A.T) * A.qst;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) bq[s] = as_bf16x8(ld16(qp + (4 * s + kg) * 8));
+    } else {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) bq[s] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    }
+  }
+  const uint32_t tile_bytes = (uint32_t)((k_hi - k_lo - 1) * A.st * 2 + D * 2);
+  const rsrc_t kr = make_rsrc(Kc + k_lo * A.st, tile_bytes);
+  const rsrc_t vr = make_rsrc(Vc + k_lo * A.st, tile_bytes);
+  const uint32_t row_bytes = (uint32_t)(A.st * 2);
+  // the route's logits of this tile and group: [quad][key][QW], queries
+  // qg0 .. qg0 + 15 are a whole row block (qg0 % 16 == 0)
+  const float* ltile = CACHED ? A.logits + (((int64_t)cache * ((A.QC + 15) / 16) + qg0 / 16) * A.nquads + (k_lo >> 2)) *
+                                               A.QW * 4
+                              : nullptr;
+
+  const int n_groups = (n_ent + 3) / 4;
+  auto load_group = [&](int g, uint4* KA, uint4* VA) {
+    if constexpr (!CACHED) {
+      const int e = 4 * g + (r16 >> 2);
+      const uint32_t ro = e < n_ent ? (4u * e_quad[e] + (r16 & 3)) * row_bytes : kOffNone;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) KA[s] = bld16<0>(kr, ro + (4 * s + kg) * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < NVL; ++u) {
+      const int pi = lane + 64 * u;
+      const int kq = pi / PIECES, pc = pi % PIECES;
+      const int e = 4 * g + (kq >> 2);
+      const uint32_t ro = e < n_ent ? (4u * e_quad[e] + (kq & 3)) * row_bytes : kOffNone;
+      VA[u] = bld16(vr, ro + pc * 16);
+    }
+  };
+
+  float m = kNegInf, l = 0.f;  // softmax state of query r16 (same in its 4 lanes)
+  f32x4 O[NB];                 // rows 4 kg + i (queries), column 16 blk + r16 (d)
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk) O[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint4 kf[CACHED ? 1 : NS], kn[CACHED ? 1 : NS], vf[NVL], vn[NVL];
+  if (wave < n_groups) load_group(wave, kf, vf);
+  for (int g = wave; g < n_groups; g += 4) {
+    if (g + 4 < n_groups) load_group(g + 4, kn, vn);
+    // logits of query r16 for the 4 keys of entry e
+    const int e = 4 * g + kg;
+    const unsigned long long msk = (e < n_ent && r16 < nq) ? e_mask[e] >> (4 * r16) : 0ull;
+    float zz[4];
+    if constexpr (CACHED) {
+      if (e < n_r && r16 < nq) {
+        const float* lz = ltile + (int64_t)e_quad[e] * 4 * A.QW + r16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zz[i] = lz[i * A.QW];
+      } else if (e < n_ent && r16 < nq) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zz[i] = f_log[e - n_r][r16][i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zz[i] = kNegInf;
+      }
+    } else {
+      f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[s]), bq[s], z, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zz[i] = z[i] * A.inv_sqrt_d;
+    }
+    float mb = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (!((msk >> i) & 1ull)) zz[i] = kNegInf;
+      mb = fmaxf(mb, zz[i]);
+    }
+    mb = fmaxf(mb, __shfl_xor(mb, 16));
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    const float mn = fmaxf(m, mb);
+    float sc = 1.f, ps = 0.f, pz[4] = {0.f, 0.f, 0.f, 0.f};
+    if (mn != kNegInf) {
+      sc = __expf(m - mn);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pz[i] = __expf(zz[i] - mn);
+        ps += pz[i];
+      }
+    }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    l = l * sc + ps;
+    m = mn;
+
+    // the group's V rows into this wave's LDS slot
+#pragma unroll
+    for (int u = 0; u < NVL; ++u) {
+      const int pi = lane + 64 * u;
+      *reinterpret_cast<uint4*>(&vs[wave][(pi / PIECES) * VROW + (pi % PIECES) * 8]) = vf[u];
+    }
+    wave_sync();
+    // rescale the output rows (query 4 kg + i: its factor is in lane 4 kg + i)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float f = __shfl(sc, 4 * kg + i);
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) O[blk][i] *= f;
+    }
+    // P = hi + mid + lo in bf16 (A operand: query r16, keys 4 kg + i)
+    short4v ph, pm, pl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t bh = bf16_bits(pz[i]);
+      const float r1 = pz[i] - __uint_as_float(bh << 16);
+      const uint32_t bm = bf16_bits(r1);
+      const float r2 = r1 - __uint_as_float(bm << 16);
+      ph[i] = (short)bh;
+      pm[i] = (short)bm;
+      pl[i] = (short)bf16_bits(r2);
+    }
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      // B operand: V[key 4 kg + i][d = 16 blk + r16]
+      short4v vb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vb[i] = (short)vs[wave][(4 * kg + i) * VROW + 16 * blk + r16];
+      O[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vb, O[blk], 0, 0, 0);
+      O[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pm, vb, O[blk], 0, 0, 0);
+      O[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vb, O[blk], 0, 0, 0);
+    }
+    wave_sync();
+    if constexpr (!CACHED) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) kf[s] = kn[s];
+    }
+#pragma unroll
+    for (int u = 0; u < NVL; ++u) vf[u] = vn[u];
+  }
+
+  // this wave's (max, sum, weighted V sum) per query for the workgroup merge
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][4 * kg + i][16 * blk + r16] = O[blk][i];
+  if (kg == 0) {
+    red[wave][r16][D] = m;
+    red[wave][r16][D + 1] = l;
+  }
+  __syncthreads();
+  write_partial<D, QG>(A, red, cache, qg0, nq, tile);
+}
+
 // Merges the per-tile partial results of one query: S slices of D threads,
 // slice s folding tiles s, s + S, ... with a running max (two tiles in flight
 // per step), then slice 0 merging the S slice states in slice order, so the
@@ -804,21 +1073,26 @@ void launch_cached(const AttendArgs& a, int n_caches, hipStream_t s) {
 
 template <int D>
 void launch_mfma_qg(const AttendArgs& a, int n_caches, hipStream_t s) {
+  if (a.QC > 8) {
+    // groups of 16 queries: P V on the matrix cores
+    dim3 grid((unsigned)a.n_tiles, (unsigned)n_caches, (unsigned)((a.QC + 15) / 16));
+    if (a.logits)
+      hipLaunchKernelGGL((k_attend_pv16<D, true>), grid, dim3(kAttThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_attend_pv16<D, false>), grid, dim3(kAttThreads), 0, s, a);
+    return;
+  }
   if (a.logits) {
     if (a.QC <= 4)
       launch_cached<D, 4>(a, n_caches, s);
-    else if (a.QC <= 8)
-      launch_cached<D, 8>(a, n_caches, s);
     else
-      launch_cached<D, 16>(a, n_caches, s);
+      launch_cached<D, 8>(a, n_caches, s);
     return;
   }
   if (a.QC <= 4)
     launch_mfma<D, 4>(a, n_caches, s);
-  else if (a.QC <= 8)
-    launch_mfma<D, 8>(a, n_caches, s);
   else
-    launch_mfma<D, 16>(a, n_caches, s);
+    launch_mfma<D, 8>(a, n_caches, s);
 }
 
 }  // namespace
