@@ -536,10 +536,9 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
     float gr[VPL];
 #pragma unroll
     for (int e = 0; e < VPL / 2; ++e) {
-      const uint32_t lo = bf16_bits(gv[2 * e]), hi = bf16_bits(gv[2 * e + 1]);
-      wd[e] = lo | (hi << 16);
-      gr[2 * e] = __uint_as_float(lo << 16);
-      gr[2 * e + 1] = __uint_as_float(hi << 16);
+      wd[e] = bf16_pair(gv[2 * e], gv[2 * e + 1]);
+      gr[2 * e] = bf16_lo(wd[e]);
+      gr[2 * e + 1] = bf16_hi(wd[e]);
     }
     float dot = 0.f;
 #pragma unroll
@@ -712,12 +711,11 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
               Gl = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, wb[s], Gl, 0, 0, 0);
             }
             const float4 rv = *reinterpret_cast<const float4*>(&refL[j][16 * blk + 4 * g]);
-            const uint32_t b0 = bf16_bits(Gl[0]), b1 = bf16_bits(Gl[1]), b2 = bf16_bits(Gl[2]), b3 = bf16_bits(Gl[3]);
-            pk[blk] = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-            dot = fmaf(rv.x, __uint_as_float(b0 << 16), dot);
-            dot = fmaf(rv.y, __uint_as_float(b1 << 16), dot);
-            dot = fmaf(rv.z, __uint_as_float(b2 << 16), dot);
-            dot = fmaf(rv.w, __uint_as_float(b3 << 16), dot);
+            pk[blk] = make_uint2(bf16_pair(Gl[0], Gl[1]), bf16_pair(Gl[2], Gl[3]));
+            dot = fmaf(rv.x, bf16_lo(pk[blk].x), dot);
+            dot = fmaf(rv.y, bf16_hi(pk[blk].x), dot);
+            dot = fmaf(rv.z, bf16_lo(pk[blk].y), dot);
+            dot = fmaf(rv.w, bf16_hi(pk[blk].y), dot);
           }
           dot += __shfl_xor(dot, 16);
           dot += __shfl_xor(dot, 32);
@@ -794,12 +792,11 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
         for (int i = 0; i < 4; ++i) gv[i] = G[blk][i] * inv2;
         *reinterpret_cast<float4*>(&chG[wave][j][16 * blk + 4 * g]) = make_float4(gv[0], gv[1], gv[2], gv[3]);
         const float4 rv = *reinterpret_cast<const float4*>(&refL[j][16 * blk + 4 * g]);
-        const uint32_t b0 = bf16_bits(gv[0]), b1 = bf16_bits(gv[1]), b2 = bf16_bits(gv[2]), b3 = bf16_bits(gv[3]);
-        pk[blk] = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-        dot = fmaf(rv.x, __uint_as_float(b0 << 16), dot);
-        dot = fmaf(rv.y, __uint_as_float(b1 << 16), dot);
-        dot = fmaf(rv.z, __uint_as_float(b2 << 16), dot);
-        dot = fmaf(rv.w, __uint_as_float(b3 << 16), dot);
+        pk[blk] = make_uint2(bf16_pair(gv[0], gv[1]), bf16_pair(gv[2], gv[3]));
+        dot = fmaf(rv.x, bf16_lo(pk[blk].x), dot);
+        dot = fmaf(rv.y, bf16_hi(pk[blk].x), dot);
+        dot = fmaf(rv.z, bf16_lo(pk[blk].y), dot);
+        dot = fmaf(rv.w, bf16_hi(pk[blk].y), dot);
       }
       dot += __shfl_xor(dot, 16);
       dot += __shfl_xor(dot, 32);
@@ -855,17 +852,17 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
 #pragma unroll
     for (int a = 0; a < NU; ++a) {
       const int lvl = RL + 1 + a;
-      const int64_t sp = geo.span_len[lvl];
-      if (uu[a] && ((rel % sp) == 0 || last)) {
+      const int sh = (C == 4 ? 2 : 3) * lvl;  // span_len[lvl] = C^lvl = 2^sh
+      if (uu[a] && ((rel & ((1ll << sh) - 1)) == 0 || last)) {
         const float L = um[a] + __logf(us[a]);
         const float inv = 1.f / us[a];
         float gv[VPL];
 #pragma unroll
         for (int e = 0; e < VPL; ++e) gv[e] = ua[a][e] * inv;
-        put_node(lvl, (end - 1) / sp, L, gv, a + 1);
+        put_node(lvl, (end - 1) >> sh, L, gv, a + 1);
         pend[a] = true;
         pL[a] = L;
-        pnode[a] = (end - 1) / sp;
+        pnode[a] = (end - 1) >> sh;
         if (a + 1 < NU) absorb(um[a + 1], us[a + 1], ua[a + 1], uu[a + 1], L, 1.f, gv, VPL);
         uu[a] = false;
       }

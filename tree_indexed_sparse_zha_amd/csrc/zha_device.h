@@ -82,16 +82,26 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, b);
 }
 
+// Two fp32 values rounded to bf16 (nearest even) by one packed conversion:
+// a in the low half, b in the high half.
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{a, b}, bf16x2v));
+}
+// The rounded values of a bf16_pair word as fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
 // Pack fp32 values of one piece, rounding to the storage type; also returns
 // the rounded values as fp32 in `rounded`.
 __device__ __forceinline__ uint4 pack(const float* x, float* rounded, bf16_t) {
   uint32_t w[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    uint32_t lo = bf16_bits(x[2 * i]), hi = bf16_bits(x[2 * i + 1]);
-    w[i] = lo | (hi << 16);
-    rounded[2 * i] = __uint_as_float(lo << 16);
-    rounded[2 * i + 1] = __uint_as_float(hi << 16);
+    w[i] = bf16_pair(x[2 * i], x[2 * i + 1]);
+    rounded[2 * i] = bf16_lo(w[i]);
+    rounded[2 * i + 1] = bf16_hi(w[i]);
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
