@@ -239,6 +239,136 @@ __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs A) {
   }
 }
 
+// Levels >= 2 with few reference queries (R <= 8, bf16 g): the MFMA's 16 A
+// rows are (node, plane) pairs, 16 / RP nodes of RP padded planes each, so
+// one MFMA chain scores 16 / RP nodes instead of one node with R of its 16
+// rows in use (R = 1, the lightweight geometry, fills every row).  Output
+// row 4 kg + i of lane (query, kg) is node (4 kg + i) / RP, plane
+// (4 kg + i) % RP; the max over a node's planes stays inside the lane for
+// RP <= 4 and takes one shuffle for RP = 8.  Tiles, candidate bits, score
+// rows and key-range slots as k_score_bf16.
+template <int D, int RP>
+__global__ __launch_bounds__(256) void k_score_smallr(ScoreArgs A) {
+  constexpr int NS = D / 32;
+  constexpr int TILE = 64;
+  constexpr int NPM = 16 / RP;  // nodes per MFMA chain
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cache = blockIdx.y;
+  const int qg0 = blockIdx.z * 16;
+  const int nq = min(16, A.QC - qg0);
+  const int64_t n0 = (int64_t)blockIdx.x * TILE;
+  const int R = A.R;
+  const int qn = lane & 15, kg = lane >> 4;
+  __shared__ float sc[16][TILE + 1];
+
+  bf16x8 bq[NS];
+  {
+    const int qi = qg0 + qn;
+    if (qn < nq) {
+      const int b = cache / A.H, h = cache % A.H, gq = qi / A.T, t = qi % A.T;
+      const bf16_t* qp = reinterpret_cast<const bf16_t*>(A.Q) + (int64_t)b * A.qsb +
+                         (int64_t)h * A.qsh + (int64_t)gq * A.qsg + (int64_t)t * A.qst;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) bq[s] = as_bf16x8(ld16(qp + (4 * s + kg) * 8));
+    } else {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) bq[s] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    }
+  }
+  const int64_t gnode = (int64_t)R * D * 2;
+  const char* gcache = A.g + (int64_t)cache * A.node_cap * gnode;
+  const float* ccache = A.c + (int64_t)cache * A.node_cap * R;
+
+  // candidate bits of this wave's 16 nodes for query qn, then "any query"
+  const int64_t nb0 = n0 + wave * 16;
+  uint32_t mybits = 0u;
+  if (qn < nq) {
+    const int64_t nvalid = A.n_nodes - nb0 < 16 ? (A.n_nodes - nb0 > 0 ? A.n_nodes - nb0 : 0) : 16;
+    const uint32_t valid = (uint32_t)((1ull << nvalid) - 1ull);
+    if (A.sel_parent) {
+      if (A.C >= 16) {
+        for (int u = 0; u < 16; ++u) {
+          const int64_t par = (nb0 + u) / A.C;
+          const uint32_t w = A.sel_parent[((int64_t)cache * A.QC + qg0 + qn) * A.parent_words + (par >> 5)];
+          if ((w >> (par & 31)) & 1u) mybits |= 1u << u;
+        }
+      } else {
+        const int64_t p0 = nb0 / A.C;
+        const uint32_t word =
+            A.sel_parent[((int64_t)cache * A.QC + qg0 + qn) * A.parent_words + (p0 >> 5)] >> (p0 & 31);
+        for (int pi = 0; pi < 16 / A.C; ++pi)
+          if ((word >> pi) & 1u) mybits |= ((1u << A.C) - 1u) << (pi * A.C);
+      }
+      mybits &= valid;
+    } else {
+      mybits = valid;
+    }
+    const int64_t hz = causal_horizon(A, qg0 + qn) - nb0;
+    if (hz < 16) mybits &= hz > 0 ? (1u << hz) - 1u : 0u;
+  }
+  uint32_t anybits = mybits;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) anybits |= (uint32_t)__shfl_xor((int)anybits, o);
+
+  // A row of this lane: node mrow / RP of the chain, plane mrow % RP
+  const int mrow = lane & 15, mnode = mrow / RP, mj = mrow % RP;
+  uint4 af[RP][NS];
+#pragma unroll
+  for (int ch = 0; ch < RP; ++ch) {
+    const int u = ch * NPM + mnode;
+    const bool live = ((anybits >> u) & 1u) && mj < R;
+    const char* gn = gcache + (nb0 + u) * gnode;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      af[ch][s] = live ? ld16(gn + ((int64_t)(4 * s + kg) * R + mj) * 16) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int ch = 0; ch < RP; ++ch) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af[ch][s]), bq[s], acc, 0, 0, 0);
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * kg + i;
+      const int u = ch * NPM + row / RP, j = row % RP;
+      const bool ok = ((anybits >> u) & 1u) && j < R;
+      v[i] = ok ? ccache[(nb0 + u) * R + j] + acc[i] * A.inv_sqrt_d : kNegInf;
+    }
+    // max over each node's planes; lane writes the nodes it then holds
+    if constexpr (RP == 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int u = ch * NPM + 4 * kg + i;
+        if (qn < nq) sc[qn][wave * 16 + u] = ((mybits >> u) & 1u) ? v[i] : kNegInf;
+      }
+    } else if constexpr (RP == 2) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int u = ch * NPM + 2 * kg + h2;
+        const float m2 = fmaxf(v[2 * h2], v[2 * h2 + 1]);
+        if (qn < nq) sc[qn][wave * 16 + u] = ((mybits >> u) & 1u) ? m2 : kNegInf;
+      }
+    } else {
+      float m4 = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+      if constexpr (RP == 8) m4 = fmaxf(m4, __shfl_xor(m4, 16));
+      const int u = ch * NPM + (RP == 4 ? kg : kg / 2);
+      if (qn < nq && (RP == 4 || (kg & 1) == 0)) sc[qn][wave * 16 + u] = ((mybits >> u) & 1u) ? m4 : kNegInf;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < nq * TILE; idx += 256) {
+    const int q = idx / TILE, x = idx % TILE;
+    const int64_t mm = n0 + x;
+    if (mm < A.n_nodes) A.score[((int64_t)cache * A.QC + qg0 + q) * A.score_stride + mm] = sc[q][x];
+  }
+  for (int q = wave; q < nq; q += 4) {
+    const float v = sc[q][lane];
+    const bool c = n0 + lane < A.n_nodes && v > kNegInf;
+    publish_range(A.keyrange + (((int64_t)cache * A.QC + qg0 + q) * A.kr_slots + blockIdx.x) * 4, c, order_key(v));
+  }
+}
+
 // ---------------------------------------------------------------------------
 // score of level-1 nodes in the weights form (bf16, C in {4, 8, 16})
 //
@@ -1496,6 +1626,23 @@ hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dty
           hipLaunchKernelGGL((k_score_bf16<128, true>), grid, dim3(256), 0, s, sa);
         else
           hipLaunchKernelGGL((k_score_bf16<64, true>), grid, dim3(256), 0, s, sa);
+      } else if (sa.R <= 8) {
+#define ZHA_SR(DD)                                                                          \
+  do {                                                                                      \
+    if (sa.R == 1)                                                                          \
+      hipLaunchKernelGGL((k_score_smallr<DD, 1>), grid, dim3(256), 0, s, sa);               \
+    else if (sa.R == 2)                                                                     \
+      hipLaunchKernelGGL((k_score_smallr<DD, 2>), grid, dim3(256), 0, s, sa);               \
+    else if (sa.R <= 4)                                                                     \
+      hipLaunchKernelGGL((k_score_smallr<DD, 4>), grid, dim3(256), 0, s, sa);               \
+    else                                                                                    \
+      hipLaunchKernelGGL((k_score_smallr<DD, 8>), grid, dim3(256), 0, s, sa);               \
+  } while (0)
+        if (sa.D == 128)
+          ZHA_SR(128);
+        else
+          ZHA_SR(64);
+#undef ZHA_SR
       } else if (sa.D == 128) {
         hipLaunchKernelGGL((k_score_bf16<128, false>), grid, dim3(256), 0, s, sa);
       } else {
