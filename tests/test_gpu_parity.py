@@ -690,22 +690,26 @@ def test_small_and_degenerate_token_counts(name, kw, sizes):
 
 
 WAVE_CASES = [
-    # name, n_tokens, p, keys repeat with period 512 (exact score ties)
+    # name, n_tokens, p, keys repeat with period 512 (exact score ties); rows of up to 2,048
+    # candidates take the one-wave form, up to 8,192 the one-workgroup row form
     ("ragged", 4096 + 4 * 37 + 3, 0.9, False),
     ("keep-all", 4096, 1.0, False),
     ("ties", 4096, 0.9, True),
     ("ties-small-p", 4096 + 64, 0.05, True),
+    ("rows-ragged", 32768 - 1003, 0.9, False),
+    ("rows-ties", 32768, 0.9, True),
 ]
 
 
 @pytest.mark.parametrize("name,N,p,repeat", WAVE_CASES, ids=[c[0] for c in WAVE_CASES])
 def test_wave_select_is_bit_identical(name, N, p, repeat):
-    """Rows of at most 2,048 candidates at levels with 64 or more queries are
-    selected by one wave per query; the same queries routed among fewer
-    queries (one workgroup per query) must give the same bits and statistics
-    on the same score rows."""
+    """Rows of at most 2,048 (8,192) candidates at levels with 64 or more
+    queries are selected by one wave (one 256-thread workgroup holding the row
+    in registers) per query; the same queries routed among fewer queries (one
+    1,024-thread workgroup per query, reading the row per pass) must give the
+    same bits and statistics on the same score rows."""
     _say(f"wave select {name}")
-    cap = 4096 + 256
+    cap = N + 256
     cfg = zha.ZhaConfig(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=4, dtype="bf16",
                         capacity=cap)
     K = torch.empty(1, 2, cap, 128, dtype=torch.bfloat16)
@@ -730,7 +734,7 @@ def test_wave_select_is_bit_identical(name, N, p, repeat):
     sizes = O.level_sizes(N, cfg.chunk, cfg.levels)
     n_cut = 0
     for lv in range(1, cfg.levels + 1):
-        assert sizes[lv - 1] <= 2048
+        assert sizes[lv - 1] <= 8192
         s1 = zha.stats_records(b1, lv)
         s16 = zha.stats_records(b16, lv)
         for cache in range(cfg.n_caches):

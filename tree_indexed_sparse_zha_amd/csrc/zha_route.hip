@@ -1309,6 +1309,220 @@ __global__ __launch_bounds__(256) void k_select_wave(SelectArgs A, int64_t n_que
   }
 }
 
+// Row form: one 256-thread workgroup per query for rows of at most
+// kRowsRow candidates, thread t holding candidates 32t .. 32t + 31 in
+// registers (and later writing bitset word t).  The steps of the wave form
+// with workgroup-wide sums and scans: 8-bit digits over one LDS histogram,
+// each thread owning one bin in the scan.
+constexpr int kRowsRow = 8192;
+
+__global__ __launch_bounds__(256) void k_select_rows(SelectArgs A) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t q = blockIdx.x;
+  __shared__ unsigned long long hist[256];
+  __shared__ unsigned long long wred[4];
+  __shared__ uint32_t wmax[4], wmin[4];
+  __shared__ int sh_i[2];
+  __shared__ unsigned long long sh_u[2];
+  const int64_t n = A.n_nodes;
+  const int64_t n4 = (n + 3) / 4;
+  const float4* row4 = reinterpret_cast<const float4*>(A.score + q * A.score_stride);
+  uint32_t* srow = A.sel + q * A.words;
+  SelStats* st = reinterpret_cast<SelStats*>(A.stats) + q;
+  const int64_t nwords = (n + 31) / 32;
+
+  // workgroup sum of a 64-bit value (every thread gets it)
+  auto bsum = [&](unsigned long long x) {
+    for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o);
+    if (lane == 0) wred[wave] = x;
+    __syncthreads();
+    const unsigned long long r = (wred[0] + wred[1]) + (wred[2] + wred[3]);
+    __syncthreads();
+    return r;
+  };
+
+  float v[32];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int64_t b4 = 8 * (int64_t)tid + c;
+    const float4 f = b4 < n4 ? row4[b4] : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+    v[4 * c] = f.x;
+    v[4 * c + 1] = f.y;
+    v[4 * c + 2] = f.z;
+    v[4 * c + 3] = f.w;
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i)
+    if (32 * (int64_t)tid + i >= n) v[i] = kNegInf;
+
+  uint32_t kmax = 0u, kmin = 0xffffffffu;
+  unsigned long long ncand = 0ull;
+  {
+    const uint4* kr = reinterpret_cast<const uint4*>(A.keyrange) + q * A.kr_slots;
+    for (int64_t i = tid; i < A.kr_used; i += 256) {
+      const uint4 s = kr[i];
+      kmax = max(kmax, s.x);
+      kmin = min(kmin, s.y);
+      ncand += s.z;
+    }
+    for (int o = 1; o < 64; o <<= 1) {
+      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+    }
+    if (lane == 0) {
+      wmax[wave] = kmax;
+      wmin[wave] = kmin;
+    }
+    __syncthreads();
+    kmax = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    kmin = min(min(wmin[0], wmin[1]), min(wmin[2], wmin[3]));
+    ncand = bsum(ncand);
+  }
+  if (ncand == 0) {
+    if (tid < nwords) srow[tid] = 0u;
+    if (tid == 0) {
+      SelStats s0 = {kNegInf, 0, 0, 0u, 0, 0, 0ull, 0ull};
+      *st = s0;
+    }
+    return;
+  }
+  const SelSetup su = sel_setup(kmax, kmin, n);
+  const float mx = su.mx;
+  const double scale = su.scale;
+
+  uint32_t want = su.want;
+  int lo = su.lo;
+  unsigned long long M = 0, P = 0, above = 0, h_tau = 0;
+  bool first = true, found = false;
+  do {
+    const int w = lo < 8 ? lo : 8;
+    const int nb = 1 << w;
+    const int top = lo;
+    lo -= w;
+    hist[tid] = 0ull;
+    __syncthreads();
+    unsigned long long part = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float s = v[i];
+      if (s > kNegInf) {
+        const uint32_t k = order_key(s);
+        const bool match = top >= 32 || (k >> top) == want;
+        if (first || match) {
+          const unsigned long long mm = fixed_mass(s, mx, scale);
+          if (first) part += mm;
+          if (match && w > 0) atomicAdd(&hist[(k >> lo) & (uint32_t)(nb - 1)], mm);
+        }
+      }
+    }
+    __syncthreads();
+    if (first) {
+      M = bsum(part);
+      first = false;
+      if (A.keep_all) break;
+      P = p_target(A.p, M);
+      if (w == 0) {  // every candidate has the same key
+        want = kmax;
+        h_tau = M;
+        found = true;
+        break;
+      }
+    }
+    // bin tid: mass of the bins above it by a suffix sum over the threads
+    const unsigned long long mine = tid < nb ? hist[tid] : 0ull;
+    unsigned long long suf = mine;
+    for (int o = 1; o < 64; o <<= 1) {
+      const unsigned long long t = __shfl_down(suf, o);
+      if (lane + o < 64) suf += t;
+    }
+    if (lane == 0) wred[wave] = suf;  // the wave's total
+    __syncthreads();
+    unsigned long long hi_waves = 0;
+    for (int w2 = wave + 1; w2 < 4; ++w2) hi_waves += wred[w2];
+    const unsigned long long cum = above + hi_waves + (suf - mine);  // mass strictly above bin tid
+    if (tid == 0) sh_i[0] = -1;
+    __syncthreads();
+    if (tid < nb && cum < P && P <= cum + mine) {
+      sh_i[0] = tid;
+      sh_u[0] = cum;
+    }
+    __syncthreads();
+    const int bsel = sh_i[0];
+    if (bsel >= 0) above = sh_u[0];
+    want = (w >= 32 ? 0u : (want << w)) | (uint32_t)bsel;
+    h_tau = hist[bsel & (nb - 1)];
+    __syncthreads();
+    found = lo == 0;
+  } while (!found);
+
+  uint32_t tau = 0u;
+  int cut_id = INT_MAX;
+  if (!A.keep_all) {
+    tau = want;
+    const unsigned long long need = ties_needed(tau, P, above, h_tau, mx, scale);
+    if (need) {
+      uint32_t tb = 0u;
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        if (v[i] > kNegInf && order_key(v[i]) == tau) tb |= 1u << i;
+      const unsigned long long c = __popc(tb);
+      unsigned long long pre = c;
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long t = __shfl_up(pre, o);
+        if (lane >= o) pre += t;
+      }
+      if (lane == 63) wred[wave] = pre;
+      __syncthreads();
+      unsigned long long lo_waves = 0;
+      for (int w2 = 0; w2 < wave; ++w2) lo_waves += wred[w2];
+      const unsigned long long before = lo_waves + pre - c;
+      if (tid == 0) sh_i[1] = INT_MAX;
+      __syncthreads();
+      if (before < need && need <= before + c) {
+        uint32_t left = (uint32_t)(need - before);
+        for (int i = 0; i < 32; ++i)
+          if ((tb >> i) & 1u) {
+            if (--left == 0u) {
+              sh_i[1] = 32 * tid + i + 1;
+              break;
+            }
+          }
+      }
+      __syncthreads();
+      cut_id = sh_i[1];
+    }
+  }
+
+  uint32_t bits = 0u;
+  unsigned long long kmass = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float s = v[i];
+    if (s > kNegInf) {
+      const uint32_t k = order_key(s);
+      if (k > tau || (k == tau && 32 * tid + i < cut_id)) {
+        bits |= 1u << i;
+        kmass += fixed_mass(s, mx, scale);
+      }
+    }
+  }
+  if (tid < nwords) srow[tid] = bits;
+  const unsigned long long nk = bsum((unsigned long long)__popc(bits));
+  const unsigned long long km = bsum(kmass);
+  if (tid == 0) {
+    SelStats s1;
+    s1.max_score = mx;
+    s1.n_cand = (int32_t)ncand;
+    s1.n_kept = (int32_t)nk;
+    s1.cut_key = tau;
+    s1.cut_id = cut_id;
+    s1.shift = su.shift;
+    s1.mass_total = M;
+    s1.mass_kept = km;
+    *st = s1;
+  }
+}
+
 // Split form: S workgroups per query, each on its share of the row's words,
 // for levels with few queries and many candidates.  The per-query state and
 // the segments' histograms live in the route workspace; a chain of kernels
@@ -1689,6 +1903,8 @@ hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dty
   sel.split_S = sel.split ? select_segments(n_queries, sel.n_nodes) : 1;
   if (sel.split_S < 2 && sel.n_nodes <= kWaveRow && n_queries >= kWaveQueries) {
     hipLaunchKernelGGL(k_select_wave, dim3((unsigned)((n_queries + 3) / 4)), dim3(256), 0, s, sel, n_queries);
+  } else if (sel.split_S < 2 && sel.n_nodes <= kRowsRow && n_queries >= kWaveQueries) {
+    hipLaunchKernelGGL(k_select_rows, dim3((unsigned)n_queries), dim3(256), 0, s, sel);
   } else if (sel.split_S < 2) {
     hipLaunchKernelGGL(k_select, dim3((unsigned)n_queries), dim3(kSelThreads), 0, s, sel);
   } else {
