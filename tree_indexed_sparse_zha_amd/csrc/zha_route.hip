@@ -588,6 +588,175 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   }
 }
 
+// Level-1 score for many queries per cache (QC > 16): a workgroup keeps its
+// 256-key tile (K rows in registers, weights and offsets in LDS) and walks up
+// to kMqBlocks query blocks of 16 over it, so the tile is read once per
+// 16 kMqBlocks queries instead of once per 16.  Per block the arithmetic is
+// the one of k_score_leafw (MFMA over the keys, fold in the MFMA layout).
+constexpr int kMqBlocks = 16;
+
+template <int D, int C, int RT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_score_leafw_mq(ScoreArgs A) {
+  constexpr int NS = D / 32;
+  constexpr int KT = 256;
+  constexpr int NCH = KT / C;
+  constexpr int GPW = 4;
+  constexpr int PARTS = C / 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cache = blockIdx.y;
+  const int qz0 = blockIdx.z * 16 * kMqBlocks;  // first query of the workgroup
+  const int nqb = min(kMqBlocks, (A.QC - qz0 + 15) / 16);
+  const int64_t k0 = (int64_t)blockIdx.x * KT;
+  const int64_t m0 = k0 / C;
+  const int R = A.R;
+  const int qn = lane & 15, kg = lane >> 4;
+  const int64_t n_keys = A.n_nodes * C;
+  constexpr int WROW = 16 * PARTS + 1;
+  __shared__ float sc[16][NCH + 1];
+  __shared__ float4 wl[NCH][WROW];
+  __shared__ float cl[NCH][17];
+
+  const int b = cache / A.H, h = cache % A.H;
+  const bf16_t* Kc = reinterpret_cast<const bf16_t*>(A.K) + (int64_t)b * A.ksb + (int64_t)h * A.ksh;
+  const float* wcache = reinterpret_cast<const float*>(A.g) + (int64_t)cache * A.node_cap * R * C;
+  const float* ccache = A.c + (int64_t)cache * A.node_cap * R;
+
+  // candidate bits of the tile's chunks for query qg0 + qn
+  auto block_bits = [&](int qg0) -> unsigned long long {
+    unsigned long long mb = 0ull;
+    if (qn < min(16, A.QC - qg0)) {
+      const int64_t nvalid = A.n_nodes - m0 < NCH ? A.n_nodes - m0 : NCH;
+      const unsigned long long valid = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1ull);
+      if (A.sel_parent) {
+        const int64_t p0 = m0 / C;
+        const uint32_t word =
+            A.sel_parent[((int64_t)cache * A.QC + qg0 + qn) * A.parent_words + (p0 >> 5)] >> (p0 & 31);
+#pragma unroll
+        for (int pi = 0; pi < NCH / C; ++pi)
+          if ((word >> pi) & 1u) mb |= ((1ull << C) - 1ull) << (pi * C);
+        mb &= valid;
+      } else {
+        mb = valid;
+      }
+      const int64_t hz = causal_horizon(A, qg0 + qn) - m0;
+      if (hz < 64) mb &= hz > 0 ? (1ull << hz) - 1ull : 0ull;
+    }
+    return mb;
+  };
+  unsigned long long anybits = 0ull;
+  for (int qb = 0; qb < nqb; ++qb) anybits |= block_bits(qz0 + 16 * qb);
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) anybits |= __shfl_xor(anybits, o);
+
+  const int64_t n_valid = min((int64_t)NCH, A.n_nodes - m0);
+  const rsrc_t wr = make_rsrc(wcache + m0 * R * C, (uint32_t)(n_valid * R * C * 4));
+  const rsrc_t cr = make_rsrc(ccache + m0 * R, (uint32_t)(n_valid * R * 4));
+  const int64_t rows = min((int64_t)KT, n_keys - k0);
+  const rsrc_t kr = make_rsrc(Kc + k0 * A.kst, (uint32_t)((rows - 1) * A.kst * 2 + D * 2));
+  constexpr int ITEMS = NCH * 16 / 256;
+  float4 wst[ITEMS][PARTS];
+  float cst[ITEMS];
+#pragma unroll
+  for (int r = 0; r < ITEMS; ++r) {
+    const int it = tid + 256 * r;
+    const int x = it / 16, j = it % 16;
+    const bool ok = ((anybits >> x) & 1ull) && j < R;
+    const uint32_t wo = ok ? (uint32_t)((x * R + j) * C * 4) : kOffNone;
+#pragma unroll
+    for (int pp = 0; pp < PARTS; ++pp) {
+      const uint4 v = bld16(wr, wo + pp * 16);
+      wst[r][pp] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+    }
+    cst[r] = bld4f(cr, ok ? (uint32_t)((x * R + j) * 4) : kOffNone);
+  }
+  uint4 kf[GPW][NS];
+  bool live[GPW];
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
+    const int g = wave * GPW + gi;
+    const unsigned long long gmask = ((1ull << (16 / C)) - 1ull) << (g * 16 / C);
+    live[gi] = (anybits & gmask) != 0ull;
+    const uint32_t ko = live[gi] ? (uint32_t)((g * 16 + qn) * A.kst * 2) : kOffNone;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kf[gi][s] = bld16<0>(kr, ko + (4 * s + kg) * 16);
+  }
+#pragma unroll
+  for (int r = 0; r < ITEMS; ++r) {
+    const int it = tid + 256 * r;
+    const int x = it / 16, j = it % 16;
+#pragma unroll
+    for (int pp = 0; pp < PARTS; ++pp) wl[x][j * PARTS + pp] = wst[r][pp];
+    cl[x][j] = cst[r];
+  }
+  __syncthreads();
+
+  const int RR = RT > 0 ? RT : R;
+  constexpr int UNR = RT <= 0 ? 1 : RT < 4 ? RT : 4;
+  const int QB = (A.QC + 15) / 16;  // 16-query blocks of the logits rows
+  for (int qb = 0; qb < nqb; ++qb) {
+    const int qg0 = qz0 + 16 * qb;
+    const int nq = min(16, A.QC - qg0);
+    const unsigned long long mybits = block_bits(qg0);
+    bf16x8 bq[NS];
+    {
+      const int qi = qg0 + qn;
+      if (qn < nq) {
+        const bf16_t* qp = reinterpret_cast<const bf16_t*>(A.Q) + (int64_t)b * A.qsb + (int64_t)h * A.qsh +
+                           (int64_t)(qi / A.T) * A.qsg + (int64_t)(qi % A.T) * A.qst;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) bq[s] = as_bf16x8(ld16(qp + (4 * s + kg) * 8));
+      } else {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) bq[s] = as_bf16x8(make_uint4(0, 0, 0, 0));
+      }
+    }
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) {
+      const int g = wave * GPW + gi;
+      const int x = (g * 16 + 4 * kg) / C;
+      const int part = kg % PARTS;
+      if (!live[gi]) {
+        if (part == 0) sc[qn][x] = kNegInf;
+        continue;
+      }
+      f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[gi][s]), bq[s], z, 0, 0, 0);
+      float zz[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zz[i] = z[i] * A.inv_sqrt_d;
+      const int64_t quad = (k0 + g * 16) / 4 + kg;
+      if (A.logits && qn < nq && quad < A.nquads) {
+        float* lp = A.logits + (((int64_t)cache * QB + qg0 / 16) * A.nquads + quad) * 4 * A.QW + qn;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lp[i * A.QW] = zz[i];
+      }
+      float best = kNegInf;
+#pragma unroll UNR
+      for (int jj = 0; jj < RR; ++jj) {
+        const float4 wv = wl[x][jj * PARTS + part];
+        float v = wv.x * zz[0] + wv.y * zz[1] + wv.z * zz[2] + wv.w * zz[3];
+#pragma unroll
+        for (int o = 16; o < 16 * PARTS; o <<= 1) v += __shfl_xor(v, o);
+        best = fmaxf(best, cl[x][jj] + v);
+      }
+      if (part == 0) sc[qn][x] = ((mybits >> x) & 1ull) ? best : kNegInf;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < nq * NCH; idx += 256) {
+      const int q = idx / NCH, x = idx % NCH;
+      const int64_t mm = m0 + x;
+      if (mm < A.n_nodes) A.score[((int64_t)cache * A.QC + qg0 + q) * A.score_stride + mm] = sc[q][x];
+    }
+    for (int q = wave; q < nq; q += 4) {
+      const float v = lane < NCH ? sc[q][lane] : kNegInf;
+      const bool c = lane < NCH && m0 + lane < A.n_nodes && v > kNegInf;
+      publish_range(A.keyrange + (((int64_t)cache * A.QC + qg0 + q) * A.kr_slots + blockIdx.x) * 4, c, order_key(v));
+    }
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------------------
 // prefill spine score (bf16 keys, levels >= 2): one wave per query scores the
 // partial node of its own prefix tree at this level, from the spine record of
@@ -1804,7 +1973,29 @@ hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dty
   hipStream_t s = prof.s;
   if (sa.n_nodes > 0) {
     prof.begin(ZHA_K_SCORE, level);
-    if (sa.leaf_weights) {
+    if (sa.leaf_weights && sa.QC > 16) {
+      dim3 grid((unsigned)((sa.n_nodes * sa.C + 255) / 256), (unsigned)n_caches,
+                (unsigned)((sa.QC + 16 * kMqBlocks - 1) / (16 * kMqBlocks)));
+#define ZHA_LWM(DD, CC)                                                                 \
+  do {                                                                                  \
+    if (sa.R == 16)                                                                     \
+      hipLaunchKernelGGL((k_score_leafw_mq<DD, CC, 16>), grid, dim3(256), 0, s, sa);    \
+    else if (sa.R == 1)                                                                 \
+      hipLaunchKernelGGL((k_score_leafw_mq<DD, CC, 1>), grid, dim3(256), 0, s, sa);     \
+    else                                                                                \
+      hipLaunchKernelGGL((k_score_leafw_mq<DD, CC, 0>), grid, dim3(256), 0, s, sa);     \
+  } while (0)
+      if (sa.D == 128) {
+        if (sa.C == 4) ZHA_LWM(128, 4);
+        else if (sa.C == 8) ZHA_LWM(128, 8);
+        else ZHA_LWM(128, 16);
+      } else {
+        if (sa.C == 4) ZHA_LWM(64, 4);
+        else if (sa.C == 8) ZHA_LWM(64, 8);
+        else ZHA_LWM(64, 16);
+      }
+#undef ZHA_LWM
+    } else if (sa.leaf_weights) {
       dim3 grid((unsigned)((sa.n_nodes * sa.C + 255) / 256), (unsigned)n_caches, (unsigned)((sa.QC + 15) / 16));
 #define ZHA_LW_Q(DD, CC, QQ)                                                            \
   do {                                                                                  \
