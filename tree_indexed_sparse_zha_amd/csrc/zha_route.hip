@@ -594,6 +594,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 // 16 kMqBlocks queries instead of once per 16.  Per block the arithmetic is
 // the one of k_score_leafw (MFMA over the keys, fold in the MFMA layout).
 constexpr int kMqBlocks = 16;
+// below this many (tile, cache) pairs a level keeps one query block per
+// workgroup: walking 16 blocks in one workgroup would leave the GPU idle
+constexpr int64_t kMqMinTiles = 256;
 
 template <int D, int C, int RT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_score_leafw_mq(ScoreArgs A) {
@@ -754,6 +757,147 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       publish_range(A.keyrange + (((int64_t)cache * A.QC + qg0 + q) * A.kr_slots + blockIdx.x) * 4, c, order_key(v));
     }
     __syncthreads();
+  }
+}
+
+// Levels >= 2 for many queries per cache (QC > 16, bf16 g, R > 8): a
+// workgroup takes 64 nodes (16 per wave, in batches of 4 held in registers)
+// and walks up to kMqBlocks query blocks of 16 over each batch, so the nodes
+// are read once per 16 kMqBlocks queries.  Scores go straight to the rows
+// (lane kg writes node kg of the batch); each (query, tile) key-range slot is
+// gathered with LDS atomics and written once.
+template <int D>
+__global__ __launch_bounds__(256) void k_score_bf16_mq(ScoreArgs A) {
+  constexpr int NS = D / 32;
+  constexpr int TILE = 64;
+  constexpr int NB = 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cache = blockIdx.y;
+  const int qz0 = blockIdx.z * 16 * kMqBlocks;
+  const int nqb = min(kMqBlocks, (A.QC - qz0 + 15) / 16);
+  const int64_t n0 = (int64_t)blockIdx.x * TILE;
+  const int64_t nb0 = n0 + wave * 16;
+  const int R = A.R;
+  const int qn = lane & 15, kg = lane >> 4;
+  const int b = cache / A.H, h = cache % A.H;
+  __shared__ uint32_t krl[kMqBlocks][16][3];  // per (block, query): max key, min key, count
+
+  for (int i = tid; i < kMqBlocks * 16; i += 256) {
+    krl[i / 16][i % 16][0] = 0u;
+    krl[i / 16][i % 16][1] = 0xffffffffu;
+    krl[i / 16][i % 16][2] = 0u;
+  }
+  const int64_t gnode = (int64_t)R * D * 2;
+  const char* gcache = A.g + (int64_t)cache * A.node_cap * gnode;
+  const float* ccache = A.c + (int64_t)cache * A.node_cap * R;
+
+  // candidate bits of this wave's 16 nodes for query qg0 + qn
+  auto block_bits = [&](int qg0) -> uint32_t {
+    uint32_t mb = 0u;
+    if (qn < min(16, A.QC - qg0)) {
+      const int64_t nvalid = A.n_nodes - nb0 < 16 ? (A.n_nodes - nb0 > 0 ? A.n_nodes - nb0 : 0) : 16;
+      const uint32_t valid = (uint32_t)((1ull << nvalid) - 1ull);
+      if (A.sel_parent) {
+        if (A.C >= 16) {
+          for (int u = 0; u < 16; ++u) {
+            const int64_t par = (nb0 + u) / A.C;
+            const uint32_t w = A.sel_parent[((int64_t)cache * A.QC + qg0 + qn) * A.parent_words + (par >> 5)];
+            if ((w >> (par & 31)) & 1u) mb |= 1u << u;
+          }
+        } else {
+          const int64_t p0 = nb0 / A.C;
+          const uint32_t word =
+              A.sel_parent[((int64_t)cache * A.QC + qg0 + qn) * A.parent_words + (p0 >> 5)] >> (p0 & 31);
+          for (int pi = 0; pi < 16 / A.C; ++pi)
+            if ((word >> pi) & 1u) mb |= ((1u << A.C) - 1u) << (pi * A.C);
+        }
+        mb &= valid;
+      } else {
+        mb = valid;
+      }
+      const int64_t hz = causal_horizon(A, qg0 + qn) - nb0;
+      if (hz < 16) mb &= hz > 0 ? (1u << hz) - 1u : 0u;
+    }
+    return mb;
+  };
+  uint32_t anybits = 0u;
+  for (int qb = 0; qb < nqb; ++qb) anybits |= block_bits(qz0 + 16 * qb);
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) anybits |= (uint32_t)__shfl_xor((int)anybits, o);
+  __syncthreads();  // krl initialised
+
+  const int jrow = lane & 15;
+  for (int u0 = 0; u0 < 16; u0 += NB) {
+    uint4 af[NB][NS];
+    float cv[NB][4];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int u = u0 + k;
+      const int64_t m = nb0 + u;
+      const bool live = (anybits >> u) & 1u;
+      const char* gn = gcache + m * gnode;
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        af[k][s] = live && jrow < R ? ld16(gn + ((int64_t)(4 * s + kg) * R + jrow) * 16) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int jj = 4 * kg + i;
+        cv[k][i] = live && jj < R ? ccache[m * R + jj] : kNegInf;
+      }
+    }
+    for (int qb = 0; qb < nqb; ++qb) {
+      const int qg0 = qz0 + 16 * qb;
+      const int nq = min(16, A.QC - qg0);
+      const uint32_t mybits = block_bits(qg0);
+      bf16x8 bq[NS];
+      {
+        const int qi = qg0 + qn;
+        if (qn < nq) {
+          const bf16_t* qp = reinterpret_cast<const bf16_t*>(A.Q) + (int64_t)b * A.qsb + (int64_t)h * A.qsh +
+                             (int64_t)(qi / A.T) * A.qsg + (int64_t)(qi % A.T) * A.qst;
+#pragma unroll
+          for (int s = 0; s < NS; ++s) bq[s] = as_bf16x8(ld16(qp + (4 * s + kg) * 8));
+        } else {
+#pragma unroll
+          for (int s = 0; s < NS; ++s) bq[s] = as_bf16x8(make_uint4(0, 0, 0, 0));
+        }
+      }
+      float mine = kNegInf;  // this lane's node: u0 + kg
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const int u = u0 + k;
+        float v = kNegInf;
+        if ((anybits >> u) & 1u) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < NS; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af[k][s]), bq[s], acc, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v = fmaxf(v, cv[k][i] + acc[i] * A.inv_sqrt_d);
+          v = fmaxf(v, __shfl_xor(v, 16));
+          v = fmaxf(v, __shfl_xor(v, 32));
+        }
+        if (k == kg) mine = ((mybits >> u) & 1u) ? v : kNegInf;
+      }
+      const int64_t m = nb0 + u0 + kg;
+      if (qn < nq && m < A.n_nodes) {
+        A.score[((int64_t)cache * A.QC + qg0 + qn) * A.score_stride + m] = mine;
+        if (mine > kNegInf) {
+          const uint32_t key = order_key(mine);
+          atomicMax(&krl[qb][qn][0], key);
+          atomicMin(&krl[qb][qn][1], key);
+          atomicAdd(&krl[qb][qn][2], 1u);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < nqb * 16; i += 256) {
+    const int qb = i / 16, q = i % 16;
+    const int qg0 = qz0 + 16 * qb;
+    if (q < min(16, A.QC - qg0)) {
+      uint32_t* slot = A.keyrange + (((int64_t)cache * A.QC + qg0 + q) * A.kr_slots + blockIdx.x) * 4;
+      *reinterpret_cast<uint4*>(slot) = make_uint4(krl[qb][q][0], krl[qb][q][1], krl[qb][q][2], 0u);
+    }
   }
 }
 
@@ -1973,7 +2117,7 @@ hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dty
   hipStream_t s = prof.s;
   if (sa.n_nodes > 0) {
     prof.begin(ZHA_K_SCORE, level);
-    if (sa.leaf_weights && sa.QC > 16) {
+    if (sa.leaf_weights && sa.QC > 16 && (sa.n_nodes * sa.C + 255) / 256 * n_caches >= kMqMinTiles) {
       dim3 grid((unsigned)((sa.n_nodes * sa.C + 255) / 256), (unsigned)n_caches,
                 (unsigned)((sa.QC + 16 * kMqBlocks - 1) / (16 * kMqBlocks)));
 #define ZHA_LWM(DD, CC)                                                                 \
@@ -2031,6 +2175,13 @@ hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dty
           hipLaunchKernelGGL((k_score_bf16<128, true>), grid, dim3(256), 0, s, sa);
         else
           hipLaunchKernelGGL((k_score_bf16<64, true>), grid, dim3(256), 0, s, sa);
+      } else if (sa.R > 8 && sa.QC > 16 && (sa.n_nodes + 63) / 64 * n_caches >= kMqMinTiles) {
+        dim3 gmq((unsigned)((sa.n_nodes + 63) / 64), (unsigned)n_caches,
+                 (unsigned)((sa.QC + 16 * kMqBlocks - 1) / (16 * kMqBlocks)));
+        if (sa.D == 128)
+          hipLaunchKernelGGL((k_score_bf16_mq<128>), gmq, dim3(256), 0, s, sa);
+        else
+          hipLaunchKernelGGL((k_score_bf16_mq<64>), gmq, dim3(256), 0, s, sa);
       } else if (sa.R <= 8) {
 #define ZHA_SR(DD)                                                                          \
   do {                                                                                      \
