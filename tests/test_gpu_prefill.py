@@ -32,13 +32,16 @@ def np64(t):
 
 
 CASES = [
-    # name, cfg kwargs, N, T, p
+    # name, cfg kwargs, N, T, p (, queries sampled per cache, caches checked)
     ("weights-C4-d128", dict(batch=1, n_kv_heads=2, q_per_kv=2, head_dim=128, n_ref=16, chunk=4, levels=4,
                              leaf_form="weights"), 3000, 96, 0.9),
     ("mean-fp8-C8-d64", dict(batch=1, n_kv_heads=1, q_per_kv=2, head_dim=64, n_ref=5, chunk=8, levels=3,
                              g_dtype="fp8"), 2100, 64, 0.85),
     ("weights-C16-start", dict(batch=1, n_kv_heads=1, q_per_kv=2, head_dim=128, n_ref=4, chunk=16, levels=2,
                                leaf_form="weights"), 300, 300, 0.9),
+    # enough tiles that levels 1 and 2 walk several query blocks per workgroup
+    ("weights-many-tiles", dict(batch=1, n_kv_heads=4, q_per_kv=2, head_dim=128, n_ref=16, chunk=4, levels=5,
+                                leaf_form="weights"), 65536 + 100, 16, 0.9, 2, [0, 3]),
 ]
 
 
@@ -80,8 +83,11 @@ def _level_rows(cfg, buf, N, qi):
     return bits, scores
 
 
-@pytest.mark.parametrize("name,kw,N,T,p", CASES, ids=[c[0] for c in CASES])
-def test_prefill_matches_prefix_decode(name, kw, N, T, p):
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_prefill_matches_prefix_decode(case):
+    name, kw, N, T, p = case[:5]
+    n_pick = case[5] if len(case) > 5 else 10
+    caches_checked = case[6] if len(case) > 6 else None
     _say(f"prefill {name}")
     cfg = zha.ZhaConfig(dtype="bf16", capacity=N, **kw)
     K, V, Q, ref = _inputs(cfg, N, T, seed=41)
@@ -107,10 +113,10 @@ def test_prefill_matches_prefix_decode(name, kw, N, T, p):
     QC = cfg.q_per_kv * T
     tol = PAR.OUT_TOL["bf16"]
     rng = np.random.default_rng(3)
-    for cache in range(cfg.n_caches):
+    for cache in (caches_checked if caches_checked is not None else range(cfg.n_caches)):
         b, h = divmod(cache, cfg.n_kv_heads)
         Kn, Vn, rn = np64(K[b, h]), np64(V[b, h]), np64(ref[h])
-        picks = sorted(set([0, QC - 1, QC // 2] + rng.choice(QC, size=min(10, QC), replace=False).tolist()))
+        picks = sorted(set([0, QC - 1, QC // 2] + rng.choice(QC, size=min(n_pick, QC), replace=False).tolist()))
         for ql in picks:
             gq, t = divmod(ql, T)
             pos = N - T + t
