@@ -551,11 +551,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       // the wave's 16 quads as rows [quad][key][query]: lane (quad qq, key
       // kk) gathers the 4 queries' logits of its key and stores them as one
       // 16-byte piece, so the wave writes 1 KiB with one coalesced store
-      // (quads of groups without a candidate are not written)
+      // (quads of chunks that are no query's candidate are not written:
+      // attention reads logits of kept chunks only)
       const int qq = lane >> 2, kk = lane & 3;
-      const unsigned long long gm = ((1ull << (16 / C)) - 1ull) << ((wave * GPW + (qq >> 2)) * 16 / C);
+      const int xq = (wave * 64 + 4 * qq) / C;  // chunk of the quad within the tile
       const int64_t quad = (k0 + wave * 64) / 4 + qq;
-      if ((anybits & gm) != 0ull && quad < A.nquads) {
+      if (((anybits >> xq) & 1ull) && quad < A.nquads) {
         const float* zr = reinterpret_cast<const float*>(&zl[wave][qq][0]);
         *reinterpret_cast<float4*>(A.logits + ((((int64_t)cache * gridDim.z + blockIdx.z) * A.nquads + quad) * 4 + kk) * 4) =
             make_float4(zr[kk], zr[4 + kk], zr[8 + kk], zr[12 + kk]);
