@@ -89,6 +89,61 @@ __global__ void k_route_init(uint32_t* kr, int64_t n) {
 // ---------------------------------------------------------------------------
 // score, bf16, MFMA
 
+// Candidate bits of 16 consecutive nodes nb0 .. nb0 + 15 of a level (bit u =
+// node nb0 + u) for query qi of a cache: nodes that exist whose parent the
+// query kept (every node at the top level), and, in prefill, only the
+// query's complete nodes (below its horizon).  The nodes' 16 / C parents
+// lie in one bitset word when C < 16.
+__device__ __forceinline__ uint32_t node_bits16(const ScoreArgs& A, int cache, int qi, int64_t nb0) {
+  const int64_t nvalid = A.n_nodes - nb0 < 16 ? (A.n_nodes - nb0 > 0 ? A.n_nodes - nb0 : 0) : 16;
+  const uint32_t valid = (uint32_t)((1ull << nvalid) - 1ull);
+  uint32_t mb = 0u;
+  if (A.sel_parent) {
+    const uint32_t* row = A.sel_parent + ((int64_t)cache * A.QC + qi) * A.parent_words;
+    if (A.C >= 16) {
+      // every node has one of at most two parents; test each node
+      for (int u = 0; u < 16; ++u) {
+        const int64_t par = (nb0 + u) / A.C;
+        if ((row[par >> 5] >> (par & 31)) & 1u) mb |= 1u << u;
+      }
+    } else {
+      const int64_t p0 = nb0 / A.C;
+      const uint32_t word = row[p0 >> 5] >> (p0 & 31);
+      for (int pi = 0; pi < 16 / A.C; ++pi)
+        if ((word >> pi) & 1u) mb |= ((1u << A.C) - 1u) << (pi * A.C);
+    }
+    mb &= valid;
+  } else {
+    mb = valid;
+  }
+  const int64_t hz = causal_horizon(A, qi) - nb0;
+  if (hz < 16) mb &= hz > 0 ? (1u << hz) - 1u : 0u;
+  return mb;
+}
+
+// Candidate bits of the NCH (<= 64) chunks m0 .. m0 + NCH - 1 of a level-1
+// tile for query qi, as node_bits16 (the chunks' NCH / C parents lie in one
+// bitset word).
+template <int NCH, int C>
+__device__ __forceinline__ unsigned long long chunk_bits(const ScoreArgs& A, int cache, int qi, int64_t m0) {
+  const int64_t nvalid = A.n_nodes - m0 < NCH ? A.n_nodes - m0 : NCH;
+  const unsigned long long valid = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1ull);
+  unsigned long long mb = 0ull;
+  if (A.sel_parent) {
+    const int64_t p0 = m0 / C;
+    const uint32_t word = A.sel_parent[((int64_t)cache * A.QC + qi) * A.parent_words + (p0 >> 5)] >> (p0 & 31);
+#pragma unroll
+    for (int pi = 0; pi < NCH / C; ++pi)
+      if ((word >> pi) & 1u) mb |= ((1ull << C) - 1ull) << (pi * C);
+    mb &= valid;
+  } else {
+    mb = valid;
+  }
+  const int64_t hz = causal_horizon(A, qi) - m0;
+  if (hz < 64) mb &= hz > 0 ? (1ull << hz) - 1ull : 0ull;
+  return mb;
+}
+
 // G8: g stored as fp8 E4M3 with a power-of-two scale per row; each 16-byte
 // load holds two MFMA steps, converted to bf16 with the row's scale applied
 // (exact: E4M3 values times powers of two are bf16 values).
@@ -125,36 +180,8 @@ __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs A) {
   const float* ccache = A.c + (int64_t)cache * A.node_cap * R;
   const int jrow = lane & 15;
 
-  // candidate bits of this wave's 16 nodes for query qn (their 16 / C parents
-  // lie in one bitset word), then per-node "any query"
-  uint32_t mybits = 0u;
-  if (qn < nq) {
-    const int64_t nb0 = n0 + wave * 16;
-    const int64_t nvalid = A.n_nodes - nb0 < 16 ? (A.n_nodes - nb0 > 0 ? A.n_nodes - nb0 : 0) : 16;
-    const uint32_t valid = (uint32_t)((1ull << nvalid) - 1ull);
-    if (A.sel_parent) {
-      if (A.C >= 16) {
-        // every node of the wave has one of at most two parents; test each node
-        for (int u = 0; u < 16; ++u) {
-          const int64_t par = (nb0 + u) / A.C;
-          const uint32_t w = A.sel_parent[((int64_t)cache * A.QC + qg0 + qn) * A.parent_words + (par >> 5)];
-          if ((w >> (par & 31)) & 1u) mybits |= 1u << u;
-        }
-      } else {
-        const int64_t p0 = nb0 / A.C;
-        const uint32_t word =
-            A.sel_parent[((int64_t)cache * A.QC + qg0 + qn) * A.parent_words + (p0 >> 5)] >> (p0 & 31);
-        for (int pi = 0; pi < 16 / A.C; ++pi)
-          if ((word >> pi) & 1u) mybits |= ((1u << A.C) - 1u) << (pi * A.C);
-      }
-      mybits &= valid;
-    } else {
-      mybits = valid;
-    }
-    // prefill: nodes at or beyond the query's horizon are not its complete nodes
-    const int64_t hz = causal_horizon(A, qg0 + qn) - nb0;
-    if (hz < 16) mybits &= hz > 0 ? (1u << hz) - 1u : 0u;
-  }
+  // candidate bits of this wave's 16 nodes for query qn, then per-node "any query"
+  const uint32_t mybits = qn < nq ? node_bits16(A, cache, qg0 + qn, n0 + wave * 16) : 0u;
   uint32_t anybits = mybits;
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) anybits |= (uint32_t)__shfl_xor((int)anybits, o);
@@ -281,31 +308,7 @@ __global__ __launch_bounds__(256) void k_score_smallr(ScoreArgs A) {
 
   // candidate bits of this wave's 16 nodes for query qn, then "any query"
   const int64_t nb0 = n0 + wave * 16;
-  uint32_t mybits = 0u;
-  if (qn < nq) {
-    const int64_t nvalid = A.n_nodes - nb0 < 16 ? (A.n_nodes - nb0 > 0 ? A.n_nodes - nb0 : 0) : 16;
-    const uint32_t valid = (uint32_t)((1ull << nvalid) - 1ull);
-    if (A.sel_parent) {
-      if (A.C >= 16) {
-        for (int u = 0; u < 16; ++u) {
-          const int64_t par = (nb0 + u) / A.C;
-          const uint32_t w = A.sel_parent[((int64_t)cache * A.QC + qg0 + qn) * A.parent_words + (par >> 5)];
-          if ((w >> (par & 31)) & 1u) mybits |= 1u << u;
-        }
-      } else {
-        const int64_t p0 = nb0 / A.C;
-        const uint32_t word =
-            A.sel_parent[((int64_t)cache * A.QC + qg0 + qn) * A.parent_words + (p0 >> 5)] >> (p0 & 31);
-        for (int pi = 0; pi < 16 / A.C; ++pi)
-          if ((word >> pi) & 1u) mybits |= ((1u << A.C) - 1u) << (pi * A.C);
-      }
-      mybits &= valid;
-    } else {
-      mybits = valid;
-    }
-    const int64_t hz = causal_horizon(A, qg0 + qn) - nb0;
-    if (hz < 16) mybits &= hz > 0 ? (1u << hz) - 1u : 0u;
-  }
+  const uint32_t mybits = qn < nq ? node_bits16(A, cache, qg0 + qn, nb0) : 0u;
   uint32_t anybits = mybits;
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) anybits |= (uint32_t)__shfl_xor((int)anybits, o);
@@ -428,27 +431,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   const float* wcache = reinterpret_cast<const float*>(A.g) + (int64_t)cache * A.node_cap * R * C;
   const float* ccache = A.c + (int64_t)cache * A.node_cap * R;
 
-  // candidate bits of the tile's chunks for query qn (bit x = chunk m0 + x).
-  // The tile's NCH chunks have NCH / C parents, which lie in one bitset word.
-  unsigned long long mybits = 0ull;
-  if (qn < nq) {
-    const int64_t nvalid = A.n_nodes - m0 < NCH ? A.n_nodes - m0 : NCH;
-    const unsigned long long valid = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1ull);
-    if (A.sel_parent) {
-      const int64_t p0 = m0 / C;
-      const uint32_t word =
-          A.sel_parent[((int64_t)cache * A.QC + qg0 + qn) * A.parent_words + (p0 >> 5)] >> (p0 & 31);
-#pragma unroll
-      for (int pi = 0; pi < NCH / C; ++pi)
-        if ((word >> pi) & 1u) mybits |= ((1ull << C) - 1ull) << (pi * C);
-      mybits &= valid;
-    } else {
-      mybits = valid;
-    }
-    // prefill: only the complete chunks below the query's horizon
-    const int64_t hz = causal_horizon(A, qg0 + qn) - m0;
-    if (hz < 64) mybits &= hz > 0 ? (1ull << hz) - 1ull : 0ull;
-  }
+  // candidate bits of the tile's chunks for query qn (bit x = chunk m0 + x)
+  const unsigned long long mybits = qn < nq ? chunk_bits<NCH, C>(A, cache, qg0 + qn, m0) : 0ull;
   // chunks that are a candidate of some query (same value in every lane)
   unsigned long long anybits = mybits;
 #pragma unroll
@@ -627,25 +611,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 
   // candidate bits of the tile's chunks for query qg0 + qn
   auto block_bits = [&](int qg0) -> unsigned long long {
-    unsigned long long mb = 0ull;
-    if (qn < min(16, A.QC - qg0)) {
-      const int64_t nvalid = A.n_nodes - m0 < NCH ? A.n_nodes - m0 : NCH;
-      const unsigned long long valid = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1ull);
-      if (A.sel_parent) {
-        const int64_t p0 = m0 / C;
-        const uint32_t word =
-            A.sel_parent[((int64_t)cache * A.QC + qg0 + qn) * A.parent_words + (p0 >> 5)] >> (p0 & 31);
-#pragma unroll
-        for (int pi = 0; pi < NCH / C; ++pi)
-          if ((word >> pi) & 1u) mb |= ((1ull << C) - 1ull) << (pi * C);
-        mb &= valid;
-      } else {
-        mb = valid;
-      }
-      const int64_t hz = causal_horizon(A, qg0 + qn) - m0;
-      if (hz < 64) mb &= hz > 0 ? (1ull << hz) - 1ull : 0ull;
-    }
-    return mb;
+    return qn < min(16, A.QC - qg0) ? chunk_bits<NCH, C>(A, cache, qg0 + qn, m0) : 0ull;
   };
   unsigned long long anybits = 0ull;
   for (int qb = 0; qb < nqb; ++qb) anybits |= block_bits(qz0 + 16 * qb);
@@ -794,32 +760,7 @@ __global__ __launch_bounds__(256) void k_score_bf16_mq(ScoreArgs A) {
 
   // candidate bits of this wave's 16 nodes for query qg0 + qn
   auto block_bits = [&](int qg0) -> uint32_t {
-    uint32_t mb = 0u;
-    if (qn < min(16, A.QC - qg0)) {
-      const int64_t nvalid = A.n_nodes - nb0 < 16 ? (A.n_nodes - nb0 > 0 ? A.n_nodes - nb0 : 0) : 16;
-      const uint32_t valid = (uint32_t)((1ull << nvalid) - 1ull);
-      if (A.sel_parent) {
-        if (A.C >= 16) {
-          for (int u = 0; u < 16; ++u) {
-            const int64_t par = (nb0 + u) / A.C;
-            const uint32_t w = A.sel_parent[((int64_t)cache * A.QC + qg0 + qn) * A.parent_words + (par >> 5)];
-            if ((w >> (par & 31)) & 1u) mb |= 1u << u;
-          }
-        } else {
-          const int64_t p0 = nb0 / A.C;
-          const uint32_t word =
-              A.sel_parent[((int64_t)cache * A.QC + qg0 + qn) * A.parent_words + (p0 >> 5)] >> (p0 & 31);
-          for (int pi = 0; pi < 16 / A.C; ++pi)
-            if ((word >> pi) & 1u) mb |= ((1u << A.C) - 1u) << (pi * A.C);
-        }
-        mb &= valid;
-      } else {
-        mb = valid;
-      }
-      const int64_t hz = causal_horizon(A, qg0 + qn) - nb0;
-      if (hz < 16) mb &= hz > 0 ? (1u << hz) - 1u : 0u;
-    }
-    return mb;
+    return qn < min(16, A.QC - qg0) ? node_bits16(A, cache, qg0 + qn, nb0) : 0u;
   };
   uint32_t anybits = 0u;
   for (int qb = 0; qb < nqb; ++qb) anybits |= block_bits(qz0 + 16 * qb);
