@@ -290,6 +290,92 @@ __device__ __forceinline__ int block_scan_excl(int cnt, int* scan, int* excl) {
   return scan[kAttThreads - 1];
 }
 
+constexpr int kMaxForcedQuads = 16;
+
+// Phase 1 of the bf16 kernels, compaction: the tile's quads with a key some
+// query of the group attends, in LDS as (quad index, 4-bit key mask per
+// query).  SPLIT puts the quads holding a routed chunk first (*n_r of them)
+// and the forced-only quads (sink, current chunk) after them, at most
+// kMaxForcedQuads; otherwise all quads are in key order and *n_r = *n_ent.
+template <int QG, bool SPLIT>
+__device__ __forceinline__ void collect_quads(const AttendArgs& A, int cache, int qg0, int nq, int64_t k_lo,
+                                              int64_t k_hi, uint16_t* e_quad, unsigned long long* e_mask,
+                                              int* scan, int* n_r, int* n_ent) {
+  const int tid = threadIdx.x;
+  unsigned long long qmask[kQPT];
+  uint32_t routed;
+  quad_masks<QG>(A, cache, qg0, nq, k_lo, k_hi, tid, qmask, &routed);
+  if constexpr (SPLIT) {
+    int cnt = 0;  // routed count in the low 16 bits, forced-only count above
+#pragma unroll
+    for (int i = 0; i < kQPT; ++i)
+      if (qmask[i]) cnt += ((routed >> i) & 1u) ? 1 : (1 << 16);
+    int excl;
+    const int tot = block_scan_excl(cnt, scan, &excl);
+    *n_r = tot & 0xffff;
+    *n_ent = *n_r + min(tot >> 16, kMaxForcedQuads);
+    int pos_r = excl & 0xffff, pos_f = *n_r + (excl >> 16);
+#pragma unroll
+    for (int i = 0; i < kQPT; ++i) {
+      if (qmask[i]) {
+        const int pos = ((routed >> i) & 1u) ? pos_r++ : pos_f++;
+        if (pos < *n_ent) {
+          e_quad[pos] = (uint16_t)(tid * kQPT + i);
+          e_mask[pos] = qmask[i];
+        }
+      }
+    }
+  } else {
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < kQPT; ++i) cnt += qmask[i] != 0ull;
+    int pos;
+    *n_ent = block_scan_excl(cnt, scan, &pos);
+    *n_r = *n_ent;
+#pragma unroll
+    for (int i = 0; i < kQPT; ++i) {
+      if (qmask[i]) {
+        e_quad[pos] = (uint16_t)(tid * kQPT + i);
+        e_mask[pos] = qmask[i];
+        ++pos;
+      }
+    }
+  }
+}
+
+// Phase 1b: logits of the n_f forced-only quads (entries n_r ..), one thread
+// per key and query, into f_log[f][query][key].
+template <int D, int QG>
+__device__ __forceinline__ void forced_logits(const AttendArgs& A, const bf16_t* Kc, int b, int h, int qg0, int nq,
+                                              int64_t k_lo, int64_t k_hi, const uint16_t* e_quad, int n_r, int n_f,
+                                              float (*f_log)[QG][4]) {
+  constexpr int PIECES = D / 8;
+  for (int idx = threadIdx.x; idx < n_f * 4 * QG; idx += kAttThreads) {
+    const int f = idx / (4 * QG), kk = (idx / QG) % 4, u = idx % QG;
+    const int64_t key = k_lo + 4 * (int64_t)e_quad[n_r + f] + kk;
+    float z = kNegInf;
+    if (u < nq && key < k_hi) {
+      const int qi = qg0 + u;
+      const bf16_t* qp = reinterpret_cast<const bf16_t*>(A.Q) + (int64_t)b * A.qsb + (int64_t)h * A.qsh +
+                         (int64_t)(qi / A.T) * A.qsg + (int64_t)(qi % A.T) * A.qst;
+      const bf16_t* kp = Kc + key * A.st;
+      float dot = 0.f;
+#pragma unroll
+      for (int pc = 0; pc < PIECES; ++pc) {
+        float kv[8], qv[8];
+        unpack(ld16(kp + pc * 8), kv, bf16_t());
+        unpack(ld16(qp + pc * 8), qv, bf16_t());
+#pragma unroll
+        for (int x = 0; x < 8; ++x) dot += kv[x] * qv[x];
+      }
+      z = dot * A.inv_sqrt_d;
+    }
+    f_log[f][u][kk] = z;
+  }
+}
+
+
+
 // Combines the 4 waves' (max, sum, weighted V sum) per query and writes the
 // workgroup's partial result for the tile.
 template <int D, int QG>
@@ -383,25 +469,8 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_mfma(AttendArgs A) {
   __shared__ float red[4][QG][D + 2];
 
   // ---- phase 1
-  int n_ent;
-  {
-    unsigned long long qmask[kQPT];
-    uint32_t routed;
-    quad_masks<QG>(A, cache, qg0, nq, k_lo, k_hi, tid, qmask, &routed);
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < kQPT; ++i) cnt += qmask[i] != 0ull;
-    int pos;
-    n_ent = block_scan_excl(cnt, scan, &pos);
-#pragma unroll
-    for (int i = 0; i < kQPT; ++i) {
-      if (qmask[i]) {
-        e_quad[pos] = (uint16_t)(tid * kQPT + i);
-        e_mask[pos] = qmask[i];
-        ++pos;
-      }
-    }
-  }
+  int n_r, n_ent;
+  collect_quads<QG, false>(A, cache, qg0, nq, k_lo, k_hi, e_quad, e_mask, scan, &n_r, &n_ent);
   __syncthreads();
 
   // ---- phase 2
@@ -555,13 +624,11 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_mfma(AttendArgs A) {
 // chunk, which lies inside one tile: at most 5 quads; in a prefill block the
 // group's queries have up to 3 current chunks, at most 13 quads); the logits
 // of those few are computed once into LDS.  Phase 2: lanes are (quad of the step, key of the quad,
-// 16-byte piece of the row); each wave takes every 4th step, with up to 8
-// steps of V (one coalesced 1 KiB load per quad for d = 128) and their cached
-// logits in flight at once (fewer for larger query groups, whose accumulators
-// take the registers), and keeps a per-lane online softmax (one rescale per
-// batch) in fp32.  No LDS traffic or barrier in the loop.
-constexpr int kMaxForcedQuads = 16;
-
+// 16-byte piece of the row); each wave takes every 4th step, with 4 steps of
+// V (one coalesced 1 KiB load per quad for d = 128) and their cached logits
+// in flight at once, and keeps a per-lane online softmax (one rescale per
+// batch) in fp32.  No LDS traffic or barrier in the loop.  Groups of 16
+// queries go to k_attend_pv16 instead.
 template <int D, int QG>
 __global__ __launch_bounds__(kAttThreads) void k_attend_cached(AttendArgs A) {
   constexpr int PIECES = D / 8;   // 16-byte pieces per row
@@ -587,61 +654,18 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_cached(AttendArgs A) {
   __shared__ float f_log[kMaxForcedQuads][QG][4];
   __shared__ float red[4][QG][D + 2];
 
-  // ---- phase 1
-  int n_r, n_f;
-  {
-    unsigned long long qmask[kQPT];
-    uint32_t routed;
-    quad_masks<QG>(A, cache, qg0, nq, k_lo, k_hi, tid, qmask, &routed);
-    int cnt = 0;  // routed count in the low 16 bits, forced-only count above
-#pragma unroll
-    for (int i = 0; i < kQPT; ++i)
-      if (qmask[i]) cnt += ((routed >> i) & 1u) ? 1 : (1 << 16);
-    int excl;
-    const int tot = block_scan_excl(cnt, scan, &excl);
-    n_r = tot & 0xffff;
-    n_f = min(tot >> 16, kMaxForcedQuads);
-    int pos_r = excl & 0xffff, pos_f = n_r + (excl >> 16);
-#pragma unroll
-    for (int i = 0; i < kQPT; ++i) {
-      if (qmask[i]) {
-        const int pos = ((routed >> i) & 1u) ? pos_r++ : pos_f++;
-        if (pos < n_r + n_f) {
-          e_quad[pos] = (uint16_t)(tid * kQPT + i);
-          e_mask[pos] = qmask[i];
-        }
-      }
-    }
-  }
+  // ---- phase 1: routed quads first, then the forced-only ones
+  int n_r, n_ent;
+  collect_quads<QG, true>(A, cache, qg0, nq, k_lo, k_hi, e_quad, e_mask, scan, &n_r, &n_ent);
+  const int n_f = n_ent - n_r;
   __syncthreads();
 
   const bf16_t* Kc = reinterpret_cast<const bf16_t*>(A.K) + (int64_t)b * A.sb + (int64_t)h * A.sh;
   const bf16_t* Vc = reinterpret_cast<const bf16_t*>(A.V) + (int64_t)b * A.sb + (int64_t)h * A.sh;
 
-  // ---- phase 1b: logits of the forced-only quads (one thread per key and query)
+  // ---- phase 1b: logits of the forced-only quads
   if (n_f) {
-    for (int idx = tid; idx < n_f * 4 * QG; idx += kAttThreads) {
-      const int f = idx / (4 * QG), kk = (idx / QG) % 4, u = idx % QG;
-      const int64_t key = k_lo + 4 * (int64_t)e_quad[n_r + f] + kk;
-      float z = kNegInf;
-      if (u < nq && key < k_hi) {
-        const int qi = qg0 + u;
-        const bf16_t* qp = reinterpret_cast<const bf16_t*>(A.Q) + (int64_t)b * A.qsb + (int64_t)h * A.qsh +
-                           (int64_t)(qi / A.T) * A.qsg + (int64_t)(qi % A.T) * A.qst;
-        const bf16_t* kp = Kc + key * A.st;
-        float dot = 0.f;
-#pragma unroll
-        for (int pc = 0; pc < PIECES; ++pc) {
-          float kv[8], qv[8];
-          unpack(ld16(kp + pc * 8), kv, bf16_t());
-          unpack(ld16(qp + pc * 8), qv, bf16_t());
-#pragma unroll
-          for (int x = 0; x < 8; ++x) dot += kv[x] * qv[x];
-        }
-        z = dot * A.inv_sqrt_d;
-      }
-      f_log[f][u][kk] = z;
-    }
+    forced_logits<D, QG>(A, Kc, b, h, qg0, nq, k_lo, k_hi, e_quad, n_r, n_f, f_log);
     __syncthreads();
   }
 
@@ -774,76 +798,14 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_pv16(AttendArgs A) {
   // ---- phase 1: the tile's quads with a key some query attends, routed
   // quads first (CACHED) or in key order
   int n_r, n_ent;
-  {
-    unsigned long long qmask[kQPT];
-    uint32_t routed;
-    quad_masks<QG>(A, cache, qg0, nq, k_lo, k_hi, tid, qmask, &routed);
-    if constexpr (CACHED) {
-      int cnt = 0;  // routed count in the low 16 bits, forced-only count above
-#pragma unroll
-      for (int i = 0; i < kQPT; ++i)
-        if (qmask[i]) cnt += ((routed >> i) & 1u) ? 1 : (1 << 16);
-      int excl;
-      const int tot = block_scan_excl(cnt, scan, &excl);
-      n_r = tot & 0xffff;
-      n_ent = n_r + min(tot >> 16, kMaxForcedQuads);
-      int pos_r = excl & 0xffff, pos_f = n_r + (excl >> 16);
-#pragma unroll
-      for (int i = 0; i < kQPT; ++i) {
-        if (qmask[i]) {
-          const int pos = ((routed >> i) & 1u) ? pos_r++ : pos_f++;
-          if (pos < n_ent) {
-            e_quad[pos] = (uint16_t)(tid * kQPT + i);
-            e_mask[pos] = qmask[i];
-          }
-        }
-      }
-    } else {
-      int cnt = 0;
-#pragma unroll
-      for (int i = 0; i < kQPT; ++i) cnt += qmask[i] != 0ull;
-      int pos;
-      n_ent = block_scan_excl(cnt, scan, &pos);
-      n_r = n_ent;
-#pragma unroll
-      for (int i = 0; i < kQPT; ++i) {
-        if (qmask[i]) {
-          e_quad[pos] = (uint16_t)(tid * kQPT + i);
-          e_mask[pos] = qmask[i];
-          ++pos;
-        }
-      }
-    }
-  }
+  collect_quads<QG, CACHED>(A, cache, qg0, nq, k_lo, k_hi, e_quad, e_mask, scan, &n_r, &n_ent);
   __syncthreads();
 
   const bf16_t* Kc = reinterpret_cast<const bf16_t*>(A.K) + (int64_t)b * A.sb + (int64_t)h * A.sh;
   const bf16_t* Vc = reinterpret_cast<const bf16_t*>(A.V) + (int64_t)b * A.sb + (int64_t)h * A.sh;
   const int n_f = n_ent - n_r;
   if (CACHED && n_f) {
-    // logits of the forced-only quads (one thread per key and query)
-    for (int idx = tid; idx < n_f * 4 * QG; idx += kAttThreads) {
-      const int f = idx / (4 * QG), kk = (idx / QG) % 4, u = idx % QG;
-      const int64_t key = k_lo + 4 * (int64_t)e_quad[n_r + f] + kk;
-      float z = kNegInf;
-      if (u < nq && key < k_hi) {
-        const int qi = qg0 + u;
-        const bf16_t* qp = reinterpret_cast<const bf16_t*>(A.Q) + (int64_t)b * A.qsb + (int64_t)h * A.qsh +
-                           (int64_t)(qi / A.T) * A.qsg + (int64_t)(qi % A.T) * A.qst;
-        const bf16_t* kp = Kc + key * A.st;
-        float dot = 0.f;
-#pragma unroll
-        for (int pc = 0; pc < PIECES; ++pc) {
-          float kv[8], qv[8];
-          unpack(ld16(kp + pc * 8), kv, bf16_t());
-          unpack(ld16(qp + pc * 8), qv, bf16_t());
-#pragma unroll
-          for (int x = 0; x < 8; ++x) dot += kv[x] * qv[x];
-        }
-        z = dot * A.inv_sqrt_d;
-      }
-      f_log[CACHED ? f : 0][u][kk] = z;
-    }
+    forced_logits<D, QG>(A, Kc, b, h, qg0, nq, k_lo, k_hi, e_quad, n_r, n_f, f_log);
     __syncthreads();
   }
 
