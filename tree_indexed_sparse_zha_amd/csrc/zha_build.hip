@@ -768,6 +768,8 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
       ps += __shfl_xor(ps, 32);
       const float L2 = m2 + __logf(ps);
       const float inv2 = 1.f / ps;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) P[s] *= inv2;  // normalised weights: the product is the mean
       // g^T[d][j] = sum over keys k[key][d] P[j][key]: A = keys (row d = 16b +
       // lane % 16, k = key 4g + s), B = P (k = key 4g + s, column j)
       f32x4 G[NB];
@@ -789,7 +791,7 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
       for (int blk = 0; blk < NB; ++blk) {
         float gv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) gv[i] = G[blk][i] * inv2;
+        for (int i = 0; i < 4; ++i) gv[i] = G[blk][i];
         *reinterpret_cast<float4*>(&chG[wave][j][16 * blk + 4 * g]) = make_float4(gv[0], gv[1], gv[2], gv[3]);
         const float4 rv = *reinterpret_cast<const float4*>(&refL[j][16 * blk + 4 * g]);
         pk[blk] = make_uint2(bf16_pair(gv[0], gv[1]), bf16_pair(gv[2], gv[3]));
