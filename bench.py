@@ -38,9 +38,11 @@ def recorded_traffic(kernel: str, workload: str, leaf_form: str, p: float):
     import hashlib
 
     path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
-    if leaf_form != "weights" or abs(p - 0.95) > 1e-9 or not os.path.exists(path):
+    if abs(p - 0.95) > 1e-9 or not os.path.exists(path):
         return None
     rec = json.load(open(path))
+    if rec.get("leaf_form", "weights") != leaf_form:
+        return None
     k = rec.get("kernels", {}).get(kernel)
     if not k:
         return None
@@ -81,9 +83,12 @@ def selection_bytes(cfg: zha.ZhaConfig, buf, n_tokens: int, T: int, logits: bool
 
     route, per cache and level: |union over the cache's queries of the
     candidates| x (R*d*2 bytes of g + 4R bytes of c; fp8 g: R*d + 8R with the
-    row scales), or at level 1 in the
-    weights form x (C*d*2 bytes of keys + 4RC of weights + 4R of c, plus
-    4*min(QC,16) bytes of logits written per key when they are kept);
+    row scales), or at a level that holds weights (level 1 in the weights
+    forms, level 2 in "weights2"; k keys per node) x (k*d*2 bytes of keys +
+    4Rk of weights + 4R of c, plus 4*min(QC,16) bytes of logits written per
+    key when they are kept); in "weights2" with at most 4 queries per cache,
+    level 1 reads the logits level 2 wrote instead of the keys
+    (4RC + 4R + 4*QC*C bytes per chunk);
     attend, per cache: |union over the cache's queries of the attended keys|
     x (d*2 bytes of V + d*2 bytes of K, or 4*min(QC,16) bytes of cached
     logits).  Also returns per-query selected share and per-level counts.
@@ -94,12 +99,19 @@ def selection_bytes(cfg: zha.ZhaConfig, buf, n_tokens: int, T: int, logits: bool
     gsize = 1 if cfg.g_dtype == "fp8" else cfg.esize  # bytes per stored g element
     node_bytes = R * d * gsize + 4 * R * (2 if cfg.g_dtype == "fp8" else 1)  # g, c (+ row scales)
     QW = min(QC, 16)  # useful logits per key (rows are padded to 4 in memory)
-    leaf_bytes = C * d * cfg.esize + R * C * 4 + 4 * R if cfg.leaf_form == "weights" else node_bytes
-    if logits:
-        leaf_bytes += C * QW * 4
+    top = top or Lv  # routing starts here; the levels above are not read
+    from_logits = logits and cfg.weight_keys(2) > 0 and QC <= 4 and top >= 2
+
+    def weights_level(k, writes):  # bytes per node of a level holding k-key weights
+        return k * d * cfg.esize + R * k * 4 + 4 * R + (k * QW * 4 if writes else 0)
+
+    level_bytes = {lv: node_bytes for lv in range(1, Lv + 1)}
+    if cfg.weights:
+        level_bytes[1] = R * C * 4 + 4 * R + C * QW * 4 if from_logits else weights_level(C, logits)
+    if cfg.weight_keys(2):
+        level_bytes[2] = weights_level(C * C, from_logits)
     per_level = {}
     kept_prev = None
-    top = top or Lv  # routing starts here; the levels above are not read
     for lv in range(top, 0, -1):
         n = sizes[lv - 1]
         if lv == top:
@@ -113,7 +125,7 @@ def selection_bytes(cfg: zha.ZhaConfig, buf, n_tokens: int, T: int, logits: bool
             cand_per_query=float(cand.sum().item()) / (caches * QC),
             kept_per_query=float(kept.sum().item()) / (caches * QC),
             union_cand_per_cache=union / caches,
-            alg_bytes=union * (leaf_bytes if lv == 1 else node_bytes),
+            alg_bytes=union * level_bytes[lv],
         )
         kept_prev = kept
     # attended keys: kept chunks + sink + current chunk
@@ -184,8 +196,9 @@ def main():
     ap.add_argument("--workload", default="deep1m")
     ap.add_argument("--p", type=float, default=None, help="top-p (default: the workload's first p)")
     ap.add_argument("--tokens", type=int, default=None, help="override the context length (sweeps)")
-    ap.add_argument("--leaf-form", default="weights", choices=["weights", "mean"],
-                    help="level-1 storage: softmax weights scored from raw keys (default) or mean keys")
+    ap.add_argument("--leaf-form", default="weights", choices=["weights", "weights2", "mean"],
+                    help="storage of the bottom levels: level 1 as softmax weights scored from raw keys "
+                         "(default), levels 1 and 2 as weights (weights2; chunk 4), or mean keys")
     ap.add_argument("--p-levels", default=None,
                     help="depth-aware schedule: comma-separated p per level, level 1 first (overrides --p)")
     ap.add_argument("--top-level", type=int, default=0, help="level routing starts from (0 = the tree's top)")
@@ -222,6 +235,8 @@ def main():
     n_steps = args.warmup + args.steps
     N0 = w.n_tokens
     capacity = N0 + n_steps * A
+    if args.leaf_form == "weights2" and (w.chunk != 4 or w.levels < 3 or args.g_dtype != "kv"):
+        args.leaf_form = "weights"
     if args.leaf_form == "weights" and w.chunk not in (4, 8, 16):
         args.leaf_form = "mean"
     cfg = cfg_of(w, capacity, args.leaf_form, args.g_dtype)
@@ -306,9 +321,10 @@ def main():
     route_bytes = sum(v["alg_bytes"] for v in per_level.values())
     g8 = cfg.g_dtype == "fp8"
     mean_node = cfg.n_ref * (cfg.head_dim * (1 if g8 else cfg.esize) + (12 if g8 else 8))  # g, L, c (+ scales)
-    tree_bytes_per_token = sum(mean_node / (cfg.chunk**l) for l in range(2, cfg.levels + 1)) + (
-        cfg.n_ref * (4 * cfg.chunk + 8) if cfg.leaf_form == "weights" else mean_node
-    ) / cfg.chunk
+    tree_bytes_per_token = sum(
+        (cfg.n_ref * (4 * cfg.weight_keys(l) + 8) if cfg.weight_keys(l) else mean_node) / (cfg.chunk**l)
+        for l in range(1, cfg.levels + 1)
+    )
     append_bytes = cfg.n_caches * A * (cfg.head_dim * cfg.esize + tree_bytes_per_token)
     alg = {"attend": attend_bytes, "build": append_bytes}
     for lv, v in per_level.items():
@@ -424,7 +440,9 @@ def prefill_main(args, w):
     # the appended positions hold the workload's appended segments (zeros when it has none)
     app = -(-n_steps * P // w.append_tokens) if w.append_tokens else 0
     capacity = N0 + max(n_steps * P, app * w.append_tokens)
-    leaf_form = args.leaf_form if w.chunk in (4, 8, 16) else "mean"
+    # the prefill spine takes mean keys above level 1: level-2 weights fall back to the weights form
+    leaf_form = "weights" if args.leaf_form == "weights2" else args.leaf_form
+    leaf_form = leaf_form if w.chunk in (4, 8, 16) else "mean"
     cfg = cfg_of(w, capacity, leaf_form, args.g_dtype)
     if cfg.q_per_kv * P > 1024:
         print("--prefill: q_per_kv * block must be <= 1024", file=sys.stderr)

@@ -69,12 +69,23 @@ enum zha_dtype { ZHA_F32 = 0, ZHA_BF16 = 1 };
  *     R*(4C+8) bytes instead of R*(d*esize+8), and routing reads the chunk's
  *     C*d key elements instead of R*d mean-key elements.  Supported with bf16
  *     and chunk in {4, 8, 16}.  Levels >= 2 are the same in both forms.
+ *   ZHA_LEAF_WEIGHTS2: level 1 as in ZHA_LEAF_WEIGHTS, and level 2 too
+ *     stores the weights of its own C*C keys ([R][C*C] fp32, with L_j and
+ *     c_j = L_j - sum_i w_ji z_ji over those keys; a trailing level-2 node
+ *     with fewer chunks holds zeros for the keys it lacks).  Routing scores
+ *     level 2 from the raw keys and, when the caller passes the logits
+ *     buffer and a cache has at most 4 queries, scores level 1 from the
+ *     logits level 2 computed, so the keys of a candidate are read once.
+ *     A level-2 node occupies R*(4C*C+8) bytes instead of R*(2d+8).
+ *     Supported with bf16, chunk 4, 3..8 levels and g_dtype ZHA_G_KV; not
+ *     with the prefill calls (zha_build_spine, zha_route_prefill).  Levels
+ *     >= 3 are the same in every form.
  */
-enum zha_leaf_form { ZHA_LEAF_MEAN = 0, ZHA_LEAF_WEIGHTS = 1 };
+enum zha_leaf_form { ZHA_LEAF_MEAN = 0, ZHA_LEAF_WEIGHTS = 1, ZHA_LEAF_WEIGHTS2 = 2 };
 
 /*
  * Storage of the mean keys g of the levels that store them (every level but
- * level 1 in the weights form).
+ * those the leaf form stores as weights).
  *   ZHA_G_KV: kv_dtype.
  *   ZHA_G_FP8: the low-precision router variant (MTP TL;DR, "FP4 router"),
  *     read as OCP FP8 E4M3 with one power-of-two scale per node and
@@ -120,7 +131,8 @@ typedef struct zha_config {
  * holds node_cap[l-1] = ceil(node_cap[l-2] / C) nodes per cache, with
  * node_cap[0] = floor(capacity / C).  Per level, three blocks:
  *   g: [caches][node_cap][g_bytes / element size]: for level 1 in the
- *      weights form, w as [R][C] fp32; otherwise R x d mean keys in kv_dtype.
+ *      weights forms, w as [R][C] fp32; for level 2 in ZHA_LEAF_WEIGHTS2,
+ *      w as [R][C*C] fp32; otherwise R x d mean keys in kv_dtype.
  *      Within one node the R x d mean
  *      keys are stored d-chunk-interleaved so that one 64-lane load yields a
  *      16 x 32 MFMA operand tile: element (j, e) with 16-byte piece
@@ -162,8 +174,10 @@ typedef struct zha_tree_layout {
  *          (in floats); score_stride = node_cap rounded up to 4.
  *   stats: [n_queries] zha_select_stats; starts at stats_offset[l-1]
  *          (in records).
- * Optional logits (leaf-weights form only): level-1 scoring computes
- * q . k_i / sqrt(d) for every key of every candidate chunk; zha_route can
+ * Optional logits (leaf-weights forms only): level-1 scoring computes
+ * q . k_i / sqrt(d) for every key of every candidate chunk (in
+ * ZHA_LEAF_WEIGHTS2 with at most 4 queries per cache, level-2 scoring does,
+ * for every key of every candidate level-2 node); zha_route can
  * keep them in a [caches][ceil(QC/16)][capacity/4][4][QW] fp32 buffer (4-key
  * quads, 4 keys, QW = min(QC rounded up to 4, 16) queries; QC = G*T queries
  * per cache; rows beyond QC unused) so that zha_attend reads 16 bytes per key
@@ -187,7 +201,7 @@ typedef struct zha_route_layout {
   int64_t score_floats_total; /* floats of the score buffer */
   int64_t stats_total;        /* records of the stats buffer */
   int64_t workspace_bytes;    /* scratch that enables every select form (see below) */
-  int64_t logits_floats;      /* floats of the optional logits buffer (weights form), else 0 */
+  int64_t logits_floats;      /* floats of the optional logits buffer (weights forms), else 0 */
   int64_t workspace_min_bytes; /* smallest scratch zha_route accepts */
 } zha_route_layout;
 
@@ -302,13 +316,13 @@ int zha_append(const zha_config* cfg, const void* K, const int64_t k_strides[3],
  *             kv head, query head, t} in elements; rows contiguous, 16-byte
  *             aligned.
  *   p         in (0, 1]; NaN or <= 0 is ZHA_ERR_ARG.
- *   K         device keys as zha_build (read by level-1 scoring in the
- *             weights form; may be NULL, with k_strides, in the mean form).
+ *   K         device keys as zha_build (read by the weights-form levels'
+ *             scoring; may be NULL, with k_strides, in the mean form).
  *   sel       device, zha_get_route_layout().sel_words_total uint32 (output).
  *   score     device, zha_get_route_layout().score_floats_total fp32 (output).
  *   stats     device, zha_get_route_layout().stats_total records (output).
  *   logits    device, zha_get_route_layout().logits_floats fp32 (optional
- *             output, NULL to skip; leaf-weights form only).
+ *             output, NULL to skip; leaf-weights forms only).
  *   ws        device scratch of at least workspace_min_bytes (ws_bytes
  *             >= workspace_bytes enables the split selection).
  * Level-1 bits of sel are the routed chunk ids consumed by zha_attend.

@@ -232,6 +232,7 @@ def build_tree(
     keep_g: bool = True,
     block: int = 8192,
     leaf_dtype: Optional[str] = None,
+    level2_dtype: Optional[str] = None,
 ) -> List[Level]:
     """Build every level for keys K[:n_tokens] (fp64 [N, d]) and ref [R, d].
 
@@ -240,7 +241,8 @@ def build_tree(
     arithmetic is the per-node definition above.  ``g_dtype`` is the storage
     precision of g; ``leaf_dtype`` (default: g_dtype) that of level 1 alone,
     "f64" when level-1 planes are evaluated from the chunk's own keys so that
-    g is never rounded there.
+    g is never rounded there; ``level2_dtype`` (default: g_dtype) likewise
+    for level 2, "f64" when level 2 too is evaluated from its own keys.
     """
     K = np.asarray(K, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
@@ -279,7 +281,7 @@ def build_tree(
             gp[a:b] = np.einsum("nkr,nkrd->nrd", wgt, gk)
         if full < n:  # incomplete trailing parent: merge the children that exist
             Lp[full], gp[full] = merge_stats(Lc[full * chunk :], gc[full * chunk :])
-        out.append(_finish(Lp, gp, ref, g_dtype, True))
+        out.append(_finish(Lp, gp, ref, (level2_dtype or g_dtype) if lv == 1 else g_dtype, True))
         if not keep_g:
             out[-2].g = None
     if not keep_g:

@@ -54,13 +54,15 @@ class LevelReport:
 
 
 def check_route_teacher_forced(q, tree, ref, chunk, p, gpu_kept: Dict[int, np.ndarray], dtype, gpu_score=None,
-                               leaf_dtype=None, top=None):
+                               leaf_dtype=None, top=None, level2_dtype=None):
     """Returns per-level reports; raises AssertionError on an unexplained difference.
 
     gpu_kept[level] = sorted kept node ids of the GPU; gpu_score[level] =
     the GPU's score row for that level (or None).  p is a scalar or one
     value per level (index l-1 for level l); routing starts at ``top``
-    (default: the top level).
+    (default: the top level).  leaf_dtype and level2_dtype are the storage
+    precisions of levels 1 and 2 when they differ from dtype ("f64" for a
+    level scored from its own keys).
     """
     levels = len(tree)
     top = levels if top is None else top
@@ -76,7 +78,8 @@ def check_route_teacher_forced(q, tree, ref, chunk, p, gpu_kept: Dict[int, np.nd
         gk = np.asarray(gpu_kept[lv], dtype=np.int64)
         assert set(gk.tolist()) <= set(cand.tolist()), f"level {lv}: GPU kept a non-candidate"
         s = O.plane_scores(q, tree[lv - 1], ref, cand)
-        eps = eps_score(leaf_dtype if (lv == 1 and leaf_dtype) else dtype, q, tree[lv - 1])
+        lv_dtype = {1: leaf_dtype, 2: level2_dtype}.get(lv) or dtype
+        eps = eps_score(lv_dtype, q, tree[lv - 1])
         err = 0.0
         if gpu_score is not None and cand.size:
             gs = np.asarray(gpu_score[lv], dtype=np.float64)[cand]

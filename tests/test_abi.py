@@ -68,6 +68,23 @@ def test_tree_layout_weights_form():
     assert tl.total_bytes < mean.total_bytes * 0.35
 
 
+def test_tree_layout_weights2_form():
+    """Levels 1 and 2 hold weights: [R][C] and [R][C*C] fp32 per node; a
+    level-2 node shrinks from R*d*2 to R*C*C*4 bytes."""
+    cfg = cfg_deep(leaf_form="weights2")
+    tl = zha.tree_layout(cfg)
+    assert tl.g_bytes[0] == 16 * 4 * 4
+    assert tl.g_bytes[1] == 16 * 16 * 4
+    assert all(tl.g_bytes[i] == 16 * 128 * 2 for i in range(2, 6))
+    w1 = zha.tree_layout(cfg_deep(leaf_form="weights"))
+    assert [int(tl.node_cap[i]) for i in range(6)] == [int(w1.node_cap[i]) for i in range(6)]
+    assert tl.total_bytes < w1.total_bytes
+    # the route's key-range slots of level 2 follow its 256-key tiles (16 nodes each)
+    r2, r1 = zha.route_layout(cfg, 1), zha.route_layout(cfg_deep(leaf_form="weights"), 1)
+    assert r2.logits_floats == r1.logits_floats
+    assert r2.workspace_min_bytes > r1.workspace_min_bytes
+
+
 def test_tree_layout_fp8():
     for leaf_form in ("mean", "weights"):
         tl = zha.tree_layout(cfg_deep(leaf_form=leaf_form, g_dtype="fp8"))
@@ -144,6 +161,12 @@ def test_route_layout_sizes():
         (dict(g_dtype="fp8"), 0),
         (dict(g_dtype="fp8", leaf_form="weights"), 0),
         (dict(g_dtype="fp8", dtype="f32", head_dim=64, n_ref=4, chunk=4, levels=3), zha.ZHA_ERR_UNSUPPORTED),
+        (dict(leaf_form="weights2"), 0),
+        (dict(leaf_form="weights2", levels=3, n_ref=1, head_dim=64), 0),
+        (dict(leaf_form="weights2", levels=2), zha.ZHA_ERR_UNSUPPORTED),
+        (dict(leaf_form="weights2", chunk=8, levels=4), zha.ZHA_ERR_UNSUPPORTED),
+        (dict(leaf_form="weights2", g_dtype="fp8"), zha.ZHA_ERR_UNSUPPORTED),
+        (dict(leaf_form="weights2", dtype="f32", head_dim=64, n_ref=4, levels=3), zha.ZHA_ERR_UNSUPPORTED),
     ],
 )
 def test_config_validation(kw, code):

@@ -130,6 +130,11 @@ CACHED_CASES = [
     ("qg4-d64-C4-p1", dict(batch=1, n_kv_heads=1, q_per_kv=2, head_dim=64, n_ref=3, chunk=4, levels=3, capacity=2100), 1, 2051, 1.0),
     ("qg4-d128-C8", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=8, levels=3, capacity=7000), 1, 6999, 0.9),
     ("qg4-d64-C16-R1", dict(batch=1, n_kv_heads=1, q_per_kv=3, head_dim=64, n_ref=1, chunk=16, levels=2, capacity=5000), 1, 4990, 0.8),
+    # levels 1 and 2 as weights: <= 4 queries per cache score level 1 from the level-2 pass's
+    # logits; 6 queries per cache score it from the keys
+    ("w2-qg4-d128-C4", dict(batch=2, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=4, capacity=9000, leaf_form="weights2"), 1, 8998, 0.9),
+    ("w2-qg4-d64-C4-p1", dict(batch=1, n_kv_heads=1, q_per_kv=2, head_dim=64, n_ref=3, chunk=4, levels=3, capacity=2100, leaf_form="weights2"), 1, 2051, 1.0),
+    ("w2-qg8-d64-C4", dict(batch=1, n_kv_heads=2, q_per_kv=3, head_dim=64, n_ref=5, chunk=4, levels=3, capacity=6000, leaf_form="weights2"), 2, 5995, 0.8),
 ]
 
 
@@ -137,7 +142,7 @@ CACHED_CASES = [
 @pytest.mark.parametrize("flags", [zha.ZHA_SINK | zha.ZHA_LAST_CHUNK, 0, zha.ZHA_SINK, zha.ZHA_LAST_CHUNK])
 def test_attend_cached_logits_matches_oracle(name, kw, T, N, p, flags):
     _say(f"attend with cached logits {name} flags={flags}")
-    cfg = zha.ZhaConfig(dtype="bf16", leaf_form="weights", **kw)
+    cfg = zha.ZhaConfig(**{"dtype": "bf16", "leaf_form": "weights", **kw})
     K, V, Q, ref = random_inputs(cfg, T, seed=5)
     tree = zha.alloc_tree(cfg)
     zha.build(cfg, K, ref, tree, N)
@@ -158,12 +163,13 @@ def test_attend_cached_logits_matches_oracle(name, kw, T, N, p, flags):
         for cache in sorted({0, cfg.n_caches - 1}):
             b, h = divmod(cache, cfg.n_kv_heads)
             Kn, rn = np64(K[b, h, :N]), np64(ref[h])
-            to = O.build_tree(Kn, rn, cfg.chunk, cfg.levels, cfg.dtype, keep_g=False, leaf_dtype="f64")
+            l2d = "f64" if cfg.weight_keys(2) else None
+            to = O.build_tree(Kn, rn, cfg.chunk, cfg.levels, cfg.dtype, keep_g=False, leaf_dtype="f64", level2_dtype=l2d)
             for ql in range(QC):
                 bits, scores = gpu_levels(cfg, buf, N, cache * QC + ql)
                 q = np64(Q[b, h, ql // T, ql % T])
                 PAR.check_route_teacher_forced(q, to, rn, cfg.chunk, p, PAR.gpu_kept_from_bits(bits), cfg.dtype,
-                                               scores, leaf_dtype="f64")
+                                               scores, leaf_dtype="f64", level2_dtype=l2d)
     for qi, (b, h, gq, t) in enumerate(query_list(cfg, T)):
         bits, _ = gpu_levels(cfg, buf, N, qi)
         chunks = np.nonzero(bits[1][:n_chunks])[0]
@@ -202,6 +208,9 @@ BUILD_CASES = [
     ("mf-c8-d64-r16-l2", dict(batch=1, n_kv_heads=2, q_per_kv=2, head_dim=64, n_ref=16, chunk=8, levels=2, dtype="bf16", capacity=3000, leaf_form="weights"), 2048 + 64 + 8 * 3 + 5),
     ("mf-c8-mean-d128-r5-l5", dict(batch=1, n_kv_heads=1, q_per_kv=4, head_dim=128, n_ref=5, chunk=8, levels=5, dtype="bf16", capacity=40000), 32768 + 8 * 100 + 3),
     ("mf-d128-r3-l8", dict(batch=1, n_kv_heads=1, q_per_kv=1, head_dim=128, n_ref=3, chunk=4, levels=8, dtype="bf16", capacity=70000, leaf_form="weights"), 65536 + 4 * 100 + 1),
+    # levels 1 and 2 as weights: a trailing level-2 node of one and of three chunks
+    ("w2-d128-r16-l6", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=6, dtype="bf16", capacity=9000, leaf_form="weights2"), 8192 + 4 * 37 + 2),
+    ("w2-d64-r5-l3", dict(batch=2, n_kv_heads=1, q_per_kv=2, head_dim=64, n_ref=5, chunk=4, levels=3, dtype="bf16", capacity=3000, leaf_form="weights2"), 2048 + 4 * 39 + 3),
 ]
 APPEND_CASES = [c for c in BUILD_CASES if c[0] != "c1-f32"]
 
@@ -225,20 +234,28 @@ def check_tree(cfg, tree, K, ref, N):
         for h in range(cfg.n_kv_heads):
             cache = b * cfg.n_kv_heads + h
             Kn, rn = np64(K[b, h, :N]), np64(ref[h])
-            weights = cfg.leaf_form == "weights"
             gd = "fp8" if cfg.g_dtype == "fp8" else cfg.dtype
-            to = O.build_tree(Kn, rn, cfg.chunk, cfg.levels, gd, n_tokens=N, leaf_dtype="f64" if weights else None)
+            to = O.build_tree(Kn, rn, cfg.chunk, cfg.levels, gd, n_tokens=N,
+                              leaf_dtype="f64" if cfg.weights else None,
+                              level2_dtype="f64" if cfg.weight_keys(2) else None)
             for lv in range(1, cfg.levels + 1):
                 n = sizes[lv - 1]
                 got = zha.read_level(cfg, tree, lv, n)
                 lvl = to[lv - 1]
-                if lv == 1 and weights:
-                    # w is the softmax of r_j . k_i / sqrt(d) over the chunk (scipy), c = L - sum w z
+                wk = cfg.weight_keys(lv)
+                if wk:
+                    # w is the softmax of r_j . k_i / sqrt(d) over the node's own keys (scipy),
+                    # zeros for the keys a trailing node lacks; c = L - sum w z
                     gw, gL, gc = np64(got["w"][cache]), np64(got["L"][cache]), np64(got["c"][cache])
-                    z = np.einsum("ncd,rd->nrc", Kn[: n * cfg.chunk].reshape(n, cfg.chunk, d), rn) / math.sqrt(d)
-                    np.testing.assert_allclose(gw, sps.softmax(z, axis=2), rtol=0, atol=2e-6, err_msg="w level 1")
-                    np.testing.assert_allclose(gL, lvl.L, rtol=1e-5, atol=3e-5, err_msg="L level 1")
-                    np.testing.assert_allclose(gc, lvl.c, rtol=1e-5, atol=3e-5, err_msg="c level 1")
+                    nk = sizes[0] * cfg.chunk  # keys of complete chunks
+                    kpad = np.zeros((n * wk, d))
+                    kpad[:nk] = Kn[:nk]
+                    z = np.einsum("ncd,rd->nrc", kpad.reshape(n, wk, d), rn) / math.sqrt(d)
+                    have = (np.arange(n * wk) < nk).reshape(n, 1, wk)
+                    z = np.where(have, z, -np.inf)
+                    np.testing.assert_allclose(gw, sps.softmax(z, axis=2), rtol=0, atol=2e-6, err_msg=f"w level {lv}")
+                    np.testing.assert_allclose(gL, lvl.L, rtol=1e-5, atol=3e-5, err_msg=f"L level {lv}")
+                    np.testing.assert_allclose(gc, lvl.c, rtol=1e-5, atol=3e-5, err_msg=f"c level {lv}")
                     continue
                 gg, gL, gc = np64(got["g"][cache]), np64(got["L"][cache]), np64(got["c"][cache])
                 np.testing.assert_allclose(gL, lvl.L, rtol=1e-5, atol=3e-5, err_msg=f"L level {lv}")
@@ -378,7 +395,7 @@ def run_path(cfg, K, V, Q, ref, N, T, p, flags=zha.ZHA_SINK | zha.ZHA_LAST_CHUNK
     is returned."""
     tree = zha.alloc_tree(cfg)
     zha.build(cfg, K, ref, tree, N)
-    buf = zha.alloc_route(cfg, T, logits=cfg.leaf_form == "weights")
+    buf = zha.alloc_route(cfg, T, logits=cfg.weights)
     zha.route(cfg, tree, N, Q, T, p, buf, K=K)
     nq = int(buf.layout.n_queries)
     out = torch.empty(nq, cfg.head_dim, device="cuda")
@@ -422,6 +439,7 @@ ROUTE_WORKLOADS = [
     ("wide256k", 2, "mean", 4, "kv"),
     ("deep32k", 2, "weights", 6, "fp8"),
     ("deep32k", 1, "mean", 6, "fp8"),
+    ("deep32k", 2, "weights2", 6, "kv"),
 ]
 
 
@@ -448,9 +466,10 @@ def test_route_and_attend_match_oracle(wname, n_caches_checked, leaf_form, q_per
     for cache in caches:
         b, h = divmod(cache, cfg.n_kv_heads)
         Kn, Vn, rn = np64(batch.K[b, h, :N]), np64(batch.V[b, h, :N]), np64(batch.ref[h])
-        leaf_dtype = "f64" if leaf_form == "weights" else None
+        leaf_dtype = "f64" if cfg.weights else None
+        l2d = "f64" if cfg.weight_keys(2) else None
         gd = "fp8" if g_dtype == "fp8" else cfg.dtype
-        to = O.build_tree(Kn, rn, cfg.chunk, cfg.levels, gd, keep_g=False, leaf_dtype=leaf_dtype)
+        to = O.build_tree(Kn, rn, cfg.chunk, cfg.levels, gd, keep_g=False, leaf_dtype=leaf_dtype, level2_dtype=l2d)
         qis = list(range(QC)) if q_per_cache >= QC else sorted(rng.choice(QC, q_per_cache, replace=False).tolist())
         for qi_local in qis:
             gq, t = divmod(qi_local, T)
@@ -458,7 +477,8 @@ def test_route_and_attend_match_oracle(wname, n_caches_checked, leaf_form, q_per
             q = np64(batch.Q[b, h, gq, t])
             bits, scores = gpu_levels(cfg, buf, N, qi)
             kept = PAR.gpu_kept_from_bits(bits)
-            PAR.check_route_teacher_forced(q, to, rn, cfg.chunk, p, kept, gd, scores, leaf_dtype=leaf_dtype)
+            PAR.check_route_teacher_forced(q, to, rn, cfg.chunk, p, kept, gd, scores, leaf_dtype=leaf_dtype,
+                                           level2_dtype=l2d)
             # attention over the GPU's set (R21)
             idx = O.attend_set(kept[1], N, cfg.chunk, True, True)
             o, l = O.attend(q, Kn, Vn, idx)
@@ -546,7 +566,7 @@ def test_route_levels_schedule_and_start_level():
         assert torch.equal(a.sel[o : o + n], c.sel[o : o + n]), f"level {lv}"
 
 
-@pytest.mark.parametrize("leaf_form", ["mean", "weights"])
+@pytest.mark.parametrize("leaf_form", ["mean", "weights", "weights2"])
 def test_route_is_deterministic(leaf_form):
     w = W.WORKLOADS["deep32k"]
     cfg = cfg_of(w, leaf_form=leaf_form)
@@ -562,6 +582,58 @@ def test_route_is_deterministic(leaf_form):
     assert torch.equal(sc0.nan_to_num(), buf.score.nan_to_num())
     assert torch.equal(st0, buf.stats)
     assert torch.equal(out0, out)
+
+
+W2_LOGIT_CASES = [
+    # name, cfg kwargs, T, n_tokens, p, top level (0 = the tree's top)
+    ("qc4-l5", dict(batch=2, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=5, capacity=70000), 1, 65536 + 4 * 301 + 3, 0.9, 0),
+    ("qc2-l3-d64", dict(batch=1, n_kv_heads=3, q_per_kv=2, head_dim=64, n_ref=5, chunk=4, levels=3, capacity=9000), 1, 8999, 0.8, 0),
+    ("qc4-top2", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=4, capacity=9000), 1, 8998, 0.9, 2),
+    ("qc3-top1", dict(batch=1, n_kv_heads=2, q_per_kv=3, head_dim=128, n_ref=7, chunk=4, levels=4, capacity=9000), 1, 8997, 0.9, 1),
+]
+
+
+@pytest.mark.parametrize("name,kw,T,N,p,top", W2_LOGIT_CASES, ids=[c[0] for c in W2_LOGIT_CASES])
+def test_level1_from_level2_logits_is_bit_identical(name, kw, T, N, p, top):
+    """Levels 1 and 2 as weights, at most 4 queries per cache: level 1 scored
+    from the logits the level-2 pass stored reaches exactly the scores,
+    selections and statistics of level 1 scored from the keys (a route call
+    without the logits buffer), and attention reading those logits agrees
+    with attention computing its own."""
+    _say(f"w2 logits {name}")
+    cfg = zha.ZhaConfig(dtype="bf16", leaf_form="weights2", **kw)
+    K, V, Q, ref = random_inputs(cfg, T, seed=9)
+    tree = zha.alloc_tree(cfg)
+    zha.build(cfg, K, ref, tree, N)
+    with_lg = zha.alloc_route(cfg, T, logits=True)
+    no_lg = zha.alloc_route(cfg, T, logits=False)
+    pl = [p] * cfg.levels
+    for buf in (with_lg, no_lg):
+        buf.score.fill_(float("nan"))
+        zha.route_levels(cfg, tree, N, Q, T, pl, buf, top_level=top, K=K)
+    torch.cuda.synchronize()
+    rl = with_lg.layout
+    for i in range(cfg.levels if top == 0 else top):
+        a0, a1 = int(rl.sel_offset[i]), int(rl.sel_offset[i]) + int(rl.n_queries) * int(rl.words[i])
+        assert torch.equal(with_lg.sel[a0:a1], no_lg.sel[a0:a1]), f"level {i + 1} bits"
+        s0, s1 = int(rl.score_offset[i]), int(rl.score_offset[i]) + int(rl.n_queries) * int(rl.score_stride[i])
+        sa, sb = with_lg.score[s0:s1], no_lg.score[s0:s1]
+        assert torch.equal(sa.nan_to_num(), sb.nan_to_num()), f"level {i + 1} scores"
+        t0 = int(rl.stats_offset[i]) * zha.STATS_BYTES
+        t1 = t0 + int(rl.n_queries) * zha.STATS_BYTES
+        assert torch.equal(with_lg.stats[t0:t1], no_lg.stats[t0:t1]), f"level {i + 1} statistics"
+    assert int(zha.level1_sel(with_lg).ne(0).sum()) > 0
+    check_cached_logits(cfg, with_lg, K, Q, N, T)
+    nq = int(rl.n_queries)
+    ws = torch.empty(zha.attend_workspace_bytes(cfg, T), dtype=torch.uint8, device="cuda")
+    outs = []
+    for lg in (None, with_lg.logits):
+        out, lse = torch.empty(nq, cfg.head_dim, device="cuda"), torch.empty(nq, device="cuda")
+        zha.attend(cfg, Q, T, K, V, N, zha.level1_sel(with_lg), 3, out, lse, ws, logits=lg)
+        outs.append((out, lse))
+    torch.cuda.synchronize()
+    assert float((outs[0][0] - outs[1][0]).abs().max()) <= 2e-5
+    assert float((outs[0][1] - outs[1][1]).abs().max()) <= 2e-5
 
 
 SPLIT_CASES = [

@@ -410,6 +410,34 @@ def test_fp8_tree_keeps_tangent_point():
             assert np.all(s - lvl.L[:, j] <= reach + 1e-12)
 
 
+def test_level2_weights_form_is_scored_from_its_own_keys():
+    """Levels 1 and 2 held as weights (f64) over bf16 mean keys above: each
+    level-2 node's plane j is H(w_j) + E_{w_j}[q . k / sqrt(d)] with w_j the
+    softmax of r_j over the node's own keys (the Gibbs form of the tangent
+    plane, from the keys directly, not from the merge), while level 3 still
+    holds bf16-rounded mean keys."""
+    K, V, ref, Q = _rand_cache(16 * 37 + 8, 16, 4, 12)
+    N, d = K.shape[0], ref.shape[1]
+    tree = O.build_tree(K, ref, 4, 3, "bf16", n_tokens=N, leaf_dtype="f64", level2_dtype="f64")
+    lv2 = tree[1]
+    n2 = lv2.L.shape[0]
+    assert n2 == 38  # 150 chunks: the last level-2 node holds 2 of them
+    for n in range(n2):
+        keys = K[16 * n : min(16 * n + 16, (N // 4) * 4)]
+        z = keys @ ref.T / math.sqrt(d)  # [keys, R]
+        w = sps.softmax(z, axis=0)
+        H = -(w * np.log(w)).sum(axis=0)
+        np.testing.assert_allclose(lv2.c[n], H, rtol=0, atol=1e-12)
+        for q in Q[:3]:
+            planes = H + w.T @ (keys @ q) / math.sqrt(d)
+            np.testing.assert_allclose(O.plane_scores(q, lv2, ref, [n]), [planes.max()], rtol=0, atol=1e-12)
+    # level 3 keeps bf16 storage, and its c uses the rounded values
+    lv3 = tree[2]
+    np.testing.assert_array_equal(lv3.ghat, O.round_bf16(lv3.g))
+    assert np.any(lv3.ghat != lv3.g)
+    np.testing.assert_allclose(lv3.c, lv3.L - np.einsum("nrd,rd->nr", lv3.ghat, ref) / math.sqrt(d), rtol=0, atol=1e-12)
+
+
 def test_golden_geometry():
     gold = json.load(open(os.path.join(GOLDEN, "geometry.json")))
     for t in gold["trees"]:

@@ -39,8 +39,11 @@ int check_config(const zha_config* c) {
   if (c->capacity_tokens < 1) return fail(ZHA_ERR_ARG, "capacity_tokens must be >= 1");
   if (c->kv_dtype != ZHA_F32 && c->kv_dtype != ZHA_BF16)
     return fail(ZHA_ERR_UNSUPPORTED, "kv_dtype %d unsupported", c->kv_dtype);
-  if (c->leaf_form != ZHA_LEAF_MEAN && c->leaf_form != ZHA_LEAF_WEIGHTS)
+  if (c->leaf_form != ZHA_LEAF_MEAN && c->leaf_form != ZHA_LEAF_WEIGHTS && c->leaf_form != ZHA_LEAF_WEIGHTS2)
     return fail(ZHA_ERR_ARG, "leaf_form %d unknown", c->leaf_form);
+  if (c->leaf_form == ZHA_LEAF_WEIGHTS2 &&
+      (c->kv_dtype != ZHA_BF16 || c->chunk != 4 || c->levels < 3 || c->levels > 8 || c->g_dtype != ZHA_G_KV))
+    return fail(ZHA_ERR_UNSUPPORTED, "weights at levels 1 and 2 need bf16, chunk 4, 3..8 levels and g in bf16");
   if (c->leaf_form == ZHA_LEAF_WEIGHTS &&
       (c->kv_dtype != ZHA_BF16 || (c->chunk != 4 && c->chunk != 8 && c->chunk != 16)))
     return fail(ZHA_ERR_UNSUPPORTED, "the leaf weights form needs bf16 and chunk 4, 8 or 16");
@@ -88,6 +91,14 @@ int check_strides(const int64_t* s, int n, int es, const char* name) {
   return ZHA_OK;
 }
 
+// Keys per node of level index l when that level stores softmax weights
+// (level 1 in both weights forms, level 2 in ZHA_LEAF_WEIGHTS2), else 0.
+static int weight_keys(const zha_config* c, int l) {
+  if (l == 0 && (c->leaf_form == ZHA_LEAF_WEIGHTS || c->leaf_form == ZHA_LEAF_WEIGHTS2)) return c->chunk;
+  if (l == 1 && c->leaf_form == ZHA_LEAF_WEIGHTS2) return c->chunk * c->chunk;
+  return 0;
+}
+
 // Appends split each top span over its C children when the top has at least
 // two levels below it and C is in 4..16 (the sub-span pass uses 4 waves).
 static bool split_top(const zha_config* c) { return c->levels >= 3 && c->chunk >= 4 && c->chunk <= 16; }
@@ -100,10 +111,10 @@ void fill_tree_layout(const zha_config* c, zha_tree_layout* out) {
   int64_t off = 0;
   for (int l = 0; l < c->levels; ++l) {
     if (l > 0) n = cdiv(n, c->chunk);
-    const bool weights = l == 0 && c->leaf_form == ZHA_LEAF_WEIGHTS;
-    const bool fp8 = !weights && c->g_dtype == ZHA_G_FP8;
-    out->g_bytes[l] = weights ? (int64_t)c->n_ref * c->chunk * 4
-                              : (int64_t)c->n_ref * c->head_dim * (fp8 ? 1 : esize(c->kv_dtype));
+    const int wk = weight_keys(c, l);
+    const bool fp8 = wk == 0 && c->g_dtype == ZHA_G_FP8;
+    out->g_bytes[l] = wk ? (int64_t)c->n_ref * wk * 4
+                         : (int64_t)c->n_ref * c->head_dim * (fp8 ? 1 : esize(c->kv_dtype));
     out->node_cap[l] = n;
     out->g_offset[l] = off;
     off = align256(off + caches * n * out->g_bytes[l]);
@@ -135,7 +146,8 @@ void fill_geom(const zha_config* c, const zha_tree_layout& tl, zha::TreeGeom* g)
   g->esize = esize(c->kv_dtype);
   g->H = c->n_kv_heads;
   g->caches = c->batch * c->n_kv_heads;
-  g->leaf_weights = c->leaf_form == ZHA_LEAF_WEIGHTS;
+  g->leaf_weights = weight_keys(c, 0) != 0;
+  g->w2 = weight_keys(c, 1) != 0;
   for (int l = 0; l < c->levels; ++l) {
     g->node_cap[l] = tl.node_cap[l];
     g->g_off[l] = tl.g_offset[l];
@@ -305,9 +317,9 @@ static int logits_row(int64_t QC) { return QC >= 16 ? 16 : (int)((QC + 3) / 4 * 
 static int64_t kr_total(const zha_config* cfg, const zha_tree_layout& tl, int64_t n_queries, int64_t* off) {
   int64_t words = 0;
   for (int l = 0; l < cfg->levels; ++l) {
-    const bool lw = cfg->leaf_form == ZHA_LEAF_WEIGHTS && l == 0;
+    const int wk = weight_keys(cfg, l);
     if (off) off[l] = words;
-    words += n_queries * zha::route_kr_slots(cfg->kv_dtype, lw, tl.node_cap[l], cfg->chunk) * 4;
+    words += n_queries * zha::route_kr_slots(cfg->kv_dtype, wk != 0, tl.node_cap[l], wk) * 4;
   }
   return words * 4;
 }
@@ -342,7 +354,7 @@ int zha_get_route_layout(const zha_config* cfg, int32_t T, zha_route_layout* out
   out->workspace_min_bytes = align256(kr_total(cfg, tl, out->n_queries, nullptr));
   out->workspace_bytes =
       out->workspace_min_bytes + align256(zha::select_split_bytes(out->n_queries, tl.node_cap[0]));
-  if (cfg->leaf_form == ZHA_LEAF_WEIGHTS) {
+  if (weight_keys(cfg, 0)) {
     const int64_t QC = (int64_t)cfg->q_per_kv * T;
     out->logits_floats = (int64_t)cfg->batch * cfg->n_kv_heads * cdiv(QC, 16) *
                          (tl.node_cap[0] * cfg->chunk / 4) * 4 * logits_row(QC);
@@ -386,13 +398,13 @@ static int do_route(const zha_config* cfg, const void* tree, int64_t n_tokens, c
   if ((rc = check_ptr16(tree, "tree"))) return rc;
   if ((rc = check_ptr16(Q, "Q"))) return rc;
   if ((rc = check_strides(q_strides, 4, esize(cfg->kv_dtype), "q_strides"))) return rc;
-  const bool leafw = cfg->leaf_form == ZHA_LEAF_WEIGHTS;
+  const bool leafw = weight_keys(cfg, 0) != 0;
   if (leafw) {
     if ((rc = check_ptr16(K, "K"))) return rc;
     if ((rc = check_strides(k_strides, 3, esize(cfg->kv_dtype), "k_strides"))) return rc;
   }
   if (logits) {
-    if (!leafw) return fail(ZHA_ERR_ARG, "logits need the leaf weights form");
+    if (!leafw) return fail(ZHA_ERR_ARG, "logits need a leaf weights form");
     if ((rc = check_ptr16(logits, "logits"))) return rc;
   }
   if ((rc = check_ptr16(sel, "sel"))) return rc;
@@ -407,6 +419,8 @@ static int do_route(const zha_config* cfg, const void* tree, int64_t n_tokens, c
   if (n_tokens < 0) return fail(ZHA_ERR_ARG, "n_tokens must be >= 0");
   if (n_tokens > cfg->capacity_tokens) return fail(ZHA_ERR_CAPACITY, "n_tokens exceeds capacity");
   if (prefill) {
+    if (cfg->leaf_form == ZHA_LEAF_WEIGHTS2)
+      return fail(ZHA_ERR_UNSUPPORTED, "prefill routing does not take level-2 weights");
     if (cfg->levels >= 2 && (rc = check_ptr16(spine, "spine"))) return rc;
     if (cfg->kv_dtype != ZHA_BF16) return fail(ZHA_ERR_UNSUPPORTED, "prefill routing needs bf16 keys");
     if (T > n_tokens) return fail(ZHA_ERR_ARG, "T = %d positions exceed n_tokens", T);
@@ -429,6 +443,9 @@ static int do_route(const zha_config* cfg, const void* tree, int64_t n_tokens, c
   void* split = rl.workspace_bytes > rl.workspace_min_bytes && ws_bytes >= rl.workspace_bytes
                     ? static_cast<void*>(static_cast<char*>(ws) + rl.workspace_min_bytes)
                     : nullptr;
+  // level 1 reads the logits the level-2 pass stores when level 2 holds
+  // weights, is scored in this call and a cache has at most 4 queries
+  const bool from_logits = logits && weight_keys(cfg, 1) && top >= 2 && (int64_t)cfg->q_per_kv * T <= 4;
   if (cfg->kv_dtype != ZHA_BF16) {
     // the fp32 score kernel accumulates its single slot per query with atomics
     hipError_t e = zha::launch_route_init(keyrange, kr_bytes / 16, pr);
@@ -461,7 +478,7 @@ static int do_route(const zha_config* cfg, const void* tree, int64_t n_tokens, c
     sa.score = score + rl.score_offset[l];
     sa.score_stride = rl.score_stride[l];
     sa.keyrange = keyrange + kr_off[l];
-    sa.kr_slots = zha::route_kr_slots(cfg->kv_dtype, leafw && l == 0, tl.node_cap[l], cfg->chunk);
+    sa.kr_slots = zha::route_kr_slots(cfg->kv_dtype, weight_keys(cfg, l) != 0, tl.node_cap[l], weight_keys(cfg, l));
     sa.inv_sqrt_d = isd;
     sa.causal_n0 = prefill ? n_tokens - T : -1;
     sa.lvl_chunks = 1;
@@ -476,13 +493,17 @@ static int do_route(const zha_config* cfg, const void* tree, int64_t n_tokens, c
       sa.spine_states = spine_states(cfg, T);
       sa.spine_rec = spine_rec_bytes(cfg);
     }
-    sa.leaf_weights = leafw && l == 0;
+    sa.wkeys = weight_keys(cfg, l);
+    sa.leaf_weights = sa.wkeys != 0;
     if (sa.leaf_weights) {
       sa.K = K;
       sa.ksb = k_strides[0];
       sa.ksh = k_strides[1];
       sa.kst = k_strides[2];
-      sa.logits = logits;
+      sa.n_keys = n[0] * cfg->chunk;
+      // level 1 writes the logits, or reads those of level 2 (from_logits)
+      sa.logits = (l == 0 || from_logits) ? logits : nullptr;
+      sa.from_logits = l == 0 && from_logits;
       sa.nquads = tl.node_cap[0] * cfg->chunk / 4;
       sa.QW = logits_row(sa.QC);
     }
@@ -531,6 +552,8 @@ int zha_build_spine(const zha_config* cfg, const void* K, const int64_t k_stride
   if ((rc = check_prof(prof))) return rc;
   if (prof) prof->n_used = 0;
   if (cfg->kv_dtype != ZHA_BF16) return fail(ZHA_ERR_UNSUPPORTED, "prefill needs bf16 keys");
+  if (cfg->leaf_form == ZHA_LEAF_WEIGHTS2)
+    return fail(ZHA_ERR_UNSUPPORTED, "the prefill spine does not take level-2 weights");
   if ((rc = check_ptr16(K, "K"))) return rc;
   if ((rc = check_strides(k_strides, 3, esize(cfg->kv_dtype), "k_strides"))) return rc;
   if ((rc = check_ptr16(ref, "ref"))) return rc;
@@ -614,7 +637,7 @@ int zha_attend(const zha_config* cfg, const void* Q, const int64_t q_strides[4],
   if (n_tokens > cfg->capacity_tokens) return fail(ZHA_ERR_CAPACITY, "n_tokens exceeds capacity");
   const int64_t n_chunks = n_tokens / cfg->chunk;
   if (logits) {
-    if (cfg->leaf_form != ZHA_LEAF_WEIGHTS) return fail(ZHA_ERR_ARG, "logits need the leaf weights form");
+    if (!weight_keys(cfg, 0)) return fail(ZHA_ERR_ARG, "logits need a leaf weights form");
     if (flags & ZHA_ALL_KEYS) return fail(ZHA_ERR_ARG, "logits cannot be used with ZHA_ALL_KEYS");
     if ((rc = check_ptr16(logits, "logits"))) return rc;
   }

@@ -784,7 +784,10 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
         }
       }
       // keep the fp32 form (L, mean g) for the round's node and, when C = 4,
-      // emit it as the level-2 node (lane: d = 16b + 4g + i of plane j)
+      // emit it as the level-2 node (lane: d = 16b + 4g + i of plane j): its
+      // rounded mean keys, or, when level 2 too holds weights, the
+      // normalised weights P of its 16 keys with c = L - sum_i P_i z_i
+      const bool w2 = C == 4 && geo.w2;
       float dot = 0.f;
       uint2 pk[NB];
 #pragma unroll
@@ -793,25 +796,37 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) gv[i] = G[blk][i];
         *reinterpret_cast<float4*>(&chG[wave][j][16 * blk + 4 * g]) = make_float4(gv[0], gv[1], gv[2], gv[3]);
-        const float4 rv = *reinterpret_cast<const float4*>(&refL[j][16 * blk + 4 * g]);
-        pk[blk] = make_uint2(bf16_pair(gv[0], gv[1]), bf16_pair(gv[2], gv[3]));
-        dot = fmaf(rv.x, bf16_lo(pk[blk].x), dot);
-        dot = fmaf(rv.y, bf16_hi(pk[blk].x), dot);
-        dot = fmaf(rv.z, bf16_lo(pk[blk].y), dot);
-        dot = fmaf(rv.w, bf16_hi(pk[blk].y), dot);
+        if (!w2) {
+          const float4 rv = *reinterpret_cast<const float4*>(&refL[j][16 * blk + 4 * g]);
+          pk[blk] = make_uint2(bf16_pair(gv[0], gv[1]), bf16_pair(gv[2], gv[3]));
+          dot = fmaf(rv.x, bf16_lo(pk[blk].x), dot);
+          dot = fmaf(rv.y, bf16_hi(pk[blk].x), dot);
+          dot = fmaf(rv.z, bf16_lo(pk[blk].y), dot);
+          dot = fmaf(rv.w, bf16_hi(pk[blk].y), dot);
+        }
+      }
+      if (w2) {
+        dot = P[0] * z[0];
+#pragma unroll
+        for (int s = 1; s < 4; ++s) dot = fmaf(P[s], z[s], dot);
       }
       dot += __shfl_xor(dot, 16);
       dot += __shfl_xor(dot, 32);
       if (g == 0) chL[wave][j] = L2;
       if (C == 4 && j < R) {
         const int64_t nidx = (int64_t)cache * geo.node_cap[1] + kb0 / 16;
-        char* gb = A.tree + geo.g_off[1] + nidx * R * D * 2;
+        if (w2) {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(A.tree + geo.g_off[1]) + (nidx * R + j) * 16 + 4 * g) =
+              make_float4(P[0], P[1], P[2], P[3]);
+        } else {
+          char* gb = A.tree + geo.g_off[1] + nidx * R * D * 2;
 #pragma unroll
-        for (int blk = 0; blk < NB; ++blk)
-          *reinterpret_cast<uint2*>(gb + ((int64_t)(2 * blk + g / 2) * R + j) * 16 + (g % 2) * 8) = pk[blk];
+          for (int blk = 0; blk < NB; ++blk)
+            *reinterpret_cast<uint2*>(gb + ((int64_t)(2 * blk + g / 2) * R + j) * 16 + (g % 2) * 8) = pk[blk];
+        }
         if (g == 0) {
           reinterpret_cast<float*>(A.tree + geo.L_off[1])[nidx * R + j] = L2;
-          reinterpret_cast<float*>(A.tree + geo.c_off[1])[nidx * R + j] = L2 - dot * isd;
+          reinterpret_cast<float*>(A.tree + geo.c_off[1])[nidx * R + j] = w2 ? L2 - dot : L2 - dot * isd;
         }
       }
     }

@@ -39,6 +39,7 @@ struct TreeGeom {
   int H;
   int caches;
   int leaf_weights;  // level 1 stores softmax weights instead of mean keys
+  int w2;            // level 2 too stores the weights of its C*C keys ([R][C*C] fp32)
   int64_t node_cap[kMaxLevels];
   int64_t g_off[kMaxLevels];
   int64_t L_off[kMaxLevels];
@@ -100,7 +101,11 @@ struct ScoreArgs {
   uint32_t* keyrange;          // [n_queries][kr_slots][4]: max key, min key, candidate count, 0
   int64_t kr_slots;            // slots per query: one per score tile (plain stores), or 1 (atomics)
   float inv_sqrt_d;
-  int leaf_weights;            // level 1 in the weights form: g holds w [R][C] fp32
+  int leaf_weights;            // a weights-form level: g holds w [R][C] fp32, C keys per node
+  int wkeys;                   // weights form: keys per node (C at level 1, C * C at level 2)
+  int64_t n_keys;              // weights form: keys of the complete chunks (a trailing node may cover fewer)
+  int from_logits;             // weights form, level 1, at most 4 queries per cache: the logits
+                               // the level-2 pass wrote stand in for the keys
   const void* K;               // keys (weights form only)
   int64_t ksb, ksh, kst;
   int64_t causal_n0;           // prefill: query t of a head sits at position causal_n0 + t; -1 = decode

@@ -121,20 +121,21 @@ __device__ __forceinline__ uint32_t node_bits16(const ScoreArgs& A, int cache, i
   return mb;
 }
 
-// Candidate bits of the NCH (<= 64) chunks m0 .. m0 + NCH - 1 of a level-1
-// tile for query qi, as node_bits16 (the chunks' NCH / C parents lie in one
-// bitset word).
-template <int NCH, int C>
+// Candidate bits of the NCH (<= 64) nodes m0 .. m0 + NCH - 1 of a
+// weights-form tile for query qi, as node_bits16, with CP children per
+// parent (the nodes' NCH / CP parents lie in one bitset word).
+template <int NCH, int CP>
 __device__ __forceinline__ unsigned long long chunk_bits(const ScoreArgs& A, int cache, int qi, int64_t m0) {
+  static_assert(NCH % CP == 0 && NCH / CP <= 32, "whole parents within one word");
   const int64_t nvalid = A.n_nodes - m0 < NCH ? A.n_nodes - m0 : NCH;
   const unsigned long long valid = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1ull);
   unsigned long long mb = 0ull;
   if (A.sel_parent) {
-    const int64_t p0 = m0 / C;
+    const int64_t p0 = m0 / CP;
     const uint32_t word = A.sel_parent[((int64_t)cache * A.QC + qi) * A.parent_words + (p0 >> 5)] >> (p0 & 31);
 #pragma unroll
-    for (int pi = 0; pi < NCH / C; ++pi)
-      if ((word >> pi) & 1u) mb |= ((1ull << C) - 1ull) << (pi * C);
+    for (int pi = 0; pi < NCH / CP; ++pi)
+      if ((word >> pi) & 1u) mb |= ((1ull << CP) - 1ull) << (pi * CP);
     mb &= valid;
   } else {
     mb = valid;
@@ -388,9 +389,13 @@ __global__ __launch_bounds__(256) void k_score_smallr(ScoreArgs A) {
 // RT: R as a compile-time constant (0 = runtime).  Q4: at most 4 queries per
 // cache; the MFMA then fills only 4 of its 16 query columns, so the logits
 // go through LDS and the plane fold runs with lanes = (chunk, part, query),
-// every lane busy.
-template <int D, int C, int RT, bool Q4>
+// every lane busy.  C is the keys per node (C * C for level 2 when it too
+// holds weights), CP the children per parent.  FROMLOG (Q4, level 1 under a
+// weights-form level 2): the logits the level-2 pass stored for every key of
+// its candidates stand in for the keys and the MFMA; the fold is the same.
+template <int D, int C, int RT, bool Q4, int CP = C, bool FROMLOG = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_score_leafw(ScoreArgs A) {
+  static_assert(!FROMLOG || (Q4 && C == 4), "logits rows are read as 4-key quads of at most 4 queries");
   constexpr int NS = D / 32;
   constexpr int KT = 256;       // keys per tile
   constexpr int NCH = KT / C;   // chunks per tile (<= 64)
@@ -404,7 +409,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   const int64_t m0 = k0 / C;
   const int R = A.R;
   const int qn = lane & 15, kg = lane >> 4;
-  const int64_t n_keys = A.n_nodes * C;  // keys of complete chunks
+  const int64_t n_keys = A.n_keys;  // keys of complete chunks
   constexpr int WROW = 16 * PARTS + 1;  // padded: chunks start on different banks
   __shared__ float sc[16][NCH + 1];
   __shared__ float4 wl[NCH][WROW];  // w of chunk x, plane j, 4-key part at [x][j * PARTS + part]
@@ -413,7 +418,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   __shared__ unsigned long long mbl[16];    // candidate bits per query
 
   bf16x8 bq[NS];
-  {
+  if constexpr (!FROMLOG) {
     const int qi = qg0 + qn;
     if (qn < nq) {
       const int b = cache / A.H, h = cache % A.H, gq = qi / A.T, t = qi % A.T;
@@ -432,7 +437,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   const float* ccache = A.c + (int64_t)cache * A.node_cap * R;
 
   // candidate bits of the tile's chunks for query qn (bit x = chunk m0 + x)
-  const unsigned long long mybits = qn < nq ? chunk_bits<NCH, C>(A, cache, qg0 + qn, m0) : 0ull;
+  const unsigned long long mybits = qn < nq ? chunk_bits<NCH, CP>(A, cache, qg0 + qn, m0) : 0ull;
   // chunks that are a candidate of some query (same value in every lane)
   unsigned long long anybits = mybits;
 #pragma unroll
@@ -465,14 +470,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   }
   uint4 kf[GPW][NS];
   bool live[GPW];
+  uint4 lg = make_uint4(0, 0, 0, 0);
+  if constexpr (FROMLOG) {
+    // lane (quad qq of the wave, key kk): the stored logits of key kk of the
+    // quad for queries 0..3 (a chunk is a quad; non-candidates read zeros)
+    const int qq = lane >> 2, kk = lane & 3;
+    const int x = wave * 16 + qq;
+    const rsrc_t lr = make_rsrc(A.logits + ((int64_t)cache * A.nquads + m0) * 16, (uint32_t)(n_valid * 64));
+    lg = bld16(lr, ((anybits >> x) & 1ull) ? (uint32_t)((x * 4 + kk) * 16) : kOffNone);
+  } else {
 #pragma unroll
-  for (int gi = 0; gi < GPW; ++gi) {
-    const int g = wave * GPW + gi;
-    const unsigned long long gmask = ((1ull << (16 / C)) - 1ull) << (g * 16 / C);
-    live[gi] = (anybits & gmask) != 0ull;
-    const uint32_t ko = live[gi] ? (uint32_t)((g * 16 + qn) * A.kst * 2) : kOffNone;
+    for (int gi = 0; gi < GPW; ++gi) {
+      const int g = wave * GPW + gi;
+      const unsigned long long gmask = ((1ull << (16 / C)) - 1ull) << (g * 16 / C);
+      live[gi] = (anybits & gmask) != 0ull;
+      const uint32_t ko = live[gi] ? (uint32_t)((g * 16 + qn) * A.kst * 2) : kOffNone;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) kf[gi][s] = bld16<0>(kr, ko + (4 * s + kg) * 16);
+      for (int s = 0; s < NS; ++s) kf[gi][s] = bld16<0>(kr, ko + (4 * s + kg) * 16);
+    }
   }
 #pragma unroll
   for (int r = 0; r < ITEMS; ++r) {
@@ -482,13 +497,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     for (int pp = 0; pp < PARTS; ++pp) wl[x][j * PARTS + pp] = wst[r][pp];
     cl[x][j] = cst[r];
   }
+  if constexpr (FROMLOG) {
+    // zl[wave][quad][query] holds the quad's 4 keys: scatter key kk
+    float* zq = reinterpret_cast<float*>(&zl[wave][lane >> 2][0]) + (lane & 3);
+    zq[0] = __uint_as_float(lg.x);
+    zq[4] = __uint_as_float(lg.y);
+    zq[8] = __uint_as_float(lg.z);
+    zq[12] = __uint_as_float(lg.w);
+  }
   if (tid < 16) mbl[tid] = mybits;  // lanes 0..15: kg 0, query qn = tid
   __syncthreads();
 
   const int RR = RT > 0 ? RT : R;
   constexpr int UNR = RT <= 0 ? 1 : RT < 4 ? RT : 4;  // plane loop unroll
 #pragma unroll
-  for (int gi = 0; gi < GPW; ++gi) {
+  for (int gi = 0; gi < (FROMLOG ? 0 : GPW); ++gi) {
     const int g = wave * GPW + gi;
     const int x = (g * 16 + 4 * kg) / C;  // chunk (within the tile) of this lane's 4 keys
     const int part = kg % PARTS;
@@ -531,7 +554,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     // lanes (query u, part, chunk cx) over the wave's 64 / C chunks; quads of
     // dead groups hold stale LDS data, discarded by the candidate bit
     wave_sync();
-    if (A.logits) {
+    if (!FROMLOG && A.logits) {
       // the wave's 16 quads as rows [quad][key][query]: lane (quad qq, key
       // kk) gathers the 4 queries' logits of its key and stores them as one
       // 16-byte piece, so the wave writes 1 KiB with one coalesced store
@@ -583,7 +606,7 @@ constexpr int kMqBlocks = 16;
 // workgroup: walking 16 blocks in one workgroup would leave the GPU idle
 constexpr int64_t kMqMinTiles = 256;
 
-template <int D, int C, int RT>
+template <int D, int C, int RT, int CP = C>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_score_leafw_mq(ScoreArgs A) {
   constexpr int NS = D / 32;
   constexpr int KT = 256;
@@ -598,7 +621,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   const int64_t m0 = k0 / C;
   const int R = A.R;
   const int qn = lane & 15, kg = lane >> 4;
-  const int64_t n_keys = A.n_nodes * C;
+  const int64_t n_keys = A.n_keys;
   constexpr int WROW = 16 * PARTS + 1;
   __shared__ float sc[16][NCH + 1];
   __shared__ float4 wl[NCH][WROW];
@@ -611,7 +634,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 
   // candidate bits of the tile's chunks for query qg0 + qn
   auto block_bits = [&](int qg0) -> unsigned long long {
-    return qn < min(16, A.QC - qg0) ? chunk_bits<NCH, C>(A, cache, qg0 + qn, m0) : 0ull;
+    return qn < min(16, A.QC - qg0) ? chunk_bits<NCH, CP>(A, cache, qg0 + qn, m0) : 0ull;
   };
   unsigned long long anybits = 0ull;
   for (int qb = 0; qb < nqb; ++qb) anybits |= block_bits(qz0 + 16 * qb);
@@ -2040,9 +2063,9 @@ int64_t select_split_bytes(int64_t n_queries, int64_t max_nodes) {
   return n_queries * kSelStateBytes + n_queries * S * kSelSlotU64 * 8;
 }
 
-int64_t route_kr_slots(int dtype, bool leaf_weights, int64_t node_cap, int C) {
+int64_t route_kr_slots(int dtype, bool leaf_weights, int64_t node_cap, int wkeys) {
   // one slot per score tile, plus one for the prefill spine score
-  if (leaf_weights) return (node_cap * C + 255) / 256 + 1;  // k_score_leafw: 256-key tiles
+  if (leaf_weights) return (node_cap * wkeys + 255) / 256 + 1;  // k_score_leafw: 256-key tiles
   if (dtype == 1) return (node_cap + 63) / 64 + 1;          // k_score_bf16: 64-node tiles
   return 1;                                                 // k_score_generic: atomics
 }
@@ -2059,54 +2082,67 @@ hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dty
   hipStream_t s = prof.s;
   if (sa.n_nodes > 0) {
     prof.begin(ZHA_K_SCORE, level);
-    if (sa.leaf_weights && sa.QC > 16 && (sa.n_nodes * sa.C + 255) / 256 * n_caches >= kMqMinTiles) {
-      dim3 grid((unsigned)((sa.n_nodes * sa.C + 255) / 256), (unsigned)n_caches,
-                (unsigned)((sa.QC + 16 * kMqBlocks - 1) / (16 * kMqBlocks)));
-#define ZHA_LWM(DD, CC)                                                                 \
-  do {                                                                                  \
-    if (sa.R == 16)                                                                     \
-      hipLaunchKernelGGL((k_score_leafw_mq<DD, CC, 16>), grid, dim3(256), 0, s, sa);    \
-    else if (sa.R == 1)                                                                 \
-      hipLaunchKernelGGL((k_score_leafw_mq<DD, CC, 1>), grid, dim3(256), 0, s, sa);     \
-    else                                                                                \
-      hipLaunchKernelGGL((k_score_leafw_mq<DD, CC, 0>), grid, dim3(256), 0, s, sa);     \
+    // weights-form levels: C keys per node at level 1 (C in {4, 8, 16}), or
+    // 16 keys per node at level 2 under chunk 4 (children per parent 4)
+    const bool w2lvl = sa.leaf_weights && sa.wkeys == 16 && sa.C == 4;
+    const int64_t wtiles = sa.leaf_weights ? (sa.n_nodes * sa.wkeys + 255) / 256 : 0;
+    if (sa.leaf_weights && sa.QC > 16 && wtiles * n_caches >= kMqMinTiles) {
+      dim3 grid((unsigned)wtiles, (unsigned)n_caches, (unsigned)((sa.QC + 16 * kMqBlocks - 1) / (16 * kMqBlocks)));
+#define ZHA_LWM(DD, CC, CPP)                                                                    \
+  do {                                                                                          \
+    if (sa.R == 16)                                                                             \
+      hipLaunchKernelGGL((k_score_leafw_mq<DD, CC, 16, CPP>), grid, dim3(256), 0, s, sa);       \
+    else if (sa.R == 1)                                                                         \
+      hipLaunchKernelGGL((k_score_leafw_mq<DD, CC, 1, CPP>), grid, dim3(256), 0, s, sa);        \
+    else                                                                                        \
+      hipLaunchKernelGGL((k_score_leafw_mq<DD, CC, 0, CPP>), grid, dim3(256), 0, s, sa);        \
   } while (0)
       if (sa.D == 128) {
-        if (sa.C == 4) ZHA_LWM(128, 4);
-        else if (sa.C == 8) ZHA_LWM(128, 8);
-        else ZHA_LWM(128, 16);
+        if (w2lvl) ZHA_LWM(128, 16, 4);
+        else if (sa.wkeys == 4) ZHA_LWM(128, 4, 4);
+        else if (sa.wkeys == 8) ZHA_LWM(128, 8, 8);
+        else ZHA_LWM(128, 16, 16);
       } else {
-        if (sa.C == 4) ZHA_LWM(64, 4);
-        else if (sa.C == 8) ZHA_LWM(64, 8);
-        else ZHA_LWM(64, 16);
+        if (w2lvl) ZHA_LWM(64, 16, 4);
+        else if (sa.wkeys == 4) ZHA_LWM(64, 4, 4);
+        else if (sa.wkeys == 8) ZHA_LWM(64, 8, 8);
+        else ZHA_LWM(64, 16, 16);
       }
 #undef ZHA_LWM
     } else if (sa.leaf_weights) {
-      dim3 grid((unsigned)((sa.n_nodes * sa.C + 255) / 256), (unsigned)n_caches, (unsigned)((sa.QC + 15) / 16));
-#define ZHA_LW_Q(DD, CC, QQ)                                                            \
-  do {                                                                                  \
-    if (sa.R == 16)                                                                     \
-      hipLaunchKernelGGL((k_score_leafw<DD, CC, 16, QQ>), grid, dim3(256), 0, s, sa);   \
-    else if (sa.R == 1)                                                                 \
-      hipLaunchKernelGGL((k_score_leafw<DD, CC, 1, QQ>), grid, dim3(256), 0, s, sa);    \
-    else                                                                                \
-      hipLaunchKernelGGL((k_score_leafw<DD, CC, 0, QQ>), grid, dim3(256), 0, s, sa);    \
+      dim3 grid((unsigned)wtiles, (unsigned)n_caches, (unsigned)((sa.QC + 15) / 16));
+#define ZHA_LW_Q(DD, CC, QQ, CPP, FL)                                                           \
+  do {                                                                                          \
+    if (sa.R == 16)                                                                             \
+      hipLaunchKernelGGL((k_score_leafw<DD, CC, 16, QQ, CPP, FL>), grid, dim3(256), 0, s, sa);  \
+    else if (sa.R == 1)                                                                         \
+      hipLaunchKernelGGL((k_score_leafw<DD, CC, 1, QQ, CPP, FL>), grid, dim3(256), 0, s, sa);   \
+    else                                                                                        \
+      hipLaunchKernelGGL((k_score_leafw<DD, CC, 0, QQ, CPP, FL>), grid, dim3(256), 0, s, sa);   \
   } while (0)
-#define ZHA_LW(DD, CC)               \
-  do {                               \
-    if (sa.QC <= 4)                  \
-      ZHA_LW_Q(DD, CC, true);        \
-    else                             \
-      ZHA_LW_Q(DD, CC, false);       \
+#define ZHA_LW(DD, CC, CPP)                 \
+  do {                                      \
+    if (sa.QC <= 4)                         \
+      ZHA_LW_Q(DD, CC, true, CPP, false);   \
+    else                                    \
+      ZHA_LW_Q(DD, CC, false, CPP, false);  \
   } while (0)
-      if (sa.D == 128) {
-        if (sa.C == 4) ZHA_LW(128, 4);
-        else if (sa.C == 8) ZHA_LW(128, 8);
-        else ZHA_LW(128, 16);
+      if (sa.from_logits) {
+        // level 1 from the logits of the level-2 pass (chunk 4, <= 4 queries per cache)
+        if (sa.D == 128)
+          ZHA_LW_Q(128, 4, true, 4, true);
+        else
+          ZHA_LW_Q(64, 4, true, 4, true);
+      } else if (sa.D == 128) {
+        if (w2lvl) ZHA_LW(128, 16, 4);
+        else if (sa.wkeys == 4) ZHA_LW(128, 4, 4);
+        else if (sa.wkeys == 8) ZHA_LW(128, 8, 8);
+        else ZHA_LW(128, 16, 16);
       } else {
-        if (sa.C == 4) ZHA_LW(64, 4);
-        else if (sa.C == 8) ZHA_LW(64, 8);
-        else ZHA_LW(64, 16);
+        if (w2lvl) ZHA_LW(64, 16, 4);
+        else if (sa.wkeys == 4) ZHA_LW(64, 4, 4);
+        else if (sa.wkeys == 8) ZHA_LW(64, 8, 8);
+        else ZHA_LW(64, 16, 16);
       }
 #undef ZHA_LW
 #undef ZHA_LW_Q
@@ -2161,7 +2197,7 @@ hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dty
   if (sa.n_nodes <= 0)
     sel.kr_used = 0;
   else if (sa.leaf_weights)
-    sel.kr_used = (sa.n_nodes * sa.C + 255) / 256;
+    sel.kr_used = (sa.n_nodes * sa.wkeys + 255) / 256;
   else if (dtype == 1)
     sel.kr_used = (sa.n_nodes + 63) / 64;
   else

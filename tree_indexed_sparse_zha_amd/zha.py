@@ -28,7 +28,8 @@ ZHA_OK, ZHA_ERR_NULL, ZHA_ERR_ARG, ZHA_ERR_UNSUPPORTED, ZHA_ERR_CAPACITY, ZHA_ER
 )
 ZHA_F32, ZHA_BF16 = 0, 1
 ZHA_SINK, ZHA_LAST_CHUNK, ZHA_ALL_KEYS, ZHA_CAUSAL = 1, 2, 4, 8
-ZHA_LEAF_MEAN, ZHA_LEAF_WEIGHTS = 0, 1
+ZHA_LEAF_MEAN, ZHA_LEAF_WEIGHTS, ZHA_LEAF_WEIGHTS2 = 0, 1, 2
+LEAF_FORMS = {"mean": ZHA_LEAF_MEAN, "weights": ZHA_LEAF_WEIGHTS, "weights2": ZHA_LEAF_WEIGHTS2}
 ZHA_G_KV, ZHA_G_FP8 = 0, 2
 MAX_LEVELS = 8
 
@@ -230,7 +231,7 @@ class ZhaConfig:
     levels: int
     dtype: str  # "f32" | "bf16"
     capacity: int
-    leaf_form: str = "mean"  # "mean" | "weights"
+    leaf_form: str = "mean"  # "mean" | "weights" (level 1 holds weights) | "weights2" (levels 1 and 2)
     g_dtype: str = "kv"  # "kv" (g in the KV dtype) | "fp8" (E4M3 with row scales)
 
     def c(self) -> Config:
@@ -243,7 +244,7 @@ class ZhaConfig:
             self.chunk,
             self.levels,
             ZHA_BF16 if self.dtype == "bf16" else ZHA_F32,
-            ZHA_LEAF_WEIGHTS if self.leaf_form == "weights" else ZHA_LEAF_MEAN,
+            LEAF_FORMS[self.leaf_form],
             ZHA_G_FP8 if self.g_dtype == "fp8" else ZHA_G_KV,
             self.capacity,
         )
@@ -251,6 +252,19 @@ class ZhaConfig:
     @property
     def n_caches(self) -> int:
         return self.batch * self.n_kv_heads
+
+    @property
+    def weights(self) -> bool:
+        """Level 1 holds softmax weights (either weights form)."""
+        return self.leaf_form in ("weights", "weights2")
+
+    def weight_keys(self, level: int) -> int:
+        """Keys per node of ``level`` when it holds softmax weights, else 0."""
+        if level == 1 and self.weights:
+            return self.chunk
+        if level == 2 and self.leaf_form == "weights2":
+            return self.chunk * self.chunk
+        return 0
 
     @property
     def esize(self) -> int:
@@ -497,7 +511,8 @@ def read_level(cfg: ZhaConfig, tree: torch.Tensor, level: int, n_nodes: Optional
 
     Returns g [caches, n, R, d] (storage dtype; fp8 levels: the decoded
     values times their row scale, fp32, plus "scale" [caches, n, R]), L and c
-    [caches, n, R] fp32; level 1 in the weights form returns w instead of g.
+    [caches, n, R] fp32; a level that holds weights (level 1 in the weights
+    forms, level 2 in "weights2") returns w [caches, n, R, keys] instead of g.
     """
     tl = tree_layout(cfg)
     i = level - 1
@@ -509,9 +524,9 @@ def read_level(cfg: ZhaConfig, tree: torch.Tensor, level: int, n_nodes: Optional
     Lb, cb = int(tl.L_offset[i]), int(tl.c_offset[i])
     L = tree[Lb : Lb + caches * cap * R * 4].view(torch.float32).view(caches, cap, R)[:, :n]
     c = tree[cb : cb + caches * cap * R * 4].view(torch.float32).view(caches, cap, R)[:, :n]
-    if level == 1 and cfg.leaf_form == "weights":
-        C = cfg.chunk
-        w = tree[gb : gb + caches * cap * R * C * 4].view(torch.float32).view(caches, cap, R, C)[:, :n]
+    wk = cfg.weight_keys(level)
+    if wk:
+        w = tree[gb : gb + caches * cap * R * wk * 4].view(torch.float32).view(caches, cap, R, wk)[:, :n]
         return {"w": w, "L": L, "c": c}
     sb = int(tl.s_offset[i])
     if sb >= 0:
