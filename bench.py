@@ -143,11 +143,13 @@ def selection_bytes(cfg: zha.ZhaConfig, buf, n_tokens: int, T: int, logits: bool
     return per_level, attend_bytes, phi.mean().item(), phi.min().item(), phi.max().item(), union_keys / caches
 
 
-def cpu_baseline(w: W.Workload, batch, n0: int, p: float, T: int):
-    """Time the CPU oracle on one cache (sequence 0, KV head 0): one decode
-    step = build of the appended top span + route and attend of its G*T
-    queries.  The oracle's full tree build for the initial tokens is done
-    first and not counted."""
+def cpu_baseline(w: W.Workload, batch, n0: int, p: float, T: int, cfg: zha.ZhaConfig, target_s: float = 10.0):
+    """Time the CPU oracle on a bounded sample of the step: caches in order
+    (sequence 0, KV head 0, then the next heads), each one decode step =
+    build of the appended top span + route and attend of its G*T queries, on
+    the oracle's tree of the same storage form, until about ``target_s``
+    seconds of timed work.  Each cache's full tree build for the initial
+    tokens is done first and not counted."""
     import oracle.zha_oracle as O
 
     try:
@@ -158,31 +160,39 @@ def cpu_baseline(w: W.Workload, batch, n0: int, p: float, T: int):
         blas_threads = 1
     A = w.append_tokens
     n1 = n0 + A
-    K = batch.K[0, 0, :n1].to(torch.float64).cpu().numpy()
-    V = batch.V[0, 0, :n1].to(torch.float64).cpu().numpy()
-    ref = batch.ref[0].to(torch.float64).cpu().numpy()
-    Q = batch.Q[0, 0].to(torch.float64).cpu().numpy()  # [G, T, d]
-    t0 = time.time()
-    tree = O.build_tree(K, ref, w.chunk, w.levels, w.dtype, n_tokens=n1, keep_g=False)
-    t_build_full = time.time() - t0
-    # the step: the appended span's nodes, then route + attend of the cache's queries
-    t0 = time.time()
-    O.build_tree(K[n0:n1], ref, w.chunk, w.levels, w.dtype, keep_g=False)
-    for g in range(w.q_per_kv):
-        for t in range(T):
-            O.route_and_attend(Q[g, t], K, V, tree, ref, w.chunk, p, n1)
-    t_step = time.time() - t0
-    nq = w.q_per_kv * T
+    form = dict(leaf_dtype="f64" if cfg.weights else None, level2_dtype="f64" if cfg.weight_keys(2) else None)
+    t_step = t_build_full = 0.0
+    nq = n_caches = 0
+    for cache in range(cfg.n_caches):
+        b, h = divmod(cache, cfg.n_kv_heads)
+        K = batch.K[b, h, :n1].to(torch.float64).cpu().numpy()
+        V = batch.V[b, h, :n1].to(torch.float64).cpu().numpy()
+        ref = batch.ref[h].to(torch.float64).cpu().numpy()
+        Q = batch.Q[b, h].to(torch.float64).cpu().numpy()  # [G, T, d]
+        t0 = time.time()
+        tree = O.build_tree(K, ref, w.chunk, w.levels, w.dtype, n_tokens=n1, keep_g=False, **form)
+        t_build_full += time.time() - t0
+        # the step: the appended span's nodes, then route + attend of the cache's queries
+        t0 = time.time()
+        O.build_tree(K[n0:n1], ref, w.chunk, w.levels, w.dtype, keep_g=False, **form)
+        for g in range(w.q_per_kv):
+            for t in range(T):
+                O.route_and_attend(Q[g, t], K, V, tree, ref, w.chunk, p, n1)
+        t_step += time.time() - t0
+        nq += w.q_per_kv * T
+        n_caches += 1
+        if t_step >= target_s:
+            break
     return {
         "value": nq / t_step,
         "unit": "queries/s",
         "cores": int(blas_threads),
         "kind": "oracle",
         "sample": (
-            f"one cache (sequence 0, KV head 0) of the same workload at {n1} tokens: build of the "
-            f"appended {A}-token top span + route and attend of its {nq} queries, fp64 numpy "
-            f"({t_step:.1f} s; the oracle's initial full tree build, {t_build_full:.1f} s, not counted); "
-            f"BLAS threads {blas_threads}, other numpy work single-threaded; host "
+            f"{n_caches} of the workload's {cfg.n_caches} caches (sequence, KV head) at {n1} tokens, each: build of "
+            f"the appended {A}-token top span + route and attend of its {w.q_per_kv * T} queries; {nq} queries, "
+            f"fp64 numpy, {t_step:.1f} s timed (the oracle's initial full tree builds, {t_build_full:.1f} s, not "
+            f"counted); BLAS threads {blas_threads}, other numpy work single-threaded; host "
             f"{platform.processor() or platform.machine()} with {len(os.sched_getaffinity(0))} usable cores"
         ),
     }
@@ -196,9 +206,11 @@ def main():
     ap.add_argument("--workload", default="deep1m")
     ap.add_argument("--p", type=float, default=None, help="top-p (default: the workload's first p)")
     ap.add_argument("--tokens", type=int, default=None, help="override the context length (sweeps)")
-    ap.add_argument("--leaf-form", default="weights", choices=["weights", "weights2", "mean"],
+    ap.add_argument("--leaf-form", default="auto", choices=["auto", "weights", "weights2", "mean"],
                     help="storage of the bottom levels: level 1 as softmax weights scored from raw keys "
-                         "(default), levels 1 and 2 as weights (weights2; chunk 4), or mean keys")
+                         "(weights), levels 1 and 2 as weights (weights2; chunk 4), or mean keys; auto (default) "
+                         "takes weights2 where level 1 can read level 2's logits (<= 4 queries per cache), "
+                         "else weights where the chunk allows it, else mean")
     ap.add_argument("--p-levels", default=None,
                     help="depth-aware schedule: comma-separated p per level, level 1 first (overrides --p)")
     ap.add_argument("--top-level", type=int, default=0, help="level routing starts from (0 = the tree's top)")
@@ -235,6 +247,8 @@ def main():
     n_steps = args.warmup + args.steps
     N0 = w.n_tokens
     capacity = N0 + n_steps * A
+    if args.leaf_form == "auto":
+        args.leaf_form = "weights2" if w.q_per_kv * T <= 4 and not args.no_logits else "weights"
     if args.leaf_form == "weights2" and (w.chunk != 4 or w.levels < 3 or args.g_dtype != "kv"):
         args.leaf_form = "weights"
     if args.leaf_form == "weights" and w.chunk not in (4, 8, 16):
@@ -370,7 +384,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        cpu = cpu_baseline(w, batch, n_final - A, p, T)
+        cpu = cpu_baseline(w, batch, n_final - A, p, T, cfg)
         log(f"cpu baseline {cpu['value']:.3f} queries/s")
 
     res = {
@@ -441,7 +455,7 @@ def prefill_main(args, w):
     app = -(-n_steps * P // w.append_tokens) if w.append_tokens else 0
     capacity = N0 + max(n_steps * P, app * w.append_tokens)
     # the prefill spine takes mean keys above level 1: level-2 weights fall back to the weights form
-    leaf_form = "weights" if args.leaf_form == "weights2" else args.leaf_form
+    leaf_form = "weights" if args.leaf_form in ("auto", "weights2") else args.leaf_form
     leaf_form = leaf_form if w.chunk in (4, 8, 16) else "mean"
     cfg = cfg_of(w, capacity, leaf_form, args.g_dtype)
     if cfg.q_per_kv * P > 1024:

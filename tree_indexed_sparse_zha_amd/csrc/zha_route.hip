@@ -453,19 +453,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   const int64_t rows = min((int64_t)KT, n_keys - k0);  // keys of complete chunks in this tile
   const rsrc_t kr = make_rsrc(Kc + k0 * A.kst, (uint32_t)((rows - 1) * A.kst * 2 + D * 2));
   constexpr int ITEMS = NCH * 16 / 256;
-  float4 wst[ITEMS][PARTS];
+  // w as 16-byte pieces in memory order, piece it -> (chunk x, plane j,
+  // part pp): with R = 16 consecutive lanes read consecutive bytes
+  float4 wst[ITEMS * PARTS];
   float cst[ITEMS];
+#pragma unroll
+  for (int r = 0; r < ITEMS * PARTS; ++r) {
+    const int it = tid + 256 * r;
+    const int x = it / (16 * PARTS), j = (it / PARTS) % 16, pp = it % PARTS;
+    const bool ok = ((anybits >> x) & 1ull) && j < R;
+    const uint4 v = bld16(wr, ok ? (uint32_t)((x * R + j) * C * 4 + pp * 16) : kOffNone);
+    wst[r] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+  }
 #pragma unroll
   for (int r = 0; r < ITEMS; ++r) {
     const int it = tid + 256 * r;
     const int x = it / 16, j = it % 16;
     const bool ok = ((anybits >> x) & 1ull) && j < R;
-    const uint32_t wo = ok ? (uint32_t)((x * R + j) * C * 4) : kOffNone;
-#pragma unroll
-    for (int pp = 0; pp < PARTS; ++pp) {
-      const uint4 v = bld16(wr, wo + pp * 16);
-      wst[r][pp] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
-    }
     cst[r] = bld4f(cr, ok ? (uint32_t)((x * R + j) * 4) : kOffNone);
   }
   uint4 kf[GPW][NS];
@@ -490,12 +494,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     }
   }
 #pragma unroll
+  for (int r = 0; r < ITEMS * PARTS; ++r) {
+    const int it = tid + 256 * r;
+    wl[it / (16 * PARTS)][it % (16 * PARTS)] = wst[r];  // [x][j * PARTS + pp]
+  }
+#pragma unroll
   for (int r = 0; r < ITEMS; ++r) {
     const int it = tid + 256 * r;
-    const int x = it / 16, j = it % 16;
-#pragma unroll
-    for (int pp = 0; pp < PARTS; ++pp) wl[x][j * PARTS + pp] = wst[r][pp];
-    cl[x][j] = cst[r];
+    cl[it / 16][it % 16] = cst[r];
   }
   if constexpr (FROMLOG) {
     // zl[wave][quad][query] holds the quad's 4 keys: scatter key kk
@@ -647,19 +653,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   const int64_t rows = min((int64_t)KT, n_keys - k0);
   const rsrc_t kr = make_rsrc(Kc + k0 * A.kst, (uint32_t)((rows - 1) * A.kst * 2 + D * 2));
   constexpr int ITEMS = NCH * 16 / 256;
-  float4 wst[ITEMS][PARTS];
+  // w as 16-byte pieces in memory order, piece it -> (chunk x, plane j,
+  // part pp): with R = 16 consecutive lanes read consecutive bytes
+  float4 wst[ITEMS * PARTS];
   float cst[ITEMS];
+#pragma unroll
+  for (int r = 0; r < ITEMS * PARTS; ++r) {
+    const int it = tid + 256 * r;
+    const int x = it / (16 * PARTS), j = (it / PARTS) % 16, pp = it % PARTS;
+    const bool ok = ((anybits >> x) & 1ull) && j < R;
+    const uint4 v = bld16(wr, ok ? (uint32_t)((x * R + j) * C * 4 + pp * 16) : kOffNone);
+    wst[r] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+  }
 #pragma unroll
   for (int r = 0; r < ITEMS; ++r) {
     const int it = tid + 256 * r;
     const int x = it / 16, j = it % 16;
     const bool ok = ((anybits >> x) & 1ull) && j < R;
-    const uint32_t wo = ok ? (uint32_t)((x * R + j) * C * 4) : kOffNone;
-#pragma unroll
-    for (int pp = 0; pp < PARTS; ++pp) {
-      const uint4 v = bld16(wr, wo + pp * 16);
-      wst[r][pp] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
-    }
     cst[r] = bld4f(cr, ok ? (uint32_t)((x * R + j) * 4) : kOffNone);
   }
   uint4 kf[GPW][NS];
@@ -674,12 +684,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     for (int s = 0; s < NS; ++s) kf[gi][s] = bld16<0>(kr, ko + (4 * s + kg) * 16);
   }
 #pragma unroll
+  for (int r = 0; r < ITEMS * PARTS; ++r) {
+    const int it = tid + 256 * r;
+    wl[it / (16 * PARTS)][it % (16 * PARTS)] = wst[r];  // [x][j * PARTS + pp]
+  }
+#pragma unroll
   for (int r = 0; r < ITEMS; ++r) {
     const int it = tid + 256 * r;
-    const int x = it / 16, j = it % 16;
-#pragma unroll
-    for (int pp = 0; pp < PARTS; ++pp) wl[x][j * PARTS + pp] = wst[r][pp];
-    cl[x][j] = cst[r];
+    cl[it / 16][it % 16] = cst[r];
   }
   __syncthreads();
 
