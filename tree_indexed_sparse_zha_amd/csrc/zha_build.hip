@@ -744,11 +744,12 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
         if constexpr (C == 8) wz += __shfl_xor(wz, 16);
         if (leaf && j < R) {
           const int64_t nidx = (int64_t)cache * geo.node_cap[0] + kb0 / C + g / LPL;
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(A.tree + geo.g_off[0]) + (nidx * R + j) * C +
-                                     4 * (g % LPL)) = make_float4(wv[0], wv[1], wv[2], wv[3]);
+          // the tree is written once here and read by later calls: nontemporal stores
+          st16_nt(reinterpret_cast<float*>(A.tree + geo.g_off[0]) + (nidx * R + j) * C + 4 * (g % LPL), wv[0], wv[1],
+                  wv[2], wv[3]);
           if (g % LPL == 0) {
-            reinterpret_cast<float*>(A.tree + geo.L_off[0])[nidx * R + j] = L1;
-            reinterpret_cast<float*>(A.tree + geo.c_off[0])[nidx * R + j] = L1 - wz;
+            st4_nt(reinterpret_cast<float*>(A.tree + geo.L_off[0]) + nidx * R + j, L1);
+            st4_nt(reinterpret_cast<float*>(A.tree + geo.c_off[0]) + nidx * R + j, L1 - wz);
           }
         }
       }
@@ -816,8 +817,7 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
       if (C == 4 && j < R) {
         const int64_t nidx = (int64_t)cache * geo.node_cap[1] + kb0 / 16;
         if (w2) {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(A.tree + geo.g_off[1]) + (nidx * R + j) * 16 + 4 * g) =
-              make_float4(P[0], P[1], P[2], P[3]);
+          st16_nt(reinterpret_cast<float*>(A.tree + geo.g_off[1]) + (nidx * R + j) * 16 + 4 * g, P[0], P[1], P[2], P[3]);
         } else {
           char* gb = A.tree + geo.g_off[1] + nidx * R * D * 2;
 #pragma unroll
@@ -825,8 +825,8 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
             *reinterpret_cast<uint2*>(gb + ((int64_t)(2 * blk + g / 2) * R + j) * 16 + (g % 2) * 8) = pk[blk];
         }
         if (g == 0) {
-          reinterpret_cast<float*>(A.tree + geo.L_off[1])[nidx * R + j] = L2;
-          reinterpret_cast<float*>(A.tree + geo.c_off[1])[nidx * R + j] = w2 ? L2 - dot : L2 - dot * isd;
+          st4_nt(reinterpret_cast<float*>(A.tree + geo.L_off[1]) + nidx * R + j, L2);
+          st4_nt(reinterpret_cast<float*>(A.tree + geo.c_off[1]) + nidx * R + j, w2 ? L2 - dot : L2 - dot * isd);
         }
       }
     }

@@ -59,6 +59,13 @@ __device__ __forceinline__ float bld4f(rsrc_t r, uint32_t off) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, AUX));
 }
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+// Nontemporal stores for streams written once and read by a later kernel:
+// on MI355X, tiles that read 64 KiB and write 16 KiB move about 4% more
+// bytes per second with them than with plain stores.
+__device__ __forceinline__ void st16_nt(float* p, float a, float b, float c, float d) {
+  __builtin_nontemporal_store(f32x4{a, b, c, d}, reinterpret_cast<f32x4*>(p));
+}
+__device__ __forceinline__ void st4_nt(float* p, float a) { __builtin_nontemporal_store(a, p); }
 
 // Unpack one 16-byte piece into fp32 values.
 __device__ __forceinline__ void unpack(const uint4& v, float* out, bf16_t) {

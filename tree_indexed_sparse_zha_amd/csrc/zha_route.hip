@@ -537,7 +537,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       // reads them): row [quad][key][query], queries innermost
       float* lp = A.logits + (((int64_t)cache * gridDim.z + blockIdx.z) * A.nquads + quad) * 4 * A.QW + qn;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lp[i * A.QW] = zz[i];
+      for (int i = 0; i < 4; ++i) st4_nt(lp + i * A.QW, zz[i]);
     }
     if constexpr (Q4) {
       if (qn < 4) zl[wave][gi * 4 + kg][qn] = make_float4(zz[0], zz[1], zz[2], zz[3]);
@@ -571,8 +571,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       const int64_t quad = (k0 + wave * 64) / 4 + qq;
       if (((anybits >> xq) & 1ull) && quad < A.nquads) {
         const float* zr = reinterpret_cast<const float*>(&zl[wave][qq][0]);
-        *reinterpret_cast<float4*>(A.logits + ((((int64_t)cache * gridDim.z + blockIdx.z) * A.nquads + quad) * 4 + kk) * 4) =
-            make_float4(zr[kk], zr[4 + kk], zr[8 + kk], zr[12 + kk]);
+        st16_nt(A.logits + ((((int64_t)cache * gridDim.z + blockIdx.z) * A.nquads + quad) * 4 + kk) * 4, zr[kk], zr[4 + kk],
+                zr[8 + kk], zr[12 + kk]);
       }
     }
     const int u = lane & 3, part = (lane >> 2) % PARTS, cx = lane / (4 * PARTS);
@@ -734,7 +734,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       if (A.logits && qn < nq && quad < A.nquads) {
         float* lp = A.logits + (((int64_t)cache * QB + qg0 / 16) * A.nquads + quad) * 4 * A.QW + qn;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lp[i * A.QW] = zz[i];
+        for (int i = 0; i < 4; ++i) st4_nt(lp + i * A.QW, zz[i]);
       }
       float best = kNegInf;
 #pragma unroll UNR
