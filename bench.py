@@ -83,12 +83,14 @@ def selection_bytes(cfg: zha.ZhaConfig, buf, n_tokens: int, T: int, logits: bool
 
     route, per cache and level: |union over the cache's queries of the
     candidates| x (R*d*2 bytes of g + 4R bytes of c; fp8 g: R*d + 8R with the
-    row scales), or at a level that holds weights (level 1 in the weights
-    forms, level 2 in "weights2"; k keys per node) x (k*d*2 bytes of keys +
-    4Rk of weights + 4R of c, plus 4*min(QC,16) bytes of logits written per
-    key when they are kept); in "weights2" with at most 4 queries per cache,
-    level 1 reads the logits level 2 wrote instead of the keys
-    (4RC + 4R + 4*QC*C bytes per chunk);
+    row scales), or at level 1 in the weights forms x (C*d*2 bytes of keys +
+    4RC of weights + 4R of c, plus 4*min(QC,16) bytes of logits written per
+    key when they are kept); level 2 in "weights2" x (C*C*d*2 bytes of keys +
+    C*4RC of its chunks' weights + 4RC of child shares + 4R of c), and with
+    at most 4 queries per cache also its chunks' c (C*4R), the logits of its
+    keys (C*C*4*QC) and its chunks' level-1 scores (C*4*QC) written, while
+    level 1 then reads or writes each score row entry once (4*QC bytes per
+    chunk of the level);
     attend, per cache: |union over the cache's queries of the attended keys|
     x (d*2 bytes of V + d*2 bytes of K, or 4*min(QC,16) bytes of cached
     logits).  Also returns per-query selected share and per-level counts.
@@ -100,16 +102,15 @@ def selection_bytes(cfg: zha.ZhaConfig, buf, n_tokens: int, T: int, logits: bool
     node_bytes = R * d * gsize + 4 * R * (2 if cfg.g_dtype == "fp8" else 1)  # g, c (+ row scales)
     QW = min(QC, 16)  # useful logits per key (rows are padded to 4 in memory)
     top = top or Lv  # routing starts here; the levels above are not read
-    from_logits = logits and cfg.weight_keys(2) > 0 and QC <= 4 and top >= 2
-
-    def weights_level(k, writes):  # bytes per node of a level holding k-key weights
-        return k * d * cfg.esize + R * k * 4 + 4 * R + (k * QW * 4 if writes else 0)
+    fused = cfg.weight_keys(2) > 0 and QC <= 4 and top >= 2
 
     level_bytes = {lv: node_bytes for lv in range(1, Lv + 1)}
-    if cfg.weights:
-        level_bytes[1] = R * C * 4 + 4 * R + C * QW * 4 if from_logits else weights_level(C, logits)
-    if cfg.weight_keys(2):
-        level_bytes[2] = weights_level(C * C, from_logits)
+    if cfg.weights:  # level 1 from its keys and weights
+        level_bytes[1] = C * d * cfg.esize + R * C * 4 + 4 * R + (C * QW * 4 if logits else 0)
+    if cfg.weight_keys(2):  # level 2 from its keys, its chunks' weights and its child shares
+        level_bytes[2] = C * C * d * cfg.esize + C * R * C * 4 + R * C * 4 + 4 * R
+        if fused:
+            level_bytes[2] += C * 4 * R + C * 4 * QC + (C * C * QW * 4 if logits else 0)
     per_level = {}
     kept_prev = None
     for lv in range(top, 0, -1):
@@ -125,7 +126,7 @@ def selection_bytes(cfg: zha.ZhaConfig, buf, n_tokens: int, T: int, logits: bool
             cand_per_query=float(cand.sum().item()) / (caches * QC),
             kept_per_query=float(kept.sum().item()) / (caches * QC),
             union_cand_per_cache=union / caches,
-            alg_bytes=union * level_bytes[lv],
+            alg_bytes=(caches * QC * n * 4) if (lv == 1 and fused) else union * level_bytes[lv],
         )
         kept_prev = kept
     # attended keys: kept chunks + sink + current chunk

@@ -69,12 +69,13 @@ def test_tree_layout_weights_form():
 
 
 def test_tree_layout_weights2_form():
-    """Levels 1 and 2 hold weights: [R][C] and [R][C*C] fp32 per node; a
-    level-2 node shrinks from R*d*2 to R*C*C*4 bytes."""
+    """Level 1 holds the weights of its keys ([R][C] fp32), level 2 its
+    children's mass shares ([R][C] fp32): a level-2 node shrinks from R*d*2
+    to R*C*4 bytes."""
     cfg = cfg_deep(leaf_form="weights2")
     tl = zha.tree_layout(cfg)
     assert tl.g_bytes[0] == 16 * 4 * 4
-    assert tl.g_bytes[1] == 16 * 16 * 4
+    assert tl.g_bytes[1] == 16 * 4 * 4
     assert all(tl.g_bytes[i] == 16 * 128 * 2 for i in range(2, 6))
     w1 = zha.tree_layout(cfg_deep(leaf_form="weights"))
     assert [int(tl.node_cap[i]) for i in range(6)] == [int(w1.node_cap[i]) for i in range(6)]

@@ -242,6 +242,17 @@ def check_tree(cfg, tree, K, ref, N):
                 n = sizes[lv - 1]
                 got = zha.read_level(cfg, tree, lv, n)
                 lvl = to[lv - 1]
+                if lv == 2 and cfg.leaf_form == "weights2":
+                    # each child's share of the node's mass: exp(L(child) - L) from the oracle's
+                    # level-1 and level-2 L (0 for the children a trailing node lacks)
+                    gr, gL, gc = np64(got["rho"][cache]), np64(got["L"][cache]), np64(got["c"][cache])
+                    L1p = np.full((n * cfg.chunk, cfg.n_ref), -np.inf)
+                    L1p[: sizes[0]] = to[0].L
+                    rho = np.exp(L1p.reshape(n, cfg.chunk, cfg.n_ref) - lvl.L[:, None, :]).transpose(0, 2, 1)
+                    np.testing.assert_allclose(gr, rho, rtol=1e-5, atol=2e-6, err_msg="rho level 2")
+                    np.testing.assert_allclose(gL, lvl.L, rtol=1e-5, atol=3e-5, err_msg="L level 2")
+                    np.testing.assert_allclose(gc, lvl.c, rtol=1e-5, atol=3e-5, err_msg="c level 2")
+                    continue
                 wk = cfg.weight_keys(lv)
                 if wk:
                     # w is the softmax of r_j . k_i / sqrt(d) over the node's own keys (scipy),
@@ -594,42 +605,51 @@ W2_LOGIT_CASES = [
 
 
 @pytest.mark.parametrize("name,kw,T,N,p,top", W2_LOGIT_CASES, ids=[c[0] for c in W2_LOGIT_CASES])
-def test_level1_from_level2_logits_is_bit_identical(name, kw, T, N, p, top):
-    """Levels 1 and 2 as weights, at most 4 queries per cache: level 1 scored
-    from the logits the level-2 pass stored reaches exactly the scores,
-    selections and statistics of level 1 scored from the keys (a route call
-    without the logits buffer), and attention reading those logits agrees
-    with attention computing its own."""
-    _say(f"w2 logits {name}")
-    cfg = zha.ZhaConfig(dtype="bf16", leaf_form="weights2", **kw)
-    K, V, Q, ref = random_inputs(cfg, T, seed=9)
-    tree = zha.alloc_tree(cfg)
-    zha.build(cfg, K, ref, tree, N)
-    with_lg = zha.alloc_route(cfg, T, logits=True)
-    no_lg = zha.alloc_route(cfg, T, logits=False)
-    pl = [p] * cfg.levels
-    for buf in (with_lg, no_lg):
+def test_fused_level1_scores_match_the_key_path(name, kw, T, N, p, top):
+    """Levels 1 and 2 as weights, at most 4 queries per cache: the level-2
+    pass writes the level-1 scores of its candidates' chunks from the same
+    MFMA logits and level-1 rows the level-1 kernel of the leaf-weights form
+    uses, so on every chunk both trees hold as a candidate the two level-1
+    scores agree (to fp32 rounding of the same expression); the fused rows
+    hold -inf exactly off the kept parents' children; attention reading the
+    kept logits agrees with attention computing its own."""
+    _say(f"w2 fused level 1 {name}")
+    cfg2 = zha.ZhaConfig(dtype="bf16", leaf_form="weights2", **kw)
+    cfg1 = zha.ZhaConfig(dtype="bf16", leaf_form="weights", **kw)
+    K, V, Q, ref = random_inputs(cfg2, T, seed=9)
+    pl = [p] * cfg2.levels
+    bufs = {}
+    for cfg in (cfg2, cfg1):
+        tree = zha.alloc_tree(cfg)
+        zha.build(cfg, K, ref, tree, N)
+        buf = zha.alloc_route(cfg, T, logits=True)
         buf.score.fill_(float("nan"))
         zha.route_levels(cfg, tree, N, Q, T, pl, buf, top_level=top, K=K)
+        bufs[cfg.leaf_form] = buf
     torch.cuda.synchronize()
-    rl = with_lg.layout
-    for i in range(cfg.levels if top == 0 else top):
-        a0, a1 = int(rl.sel_offset[i]), int(rl.sel_offset[i]) + int(rl.n_queries) * int(rl.words[i])
-        assert torch.equal(with_lg.sel[a0:a1], no_lg.sel[a0:a1]), f"level {i + 1} bits"
-        s0, s1 = int(rl.score_offset[i]), int(rl.score_offset[i]) + int(rl.n_queries) * int(rl.score_stride[i])
-        sa, sb = with_lg.score[s0:s1], no_lg.score[s0:s1]
-        assert torch.equal(sa.nan_to_num(), sb.nan_to_num()), f"level {i + 1} scores"
-        t0 = int(rl.stats_offset[i]) * zha.STATS_BYTES
-        t1 = t0 + int(rl.n_queries) * zha.STATS_BYTES
-        assert torch.equal(with_lg.stats[t0:t1], no_lg.stats[t0:t1]), f"level {i + 1} statistics"
-    assert int(zha.level1_sel(with_lg).ne(0).sum()) > 0
-    check_cached_logits(cfg, with_lg, K, Q, N, T)
-    nq = int(rl.n_queries)
-    ws = torch.empty(zha.attend_workspace_bytes(cfg, T), dtype=torch.uint8, device="cuda")
+    b2, b1 = bufs["weights2"], bufs["weights"]
+    n1 = N // cfg2.chunk
+    nq = int(b2.layout.n_queries)
+    both = 0
+    for qi in range(nq):
+        bits2, s2 = gpu_levels(cfg2, b2, N, qi)
+        bits1, s1 = gpu_levels(cfg1, b1, N, qi)
+        # candidates of the fused row: children of the kept level-2 nodes (all chunks when level 1 is the top)
+        cand = np.ones(n1, bool) if top == 1 else np.repeat(bits2[2], cfg2.chunk)[:n1].astype(bool)
+        assert np.all(np.isfinite(s2[1][cand])), f"query {qi}: a candidate without a score"
+        assert np.all(np.isneginf(s2[1][~cand])), f"query {qi}: a non-candidate with a score"
+        common = cand & np.isfinite(s1[1])
+        both += int(common.sum())
+        d = np.abs(s2[1][common].astype(np.float64) - s1[1][common].astype(np.float64))
+        tol = 4e-6 * (1.0 + np.abs(s1[1][common]))
+        assert np.all(d <= tol), f"query {qi}: level-1 scores differ by {float(d.max())}"
+    assert both > 0
+    check_cached_logits(cfg2, b2, K, Q, N, T)
+    ws = torch.empty(zha.attend_workspace_bytes(cfg2, T), dtype=torch.uint8, device="cuda")
     outs = []
-    for lg in (None, with_lg.logits):
-        out, lse = torch.empty(nq, cfg.head_dim, device="cuda"), torch.empty(nq, device="cuda")
-        zha.attend(cfg, Q, T, K, V, N, zha.level1_sel(with_lg), 3, out, lse, ws, logits=lg)
+    for lg in (None, b2.logits):
+        out, lse = torch.empty(nq, cfg2.head_dim, device="cuda"), torch.empty(nq, device="cuda")
+        zha.attend(cfg2, Q, T, K, V, N, zha.level1_sel(b2), 3, out, lse, ws, logits=lg)
         outs.append((out, lse))
     torch.cuda.synchronize()
     assert float((outs[0][0] - outs[1][0]).abs().max()) <= 2e-5

@@ -91,8 +91,10 @@ int check_strides(const int64_t* s, int n, int es, const char* name) {
   return ZHA_OK;
 }
 
-// Keys per node of level index l when that level stores softmax weights
-// (level 1 in both weights forms, level 2 in ZHA_LEAF_WEIGHTS2), else 0.
+// Keys per node of level index l when routing scores that level from its
+// keys (level 1 in both weights forms, which store the weights of the C
+// keys; level 2 in ZHA_LEAF_WEIGHTS2, which stores its C children's mass
+// shares), else 0.
 static int weight_keys(const zha_config* c, int l) {
   if (l == 0 && (c->leaf_form == ZHA_LEAF_WEIGHTS || c->leaf_form == ZHA_LEAF_WEIGHTS2)) return c->chunk;
   if (l == 1 && c->leaf_form == ZHA_LEAF_WEIGHTS2) return c->chunk * c->chunk;
@@ -113,7 +115,8 @@ void fill_tree_layout(const zha_config* c, zha_tree_layout* out) {
     if (l > 0) n = cdiv(n, c->chunk);
     const int wk = weight_keys(c, l);
     const bool fp8 = wk == 0 && c->g_dtype == ZHA_G_FP8;
-    out->g_bytes[l] = wk ? (int64_t)c->n_ref * wk * 4
+    // weights [R][wk] fp32, or at level 2 of ZHA_LEAF_WEIGHTS2 the child shares [R][C]
+    out->g_bytes[l] = wk ? (int64_t)c->n_ref * (l == 1 ? c->chunk : wk) * 4
                          : (int64_t)c->n_ref * c->head_dim * (fp8 ? 1 : esize(c->kv_dtype));
     out->node_cap[l] = n;
     out->g_offset[l] = off;
@@ -443,9 +446,10 @@ static int do_route(const zha_config* cfg, const void* tree, int64_t n_tokens, c
   void* split = rl.workspace_bytes > rl.workspace_min_bytes && ws_bytes >= rl.workspace_bytes
                     ? static_cast<void*>(static_cast<char*>(ws) + rl.workspace_min_bytes)
                     : nullptr;
-  // level 1 reads the logits the level-2 pass stores when level 2 holds
-  // weights, is scored in this call and a cache has at most 4 queries
-  const bool from_logits = logits && weight_keys(cfg, 1) && top >= 2 && (int64_t)cfg->q_per_kv * T <= 4;
+  // levels 1-2 as weights, level 2 scored in this call and at most 4 queries
+  // per cache: the level-2 pass also writes the level-1 scores (and the
+  // logits attention reads), and level 1 only masks them by the kept parents
+  const bool fuse1 = weight_keys(cfg, 1) && top >= 2 && (int64_t)cfg->q_per_kv * T <= 4;
   if (cfg->kv_dtype != ZHA_BF16) {
     // the fp32 score kernel accumulates its single slot per query with atomics
     hipError_t e = zha::launch_route_init(keyrange, kr_bytes / 16, pr);
@@ -501,11 +505,18 @@ static int do_route(const zha_config* cfg, const void* tree, int64_t n_tokens, c
       sa.ksh = k_strides[1];
       sa.kst = k_strides[2];
       sa.n_keys = n[0] * cfg->chunk;
-      // level 1 writes the logits, or reads those of level 2 (from_logits)
-      sa.logits = (l == 0 || from_logits) ? logits : nullptr;
-      sa.from_logits = l == 0 && from_logits;
+      // the logits are written by level 1, or by level 2 when it is fused
+      sa.logits = (l == 0) != fuse1 ? logits : nullptr;
+      sa.fuse1 = l == 0 && fuse1;
       sa.nquads = tl.node_cap[0] * cfg->chunk / 4;
       sa.QW = logits_row(sa.QC);
+      if (l == 1) {  // level 2 holding child shares: the level-1 rows it reads (and fills)
+        sa.w1 = reinterpret_cast<const float*>(static_cast<const char*>(tree) + tl.g_offset[0]);
+        sa.c1 = reinterpret_cast<const float*>(static_cast<const char*>(tree) + tl.c_offset[0]);
+        sa.node_cap1 = tl.node_cap[0];
+        sa.score1 = fuse1 ? score + rl.score_offset[0] : nullptr;
+        sa.score1_stride = rl.score_stride[0];
+      }
     }
     zha::SelectArgs se;
     std::memset(&se, 0, sizeof(se));

@@ -683,6 +683,7 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
         s1 += e[s];
       }
       if constexpr (C == 8) s1 += __shfl_xor(s1, 16);
+      float Lleaf = 0.f;  // weights form: the log mass of this lane's leaf
       if (!geo.leaf_weights) {
         // mean form: leaf l's g_j = sum_i w_ji k_i over its C keys is C / 4
         // fp32 MFMAs per 16 values of d (K = 4 of the leaf's keys; lane (j, g)
@@ -734,6 +735,7 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
       } else {
         // weights form: w_ji = exp(z_ji - L_j), c_j = L_j - sum_i w_ji z_ji
         const float L1 = m1 + __logf(s1);
+        Lleaf = L1;
         const float inv1 = 1.f / s1;
         float wv[4], wz = 0.f;
 #pragma unroll
@@ -786,8 +788,10 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
       }
       // keep the fp32 form (L, mean g) for the round's node and, when C = 4,
       // emit it as the level-2 node (lane: d = 16b + 4g + i of plane j): its
-      // rounded mean keys, or, when level 2 too holds weights, the
-      // normalised weights P of its 16 keys with c = L - sum_i P_i z_i
+      // rounded mean keys, or, when level 2 is scored from its keys, the mass
+      // share exp(L(leaf g) - L) of each child (so that the weight of key i
+      // of leaf g is that share times the leaf's own w) with
+      // c = L - sum_i P_i z_i, P the normalised weights of its 16 keys
       const bool w2 = C == 4 && geo.w2;
       float dot = 0.f;
       uint2 pk[NB];
@@ -817,7 +821,7 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
       if (C == 4 && j < R) {
         const int64_t nidx = (int64_t)cache * geo.node_cap[1] + kb0 / 16;
         if (w2) {
-          st16_nt(reinterpret_cast<float*>(A.tree + geo.g_off[1]) + (nidx * R + j) * 16 + 4 * g, P[0], P[1], P[2], P[3]);
+          st4_nt(reinterpret_cast<float*>(A.tree + geo.g_off[1]) + (nidx * R + j) * 4 + g, leaf ? __expf(Lleaf - L2) : 0.f);
         } else {
           char* gb = A.tree + geo.g_off[1] + nidx * R * D * 2;
 #pragma unroll

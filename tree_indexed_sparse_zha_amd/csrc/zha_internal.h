@@ -104,8 +104,15 @@ struct ScoreArgs {
   int leaf_weights;            // a weights-form level: g holds w [R][C] fp32, C keys per node
   int wkeys;                   // weights form: keys per node (C at level 1, C * C at level 2)
   int64_t n_keys;              // weights form: keys of the complete chunks (a trailing node may cover fewer)
-  int from_logits;             // weights form, level 1, at most 4 queries per cache: the logits
-                               // the level-2 pass wrote stand in for the keys
+  // level 2 holding its children's mass shares (chunk 4): g holds rho
+  // [R][4] per node, and its plane sums are rho-weighted sums of the
+  // children's level-1 sums, from the level-1 weights w1 [R][4] per chunk
+  const float* w1;
+  const float* c1;             // level-1 c (fused level-1 scores)
+  int64_t node_cap1;           // level-1 nodes per cache
+  float* score1;               // fused: level-1 score rows the level-2 pass writes, or nullptr
+  int64_t score1_stride;
+  int fuse1;                   // level 1 after a fused level-2 pass: mask the rows, publish key ranges
   const void* K;               // keys (weights form only)
   int64_t ksb, ksh, kst;
   int64_t causal_n0;           // prefill: query t of a head sits at position causal_n0 + t; -1 = decode

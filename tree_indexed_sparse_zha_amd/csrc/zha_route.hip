@@ -389,13 +389,20 @@ __global__ __launch_bounds__(256) void k_score_smallr(ScoreArgs A) {
 // RT: R as a compile-time constant (0 = runtime).  Q4: at most 4 queries per
 // cache; the MFMA then fills only 4 of its 16 query columns, so the logits
 // go through LDS and the plane fold runs with lanes = (chunk, part, query),
-// every lane busy.  C is the keys per node (C * C for level 2 when it too
-// holds weights), CP the children per parent.  FROMLOG (Q4, level 1 under a
-// weights-form level 2): the logits the level-2 pass stored for every key of
-// its candidates stand in for the keys and the MFMA; the fold is the same.
-template <int D, int C, int RT, bool Q4, int CP = C, bool FROMLOG = false>
+// every lane busy.  C is the keys per node.  MODE 1: level 2 under chunk 4
+// (16-key nodes, 4 children per parent) holding its children's mass shares
+// rho_cj = exp(L_j(chunk c) - L_j(node)): the node's weight of key i in chunk
+// c is rho_cj w_ji(chunk c), so its plane sum is sum_c rho_cj times the
+// chunk's own sum over its keys, which the fold forms anyway.  MODE 2 (Q4):
+// MODE 1, and the chunk sums also give every chunk's level-1 plane
+// c_j(chunk) + sum_i w_ji s_i, written to the level-1 score rows, so level 1
+// needs neither its keys nor its logits again.
+template <int D, int C, int RT, bool Q4, int MODE = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_score_leafw(ScoreArgs A) {
-  static_assert(!FROMLOG || (Q4 && C == 4), "logits rows are read as 4-key quads of at most 4 queries");
+  static_assert(MODE == 0 || C == 16, "child shares: 16-key nodes of 4 chunks");
+  static_assert(MODE < 2 || Q4, "fused level-1 scores: at most 4 queries per cache");
+  constexpr int CP = MODE ? 4 : C;   // children per parent
+  constexpr int GW = MODE ? 4 : C;   // floats per plane of a node's g block (w, or rho)
   constexpr int NS = D / 32;
   constexpr int KT = 256;       // keys per tile
   constexpr int NCH = KT / C;   // chunks per tile (<= 64)
@@ -416,9 +423,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   __shared__ float cl[NCH][17];
   __shared__ float4 zl[Q4 ? 4 : 1][16][4];  // Q4: [wave][quad of the wave][query] logits
   __shared__ unsigned long long mbl[16];    // candidate bits per query
+  __shared__ float rl[MODE ? NCH : 1][WROW];     // MODE: rho of node x, plane j, chunk part
+  __shared__ float c1l[MODE == 2 ? 4 * NCH : 1][17];  // MODE 2: c of the tile's chunks
 
   bf16x8 bq[NS];
-  if constexpr (!FROMLOG) {
+  {
     const int qi = qg0 + qn;
     if (qn < nq) {
       const int b = cache / A.H, h = cache % A.H, gq = qi / A.T, t = qi % A.T;
@@ -433,7 +442,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   }
   const int b = cache / A.H, h = cache % A.H;
   const bf16_t* Kc = reinterpret_cast<const bf16_t*>(A.K) + (int64_t)b * A.ksb + (int64_t)h * A.ksh;
-  const float* wcache = reinterpret_cast<const float*>(A.g) + (int64_t)cache * A.node_cap * R * C;
+  const float* wcache = reinterpret_cast<const float*>(A.g) + (int64_t)cache * A.node_cap * R * GW;
   const float* ccache = A.c + (int64_t)cache * A.node_cap * R;
 
   // candidate bits of the tile's chunks for query qn (bit x = chunk m0 + x)
@@ -448,21 +457,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   // this wave's live groups; only the w/c loads are waited for before the
   // LDS stores, the K loads stay in flight across the barrier.
   const int64_t n_valid = min((int64_t)NCH, A.n_nodes - m0);  // chunks of this tile (>= 1)
-  const rsrc_t wr = make_rsrc(wcache + m0 * R * C, (uint32_t)(n_valid * R * C * 4));
+  const rsrc_t wr = make_rsrc(wcache + m0 * R * GW, (uint32_t)(n_valid * R * GW * 4));
   const rsrc_t cr = make_rsrc(ccache + m0 * R, (uint32_t)(n_valid * R * 4));
   const int64_t rows = min((int64_t)KT, n_keys - k0);  // keys of complete chunks in this tile
   const rsrc_t kr = make_rsrc(Kc + k0 * A.kst, (uint32_t)((rows - 1) * A.kst * 2 + D * 2));
+  // MODE: the level-1 rows of the tile's chunks (w1, and c1 in MODE 2)
+  const int64_t c0 = m0 * 4;                                    // first chunk of the tile
+  const int64_t n1v = MODE ? min((int64_t)KT / 4, n_keys / 4 - c0) : 0;  // its chunks (>= 1)
+  const rsrc_t w1r = make_rsrc(MODE ? A.w1 + ((int64_t)cache * A.node_cap1 + c0) * R * 4 : nullptr,
+                               (uint32_t)(n1v * R * 16));
   constexpr int ITEMS = NCH * 16 / 256;
   // w as 16-byte pieces in memory order, piece it -> (chunk x, plane j,
-  // part pp): with R = 16 consecutive lanes read consecutive bytes
+  // part pp): with R = 16 consecutive lanes read consecutive bytes (MODE:
+  // part pp of node x is chunk 4x + pp, read from its own w1 row, and rho
+  // of (node x, plane j, chunk pp) is one float in the same order)
   float4 wst[ITEMS * PARTS];
+  float rst[MODE ? ITEMS * PARTS : 1];
   float cst[ITEMS];
 #pragma unroll
   for (int r = 0; r < ITEMS * PARTS; ++r) {
     const int it = tid + 256 * r;
     const int x = it / (16 * PARTS), j = (it / PARTS) % 16, pp = it % PARTS;
     const bool ok = ((anybits >> x) & 1ull) && j < R;
-    const uint4 v = bld16(wr, ok ? (uint32_t)((x * R + j) * C * 4 + pp * 16) : kOffNone);
+    uint4 v;
+    if constexpr (MODE) {
+      v = bld16(w1r, ok ? (uint32_t)(((4 * x + pp) * R + j) * 16) : kOffNone);
+      rst[r] = bld4f(wr, ok ? (uint32_t)(((x * R + j) * 4 + pp) * 4) : kOffNone);
+    } else {
+      v = bld16(wr, ok ? (uint32_t)((x * R + j) * C * 4 + pp * 16) : kOffNone);
+    }
     wst[r] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
   }
 #pragma unroll
@@ -472,44 +495,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     const bool ok = ((anybits >> x) & 1ull) && j < R;
     cst[r] = bld4f(cr, ok ? (uint32_t)((x * R + j) * 4) : kOffNone);
   }
+  constexpr int C1I = MODE == 2 ? 4 * NCH * 16 / 256 : 1;  // c1 items per thread
+  float c1st[C1I];
+  if constexpr (MODE == 2) {
+    const rsrc_t c1r = make_rsrc(A.c1 + ((int64_t)cache * A.node_cap1 + c0) * R, (uint32_t)(n1v * R * 4));
+#pragma unroll
+    for (int r = 0; r < C1I; ++r) {
+      const int it = tid + 256 * r;
+      const int ch = it / 16, j = it % 16;
+      const bool ok = ((anybits >> (ch / 4)) & 1ull) && j < R;
+      c1st[r] = bld4f(c1r, ok ? (uint32_t)((ch * R + j) * 4) : kOffNone);
+    }
+  }
   uint4 kf[GPW][NS];
   bool live[GPW];
-  uint4 lg = make_uint4(0, 0, 0, 0);
-  if constexpr (FROMLOG) {
-    // lane (quad qq of the wave, key kk): the stored logits of key kk of the
-    // quad for queries 0..3 (a chunk is a quad; non-candidates read zeros)
-    const int qq = lane >> 2, kk = lane & 3;
-    const int x = wave * 16 + qq;
-    const rsrc_t lr = make_rsrc(A.logits + ((int64_t)cache * A.nquads + m0) * 16, (uint32_t)(n_valid * 64));
-    lg = bld16(lr, ((anybits >> x) & 1ull) ? (uint32_t)((x * 4 + kk) * 16) : kOffNone);
-  } else {
 #pragma unroll
-    for (int gi = 0; gi < GPW; ++gi) {
-      const int g = wave * GPW + gi;
-      const unsigned long long gmask = ((1ull << (16 / C)) - 1ull) << (g * 16 / C);
-      live[gi] = (anybits & gmask) != 0ull;
-      const uint32_t ko = live[gi] ? (uint32_t)((g * 16 + qn) * A.kst * 2) : kOffNone;
+  for (int gi = 0; gi < GPW; ++gi) {
+    const int g = wave * GPW + gi;
+    const unsigned long long gmask = ((1ull << (16 / C)) - 1ull) << (g * 16 / C);
+    live[gi] = (anybits & gmask) != 0ull;
+    const uint32_t ko = live[gi] ? (uint32_t)((g * 16 + qn) * A.kst * 2) : kOffNone;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) kf[gi][s] = bld16<0>(kr, ko + (4 * s + kg) * 16);
-    }
+    for (int s = 0; s < NS; ++s) kf[gi][s] = bld16<0>(kr, ko + (4 * s + kg) * 16);
   }
 #pragma unroll
   for (int r = 0; r < ITEMS * PARTS; ++r) {
     const int it = tid + 256 * r;
     wl[it / (16 * PARTS)][it % (16 * PARTS)] = wst[r];  // [x][j * PARTS + pp]
+    if constexpr (MODE) rl[it / (16 * PARTS)][it % (16 * PARTS)] = rst[r];
   }
 #pragma unroll
   for (int r = 0; r < ITEMS; ++r) {
     const int it = tid + 256 * r;
     cl[it / 16][it % 16] = cst[r];
   }
-  if constexpr (FROMLOG) {
-    // zl[wave][quad][query] holds the quad's 4 keys: scatter key kk
-    float* zq = reinterpret_cast<float*>(&zl[wave][lane >> 2][0]) + (lane & 3);
-    zq[0] = __uint_as_float(lg.x);
-    zq[4] = __uint_as_float(lg.y);
-    zq[8] = __uint_as_float(lg.z);
-    zq[12] = __uint_as_float(lg.w);
+  if constexpr (MODE == 2) {
+#pragma unroll
+    for (int r = 0; r < C1I; ++r) {
+      const int it = tid + 256 * r;
+      c1l[it / 16][it % 16] = c1st[r];
+    }
   }
   if (tid < 16) mbl[tid] = mybits;  // lanes 0..15: kg 0, query qn = tid
   __syncthreads();
@@ -517,7 +542,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   const int RR = RT > 0 ? RT : R;
   constexpr int UNR = RT <= 0 ? 1 : RT < 4 ? RT : 4;  // plane loop unroll
 #pragma unroll
-  for (int gi = 0; gi < (FROMLOG ? 0 : GPW); ++gi) {
+  for (int gi = 0; gi < GPW; ++gi) {
     const int g = wave * GPW + gi;
     const int x = (g * 16 + 4 * kg) / C;  // chunk (within the tile) of this lane's 4 keys
     const int part = kg % PARTS;
@@ -549,6 +574,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       for (int jj = 0; jj < RR; ++jj) {
         const float4 wv = wl[x][jj * PARTS + part];
         float v = wv.x * zz[0] + wv.y * zz[1] + wv.z * zz[2] + wv.w * zz[3];
+        if constexpr (MODE) v *= rl[x][jj * PARTS + part];  // the chunk's share of the node
 #pragma unroll
         for (int o = 16; o < 16 * PARTS; o <<= 1) v += __shfl_xor(v, o);
         best = fmaxf(best, cl[x][jj] + v);
@@ -560,7 +586,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     // lanes (query u, part, chunk cx) over the wave's 64 / C chunks; quads of
     // dead groups hold stale LDS data, discarded by the candidate bit
     wave_sync();
-    if (!FROMLOG && A.logits) {
+    if (A.logits) {
       // the wave's 16 quads as rows [quad][key][query]: lane (quad qq, key
       // kk) gathers the 4 queries' logits of its key and stores them as one
       // 16-byte piece, so the wave writes 1 KiB with one coalesced store
@@ -578,16 +604,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     const int u = lane & 3, part = (lane >> 2) % PARTS, cx = lane / (4 * PARTS);
     const int x = wave * (64 / C) + cx;
     const float4 zv = zl[wave][cx * PARTS + part][u];
-    float best = kNegInf;
+    float best = kNegInf, best1 = kNegInf;
 #pragma unroll UNR
     for (int jj = 0; jj < RR; ++jj) {
       const float4 wv = wl[x][jj * PARTS + part];
       float v = wv.x * zv.x + wv.y * zv.y + wv.z * zv.z + wv.w * zv.w;
+      if constexpr (MODE == 2) best1 = fmaxf(best1, c1l[4 * x + part][jj] + v);  // chunk 4x + part's plane
+      if constexpr (MODE) v *= rl[x][jj * PARTS + part];  // the chunk's share of the node
 #pragma unroll
       for (int o = 4; o < 4 * PARTS; o <<= 1) v += __shfl_xor(v, o);
       best = fmaxf(best, cl[x][jj] + v);
     }
     if (part == 0 && u < nq) sc[u][x] = ((mbl[u] >> x) & 1ull) ? best : kNegInf;
+    if constexpr (MODE == 2) {
+      // level-1 score of chunk 4(m0 + x) + part for query u, for every chunk
+      // of a node some query has as candidate (the level-1 pass keeps those
+      // whose parent is kept)
+      const int64_t ch = 4 * (m0 + x) + part;
+      if (u < nq && ((anybits >> x) & 1ull) && ch < n_keys / 4)
+        A.score1[((int64_t)cache * A.QC + qg0 + u) * A.score1_stride + ch] = best1;
+    }
   }
   __syncthreads();
   for (int idx = tid; idx < nq * NCH; idx += 256) {
@@ -612,8 +648,10 @@ constexpr int kMqBlocks = 16;
 // workgroup: walking 16 blocks in one workgroup would leave the GPU idle
 constexpr int64_t kMqMinTiles = 256;
 
-template <int D, int C, int RT, int CP = C>
+template <int D, int C, int RT, int MODE = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_score_leafw_mq(ScoreArgs A) {
+  static_assert(MODE == 0 || C == 16, "child shares: 16-key nodes of 4 chunks");
+  constexpr int CP = MODE ? 4 : C;  // children per parent
   constexpr int NS = D / 32;
   constexpr int KT = 256;
   constexpr int NCH = KT / C;
@@ -629,13 +667,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   const int qn = lane & 15, kg = lane >> 4;
   const int64_t n_keys = A.n_keys;
   constexpr int WROW = 16 * PARTS + 1;
+  constexpr int GW = MODE ? 4 : C;  // floats per plane of a node's g block (w, or rho)
   __shared__ float sc[16][NCH + 1];
   __shared__ float4 wl[NCH][WROW];
   __shared__ float cl[NCH][17];
+  __shared__ float rl[MODE ? NCH : 1][WROW];
 
   const int b = cache / A.H, h = cache % A.H;
   const bf16_t* Kc = reinterpret_cast<const bf16_t*>(A.K) + (int64_t)b * A.ksb + (int64_t)h * A.ksh;
-  const float* wcache = reinterpret_cast<const float*>(A.g) + (int64_t)cache * A.node_cap * R * C;
+  const float* wcache = reinterpret_cast<const float*>(A.g) + (int64_t)cache * A.node_cap * R * GW;
   const float* ccache = A.c + (int64_t)cache * A.node_cap * R;
 
   // candidate bits of the tile's chunks for query qg0 + qn
@@ -648,21 +688,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   for (int o = 1; o < 16; o <<= 1) anybits |= __shfl_xor(anybits, o);
 
   const int64_t n_valid = min((int64_t)NCH, A.n_nodes - m0);
-  const rsrc_t wr = make_rsrc(wcache + m0 * R * C, (uint32_t)(n_valid * R * C * 4));
+  const rsrc_t wr = make_rsrc(wcache + m0 * R * GW, (uint32_t)(n_valid * R * GW * 4));
   const rsrc_t cr = make_rsrc(ccache + m0 * R, (uint32_t)(n_valid * R * 4));
   const int64_t rows = min((int64_t)KT, n_keys - k0);
   const rsrc_t kr = make_rsrc(Kc + k0 * A.kst, (uint32_t)((rows - 1) * A.kst * 2 + D * 2));
+  const int64_t c0 = m0 * 4;  // MODE: first level-1 chunk of the tile, and its chunks
+  const int64_t n1v = MODE ? min((int64_t)KT / 4, n_keys / 4 - c0) : 0;
+  const rsrc_t w1r = make_rsrc(MODE ? A.w1 + ((int64_t)cache * A.node_cap1 + c0) * R * 4 : nullptr,
+                               (uint32_t)(n1v * R * 16));
   constexpr int ITEMS = NCH * 16 / 256;
   // w as 16-byte pieces in memory order, piece it -> (chunk x, plane j,
-  // part pp): with R = 16 consecutive lanes read consecutive bytes
+  // part pp): with R = 16 consecutive lanes read consecutive bytes (MODE:
+  // chunk 4x + pp's own w1 row, and its share rho of node x)
   float4 wst[ITEMS * PARTS];
+  float rst[MODE ? ITEMS * PARTS : 1];
   float cst[ITEMS];
 #pragma unroll
   for (int r = 0; r < ITEMS * PARTS; ++r) {
     const int it = tid + 256 * r;
     const int x = it / (16 * PARTS), j = (it / PARTS) % 16, pp = it % PARTS;
     const bool ok = ((anybits >> x) & 1ull) && j < R;
-    const uint4 v = bld16(wr, ok ? (uint32_t)((x * R + j) * C * 4 + pp * 16) : kOffNone);
+    uint4 v;
+    if constexpr (MODE) {
+      v = bld16(w1r, ok ? (uint32_t)(((4 * x + pp) * R + j) * 16) : kOffNone);
+      rst[r] = bld4f(wr, ok ? (uint32_t)(((x * R + j) * 4 + pp) * 4) : kOffNone);
+    } else {
+      v = bld16(wr, ok ? (uint32_t)((x * R + j) * C * 4 + pp * 16) : kOffNone);
+    }
     wst[r] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
   }
 #pragma unroll
@@ -687,6 +739,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   for (int r = 0; r < ITEMS * PARTS; ++r) {
     const int it = tid + 256 * r;
     wl[it / (16 * PARTS)][it % (16 * PARTS)] = wst[r];  // [x][j * PARTS + pp]
+    if constexpr (MODE) rl[it / (16 * PARTS)][it % (16 * PARTS)] = rst[r];
   }
 #pragma unroll
   for (int r = 0; r < ITEMS; ++r) {
@@ -741,6 +794,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       for (int jj = 0; jj < RR; ++jj) {
         const float4 wv = wl[x][jj * PARTS + part];
         float v = wv.x * zz[0] + wv.y * zz[1] + wv.z * zz[2] + wv.w * zz[3];
+        if constexpr (MODE) v *= rl[x][jj * PARTS + part];  // the chunk's share of the node
 #pragma unroll
         for (int o = 16; o < 16 * PARTS; o <<= 1) v += __shfl_xor(v, o);
         best = fmaxf(best, cl[x][jj] + v);
@@ -759,6 +813,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       publish_range(A.keyrange + (((int64_t)cache * A.QC + qg0 + q) * A.kr_slots + blockIdx.x) * 4, c, order_key(v));
     }
     __syncthreads();
+  }
+}
+
+// Level 1 after a fused level-2 pass (chunk 4, at most 4 queries per cache):
+// that pass wrote the plane score of every chunk of its candidates; a chunk
+// is a candidate of a query iff the query kept its parent, so the others
+// become -inf here, and every (query, 256-key tile) publishes its candidate
+// key range for the select.  Wave w of a workgroup is query w; a workgroup
+// walks kMaskTiles consecutive tiles of 64 chunks.
+constexpr int kMaskTiles = 16;
+__global__ __launch_bounds__(256) void k_score_mask1(ScoreArgs A, int64_t n_tiles) {
+  const int qi = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (qi >= A.QC) return;  // whole waves
+  const int cache = blockIdx.y;
+  const int64_t row = (int64_t)cache * A.QC + qi;
+  const uint32_t* prow = A.sel_parent + row * A.parent_words;
+  float* srow = A.score + row * A.score_stride;
+  // every load first (the row entry and the parent word of each of the
+  // lane's kMaskTiles chunks), then the masking and the key ranges
+  const int64_t m0 = (int64_t)blockIdx.x * kMaskTiles * 64 + lane;
+  float v[kMaskTiles];
+  uint32_t pw[kMaskTiles];
+#pragma unroll
+  for (int t = 0; t < kMaskTiles; ++t) {
+    const int64_t m = m0 + 64 * t;
+    const bool in = m < A.n_nodes;
+    v[t] = in ? srow[m] : kNegInf;
+    pw[t] = in ? prow[(m / 4) >> 5] : 0u;
+  }
+#pragma unroll
+  for (int t = 0; t < kMaskTiles; ++t) {
+    const int64_t tile = (int64_t)blockIdx.x * kMaskTiles + t;
+    if (tile >= n_tiles) break;  // uniform
+    const int64_t m = m0 + 64 * t;
+    const bool kept = (pw[t] >> ((m / 4) & 31)) & 1u;
+    if (!kept && m < A.n_nodes) srow[m] = kNegInf;
+    const float s = kept ? v[t] : kNegInf;
+    publish_range(A.keyrange + (row * A.kr_slots + tile) * 4, s > kNegInf, order_key(s));
   }
 }
 
@@ -2095,66 +2187,70 @@ hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dty
   if (sa.n_nodes > 0) {
     prof.begin(ZHA_K_SCORE, level);
     // weights-form levels: C keys per node at level 1 (C in {4, 8, 16}), or
-    // 16 keys per node at level 2 under chunk 4 (children per parent 4)
+    // 16-key nodes of 4 chunks at level 2 holding child shares (MODE 1; MODE
+    // 2 also writes the level-1 scores), or level 1 after such a fused pass
     const bool w2lvl = sa.leaf_weights && sa.wkeys == 16 && sa.C == 4;
     const int64_t wtiles = sa.leaf_weights ? (sa.n_nodes * sa.wkeys + 255) / 256 : 0;
-    if (sa.leaf_weights && sa.QC > 16 && wtiles * n_caches >= kMqMinTiles) {
+    if (sa.fuse1) {
+      hipLaunchKernelGGL(k_score_mask1, dim3((unsigned)((wtiles + kMaskTiles - 1) / kMaskTiles), (unsigned)n_caches),
+                         dim3(256), 0, s, sa, wtiles);
+    } else if (sa.leaf_weights && sa.QC > 16 && wtiles * n_caches >= kMqMinTiles) {
       dim3 grid((unsigned)wtiles, (unsigned)n_caches, (unsigned)((sa.QC + 16 * kMqBlocks - 1) / (16 * kMqBlocks)));
-#define ZHA_LWM(DD, CC, CPP)                                                                    \
+#define ZHA_LWM(DD, CC, MM)                                                                     \
   do {                                                                                          \
     if (sa.R == 16)                                                                             \
-      hipLaunchKernelGGL((k_score_leafw_mq<DD, CC, 16, CPP>), grid, dim3(256), 0, s, sa);       \
+      hipLaunchKernelGGL((k_score_leafw_mq<DD, CC, 16, MM>), grid, dim3(256), 0, s, sa);        \
     else if (sa.R == 1)                                                                         \
-      hipLaunchKernelGGL((k_score_leafw_mq<DD, CC, 1, CPP>), grid, dim3(256), 0, s, sa);        \
+      hipLaunchKernelGGL((k_score_leafw_mq<DD, CC, 1, MM>), grid, dim3(256), 0, s, sa);         \
     else                                                                                        \
-      hipLaunchKernelGGL((k_score_leafw_mq<DD, CC, 0, CPP>), grid, dim3(256), 0, s, sa);        \
+      hipLaunchKernelGGL((k_score_leafw_mq<DD, CC, 0, MM>), grid, dim3(256), 0, s, sa);         \
   } while (0)
       if (sa.D == 128) {
-        if (w2lvl) ZHA_LWM(128, 16, 4);
-        else if (sa.wkeys == 4) ZHA_LWM(128, 4, 4);
-        else if (sa.wkeys == 8) ZHA_LWM(128, 8, 8);
-        else ZHA_LWM(128, 16, 16);
+        if (w2lvl) ZHA_LWM(128, 16, 1);
+        else if (sa.wkeys == 4) ZHA_LWM(128, 4, 0);
+        else if (sa.wkeys == 8) ZHA_LWM(128, 8, 0);
+        else ZHA_LWM(128, 16, 0);
       } else {
-        if (w2lvl) ZHA_LWM(64, 16, 4);
-        else if (sa.wkeys == 4) ZHA_LWM(64, 4, 4);
-        else if (sa.wkeys == 8) ZHA_LWM(64, 8, 8);
-        else ZHA_LWM(64, 16, 16);
+        if (w2lvl) ZHA_LWM(64, 16, 1);
+        else if (sa.wkeys == 4) ZHA_LWM(64, 4, 0);
+        else if (sa.wkeys == 8) ZHA_LWM(64, 8, 0);
+        else ZHA_LWM(64, 16, 0);
       }
 #undef ZHA_LWM
     } else if (sa.leaf_weights) {
       dim3 grid((unsigned)wtiles, (unsigned)n_caches, (unsigned)((sa.QC + 15) / 16));
-#define ZHA_LW_Q(DD, CC, QQ, CPP, FL)                                                           \
+#define ZHA_LW_Q(DD, CC, QQ, MM)                                                                \
   do {                                                                                          \
     if (sa.R == 16)                                                                             \
-      hipLaunchKernelGGL((k_score_leafw<DD, CC, 16, QQ, CPP, FL>), grid, dim3(256), 0, s, sa);  \
+      hipLaunchKernelGGL((k_score_leafw<DD, CC, 16, QQ, MM>), grid, dim3(256), 0, s, sa);       \
     else if (sa.R == 1)                                                                         \
-      hipLaunchKernelGGL((k_score_leafw<DD, CC, 1, QQ, CPP, FL>), grid, dim3(256), 0, s, sa);   \
+      hipLaunchKernelGGL((k_score_leafw<DD, CC, 1, QQ, MM>), grid, dim3(256), 0, s, sa);        \
     else                                                                                        \
-      hipLaunchKernelGGL((k_score_leafw<DD, CC, 0, QQ, CPP, FL>), grid, dim3(256), 0, s, sa);   \
+      hipLaunchKernelGGL((k_score_leafw<DD, CC, 0, QQ, MM>), grid, dim3(256), 0, s, sa);        \
   } while (0)
-#define ZHA_LW(DD, CC, CPP)                 \
-  do {                                      \
-    if (sa.QC <= 4)                         \
-      ZHA_LW_Q(DD, CC, true, CPP, false);   \
-    else                                    \
-      ZHA_LW_Q(DD, CC, false, CPP, false);  \
+#define ZHA_LW(DD, CC, MM)               \
+  do {                                   \
+    if (sa.QC <= 4)                      \
+      ZHA_LW_Q(DD, CC, true, MM);        \
+    else                                 \
+      ZHA_LW_Q(DD, CC, false, MM);       \
   } while (0)
-      if (sa.from_logits) {
-        // level 1 from the logits of the level-2 pass (chunk 4, <= 4 queries per cache)
+      if (w2lvl && sa.score1) {
+        // level 2 with the level-1 scores (<= 4 queries per cache)
         if (sa.D == 128)
-          ZHA_LW_Q(128, 4, true, 4, true);
+          ZHA_LW_Q(128, 16, true, 2);
         else
-          ZHA_LW_Q(64, 4, true, 4, true);
+          ZHA_LW_Q(64, 16, true, 2);
       } else if (sa.D == 128) {
-        if (w2lvl) ZHA_LW(128, 16, 4);
-        else if (sa.wkeys == 4) ZHA_LW(128, 4, 4);
-        else if (sa.wkeys == 8) ZHA_LW(128, 8, 8);
-        else ZHA_LW(128, 16, 16);
+        if (w2lvl) ZHA_LW(128, 16, 1);
+        else if (sa.wkeys == 4) ZHA_LW(128, 4, 0);
+        else if (sa.wkeys == 8) ZHA_LW(128, 8, 0);
+        else ZHA_LW(128, 16, 0);
       } else {
-        if (w2lvl) ZHA_LW(64, 16, 4);
-        else if (sa.wkeys == 4) ZHA_LW(64, 4, 4);
-        else if (sa.wkeys == 8) ZHA_LW(64, 8, 8);
-        else ZHA_LW(64, 16, 16);
+        if (w2lvl) ZHA_LW(64, 16, 1);
+        else if (sa.wkeys == 4) ZHA_LW(64, 4, 0);
+        else if (sa.wkeys == 8) ZHA_LW(64, 8, 0);
+        else ZHA_LW(64, 16, 0);
       }
 #undef ZHA_LW
 #undef ZHA_LW_Q

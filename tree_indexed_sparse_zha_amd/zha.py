@@ -259,7 +259,8 @@ class ZhaConfig:
         return self.leaf_form in ("weights", "weights2")
 
     def weight_keys(self, level: int) -> int:
-        """Keys per node of ``level`` when it holds softmax weights, else 0."""
+        """Keys per node of ``level`` when routing scores it from its keys
+        (level 1 of the weights forms, level 2 of "weights2"), else 0."""
         if level == 1 and self.weights:
             return self.chunk
         if level == 2 and self.leaf_form == "weights2":
@@ -511,8 +512,9 @@ def read_level(cfg: ZhaConfig, tree: torch.Tensor, level: int, n_nodes: Optional
 
     Returns g [caches, n, R, d] (storage dtype; fp8 levels: the decoded
     values times their row scale, fp32, plus "scale" [caches, n, R]), L and c
-    [caches, n, R] fp32; a level that holds weights (level 1 in the weights
-    forms, level 2 in "weights2") returns w [caches, n, R, keys] instead of g.
+    [caches, n, R] fp32; level 1 in the weights forms returns w [caches, n,
+    R, C] instead of g, and level 2 in "weights2" rho [caches, n, R, C], the
+    children's mass shares exp(L(child) - L).
     """
     tl = tree_layout(cfg)
     i = level - 1
@@ -524,6 +526,10 @@ def read_level(cfg: ZhaConfig, tree: torch.Tensor, level: int, n_nodes: Optional
     Lb, cb = int(tl.L_offset[i]), int(tl.c_offset[i])
     L = tree[Lb : Lb + caches * cap * R * 4].view(torch.float32).view(caches, cap, R)[:, :n]
     c = tree[cb : cb + caches * cap * R * 4].view(torch.float32).view(caches, cap, R)[:, :n]
+    if level == 2 and cfg.leaf_form == "weights2":
+        C = cfg.chunk  # rho [R][C]: each child's share exp(L(child) - L) of the node's mass
+        rho = tree[gb : gb + caches * cap * R * C * 4].view(torch.float32).view(caches, cap, R, C)[:, :n]
+        return {"rho": rho, "L": L, "c": c}
     wk = cfg.weight_keys(level)
     if wk:
         w = tree[gb : gb + caches * cap * R * wk * 4].view(torch.float32).view(caches, cap, R, wk)[:, :n]
