@@ -336,8 +336,9 @@ def main():
     route_bytes = sum(v["alg_bytes"] for v in per_level.values())
     g8 = cfg.g_dtype == "fp8"
     mean_node = cfg.n_ref * (cfg.head_dim * (1 if g8 else cfg.esize) + (12 if g8 else 8))  # g, L, c (+ scales)
+    # node bytes: weights [R][C] or child shares [R][C] (4RC) + L, c (8R); else the mean-key node
     tree_bytes_per_token = sum(
-        (cfg.n_ref * (4 * cfg.weight_keys(l) + 8) if cfg.weight_keys(l) else mean_node) / (cfg.chunk**l)
+        (cfg.n_ref * (4 * cfg.chunk + 8) if cfg.weight_keys(l) else mean_node) / (cfg.chunk**l)
         for l in range(1, cfg.levels + 1)
     )
     append_bytes = cfg.n_caches * A * (cfg.head_dim * cfg.esize + tree_bytes_per_token)

@@ -830,17 +830,25 @@ __global__ __launch_bounds__(256) void k_score_mask1(ScoreArgs A, int64_t n_tile
   const int64_t row = (int64_t)cache * A.QC + qi;
   const uint32_t* prow = A.sel_parent + row * A.parent_words;
   float* srow = A.score + row * A.score_stride;
-  // every load first (the row entry and the parent word of each of the
-  // lane's kMaskTiles chunks), then the masking and the key ranges
+  // every load first: the parent words of the lane's kMaskTiles chunks,
+  // then the row entries of the kept parents' children (buffer loads; the
+  // others are masked and move nothing), then the masking and key ranges
   const int64_t m0 = (int64_t)blockIdx.x * kMaskTiles * 64 + lane;
-  float v[kMaskTiles];
   uint32_t pw[kMaskTiles];
 #pragma unroll
   for (int t = 0; t < kMaskTiles; ++t) {
     const int64_t m = m0 + 64 * t;
-    const bool in = m < A.n_nodes;
-    v[t] = in ? srow[m] : kNegInf;
-    pw[t] = in ? prow[(m / 4) >> 5] : 0u;
+    pw[t] = m < A.n_nodes ? prow[(m / 4) >> 5] : 0u;
+  }
+  const int64_t mb = (int64_t)blockIdx.x * kMaskTiles * 64;  // first chunk of the workgroup
+  const rsrc_t sr = make_rsrc(srow + mb, (uint32_t)(min((int64_t)kMaskTiles * 64, A.n_nodes - mb) * 4));
+  float v[kMaskTiles];
+#pragma unroll
+  for (int t = 0; t < kMaskTiles; ++t) {
+    const int64_t m = m0 + 64 * t;
+    const bool kept = (pw[t] >> ((m / 4) & 31)) & 1u;
+    const float x = bld4f<0>(sr, kept ? (uint32_t)((lane + 64 * t) * 4) : kOffNone);
+    v[t] = kept ? x : kNegInf;
   }
 #pragma unroll
   for (int t = 0; t < kMaskTiles; ++t) {
@@ -849,8 +857,7 @@ __global__ __launch_bounds__(256) void k_score_mask1(ScoreArgs A, int64_t n_tile
     const int64_t m = m0 + 64 * t;
     const bool kept = (pw[t] >> ((m / 4) & 31)) & 1u;
     if (!kept && m < A.n_nodes) srow[m] = kNegInf;
-    const float s = kept ? v[t] : kNegInf;
-    publish_range(A.keyrange + (row * A.kr_slots + tile) * 4, s > kNegInf, order_key(s));
+    publish_range(A.keyrange + (row * A.kr_slots + tile) * 4, v[t] > kNegInf, order_key(v[t]));
   }
 }
 
