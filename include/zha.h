@@ -69,17 +69,19 @@ enum zha_dtype { ZHA_F32 = 0, ZHA_BF16 = 1 };
  *     R*(4C+8) bytes instead of R*(d*esize+8), and routing reads the chunk's
  *     C*d key elements instead of R*d mean-key elements.  Supported with bf16
  *     and chunk in {4, 8, 16}.  Levels >= 2 are the same in both forms.
- *   ZHA_LEAF_WEIGHTS2: level 1 as in ZHA_LEAF_WEIGHTS, and level 2 too
- *     stores the weights of its own C*C keys ([R][C*C] fp32, with L_j and
- *     c_j = L_j - sum_i w_ji z_ji over those keys; a trailing level-2 node
- *     with fewer chunks holds zeros for the keys it lacks).  Routing scores
- *     level 2 from the raw keys and, when the caller passes the logits
- *     buffer and a cache has at most 4 queries, scores level 1 from the
- *     logits level 2 computed, so the keys of a candidate are read once.
- *     A level-2 node occupies R*(4C*C+8) bytes instead of R*(2d+8).
- *     Supported with bf16, chunk 4, 3..8 levels and g_dtype ZHA_G_KV; not
- *     with the prefill calls (zha_build_spine, zha_route_prefill).  Levels
- *     >= 3 are the same in every form.
+ *   ZHA_LEAF_WEIGHTS2: level 1 as in ZHA_LEAF_WEIGHTS; a level-2 node
+ *     stores its C children's mass shares rho_cj = exp(L_j(child c) - L_j)
+ *     ([R][C] fp32; 0 for the children a trailing node lacks), L_j and
+ *     c_j = L_j - sum_i w_ji z_ji over its C*C keys, where the node's weight
+ *     of key i in child c is rho_cj times the child's own w_ji.  Routing
+ *     scores level 2 from its raw keys (the same plane with g unrounded);
+ *     with at most 4 queries per cache and routing from level 2 or above,
+ *     that pass also forms the level-1 scores of its children (the keys of
+ *     a candidate are read once) and keeps the logits when the caller
+ *     passes the buffer.  A level-2 node occupies R*(4C+8) bytes instead of
+ *     R*(2d+8).  Supported with bf16, chunk 4, 3..8 levels and g_dtype
+ *     ZHA_G_KV; not with the prefill calls (zha_build_spine,
+ *     zha_route_prefill).  Levels >= 3 are the same in every form.
  */
 enum zha_leaf_form { ZHA_LEAF_MEAN = 0, ZHA_LEAF_WEIGHTS = 1, ZHA_LEAF_WEIGHTS2 = 2 };
 
@@ -132,7 +134,7 @@ typedef struct zha_config {
  * node_cap[0] = floor(capacity / C).  Per level, three blocks:
  *   g: [caches][node_cap][g_bytes / element size]: for level 1 in the
  *      weights forms, w as [R][C] fp32; for level 2 in ZHA_LEAF_WEIGHTS2,
- *      w as [R][C*C] fp32; otherwise R x d mean keys in kv_dtype.
+ *      rho as [R][C] fp32; otherwise R x d mean keys in kv_dtype.
  *      Within one node the R x d mean
  *      keys are stored d-chunk-interleaved so that one 64-lane load yields a
  *      16 x 32 MFMA operand tile: element (j, e) with 16-byte piece
@@ -176,8 +178,8 @@ typedef struct zha_tree_layout {
  *          (in records).
  * Optional logits (leaf-weights forms only): level-1 scoring computes
  * q . k_i / sqrt(d) for every key of every candidate chunk (in
- * ZHA_LEAF_WEIGHTS2 with at most 4 queries per cache, level-2 scoring does,
- * for every key of every candidate level-2 node); zha_route can
+ * ZHA_LEAF_WEIGHTS2 level-2 scoring does, for every key of every candidate
+ * level-2 node, when it also forms the level-1 scores); zha_route can
  * keep them in a [caches][ceil(QC/16)][capacity/4][4][QW] fp32 buffer (4-key
  * quads, 4 keys, QW = min(QC rounded up to 4, 16) queries; QC = G*T queries
  * per cache; rows beyond QC unused) so that zha_attend reads 16 bytes per key
