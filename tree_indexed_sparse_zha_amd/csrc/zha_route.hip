@@ -397,14 +397,16 @@ __global__ __launch_bounds__(256) void k_score_smallr(ScoreArgs A) {
 // MODE 1, and the chunk sums also give every chunk's level-1 plane
 // c_j(chunk) + sum_i w_ji s_i, written to the level-1 score rows, so level 1
 // needs neither its keys nor its logits again.
-template <int D, int C, int RT, bool Q4, int MODE = 0>
+template <int D, int C, int RT, bool Q4, int MODE = 0, int KT = 256>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_score_leafw(ScoreArgs A) {
   static_assert(MODE == 0 || C == 16, "child shares: 16-key nodes of 4 chunks");
   static_assert(MODE < 2 || Q4, "fused level-1 scores: at most 4 queries per cache");
+  static_assert(KT == 256 || (KT == 64 && MODE == 0), "tiles of 256 keys, or of 64 (one wave)");
+  constexpr int NT = KT;       // threads: one wave per 64 keys
+  constexpr int NW = KT / 64;  // waves
   constexpr int CP = MODE ? 4 : C;   // children per parent
   constexpr int GW = MODE ? 4 : C;   // floats per plane of a node's g block (w, or rho)
   constexpr int NS = D / 32;
-  constexpr int KT = 256;       // keys per tile
   constexpr int NCH = KT / C;   // chunks per tile (<= 64)
   constexpr int GPW = 4;        // groups of 16 keys per wave
   constexpr int PARTS = C / 4;  // 4-key lane parts per chunk
@@ -421,7 +423,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   __shared__ float sc[16][NCH + 1];
   __shared__ float4 wl[NCH][WROW];  // w of chunk x, plane j, 4-key part at [x][j * PARTS + part]
   __shared__ float cl[NCH][17];
-  __shared__ float4 zl[Q4 ? 4 : 1][16][4];  // Q4: [wave][quad of the wave][query] logits
+  __shared__ float4 zl[Q4 ? NW : 1][16][4];  // Q4: [wave][quad of the wave][query] logits
   __shared__ unsigned long long mbl[16];    // candidate bits per query
   __shared__ float rl[MODE ? NCH : 1][WROW];     // MODE: rho of node x, plane j, chunk part
   __shared__ float c1l[MODE == 2 ? 4 * NCH : 1][17];  // MODE 2: c of the tile's chunks
@@ -451,6 +453,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   unsigned long long anybits = mybits;
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) anybits |= __shfl_xor(anybits, o);
+  if (anybits == 0ull) {
+    // no chunk of the tile is any query's candidate (same in every wave):
+    // -inf scores and empty key ranges, nothing read
+    for (int idx = tid; idx < nq * NCH; idx += NT) {
+      const int q = idx / NCH, x = idx % NCH;
+      if (m0 + x < A.n_nodes) A.score[((int64_t)cache * A.QC + qg0 + q) * A.score_stride + m0 + x] = kNegInf;
+    }
+    for (int q = wave; q < nq; q += NW)
+      publish_range(A.keyrange + (((int64_t)cache * A.QC + qg0 + q) * A.kr_slots + blockIdx.x) * 4, false, 0u);
+    return;
+  }
 
   // All loads of the tile are issued together as buffer loads (masked rows
   // read zeros): w and c of the candidate chunks first, then the K rows of
@@ -466,7 +479,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   const int64_t n1v = MODE ? min((int64_t)KT / 4, n_keys / 4 - c0) : 0;  // its chunks (>= 1)
   const rsrc_t w1r = make_rsrc(MODE ? A.w1 + ((int64_t)cache * A.node_cap1 + c0) * R * 4 : nullptr,
                                (uint32_t)(n1v * R * 16));
-  constexpr int ITEMS = NCH * 16 / 256;
+  constexpr int ITEMS = NCH * 16 / NT;
+  static_assert(ITEMS * NT == NCH * 16, "whole (chunk, plane) items per thread");
   // w as 16-byte pieces in memory order, piece it -> (chunk x, plane j,
   // part pp): with R = 16 consecutive lanes read consecutive bytes (MODE:
   // part pp of node x is chunk 4x + pp, read from its own w1 row, and rho
@@ -476,7 +490,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   float cst[ITEMS];
 #pragma unroll
   for (int r = 0; r < ITEMS * PARTS; ++r) {
-    const int it = tid + 256 * r;
+    const int it = tid + NT * r;
     const int x = it / (16 * PARTS), j = (it / PARTS) % 16, pp = it % PARTS;
     const bool ok = ((anybits >> x) & 1ull) && j < R;
     uint4 v;
@@ -490,7 +504,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   }
 #pragma unroll
   for (int r = 0; r < ITEMS; ++r) {
-    const int it = tid + 256 * r;
+    const int it = tid + NT * r;
     const int x = it / 16, j = it % 16;
     const bool ok = ((anybits >> x) & 1ull) && j < R;
     cst[r] = bld4f(cr, ok ? (uint32_t)((x * R + j) * 4) : kOffNone);
@@ -501,7 +515,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     const rsrc_t c1r = make_rsrc(A.c1 + ((int64_t)cache * A.node_cap1 + c0) * R, (uint32_t)(n1v * R * 4));
 #pragma unroll
     for (int r = 0; r < C1I; ++r) {
-      const int it = tid + 256 * r;
+      const int it = tid + NT * r;
       const int ch = it / 16, j = it % 16;
       const bool ok = ((anybits >> (ch / 4)) & 1ull) && j < R;
       c1st[r] = bld4f(c1r, ok ? (uint32_t)((ch * R + j) * 4) : kOffNone);
@@ -520,19 +534,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   }
 #pragma unroll
   for (int r = 0; r < ITEMS * PARTS; ++r) {
-    const int it = tid + 256 * r;
+    const int it = tid + NT * r;
     wl[it / (16 * PARTS)][it % (16 * PARTS)] = wst[r];  // [x][j * PARTS + pp]
     if constexpr (MODE) rl[it / (16 * PARTS)][it % (16 * PARTS)] = rst[r];
   }
 #pragma unroll
   for (int r = 0; r < ITEMS; ++r) {
-    const int it = tid + 256 * r;
+    const int it = tid + NT * r;
     cl[it / 16][it % 16] = cst[r];
   }
   if constexpr (MODE == 2) {
 #pragma unroll
     for (int r = 0; r < C1I; ++r) {
-      const int it = tid + 256 * r;
+      const int it = tid + NT * r;
       c1l[it / 16][it % 16] = c1st[r];
     }
   }
@@ -626,12 +640,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < nq * NCH; idx += 256) {
+  for (int idx = tid; idx < nq * NCH; idx += NT) {
     const int q = idx / NCH, x = idx % NCH;
     const int64_t mm = m0 + x;
     if (mm < A.n_nodes) A.score[((int64_t)cache * A.QC + qg0 + q) * A.score_stride + mm] = sc[q][x];
   }
-  for (int q = wave; q < nq; q += 4) {
+  for (int q = wave; q < nq; q += NW) {
     const float v = lane < NCH ? sc[q][lane] : kNegInf;
     const bool c = lane < NCH && m0 + lane < A.n_nodes && v > kNegInf;
     publish_range(A.keyrange + (((int64_t)cache * A.QC + qg0 + q) * A.kr_slots + blockIdx.x) * 4, c, order_key(v));
@@ -2174,9 +2188,15 @@ int64_t select_split_bytes(int64_t n_queries, int64_t max_nodes) {
   return n_queries * kSelStateBytes + n_queries * S * kSelSlotU64 * 8;
 }
 
+// Keys per tile of the weights-form score kernel launched for a level with
+// wkeys keys per node and QC queries per cache: 8-key chunks (the light
+// geometry, whose candidates come in 64-key runs) take one wave per 64 keys,
+// so that a tile no query reaches ends at once; else 256 keys.
+static int leafw_tile(int wkeys, bool mq) { return wkeys == 8 && !mq ? 64 : 256; }
+
 int64_t route_kr_slots(int dtype, bool leaf_weights, int64_t node_cap, int wkeys) {
   // one slot per score tile, plus one for the prefill spine score
-  if (leaf_weights) return (node_cap * wkeys + 255) / 256 + 1;  // k_score_leafw: 256-key tiles
+  if (leaf_weights) return (node_cap * wkeys + leafw_tile(wkeys, false) - 1) / leafw_tile(wkeys, false) + 1;
   if (dtype == 1) return (node_cap + 63) / 64 + 1;          // k_score_bf16: 64-node tiles
   return 1;                                                 // k_score_generic: atomics
 }
@@ -2191,17 +2211,21 @@ hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dty
                               int level, Prof& prof) {
   const int64_t n_queries = (int64_t)n_caches * sa.QC;
   hipStream_t s = prof.s;
+  // weights form: many queries per cache walk 16 query blocks over a tile;
+  // the tile's keys
+  const bool mq = sa.leaf_weights && sa.QC > 16 && (sa.n_nodes * sa.wkeys + 255) / 256 * n_caches >= kMqMinTiles;
+  const int kt = leafw_tile(sa.wkeys, mq);
   if (sa.n_nodes > 0) {
     prof.begin(ZHA_K_SCORE, level);
     // weights-form levels: C keys per node at level 1 (C in {4, 8, 16}), or
     // 16-key nodes of 4 chunks at level 2 holding child shares (MODE 1; MODE
     // 2 also writes the level-1 scores), or level 1 after such a fused pass
     const bool w2lvl = sa.leaf_weights && sa.wkeys == 16 && sa.C == 4;
-    const int64_t wtiles = sa.leaf_weights ? (sa.n_nodes * sa.wkeys + 255) / 256 : 0;
+    const int64_t wtiles = sa.leaf_weights ? (sa.n_nodes * sa.wkeys + kt - 1) / kt : 0;
     if (sa.fuse1) {
       hipLaunchKernelGGL(k_score_mask1, dim3((unsigned)((wtiles + kMaskTiles - 1) / kMaskTiles), (unsigned)n_caches),
                          dim3(256), 0, s, sa, wtiles);
-    } else if (sa.leaf_weights && sa.QC > 16 && wtiles * n_caches >= kMqMinTiles) {
+    } else if (mq) {
       dim3 grid((unsigned)wtiles, (unsigned)n_caches, (unsigned)((sa.QC + 16 * kMqBlocks - 1) / (16 * kMqBlocks)));
 #define ZHA_LWM(DD, CC, MM)                                                                     \
   do {                                                                                          \
@@ -2226,14 +2250,15 @@ hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dty
 #undef ZHA_LWM
     } else if (sa.leaf_weights) {
       dim3 grid((unsigned)wtiles, (unsigned)n_caches, (unsigned)((sa.QC + 15) / 16));
-#define ZHA_LW_Q(DD, CC, QQ, MM)                                                                \
-  do {                                                                                          \
-    if (sa.R == 16)                                                                             \
-      hipLaunchKernelGGL((k_score_leafw<DD, CC, 16, QQ, MM>), grid, dim3(256), 0, s, sa);       \
-    else if (sa.R == 1)                                                                         \
-      hipLaunchKernelGGL((k_score_leafw<DD, CC, 1, QQ, MM>), grid, dim3(256), 0, s, sa);        \
-    else                                                                                        \
-      hipLaunchKernelGGL((k_score_leafw<DD, CC, 0, QQ, MM>), grid, dim3(256), 0, s, sa);        \
+#define ZHA_LW_Q(DD, CC, QQ, MM)                                                                      \
+  do {                                                                                                \
+    constexpr int KTT = (CC) == 8 ? 64 : 256; /* leafw_tile */                                        \
+    if (sa.R == 16)                                                                                   \
+      hipLaunchKernelGGL((k_score_leafw<DD, CC, 16, QQ, MM, KTT>), grid, dim3(KTT), 0, s, sa);        \
+    else if (sa.R == 1)                                                                               \
+      hipLaunchKernelGGL((k_score_leafw<DD, CC, 1, QQ, MM, KTT>), grid, dim3(KTT), 0, s, sa);         \
+    else                                                                                              \
+      hipLaunchKernelGGL((k_score_leafw<DD, CC, 0, QQ, MM, KTT>), grid, dim3(KTT), 0, s, sa);         \
   } while (0)
 #define ZHA_LW(DD, CC, MM)               \
   do {                                   \
@@ -2312,7 +2337,7 @@ hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dty
   if (sa.n_nodes <= 0)
     sel.kr_used = 0;
   else if (sa.leaf_weights)
-    sel.kr_used = (sa.n_nodes * sa.wkeys + 255) / 256;
+    sel.kr_used = (sa.n_nodes * sa.wkeys + kt - 1) / kt;
   else if (dtype == 1)
     sel.kr_used = (sa.n_nodes + 63) / 64;
   else
