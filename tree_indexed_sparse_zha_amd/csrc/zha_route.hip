@@ -374,17 +374,19 @@ __global__ __launch_bounds__(256) void k_score_smallr(ScoreArgs A) {
 }
 
 // ---------------------------------------------------------------------------
-// score of level-1 nodes in the weights form (bf16, C in {4, 8, 16})
+// score of the levels scored from their keys (bf16): level 1 of the weights
+// forms (C in {4, 8, 16}), level 2 holding child shares (16-key nodes)
 //
 // s(q, chunk) = max_j [ c_j + sum_i w_ji (q . k_i) / sqrt(d) ]: the chunk's
 // raw keys go through the MFMA (A = 16 keys, B = up to 16 queries) exactly
 // as in attention; the MFMA leaves, in each lane, the logits of 4 keys for
 // one query, and the lane folds them with the weights of all R planes of
 // their chunk (staged once per tile in LDS and read as broadcasts) and takes
-// the max itself, so no lane exchange is needed when C = 4.  A tile is 256
-// keys; each wave owns 4 groups of 16 keys and skips groups none of whose
-// chunks is a candidate of any query; weights are staged only for candidate
-// chunks.
+// the max itself, so no lane exchange is needed when C = 4.  A tile is KT
+// keys (256, or 64 for 8-key chunks: one wave); each wave owns 4 groups of
+// 16 keys and skips groups none of whose chunks is a candidate of any query,
+// and a tile with no candidate at all ends after writing -inf; weights are
+// staged only for candidate chunks.
 
 // RT: R as a compile-time constant (0 = runtime).  Q4: at most 4 queries per
 // cache; the MFMA then fills only 4 of its 16 query columns, so the logits
