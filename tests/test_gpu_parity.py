@@ -135,6 +135,7 @@ CACHED_CASES = [
     ("w2-qg4-d128-C4", dict(batch=2, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=4, capacity=9000, leaf_form="weights2"), 1, 8998, 0.9),
     ("w2-qg4-d64-C4-p1", dict(batch=1, n_kv_heads=1, q_per_kv=2, head_dim=64, n_ref=3, chunk=4, levels=3, capacity=2100, leaf_form="weights2"), 1, 2051, 1.0),
     ("w2-qg8-d64-C4", dict(batch=1, n_kv_heads=2, q_per_kv=3, head_dim=64, n_ref=5, chunk=4, levels=3, capacity=6000, leaf_form="weights2"), 2, 5995, 0.8),
+    ("w2-qg4-d128-R1", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=1, chunk=4, levels=4, capacity=9000, leaf_form="weights2"), 1, 8990, 0.8),
 ]
 
 
@@ -211,6 +212,7 @@ BUILD_CASES = [
     # levels 1 and 2 as weights: a trailing level-2 node of one and of three chunks
     ("w2-d128-r16-l6", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=6, dtype="bf16", capacity=9000, leaf_form="weights2"), 8192 + 4 * 37 + 2),
     ("w2-d64-r5-l3", dict(batch=2, n_kv_heads=1, q_per_kv=2, head_dim=64, n_ref=5, chunk=4, levels=3, dtype="bf16", capacity=3000, leaf_form="weights2"), 2048 + 4 * 39 + 3),
+    ("w2-d128-r1-l5", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=1, chunk=4, levels=5, dtype="bf16", capacity=5000, leaf_form="weights2"), 4096 + 16 * 7 + 4 * 3 + 1),
 ]
 APPEND_CASES = [c for c in BUILD_CASES if c[0] != "c1-f32"]
 
