@@ -86,11 +86,12 @@ def selection_bytes(cfg: zha.ZhaConfig, buf, n_tokens: int, T: int, logits: bool
     row scales), or at level 1 in the weights forms x (C*d*2 bytes of keys +
     4RC of weights + 4R of c, plus 4*min(QC,16) bytes of logits written per
     key when they are kept); level 2 in "weights2" x (C*C*d*2 bytes of keys +
-    C*4RC of its chunks' weights + 4RC of child shares + 4R of c), and with
-    at most 4 queries per cache also its chunks' c (C*4R), the logits of its
-    keys (C*C*4*QC) and its chunks' level-1 scores (C*4*QC) written, while
-    level 1 then reads or writes each score row entry once (4*QC bytes per
-    chunk of the level);
+    C*4RC of its chunks' weights + 4RC of child shares + 4R of c), or with
+    at most 4 queries per cache x (C*C*d*2 bytes of keys + 4R of its L +
+    C*4R of its chunks' L read, the weights, shares and offsets recomputed;
+    its chunks' level-1 scores (C*4*QC) and the logits of its keys
+    (C*C*4*QC) written), while level 1 then reads or writes each score row
+    entry once (4*QC bytes per chunk of the level);
     attend, per cache: |union over the cache's queries of the attended keys|
     x (d*2 bytes of V + d*2 bytes of K, or 4*min(QC,16) bytes of cached
     logits).  Also returns per-query selected share and per-level counts.
@@ -107,10 +108,11 @@ def selection_bytes(cfg: zha.ZhaConfig, buf, n_tokens: int, T: int, logits: bool
     level_bytes = {lv: node_bytes for lv in range(1, Lv + 1)}
     if cfg.weights:  # level 1 from its keys and weights
         level_bytes[1] = C * d * cfg.esize + R * C * 4 + 4 * R + (C * QW * 4 if logits else 0)
-    if cfg.weight_keys(2):  # level 2 from its keys, its chunks' weights and its child shares
-        level_bytes[2] = C * C * d * cfg.esize + C * R * C * 4 + R * C * 4 + 4 * R
-        if fused:
-            level_bytes[2] += C * 4 * R + C * 4 * QC + (C * C * QW * 4 if logits else 0)
+    if cfg.weight_keys(2):
+        if fused:  # its keys and the L of it and of its chunks; writes the level-1 scores (and logits)
+            level_bytes[2] = C * C * d * cfg.esize + C * 4 * R + 4 * R + C * 4 * QC + (C * C * QW * 4 if logits else 0)
+        else:  # its keys, its chunks' weights, its child shares and its c
+            level_bytes[2] = C * C * d * cfg.esize + C * R * C * 4 + R * C * 4 + 4 * R
     per_level = {}
     kept_prev = None
     for lv in range(top, 0, -1):

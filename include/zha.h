@@ -163,6 +163,10 @@ typedef struct zha_tree_layout {
   int64_t scratch_offset; /* fp32 children of up to 2 top nodes per cache, used by
                              zha_append to split its spans over more workgroups;
                              -1 when the geometry does not split */
+  int64_t ref_offset;     /* ZHA_LEAF_WEIGHTS2: the reference queries the tree was
+                             built with, [H][R][d] fp32 (zha_build and zha_append
+                             store them; routing recomputes the level-1 and
+                             level-2 weights from them and the stored L); else -1 */
 } zha_tree_layout;
 
 /*

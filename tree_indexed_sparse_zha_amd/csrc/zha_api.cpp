@@ -137,6 +137,11 @@ void fill_tree_layout(const zha_config* c, zha_tree_layout* out) {
     out->scratch_offset = off;
     off = align256(off + caches * 2 * c->chunk * (int64_t)c->n_ref * (c->head_dim + 2) * 4);
   }
+  out->ref_offset = -1;
+  if (weight_keys(c, 1)) {
+    out->ref_offset = off;
+    off = align256(off + (int64_t)c->n_kv_heads * c->n_ref * c->head_dim * 4);
+  }
   out->total_bytes = off > 0 ? off : 256;
 }
 
@@ -247,6 +252,13 @@ int do_build(const zha_config* cfg, const void* K, const int64_t* ks, int64_t n_
   if (a.n_spans <= 0) return ZHA_OK;
   if (a.n_spans > 0x7fffffffll) return fail(ZHA_ERR_UNSUPPORTED, "too many spans");
   zha::Prof pr{prof, static_cast<hipStream_t>(stream)};
+  if (tl.ref_offset >= 0) {
+    // the reference queries travel with the tree (routing recomputes weights from them)
+    hipError_t e = hipMemcpyAsync(static_cast<char*>(tree) + tl.ref_offset, ref,
+                                  (size_t)cfg->n_kv_heads * cfg->n_ref * cfg->head_dim * 4, hipMemcpyDeviceToDevice,
+                                  static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "reference copy");
+  }
   a.top_level = cfg->levels;
   a.mf = build_mf(cfg);
   // on the matrix-core path the split's sub-span pass must itself reach the
@@ -511,6 +523,9 @@ static int do_route(const zha_config* cfg, const void* tree, int64_t n_tokens, c
       sa.nquads = tl.node_cap[0] * cfg->chunk / 4;
       sa.QW = logits_row(sa.QC);
       if (l == 1) {  // level 2 holding child shares: the level-1 rows it reads (and fills)
+        sa.L = reinterpret_cast<const float*>(static_cast<const char*>(tree) + tl.L_offset[1]);
+        sa.L1 = reinterpret_cast<const float*>(static_cast<const char*>(tree) + tl.L_offset[0]);
+        sa.ref = reinterpret_cast<const float*>(static_cast<const char*>(tree) + tl.ref_offset);
         sa.w1 = reinterpret_cast<const float*>(static_cast<const char*>(tree) + tl.g_offset[0]);
         sa.c1 = reinterpret_cast<const float*>(static_cast<const char*>(tree) + tl.c_offset[0]);
         sa.node_cap1 = tl.node_cap[0];

@@ -110,6 +110,9 @@ struct ScoreArgs {
   const float* w1;
   const float* c1;             // level-1 c (fused level-1 scores)
   int64_t node_cap1;           // level-1 nodes per cache
+  const float* L;              // this level's L, and level 1's (fused level 2: the weights,
+  const float* L1;             // shares and offsets are recomputed from L and the logits r . k)
+  const float* ref;            // the tree's reference queries [H][R][D] fp32 (fused level 2)
   float* score1;               // fused: level-1 score rows the level-2 pass writes, or nullptr
   int64_t score1_stride;
   int fuse1;                   // level 1 after a fused level-2 pass: mask the rows, publish key ranges

@@ -445,6 +445,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     }
   }
   const int b = cache / A.H, h = cache % A.H;
+  // MODE 2: the tree's reference queries in bf16 (exact: they hold bf16
+  // values) in LDS, read per group as a second B operand (column = plane
+  // j = qn), so that the weights come from z_ji = r_j . k_i / sqrt(d) and
+  // the stored L instead of memory
+  constexpr int RPC = D / 8;  // 16-byte bf16 pieces of a reference row
+  __shared__ uint4 refs[MODE == 2 ? 16 : 1][RPC + 1];
+  if constexpr (MODE == 2) {
+    if (tid < 16 * RPC) {
+      const int j = tid / RPC, pc = tid % RPC;
+      float rr[8], dummy[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rr[e] = j < R ? A.ref[((int64_t)h * R + j) * D + pc * 8 + e] : 0.f;
+      refs[j][pc] = pack(rr, dummy, bf16_t());
+    }
+  }
   const bf16_t* Kc = reinterpret_cast<const bf16_t*>(A.K) + (int64_t)b * A.ksb + (int64_t)h * A.ksh;
   const float* wcache = reinterpret_cast<const float*>(A.g) + (int64_t)cache * A.node_cap * R * GW;
   const float* ccache = A.c + (int64_t)cache * A.node_cap * R;
@@ -478,7 +493,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   const rsrc_t kr = make_rsrc(Kc + k0 * A.kst, (uint32_t)((rows - 1) * A.kst * 2 + D * 2));
   // MODE: the level-1 rows of the tile's chunks (w1, and c1 in MODE 2)
   const int64_t c0 = m0 * 4;                                    // first chunk of the tile
-  const int64_t n1v = MODE ? min((int64_t)KT / 4, n_keys / 4 - c0) : 0;  // its chunks (>= 1)
+  const int64_t n1 = n_keys / 4;                                // chunks of level 1
+  const int64_t n1v = MODE ? min((int64_t)KT / 4, n1 - c0) : 0;  // the tile's (>= 1)
   const rsrc_t w1r = make_rsrc(MODE ? A.w1 + ((int64_t)cache * A.node_cap1 + c0) * R * 4 : nullptr,
                                (uint32_t)(n1v * R * 16));
   constexpr int ITEMS = NCH * 16 / NT;
@@ -490,6 +506,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   float4 wst[ITEMS * PARTS];
   float rst[MODE ? ITEMS * PARTS : 1];
   float cst[ITEMS];
+  if constexpr (MODE != 2) {
 #pragma unroll
   for (int r = 0; r < ITEMS * PARTS; ++r) {
     const int it = tid + NT * r;
@@ -511,16 +528,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     const bool ok = ((anybits >> x) & 1ull) && j < R;
     cst[r] = bld4f(cr, ok ? (uint32_t)((x * R + j) * 4) : kOffNone);
   }
-  constexpr int C1I = MODE == 2 ? 4 * NCH * 16 / 256 : 1;  // c1 items per thread
-  float c1st[C1I];
+  }
+  // MODE 2: L of each of the lane's 4 nodes and of chunk kg of each (plane qn)
+  float L1v[MODE == 2 ? GPW : 1], L2v[MODE == 2 ? GPW : 1];
   if constexpr (MODE == 2) {
-    const rsrc_t c1r = make_rsrc(A.c1 + ((int64_t)cache * A.node_cap1 + c0) * R, (uint32_t)(n1v * R * 4));
+    const rsrc_t l1r = make_rsrc(A.L1 + ((int64_t)cache * A.node_cap1 + c0) * R, (uint32_t)(n1v * R * 4));
+    const rsrc_t l2r = make_rsrc(A.L + ((int64_t)cache * A.node_cap + m0) * R, (uint32_t)(n_valid * R * 4));
 #pragma unroll
-    for (int r = 0; r < C1I; ++r) {
-      const int it = tid + NT * r;
-      const int ch = it / 16, j = it % 16;
-      const bool ok = ((anybits >> (ch / 4)) & 1ull) && j < R;
-      c1st[r] = bld4f(c1r, ok ? (uint32_t)((ch * R + j) * 4) : kOffNone);
+    for (int gi = 0; gi < GPW; ++gi) {
+      const int g = wave * GPW + gi;
+      const bool ok = ((anybits >> g) & 1ull) && qn < R;
+      L1v[gi] = bld4f<0>(l1r, ok ? (uint32_t)(((4 * g + kg) * R + qn) * 4) : kOffNone);
+      L2v[gi] = bld4f<0>(l2r, ok ? (uint32_t)((g * R + qn) * 4) : kOffNone);
     }
   }
   uint4 kf[GPW][NS];
@@ -534,22 +553,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 #pragma unroll
     for (int s = 0; s < NS; ++s) kf[gi][s] = bld16<0>(kr, ko + (4 * s + kg) * 16);
   }
+  if constexpr (MODE != 2) {
 #pragma unroll
-  for (int r = 0; r < ITEMS * PARTS; ++r) {
-    const int it = tid + NT * r;
-    wl[it / (16 * PARTS)][it % (16 * PARTS)] = wst[r];  // [x][j * PARTS + pp]
-    if constexpr (MODE) rl[it / (16 * PARTS)][it % (16 * PARTS)] = rst[r];
-  }
-#pragma unroll
-  for (int r = 0; r < ITEMS; ++r) {
-    const int it = tid + NT * r;
-    cl[it / 16][it % 16] = cst[r];
-  }
-  if constexpr (MODE == 2) {
-#pragma unroll
-    for (int r = 0; r < C1I; ++r) {
+    for (int r = 0; r < ITEMS * PARTS; ++r) {
       const int it = tid + NT * r;
-      c1l[it / 16][it % 16] = c1st[r];
+      wl[it / (16 * PARTS)][it % (16 * PARTS)] = wst[r];  // [x][j * PARTS + pp]
+      if constexpr (MODE) rl[it / (16 * PARTS)][it % (16 * PARTS)] = rst[r];
+    }
+#pragma unroll
+    for (int r = 0; r < ITEMS; ++r) {
+      const int it = tid + NT * r;
+      cl[it / 16][it % 16] = cst[r];
     }
   }
   if (tid < 16) mbl[tid] = mybits;  // lanes 0..15: kg 0, query qn = tid
@@ -579,6 +593,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       float* lp = A.logits + (((int64_t)cache * gridDim.z + blockIdx.z) * A.nquads + quad) * 4 * A.QW + qn;
 #pragma unroll
       for (int i = 0; i < 4; ++i) st4_nt(lp + i * A.QW, zz[i]);
+    }
+    if constexpr (MODE == 2) {
+      // lane (plane j = qn, chunk kg of node g): z of the chunk's 4 keys, its
+      // weights w = exp(z - L(chunk)), offset c = L(chunk) - sum w z, its share
+      // rho = exp(L(chunk) - L(node)); the node's offset is L(node) - sum over
+      // its chunks of rho (L(chunk) - c(chunk))
+      f32x4 zr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        zr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[gi][s]), as_bf16x8(refs[qn][4 * s + kg]), zr, 0, 0, 0);
+      const bool ok = qn < R && c0 + 4 * g + kg < n1;
+      float w[4], wz = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float zi = zr[i] * A.inv_sqrt_d;
+        w[i] = ok ? __expf(zi - L1v[gi]) : 0.f;
+        wz = fmaf(w[i], zi, wz);
+      }
+      const float rho = ok ? __expf(L1v[gi] - L2v[gi]) : 0.f;
+      float t = rho * wz;
+      t += __shfl_xor(t, 16);
+      t += __shfl_xor(t, 32);
+      if (qn < R) {
+        wl[g][qn * PARTS + kg] = make_float4(w[0], w[1], w[2], w[3]);
+        rl[g][qn * PARTS + kg] = rho;
+        c1l[4 * g + kg][qn] = L1v[gi] - wz;
+        if (kg == 0) cl[g][qn] = L2v[gi] - t;
+      }
     }
     if constexpr (Q4) {
       if (qn < 4) zl[wave][gi * 4 + kg][qn] = make_float4(zz[0], zz[1], zz[2], zz[3]);

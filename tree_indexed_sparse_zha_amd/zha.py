@@ -68,6 +68,7 @@ class TreeLayout(ct.Structure):
         ("total_bytes", ct.c_int64),
         ("s_offset", ct.c_int64 * MAX_LEVELS),
         ("scratch_offset", ct.c_int64),
+        ("ref_offset", ct.c_int64),
     ]
 
 
