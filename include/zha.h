@@ -78,7 +78,10 @@ enum zha_dtype { ZHA_F32 = 0, ZHA_BF16 = 1 };
  *     with at most 4 queries per cache and routing from level 2 or above,
  *     that pass also forms the level-1 scores of its children (the keys of
  *     a candidate are read once) and keeps the logits when the caller
- *     passes the buffer.  A level-2 node occupies R*(4C+8) bytes instead of
+ *     passes the buffer; that pass reads only the keys and the L of the
+ *     node and of its children, and recomputes the weights, shares and c
+ *     from the reference queries the tree keeps (ref_offset) and the keys,
+ *     to fp32 rounding of the stored ones.  A level-2 node occupies R*(4C+8) bytes instead of
  *     R*(2d+8).  Supported with bf16, chunk 4, 3..8 levels and g_dtype
  *     ZHA_G_KV; not with the prefill calls (zha_build_spine,
  *     zha_route_prefill).  Levels >= 3 are the same in every form.
