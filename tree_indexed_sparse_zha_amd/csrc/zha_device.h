@@ -96,6 +96,15 @@ typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{a, b}, bf16x2v));
 }
+// Sum of v over the lanes l, l + 4, l + 8 and l + 12 of each 16-lane row (the
+// four lanes whose indexes agree in bits 0-1 and differ in bits 2-3), in
+// every lane: two DPP row rotations (by 4, then by 8) feed the adds, so no
+// LDS permute is involved.
+__device__ __forceinline__ float row_sum_stride4(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xf, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
+  return v;
+}
 // The rounded values of a bf16_pair word as fp32.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

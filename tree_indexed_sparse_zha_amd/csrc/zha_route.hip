@@ -421,7 +421,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   const int R = A.R;
   const int qn = lane & 15, kg = lane >> 4;
   const int64_t n_keys = A.n_keys;  // keys of complete chunks
-  constexpr int WROW = 16 * PARTS + 1;  // padded: chunks start on different banks
+  // padded: the fold's lanes (chunk cx, part) read WROW cx + part, distinct
+  // modulo 16 float4s (64 banks), and rl's floats 4 cx + part
+  constexpr int WROW = 17 * PARTS;
   __shared__ float sc[16][NCH + 1];
   __shared__ float4 wl[NCH][WROW];  // w of chunk x, plane j, 4-key part at [x][j * PARTS + part]
   __shared__ float cl[NCH][17];
@@ -449,16 +451,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   // values) in LDS, read per group as a second B operand (column = plane
   // j = qn), so that the weights come from z_ji = r_j . k_i / sqrt(d) and
   // the stored L instead of memory
+  // (loaded here, stored to LDS once the tile's key loads are issued)
   constexpr int RPC = D / 8;  // 16-byte bf16 pieces of a reference row
   __shared__ uint4 refs[MODE == 2 ? 16 : 1][RPC + 1];
+  float4 rr4[MODE == 2 ? 2 : 1];
   if constexpr (MODE == 2) {
-    if (tid < 16 * RPC) {
-      const int j = tid / RPC, pc = tid % RPC;
-      float rr[8], dummy[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) rr[e] = j < R ? A.ref[((int64_t)h * R + j) * D + pc * 8 + e] : 0.f;
-      refs[j][pc] = pack(rr, dummy, bf16_t());
-    }
+    const int j = tid / RPC, pc = tid % RPC;
+    const bool ok = tid < 16 * RPC && j < R;
+    const float4* rp = reinterpret_cast<const float4*>(A.ref + ((int64_t)h * R + (ok ? j : 0)) * D + pc * 8);
+    rr4[0] = ok ? rp[0] : make_float4(0.f, 0.f, 0.f, 0.f);
+    rr4[1] = ok ? rp[1] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   const bf16_t* Kc = reinterpret_cast<const bf16_t*>(A.K) + (int64_t)b * A.ksb + (int64_t)h * A.ksh;
   const float* wcache = reinterpret_cast<const float*>(A.g) + (int64_t)cache * A.node_cap * R * GW;
@@ -552,6 +554,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     const uint32_t ko = live[gi] ? (uint32_t)((g * 16 + qn) * A.kst * 2) : kOffNone;
 #pragma unroll
     for (int s = 0; s < NS; ++s) kf[gi][s] = bld16<0>(kr, ko + (4 * s + kg) * 16);
+  }
+  if constexpr (MODE == 2) {
+    if (tid < 16 * RPC) {
+      const float rr[8] = {rr4[0].x, rr4[0].y, rr4[0].z, rr4[0].w, rr4[1].x, rr4[1].y, rr4[1].z, rr4[1].w};
+      float dummy[8];
+      refs[tid / RPC][tid % RPC] = pack(rr, dummy, bf16_t());
+    }
   }
   if constexpr (MODE != 2) {
 #pragma unroll
@@ -669,8 +678,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       float v = wv.x * zv.x + wv.y * zv.y + wv.z * zv.z + wv.w * zv.w;
       if constexpr (MODE == 2) best1 = fmaxf(best1, c1l[4 * x + part][jj] + v);  // chunk 4x + part's plane
       if constexpr (MODE) v *= rl[x][jj * PARTS + part];  // the chunk's share of the node
+      if constexpr (PARTS == 4) {
+        v = row_sum_stride4(v);  // lane = u + 4 part + 16 cx: the 4 parts of a row
+      } else {
 #pragma unroll
-      for (int o = 4; o < 4 * PARTS; o <<= 1) v += __shfl_xor(v, o);
+        for (int o = 4; o < 4 * PARTS; o <<= 1) v += __shfl_xor(v, o);
+      }
       best = fmaxf(best, cl[x][jj] + v);
     }
     if (part == 0 && u < nq) sc[u][x] = ((mbl[u] >> x) & 1ull) ? best : kNegInf;
