@@ -630,7 +630,7 @@ __global__ __launch_bounds__(kAttThreads) void k_attend_mfma(AttendArgs A) {
 // batch) in fp32.  No LDS traffic or barrier in the loop.  Groups of 16
 // queries go to k_attend_pv16 instead.
 template <int D, int QG>
-__global__ __launch_bounds__(kAttThreads) void k_attend_cached(AttendArgs A) {
+__global__ __launch_bounds__(kAttThreads) __attribute__((amdgpu_waves_per_eu(QG <= 4 ? 5 : 1))) void k_attend_cached(AttendArgs A) {
   constexpr int PIECES = D / 8;   // 16-byte pieces per row
   constexpr int LPQ = 4 * PIECES; // lanes per quad
   constexpr int EPS = 64 / LPQ;   // quads per wave step
