@@ -80,6 +80,13 @@ def test_tree_layout_weights2_form():
     w1 = zha.tree_layout(cfg_deep(leaf_form="weights"))
     assert [int(tl.node_cap[i]) for i in range(6)] == [int(w1.node_cap[i]) for i in range(6)]
     assert tl.total_bytes < w1.total_bytes
+    # the reference queries ([H][R][d] fp32) kept for the fused level-2 pass:
+    # a 256-byte aligned block inside the tree, past every level's arrays
+    assert tl.ref_offset > 0 and tl.ref_offset % 256 == 0
+    assert tl.ref_offset + cfg.n_kv_heads * 16 * 128 * 4 <= tl.total_bytes
+    for i in range(6):
+        assert tl.ref_offset >= tl.c_offset[i] + 8 * int(tl.node_cap[i]) * 16 * 4  # 8 caches
+    assert w1.ref_offset == -1 and zha.tree_layout(cfg_deep()).ref_offset == -1
     # the route's key-range slots of level 2 follow its 256-key tiles (16 nodes each)
     r2, r1 = zha.route_layout(cfg, 1), zha.route_layout(cfg_deep(leaf_form="weights"), 1)
     assert r2.logits_floats == r1.logits_floats
