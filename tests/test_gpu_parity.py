@@ -171,6 +171,7 @@ def test_attend_cached_logits_matches_oracle(name, kw, T, N, p, flags):
                 q = np64(Q[b, h, ql // T, ql % T])
                 PAR.check_route_teacher_forced(q, to, rn, cfg.chunk, p, PAR.gpu_kept_from_bits(bits), cfg.dtype,
                                                scores, leaf_dtype="f64", level2_dtype=l2d)
+        PAR.check_stats_all(zha, cfg, buf, N, p, range(int(buf.layout.n_queries)))
     for qi, (b, h, gq, t) in enumerate(query_list(cfg, T)):
         bits, _ = gpu_levels(cfg, buf, N, qi)
         chunks = np.nonzero(bits[1][:n_chunks])[0]
@@ -475,7 +476,7 @@ def test_route_and_attend_match_oracle(wname, n_caches_checked, leaf_form, q_per
         caches = [0, cfg.n_caches - 1][:n_caches_checked]
     rng = np.random.default_rng(5)
     out_c, lse_c = out.cpu().numpy(), lse.cpu().numpy()
-    n_same = 0
+    n_same = n_checked = 0
     for cache in caches:
         b, h = divmod(cache, cfg.n_kv_heads)
         Kn, Vn, rn = np64(batch.K[b, h, :N]), np64(batch.V[b, h, :N]), np64(batch.ref[h])
@@ -490,35 +491,35 @@ def test_route_and_attend_match_oracle(wname, n_caches_checked, leaf_form, q_per
             q = np64(batch.Q[b, h, gq, t])
             bits, scores = gpu_levels(cfg, buf, N, qi)
             kept = PAR.gpu_kept_from_bits(bits)
-            PAR.check_route_teacher_forced(q, to, rn, cfg.chunk, p, kept, gd, scores, leaf_dtype=leaf_dtype,
-                                           level2_dtype=l2d)
+            reps = PAR.check_route_teacher_forced(q, to, rn, cfg.chunk, p, kept, gd, scores, leaf_dtype=leaf_dtype,
+                                                  level2_dtype=l2d)
             # attention over the GPU's set (R21)
             idx = O.attend_set(kept[1], N, cfg.chunk, True, True)
             o, l = O.attend(q, Kn, Vn, idx)
             np.testing.assert_allclose(out_c[qi], o, rtol=0, atol=tol)
             np.testing.assert_allclose(lse_c[qi], l, rtol=0, atol=tol)
-            # end to end when the oracle's own routing reaches the same set
+            # end to end: with no ambiguous node at any level the oracle's own
+            # routing must reach exactly the GPU's set
             o2, l2, idx2, _ = O.route_and_attend(q, Kn, Vn, to, rn, cfg.chunk, p, N)
-            if np.array_equal(idx, idx2):
+            n_checked += 1
+            if all(r.n_diff == 0 for r in reps):
+                assert np.array_equal(idx, idx2), f"query {qi}: free-running oracle set differs"
                 n_same += 1
                 np.testing.assert_allclose(out_c[qi], o2, rtol=0, atol=tol)
-    assert n_same >= 1
+    PAR.check_stats_all(zha, cfg, buf, N, p, range(int(buf.layout.n_queries)))
+    # ambiguous nodes are rare: most queries match the oracle end to end
+    assert n_same >= max(1, (9 * n_checked) // 10), (n_same, n_checked)
 
 
 def test_route_stats_consistent():
+    """The selection records of every level and query against the GPU's own
+    score rows and bits: kept mass >= ceil(p M), minimality, the cut rule."""
     w = W.WORKLOADS["tiny"]
     cfg = cfg_of(w)
     batch = W.make_batch(w, device="cuda")
     N, T, p = w.n_tokens, w.queries_per_head, w.p[0]
     tree, buf, out, lse = run_path(cfg, batch.K, batch.V, batch.Q, batch.ref, N, T, p)
-    for lv in range(1, cfg.levels + 1):
-        recs = zha.stats_records(buf, lv)
-        for qi, r in enumerate(recs):
-            bits, scores = gpu_levels(cfg, buf, N, qi)
-            assert r.n_kept == int(bits[lv].sum())
-            assert r.n_cand == int(np.isfinite(scores[lv]).sum())
-            assert r.mass_kept >= math.ceil(p * r.mass_total) - 1
-            assert 1 <= r.n_kept <= r.n_cand
+    PAR.check_stats_all(zha, cfg, buf, N, p, range(int(buf.layout.n_queries)))
 
 
 def test_p1_is_dense():
@@ -569,6 +570,7 @@ def test_route_levels_schedule_and_start_level():
             q = np64(batch.Q[b, h, ql // T, ql % T])
             PAR.check_route_teacher_forced(q, to, rn, cfg.chunk, pl, kept, cfg.dtype,
                                            {lv: scores[lv] for lv in range(1, t + 1)}, leaf_dtype="f64", top=t)
+        PAR.check_stats_all(zha, cfg, buf, N, pl, range(int(buf.layout.n_queries)), top=top or L)
     a, c = zha.alloc_route(cfg, T), zha.alloc_route(cfg, T)
     zha.route_levels(cfg, tree, N, batch.Q, T, [0.9] * (L - 1) + [1.0], a, K=batch.K)
     zha.route_levels(cfg, tree, N, batch.Q, T, [0.9] * L, c, top_level=L - 1, K=batch.K)
@@ -726,6 +728,7 @@ def test_split_select_is_bit_identical(name, leaf_form, N, p, repeat):
             n_cut += a.cut_id != 2**31 - 1
     if repeat and p < 1.0:
         assert n_cut > 0, "no level split its ties at the cut"
+    PAR.check_stats_all(zha, cfg, bufs[0], N, p, range(int(rl.n_queries)))
 
 
 SMALL_CASES = [
@@ -781,6 +784,7 @@ def test_small_and_degenerate_token_counts(name, kw, sizes):
             o, l = O.attend(q, Kn, Vn, idx)
             np.testing.assert_allclose(out_c[qi], o, rtol=0, atol=tol, err_msg=f"N={N} query {qi}")
             np.testing.assert_allclose(lse_c[qi], l, rtol=0, atol=tol, err_msg=f"N={N} query {qi}")
+        PAR.check_stats_all(zha, cfg, buf, N, p, range(nq))
 
 
 WAVE_CASES = [
@@ -843,3 +847,4 @@ def test_wave_select_is_bit_identical(name, N, p, repeat):
                 n_cut += s1[qa].cut_id != 2**31 - 1
     if repeat and p < 1.0:
         assert n_cut > 0, "no level split its ties at the cut"
+    PAR.check_stats_all(zha, cfg, b16, N, p, range(int(b16.layout.n_queries)))

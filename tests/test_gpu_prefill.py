@@ -146,6 +146,8 @@ def test_prefill_matches_prefix_decode(case):
             o, l = O.attend(q, Kn, Vn, idx)
             np.testing.assert_allclose(out_c[qi], o, rtol=0, atol=tol, err_msg=f"q{ql}")
             np.testing.assert_allclose(lse_c[qi], l, rtol=0, atol=tol, err_msg=f"q{ql}")
+    # the GPU's own selection records of every query of the block
+    PAR.check_stats_all(zha, cfg, buf, N, p, range(nq))
     _say(f"prefill {name}: {cfg.n_caches} caches checked")
 
 
