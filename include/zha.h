@@ -14,7 +14,9 @@
  * Conventions for every entry point:
  *   - Every pointer argument named *device* is device memory owned by the
  *     caller; the library never allocates, frees or retains device memory and
- *     keeps no global mutable state apart from a thread-local error string.
+ *     keeps no global mutable state apart from a thread-local error string
+ *     (and, for zha_attend_noalloc, one static scratch array per GPU and a
+ *     table of their addresses).
  *   - Calls are asynchronous and ordered on the given HIP stream (a
  *     hipStream_t passed as void*; NULL = the default stream).  No call
  *     synchronises the host.  Device faults surface at the caller's next
@@ -432,6 +434,29 @@ int zha_attend(const zha_config* cfg, const void* Q, const int64_t q_strides[4],
                const uint32_t* sel1, int64_t sel1_words, const float* logits, uint32_t flags,
                float* out, float* lse, void* ws, int64_t ws_bytes, zha_profile* prof,
                void* stream);
+
+/*
+ * zha_attend_noalloc - zha_attend for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation, argument meanings, outputs and
+ * errors as zha_attend, without ws / ws_bytes.  The split-K partials go to a
+ * static device array of ZHA_NOALLOC_SCRATCH_BYTES bytes inside the library
+ * (one per GPU, held from the first call on that GPU until the process
+ * ends); the call allocates nothing.  It uses the array of the calling
+ * thread's current device, so `stream` must belong to that device.  Every
+ * partial is written before it is read, so no call depends on what an
+ * earlier call left there; but all calls on one GPU share the one array, so
+ * two calls whose executions overlap on a GPU (different streams, or
+ * threads) race and their results are undefined.
+ * Errors: as zha_attend, plus ZHA_ERR_CAPACITY when the configuration needs
+ * more than ZHA_NOALLOC_SCRATCH_BYTES (zha_attend_workspace_bytes(cfg, T)),
+ * and ZHA_ERR_ARG when `stream` belongs to another device.
+ */
+#define ZHA_NOALLOC_SCRATCH_BYTES (32ll << 20)
+int zha_attend_noalloc(const zha_config* cfg, const void* Q, const int64_t q_strides[4], int32_t T,
+                       const void* K, const void* V, const int64_t kv_strides[3], int64_t n_tokens,
+                       const uint32_t* sel1, int64_t sel1_words, const float* logits, uint32_t flags,
+                       float* out, float* lse, zha_profile* prof, void* stream);
 
 /*
  * zha_dense_decode - dense flash-decode over all n_tokens keys, the

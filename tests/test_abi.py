@@ -320,3 +320,22 @@ def test_bit_helpers_roundtrip():
     w = zha.pack_bits(m, 3)
     assert w.dtype == torch.int32 and w.shape == (3, 3)
     assert torch.equal(zha.unpack_bits(w, 77), m)
+
+
+def test_attend_noalloc_rejects_oversized_configuration(lib):
+    """zha_attend_noalloc checks on the host that the split-K partials fit its
+    static scratch (before touching any pointer or the GPU)."""
+    import torch
+
+    cfg = zha.ZhaConfig(8, 8, 4, 128, 16, 4, 6, "bf16", 1 << 20, "weights")
+    assert zha.attend_workspace_bytes(cfg, 256) > zha.ZHA_NOALLOC_SCRATCH_BYTES
+    q = torch.empty(8, 8, 4, 256, 128, dtype=torch.bfloat16)
+    k = torch.empty(1, 1, 16, 128, dtype=torch.bfloat16)
+    out = torch.empty(16, 128)
+    with pytest.raises(zha.ZhaError) as ei:
+        zha.attend_noalloc(cfg, q, 256, k, k, 1 << 20, None, zha.ZHA_ALL_KEYS, out, None)
+    assert ei.value.code == zha.ZHA_ERR_CAPACITY
+    assert "static scratch" in str(ei.value)
+    # the header's limit is the binding's
+    text = open(HEADER).read()
+    assert "#define ZHA_NOALLOC_SCRATCH_BYTES (32ll << 20)" in text

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "zha_internal.h"
 
@@ -284,6 +285,42 @@ int do_build(const zha_config* cfg, const void* K, const int64_t* ks, int64_t n_
   }
   hipError_t e = zha::launch_build(a, cfg->kv_dtype, pr);
   if (e != hipSuccess) return hip_fail(e, "build launch");
+  return ZHA_OK;
+}
+
+// Scratch of zha_attend_noalloc: one static array per GPU (each device
+// holds its own copy at its own address from the library's first use of it
+// until the process ends).  Host code never uses the array's name as an
+// address: the device address comes from hipGetSymbolAddress, once per
+// device, with that device current, and is kept in g_scratch_ptr.
+static __device__ __align__(256) char scratch[ZHA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the calling thread's current device, which must be
+// the device of `stream` (NULL = the current device's default stream).
+int scratch_on_current_device(void* stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(ZHA_ERR_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+  if (stream) {
+    hipDevice_t sd = -1;
+    e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sd);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+    if (sd != dev) return fail(ZHA_ERR_ARG, "stream belongs to device %d, the current device is %d", (int)sd, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(ZHA_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
   return ZHA_OK;
 }
 
@@ -716,6 +753,25 @@ int zha_attend(const zha_config* cfg, const void* Q, const int64_t q_strides[4],
   hipError_t e = zha::launch_attend(a, cfg->kv_dtype, cfg->batch * cfg->n_kv_heads, pr);
   if (e != hipSuccess) return hip_fail(e, "attend launch");
   return ZHA_OK;
+}
+
+int zha_attend_noalloc(const zha_config* cfg, const void* Q, const int64_t q_strides[4], int32_t T,
+                       const void* K, const void* V, const int64_t kv_strides[3], int64_t n_tokens,
+                       const uint32_t* sel1, int64_t sel1_words, const float* logits, uint32_t flags,
+                       float* out, float* lse, zha_profile* prof, void* stream) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if ((rc = check_T(cfg, T))) return rc;
+  const int64_t need = attend_ws(cfg, T);
+  if (need > ZHA_NOALLOC_SCRATCH_BYTES)
+    return fail(ZHA_ERR_CAPACITY,
+                "zha_attend_noalloc: %lld bytes of split-K partials needed, the static scratch holds %lld "
+                "(use zha_attend with a workspace)",
+                (long long)need, (long long)ZHA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((rc = scratch_on_current_device(stream, &ws))) return rc;
+  return zha_attend(cfg, Q, q_strides, T, K, V, kv_strides, n_tokens, sel1, sel1_words, logits, flags, out, lse,
+                    ws, ZHA_NOALLOC_SCRATCH_BYTES, prof, stream);
 }
 
 int zha_dense_decode(const zha_config* cfg, const void* Q, const int64_t q_strides[4], int32_t T,

@@ -32,6 +32,7 @@ ZHA_LEAF_MEAN, ZHA_LEAF_WEIGHTS, ZHA_LEAF_WEIGHTS2 = 0, 1, 2
 LEAF_FORMS = {"mean": ZHA_LEAF_MEAN, "weights": ZHA_LEAF_WEIGHTS, "weights2": ZHA_LEAF_WEIGHTS2}
 ZHA_G_KV, ZHA_G_FP8 = 0, 2
 MAX_LEVELS = 8
+ZHA_NOALLOC_SCRATCH_BYTES = 32 << 20  # static scratch of zha_attend_noalloc (include/zha.h)
 
 
 class ZhaError(RuntimeError):
@@ -187,6 +188,7 @@ def load(path: str = LIB_PATH) -> ct.CDLL:
         "zha_route_prefill": (ct.c_int, [cfgp, P, P, I64, P, i64p, I32, F, P, i64p, P, P, P, P, P, I64, P, P]),
         "zha_attend": (ct.c_int, [cfgp, P, i64p, I32, P, P, i64p, I64, P, I64, P, ct.c_uint32, P, P, P, I64, P, P]),
         "zha_dense_decode": (ct.c_int, [cfgp, P, i64p, I32, P, P, i64p, I64, P, P, P, I64, P, P]),
+        "zha_attend_noalloc": (ct.c_int, [cfgp, P, i64p, I32, P, P, i64p, I64, P, I64, P, ct.c_uint32, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -488,6 +490,26 @@ def attend(
             int(ws.numel()),
             _prof(ev),
             _stream(Q),
+        )
+    )
+
+
+def attend_noalloc(cfg: ZhaConfig, Q: torch.Tensor, T: int, K: torch.Tensor, V: torch.Tensor, n_tokens: int,
+                   sel1: Optional[torch.Tensor], flags: int, out: torch.Tensor, lse: Optional[torch.Tensor], ev=None,
+                   logits: Optional[torch.Tensor] = None):
+    """zha_attend_noalloc: zha_attend with the library's static per-GPU
+    scratch instead of a caller workspace (allocates nothing; calls that
+    overlap on one GPU race)."""
+    c = cfg.c()
+    qs = _i64(*_elem_strides(Q, 4))
+    kvs = _i64(*_elem_strides(K, 3))
+    if tuple(V.stride()[:3]) != tuple(K.stride()[:3]):
+        raise ValueError("K and V must share strides")
+    words = 0 if sel1 is None else int(sel1.shape[-1])
+    _check(
+        load().zha_attend_noalloc(
+            ct.byref(c), _ptr(Q), qs, int(T), _ptr(K), _ptr(V), kvs, int(n_tokens), _ptr(sel1), words, _ptr(logits),
+            int(flags), _ptr(out), _ptr(lse), _prof(ev), _stream(Q),
         )
     )
 
