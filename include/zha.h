@@ -248,7 +248,8 @@ enum zha_kernel_id {
   ZHA_K_SCORE = 2,   /* plane scores of one level's candidates */
   ZHA_K_SELECT = 3,  /* top-p selection of one level */
   ZHA_K_ATTEND = 4,  /* split-K attention over the routed keys */
-  ZHA_K_COMBINE = 5  /* merge of the split-K partials */
+  ZHA_K_COMBINE = 5, /* merge of the split-K partials */
+  ZHA_K_PROBE = 6    /* zha_stream_probe (level field = its mode) */
 };
 typedef struct zha_profile {
   void* events[2 * ZHA_PROFILE_MAX]; /* hipEvent_t */
@@ -467,6 +468,47 @@ int zha_dense_decode(const zha_config* cfg, const void* Q, const int64_t q_strid
                      const void* K, const void* V, const int64_t kv_strides[3], int64_t n_tokens,
                      float* out, float* lse, void* ws, int64_t ws_bytes, zha_profile* prof,
                      void* stream);
+
+/* ---- measurement (not part of the decode path) ------------------------- */
+
+/*
+ * zha_stream_probe - one launch of a plain streaming kernel over n_bytes of
+ * device memory, timed like any other call through prof: the achievable HBM
+ * bandwidth of simple access patterns on the GPU (the ceiling against which
+ * the decode kernels' roofline fractions are read) and, as ZHA_PROBE_COPY, a
+ * copy of known size that calibrates the byte counters of a profiler.
+ * Every mode reads each 16-byte piece of src[0, n_bytes) exactly once:
+ *   ZHA_PROBE_READ / _NT   read only (plain / nontemporal loads), grid-stride
+ *                          over 4,096 workgroups; dst receives at most one word
+ *                          per workgroup (>= 16 KiB needed);
+ *   ZHA_PROBE_READ_SLAB / _SLAB_NT  read only, one contiguous 512 KiB slab
+ *                          per workgroup (dst as above);
+ *   ZHA_PROBE_COPY / _NT   dst[0, n_bytes) = src (plain / nontemporal), one
+ *                          contiguous 512 KiB slab per workgroup;
+ *   ZHA_PROBE_MIX / _NT    slab by slab, every 16 KiB span of src folded
+ *                          (xor of its four 4 KiB quarters) into the matching
+ *                          4 KiB span of dst[0, n_bytes / 4): four bytes read
+ *                          per byte
+ *                          written (plain / nontemporal stores), the mix of
+ *                          the scoring passes that read keys and write
+ *                          logits.
+ *   src, dst  device, 16-byte aligned, not overlapping; dst_bytes its size.
+ *   n_bytes   a positive multiple of 64.
+ * Errors: ZHA_ERR_ARG (mode, n_bytes), ZHA_ERR_NULL, ZHA_ERR_ALIGN,
+ * ZHA_ERR_CAPACITY (dst_bytes too small), ZHA_ERR_HIP.
+ */
+enum zha_probe_mode {
+  ZHA_PROBE_READ = 0,
+  ZHA_PROBE_READ_NT = 1,
+  ZHA_PROBE_COPY = 2,
+  ZHA_PROBE_COPY_NT = 3,
+  ZHA_PROBE_MIX = 4,
+  ZHA_PROBE_MIX_NT = 5,
+  ZHA_PROBE_READ_SLAB = 6,
+  ZHA_PROBE_READ_SLAB_NT = 7
+};
+int zha_stream_probe(int32_t mode, const void* src, void* dst, int64_t n_bytes, int64_t dst_bytes,
+                     zha_profile* prof, void* stream);
 
 #ifdef __cplusplus
 }

@@ -339,3 +339,32 @@ def test_attend_noalloc_rejects_oversized_configuration(lib):
     # the header's limit is the binding's
     text = open(HEADER).read()
     assert "#define ZHA_NOALLOC_SCRATCH_BYTES (32ll << 20)" in text
+
+
+def test_stream_probe_rejects_bad_arguments(lib):
+    """The measurement probe checks mode, size, alignment, overlap and the
+    destination's size on the host before any launch."""
+    import torch
+
+    src = torch.empty(1024, dtype=torch.int32)
+    dst = torch.empty(1024, dtype=torch.int32)
+    with pytest.raises(zha.ZhaError) as ei:
+        lib_mode = 9
+        zha._check(lib.zha_stream_probe(lib_mode, zha._ptr(src), zha._ptr(dst), 4096, 4096, None, None))
+    assert ei.value.code == zha.ZHA_ERR_ARG
+    for n in (0, 100):
+        with pytest.raises(zha.ZhaError) as ei:
+            zha.stream_probe("copy", src, dst, n)
+        assert ei.value.code == zha.ZHA_ERR_ARG
+    with pytest.raises(zha.ZhaError) as ei:  # a copy writes n_bytes
+        zha.stream_probe("copy", src, dst[:512], 4096)
+    assert ei.value.code == zha.ZHA_ERR_CAPACITY
+    with pytest.raises(zha.ZhaError) as ei:  # read-only probes write one word per workgroup
+        zha.stream_probe("read", src, dst, 4096)
+    assert ei.value.code == zha.ZHA_ERR_CAPACITY
+    with pytest.raises(zha.ZhaError) as ei:
+        zha.stream_probe("mix", src, src, 4096)
+    assert ei.value.code == zha.ZHA_ERR_ARG
+    with pytest.raises(zha.ZhaError) as ei:
+        zha._check(lib.zha_stream_probe(2, ct.c_void_p(src.data_ptr() + 4), zha._ptr(dst), 64, 4096, None, None))
+    assert ei.value.code == zha.ZHA_ERR_ALIGN

@@ -848,3 +848,59 @@ def test_wave_select_is_bit_identical(name, N, p, repeat):
     if repeat and p < 1.0:
         assert n_cut > 0, "no level split its ties at the cut"
     PAR.check_stats_all(zha, cfg, b16, N, p, range(int(b16.layout.n_queries)))
+
+
+CUT_CASES = [
+    # name, leaf form, n_tokens, p, keys repeat with period 4096 (exact score ties), queries per head
+    ("weights", "weights", (1 << 18) - 1003, 0.95, False, 1),
+    ("weights2-fused", "weights2", (1 << 18) - 64, 0.9, False, 1),
+    ("mean-ties", "mean", 1 << 18, 0.9, True, 1),
+    ("mean-small-p", "mean", (1 << 18) - 4 * 37, 0.05, False, 1),
+    ("mean-keep-all", "mean", 1 << 17, 1.0, False, 1),
+    ("weights-16q", "weights", 1 << 17, 0.95, False, 4),
+]
+
+
+@pytest.mark.parametrize("name,leaf_form,N,p,repeat,T", CUT_CASES, ids=[c[0] for c in CUT_CASES])
+def test_select_cut_bin_matches_radix(name, leaf_form, N, p, repeat, T, monkeypatch):
+    """The one-workgroup select resolves the cut among the candidates of one
+    score bin held in LDS (two reads of the row, children of dropped parents
+    skipped); forced onto its radix passes (ZHA_SELECT_CUT_CAP=0) it must
+    reach the same bits and statistics, and both agree with the selection
+    records' exact rule."""
+    _say(f"select cut bin {name}")
+    cap = 1 << 18
+    cfg = zha.ZhaConfig(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=5, dtype="bf16",
+                        capacity=cap, leaf_form=leaf_form)
+    K = torch.empty(1, 2, cap, 128, dtype=torch.bfloat16)
+    Q = torch.empty(1, 2, 4, T, 128, dtype=torch.bfloat16)
+    ref = torch.empty(2, 16, 128)
+    for h in range(2):
+        k, _, r, q = W.random_cache(cap, 128, 16, "bf16", seed=171 + h, n_queries=4 * T, segment_len=16)
+        if repeat:
+            k = k[:4096].repeat(cap // 4096, 1)
+        n_even = q[::2].shape[0]  # needle queries: half of each head's queries
+        pos = (torch.arange(n_even) * 48611 + 777) % N
+        q[::2] = (1.5 * k[pos].float()).to(torch.bfloat16)
+        K[0, h], ref[h], Q[0, h] = k, r, q.view(4, T, 128)
+    K, Q, ref = K.cuda(), Q.cuda(), ref.cuda()
+    tree = zha.alloc_tree(cfg)
+    zha.build(cfg, K, ref, tree, N)
+    bufs = []
+    for cut in (None, "0"):
+        if cut is None:
+            monkeypatch.delenv("ZHA_SELECT_CUT_CAP", raising=False)
+        else:
+            monkeypatch.setenv("ZHA_SELECT_CUT_CAP", cut)
+        buf = zha.alloc_route(cfg, T, logits=cfg.weights, split_select=False)
+        buf.sel.fill_(-1)  # every word must be written
+        buf.score.zero_()  # entries past a level's nodes are never written
+        zha.route(cfg, tree, N, Q, T, p, buf, K=K)
+        torch.cuda.synchronize()
+        bufs.append(buf)
+    monkeypatch.delenv("ZHA_SELECT_CUT_CAP", raising=False)
+    a, b = bufs
+    assert torch.equal(a.sel, b.sel), "bits differ between the LDS cut bin and the radix passes"
+    assert torch.equal(a.stats, b.stats), "statistics differ between the LDS cut bin and the radix passes"
+    assert torch.equal(a.score.nan_to_num(), b.score.nan_to_num())
+    PAR.check_stats_all(zha, cfg, a, N, p, range(int(a.layout.n_queries)))

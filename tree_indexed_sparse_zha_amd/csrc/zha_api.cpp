@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -190,6 +191,17 @@ int64_t attend_ws(const zha_config* c, int32_t T) {
   const int64_t nq = (int64_t)c->batch * c->n_kv_heads * c->q_per_kv * T;
   const int64_t tk = attend_tile_keys(c, T);
   return align256(nq * cdiv(c->capacity_tokens, tk) * (c->head_dim + 2) * 4);
+}
+
+// Cut-bin candidates the one-workgroup select resolves in LDS (1536, its
+// list size).  The ZHA_SELECT_CUT_CAP environment variable lowers it (0
+// makes every level take the radix passes), so that tests can check that
+// both ways reach the same bits.
+int select_cut_cap() {
+  const char* e = std::getenv("ZHA_SELECT_CUT_CAP");
+  if (!e || !*e) return 1536;
+  const long v = std::strtol(e, nullptr, 10);
+  return v < 0 ? 0 : (v > 1536 ? 1536 : (int)v);
 }
 
 int check_prof(zha_profile* prof) {
@@ -583,6 +595,12 @@ static int do_route(const zha_config* cfg, const void* tree, int64_t n_tokens, c
     se.p = pl[l];
     se.keep_all = pl[l] >= 1.0f;
     se.split = split;
+    // decode levels below the start: children of dropped parents hold -inf
+    // and need not be read (prefill rows also hold each query's partial node)
+    se.sel_parent = (!prefill && cfg->chunk >= 4) ? sa.sel_parent : nullptr;
+    se.parent_words = sa.parent_words;
+    se.C = cfg->chunk;
+    se.cut_cap = select_cut_cap();
     hipError_t e = zha::launch_route_level(sa, se, cfg->kv_dtype, caches, l + 1, pr);
     if (e != hipSuccess) return hip_fail(e, "route launch");
   }
@@ -780,6 +798,29 @@ int zha_dense_decode(const zha_config* cfg, const void* Q, const int64_t q_strid
                      void* stream) {
   return zha_attend(cfg, Q, q_strides, T, K, V, kv_strides, n_tokens, nullptr, 0, nullptr, ZHA_ALL_KEYS,
                     out, lse, ws, ws_bytes, prof, stream);
+}
+
+int zha_stream_probe(int32_t mode, const void* src, void* dst, int64_t n_bytes, int64_t dst_bytes,
+                     zha_profile* prof, void* stream) {
+  int rc = check_prof(prof);
+  if (rc) return rc;
+  if (mode < ZHA_PROBE_READ || mode > ZHA_PROBE_READ_SLAB_NT) return fail(ZHA_ERR_ARG, "probe mode %d unknown", mode);
+  if (n_bytes < 64 || n_bytes % 64) return fail(ZHA_ERR_ARG, "n_bytes must be a positive multiple of 64");
+  if ((rc = check_ptr16(src, "src"))) return rc;
+  if ((rc = check_ptr16(dst, "dst"))) return rc;
+  const bool read_only = mode <= ZHA_PROBE_READ_NT || mode >= ZHA_PROBE_READ_SLAB;
+  const int64_t need = read_only ? 16384 : mode <= ZHA_PROBE_COPY_NT ? n_bytes : n_bytes / 4;
+  if (dst_bytes < need)
+    return fail(ZHA_ERR_CAPACITY, "dst holds %lld bytes, the probe writes up to %lld", (long long)dst_bytes,
+                (long long)need);
+  const char* a = static_cast<const char*>(src);
+  const char* b = static_cast<const char*>(dst);
+  if (a < b + dst_bytes && b < a + n_bytes) return fail(ZHA_ERR_ARG, "src and dst overlap");
+  if (prof) prof->n_used = 0;
+  zha::Prof pr{prof, static_cast<hipStream_t>(stream)};
+  hipError_t e = zha::launch_probe(mode, src, dst, n_bytes, pr);
+  if (e != hipSuccess) return hip_fail(e, "probe launch");
+  return ZHA_OK;
 }
 
 }  // extern "C"

@@ -144,6 +144,13 @@ struct SelectArgs {
   int keep_all;
   void* split;      // split-select workspace (select_split_bytes), or null
   int64_t split_S;  // workgroups per query in the split form (set at launch)
+  // one-workgroup select: the parent level's bitsets (nullptr at the routing
+  // start or when C < 4), whose dropped parents' children it need not read,
+  // and how many cut-bin candidates it resolves in LDS (0: radix passes only)
+  const uint32_t* sel_parent;
+  int64_t parent_words;
+  int C;
+  int cut_cap;
 };
 
 // Split select: per query a state record, and per (query, segment) a slot of
@@ -190,5 +197,7 @@ int64_t route_kr_slots(int dtype, bool leaf_weights, int64_t node_cap, int C);
 hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dtype, int n_caches,
                               int level, Prof& prof);
 hipError_t launch_attend(const AttendArgs& a, int dtype, int n_caches, Prof& prof);
+// streaming probes (zha_stream_probe); arguments checked by the caller
+hipError_t launch_probe(int mode, const void* src, void* dst, int64_t n_bytes, Prof& prof);
 
 }  // namespace zha

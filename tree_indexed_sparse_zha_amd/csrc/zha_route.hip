@@ -1469,6 +1469,66 @@ __device__ __forceinline__ unsigned long long p_target(float p, unsigned long lo
   return P;
 }
 
+// ---- the one-workgroup select: two reads of the row in the common case
+//
+// Pass 1 sums the fixed-point masses (M) and histograms them over a linear
+// grid of scores, 2048 bins over [max - span, max], where span is wide
+// enough that every score below it has a fixed-point mass that rounds to 0
+// (all of them land in bin 0, which then holds no mass and so never the
+// cut).  The bin of a score is monotone in the score, so the cut lies in
+// the one bin b whose mass interval holds P, exactly as in a radix digit.
+// Pass 2 writes the bitset: every candidate in a bin above b is kept, every
+// one below dropped, and the candidates of bin b (key, id, mass) are
+// compacted into LDS.  Among those few the keep rule is applied exactly: a
+// candidate is kept iff the mass of the bins above b plus the mass of the
+// bin-b candidates ranked before it (score descending, id ascending) is
+// below P; their bits are or-ed in.  This is the same cut the radix select
+// reaches (the fixed-point rule has one answer).  When bin b holds more
+// candidates than the LDS list takes, the radix passes run instead.
+//
+// Both passes read the row as consecutive float4s per thread (four in
+// flight).  At levels below the routing start with C >= 4 the parent
+// level's bits of the query are first copied to LDS (when they fit), and
+// float4s whose parent was not kept are not read: their entries are -inf
+// (not candidates).
+
+constexpr int kLinBins = 2048;
+constexpr int kCutCap = 1536;
+constexpr int kParentWords = 2560;  // parent bits held in LDS: levels of up to 81,920 parents
+constexpr int kSelUnroll = 4;
+
+__device__ __forceinline__ int lin_bin(float s, float lo, float inv_w) {
+  const float x = (s - lo) * inv_w;
+  return x <= 0.0f ? 0 : (x >= (float)(kLinBins - 1) ? kLinBins - 1 : (int)x);
+}
+
+// float4 b of a row (nodes 4b .. 4b+3): -inf past the row's end or, with
+// parent bits in LDS, when its parent (node 4b / C = 4b >> lgC) was not kept.
+__device__ __forceinline__ float4 row_f4(const float4* row4, int64_t n4, const uint32_t* pbits, int lgC, int64_t b) {
+  bool ok = b < n4;
+  if (pbits && ok) {
+    const int64_t pi = (4 * b) >> lgC;
+    ok = (pbits[pi >> 5] >> (pi & 31)) & 1u;
+  }
+  return ok ? row4[b] : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+}
+
+__device__ uint32_t block_minmax_u32(uint32_t v, bool want_max, unsigned long long* red) {
+  const int tid = threadIdx.x;
+  red[tid] = v;
+  __syncthreads();
+  for (int off = kSelThreads / 2; off > 0; off >>= 1) {
+    if (tid < off) {
+      const uint32_t a = (uint32_t)red[tid], b = (uint32_t)red[tid + off];
+      red[tid] = want_max ? max(a, b) : min(a, b);
+    }
+    __syncthreads();
+  }
+  const uint32_t r = (uint32_t)red[0];
+  __syncthreads();
+  return r;
+}
+
 // One workgroup per query.
 __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs A) {
   const int tid = threadIdx.x;
@@ -1485,6 +1545,11 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs A) {
   __shared__ unsigned long long red[kSelThreads];
   __shared__ int sh_bin;
   __shared__ unsigned long long sh_above;
+  __shared__ uint32_t l_key[kCutCap];
+  __shared__ int l_id[kCutCap];
+  __shared__ unsigned long long l_mass[kCutCap];
+  __shared__ uint32_t l_par[kParentWords];
+  __shared__ int l_n;
 
   uint32_t kmax, kmin;
   unsigned long long ncand;
@@ -1501,50 +1566,201 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs A) {
   const float mx = su.mx;
   const double scale = su.scale;
 
-  // digit passes; the first one also sums the total mass M
-  uint32_t want = su.want;
-  int lo = su.lo;
   unsigned long long M = 0, P = 0, above = 0, h_tau = 0;
-  bool first = true;
   uint32_t tau = 0u;
   int cut_id = INT_MAX;
-  bool found = false;
-  do {
-    const int w = lo < 11 ? lo : 11;
-    const int nb = 1 << w;
-    const int top = lo;  // bits [top, 32) must equal `want`
-    lo -= w;
-    for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0ull;
-    __syncthreads();
-    const unsigned long long part = digit_pass(row4, n, 0, n4, first, top, lo, w, want, mx, scale, hist);
-    __syncthreads();
-    if (first) {
-      M = block_sum_u64(part, red);
-      first = false;
-      if (A.keep_all) break;
-      P = p_target(A.p, M);
-      if (w == 0) {  // every candidate has the same key
-        want = kmax;
-        h_tau = M;
-        found = true;
-        break;
+  unsigned long long kept = 0, kmass = 0;
+  bool done = false;
+
+  if (!A.keep_all && A.cut_cap > 0) {
+    // the parent bits of this query, when there are any and they fit
+    const uint32_t* pbits = nullptr;
+    const int lgC = __ffs(A.C) - 1;  // C is a power of two
+    if (A.sel_parent) {
+      const int64_t pw = (((n4 - 1) * 4 >> lgC) >> 5) + 1;  // parent words the row's float4s reach
+      if (pw <= kParentWords) {
+        const uint32_t* prow = A.sel_parent + q * A.parent_words;
+        for (int64_t i = tid; i < pw; i += kSelThreads) l_par[i] = prow[i];
+        pbits = l_par;
       }
     }
-    const int bsel = find_bin(hist, nb, P, &above, red, &sh_bin, &sh_above);
-    want = (w >= 32 ? 0u : (want << w)) | (uint32_t)bsel;
-    h_tau = hist[bsel];
+    // pass 1: M and the linear-bin histogram
+    const float span = (float)(su.shift + 2) * 0.6931472f;  // exp(-span) * 2^shift < 1/4: mass 0 below
+    const float lo = mx - span;
+    const float inv_w = (float)kLinBins / span;
+    for (int i = tid; i < kLinBins; i += kSelThreads) hist[i] = 0ull;
+    if (tid == 0) l_n = 0;
     __syncthreads();
-    found = lo == 0;
-  } while (!found);
-
-  if (!A.keep_all) {
-    tau = want;
-    const unsigned long long need = ties_needed(tau, P, above, h_tau, mx, scale);
-    if (need) cut_id = tie_find(row, 0, n, tau, need);
+    unsigned long long part = 0;
+    for (int64_t b0 = 0; b0 < n4; b0 += (int64_t)kSelThreads * kSelUnroll) {
+      float4 v[kSelUnroll];
+#pragma unroll
+      for (int u = 0; u < kSelUnroll; ++u) v[u] = row_f4(row4, n4, pbits, lgC, b0 + u * kSelThreads + tid);
+#pragma unroll
+      for (int u = 0; u < kSelUnroll; ++u) {
+        const float a[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        const int64_t i0 = (b0 + u * kSelThreads + tid) * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (i0 + e < n && a[e] > kNegInf) {
+            const unsigned long long m = fixed_mass(a[e], mx, scale);
+            part += m;
+            if (m) atomicAdd(&hist[lin_bin(a[e], lo, inv_w)], m);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    M = block_sum_u64(part, red);
+    P = p_target(A.p, M);
+    const int bcut = find_bin(hist, kLinBins, P, &above, red, &sh_bin, &sh_above);
+    // pass 2: bits of the bins above the cut bin; the cut bin's candidates to
+    // LDS.  Eight consecutive lanes hold one bitset word's 32 candidates.
+    for (int64_t b0 = 0; b0 < n4; b0 += (int64_t)kSelThreads * kSelUnroll) {
+      float4 v[kSelUnroll];
+#pragma unroll
+      for (int u = 0; u < kSelUnroll; ++u) v[u] = row_f4(row4, n4, pbits, lgC, b0 + u * kSelThreads + tid);
+#pragma unroll
+      for (int u = 0; u < kSelUnroll; ++u) {
+        const float a[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        const int64_t b = b0 + u * kSelThreads + tid;
+        uint32_t nib = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t i = b * 4 + e;
+          if (i < n && a[e] > kNegInf) {
+            const int bin = lin_bin(a[e], lo, inv_w);
+            if (bin > bcut) {
+              nib |= 1u << e;
+              kmass += fixed_mass(a[e], mx, scale);
+            } else if (bin == bcut) {
+              const int j = atomicAdd(&l_n, 1);
+              if (j < A.cut_cap) {
+                l_key[j] = order_key(a[e]);
+                l_id[j] = (int)i;
+                l_mass[j] = fixed_mass(a[e], mx, scale);
+              }
+            }
+          }
+        }
+        kept += __popc(nib);
+        uint32_t word = nib << (4 * (tid & 7));
+        word |= __shfl_xor(word, 1);
+        word |= __shfl_xor(word, 2);
+        word |= __shfl_xor(word, 4);
+        if ((tid & 7) == 0 && b / 8 < nwords) srow[b / 8] = word;
+      }
+    }
+    __syncthreads();  // the row's words are stored and visible to the workgroup before the or-ed bits
+    const int nl = l_n;
+    if (nl <= A.cut_cap) {
+      // radix digits over the cut bin's candidates in LDS find the cut key,
+      // starting below the common prefix of their keys
+      uint32_t kl_max = 0u, kl_min = 0xffffffffu;
+      for (int j = tid; j < nl; j += kSelThreads) {
+        kl_max = max(kl_max, l_key[j]);
+        kl_min = min(kl_min, l_key[j]);
+      }
+      kl_max = block_minmax_u32(kl_max, true, red);
+      kl_min = block_minmax_u32(kl_min, false, red);
+      const int hb = kl_max == kl_min ? 0 : 32 - __clz(kl_max ^ kl_min);
+      uint32_t want = hb >= 32 ? 0u : (kl_max >> hb);
+      int lo2 = hb;
+      h_tau = hist[bcut];
+      __syncthreads();
+      while (lo2 > 0) {
+        const int w = lo2 < 11 ? lo2 : 11;
+        const int nb = 1 << w;
+        const int top = lo2;
+        lo2 -= w;
+        for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0ull;
+        __syncthreads();
+        const uint32_t mask = (uint32_t)(nb - 1);
+        for (int j = tid; j < nl; j += kSelThreads) {
+          const uint32_t k = l_key[j];
+          if (top >= 32 || (k >> top) == want) atomicAdd(&hist[(k >> lo2) & mask], l_mass[j]);
+        }
+        __syncthreads();
+        const int bsel = find_bin(hist, nb, P, &above, red, &sh_bin, &sh_above);
+        want = (w >= 32 ? 0u : (want << w)) | (uint32_t)bsel;
+        h_tau = hist[bsel];
+        __syncthreads();
+      }
+      tau = want;
+      // ties at tau carry one mass: the lowest `need` ids are kept (0: all)
+      const unsigned long long need = ties_needed(tau, P, above, h_tau, mx, scale);
+      if (need) {
+        __shared__ int sh_cut;
+        if (tid == 0) sh_cut = INT_MAX;
+        __syncthreads();
+        for (int j = tid; j < nl; j += kSelThreads) {
+          if (l_key[j] != tau) continue;
+          unsigned long long rank = 0ull;  // ties with a lower id
+          for (int f = 0; f < nl; ++f) rank += (l_key[f] == tau && l_id[f] < l_id[j]) ? 1ull : 0ull;
+          if (rank == need - 1ull) sh_cut = l_id[j] + 1;
+        }
+        __syncthreads();
+        cut_id = sh_cut;
+        __syncthreads();
+      }
+      for (int j = tid; j < nl; j += kSelThreads) {
+        const uint32_t k = l_key[j];
+        const int id = l_id[j];
+        if (k > tau || (k == tau && id < cut_id)) {
+          atomicOr(&srow[id >> 5], 1u << (id & 31));
+          kmass += l_mass[j];
+          ++kept;
+        }
+      }
+      done = true;
+    } else {
+      kept = 0ull;
+      kmass = 0ull;
+      above = 0ull;
+    }
   }
 
-  unsigned long long kept = 0, kmass = 0;
-  write_bits(row4, n, 0, nwords, tau, cut_id, mx, scale, srow, &kept, &kmass);
+  if (!done) {
+    // radix digit passes on the order key; the first one also sums M
+    uint32_t want = su.want;
+    int lo = su.lo;
+    bool first = true;
+    bool found = false;
+    do {
+      const int w = lo < 11 ? lo : 11;
+      const int nb = 1 << w;
+      const int top = lo;  // bits [top, 32) must equal `want`
+      lo -= w;
+      for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0ull;
+      __syncthreads();
+      const unsigned long long part = digit_pass(row4, n, 0, n4, first, top, lo, w, want, mx, scale, hist);
+      __syncthreads();
+      if (first) {
+        M = block_sum_u64(part, red);
+        first = false;
+        if (A.keep_all) break;
+        P = p_target(A.p, M);
+        if (w == 0) {  // every candidate has the same key
+          want = kmax;
+          h_tau = M;
+          found = true;
+          break;
+        }
+      }
+      const int bsel = find_bin(hist, nb, P, &above, red, &sh_bin, &sh_above);
+      want = (w >= 32 ? 0u : (want << w)) | (uint32_t)bsel;
+      h_tau = hist[bsel];
+      __syncthreads();
+      found = lo == 0;
+    } while (!found);
+
+    if (!A.keep_all) {
+      tau = want;
+      const unsigned long long need = ties_needed(tau, P, above, h_tau, mx, scale);
+      if (need) cut_id = tie_find(row, 0, n, tau, need);
+    }
+    write_bits(row4, n, 0, nwords, tau, cut_id, mx, scale, srow, &kept, &kmass);
+  }
   const unsigned long long nk = block_sum_u64(kept, red);
   const unsigned long long km = block_sum_u64(kmass, red);
   if (tid == 0) {

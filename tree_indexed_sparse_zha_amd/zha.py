@@ -109,8 +109,11 @@ STATS_BYTES = ct.sizeof(SelectStats)
 assert STATS_BYTES == 40
 
 PROFILE_MAX = 32
-K_BUILD, K_SCORE, K_SELECT, K_ATTEND, K_COMBINE = 1, 2, 3, 4, 5
-KERNEL_NAMES = {K_BUILD: "build", K_SCORE: "score", K_SELECT: "select", K_ATTEND: "attend", K_COMBINE: "combine"}
+K_BUILD, K_SCORE, K_SELECT, K_ATTEND, K_COMBINE, K_PROBE = 1, 2, 3, 4, 5, 6
+KERNEL_NAMES = {K_BUILD: "build", K_SCORE: "score", K_SELECT: "select", K_ATTEND: "attend", K_COMBINE: "combine",
+                K_PROBE: "probe"}
+PROBE_MODES = {"read": 0, "read_nt": 1, "copy": 2, "copy_nt": 3, "mix": 4, "mix_nt": 5, "read_slab": 6,
+               "read_slab_nt": 7}
 
 
 class Profile(ct.Structure):
@@ -189,6 +192,7 @@ def load(path: str = LIB_PATH) -> ct.CDLL:
         "zha_attend": (ct.c_int, [cfgp, P, i64p, I32, P, P, i64p, I64, P, I64, P, ct.c_uint32, P, P, P, I64, P, P]),
         "zha_dense_decode": (ct.c_int, [cfgp, P, i64p, I32, P, P, i64p, I64, P, P, P, I64, P, P]),
         "zha_attend_noalloc": (ct.c_int, [cfgp, P, i64p, I32, P, P, i64p, I64, P, I64, P, ct.c_uint32, P, P, P, P]),
+        "zha_stream_probe": (ct.c_int, [I32, P, P, I64, I64, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -512,6 +516,12 @@ def attend_noalloc(cfg: ZhaConfig, Q: torch.Tensor, T: int, K: torch.Tensor, V: 
             int(flags), _ptr(out), _ptr(lse), _prof(ev), _stream(Q),
         )
     )
+
+
+def stream_probe(mode: str, src: torch.Tensor, dst: torch.Tensor, n_bytes: int, ev=None):
+    """zha_stream_probe: one launch of a plain streaming kernel (measurement only)."""
+    _check(load().zha_stream_probe(PROBE_MODES[mode], _ptr(src), _ptr(dst), int(n_bytes),
+                                   int(dst.numel() * dst.element_size()), _prof(ev), _stream(src)))
 
 
 def dense_decode(cfg, Q, T, K, V, n_tokens, out, lse, ws, ev=None):
