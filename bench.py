@@ -278,7 +278,7 @@ def resolve_leaf_form(w, leaf_form, g_dtype, no_logits):
     T = w.queries_per_head
     if leaf_form == "auto":
         leaf_form = "weights2" if w.q_per_kv * T <= 4 and not no_logits else "weights"
-    if leaf_form == "weights2" and (w.chunk != 4 or w.levels < 3 or g_dtype != "kv"):
+    if leaf_form == "weights2" and (w.chunk != 4 or w.levels < 3):
         leaf_form = "weights"
     if leaf_form == "weights" and w.chunk not in (4, 8, 16):
         leaf_form = "mean"

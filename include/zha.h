@@ -84,9 +84,10 @@ enum zha_dtype { ZHA_F32 = 0, ZHA_BF16 = 1 };
  *     node and of its children, and recomputes the weights, shares and c
  *     from the reference queries the tree keeps (ref_offset) and the keys,
  *     to fp32 rounding of the stored ones.  A level-2 node occupies R*(4C+8) bytes instead of
- *     R*(2d+8).  Supported with bf16, chunk 4, 3..8 levels and g_dtype
- *     ZHA_G_KV; not with the prefill calls (zha_build_spine,
- *     zha_route_prefill).  Levels >= 3 are the same in every form.
+ *     R*(2d+8).  Supported with bf16, chunk 4 and 3..8 levels, with either
+ *     g_dtype (ZHA_G_FP8 then stores levels >= 3 in fp8); not with the
+ *     prefill calls (zha_build_spine, zha_route_prefill).  Levels >= 3 are
+ *     the same in every form.
  */
 enum zha_leaf_form { ZHA_LEAF_MEAN = 0, ZHA_LEAF_WEIGHTS = 1, ZHA_LEAF_WEIGHTS2 = 2 };
 

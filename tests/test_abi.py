@@ -94,11 +94,11 @@ def test_tree_layout_weights2_form():
 
 
 def test_tree_layout_fp8():
-    for leaf_form in ("mean", "weights"):
+    for leaf_form in ("mean", "weights", "weights2"):
         tl = zha.tree_layout(cfg_deep(leaf_form=leaf_form, g_dtype="fp8"))
         kv = zha.tree_layout(cfg_deep(leaf_form=leaf_form))
         for i in range(6):
-            weights = leaf_form == "weights" and i == 0
+            weights = (leaf_form == "weights" and i == 0) or (leaf_form == "weights2" and i <= 1)
             assert tl.g_bytes[i] == (16 * 4 * 4 if weights else 16 * 128)
             assert (tl.s_offset[i] == -1) if weights else (tl.s_offset[i] % 256 == 0 and tl.s_offset[i] > tl.c_offset[i])
             assert kv.s_offset[i] == -1
@@ -173,7 +173,7 @@ def test_route_layout_sizes():
         (dict(leaf_form="weights2", levels=3, n_ref=1, head_dim=64), 0),
         (dict(leaf_form="weights2", levels=2), zha.ZHA_ERR_UNSUPPORTED),
         (dict(leaf_form="weights2", chunk=8, levels=4), zha.ZHA_ERR_UNSUPPORTED),
-        (dict(leaf_form="weights2", g_dtype="fp8"), zha.ZHA_ERR_UNSUPPORTED),
+        (dict(leaf_form="weights2", g_dtype="fp8"), 0),
         (dict(leaf_form="weights2", dtype="f32", head_dim=64, n_ref=4, levels=3), zha.ZHA_ERR_UNSUPPORTED),
     ],
 )

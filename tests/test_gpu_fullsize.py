@@ -69,6 +69,8 @@ def _levels(cfg, buf, N, qi):
 
 
 FORMS = ["weights2", "weights"]
+# the bench's form with fp8 rows from level 3 up (the low-precision router variant)
+FORMS_1M = FORMS + ["weights2-fp8"]
 # the bench's default run: 2 warm-up + 8 timed append steps sized into the capacity
 BENCH_STEPS = 10
 
@@ -93,12 +95,16 @@ def _run_step(cfg, b, N0, A, T, p):
     return tree, buf, out, lse
 
 
-@pytest.mark.parametrize("leaf_form", FORMS)
-def test_deep1m_full_size_two_caches(leaf_form):
+@pytest.mark.parametrize("form", FORMS_1M)
+def test_deep1m_full_size_two_caches(form):
     w = W.WORKLOADS["deep1m"]
     N0, A, T, p = w.n_tokens, w.append_tokens, w.queries_per_head, 0.95
+    leaf_form, _, g8 = form.partition("-")
     cfg = _cfg(w, N0 + BENCH_STEPS * A, leaf_form)
-    _say(f"deep1m {leaf_form}: generating and running the bench step")
+    if g8:
+        cfg.g_dtype = "fp8"
+    gd = "fp8" if g8 else w.dtype
+    _say(f"deep1m {form}: generating and running the bench step")
     b = W.make_batch(w, device="cuda", capacity=cfg.capacity, append_steps=1)
     tree, buf, out, lse = _run_step(cfg, b, N0, A, T, p)
     assert buf.logits is not None
@@ -109,9 +115,9 @@ def test_deep1m_full_size_two_caches(leaf_form):
     out_c, lse_c = out.cpu().numpy(), lse.cpu().numpy()
     for cache in (0, cfg.n_caches - 1):
         bb, h = divmod(cache, cfg.n_kv_heads)
-        _say(f"deep1m {leaf_form}: oracle tree of cache {cache}")
+        _say(f"deep1m {form}: oracle tree of cache {cache}")
         Kn, Vn, rn = np64(b.K[bb, h, :N]), np64(b.V[bb, h, :N]), np64(b.ref[h])
-        to = O.build_tree(Kn, rn, w.chunk, w.levels, w.dtype, keep_g=False, leaf_dtype="f64", level2_dtype=l2d)
+        to = O.build_tree(Kn, rn, w.chunk, w.levels, gd, keep_g=False, leaf_dtype="f64", level2_dtype=l2d)
         # sampled tree fields, including the appended span
         sizes = O.level_sizes(N, w.chunk, w.levels)
         for lv in range(1, w.levels + 1):
@@ -119,20 +125,27 @@ def test_deep1m_full_size_two_caches(leaf_form):
             n = sizes[lv - 1]
             idx = np.unique(np.r_[0, n // 2, n - 1, np.random.default_rng(lv).integers(0, n, 16)])
             np.testing.assert_allclose(np64(got["L"][cache][idx]), to[lv - 1].L[idx], rtol=1e-5, atol=3e-5)
-            np.testing.assert_allclose(np64(got["c"][cache][idx]), to[lv - 1].c[idx], rtol=1e-5, atol=2e-4)
+            if "g" in got:
+                # c against the oracle's L and the GPU's own stored g (an fp8 or bf16 rounding-boundary
+                # flip of g moves both sides' c alike)
+                gg = np64(got["g"][cache][idx])
+                c_ref = to[lv - 1].L[idx] - np.einsum("nrd,rd->nr", gg, rn) / math.sqrt(w.head_dim)
+                np.testing.assert_allclose(np64(got["c"][cache][idx]), c_ref, rtol=1e-5, atol=5e-5)
+            else:
+                np.testing.assert_allclose(np64(got["c"][cache][idx]), to[lv - 1].c[idx], rtol=1e-5, atol=2e-4)
         for qi_local in range(QC):
             gq, t = divmod(qi_local, T)
             qi = cache * QC + qi_local
             q = np64(b.Q[bb, h, gq, t])
             bits, scores = _levels(cfg, buf, N, qi)
             kept = PAR.gpu_kept_from_bits(bits)
-            reps = PAR.check_route_teacher_forced(q, to, rn, w.chunk, p, kept, w.dtype, scores, leaf_dtype="f64",
+            reps = PAR.check_route_teacher_forced(q, to, rn, w.chunk, p, kept, gd, scores, leaf_dtype="f64",
                                                   level2_dtype=l2d)
             idx = O.attend_set(kept[1], N, w.chunk)
             o, l = O.attend(q, Kn, Vn, idx)
             np.testing.assert_allclose(out_c[qi], o, rtol=0, atol=PAR.OUT_TOL[w.dtype])
             np.testing.assert_allclose(lse_c[qi], l, rtol=0, atol=PAR.OUT_TOL[w.dtype])
-            _say(f"deep1m {leaf_form} cache {cache} query {qi_local}: share {idx.size / N:.3f}, level diffs "
+            _say(f"deep1m {form} cache {cache} query {qi_local}: share {idx.size / N:.3f}, level diffs "
                  f"{[r.n_diff for r in reps]}, score errors {[f'{r.max_score_err:.1e}' for r in reps]}")
         del to
         gc.collect()

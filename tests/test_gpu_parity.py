@@ -136,6 +136,7 @@ CACHED_CASES = [
     ("w2-qg4-d64-C4-p1", dict(batch=1, n_kv_heads=1, q_per_kv=2, head_dim=64, n_ref=3, chunk=4, levels=3, capacity=2100, leaf_form="weights2"), 1, 2051, 1.0),
     ("w2-qg8-d64-C4", dict(batch=1, n_kv_heads=2, q_per_kv=3, head_dim=64, n_ref=5, chunk=4, levels=3, capacity=6000, leaf_form="weights2"), 2, 5995, 0.8),
     ("w2-qg4-d128-R1", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=1, chunk=4, levels=4, capacity=9000, leaf_form="weights2"), 1, 8990, 0.8),
+    ("w2-fp8-qg4-d128-C4", dict(batch=2, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=5, capacity=9000, leaf_form="weights2", g_dtype="fp8"), 1, 8998, 0.9),
 ]
 
 
@@ -165,11 +166,12 @@ def test_attend_cached_logits_matches_oracle(name, kw, T, N, p, flags):
             b, h = divmod(cache, cfg.n_kv_heads)
             Kn, rn = np64(K[b, h, :N]), np64(ref[h])
             l2d = "f64" if cfg.weight_keys(2) else None
-            to = O.build_tree(Kn, rn, cfg.chunk, cfg.levels, cfg.dtype, keep_g=False, leaf_dtype="f64", level2_dtype=l2d)
+            gd = "fp8" if cfg.g_dtype == "fp8" else cfg.dtype
+            to = O.build_tree(Kn, rn, cfg.chunk, cfg.levels, gd, keep_g=False, leaf_dtype="f64", level2_dtype=l2d)
             for ql in range(QC):
                 bits, scores = gpu_levels(cfg, buf, N, cache * QC + ql)
                 q = np64(Q[b, h, ql // T, ql % T])
-                PAR.check_route_teacher_forced(q, to, rn, cfg.chunk, p, PAR.gpu_kept_from_bits(bits), cfg.dtype,
+                PAR.check_route_teacher_forced(q, to, rn, cfg.chunk, p, PAR.gpu_kept_from_bits(bits), gd,
                                                scores, leaf_dtype="f64", level2_dtype=l2d)
         PAR.check_stats_all(zha, cfg, buf, N, p, range(int(buf.layout.n_queries)))
     for qi, (b, h, gq, t) in enumerate(query_list(cfg, T)):
@@ -214,6 +216,10 @@ BUILD_CASES = [
     ("w2-d128-r16-l6", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=6, dtype="bf16", capacity=9000, leaf_form="weights2"), 8192 + 4 * 37 + 2),
     ("w2-d64-r5-l3", dict(batch=2, n_kv_heads=1, q_per_kv=2, head_dim=64, n_ref=5, chunk=4, levels=3, dtype="bf16", capacity=3000, leaf_form="weights2"), 2048 + 4 * 39 + 3),
     ("w2-d128-r1-l5", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=1, chunk=4, levels=5, dtype="bf16", capacity=5000, leaf_form="weights2"), 4096 + 16 * 7 + 4 * 3 + 1),
+    # levels 1 and 2 as weights, fp8 rows (power-of-two scales) from level 3 up: d = 128 (8 values
+    # per lane) and d = 64 (4 per lane), trailing partial nodes, a partial second top span
+    ("w2-fp8-d128-r16-l6", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=6, dtype="bf16", capacity=9000, leaf_form="weights2", g_dtype="fp8"), 8192 + 4 * 37 + 2),
+    ("w2-fp8-d64-r5-l4", dict(batch=2, n_kv_heads=1, q_per_kv=2, head_dim=64, n_ref=5, chunk=4, levels=4, dtype="bf16", capacity=5000, leaf_form="weights2", g_dtype="fp8"), 4096 + 64 * 3 + 16 * 2 + 4 * 3 + 1),
 ]
 APPEND_CASES = [c for c in BUILD_CASES if c[0] != "c1-f32"]
 
@@ -454,6 +460,7 @@ ROUTE_WORKLOADS = [
     ("deep32k", 2, "weights", 6, "fp8"),
     ("deep32k", 1, "mean", 6, "fp8"),
     ("deep32k", 2, "weights2", 6, "kv"),
+    ("deep32k", 2, "weights2", 6, "fp8"),
 ]
 
 

@@ -43,9 +43,8 @@ int check_config(const zha_config* c) {
     return fail(ZHA_ERR_UNSUPPORTED, "kv_dtype %d unsupported", c->kv_dtype);
   if (c->leaf_form != ZHA_LEAF_MEAN && c->leaf_form != ZHA_LEAF_WEIGHTS && c->leaf_form != ZHA_LEAF_WEIGHTS2)
     return fail(ZHA_ERR_ARG, "leaf_form %d unknown", c->leaf_form);
-  if (c->leaf_form == ZHA_LEAF_WEIGHTS2 &&
-      (c->kv_dtype != ZHA_BF16 || c->chunk != 4 || c->levels < 3 || c->levels > 8 || c->g_dtype != ZHA_G_KV))
-    return fail(ZHA_ERR_UNSUPPORTED, "weights at levels 1 and 2 need bf16, chunk 4, 3..8 levels and g in bf16");
+  if (c->leaf_form == ZHA_LEAF_WEIGHTS2 && (c->kv_dtype != ZHA_BF16 || c->chunk != 4 || c->levels < 3 || c->levels > 8))
+    return fail(ZHA_ERR_UNSUPPORTED, "weights at levels 1 and 2 need bf16, chunk 4 and 3..8 levels");
   if (c->leaf_form == ZHA_LEAF_WEIGHTS &&
       (c->kv_dtype != ZHA_BF16 || (c->chunk != 4 && c->chunk != 8 && c->chunk != 16)))
     return fail(ZHA_ERR_UNSUPPORTED, "the leaf weights form needs bf16 and chunk 4, 8 or 16");
@@ -213,11 +212,13 @@ int check_prof(zha_profile* prof) {
   return ZHA_OK;
 }
 
-// Trees built by k_build_mf: bf16 keys, g in bf16, R <= 16, and a 64-key
-// round's node at a level of the tree: chunk 4 with 3..8 levels (the round's
-// node is level 3) or chunk 8 with 2..7 levels (level 2).
+// Trees built by k_build_mf: bf16 keys, R <= 16, and a 64-key round's node
+// at a level of the tree: chunk 4 with 3..8 levels (the round's node is
+// level 3) or chunk 8 with 2..7 levels (level 2); g in bf16, or in fp8 when
+// levels 1 and 2 are held as weights (fp8 then starts at the round's level).
 static bool build_mf(const zha_config* c) {
-  if (c->kv_dtype != ZHA_BF16 || c->g_dtype != ZHA_G_KV || c->n_ref > 16) return false;
+  if (c->kv_dtype != ZHA_BF16 || c->n_ref > 16) return false;
+  if (c->g_dtype != ZHA_G_KV && c->leaf_form != ZHA_LEAF_WEIGHTS2) return false;
   if (c->chunk == 4) return c->levels >= 3 && c->levels <= 8;
   if (c->chunk == 8) return c->levels >= 2 && c->levels <= 7;
   return false;

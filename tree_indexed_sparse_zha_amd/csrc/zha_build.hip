@@ -485,7 +485,7 @@ __global__ __launch_bounds__(64 * W) void k_build_span(BuildArgs A) {
 // (L, mass 1, fp32 mean g); the append split (sub-span pass, then the top
 // node from the stored fp32 children) therefore reproduces a fresh build bit
 // for bit when both of its passes also run here.
-template <int D, int NU, int C>
+template <int D, int NU, int C, bool G8 = false>
 __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
   static_assert(C == 4 || C == 8, "chunk of 4 or 8 keys");
   constexpr int RL = C == 4 ? 3 : 2;  // level of a round's node (64 keys)
@@ -518,6 +518,7 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
   __shared__ float chL[4][16];
   __shared__ float refL[16][GROW];
   __shared__ float dotp[kMaxLevels][4][16];
+  __shared__ float rmax[kMaxLevels][4][16];  // fp8 levels: the waves' row maxima of a node's g
 
   for (int i = threadIdx.x; i < 16 * D; i += 256) {
     const int jr = i / D, d = i % D;
@@ -530,15 +531,46 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
 
   // node writers above level 2: this lane's D/16 values of g (rounded to
   // bf16), the wave's share of r . g into dotp[slot]; L and c are stored by
-  // finish() once every wave's share is in
+  // finish() once every wave's share is in.  With fp8 rows (G8: ZHA_G_FP8
+  // above levels 1-2 held as weights) row j of g is stored as
+  // s_j * e4m3(g_j / s_j), s_j = 2^(ceil(log2 max_d |g_jd|) - 8) (1 for a
+  // zero row): the row's maximum is gathered over the four waves through
+  // LDS (one barrier; every lane of the workgroup calls put_node together).
   auto put_node = [&](int lvl, int64_t node, float L, const float* gv, int slot) {
-    uint32_t wd[VPL / 2];
-    float gr[VPL];
+    uint32_t wd[VPL / 2];  // bf16 pairs, or (G8) E4M3 codes in wd[0 .. VPL / 4)
+    float gr[VPL];         // the stored values
+    float scl = 1.f;
+    if constexpr (G8) {
+      float mx = 0.f;
 #pragma unroll
-    for (int e = 0; e < VPL / 2; ++e) {
-      wd[e] = bf16_pair(gv[2 * e], gv[2 * e + 1]);
-      gr[2 * e] = bf16_lo(wd[e]);
-      gr[2 * e + 1] = bf16_hi(wd[e]);
+      for (int e = 0; e < VPL; ++e) mx = fmaxf(mx, fabsf(gv[e]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (g == 0) rmax[slot][wave][j] = mx;
+      __syncthreads();
+      mx = fmaxf(fmaxf(rmax[slot][0][j], rmax[slot][1][j]), fmaxf(rmax[slot][2][j], rmax[slot][3][j]));
+      const uint32_t mb = __float_as_uint(mx);
+      const int ex = (int)(mb >> 23) & 255;
+      const int es = ex == 0 ? 0 : ((mb & 0x7fffffu) == 0u ? ex - 127 : ex - 126) - 8;
+      scl = ldexpf(1.f, es);
+#pragma unroll
+      for (int k = 0; k < VPL / 4; ++k) {  // hardware E4M3 conversion, round to nearest even
+        const float a0 = ldexpf(gv[4 * k], -es), a1 = ldexpf(gv[4 * k + 1], -es);
+        const float a2 = ldexpf(gv[4 * k + 2], -es), a3 = ldexpf(gv[4 * k + 3], -es);
+        const int lo8 = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+        wd[k] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, lo8, true);
+        gr[4 * k + 0] = __builtin_amdgcn_cvt_f32_fp8((int)wd[k], 0) * scl;
+        gr[4 * k + 1] = __builtin_amdgcn_cvt_f32_fp8((int)wd[k], 1) * scl;
+        gr[4 * k + 2] = __builtin_amdgcn_cvt_f32_fp8((int)wd[k], 2) * scl;
+        gr[4 * k + 3] = __builtin_amdgcn_cvt_f32_fp8((int)wd[k], 3) * scl;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < VPL / 2; ++e) {
+        wd[e] = bf16_pair(gv[2 * e], gv[2 * e + 1]);
+        gr[2 * e] = bf16_lo(wd[e]);
+        gr[2 * e + 1] = bf16_hi(wd[e]);
+      }
     }
     float dot = 0.f;
 #pragma unroll
@@ -548,11 +580,24 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
     if (g == 0) dotp[slot][wave][j] = dot;
     if (j < R) {
       const int64_t nidx = (int64_t)cache * geo.node_cap[lvl - 1] + node;
-      char* gb = A.tree + geo.g_off[lvl - 1] + nidx * R * D * 2 + ((int64_t)(d0 / 8) * R + j) * 16 + (d0 % 8) * 2;
-      if constexpr (VPL == 8)
-        st16(gb, make_uint4(wd[0], wd[1], wd[2], wd[3]));
-      else
-        *reinterpret_cast<uint2*>(gb) = make_uint2(wd[0], wd[1]);
+      if constexpr (G8) {
+        // byte of (j, d): MFMA step st = d / 32, k-group kg = (d % 32) / 8, at
+        // ((st / 2) * 4R + kg * R + j) * 16 + (st % 2) * 8 + d % 8
+        const int st = d0 / 32, kg = (d0 % 32) / 8;
+        char* gb = A.tree + geo.g_off[lvl - 1] + nidx * R * D + ((int64_t)((st / 2) * 4 + kg) * R + j) * 16 +
+                   (st % 2) * 8 + d0 % 8;
+        if constexpr (VPL == 8)
+          *reinterpret_cast<uint2*>(gb) = make_uint2(wd[0], wd[1]);
+        else
+          *reinterpret_cast<uint32_t*>(gb) = wd[0];
+        if (d0 == 0) reinterpret_cast<float*>(A.tree + geo.s_off[lvl - 1])[nidx * R + j] = scl;
+      } else {
+        char* gb = A.tree + geo.g_off[lvl - 1] + nidx * R * D * 2 + ((int64_t)(d0 / 8) * R + j) * 16 + (d0 % 8) * 2;
+        if constexpr (VPL == 8)
+          st16(gb, make_uint4(wd[0], wd[1], wd[2], wd[3]));
+        else
+          *reinterpret_cast<uint2*>(gb) = make_uint2(wd[0], wd[1]);
+      }
       if (lvl == top && A.top_scratch && !A.merge_top) {
         // sub-span pass: the top node is a child of a split top node; keep it
         // in fp32 as (L, mass 1, mean g) for the merge pass
@@ -945,25 +990,31 @@ hipError_t dispatch_leaf(const BuildArgs& a, dim3 grid, hipStream_t s) {
   }
 }
 
-template <int D, int C>
+template <int D, int C, bool G8>
 hipError_t dispatch_mf_c(const BuildArgs& a, dim3 grid, hipStream_t s) {
   const int nu = a.merge_top ? 0 : a.top_level - (C == 4 ? 3 : 2);
   switch (nu) {
-    case 0: hipLaunchKernelGGL((k_build_mf<D, 0, C>), grid, dim3(256), 0, s, a); break;
-    case 1: hipLaunchKernelGGL((k_build_mf<D, 1, C>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_build_mf<D, 2, C>), grid, dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_build_mf<D, 3, C>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_build_mf<D, 4, C>), grid, dim3(256), 0, s, a); break;
-    case 5: hipLaunchKernelGGL((k_build_mf<D, 5, C>), grid, dim3(256), 0, s, a); break;
+    case 0: hipLaunchKernelGGL((k_build_mf<D, 0, C, G8>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_build_mf<D, 1, C, G8>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_build_mf<D, 2, C, G8>), grid, dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_build_mf<D, 3, C, G8>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_build_mf<D, 4, C, G8>), grid, dim3(256), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((k_build_mf<D, 5, C, G8>), grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+// fp8 rows are built here only above levels 1-2 held as weights (chunk 4):
+// then every level k_build_mf writes through put_node is fp8
 template <int D>
 hipError_t dispatch_mf(const BuildArgs& a, dim3 grid, hipStream_t s) {
-  if (a.geo.C == 8) return dispatch_mf_c<D, 8>(a, grid, s);
-  if (a.geo.C == 4) return dispatch_mf_c<D, 4>(a, grid, s);
+  if (a.geo.g8) {
+    if (a.geo.C != 4 || !a.geo.w2) return hipErrorInvalidValue;
+    return dispatch_mf_c<D, 4, true>(a, grid, s);
+  }
+  if (a.geo.C == 8) return dispatch_mf_c<D, 8, false>(a, grid, s);
+  if (a.geo.C == 4) return dispatch_mf_c<D, 4, false>(a, grid, s);
   return hipErrorInvalidValue;
 }
 

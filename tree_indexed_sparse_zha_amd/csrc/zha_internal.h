@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "../../include/zha.h"
@@ -162,8 +163,33 @@ constexpr int64_t kSelSlotU64 = 2056;
 constexpr int64_t kSelSplitBlocks = 2048;
 constexpr int64_t kSelSplitNodes = 32768;
 constexpr int64_t kSelSplitQueries = 64;
-int select_segments(int64_t n_queries, int64_t n_nodes);
-int64_t select_split_bytes(int64_t n_queries, int64_t max_nodes);
+// workgroups per query of the split select for a level (1: no split)
+inline int select_segments(int64_t n_queries, int64_t n_nodes) {
+  if (n_queries <= 0 || n_queries > kSelSplitQueries) return 1;
+  const int64_t s = std::min<int64_t>(kSelSplitBlocks / n_queries, n_nodes / kSelSplitNodes);
+  return s >= 2 ? (int)std::min<int64_t>(s, 256) : 1;
+}
+
+inline int64_t select_split_bytes(int64_t n_queries, int64_t max_nodes) {
+  const int S = select_segments(n_queries, max_nodes);
+  if (S < 2) return 0;
+  return n_queries * kSelStateBytes + n_queries * S * kSelSlotU64 * 8;
+}
+
+// Keys per tile of the weights-form score kernel launched for a level with
+// wkeys keys per node: 8-key chunks (the light geometry, whose candidates
+// come in 64-key runs) take one wave per 64 keys, so that a tile no query
+// reaches ends at once; else 256 keys (also for many queries per cache, mq).
+inline int leafw_tile(int wkeys, bool mq) { return wkeys == 8 && !mq ? 64 : 256; }
+
+// key-range slots per query of one level's score kernel, for a level of
+// `node_cap` nodes: one per tile for the bf16 kernels (plus one for the
+// prefill spine score), 1 for the fp32 one (atomics)
+inline int64_t route_kr_slots(int dtype, bool leaf_weights, int64_t node_cap, int wkeys) {
+  if (leaf_weights) return (node_cap * wkeys + leafw_tile(wkeys, false) - 1) / leafw_tile(wkeys, false) + 1;
+  if (dtype == 1) return (node_cap + 63) / 64 + 1;  // k_score_bf16: 64-node tiles
+  return 1;                                         // k_score_generic
+}
 
 struct AttendArgs {
   const void* Q;
@@ -191,9 +217,6 @@ struct AttendArgs {
 
 hipError_t launch_build(const BuildArgs& a, int dtype, Prof& prof);
 hipError_t launch_route_init(uint32_t* keyrange, int64_t n, Prof& prof);
-// key-range slots per query of one level's score kernel, for a level of
-// `node_cap` nodes: one per tile for the bf16 kernels, 1 for the fp32 one
-int64_t route_kr_slots(int dtype, bool leaf_weights, int64_t node_cap, int C);
 hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dtype, int n_caches,
                               int level, Prof& prof);
 hipError_t launch_attend(const AttendArgs& a, int dtype, int n_caches, Prof& prof);

@@ -2449,31 +2449,6 @@ __global__ __launch_bounds__(64) void k_select_stats(SelectArgs A, int64_t n_que
 
 }  // namespace
 
-int select_segments(int64_t n_queries, int64_t n_nodes) {
-  if (n_queries <= 0 || n_queries > kSelSplitQueries) return 1;
-  const int64_t s = std::min<int64_t>(kSelSplitBlocks / n_queries, n_nodes / kSelSplitNodes);
-  return s >= 2 ? (int)std::min<int64_t>(s, 256) : 1;
-}
-
-int64_t select_split_bytes(int64_t n_queries, int64_t max_nodes) {
-  const int S = select_segments(n_queries, max_nodes);
-  if (S < 2) return 0;
-  return n_queries * kSelStateBytes + n_queries * S * kSelSlotU64 * 8;
-}
-
-// Keys per tile of the weights-form score kernel launched for a level with
-// wkeys keys per node and QC queries per cache: 8-key chunks (the light
-// geometry, whose candidates come in 64-key runs) take one wave per 64 keys,
-// so that a tile no query reaches ends at once; else 256 keys.
-static int leafw_tile(int wkeys, bool mq) { return wkeys == 8 && !mq ? 64 : 256; }
-
-int64_t route_kr_slots(int dtype, bool leaf_weights, int64_t node_cap, int wkeys) {
-  // one slot per score tile, plus one for the prefill spine score
-  if (leaf_weights) return (node_cap * wkeys + leafw_tile(wkeys, false) - 1) / leafw_tile(wkeys, false) + 1;
-  if (dtype == 1) return (node_cap + 63) / 64 + 1;          // k_score_bf16: 64-node tiles
-  return 1;                                                 // k_score_generic: atomics
-}
-
 hipError_t launch_route_init(uint32_t* keyrange, int64_t n, Prof& prof) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_route_init, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, prof.s, keyrange, n);

@@ -15,7 +15,9 @@ from typing import Dict, List, Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libzha.so")
+# ZHA_LIB_PATH selects another build of the library (the host-sanitizer
+# build the CPU tests use); by default the in-tree one
+LIB_PATH = os.environ.get("ZHA_LIB_PATH") or os.path.join(_HERE, "libzha.so")
 
 ZHA_OK, ZHA_ERR_NULL, ZHA_ERR_ARG, ZHA_ERR_UNSUPPORTED, ZHA_ERR_CAPACITY, ZHA_ERR_ALIGN, ZHA_ERR_HIP = (
     0,
