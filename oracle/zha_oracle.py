@@ -33,9 +33,11 @@ What is computed, for one cache (one sequence x one KV head):
     L_j(P) = logsumexp_c L_j(c),   g_j(P) = sum_c exp(L_j(c) - L_j(P)) g_j(c),
   which is exactly the statistic of all descendant keys.
 * Storage.  g is stored in the KV dtype (rounded once, round-to-nearest-even,
-  from the unrounded merge value), or, in the low-precision router variant
-  (MTP TL;DR "FP4 router"; read here as FP8 E4M3), per row j as a
-  power-of-two scale times E4M3 values; L in fp32-or-better; the plane offset
+  from the unrounded merge value), or, in the low-precision router variants
+  (MTP TL;DR "FP4 router"; the pages name no format), per row j as a
+  power-of-two scale times FP8 E4M3 values, or as OCP MXFP4: blocks of 32
+  elements of d, each an E8M0 power-of-two scale times FP4 E2M1 values
+  (ties to even, saturating); L in fp32-or-better; the plane offset
   c_j = L_j - r_j . ghat_j / sqrt(d) makes c_j + q . ghat_j / sqrt(d) equal the
   tangent plane written with the stored ghat.
 * Score (MTP "Building the tree": the max over the planes approximates the
@@ -128,11 +130,56 @@ def round_fp8_rows(g: np.ndarray):
     return scale[..., None] * round_e4m3(np.asarray(g, dtype=np.float64) / scale[..., None]), scale
 
 
+def round_e2m1(x: np.ndarray) -> np.ndarray:
+    """Round fp64 values to the nearest OCP FP4 E2M1 value (ties to even),
+    saturating at +-6, as fp64.
+
+    E2M1: 1 sign, 2 exponent (bias 1) and 1 mantissa bit: 0 and 0.5
+    (exponent field 0), (1 + m/2) * 2**(e-1) for e = 1..3: 1, 1.5, 2, 3, 4, 6.
+    The spacing is 0.5 below 2, 1 in [2, 4) and 2 from 4 on; the format has
+    no infinity, so magnitudes past 6 saturate to 6.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, e = np.frexp(a)  # a lies in [2**(e-1), 2**e)
+    quantum = np.ldexp(1.0, np.maximum(e - 1, 0) - 1)
+    r = np.minimum(np.rint(a / quantum) * quantum, 6.0)  # np.rint: half to even
+    return np.copysign(r, x)
+
+
+MX_BLOCK = 32  # elements sharing one scale in the OCP MX formats
+
+
+def mxfp4_block_scale(g: np.ndarray) -> np.ndarray:
+    """E8M0 scale 2**s per block of 32 consecutive elements of the last axis
+    (shape [..., d / 32]): s = floor(log2 max|block|) - 2, the OCP MX rule
+    (the largest E2M1 exponent is 2, so the block max lands in [4, 8) and
+    saturates above 6), clamped to the E8M0 range [-127, 127]; an all-zero
+    block gets 2**-127."""
+    g = np.asarray(g, dtype=np.float64)
+    blocks = g.reshape(*g.shape[:-1], g.shape[-1] // MX_BLOCK, MX_BLOCK)
+    m = np.max(np.abs(blocks), axis=-1)
+    _, e = np.frexp(m)  # m in [2**(e-1), 2**e): floor(log2 m) = e - 1
+    s = np.where(m > 0, np.clip(e - 1 - 2, -127, 127), -127)
+    return np.ldexp(1.0, s)
+
+
+def round_mxfp4_rows(g: np.ndarray):
+    """(ghat, scale): the last axis of g in blocks of 32, each stored as
+    scale * E2M1(g / scale) (OCP MXFP4)."""
+    g = np.asarray(g, dtype=np.float64)
+    scale = mxfp4_block_scale(g)
+    sc = np.repeat(scale, MX_BLOCK, axis=-1)
+    return sc * round_e2m1(g / sc), scale
+
+
 def round_storage(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return round_bf16(x)
     if dtype == "fp8":
         return round_fp8_rows(x)[0]
+    if dtype == "fp4":
+        return round_mxfp4_rows(x)[0]
     if dtype == "f32":
         return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
     if dtype == "f64":
@@ -179,7 +226,7 @@ class Level:
     g: Optional[np.ndarray]  # [n, R, d] unrounded softmax-weighted mean key
     ghat: np.ndarray  # [n, R, d] stored (rounded) g
     c: np.ndarray  # [n, R] plane offset L - r . ghat / sqrt(d)
-    scale: Optional[np.ndarray] = None  # [n, R] row scales of fp8 storage
+    scale: Optional[np.ndarray] = None  # [n, R] fp8 row scales, or [n, R, d/32] fp4 block scales
 
 
 def _logsumexp(a: np.ndarray, axis: int) -> np.ndarray:
@@ -211,11 +258,17 @@ def _finish(L, g, ref, g_dtype, keep_g, block=8192):
     d = ref.shape[-1]
     ghat = np.empty_like(g)
     c = np.empty_like(L)
-    scale = np.empty_like(L) if g_dtype == "fp8" else None
+    scale = None
+    if g_dtype == "fp8":
+        scale = np.empty_like(L)
+    elif g_dtype == "fp4":
+        scale = np.empty(L.shape + (d // MX_BLOCK,))
     for a in range(0, L.shape[0], block):
         b = min(L.shape[0], a + block)
         if g_dtype == "fp8":
             ghat[a:b], scale[a:b] = round_fp8_rows(g[a:b])
+        elif g_dtype == "fp4":
+            ghat[a:b], scale[a:b] = round_mxfp4_rows(g[a:b])
         else:
             ghat[a:b] = round_storage(g[a:b], g_dtype)
         c[a:b] = L[a:b] - np.einsum("nrd,rd->nr", ghat[a:b], ref) / math.sqrt(d)

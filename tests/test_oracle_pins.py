@@ -410,6 +410,105 @@ def test_fp8_tree_keeps_tangent_point():
             assert np.all(s - lvl.L[:, j] <= reach + 1e-12)
 
 
+def _e2m1_table():
+    """All 16 FP4 E2M1 codes by value, from the bit layout alone: sign, 2
+    exponent bits (bias 1), 1 mantissa bit; exponent 0 is subnormal
+    (m * 2**-1).  No code is infinite or NaN."""
+    vals = {}
+    for code in range(16):
+        sgn = -1.0 if code & 8 else 1.0
+        e, m = (code >> 1) & 3, code & 1
+        vals[code] = sgn * (m * 0.5 if e == 0 else (1.0 + m / 2.0) * 2.0 ** (e - 1))
+    return vals
+
+
+def _e2m1_brute(x):
+    """Nearest E2M1 value by exhaustive search over the 16 codes, ties to the
+    even code, magnitudes past the largest value saturating to it."""
+    table = _e2m1_table()
+    top = max(table.values())
+    x = min(max(x, -top), top)
+    best = min(table.items(), key=lambda kv: (abs(kv[1] - x), kv[0] & 1, kv[0]))
+    return best[1]
+
+
+def test_e2m1_rounding_matches_brute_force():
+    table = _e2m1_table()
+    pos = sorted(set(abs(v) for v in table.values()))
+    assert pos == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    xs = [0.0, 6.5, 7.0, 7.999, 8.0, 100.0, 1e30]
+    for a, b in zip(pos[:-1], pos[1:]):
+        mid = 0.5 * (a + b)
+        xs += [a, mid, np.nextafter(mid, 0.0), np.nextafter(mid, 1e9)]
+    rng = np.random.default_rng(5)
+    xs += list(rng.uniform(-9, 9, 3000)) + list(rng.normal(0, 0.3, 1000))
+    xs = np.array(xs + [-v for v in xs])
+    got = O.round_e2m1(xs)
+    want = np.array([_e2m1_brute(float(x)) for x in xs])
+    np.testing.assert_array_equal(np.abs(got), np.abs(want))
+    assert np.all((got == 0) | (np.sign(got) == np.sign(xs)))
+
+
+def test_e2m1_pin_rejects_ties_away_from_zero(monkeypatch):
+    """Planted mistake: rounding half away from zero (np.round is half-even,
+    floor(a / q + 0.5) is not) must fail the brute-force pin."""
+    def bad(x):
+        x = np.asarray(x, dtype=np.float64)
+        a = np.abs(x)
+        _, e = np.frexp(a)
+        q = np.ldexp(1.0, np.maximum(e - 1, 0) - 1)
+        return np.copysign(np.minimum(np.floor(a / q + 0.5) * q, 6.0), x)
+
+    monkeypatch.setattr(O, "round_e2m1", bad)
+    with pytest.raises(AssertionError):
+        test_e2m1_rounding_matches_brute_force()
+
+
+def test_mxfp4_block_scale_rule_and_error():
+    """OCP MXFP4: per block of 32 elements an E8M0 scale 2**(floor(log2 max) - 2),
+    so the block max sits in [4, 8) scale units; each element is the nearest
+    E2M1 value (half a spacing of error) unless it saturates at 6 units."""
+    rng = np.random.default_rng(6)
+    g = rng.normal(size=(40, 16, 128)) * np.exp(rng.normal(size=(40, 16, 1)) * 2)
+    g[0, 0] = 0.0
+    g[1, 1, :64] = 0.0
+    g[1, 1, 40] = 2.0**-3  # block max exactly a power of two: 4 scale units
+    ghat, scale = O.round_mxfp4_rows(g)
+    assert scale.shape == (40, 16, 4)
+    assert np.all(np.log2(scale) == np.round(np.log2(scale)))
+    blocks = np.abs(g).reshape(40, 16, 4, 32)
+    m = blocks.max(axis=-1)
+    nz = m > 0
+    r = m[nz] / scale[nz]
+    assert np.all((r >= 4) & (r < 8))
+    assert np.all(scale[0, 0] == 2.0**-127) and np.all(ghat[0, 0] == 0)
+    assert scale[1, 1, 0] == 2.0**-127 and scale[1, 1, 1] == 2.0**-5 and ghat[1, 1, 40] == 2.0**-3
+    sc = np.repeat(scale, 32, axis=-1)
+    u = np.abs(g) / sc  # scale units
+    spacing = np.where(u < 2, 0.5, np.where(u < 4, 1.0, 2.0))
+    err = np.abs(ghat - g) / sc
+    ok = np.where(u <= 6, err <= 0.5 * spacing * (1 + 1e-12), np.abs(ghat) / sc == 6.0)
+    assert np.all(ok)
+    # storage rounding is the same function
+    np.testing.assert_array_equal(O.round_storage(g, "fp4"), ghat)
+
+
+def test_fp4_tree_keeps_tangent_point():
+    """With MXFP4 storage plane j still passes through (r_j, L_j): c absorbs
+    the rounding of g."""
+    K, V, ref, Q = _rand_cache(256, 16, 4, 13)
+    ref = np.concatenate([ref, ref], axis=1)  # d = 128 (blocks of 32)
+    K = np.concatenate([K, K[::-1]], axis=1)
+    d = ref.shape[1]
+    tree = O.build_tree(K, ref, 4, 3, "fp4")
+    for lvl in tree:
+        assert lvl.scale.shape == lvl.L.shape + (d // 32,)
+        np.testing.assert_array_equal(lvl.ghat, O.round_mxfp4_rows(lvl.g)[0])
+        for j in range(4):
+            plane_j = lvl.c[:, j] + lvl.ghat[:, j] @ ref[j] / math.sqrt(d)
+            np.testing.assert_allclose(plane_j, lvl.L[:, j], rtol=0, atol=1e-12)
+
+
 def test_level2_weights_form_is_scored_from_its_own_keys():
     """Levels 1 and 2 held as weights (f64) over bf16 mean keys above: each
     level-2 node's plane j is H(w_j) + E_{w_j}[q . k / sqrt(d)] with w_j the
