@@ -124,8 +124,11 @@ def selection_bytes(cfg: zha.ZhaConfig, buf, n_tokens: int, T: int, logits: bool
     C, Lv, R, d = cfg.chunk, cfg.levels, cfg.n_ref, cfg.head_dim
     sizes = level_sizes(n_tokens, C, Lv)
     caches, QC = cfg.n_caches, cfg.q_per_kv * T
-    gsize = 1 if cfg.g_dtype == "fp8" else cfg.esize  # bytes per stored g element
-    node_bytes = R * d * gsize + 4 * R * (2 if cfg.g_dtype == "fp8" else 1)  # g, c (+ row scales)
+    if cfg.g_dtype == "fp4":  # E2M1 codes, one E8M0 scale per 32 values, c
+        node_bytes = R * d // 2 + R * (d // 32) + 4 * R
+    else:
+        gsize = 1 if cfg.g_dtype == "fp8" else cfg.esize  # bytes per stored g element
+        node_bytes = R * d * gsize + 4 * R * (2 if cfg.g_dtype == "fp8" else 1)  # g, c (+ row scales)
     QW = min(QC, 16)  # useful logits per key (rows are padded to 4 in memory)
     top = top or Lv  # routing starts here; the levels above are not read
     fused = cfg.weight_keys(2) > 0 and QC <= 4 and top >= 2
@@ -188,7 +191,10 @@ def tree_bytes_per_token(cfg):
     [R][C] (4RC) + L, c (8R) at the levels held as weights, else the
     mean-key node (g, L, c, + fp8 row scales)."""
     g8 = cfg.g_dtype == "fp8"
-    mean_node = cfg.n_ref * (cfg.head_dim * (1 if g8 else cfg.esize) + (12 if g8 else 8))
+    if cfg.g_dtype == "fp4":  # codes, block scales, L, c
+        mean_node = cfg.n_ref * (cfg.head_dim // 2 + cfg.head_dim // 32 + 8)
+    else:
+        mean_node = cfg.n_ref * (cfg.head_dim * (1 if g8 else cfg.esize) + (12 if g8 else 8))
     return sum(
         (cfg.n_ref * (4 * cfg.chunk + 8) if cfg.weight_keys(l) else mean_node) / (cfg.chunk**l)
         for l in range(1, cfg.levels + 1)
@@ -622,8 +628,9 @@ def main():
     ap.add_argument("--p-levels", default=None,
                     help="depth-aware schedule: comma-separated p per level, level 1 first (overrides --p)")
     ap.add_argument("--top-level", type=int, default=0, help="level routing starts from (0 = the tree's top)")
-    ap.add_argument("--g-dtype", default="kv", choices=["kv", "fp8"],
-                    help="storage of the mean keys g: the KV dtype (default) or FP8 E4M3 with row scales")
+    ap.add_argument("--g-dtype", default="kv", choices=["kv", "fp8", "fp4"],
+                    help="storage of the mean keys g: the KV dtype (default), FP8 E4M3 with row scales, or "
+                         "OCP MXFP4 (with levels 1-2 as weights)")
     ap.add_argument("--no-logits", action="store_true",
                     help="attention recomputes every logit from K instead of reading the route's level-1 logits")
     ap.add_argument("--prefill", type=int, default=0,

@@ -101,8 +101,15 @@ enum zha_leaf_form { ZHA_LEAF_MEAN = 0, ZHA_LEAF_WEIGHTS = 1, ZHA_LEAF_WEIGHTS2 
  *     nearest even, with s_j = 2^(ceil(log2 max_e |g_je|) - 8) (1 for a zero
  *     row) in the tree's scale block; c_j uses the stored values.  Halves
  *     the bytes routing reads per node.  Needs kv_dtype ZHA_BF16.
+ *   ZHA_G_FP4: the same variant read as OCP MXFP4: each row j of g in
+ *     blocks of 32 consecutive elements of d, each block an E8M0 scale
+ *     2^(floor(log2 max |block|) - 2) (2^-127 for a zero block) times FP4
+ *     E2M1 values (round to nearest even, saturating at 6); c_j uses the
+ *     stored values.  A quarter of the bf16 bytes plus one scale byte per 32
+ *     elements.  Needs kv_dtype ZHA_BF16, head_dim 128 and
+ *     ZHA_LEAF_WEIGHTS2 (levels >= 3 store MXFP4).
  */
-enum zha_g_dtype { ZHA_G_KV = 0, ZHA_G_FP8 = 2 };
+enum zha_g_dtype { ZHA_G_KV = 0, ZHA_G_FP8 = 2, ZHA_G_FP4 = 4 };
 
 /* Flags of zha_attend. */
 enum zha_attend_flags {
@@ -154,6 +161,12 @@ typedef struct zha_config {
  * kg = (e % 32) / 8 lives at byte ((s / 2) * 4 * R + kg * R + j) * 16 +
  * (s % 2) * 8 + e % 8 (one 16-byte load yields two MFMA steps), and a fourth
  * block s: [caches][node_cap][R] fp32 holds the row scales (s_offset).
+ * With ZHA_G_FP4 those levels hold R x d / 2 bytes per node: element (j, e)
+ * with MFMA step s = e / 32 and k-group kg = (e % 32) / 8 is nibble e % 2
+ * (low first) of byte (kg * R + j) * 16 + s * 4 + (e % 8) / 2 (one 16-byte
+ * load yields the four steps of d = 128), and the scale block s:
+ * [caches][node_cap][R][d / 32] holds the E8M0 block scales (byte b means
+ * 2^(b - 127)).
  * Offsets are bytes from the tree base; every block is 256-byte aligned.
  */
 typedef struct zha_tree_layout {
@@ -165,7 +178,7 @@ typedef struct zha_tree_layout {
   int64_t c_offset[ZHA_MAX_LEVELS];
   int64_t g_bytes[ZHA_MAX_LEVELS]; /* bytes of one node's g (or w) block, per level */
   int64_t total_bytes;  /* size of the caller's tree buffer */
-  int64_t s_offset[ZHA_MAX_LEVELS]; /* fp8 row scales per level, or -1 */
+  int64_t s_offset[ZHA_MAX_LEVELS]; /* fp8 row scales or fp4 block scales per level, or -1 */
   int64_t scratch_offset; /* fp32 children of up to 2 top nodes per cache, used by
                              zha_append to split its spans over more workgroups;
                              -1 when the geometry does not split */

@@ -26,8 +26,8 @@ kept mass >= P = ceil(p * M) in the GPU's fixed-point masses, minimality
 rule, and the counts.
 
 eps_score (below) bounds the GPU-oracle score error that the tests accept:
-5e-5 when g is effectively fp32; with bf16 or fp8 storage it bounds two
-rounding flips of g at the level's largest magnitudes.
+5e-5 when g is effectively fp32; with bf16, fp8 or MXFP4 storage it bounds
+two rounding flips of g at the level's largest magnitudes.
 """
 from __future__ import annotations
 
@@ -58,8 +58,9 @@ def eps_score(dtype: str, q: np.ndarray, level) -> float:
         return 5e-5
     d = q.shape[-1]
     gmax = float(np.abs(level.ghat).max()) if level.ghat.size else 0.0
-    # relative spacing of the stored format: bf16 2^-7, fp8 E4M3 2^-3
-    rel = 2.0**-3 if dtype == "fp8" else 2.0**-7
+    # relative spacing of the stored format: bf16 2^-7, fp8 E4M3 2^-3; MXFP4 at
+    # most 2 scale units where the block max is at least 4 units: 1/2 of the max
+    rel = {"fp8": 2.0**-3, "fp4": 0.5}.get(dtype, 2.0**-7)
     return 2.0 * (float(np.abs(q).max()) + 1.0) * gmax * rel / np.sqrt(d) + 5e-5
 
 

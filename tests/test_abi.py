@@ -107,6 +107,21 @@ def test_tree_layout_fp8():
         assert tl.total_bytes < kv.total_bytes
 
 
+def test_tree_layout_mxfp4():
+    """MXFP4 levels (>= 3 with levels 1-2 as weights): R*d/2 bytes of codes per
+    node and an E8M0 scale block of R*d/32 bytes per node."""
+    tl = zha.tree_layout(cfg_deep(leaf_form="weights2", g_dtype="fp4"))
+    w2 = zha.tree_layout(cfg_deep(leaf_form="weights2"))
+    assert tl.g_bytes[0] == tl.g_bytes[1] == 16 * 4 * 4
+    assert tl.s_offset[0] == tl.s_offset[1] == -1
+    for i in range(2, 6):
+        assert tl.g_bytes[i] == 16 * 128 // 2
+        assert tl.s_offset[i] % 256 == 0 and tl.s_offset[i] > tl.c_offset[i]
+        nxt = tl.g_offset[i + 1] if i + 1 < 6 else tl.total_bytes
+        assert nxt - tl.s_offset[i] >= 8 * tl.node_cap[i] * 16 * 4  # caches x nodes x R x d/32
+    assert tl.total_bytes < w2.total_bytes
+
+
 def test_route_layout_logits():
     assert zha.route_layout(cfg_deep(), 1).logits_floats == 0
     rl = zha.route_layout(cfg_deep(leaf_form="weights"), 1)
@@ -174,6 +189,10 @@ def test_route_layout_sizes():
         (dict(leaf_form="weights2", levels=2), zha.ZHA_ERR_UNSUPPORTED),
         (dict(leaf_form="weights2", chunk=8, levels=4), zha.ZHA_ERR_UNSUPPORTED),
         (dict(leaf_form="weights2", g_dtype="fp8"), 0),
+        (dict(leaf_form="weights2", g_dtype="fp4"), 0),
+        (dict(g_dtype="fp4"), zha.ZHA_ERR_UNSUPPORTED),
+        (dict(leaf_form="weights", g_dtype="fp4"), zha.ZHA_ERR_UNSUPPORTED),
+        (dict(leaf_form="weights2", g_dtype="fp4", head_dim=64), zha.ZHA_ERR_UNSUPPORTED),
         (dict(leaf_form="weights2", dtype="f32", head_dim=64, n_ref=4, levels=3), zha.ZHA_ERR_UNSUPPORTED),
     ],
 )

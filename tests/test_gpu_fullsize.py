@@ -69,8 +69,8 @@ def _levels(cfg, buf, N, qi):
 
 
 FORMS = ["weights2", "weights"]
-# the bench's form with fp8 rows from level 3 up (the low-precision router variant)
-FORMS_1M = FORMS + ["weights2-fp8"]
+# the bench's form with fp8 rows or MXFP4 blocks from level 3 up (the low-precision router variants)
+FORMS_1M = FORMS + ["weights2-fp8", "weights2-fp4"]
 # the bench's default run: 2 warm-up + 8 timed append steps sized into the capacity
 BENCH_STEPS = 10
 
@@ -102,8 +102,8 @@ def test_deep1m_full_size_two_caches(form):
     leaf_form, _, g8 = form.partition("-")
     cfg = _cfg(w, N0 + BENCH_STEPS * A, leaf_form)
     if g8:
-        cfg.g_dtype = "fp8"
-    gd = "fp8" if g8 else w.dtype
+        cfg.g_dtype = g8  # fp8 rows or MXFP4 blocks from level 3 up
+    gd = g8 or w.dtype
     _say(f"deep1m {form}: generating and running the bench step")
     b = W.make_batch(w, device="cuda", capacity=cfg.capacity, append_steps=1)
     tree, buf, out, lse = _run_step(cfg, b, N0, A, T, p)

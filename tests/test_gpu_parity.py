@@ -137,6 +137,7 @@ CACHED_CASES = [
     ("w2-qg8-d64-C4", dict(batch=1, n_kv_heads=2, q_per_kv=3, head_dim=64, n_ref=5, chunk=4, levels=3, capacity=6000, leaf_form="weights2"), 2, 5995, 0.8),
     ("w2-qg4-d128-R1", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=1, chunk=4, levels=4, capacity=9000, leaf_form="weights2"), 1, 8990, 0.8),
     ("w2-fp8-qg4-d128-C4", dict(batch=2, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=5, capacity=9000, leaf_form="weights2", g_dtype="fp8"), 1, 8998, 0.9),
+    ("w2-fp4-qg4-d128-C4", dict(batch=2, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=5, capacity=9000, leaf_form="weights2", g_dtype="fp4"), 1, 8998, 0.9),
 ]
 
 
@@ -166,7 +167,7 @@ def test_attend_cached_logits_matches_oracle(name, kw, T, N, p, flags):
             b, h = divmod(cache, cfg.n_kv_heads)
             Kn, rn = np64(K[b, h, :N]), np64(ref[h])
             l2d = "f64" if cfg.weight_keys(2) else None
-            gd = "fp8" if cfg.g_dtype == "fp8" else cfg.dtype
+            gd = cfg.g_dtype if cfg.g_dtype in ("fp8", "fp4") else cfg.dtype
             to = O.build_tree(Kn, rn, cfg.chunk, cfg.levels, gd, keep_g=False, leaf_dtype="f64", level2_dtype=l2d)
             for ql in range(QC):
                 bits, scores = gpu_levels(cfg, buf, N, cache * QC + ql)
@@ -220,6 +221,9 @@ BUILD_CASES = [
     # per lane) and d = 64 (4 per lane), trailing partial nodes, a partial second top span
     ("w2-fp8-d128-r16-l6", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=6, dtype="bf16", capacity=9000, leaf_form="weights2", g_dtype="fp8"), 8192 + 4 * 37 + 2),
     ("w2-fp8-d64-r5-l4", dict(batch=2, n_kv_heads=1, q_per_kv=2, head_dim=64, n_ref=5, chunk=4, levels=4, dtype="bf16", capacity=5000, leaf_form="weights2", g_dtype="fp8"), 4096 + 64 * 3 + 16 * 2 + 4 * 3 + 1),
+    # levels 1 and 2 as weights, OCP MXFP4 from level 3 up (d = 128): R = 16 and R = 5, ragged
+    ("w2-fp4-d128-r16-l6", dict(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=6, dtype="bf16", capacity=9000, leaf_form="weights2", g_dtype="fp4"), 8192 + 4 * 37 + 2),
+    ("w2-fp4-d128-r5-l4", dict(batch=2, n_kv_heads=1, q_per_kv=2, head_dim=128, n_ref=5, chunk=4, levels=4, dtype="bf16", capacity=5000, leaf_form="weights2", g_dtype="fp4"), 4096 + 64 * 3 + 16 * 2 + 4 * 3 + 1),
 ]
 APPEND_CASES = [c for c in BUILD_CASES if c[0] != "c1-f32"]
 
@@ -243,7 +247,7 @@ def check_tree(cfg, tree, K, ref, N):
         for h in range(cfg.n_kv_heads):
             cache = b * cfg.n_kv_heads + h
             Kn, rn = np64(K[b, h, :N]), np64(ref[h])
-            gd = "fp8" if cfg.g_dtype == "fp8" else cfg.dtype
+            gd = cfg.g_dtype if cfg.g_dtype in ("fp8", "fp4") else cfg.dtype
             to = O.build_tree(Kn, rn, cfg.chunk, cfg.levels, gd, n_tokens=N,
                               leaf_dtype="f64" if cfg.weights else None,
                               level2_dtype="f64" if cfg.weight_keys(2) else None)
@@ -290,6 +294,8 @@ def check_tree(cfg, tree, K, ref, N):
                     np.testing.assert_allclose(gg, lvl.g, rtol=0, atol=2e-6 * scale, err_msg=f"g level {lv}")
                 elif cfg.g_dtype == "fp8":
                     check_fp8_level(lv, np64(got["g"][cache]), np64(got["scale"][cache]), lvl)
+                elif cfg.g_dtype == "fp4":
+                    check_fp4_level(lv, np64(got["g"][cache]), np64(got["scale"][cache]), lvl)
                 else:
                     mism = gg != lvl.ghat
                     # at most 1e-3 of the values, and never fewer than 2 allowed (a level of a few
@@ -335,6 +341,31 @@ def check_fp8_level(lv, gg, gs, lvl):
         dev = np.abs(a[mism] - b[mism])
         bad = dev > spacing + 4e-6 * row
         assert not bad.any(), f"level {lv}: {int(bad.sum())} fp8 flips beyond one spacing"
+
+
+def check_fp4_level(lv, gg, gs, lvl):
+    """MXFP4 blocks: the GPU's E8M0 scale equals the oracle's except where the
+    block max sits at a power of two (fp32 and fp64 may then pick neighbouring
+    exponents); E2M1 codes differ only at rounding boundaries, by one spacing
+    (0.5, 1 or 2 scale units), on at most 1e-3 of the elements."""
+    n, R, d = gg.shape
+    m = np.abs(lvl.g).reshape(n, R, d // 32, 32).max(axis=-1)
+    f, _ = np.frexp(np.maximum(m, 1e-300))
+    near_pow2 = np.abs(f - 0.5) < 1e-5
+    same = gs == lvl.scale
+    assert np.all(same | near_pow2), f"level {lv}: {int((~same & ~near_pow2).sum())} block scales differ"
+    assert np.all(np.log2(gs) == np.round(np.log2(gs)))
+    blk = np.repeat(same, 32, axis=-1)
+    sc = np.repeat(gs, 32, axis=-1)
+    a, b = gg[blk], lvl.ghat[blk]
+    mism = a != b
+    frac = mism.mean() if mism.size else 0.0
+    assert frac <= 1e-3, f"level {lv}: {frac:.2e} of MXFP4 g differ"
+    if mism.any():
+        u = np.maximum(np.abs(a[mism]), np.abs(b[mism])) / sc[blk][mism]
+        spacing = np.where(u <= 2, 0.5, np.where(u <= 4, 1.0, 2.0)) * sc[blk][mism]
+        bad = np.abs(a[mism] - b[mism]) > spacing * (1 + 1e-6)
+        assert not bad.any(), f"level {lv}: {int(bad.sum())} MXFP4 flips beyond one spacing"
 
 
 @pytest.mark.parametrize("name,kw,N", BUILD_CASES, ids=[c[0] for c in BUILD_CASES])
@@ -461,13 +492,14 @@ ROUTE_WORKLOADS = [
     ("deep32k", 1, "mean", 6, "fp8"),
     ("deep32k", 2, "weights2", 6, "kv"),
     ("deep32k", 2, "weights2", 6, "fp8"),
+    ("deep32k", 2, "weights2", 6, "fp4"),
 ]
 
 
 @pytest.mark.parametrize(
     "wname,n_caches_checked,leaf_form,q_per_cache,g_dtype",
     ROUTE_WORKLOADS,
-    ids=[f"{r[0]}-{r[2]}" + ("-fp8" if r[4] == "fp8" else "") for r in ROUTE_WORKLOADS],
+    ids=[f"{r[0]}-{r[2]}" + ("" if r[4] == "kv" else "-" + r[4]) for r in ROUTE_WORKLOADS],
 )
 def test_route_and_attend_match_oracle(wname, n_caches_checked, leaf_form, q_per_cache, g_dtype):
     w = W.WORKLOADS[wname]
@@ -489,7 +521,7 @@ def test_route_and_attend_match_oracle(wname, n_caches_checked, leaf_form, q_per
         Kn, Vn, rn = np64(batch.K[b, h, :N]), np64(batch.V[b, h, :N]), np64(batch.ref[h])
         leaf_dtype = "f64" if cfg.weights else None
         l2d = "f64" if cfg.weight_keys(2) else None
-        gd = "fp8" if g_dtype == "fp8" else cfg.dtype
+        gd = g_dtype if g_dtype in ("fp8", "fp4") else cfg.dtype
         to = O.build_tree(Kn, rn, cfg.chunk, cfg.levels, gd, keep_g=False, leaf_dtype=leaf_dtype, level2_dtype=l2d)
         qis = list(range(QC)) if q_per_cache >= QC else sorted(rng.choice(QC, q_per_cache, replace=False).tolist())
         for qi_local in qis:

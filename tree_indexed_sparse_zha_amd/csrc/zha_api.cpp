@@ -48,10 +48,12 @@ int check_config(const zha_config* c) {
   if (c->leaf_form == ZHA_LEAF_WEIGHTS &&
       (c->kv_dtype != ZHA_BF16 || (c->chunk != 4 && c->chunk != 8 && c->chunk != 16)))
     return fail(ZHA_ERR_UNSUPPORTED, "the leaf weights form needs bf16 and chunk 4, 8 or 16");
-  if (c->g_dtype != ZHA_G_KV && c->g_dtype != ZHA_G_FP8)
+  if (c->g_dtype != ZHA_G_KV && c->g_dtype != ZHA_G_FP8 && c->g_dtype != ZHA_G_FP4)
     return fail(ZHA_ERR_ARG, "g_dtype %d unknown", c->g_dtype);
   if (c->g_dtype == ZHA_G_FP8 && c->kv_dtype != ZHA_BF16)
     return fail(ZHA_ERR_UNSUPPORTED, "fp8 g needs bf16 keys");
+  if (c->g_dtype == ZHA_G_FP4 && (c->kv_dtype != ZHA_BF16 || c->head_dim != 128 || c->leaf_form != ZHA_LEAF_WEIGHTS2))
+    return fail(ZHA_ERR_UNSUPPORTED, "MXFP4 g needs bf16 keys, head_dim 128 and levels 1-2 held as weights");
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(ZHA_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", c->head_dim);
   if (c->n_ref > 16) return fail(ZHA_ERR_UNSUPPORTED, "n_ref %d unsupported (1..16)", c->n_ref);
@@ -116,9 +118,11 @@ void fill_tree_layout(const zha_config* c, zha_tree_layout* out) {
     if (l > 0) n = cdiv(n, c->chunk);
     const int wk = weight_keys(c, l);
     const bool fp8 = wk == 0 && c->g_dtype == ZHA_G_FP8;
+    const bool fp4 = wk == 0 && c->g_dtype == ZHA_G_FP4;
     // weights [R][wk] fp32, or at level 2 of ZHA_LEAF_WEIGHTS2 the child shares [R][C]
-    out->g_bytes[l] = wk ? (int64_t)c->n_ref * (l == 1 ? c->chunk : wk) * 4
-                         : (int64_t)c->n_ref * c->head_dim * (fp8 ? 1 : esize(c->kv_dtype));
+    out->g_bytes[l] = wk    ? (int64_t)c->n_ref * (l == 1 ? c->chunk : wk) * 4
+                      : fp4 ? (int64_t)c->n_ref * c->head_dim / 2
+                            : (int64_t)c->n_ref * c->head_dim * (fp8 ? 1 : esize(c->kv_dtype));
     out->node_cap[l] = n;
     out->g_offset[l] = off;
     off = align256(off + caches * n * out->g_bytes[l]);
@@ -127,9 +131,9 @@ void fill_tree_layout(const zha_config* c, zha_tree_layout* out) {
     out->c_offset[l] = off;
     off = align256(off + caches * n * c->n_ref * 4);
     out->s_offset[l] = -1;
-    if (fp8) {
+    if (fp8 || fp4) {  // fp32 row scales, or one E8M0 byte per 32 elements of a row
       out->s_offset[l] = off;
-      off = align256(off + caches * n * c->n_ref * 4);
+      off = align256(off + caches * n * c->n_ref * (fp8 ? 4 : c->head_dim / 32));
     }
   }
   for (int l = c->levels; l < ZHA_MAX_LEVELS; ++l) out->s_offset[l] = -1;
@@ -163,7 +167,12 @@ void fill_geom(const zha_config* c, const zha_tree_layout& tl, zha::TreeGeom* g)
     g->L_off[l] = tl.L_offset[l];
     g->c_off[l] = tl.c_offset[l];
     g->s_off[l] = tl.s_offset[l];
-    if (tl.s_offset[l] >= 0) g->g8 |= 1u << l;
+    if (tl.s_offset[l] >= 0) {
+      if (c->g_dtype == ZHA_G_FP4)
+        g->g4 |= 1u << l;
+      else
+        g->g8 |= 1u << l;
+    }
   }
   g->span_len[0] = 1;
   for (int l = 1; l <= c->levels; ++l) g->span_len[l] = g->span_len[l - 1] * c->chunk;
@@ -525,6 +534,7 @@ static int do_route(const zha_config* cfg, const void* tree, int64_t n_tokens, c
     sa.gscale = tl.s_offset[l] >= 0
                     ? reinterpret_cast<const float*>(static_cast<const char*>(tree) + tl.s_offset[l])
                     : nullptr;
+    sa.gfmt = tl.s_offset[l] < 0 ? 0 : (cfg->g_dtype == ZHA_G_FP4 ? 2 : 1);
     sa.node_cap = tl.node_cap[l];
     sa.n_nodes = n[l];
     sa.R = cfg->n_ref;

@@ -485,8 +485,11 @@ __global__ __launch_bounds__(64 * W) void k_build_span(BuildArgs A) {
 // (L, mass 1, fp32 mean g); the append split (sub-span pass, then the top
 // node from the stored fp32 children) therefore reproduces a fresh build bit
 // for bit when both of its passes also run here.
-template <int D, int NU, int C, bool G8 = false>
+template <int D, int NU, int C, int GF = 0>
 __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
+  constexpr bool G8 = GF == 1;  // levels written by put_node hold fp8 rows
+  constexpr bool G4 = GF == 2;  // ... or MXFP4 blocks (d = 128)
+  static_assert(!G4 || D == 128, "MXFP4 rows need d = 128 (a 32-block is four lanes of a wave)");
   static_assert(C == 4 || C == 8, "chunk of 4 or 8 keys");
   constexpr int RL = C == 4 ? 3 : 2;  // level of a round's node (64 keys)
   constexpr int LPL = C / 4;          // lanes of one plane sharing a leaf
@@ -536,11 +539,44 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
   // s_j * e4m3(g_j / s_j), s_j = 2^(ceil(log2 max_d |g_jd|) - 8) (1 for a
   // zero row): the row's maximum is gathered over the four waves through
   // LDS (one barrier; every lane of the workgroup calls put_node together).
+  // With MXFP4 (G4) each block of 32 values of d is the four lanes g = 0..3
+  // of one wave: its E8M0 scale 2^(floor(log2 max) - 2) comes from two
+  // shuffles, and the hardware conversion rounds g / scale to E2M1 (nearest
+  // even, saturating at 6).
   auto put_node = [&](int lvl, int64_t node, float L, const float* gv, int slot) {
-    uint32_t wd[VPL / 2];  // bf16 pairs, or (G8) E4M3 codes in wd[0 .. VPL / 4)
+    uint32_t wd[VPL / 2];  // bf16 pairs, (G8) E4M3 codes in wd[0 .. VPL / 4) or (G4) E2M1 codes in wd[0]
     float gr[VPL];         // the stored values
     float scl = 1.f;
-    if constexpr (G8) {
+    uint32_t e8 = 0u;      // G4: the E8M0 byte of this lane's block
+    if constexpr (G4) {
+      float mx = 0.f;
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) mx = fmaxf(mx, fabsf(gv[e]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const int ex = (int)(__float_as_uint(mx) >> 23) & 255;  // floor(log2 mx) = ex - 127 for normal mx
+      const int es = ex == 0 ? -127 : max(ex - 129, -127);
+      e8 = (uint32_t)(es + 127);
+      scl = __uint_as_float(e8 == 0u ? 0x00400000u : e8 << 23);  // 2^es
+      uint32_t w4 = 0u;
+      w4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w4, gv[0], gv[1], scl, 0);
+      w4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w4, gv[2], gv[3], scl, 1);
+      w4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w4, gv[4], gv[5], scl, 2);
+      w4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w4, gv[6], gv[7], scl, 3);
+      wd[0] = w4;
+      const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w4, scl, 0);
+      const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w4, scl, 1);
+      const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w4, scl, 2);
+      const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w4, scl, 3);
+      gr[0] = (float)p0[0];
+      gr[1] = (float)p0[1];
+      gr[2] = (float)p1[0];
+      gr[3] = (float)p1[1];
+      gr[4] = (float)p2[0];
+      gr[5] = (float)p2[1];
+      gr[6] = (float)p3[0];
+      gr[7] = (float)p3[1];
+    } else if constexpr (G8) {
       float mx = 0.f;
 #pragma unroll
       for (int e = 0; e < VPL; ++e) mx = fmaxf(mx, fabsf(gv[e]));
@@ -580,7 +616,13 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
     if (g == 0) dotp[slot][wave][j] = dot;
     if (j < R) {
       const int64_t nidx = (int64_t)cache * geo.node_cap[lvl - 1] + node;
-      if constexpr (G8) {
+      if constexpr (G4) {
+        // lane (j, g) of wave w holds d = 32w + 8g .. +7: MFMA step w, k-group g;
+        // its 4 code bytes at (g * R + j) * 16 + 4w, its block's scale byte at [j][w]
+        char* gb = A.tree + geo.g_off[lvl - 1] + nidx * R * (D / 2) + ((int64_t)g * R + j) * 16 + wave * 4;
+        *reinterpret_cast<uint32_t*>(gb) = wd[0];
+        if (g == 0) (A.tree + geo.s_off[lvl - 1])[(nidx * R + j) * (D / 32) + wave] = (char)e8;
+      } else if constexpr (G8) {
         // byte of (j, d): MFMA step st = d / 32, k-group kg = (d % 32) / 8, at
         // ((st / 2) * 4R + kg * R + j) * 16 + (st % 2) * 8 + d % 8
         const int st = d0 / 32, kg = (d0 % 32) / 8;
@@ -990,31 +1032,33 @@ hipError_t dispatch_leaf(const BuildArgs& a, dim3 grid, hipStream_t s) {
   }
 }
 
-template <int D, int C, bool G8>
+template <int D, int C, int GF>
 hipError_t dispatch_mf_c(const BuildArgs& a, dim3 grid, hipStream_t s) {
   const int nu = a.merge_top ? 0 : a.top_level - (C == 4 ? 3 : 2);
   switch (nu) {
-    case 0: hipLaunchKernelGGL((k_build_mf<D, 0, C, G8>), grid, dim3(256), 0, s, a); break;
-    case 1: hipLaunchKernelGGL((k_build_mf<D, 1, C, G8>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_build_mf<D, 2, C, G8>), grid, dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_build_mf<D, 3, C, G8>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_build_mf<D, 4, C, G8>), grid, dim3(256), 0, s, a); break;
-    case 5: hipLaunchKernelGGL((k_build_mf<D, 5, C, G8>), grid, dim3(256), 0, s, a); break;
+    case 0: hipLaunchKernelGGL((k_build_mf<D, 0, C, GF>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_build_mf<D, 1, C, GF>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_build_mf<D, 2, C, GF>), grid, dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_build_mf<D, 3, C, GF>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_build_mf<D, 4, C, GF>), grid, dim3(256), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((k_build_mf<D, 5, C, GF>), grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-// fp8 rows are built here only above levels 1-2 held as weights (chunk 4):
-// then every level k_build_mf writes through put_node is fp8
+// fp8 and MXFP4 rows are built here only above levels 1-2 held as weights
+// (chunk 4): then every level k_build_mf writes through put_node holds them
 template <int D>
 hipError_t dispatch_mf(const BuildArgs& a, dim3 grid, hipStream_t s) {
-  if (a.geo.g8) {
+  if (a.geo.g8 || a.geo.g4) {
     if (a.geo.C != 4 || !a.geo.w2) return hipErrorInvalidValue;
-    return dispatch_mf_c<D, 4, true>(a, grid, s);
+    if (a.geo.g8) return dispatch_mf_c<D, 4, 1>(a, grid, s);
+    if constexpr (D == 128) return dispatch_mf_c<D, 4, 2>(a, grid, s);
+    return hipErrorInvalidValue;
   }
-  if (a.geo.C == 8) return dispatch_mf_c<D, 8, false>(a, grid, s);
-  if (a.geo.C == 4) return dispatch_mf_c<D, 4, false>(a, grid, s);
+  if (a.geo.C == 8) return dispatch_mf_c<D, 8, 0>(a, grid, s);
+  if (a.geo.C == 4) return dispatch_mf_c<D, 4, 0>(a, grid, s);
   return hipErrorInvalidValue;
 }
 

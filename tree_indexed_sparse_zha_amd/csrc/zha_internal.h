@@ -47,6 +47,7 @@ struct TreeGeom {
   int64_t c_off[kMaxLevels];
   int64_t s_off[kMaxLevels];  // fp8 row scales per level, or -1
   uint32_t g8;                // bit l-1: level l stores g as fp8 E4M3 with row scales
+  uint32_t g4;                // bit l-1: level l stores g as MXFP4 (E2M1, E8M0 scale per 32 of d)
   int64_t span_len[kMaxLevels + 1];  // span_len[l] = C^l tokens covered by a level-l node
 };
 
@@ -89,7 +90,8 @@ __host__ __device__ inline int64_t spine_record(int64_t cache, int64_t k, int lv
 struct ScoreArgs {
   const char* g;         // level base of g
   const float* c;        // level base of c
-  const float* gscale;   // level base of the fp8 row scales, or nullptr (g in the KV dtype)
+  const float* gscale;   // level base of the fp8 row scales or MXFP4 block scales, or nullptr (KV dtype)
+  int gfmt;              // g storage of this level: 0 KV dtype, 1 fp8, 2 MXFP4
   int64_t node_cap;      // nodes per cache at this level
   int64_t n_nodes;       // valid nodes per cache at this level
   int R, C, D, H, G, T, QC;  // QC = G * T queries per cache

@@ -145,11 +145,17 @@ __device__ __forceinline__ unsigned long long chunk_bits(const ScoreArgs& A, int
   return mb;
 }
 
-// G8: g stored as fp8 E4M3 with a power-of-two scale per row; each 16-byte
-// load holds two MFMA steps, converted to bf16 with the row's scale applied
-// (exact: E4M3 values times powers of two are bf16 values).
-template <int D, bool G8>
+// GF = 1: g stored as fp8 E4M3 with a power-of-two scale per row; each
+// 16-byte load holds two MFMA steps, converted to bf16 with the row's scale
+// applied (exact: E4M3 values times powers of two are bf16 values).
+// GF = 2: g stored as MXFP4; one 16-byte load holds the four steps of
+// d = 128, each step's 8 E2M1 codes converted to bf16 times its block's
+// E8M0 scale (exact as well).
+template <int D, int GF>
 __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs A) {
+  constexpr bool G8 = GF == 1;  // fp8 rows with fp32 row scales
+  constexpr bool G4 = GF == 2;  // MXFP4: E2M1 codes, an E8M0 scale per 32 values of d
+  static_assert(!G4 || D == 128, "MXFP4 rows need d = 128");
   constexpr int NS = D / 32;  // MFMA k-steps of 32 bf16
   constexpr int TILE = 64;
   constexpr int NB = 4;       // nodes per batch
@@ -176,7 +182,7 @@ __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs A) {
       for (int s = 0; s < NS; ++s) bq[s] = as_bf16x8(make_uint4(0, 0, 0, 0));
     }
   }
-  const int64_t gnode = (int64_t)R * D * (G8 ? 1 : 2);
+  const int64_t gnode = G4 ? (int64_t)R * D / 2 : (int64_t)R * D * (G8 ? 1 : 2);
   const char* gcache = A.g + (int64_t)cache * A.node_cap * gnode;
   const float* ccache = A.c + (int64_t)cache * A.node_cap * R;
   const int jrow = lane & 15;
@@ -187,9 +193,13 @@ __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs A) {
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) anybits |= (uint32_t)__shfl_xor((int)anybits, o);
 
-  // raw 16-byte loads per node and lane: NS pieces (bf16) or NS / 2 (fp8)
-  constexpr int NL = G8 ? NS / 2 : NS;
+  // raw 16-byte loads per node and lane: NS pieces (bf16), NS / 2 (fp8) or 1
+  // (MXFP4: the four steps of lane (row, k-group) in one piece)
+  constexpr int NL = G4 ? 1 : (G8 ? NS / 2 : NS);
   const float* scache = G8 ? A.gscale + (int64_t)cache * A.node_cap * R : nullptr;
+  // MXFP4: the 4 E8M0 bytes of a row (one per step), as one word
+  const uint32_t* s4cache =
+      G4 ? reinterpret_cast<const uint32_t*>(A.gscale) + (int64_t)cache * A.node_cap * R : nullptr;
   auto load_batch = [&](int u0, uint4 (*af)[NL], float (*cv)[4], float* sv) {
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
@@ -201,6 +211,7 @@ __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs A) {
       for (int s = 0; s < NL; ++s)
         af[k][s] = live && jrow < R ? ld16(gn + ((int64_t)(4 * s + kg) * R + jrow) * 16) : make_uint4(0, 0, 0, 0);
       if constexpr (G8) sv[k] = live && jrow < R ? scache[m * R + jrow] : 0.f;
+      if constexpr (G4) sv[k] = __uint_as_float(live && jrow < R ? s4cache[m * R + jrow] : 0u);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int jj = 4 * kg + i;
@@ -224,7 +235,16 @@ __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs A) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           uint4 op;
-          if constexpr (G8) {
+          if constexpr (G4) {
+            // 8 E2M1 codes of step s (word s of the piece) -> bf16 x 2^(e8 - 127)
+            const uint32_t w = s == 0 ? af[k][0].x : s == 1 ? af[k][0].y : s == 2 ? af[k][0].z : af[k][0].w;
+            const uint32_t e8 = (__float_as_uint(sv[k]) >> (8 * s)) & 255u;
+            const float sf = __uint_as_float(e8 == 0u ? 0x00400000u : e8 << 23);
+            op.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sf, 0));
+            op.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sf, 1));
+            op.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sf, 2));
+            op.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sf, 3));
+          } else if constexpr (G8) {
             // 8 E4M3 codes of step s (words x, y or z, w of the pair's slot) -> bf16 x scale
             const uint32_t w0 = (s & 1) ? af[k][s / 2].z : af[k][s / 2].x;
             const uint32_t w1 = (s & 1) ? af[k][s / 2].w : af[k][s / 2].y;
@@ -2536,11 +2556,14 @@ hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dty
 #undef ZHA_LW_Q
     } else if (dtype == 1) {
       dim3 grid((unsigned)((sa.n_nodes + 63) / 64), (unsigned)n_caches, (unsigned)((sa.QC + 15) / 16));
-      if (sa.gscale) {
+      if (sa.gscale && sa.gfmt == 2) {
+        if (sa.D != 128) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((k_score_bf16<128, 2>), grid, dim3(256), 0, s, sa);
+      } else if (sa.gscale) {
         if (sa.D == 128)
-          hipLaunchKernelGGL((k_score_bf16<128, true>), grid, dim3(256), 0, s, sa);
+          hipLaunchKernelGGL((k_score_bf16<128, 1>), grid, dim3(256), 0, s, sa);
         else
-          hipLaunchKernelGGL((k_score_bf16<64, true>), grid, dim3(256), 0, s, sa);
+          hipLaunchKernelGGL((k_score_bf16<64, 1>), grid, dim3(256), 0, s, sa);
       } else if (sa.R > 8 && sa.QC > 16 && (sa.n_nodes + 63) / 64 * n_caches >= kMqMinTiles) {
         dim3 gmq((unsigned)((sa.n_nodes + 63) / 64), (unsigned)n_caches,
                  (unsigned)((sa.QC + 16 * kMqBlocks - 1) / (16 * kMqBlocks)));
@@ -2566,9 +2589,9 @@ hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dty
           ZHA_SR(64);
 #undef ZHA_SR
       } else if (sa.D == 128) {
-        hipLaunchKernelGGL((k_score_bf16<128, false>), grid, dim3(256), 0, s, sa);
+        hipLaunchKernelGGL((k_score_bf16<128, 0>), grid, dim3(256), 0, s, sa);
       } else {
-        hipLaunchKernelGGL((k_score_bf16<64, false>), grid, dim3(256), 0, s, sa);
+        hipLaunchKernelGGL((k_score_bf16<64, 0>), grid, dim3(256), 0, s, sa);
       }
     } else {
       dim3 grid((unsigned)((sa.n_nodes + 3) / 4), (unsigned)n_caches);
@@ -2591,6 +2614,7 @@ hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dty
   else
     sel.kr_used = 1;
   if (sa.spine && level >= 2 && sa.n_nodes > 0) {
+    if (sa.gfmt == 2) return hipErrorInvalidValue;  // prefill takes no MXFP4 rows
     // prefill: each query's partial node of this level, scored from the spine
     ScoreArgs sp = sa;
     sp.kr_spine_slot = sel.kr_used;

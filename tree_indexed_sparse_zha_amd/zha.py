@@ -32,7 +32,8 @@ ZHA_F32, ZHA_BF16 = 0, 1
 ZHA_SINK, ZHA_LAST_CHUNK, ZHA_ALL_KEYS, ZHA_CAUSAL = 1, 2, 4, 8
 ZHA_LEAF_MEAN, ZHA_LEAF_WEIGHTS, ZHA_LEAF_WEIGHTS2 = 0, 1, 2
 LEAF_FORMS = {"mean": ZHA_LEAF_MEAN, "weights": ZHA_LEAF_WEIGHTS, "weights2": ZHA_LEAF_WEIGHTS2}
-ZHA_G_KV, ZHA_G_FP8 = 0, 2
+ZHA_G_KV, ZHA_G_FP8, ZHA_G_FP4 = 0, 2, 4
+G_DTYPES = {"kv": ZHA_G_KV, "fp8": ZHA_G_FP8, "fp4": ZHA_G_FP4}
 MAX_LEVELS = 8
 ZHA_NOALLOC_SCRATCH_BYTES = 32 << 20  # static scratch of zha_attend_noalloc (include/zha.h)
 
@@ -241,7 +242,7 @@ class ZhaConfig:
     dtype: str  # "f32" | "bf16"
     capacity: int
     leaf_form: str = "mean"  # "mean" | "weights" (level 1 holds weights) | "weights2" (levels 1 and 2)
-    g_dtype: str = "kv"  # "kv" (g in the KV dtype) | "fp8" (E4M3 with row scales)
+    g_dtype: str = "kv"  # "kv" (g in the KV dtype) | "fp8" (E4M3 with row scales) | "fp4" (OCP MXFP4)
 
     def c(self) -> Config:
         return Config(
@@ -254,7 +255,7 @@ class ZhaConfig:
             self.levels,
             ZHA_BF16 if self.dtype == "bf16" else ZHA_F32,
             LEAF_FORMS[self.leaf_form],
-            ZHA_G_FP8 if self.g_dtype == "fp8" else ZHA_G_KV,
+            G_DTYPES[self.g_dtype],
             self.capacity,
         )
 
@@ -570,6 +571,17 @@ def read_level(cfg: ZhaConfig, tree: torch.Tensor, level: int, n_nodes: Optional
         w = tree[gb : gb + caches * cap * R * wk * 4].view(torch.float32).view(caches, cap, R, wk)[:, :n]
         return {"w": w, "L": L, "c": c}
     sb = int(tl.s_offset[i])
+    if sb >= 0 and cfg.g_dtype == "fp4":
+        # E2M1 nibble (low first) of (j, e), step st = e // 32, k-group kg = (e % 32) // 8, in byte
+        # (kg * R + j) * 16 + st * 4 + (e % 8) // 2; block scales [R][d / 32] as E8M0 bytes
+        raw = tree[gb : gb + caches * cap * R * d // 2].view(caches, cap, -1)[:, :n].to(torch.int32)
+        nib = torch.stack([raw & 15, raw >> 4], dim=-1).reshape(caches, n, 4, R, 4, 8)  # [kg][j][st][e % 8]
+        table = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], device=tree.device)
+        vals = table[nib & 7] * torch.where(nib >= 8, -1.0, 1.0)
+        vals = vals.permute(0, 1, 3, 4, 2, 5).reshape(caches, n, R, d)  # [j][st][kg][e % 8] -> d
+        e8 = tree[sb : sb + caches * cap * R * (d // 32)].view(caches, cap, R, d // 32)[:, :n].to(torch.float32)
+        scale = torch.where(e8 == 0, torch.tensor(2.0**-127, device=tree.device), torch.exp2(e8 - 127.0))
+        return {"g": vals * scale.repeat_interleave(32, dim=-1), "scale": scale, "L": L, "c": c}
     if sb >= 0:
         # E4M3 byte of (j, e) with step s = e // 32, k-group kg = (e % 32) // 8 at
         # ((s // 2) * 4 * R + kg * R + j) * 16 + (s % 2) * 8 + e % 8
