@@ -546,11 +546,14 @@ def sweep_main(args):
     geometry, the other p of the 1M workload, and the other configurations
     (32K deep with 64 queries per head, 256K wide, 10M deep with its full
     build timed).  Each point: 2 warm-up + 4 timed steps, the flushed
-    replay with matched-N dense."""
+    replay with matched-N dense; crossover points append nothing, so each
+    decodes at its stated context length."""
+    import dataclasses
+
     points = []
     for n in (32768, 65536, 131072, 262144, 524288, 1048576, 2097152):
         points.append(("deep-crossover", "deep1m", n, None))
-    for n in (16384, 32768, 65536, 131072, 262144, 1048576, 4194304):
+    for n in (16384, 32768, 49152, 65536, 131072, 262144, 1048576, 4194304):
         points.append(("light-crossover", "light1m", n, None))
     points.append(("deep1m-p", "deep1m", None, 0.9))
     points.append(("deep1m-p", "deep1m", None, 0.99))
@@ -563,7 +566,8 @@ def sweep_main(args):
             continue
         w = W.WORKLOADS[wname]
         if n:
-            w = w.with_tokens(n)
+            # a crossover point decodes at its own context length: no appends between steps
+            w = dataclasses.replace(w.with_tokens(n), append_tokens=0)
         pp = p if p is not None else w.p[0]
         res = run_decode(w, pp, args, steps=4, warmup=2, log_prefix=f"[{kind}] ")
         line = frame(res, args, 4, 2, metric=f"sweep point ({kind}): routed decode queries/s against same-GPU dense")

@@ -303,8 +303,10 @@ int64_t zha_attend_workspace_bytes(const zha_config* cfg, int32_t T);
  *   K        device, [B][H][capacity][d] kv_dtype addressed by
  *            k_strides = {batch, head, token} in elements; each token row
  *            is d contiguous elements, 16-byte aligned.
- *   ref      device, [H][R][d] fp32 reference queries (bf16-representable
- *            values when kv_dtype is bf16).
+ *   ref      device, [H][R][d] fp32 reference queries.  With kv_dtype
+ *            bf16 every value is rounded to bf16 (nearest even) before use:
+ *            the tree is that of the bf16-rounded reference queries (the
+ *            logits r . k run on bf16 matrix cores).
  *   tree     device, zha_get_tree_layout(cfg).total_bytes bytes; overwritten for
  *            the nodes that exist at n_tokens.
  * Errors: NULL pointers, n_tokens < 0 or > capacity, misalignment.

@@ -379,6 +379,41 @@ def test_build_matches_oracle(name, kw, N):
     check_tree(cfg, tree, K, ref, N)
 
 
+REF_ROUNDING_CASES = [c for c in BUILD_CASES if c[0] in ("w2-d128-r16-l6", "c16-bf16-d64-weights", "deep-bf16-fp8")]
+
+
+@pytest.mark.parametrize("name,kw,N", REF_ROUNDING_CASES, ids=[c[0] for c in REF_ROUNDING_CASES])
+def test_build_takes_bf16_rounded_reference_queries(name, kw, N):
+    """Reference queries that are not bf16 values: with bf16 keys the tree is
+    that of the bf16-rounded reference queries (matrix-core logits and plane
+    offsets alike), checked against the oracle given round_bf16(ref); level 2
+    of the weights2 form is then routed (fused pass) teacher-forced."""
+    _say(f"bf16-rounded reference queries {name}")
+    cfg = zha.ZhaConfig(**kw)
+    K, _ = _segmented_keys(cfg, 7)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(8)
+    ref = torch.randn(cfg.n_kv_heads, cfg.n_ref, cfg.head_dim, generator=g, device="cuda")
+    assert not torch.equal(ref, ref.to(torch.bfloat16).float())
+    tree = zha.alloc_tree(cfg)
+    zha.build(cfg, K, ref, tree, N)
+    torch.cuda.synchronize()
+    ref_r = torch.from_numpy(O.round_bf16(np64(ref))).float().cuda()
+    check_tree(cfg, tree, K, ref_r, N)
+    if cfg.leaf_form == "weights2":
+        Q = torch.randn(cfg.batch, cfg.n_kv_heads, cfg.q_per_kv, 1, cfg.head_dim, generator=g,
+                        device="cuda").to(torch.bfloat16)
+        buf = zha.alloc_route(cfg, 1, logits=True)
+        zha.route(cfg, tree, N, Q, 1, 0.9, buf, K=K)
+        torch.cuda.synchronize()
+        Kn, rn = np64(K[0, 0, :N]), np64(ref_r[0])
+        to = O.build_tree(Kn, rn, cfg.chunk, cfg.levels, cfg.dtype, keep_g=False, leaf_dtype="f64", level2_dtype="f64")
+        for ql in range(cfg.q_per_kv):
+            bits, scores = gpu_levels(cfg, buf, N, ql)
+            PAR.check_route_teacher_forced(np64(Q[0, 0, ql, 0]), to, rn, cfg.chunk, 0.9, PAR.gpu_kept_from_bits(bits),
+                                           cfg.dtype, scores, leaf_dtype="f64", level2_dtype="f64")
+
+
 @pytest.mark.parametrize("name,kw,N", APPEND_CASES, ids=[c[0] for c in APPEND_CASES])
 def test_append_equals_build(name, kw, N):
     _say(f"append {name}")

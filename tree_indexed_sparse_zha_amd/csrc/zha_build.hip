@@ -79,14 +79,18 @@ __global__ __launch_bounds__(64 * W) void k_build_span(BuildArgs A) {
   const int64_t t1 = min(w0 + sub, tend);
   const float isd = A.inv_sqrt_d;
 
-  // reference query j, this lane's quarter of d
+  // reference query j, this lane's quarter of d (with bf16 keys, rounded
+  // to bf16: the tree is that of the bf16-rounded reference queries)
   float rj[NV];
   {
     const float* rp = A.ref + ((int64_t)h * R + (j < R ? j : 0)) * D;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int e = 0; e < E; ++e) rj[s * E + e] = (j < R) ? rp[(4 * s + dg) * E + e] : 0.f;
+      for (int e = 0; e < E; ++e) {
+        const float r = (j < R) ? rp[(4 * s + dg) * E + e] : 0.f;
+        rj[s * E + e] = sizeof(T) == 2 ? round_bf16f(r) : r;
+      }
   }
 
   __shared__ uint4 Ks_all[W][KB * PIECES];
@@ -525,7 +529,8 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
 
   for (int i = threadIdx.x; i < 16 * D; i += 256) {
     const int jr = i / D, d = i % D;
-    refL[jr][d] = jr < R ? A.ref[((int64_t)h * R + jr) * D + d] : 0.f;
+    // with bf16 keys the tree is that of the bf16-rounded reference queries
+    refL[jr][d] = jr < R ? round_bf16f(A.ref[((int64_t)h * R + jr) * D + d]) : 0.f;
   }
   __syncthreads();
   float rp[VPL];

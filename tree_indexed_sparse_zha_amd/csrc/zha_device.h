@@ -108,6 +108,8 @@ __device__ __forceinline__ float row_sum_stride4(float v) {
 // The rounded values of a bf16_pair word as fp32.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// x rounded to bf16 (nearest even), as fp32.
+__device__ __forceinline__ float round_bf16f(float x) { return bf16_lo(bf16_pair(x, 0.f)); }
 
 // Pack fp32 values of one piece, rounding to the storage type; also returns
 // the rounded values as fp32 in `rounded`.
