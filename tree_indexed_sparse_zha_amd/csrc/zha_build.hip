@@ -526,6 +526,7 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
   __shared__ float refL[16][GROW];
   __shared__ float dotp[kMaxLevels][4][16];
   __shared__ float rmax[kMaxLevels][4][16];  // fp8 levels: the waves' row maxima of a node's g
+  __shared__ uint4 refB[16][KROW];          // reference rows in bf16 (MFMA operands)
 
   for (int i = threadIdx.x; i < 16 * D; i += 256) {
     const int jr = i / D, d = i % D;
@@ -533,9 +534,6 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
     refL[jr][d] = jr < R ? round_bf16f(A.ref[((int64_t)h * R + jr) * D + d]) : 0.f;
   }
   __syncthreads();
-  float rp[VPL];
-#pragma unroll
-  for (int e = 0; e < VPL; ++e) rp[e] = refL[j][d0 + e];
 
   // node writers above level 2: this lane's D/16 values of g (rounded to
   // bf16), the wave's share of r . g into dotp[slot]; L and c are stored by
@@ -615,7 +613,7 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
     }
     float dot = 0.f;
 #pragma unroll
-    for (int e = 0; e < VPL; ++e) dot = fmaf(rp[e], gr[e], dot);
+    for (int e = 0; e < VPL; ++e) dot = fmaf(refL[j][d0 + e], gr[e], dot);
     dot += __shfl_xor(dot, 16);
     dot += __shfl_xor(dot, 32);
     if (g == 0) dotp[slot][wave][j] = dot;
@@ -695,16 +693,16 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
     return;
   }
 
-  // reference rows as bf16 MFMA A operands of the logits (exact: ref holds
-  // bf16 values)
-  bf16x8 afr[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
+  // reference rows as bf16 MFMA A operands of the logits (exact: refL holds
+  // bf16 values), kept in LDS (registers are the kernel's limit)
+  for (int i = threadIdx.x; i < 16 * PIECES; i += 256) {
+    const int jr = i / PIECES, pc = i % PIECES;
     float rr[8], dummy[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) rr[e] = refL[j][(4 * s + g) * 8 + e];
-    afr[s] = as_bf16x8(pack(rr, dummy, bf16_t()));
+    for (int e = 0; e < 8; ++e) rr[e] = refL[jr][pc * 8 + e];
+    refB[jr][pc] = pack(rr, dummy, bf16_t());
   }
+  __syncthreads();
 
   const bf16_t* Kc = reinterpret_cast<const bf16_t*>(A.K) + (int64_t)b * A.sb + (int64_t)h * A.sh;
   const int64_t nkeys = tend - t0;
@@ -754,8 +752,8 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < NS; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[s], as_bf16x8(Ks[wave][(lane & 15) * KROW + 4 * s + g]),
-                                                      acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(refB[lane & 15][4 * s + g]),
+                                                      as_bf16x8(Ks[wave][(lane & 15) * KROW + 4 * s + g]), acc, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) zs[wave][4 * g + i][lane & 15] = acc[i] * isd;
       wave_sync();
@@ -865,37 +863,53 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
       const float inv2 = 1.f / ps;
 #pragma unroll
       for (int s = 0; s < 4; ++s) P[s] *= inv2;  // normalised weights: the product is the mean
-      // g^T[d][j] = sum over keys k[key][d] P[j][key]: A = keys (row d = 16b +
-      // lane % 16, k = key 4g + s), B = P (k = key 4g + s, column j)
-      f32x4 G[NB];
-#pragma unroll
-      for (int blk = 0; blk < NB; ++blk) {
-        G[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int d = 16 * blk + (lane & 15);
+      // g^T[d][j] = sum over keys k[key][d] P[j][key] on the bf16 matrix cores
+      // (v_mfma_f32_16x16x16_bf16, the 16 keys as the contraction): A = keys
+      // (row d = 16b + lane % 16, k = key 4g + s: exact in bf16), B = P (k =
+      // key 4g + s, column j: this lane's own four weights).  P is split into
+      // three bf16 terms, hi + mid + lo = P to within 2^-27 relative, so the
+      // three products accumulate the fp32 weighted sum.
+      s16x4 pw[3];
+      {
+        float hi[4], mid[4], lo[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const float kv = __uint_as_float((uint32_t)Ks16[((4 * g + s) * KROW + d / 8) * 8 + d % 8] << 16);
-          G[blk] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, P[s], G[blk], 0, 0, 0);
+          hi[s] = round_bf16f(P[s]);
+          const float r1 = P[s] - hi[s];
+          mid[s] = round_bf16f(r1);
+          lo[s] = round_bf16f(r1 - mid[s]);
         }
+        pw[0] = pack_s16x4(bf16_pair(hi[0], hi[1]), bf16_pair(hi[2], hi[3]));
+        pw[1] = pack_s16x4(bf16_pair(mid[0], mid[1]), bf16_pair(mid[2], mid[3]));
+        pw[2] = pack_s16x4(bf16_pair(lo[0], lo[1]), bf16_pair(lo[2], lo[3]));
       }
-      // keep the fp32 form (L, mean g) for the round's node and, when C = 4,
-      // emit it as the level-2 node (lane: d = 16b + 4g + i of plane j): its
-      // rounded mean keys, or, when level 2 is scored from its keys, the mass
-      // share exp(L(leaf g) - L) of each child (so that the weight of key i
-      // of leaf g is that share times the leaf's own w) with
+      // the fp32 form (L, mean g) goes to LDS for the round's node; when C = 4
+      // it is also emitted as the level-2 node (lane: d = 16b + 4g + i of
+      // plane j): its rounded mean keys, or, when level 2 is scored from its
+      // keys, the mass share exp(L(leaf g) - L) of each child (so that the
+      // weight of key i of leaf g is that share times the leaf's own w) with
       // c = L - sum_i P_i z_i, P the normalised weights of its 16 keys
       const bool w2 = C == 4 && geo.w2;
       float dot = 0.f;
       uint2 pk[NB];
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk) {
-        float gv[4];
+        f32x4 G = {0.f, 0.f, 0.f, 0.f};
+        const int d = 16 * blk + (lane & 15);
+        uint32_t kw[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) gv[i] = G[blk][i];
-        *reinterpret_cast<float4*>(&chG[wave][j][16 * blk + 4 * g]) = make_float4(gv[0], gv[1], gv[2], gv[3]);
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const uint32_t k0 = Ks16[((4 * g + 2 * h2) * KROW + d / 8) * 8 + d % 8];
+          const uint32_t k1 = Ks16[((4 * g + 2 * h2 + 1) * KROW + d / 8) * 8 + d % 8];
+          kw[h2] = k0 | (k1 << 16);
+        }
+        const s16x4 ka = pack_s16x4(kw[0], kw[1]);
+#pragma unroll
+        for (int t = 0; t < 3; ++t) G = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka, pw[t], G, 0, 0, 0);
+        *reinterpret_cast<float4*>(&chG[wave][j][16 * blk + 4 * g]) = make_float4(G[0], G[1], G[2], G[3]);
         if (!w2) {
           const float4 rv = *reinterpret_cast<const float4*>(&refL[j][16 * blk + 4 * g]);
-          pk[blk] = make_uint2(bf16_pair(gv[0], gv[1]), bf16_pair(gv[2], gv[3]));
+          pk[blk] = make_uint2(bf16_pair(G[0], G[1]), bf16_pair(G[2], G[3]));
           dot = fmaf(rv.x, bf16_lo(pk[blk].x), dot);
           dot = fmaf(rv.y, bf16_hi(pk[blk].x), dot);
           dot = fmaf(rv.z, bf16_lo(pk[blk].y), dot);
@@ -928,28 +942,44 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
     }
     __syncthreads();  // the round's four 16-key parts are in LDS
 
-    // the round's node (level 3 when C = 4, level 2 when C = 8): ordered fold
-    // of its four 16-key parts
+    // the round's node (level 3 when C = 4, level 2 when C = 8): fold
+    // of its four 16-key parts: the max of their L first, then each part's
+    // share exp(L_c - max) / sum, and the shares' weighted sum of the parts'
+    // fp32 mean keys in part order
     const int nch = (int)min<int64_t>(4, (nkeys - 64 * r + 15) / 16);
-    float m3 = 0.f, s3 = 0.f, a3[VPL];
-    bool u3 = false;
-    for (int c = 0; c < nch; ++c) {
-      float gc[VPL];
+    float lc[4], m3 = chL[0][j];
 #pragma unroll
-      for (int e = 0; e < VPL; e += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(&chG[c][j][d0 + e]);
-        gc[e] = v.x;
-        gc[e + 1] = v.y;
-        gc[e + 2] = v.z;
-        gc[e + 3] = v.w;
-      }
-      absorb(m3, s3, a3, u3, chL[c][j], 1.f, gc, VPL);
+    for (int c = 0; c < 4; ++c) {
+      lc[c] = c < nch ? chL[c][j] : kNegInf;
+      m3 = fmaxf(m3, lc[c]);
+    }
+    float wc[4], s3 = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      wc[c] = c < nch ? __expf(lc[c] - m3) : 0.f;
+      s3 += wc[c];
     }
     const float L3 = m3 + __logf(s3);
     {
       const float inv = 1.f / s3;
 #pragma unroll
-      for (int e = 0; e < VPL; ++e) a3[e] *= inv;
+      for (int c = 0; c < 4; ++c) wc[c] *= inv;
+    }
+    float a3[VPL];
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) a3[e] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (c < nch) {
+#pragma unroll
+        for (int e = 0; e < VPL; e += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(&chG[c][j][d0 + e]);
+          a3[e] = fmaf(wc[c], v.x, a3[e]);
+          a3[e + 1] = fmaf(wc[c], v.y, a3[e + 1]);
+          a3[e + 2] = fmaf(wc[c], v.z, a3[e + 2]);
+          a3[e + 3] = fmaf(wc[c], v.w, a3[e + 3]);
+        }
+      }
     }
     const int64_t rel = min<int64_t>(64 * (r + 1), nkeys);
     const int64_t end = t0 + rel;

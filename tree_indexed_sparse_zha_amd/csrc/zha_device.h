@@ -110,6 +110,13 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 // x rounded to bf16 (nearest even), as fp32.
 __device__ __forceinline__ float round_bf16f(float x) { return bf16_lo(bf16_pair(x, 0.f)); }
+// Four bf16 values (two bf16_pair words, low word first) as the operand of
+// a K = 16 bf16 MFMA.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ s16x4 pack_s16x4(uint32_t lo, uint32_t hi) {
+  return __builtin_bit_cast(s16x4, u32x2v{lo, hi});
+}
 
 // Pack fp32 values of one piece, rounding to the storage type; also returns
 // the rounded values as fp32 in `rounded`.
