@@ -932,6 +932,8 @@ CUT_CASES = [
     ("mean-small-p", "mean", (1 << 18) - 4 * 37, 0.05, False, 1),
     ("mean-keep-all", "mean", 1 << 17, 1.0, False, 1),
     ("weights-16q", "weights", 1 << 17, 0.95, False, 4),
+    # level 1 with 131,008 parents: their bits take 4,094 words of LDS
+    ("weights2-2m", "weights2", (1 << 21) - 1003, 0.95, False, 1),
 ]
 
 
@@ -943,7 +945,7 @@ def test_select_cut_bin_matches_radix(name, leaf_form, N, p, repeat, T, monkeypa
     reach the same bits and statistics, and both agree with the selection
     records' exact rule."""
     _say(f"select cut bin {name}")
-    cap = 1 << 18
+    cap = max(1 << 18, N)
     cfg = zha.ZhaConfig(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=5, dtype="bf16",
                         capacity=cap, leaf_form=leaf_form)
     K = torch.empty(1, 2, cap, 128, dtype=torch.bfloat16)

@@ -503,7 +503,6 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
   constexpr int VPL = D / 16;     // values of d per lane above level 2
   constexpr int KB = 16;
   constexpr int KROW = PIECES + 1;  // padded LDS key row (uint4)
-  constexpr int GROW = D + 4;       // padded LDS child row (floats)
   constexpr int NUR = NU > 0 ? NU : 1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15, g = lane >> 4;
@@ -521,19 +520,26 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
 
   __shared__ uint4 Ks[4][KB * KROW];
   __shared__ float zs[4][16][KB + 1];
-  __shared__ float chG[4][16][GROW];
   __shared__ float chL[4][16];
-  __shared__ float refL[16][GROW];
+  __shared__ s16x4 Wb[4][3][64];  // the round node's weights of each 16-key part (three bf16 terms)
   __shared__ float dotp[kMaxLevels][4][16];
   __shared__ float rmax[kMaxLevels][4][16];  // fp8 levels: the waves' row maxima of a node's g
-  __shared__ uint4 refB[16][KROW];          // reference rows in bf16 (MFMA operands)
+  __shared__ uint4 refB[16][KROW];          // reference rows in bf16 (MFMA operands and the dots r . g)
 
-  for (int i = threadIdx.x; i < 16 * D; i += 256) {
-    const int jr = i / D, d = i % D;
-    // with bf16 keys the tree is that of the bf16-rounded reference queries
-    refL[jr][d] = jr < R ? round_bf16f(A.ref[((int64_t)h * R + jr) * D + d]) : 0.f;
+  // with bf16 keys the tree is that of the bf16-rounded reference queries
+  for (int i = threadIdx.x; i < 16 * PIECES; i += 256) {
+    const int jr = i / PIECES, pc = i % PIECES;
+    float rr[8], dummy[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rr[e] = jr < R ? round_bf16f(A.ref[((int64_t)h * R + jr) * D + pc * 8 + e]) : 0.f;
+    refB[jr][pc] = pack(rr, dummy, bf16_t());
   }
   __syncthreads();
+  // r_j[d .. d + 3] (d a multiple of 4) from the bf16 rows
+  auto ref4 = [&](int jr, int d) -> float4 {
+    const uint2 w = reinterpret_cast<const uint2*>(&refB[jr][d / 8])[(d % 8) / 4];
+    return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
+  };
 
   // node writers above level 2: this lane's D/16 values of g (rounded to
   // bf16), the wave's share of r . g into dotp[slot]; L and c are stored by
@@ -613,7 +619,13 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
     }
     float dot = 0.f;
 #pragma unroll
-    for (int e = 0; e < VPL; ++e) dot = fmaf(refL[j][d0 + e], gr[e], dot);
+    for (int e = 0; e < VPL; e += 4) {
+      const float4 rv = ref4(j, d0 + e);
+      dot = fmaf(rv.x, gr[e], dot);
+      dot = fmaf(rv.y, gr[e + 1], dot);
+      dot = fmaf(rv.z, gr[e + 2], dot);
+      dot = fmaf(rv.w, gr[e + 3], dot);
+    }
     dot += __shfl_xor(dot, 16);
     dot += __shfl_xor(dot, 32);
     if (g == 0) dotp[slot][wave][j] = dot;
@@ -693,17 +705,6 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
     return;
   }
 
-  // reference rows as bf16 MFMA A operands of the logits (exact: refL holds
-  // bf16 values), kept in LDS (registers are the kernel's limit)
-  for (int i = threadIdx.x; i < 16 * PIECES; i += 256) {
-    const int jr = i / PIECES, pc = i % PIECES;
-    float rr[8], dummy[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) rr[e] = refL[jr][pc * 8 + e];
-    refB[jr][pc] = pack(rr, dummy, bf16_t());
-  }
-  __syncthreads();
-
   const bf16_t* Kc = reinterpret_cast<const bf16_t*>(A.K) + (int64_t)b * A.sb + (int64_t)h * A.sh;
   const int64_t nkeys = tend - t0;
   const int64_t nrounds = (nkeys + 63) / 64;
@@ -725,6 +726,33 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
     if (nk0 > 0) load_block(t0 + 16 * wave, nk0, pre);
   }
   const uint16_t* Ks16 = reinterpret_cast<const uint16_t*>(Ks[wave]);
+  // A operand of a 16x16x16 bf16 product over a part's 16 keys: keys
+  // 4gg .. 4gg + 3 at column d (exact)
+  auto key_operand = [&](const uint16_t* K16, int d, int gg) -> s16x4 {
+    uint32_t kw[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const uint32_t k0 = K16[((4 * gg + 2 * h2) * KROW + d / 8) * 8 + d % 8];
+      const uint32_t k1 = K16[((4 * gg + 2 * h2 + 1) * KROW + d / 8) * 8 + d % 8];
+      kw[h2] = k0 | (k1 << 16);
+    }
+    return pack_s16x4(kw[0], kw[1]);
+  };
+  // four fp32 weights as three bf16 B operands, hi + mid + lo = x to within
+  // 2^-27 relative
+  auto split3 = [](const float* x, s16x4* pw) {
+    float hi[4], mid[4], lo[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      hi[s] = round_bf16f(x[s]);
+      const float r1 = x[s] - hi[s];
+      mid[s] = round_bf16f(r1);
+      lo[s] = round_bf16f(r1 - mid[s]);
+    }
+    pw[0] = pack_s16x4(bf16_pair(hi[0], hi[1]), bf16_pair(hi[2], hi[3]));
+    pw[1] = pack_s16x4(bf16_pair(mid[0], mid[1]), bf16_pair(mid[2], mid[3]));
+    pw[2] = pack_s16x4(bf16_pair(lo[0], lo[1]), bf16_pair(lo[2], lo[3]));
+  };
 
   // open accumulators of levels RL + 1 .. RL + NU
   float um[NUR], us[NUR], ua[NUR][VPL];
@@ -747,6 +775,7 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
       const int nnk = block_keys(r + 1);
       if (nnk > 0) load_block(kb0 + 64, nnk, pre);
     }
+    float P[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's normalised weights of its 4 keys in the block
     if (nk > 0) {
       // z[j][i] = r_j . k_i / sqrt(d)
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -801,7 +830,7 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
                   __uint_as_float((uint32_t)Ks16[((C * l + 4 * s + g) * KROW + d / 8) * 8 + d % 8] << 16);
               Gl = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, wb[s], Gl, 0, 0, 0);
             }
-            const float4 rv = *reinterpret_cast<const float4*>(&refL[j][16 * blk + 4 * g]);
+            const float4 rv = ref4(j, 16 * blk + 4 * g);
             pk[blk] = make_uint2(bf16_pair(Gl[0], Gl[1]), bf16_pair(Gl[2], Gl[3]));
             dot = fmaf(rv.x, bf16_lo(pk[blk].x), dot);
             dot = fmaf(rv.y, bf16_hi(pk[blk].x), dot);
@@ -851,7 +880,7 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
       float m2 = leaf ? m1 : kNegInf;
       m2 = fmaxf(m2, __shfl_xor(m2, 16));
       m2 = fmaxf(m2, __shfl_xor(m2, 32));
-      float P[4], ps = 0.f;
+      float ps = 0.f;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         P[s] = leaf ? __expf(z[s] - m2) : 0.f;
@@ -862,61 +891,38 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
       const float L2 = m2 + __logf(ps);
       const float inv2 = 1.f / ps;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) P[s] *= inv2;  // normalised weights: the product is the mean
-      // g^T[d][j] = sum over keys k[key][d] P[j][key] on the bf16 matrix cores
-      // (v_mfma_f32_16x16x16_bf16, the 16 keys as the contraction): A = keys
-      // (row d = 16b + lane % 16, k = key 4g + s: exact in bf16), B = P (k =
-      // key 4g + s, column j: this lane's own four weights).  P is split into
-      // three bf16 terms, hi + mid + lo = P to within 2^-27 relative, so the
-      // three products accumulate the fp32 weighted sum.
-      s16x4 pw[3];
-      {
-        float hi[4], mid[4], lo[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          hi[s] = round_bf16f(P[s]);
-          const float r1 = P[s] - hi[s];
-          mid[s] = round_bf16f(r1);
-          lo[s] = round_bf16f(r1 - mid[s]);
-        }
-        pw[0] = pack_s16x4(bf16_pair(hi[0], hi[1]), bf16_pair(hi[2], hi[3]));
-        pw[1] = pack_s16x4(bf16_pair(mid[0], mid[1]), bf16_pair(mid[2], mid[3]));
-        pw[2] = pack_s16x4(bf16_pair(lo[0], lo[1]), bf16_pair(lo[2], lo[3]));
-      }
-      // the fp32 form (L, mean g) goes to LDS for the round's node; when C = 4
-      // it is also emitted as the level-2 node (lane: d = 16b + 4g + i of
-      // plane j): its rounded mean keys, or, when level 2 is scored from its
-      // keys, the mass share exp(L(leaf g) - L) of each child (so that the
-      // weight of key i of leaf g is that share times the leaf's own w) with
-      // c = L - sum_i P_i z_i, P the normalised weights of its 16 keys
+      for (int s = 0; s < 4; ++s) P[s] *= inv2;  // normalised weights of the block
+      // when C = 4 the block is also emitted as the level-2 node: its rounded
+      // mean keys (lane: d = 16b + 4g + i of plane j, from the product below),
+      // or, when level 2 is scored from its keys, the mass share
+      // exp(L(leaf g) - L) of each child (so that the weight of key i of leaf
+      // g is that share times the leaf's own w) with c = L - sum_i P_i z_i
       const bool w2 = C == 4 && geo.w2;
       float dot = 0.f;
       uint2 pk[NB];
+      if (C == 4 && !w2) {
+        // g^T[d][j] = sum over keys k[key][d] P[j][key] on the bf16 matrix
+        // cores (v_mfma_f32_16x16x16_bf16, the 16 keys as the contraction):
+        // A = keys (row d = 16b + lane % 16, k = key 4g + s: exact in bf16),
+        // B = P (k = key 4g + s, column j: this lane's own four weights), P
+        // split into three bf16 terms (hi + mid + lo = P to within 2^-27
+        // relative), so that the three products accumulate the fp32 sum
+        s16x4 pw[3];
+        split3(P, pw);
 #pragma unroll
-      for (int blk = 0; blk < NB; ++blk) {
-        f32x4 G = {0.f, 0.f, 0.f, 0.f};
-        const int d = 16 * blk + (lane & 15);
-        uint32_t kw[2];
+        for (int blk = 0; blk < NB; ++blk) {
+          f32x4 G = {0.f, 0.f, 0.f, 0.f};
+          const s16x4 ka = key_operand(Ks16, 16 * blk + (lane & 15), g);
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const uint32_t k0 = Ks16[((4 * g + 2 * h2) * KROW + d / 8) * 8 + d % 8];
-          const uint32_t k1 = Ks16[((4 * g + 2 * h2 + 1) * KROW + d / 8) * 8 + d % 8];
-          kw[h2] = k0 | (k1 << 16);
-        }
-        const s16x4 ka = pack_s16x4(kw[0], kw[1]);
-#pragma unroll
-        for (int t = 0; t < 3; ++t) G = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka, pw[t], G, 0, 0, 0);
-        *reinterpret_cast<float4*>(&chG[wave][j][16 * blk + 4 * g]) = make_float4(G[0], G[1], G[2], G[3]);
-        if (!w2) {
-          const float4 rv = *reinterpret_cast<const float4*>(&refL[j][16 * blk + 4 * g]);
+          for (int t = 0; t < 3; ++t) G = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka, pw[t], G, 0, 0, 0);
+          const float4 rv = ref4(j, 16 * blk + 4 * g);
           pk[blk] = make_uint2(bf16_pair(G[0], G[1]), bf16_pair(G[2], G[3]));
           dot = fmaf(rv.x, bf16_lo(pk[blk].x), dot);
           dot = fmaf(rv.y, bf16_hi(pk[blk].x), dot);
           dot = fmaf(rv.z, bf16_lo(pk[blk].y), dot);
           dot = fmaf(rv.w, bf16_hi(pk[blk].y), dot);
         }
-      }
-      if (w2) {
+      } else if (w2) {
         dot = P[0] * z[0];
 #pragma unroll
         for (int s = 1; s < 4; ++s) dot = fmaf(P[s], z[s], dot);
@@ -940,12 +946,13 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
         }
       }
     }
-    __syncthreads();  // the round's four 16-key parts are in LDS
+    __syncthreads();  // the round's four 16-key parts (keys, L) are in LDS
 
-    // the round's node (level 3 when C = 4, level 2 when C = 8): fold
-    // of its four 16-key parts: the max of their L first, then each part's
-    // share exp(L_c - max) / sum, and the shares' weighted sum of the parts'
-    // fp32 mean keys in part order
+    // the round's node (level 3 when C = 4, level 2 when C = 8) over its up
+    // to 64 keys: each 16-key part's share exp(L_c - max) / sum (the max of
+    // the parts' L first), and the key weights W = share_c * P (P the part's
+    // normalised weights), so that g = sum_i W_i k_i; L is the LSE of the
+    // parts' L
     const int nch = (int)min<int64_t>(4, (nkeys - 64 * r + 15) / 16);
     float lc[4], m3 = chL[0][j];
 #pragma unroll
@@ -965,21 +972,49 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) wc[c] *= inv;
     }
+    if (wave < nch) {
+      // this wave's part: its weights as the B operand of k-step `wave` of
+      // the round's product (lane (j, g): keys 4g + s of the part, plane j)
+      const float ws = wave == 0 ? wc[0] : wave == 1 ? wc[1] : wave == 2 ? wc[2] : wc[3];
+      float W[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) W[s] = ws * P[s];
+      s16x4 pw[3];
+      split3(W, pw);
+#pragma unroll
+      for (int t = 0; t < 3; ++t) Wb[wave][t][lane] = pw[t];
+    }
+    __syncthreads();  // every part's weights are in
+    // g^T[d][j] = sum over the round's keys k[key][d] W[j][key] on the bf16
+    // matrix cores, 16 keys (one part) per k-step.  Wave w computes this
+    // lane's own values above level 2, d = d0 + 4q + i (q < D / 64, i < 4):
+    // A-operand row rr of step q takes d = VPL (4w + rr / 4) + 4q + rr % 4,
+    // so that output rows 4g + i land on lane (j, g).
     float a3[VPL];
+    {
+      f32x4 G3[VPL / 4];
 #pragma unroll
-    for (int e = 0; e < VPL; ++e) a3[e] = 0.f;
+      for (int q = 0; q < VPL / 4; ++q) G3[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int rr = lane & 15;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if (c < nch) {
+      for (int c = 0; c < 4; ++c) {
+        if (c < nch) {
+          const uint16_t* Kp = reinterpret_cast<const uint16_t*>(Ks[c]);
+          s16x4 wb[3];
 #pragma unroll
-        for (int e = 0; e < VPL; e += 4) {
-          const float4 v = *reinterpret_cast<const float4*>(&chG[c][j][d0 + e]);
-          a3[e] = fmaf(wc[c], v.x, a3[e]);
-          a3[e + 1] = fmaf(wc[c], v.y, a3[e + 1]);
-          a3[e + 2] = fmaf(wc[c], v.z, a3[e + 2]);
-          a3[e + 3] = fmaf(wc[c], v.w, a3[e + 3]);
+          for (int t = 0; t < 3; ++t) wb[t] = Wb[c][t][lane];
+#pragma unroll
+          for (int q = 0; q < VPL / 4; ++q) {
+            const s16x4 ka = key_operand(Kp, VPL * (4 * wave + rr / 4) + 4 * q + rr % 4, g);
+#pragma unroll
+            for (int t = 0; t < 3; ++t) G3[q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka, wb[t], G3[q], 0, 0, 0);
+          }
         }
       }
+#pragma unroll
+      for (int q = 0; q < VPL / 4; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a3[4 * q + i] = G3[q][i];
     }
     const int64_t rel = min<int64_t>(64 * (r + 1), nkeys);
     const int64_t end = t0 + rel;

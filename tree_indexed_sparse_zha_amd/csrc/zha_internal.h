@@ -154,6 +154,7 @@ struct SelectArgs {
   int64_t parent_words;
   int C;
   int cut_cap;
+  int parent_lds;  // parent-bit words of LDS the one-workgroup select is launched with (set at launch)
 };
 
 // Split select: per query a state record, and per (query, segment) a slot of

@@ -1492,11 +1492,11 @@ __device__ __forceinline__ unsigned long long p_target(float p, unsigned long lo
 // ---- the one-workgroup select: two reads of the row in the common case
 //
 // Pass 1 sums the fixed-point masses (M) and histograms them over a linear
-// grid of scores, 2048 bins over [max - span, max], where span is wide
-// enough that every score below it has a fixed-point mass that rounds to 0
-// (all of them land in bin 0, which then holds no mass and so never the
-// cut).  The bin of a score is monotone in the score, so the cut lies in
-// the one bin b whose mass interval holds P, exactly as in a radix digit.
+// grid of scores, 2048 bins over [lo, max]: lo is the lowest candidate
+// score, or max - span when that is higher, span wide enough that every
+// score below it has a fixed-point mass that rounds to 0 (all of them land
+// in bin 0).  The bin of a score is monotone in the score, so the cut lies
+// in the one bin b whose mass interval holds P, exactly as in a radix digit.
 // Pass 2 writes the bitset: every candidate in a bin above b is kept, every
 // one below dropped, and the candidates of bin b (key, id, mass) are
 // compacted into LDS.  Among those few the keep rule is applied exactly: a
@@ -1514,7 +1514,10 @@ __device__ __forceinline__ unsigned long long p_target(float p, unsigned long lo
 
 constexpr int kLinBins = 2048;
 constexpr int kCutCap = 1536;
-constexpr int kParentWords = 2560;  // parent bits held in LDS: levels of up to 81,920 parents
+// parent bits held in LDS (dynamic, sized per launch to the words a row
+// reaches): levels of up to 163,840 parents (with the static arrays, at
+// most 68 KiB of the 160 KiB a workgroup may take)
+constexpr int kParentWords = 5120;
 constexpr int kSelUnroll = 4;
 
 __device__ __forceinline__ int lin_bin(float s, float lo, float inv_w) {
@@ -1568,7 +1571,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs A) {
   __shared__ uint32_t l_key[kCutCap];
   __shared__ int l_id[kCutCap];
   __shared__ unsigned long long l_mass[kCutCap];
-  __shared__ uint32_t l_par[kParentWords];
+  extern __shared__ uint32_t l_par[];  // A.parent_lds words
   __shared__ int l_n;
 
   uint32_t kmax, kmin;
@@ -1598,16 +1601,17 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs A) {
     const int lgC = __ffs(A.C) - 1;  // C is a power of two
     if (A.sel_parent) {
       const int64_t pw = (((n4 - 1) * 4 >> lgC) >> 5) + 1;  // parent words the row's float4s reach
-      if (pw <= kParentWords) {
+      if (pw <= A.parent_lds) {
         const uint32_t* prow = A.sel_parent + q * A.parent_words;
         for (int64_t i = tid; i < pw; i += kSelThreads) l_par[i] = prow[i];
         pbits = l_par;
       }
     }
-    // pass 1: M and the linear-bin histogram
+    // pass 1: M and the linear-bin histogram, over the candidates' score
+    // range down to where the masses reach 0
     const float span = (float)(su.shift + 2) * 0.6931472f;  // exp(-span) * 2^shift < 1/4: mass 0 below
-    const float lo = mx - span;
-    const float inv_w = (float)kLinBins / span;
+    const float lo = fmaxf(mx - span, key_to_float(kmin));
+    const float inv_w = (float)kLinBins / fmaxf(mx - lo, 1e-30f);
     for (int i = tid; i < kLinBins; i += kSelThreads) hist[i] = 0ull;
     if (tid == 0) l_n = 0;
     __syncthreads();
@@ -2638,7 +2642,15 @@ hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dty
   } else if (sel.split_S < 2 && sel.n_nodes <= kRowsRow && n_queries >= kWaveQueries) {
     hipLaunchKernelGGL(k_select_rows, dim3((unsigned)n_queries), dim3(256), 0, s, sel);
   } else if (sel.split_S < 2) {
-    hipLaunchKernelGGL(k_select, dim3((unsigned)n_queries), dim3(kSelThreads), 0, s, sel);
+    // LDS for the parent bits the rows reach (the kernel computes the same count)
+    sel.parent_lds = 0;
+    if (sel.sel_parent && !sel.keep_all && sel.cut_cap > 0 && sel.n_nodes > 0) {
+      const int lgC = __builtin_ctz((unsigned)sel.C);
+      const int64_t n4 = (sel.n_nodes + 3) / 4;
+      const int64_t pw = (((n4 - 1) * 4 >> lgC) >> 5) + 1;
+      if (pw <= kParentWords) sel.parent_lds = (int)pw;
+    }
+    hipLaunchKernelGGL(k_select, dim3((unsigned)n_queries), dim3(kSelThreads), (size_t)sel.parent_lds * 4, s, sel);
   } else {
     const dim3 segs((unsigned)sel.split_S, (unsigned)n_queries);
     hipLaunchKernelGGL(k_select_setup, dim3((unsigned)n_queries), dim3(kSelThreads), 0, s, sel);
