@@ -444,10 +444,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   // padded: the fold's lanes (chunk cx, part) read WROW cx + part, distinct
   // modulo 16 float4s (64 banks), and rl's floats 4 cx + part
   constexpr int WROW = 17 * PARTS;
+  // w row order: plane-major in memory order (staged from 16-byte pieces
+  // read as [j][part]); MODE 2 writes its own w (lanes (plane, part)) part-
+  // major, [part][17 planes], so that 16 lanes of one part store to distinct
+  // banks; the folds read either order conflict-free
+  auto wix = [](int j, int part) { return MODE == 2 ? part * 17 + j : j * PARTS + part; };
   __shared__ float sc[16][NCH + 1];
-  __shared__ float4 wl[NCH][WROW];  // w of chunk x, plane j, 4-key part at [x][j * PARTS + part]
+  __shared__ float4 wl[NCH][WROW];  // w of chunk x, plane j, 4-key part at [x][wix(j, part)]
   __shared__ float cl[NCH][17];
-  __shared__ float4 zl[Q4 ? NW : 1][16][4];  // Q4: [wave][quad of the wave][query] logits
+  // Q4: [wave][quad of the wave][query] logits; rows padded to 5 float4s so
+  // that the gather of a key's 4 queries (16 rows of a wave at once) reads
+  // distinct banks
+  __shared__ float4 zl[Q4 ? NW : 1][16][5];
   __shared__ unsigned long long mbl[16];    // candidate bits per query
   __shared__ float rl[MODE ? NCH : 1][WROW];     // MODE: rho of node x, plane j, chunk part
   __shared__ float c1l[MODE == 2 ? 4 * NCH : 1][17];  // MODE 2: c of the tile's chunks
@@ -645,7 +653,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       t += __shfl_xor(t, 16);
       t += __shfl_xor(t, 32);
       if (qn < R) {
-        wl[g][qn * PARTS + kg] = make_float4(w[0], w[1], w[2], w[3]);
+        wl[g][wix(qn, kg)] = make_float4(w[0], w[1], w[2], w[3]);
         rl[g][qn * PARTS + kg] = rho;
         c1l[4 * g + kg][qn] = L1v[gi] - wz;
         if (kg == 0) cl[g][qn] = L2v[gi] - t;
@@ -659,7 +667,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       float best = kNegInf;
 #pragma unroll UNR
       for (int jj = 0; jj < RR; ++jj) {
-        const float4 wv = wl[x][jj * PARTS + part];
+        const float4 wv = wl[x][wix(jj, part)];
         float v = wv.x * zz[0] + wv.y * zz[1] + wv.z * zz[2] + wv.w * zz[3];
         if constexpr (MODE) v *= rl[x][jj * PARTS + part];  // the chunk's share of the node
 #pragma unroll
@@ -694,7 +702,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     float best = kNegInf, best1 = kNegInf;
 #pragma unroll UNR
     for (int jj = 0; jj < RR; ++jj) {
-      const float4 wv = wl[x][jj * PARTS + part];
+      const float4 wv = wl[x][wix(jj, part)];
       float v = wv.x * zv.x + wv.y * zv.y + wv.z * zv.z + wv.w * zv.w;
       if constexpr (MODE == 2) best1 = fmaxf(best1, c1l[4 * x + part][jj] + v);  // chunk 4x + part's plane
       if constexpr (MODE) v *= rl[x][jj * PARTS + part];  // the chunk's share of the node
