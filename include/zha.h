@@ -526,6 +526,30 @@ enum zha_probe_mode {
 int zha_stream_probe(int32_t mode, const void* src, void* dst, int64_t n_bytes, int64_t dst_bytes,
                      zha_profile* prof, void* stream);
 
+/* ------------------------------------------------------------------------
+ * zha_selected_chunks: the level-1 selection of zha_route as sorted lists of
+ * chunk ids (MTP "How does top-p routing pick tokens?": a query attends the
+ * raw chunks kept at the bottom level, plus the sink and its current chunk,
+ * which zha_attend adds by flag and which are not listed here).
+ *   sel1        device, n_queries x sel1_words uint32: bit c of query q's row
+ *               (word c / 32, bit c % 32) set when chunk c is kept, as
+ *               zha_route writes the level-1 rows (zha_route_layout
+ *               sel_offset[0], words[0]); bits at or past n_chunks ignored.
+ *   n_chunks    chunks the rows cover (floor(n_tokens / chunk)).
+ *   chunk_ids   device, n_queries x cap int32 (output): query q's kept chunk
+ *               ids in increasing order at chunk_ids[q * cap ...]; entries
+ *               past its count (or past cap) are not written.
+ *   chunk_count device, n_queries int32 (output): query q's number of kept
+ *               chunks, which may exceed cap (only the first cap ids are
+ *               then written).
+ * One workgroup per query, stream-ordered, no host sync.
+ * Errors: ZHA_ERR_NULL, ZHA_ERR_ALIGN (pointers not 4-byte aligned),
+ * ZHA_ERR_ARG (n_queries < 1 or >= 2^31, n_chunks < 0 or >= 2^31, cap < 0),
+ * ZHA_ERR_CAPACITY (sel1_words < ceil(n_chunks / 32)), ZHA_ERR_HIP.
+ */
+int zha_selected_chunks(const uint32_t* sel1, int64_t sel1_words, int64_t n_queries, int64_t n_chunks,
+                        int32_t* chunk_ids, int32_t* chunk_count, int64_t cap, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,5 +13,9 @@ hipError_t launch_route_level(const ScoreArgs&, const SelectArgs&, int, int, int
 }
 hipError_t launch_attend(const AttendArgs&, int, int, Prof&) { return hipErrorNotSupported; }
 hipError_t launch_probe(int, const void*, void*, int64_t, Prof&) { return hipErrorNotSupported; }
+hipError_t launch_selected_chunks(const uint32_t*, int64_t, int64_t, int64_t, int32_t*, int32_t*, int64_t,
+                                  hipStream_t) {
+  return hipErrorNotSupported;
+}
 
 }  // namespace zha

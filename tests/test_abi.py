@@ -387,3 +387,22 @@ def test_stream_probe_rejects_bad_arguments(lib):
     with pytest.raises(zha.ZhaError) as ei:
         zha._check(lib.zha_stream_probe(2, ct.c_void_p(src.data_ptr() + 4), zha._ptr(dst), 64, 4096, None, None))
     assert ei.value.code == zha.ZHA_ERR_ALIGN
+
+
+def test_selected_chunks_rejects_bad_arguments(lib):
+    """The chunk-id export checks pointers, alignment, counts and the row
+    width on the host before any launch (fake, aligned addresses)."""
+    A = ct.c_void_p(1 << 20)
+
+    def call(sel=A, words=4, nq=2, n=100, ids=A, cnt=A, cap=8):
+        return lib.zha_selected_chunks(sel, words, nq, n, ids, cnt, cap, None)
+
+    assert call(sel=None) == zha.ZHA_ERR_NULL
+    assert call(cnt=None) == zha.ZHA_ERR_NULL
+    assert call(ids=None) == zha.ZHA_ERR_NULL
+    assert call(sel=ct.c_void_p((1 << 20) + 2)) == zha.ZHA_ERR_ALIGN
+    assert call(nq=0) == zha.ZHA_ERR_ARG
+    assert call(n=-1) == zha.ZHA_ERR_ARG
+    assert call(n=1 << 31) == zha.ZHA_ERR_ARG
+    assert call(cap=-1) == zha.ZHA_ERR_ARG
+    assert call(words=3, n=97) == zha.ZHA_ERR_CAPACITY  # 97 chunks need 4 words

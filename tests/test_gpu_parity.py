@@ -673,6 +673,66 @@ def test_route_is_deterministic(leaf_form):
     assert torch.equal(out0, out)
 
 
+CHUNK_ID_CASES = [
+    # name, n_queries, n_chunks, words (>= ceil(n_chunks / 32)), keep probability, cap
+    ("ragged-dense", 5, 1000, 40, 0.5, 1000),
+    ("many-segments", 3, 100003, 3126, 0.3, 100003),
+    ("cap-cut", 4, 5000, 157, 0.6, 777),
+    ("empty-and-full", 2, 4097, 129, None, 4097),
+    ("no-chunks", 2, 0, 1, 0.5, 4),
+]
+
+
+@pytest.mark.parametrize("name,nq,n,words,prob,cap", CHUNK_ID_CASES, ids=[c[0] for c in CHUNK_ID_CASES])
+def test_selected_chunks_lists_the_set_bits(name, nq, n, words, prob, cap):
+    """zha_selected_chunks returns, per query, the ids of the set bits below
+    n_chunks in increasing order (bits past n_chunks set on purpose must be
+    ignored), the full count even when it exceeds cap, and writes nothing
+    past min(count, cap)."""
+    _say(f"selected chunks {name}")
+    g = torch.Generator().manual_seed(77)
+    if prob is None:
+        mask = torch.zeros(nq, n, dtype=torch.bool)
+        mask[1] = True  # query 0 keeps nothing, query 1 everything
+    else:
+        mask = torch.rand(nq, n, generator=g) < prob
+    full = torch.zeros(nq, words * 32, dtype=torch.bool)
+    full[:, :n] = mask
+    full[:, n:] = True  # garbage past n_chunks
+    words_t = zha.pack_bits(full, words).cuda()
+    ids, count = zha.selected_chunks(words_t, n, cap)
+    torch.cuda.synchronize()
+    ids, count = ids.cpu(), count.cpu()
+    for q in range(nq):
+        want = torch.nonzero(mask[q]).flatten().to(torch.int32)
+        assert int(count[q]) == want.numel(), (q, int(count[q]), want.numel())
+        k = min(want.numel(), cap)
+        assert torch.equal(ids[q, :k], want[:k]), q
+        assert bool((ids[q, k:] == -1).all()), f"query {q}: entries written past its count"
+
+
+def test_selected_chunks_of_a_route_match_its_bits():
+    """On a real route's level-1 rows the lists are exactly the kept chunks."""
+    _say("selected chunks of a route")
+    cfg = zha.ZhaConfig(batch=1, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=5, dtype="bf16",
+                        capacity=70000, leaf_form="weights2")
+    N, T = 65536 + 4 * 301 + 3, 1
+    K, V, Q, ref = random_inputs(cfg, T, seed=21)
+    tree = zha.alloc_tree(cfg)
+    zha.build(cfg, K, ref, tree, N)
+    buf = zha.alloc_route(cfg, T, logits=True)
+    zha.route(cfg, tree, N, Q, T, 0.9, buf, K=K)
+    sel = zha.level1_sel(buf)
+    n1 = N // cfg.chunk
+    ids, count = zha.selected_chunks(sel, n1, n1)
+    torch.cuda.synchronize()
+    bits = zha.unpack_bits(sel.cpu(), n1)
+    for q in range(sel.shape[0]):
+        want = torch.nonzero(bits[q]).flatten().to(torch.int32)
+        assert int(count[q]) == want.numel() > 0
+        assert torch.equal(ids[q, : want.numel()].cpu(), want)
+
+
 W2_LOGIT_CASES = [
     # name, cfg kwargs, T, n_tokens, p, top level (0 = the tree's top)
     ("qc4-l5", dict(batch=2, n_kv_heads=2, q_per_kv=4, head_dim=128, n_ref=16, chunk=4, levels=5, capacity=70000), 1, 65536 + 4 * 301 + 3, 0.9, 0),

@@ -834,4 +834,22 @@ int zha_stream_probe(int32_t mode, const void* src, void* dst, int64_t n_bytes, 
   return ZHA_OK;
 }
 
+int zha_selected_chunks(const uint32_t* sel1, int64_t sel1_words, int64_t n_queries, int64_t n_chunks,
+                        int32_t* chunk_ids, int32_t* chunk_count, int64_t cap, void* stream) {
+  if (!sel1) return fail(ZHA_ERR_NULL, "sel1 is NULL");
+  if (!chunk_count) return fail(ZHA_ERR_NULL, "chunk_count is NULL");
+  if (cap > 0 && !chunk_ids) return fail(ZHA_ERR_NULL, "chunk_ids is NULL");
+  if ((reinterpret_cast<uintptr_t>(sel1) | reinterpret_cast<uintptr_t>(chunk_count) |
+       reinterpret_cast<uintptr_t>(chunk_ids)) % 4)
+    return fail(ZHA_ERR_ALIGN, "pointers must be 4-byte aligned");
+  if (n_queries < 1 || n_queries > INT32_MAX) return fail(ZHA_ERR_ARG, "n_queries %lld out of range", (long long)n_queries);
+  if (n_chunks < 0 || n_chunks > INT32_MAX) return fail(ZHA_ERR_ARG, "n_chunks %lld out of range", (long long)n_chunks);
+  if (cap < 0) return fail(ZHA_ERR_ARG, "cap must be >= 0");
+  if (sel1_words < cdiv(n_chunks, 32)) return fail(ZHA_ERR_CAPACITY, "sel1_words too small");
+  hipError_t e = zha::launch_selected_chunks(sel1, sel1_words, n_queries, n_chunks, chunk_ids, chunk_count, cap,
+                                             static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "selected-chunks launch");
+  return ZHA_OK;
+}
+
 }  // extern "C"

@@ -290,6 +290,52 @@ __device__ __forceinline__ int block_scan_excl(int cnt, int* scan, int* excl) {
   return scan[kAttThreads - 1];
 }
 
+// Level-1 bitsets to sorted chunk id lists: one workgroup per query walks
+// its row in segments of kAttThreads x kIdWords words; each thread counts
+// the set bits of its words, an exclusive scan over the workgroup gives each
+// thread its first output position, and the ids are written in bit order.
+constexpr int kIdWords = 4;
+__global__ __launch_bounds__(kAttThreads) void k_selected_chunks(const uint32_t* __restrict__ sel1, int64_t words,
+                                                                int64_t n_chunks, int32_t* __restrict__ ids,
+                                                                int32_t* __restrict__ count, int64_t cap) {
+  __shared__ int scan[kAttThreads];
+  const int64_t q = blockIdx.x;
+  const uint32_t* row = sel1 + q * words;
+  int32_t* out = ids + q * cap;
+  const int64_t nw = (n_chunks + 31) / 32;  // words the chunks reach
+  int64_t base = 0;
+  for (int64_t w0 = 0; w0 < nw; w0 += (int64_t)kAttThreads * kIdWords) {
+    uint32_t bits[kIdWords];
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < kIdWords; ++k) {
+      const int64_t w = w0 + (int64_t)threadIdx.x * kIdWords + k;
+      uint32_t b = w < nw ? row[w] : 0u;
+      const int64_t lo = w * 32;
+      if (lo + 32 > n_chunks) b &= lo >= n_chunks ? 0u : ((1u << (n_chunks - lo)) - 1u);  // bits past n_chunks
+      bits[k] = b;
+      cnt += __popc(b);
+    }
+    int excl;
+    const int tot = block_scan_excl(cnt, scan, &excl);
+    int64_t pos = base + excl;
+#pragma unroll
+    for (int k = 0; k < kIdWords; ++k) {
+      const int64_t w = w0 + (int64_t)threadIdx.x * kIdWords + k;
+      uint32_t b = bits[k];
+      while (b) {
+        const int bit = __ffs(b) - 1;
+        b &= b - 1u;
+        if (pos < cap) out[pos] = (int32_t)(w * 32 + bit);
+        ++pos;
+      }
+    }
+    base += tot;
+    __syncthreads();  // scan[] is reused by the next segment
+  }
+  if (threadIdx.x == 0) count[q] = (int32_t)base;
+}
+
 constexpr int kMaxForcedQuads = 16;
 
 // Phase 1 of the bf16 kernels, compaction: the tile's quads with a key some
@@ -1088,6 +1134,13 @@ hipError_t launch_attend(const AttendArgs& a, int dtype, int n_caches, Prof& pro
   else
     hipLaunchKernelGGL((k_combine<64, 16>), dim3((unsigned)n_queries), dim3(1024), 0, s, a);
   prof.end();
+  return hipGetLastError();
+}
+
+hipError_t launch_selected_chunks(const uint32_t* sel1, int64_t words, int64_t n_queries, int64_t n_chunks,
+                                  int32_t* ids, int32_t* count, int64_t cap, hipStream_t s) {
+  hipLaunchKernelGGL(k_selected_chunks, dim3((unsigned)n_queries), dim3(kAttThreads), 0, s, sel1, words, n_chunks,
+                     ids, count, cap);
   return hipGetLastError();
 }
 

@@ -225,5 +225,9 @@ hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dty
 hipError_t launch_attend(const AttendArgs& a, int dtype, int n_caches, Prof& prof);
 // streaming probes (zha_stream_probe); arguments checked by the caller
 hipError_t launch_probe(int mode, const void* src, void* dst, int64_t n_bytes, Prof& prof);
+// level-1 bitsets -> sorted chunk id lists (zha_selected_chunks); arguments
+// checked by the caller
+hipError_t launch_selected_chunks(const uint32_t* sel1, int64_t words, int64_t n_queries, int64_t n_chunks,
+                                  int32_t* ids, int32_t* count, int64_t cap, hipStream_t s);
 
 }  // namespace zha

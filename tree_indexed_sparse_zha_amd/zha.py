@@ -196,6 +196,7 @@ def load(path: str = LIB_PATH) -> ct.CDLL:
         "zha_dense_decode": (ct.c_int, [cfgp, P, i64p, I32, P, P, i64p, I64, P, P, P, I64, P, P]),
         "zha_attend_noalloc": (ct.c_int, [cfgp, P, i64p, I32, P, P, i64p, I64, P, I64, P, ct.c_uint32, P, P, P, P]),
         "zha_stream_probe": (ct.c_int, [I32, P, P, I64, I64, P, P]),
+        "zha_selected_chunks": (ct.c_int, [P, I64, I64, I64, P, P, I64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -519,6 +520,19 @@ def attend_noalloc(cfg: ZhaConfig, Q: torch.Tensor, T: int, K: torch.Tensor, V: 
             int(flags), _ptr(out), _ptr(lse), _prof(ev), _stream(Q),
         )
     )
+
+
+def selected_chunks(sel1: torch.Tensor, n_chunks: int, cap: int):
+    """zha_selected_chunks: level-1 bitsets [n_queries, words] (int32 or
+    uint32 words) -> (chunk_ids [n_queries, cap] int32, chunk_count
+    [n_queries] int32); ids past a query's count are left at -1."""
+    assert sel1.dim() == 2 and sel1.element_size() == 4 and sel1.is_contiguous()
+    nq, words = sel1.shape
+    ids = torch.full((nq, max(int(cap), 1)), -1, dtype=torch.int32, device=sel1.device)
+    count = torch.empty(nq, dtype=torch.int32, device=sel1.device)
+    _check(load().zha_selected_chunks(_ptr(sel1), int(words), int(nq), int(n_chunks), _ptr(ids), _ptr(count),
+                                      int(cap), _stream(sel1)))
+    return ids[:, : int(cap)], count
 
 
 def stream_probe(mode: str, src: torch.Tensor, dst: torch.Tensor, n_bytes: int, ev=None):
