@@ -288,6 +288,13 @@ int zha_get_tree_layout(const zha_config* cfg, zha_tree_layout* out);
 int zha_get_route_layout(const zha_config* cfg, int32_t T, zha_route_layout* out);
 /* Scratch bytes zha_attend / zha_dense_decode need for T queries per head. */
 int64_t zha_attend_workspace_bytes(const zha_config* cfg, int32_t T);
+/* Single-number forms of the layouts above (negative on a validation
+ * error): the tree buffer (zha_get_tree_layout total_bytes), the route
+ * scratch that enables every select form (zha_get_route_layout
+ * workspace_bytes), and the dense decode's scratch (the attend scratch). */
+int64_t zha_tree_bytes(const zha_config* cfg);
+int64_t zha_route_workspace_bytes(const zha_config* cfg, int32_t T);
+int64_t zha_dense_workspace_bytes(const zha_config* cfg, int32_t T);
 
 /* ---- the hot path ------------------------------------------------------- */
 

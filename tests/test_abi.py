@@ -406,3 +406,21 @@ def test_selected_chunks_rejects_bad_arguments(lib):
     assert call(n=1 << 31) == zha.ZHA_ERR_ARG
     assert call(cap=-1) == zha.ZHA_ERR_ARG
     assert call(words=3, n=97) == zha.ZHA_ERR_CAPACITY  # 97 chunks need 4 words
+
+
+def test_single_number_size_queries_match_the_layouts(lib):
+    """zha_tree_bytes / zha_route_workspace_bytes / zha_dense_workspace_bytes
+    are the layouts' totals; an invalid configuration gives a negative code."""
+    for kw in (dict(), dict(leaf_form="weights2"), dict(g_dtype="fp8", leaf_form="weights2")):
+        cfg = cfg_deep(**kw)
+        c = cfg.c()
+        assert lib.zha_tree_bytes(ct.byref(c)) == zha.tree_layout(cfg).total_bytes
+        for T in (1, 16):
+            assert lib.zha_route_workspace_bytes(ct.byref(c), T) == zha.route_layout(cfg, T).workspace_bytes
+            assert lib.zha_dense_workspace_bytes(ct.byref(c), T) == zha.attend_workspace_bytes(cfg, T)
+    bad = cfg_deep()
+    c = bad.c()
+    c.head_dim = 96
+    assert lib.zha_tree_bytes(ct.byref(c)) < 0
+    assert lib.zha_route_workspace_bytes(ct.byref(c), 1) < 0
+    assert lib.zha_dense_workspace_bytes(ct.byref(c), 1) < 0

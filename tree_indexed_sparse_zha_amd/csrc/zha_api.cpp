@@ -441,6 +441,20 @@ int64_t zha_attend_workspace_bytes(const zha_config* cfg, int32_t T) {
   return attend_ws(cfg, T);
 }
 
+int64_t zha_tree_bytes(const zha_config* cfg) {
+  zha_tree_layout tl;
+  const int rc = zha_get_tree_layout(cfg, &tl);
+  return rc ? rc : tl.total_bytes;
+}
+
+int64_t zha_route_workspace_bytes(const zha_config* cfg, int32_t T) {
+  zha_route_layout rl;
+  const int rc = zha_get_route_layout(cfg, T, &rl);
+  return rc ? rc : rl.workspace_bytes;
+}
+
+int64_t zha_dense_workspace_bytes(const zha_config* cfg, int32_t T) { return zha_attend_workspace_bytes(cfg, T); }
+
 int zha_build(const zha_config* cfg, const void* K, const int64_t k_strides[3], int64_t n_tokens,
               const float* ref, void* tree, zha_profile* prof, void* stream) {
   return do_build(cfg, K, k_strides, 0, n_tokens, ref, tree, prof, stream, false);

@@ -197,6 +197,9 @@ def load(path: str = LIB_PATH) -> ct.CDLL:
         "zha_attend_noalloc": (ct.c_int, [cfgp, P, i64p, I32, P, P, i64p, I64, P, I64, P, ct.c_uint32, P, P, P, P]),
         "zha_stream_probe": (ct.c_int, [I32, P, P, I64, I64, P, P]),
         "zha_selected_chunks": (ct.c_int, [P, I64, I64, I64, P, P, I64, P]),
+        "zha_tree_bytes": (I64, [cfgp]),
+        "zha_route_workspace_bytes": (I64, [cfgp, I32]),
+        "zha_dense_workspace_bytes": (I64, [cfgp, I32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
