@@ -490,7 +490,7 @@ __global__ __launch_bounds__(64 * W) void k_build_span(BuildArgs A) {
 // node from the stored fp32 children) therefore reproduces a fresh build bit
 // for bit when both of its passes also run here.
 template <int D, int NU, int C, int GF = 0>
-__global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
+__global__ __launch_bounds__(256, NU <= 3 ? 4 : 3) void k_build_mf(BuildArgs A) {
   constexpr bool G8 = GF == 1;  // levels written by put_node hold fp8 rows
   constexpr bool G4 = GF == 2;  // ... or MXFP4 blocks (d = 128)
   static_assert(!G4 || D == 128, "MXFP4 rows need d = 128 (a 32-block is four lanes of a wave)");
@@ -504,8 +504,14 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
   constexpr int KB = 16;
   constexpr int KROW = PIECES + 1;  // padded LDS key row (uint4)
   constexpr int NUR = NU > 0 ? NU : 1;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int j = lane & 15, g = lane >> 4;
+  // lane indices: lane, j, g and d0 are re-declared opaque at the top of
+  // every round (an empty asm that may change them), so that the compiler
+  // derives the per-lane addresses inside the round instead of keeping them
+  // all live across the loop (about 250 VGPRs and 2 waves per SIMD, against
+  // 128-160 and 3-4 waves per SIMD now)
+  int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int j = lane & 15, g = lane >> 4;
   const TreeGeom& geo = A.geo;
   const int R = geo.R;
   const int cache = blockIdx.y;
@@ -516,7 +522,7 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
   if (t0 >= tend) return;  // uniform over the workgroup
   const float isd = A.inv_sqrt_d;
   const int top = A.top_level;
-  const int d0 = VPL * (4 * wave + g);  // this lane's first d above level 2
+  int d0 = VPL * (4 * wave + g);  // this lane's first d above level 2
 
   __shared__ uint4 Ks[4][KB * KROW];
   __shared__ float zs[4][16][KB + 1];
@@ -761,6 +767,7 @@ __global__ __launch_bounds__(256, 2) void k_build_mf(BuildArgs A) {
   for (int a = 0; a < NUR; ++a) uu[a] = false;
 
   for (int64_t r = 0; r < nrounds; ++r) {
+    asm volatile("" : "+v"(lane), "+v"(j), "+v"(g), "+v"(d0));
     const int nk = block_keys(r);
     const int64_t kb0 = t0 + 64 * r + 16 * wave;  // this wave's 16-key block
     if (nk > 0) {
