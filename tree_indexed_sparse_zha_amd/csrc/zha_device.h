@@ -28,6 +28,13 @@ struct Elem<bf16_t> {
 };
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+// 16-byte load with the nontemporal hint (a streamed operand read once,
+// whole 128-byte lines per instruction)
+__device__ __forceinline__ uint4 ld16_nt(const void* p) {
+  typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+  const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // Raw buffer loads: the base is wave-uniform, offsets are bytes, and a load
 // at an offset past `bytes` returns zeros (no branch, no fault), so masked

@@ -209,7 +209,8 @@ __global__ __launch_bounds__(256) void k_score_bf16(ScoreArgs A) {
       const char* gn = gcache + m * gnode;
 #pragma unroll
       for (int s = 0; s < NL; ++s)
-        af[k][s] = live && jrow < R ? ld16(gn + ((int64_t)(4 * s + kg) * R + jrow) * 16) : make_uint4(0, 0, 0, 0);
+        // (each node's rows are read once per call: nontemporal)
+        af[k][s] = live && jrow < R ? ld16_nt(gn + ((int64_t)(4 * s + kg) * R + jrow) * 16) : make_uint4(0, 0, 0, 0);
       if constexpr (G8) sv[k] = live && jrow < R ? scache[m * R + jrow] : 0.f;
       if constexpr (G4) sv[k] = __uint_as_float(live && jrow < R ? s4cache[m * R + jrow] : 0u);
 #pragma unroll
