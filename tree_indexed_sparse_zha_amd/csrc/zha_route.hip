@@ -919,9 +919,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 // Level 1 after a fused level-2 pass (chunk 4, at most 4 queries per cache):
 // that pass wrote the plane score of every chunk of its candidates; a chunk
 // is a candidate of a query iff the query kept its parent, so the others
-// become -inf here, and every (query, 256-key tile) publishes its candidate
-// key range for the select.  Wave w of a workgroup is query w; a workgroup
-// walks kMaskTiles consecutive tiles of 64 chunks.
+// become -inf here, and every (query, workgroup) publishes the candidate key
+// range of its kMaskTiles x 64 chunks for the select (one slot per
+// workgroup).  Wave w of a workgroup is query w; a workgroup walks
+// kMaskTiles consecutive tiles of 64 chunks.
 constexpr int kMaskTiles = 16;
 __global__ __launch_bounds__(256) void k_score_mask1(ScoreArgs A, int64_t n_tiles) {
   const int qi = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -950,6 +951,7 @@ __global__ __launch_bounds__(256) void k_score_mask1(ScoreArgs A, int64_t n_tile
     const float x = bld4f<0>(sr, kept ? (uint32_t)((lane + 64 * t) * 4) : kOffNone);
     v[t] = kept ? x : kNegInf;
   }
+  uint32_t kmax = 0u, kmin = 0xffffffffu, cnt = 0u;
 #pragma unroll
   for (int t = 0; t < kMaskTiles; ++t) {
     const int64_t tile = (int64_t)blockIdx.x * kMaskTiles + t;
@@ -957,8 +959,20 @@ __global__ __launch_bounds__(256) void k_score_mask1(ScoreArgs A, int64_t n_tile
     const int64_t m = m0 + 64 * t;
     const bool kept = (pw[t] >> ((m / 4) & 31)) & 1u;
     if (!kept && m < A.n_nodes) srow[m] = kNegInf;
-    publish_range(A.keyrange + (row * A.kr_slots + tile) * 4, v[t] > kNegInf, order_key(v[t]));
+    if (v[t] > kNegInf) {
+      const uint32_t k = order_key(v[t]);
+      kmax = max(kmax, k);
+      kmin = min(kmin, k);
+      ++cnt;
+    }
   }
+  for (int o = 1; o < 64; o <<= 1) {
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+    cnt += (uint32_t)__shfl_xor((int)cnt, o);
+  }
+  if (lane == 0)
+    *reinterpret_cast<uint4*>(A.keyrange + (row * A.kr_slots + blockIdx.x) * 4) = make_uint4(kmax, kmin, cnt, 0u);
 }
 
 // Levels >= 2 for many queries per cache (QC > 16, bf16 g, R > 8): a
@@ -2620,6 +2634,8 @@ hipError_t launch_route_level(const ScoreArgs& sa, const SelectArgs& se, int dty
   SelectArgs sel = se;
   if (sa.n_nodes <= 0)
     sel.kr_used = 0;
+  else if (sa.fuse1)  // k_score_mask1: one slot per workgroup of kMaskTiles tiles
+    sel.kr_used = ((sa.n_nodes * sa.wkeys + kt - 1) / kt + kMaskTiles - 1) / kMaskTiles;
   else if (sa.leaf_weights)
     sel.kr_used = (sa.n_nodes * sa.wkeys + kt - 1) / kt;
   else if (dtype == 1)
