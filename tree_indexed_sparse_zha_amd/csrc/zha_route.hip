@@ -1229,17 +1229,18 @@ __device__ __forceinline__ unsigned long long fixed_mass(float s, float mx, doub
   return (unsigned long long)llrint((double)expf(s - mx) * scale);
 }
 
-// Block-wide sum of a 64-bit value.
+// Block-wide sum of a 64-bit value (blocks of kSelThreads): within each
+// wave by shuffles, then over the waves' totals in LDS (two barriers; the
+// integer sum is exact in any order).
 __device__ unsigned long long block_sum_u64(unsigned long long v, unsigned long long* red) {
   const int tid = threadIdx.x;
-  red[tid] = v;
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  if ((tid & 63) == 0) red[tid >> 6] = v;
   __syncthreads();
-  for (int off = kSelThreads / 2; off > 0; off >>= 1) {
-    if (tid < off) red[tid] += red[tid + off];
-    __syncthreads();
-  }
-  const unsigned long long r = red[0];
-  __syncthreads();
+  unsigned long long r = 0ull;
+#pragma unroll
+  for (int w = 0; w < kSelThreads / 64; ++w) r += red[w];
+  __syncthreads();  // red is free again
   return r;
 }
 
@@ -1250,24 +1251,25 @@ __device__ unsigned long long block_sum_u64(unsigned long long v, unsigned long 
 __device__ int find_bin(const unsigned long long* hist, int nbins, unsigned long long P,
                         unsigned long long* A_io, unsigned long long* red, int* sh_bin,
                         unsigned long long* sh_above) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int per = nbins >= kSelThreads ? nbins / kSelThreads : 1;
   const int b0 = tid * per;
   const int nb = b0 < nbins ? per : 0;
   unsigned long long mine = 0;
   for (int i = 0; i < nb; ++i) mine += hist[b0 + i];
-  red[tid] = mine;
-  __syncthreads();
-  // inclusive suffix scan (Hillis-Steele) over the threads' sums
-  for (int off = 1; off < kSelThreads; off <<= 1) {
-    const unsigned long long add = (tid + off < kSelThreads) ? red[tid + off] : 0ull;
-    __syncthreads();
-    red[tid] += add;
-    __syncthreads();
+  // inclusive suffix sum over the threads' sums: within the wave by
+  // shuffles, then the totals of the higher waves from LDS
+  unsigned long long suf = mine;
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned long long t = __shfl_down(suf, o);
+    if (lane + o < 64) suf += t;
   }
-  unsigned long long cum = *A_io + (red[tid] - mine);  // mass of the bins above this thread's range
+  if (lane == 0) red[wv] = suf;
   if (tid == 0) *sh_bin = -1;
   __syncthreads();
+  unsigned long long higher = 0ull;
+  for (int w = wv + 1; w < kSelThreads / 64; ++w) higher += red[w];
+  unsigned long long cum = *A_io + higher + (suf - mine);  // mass of the bins above this thread's range
   for (int i = nb - 1; i >= 0; --i) {
     const unsigned long long h = hist[b0 + i];
     if (cum < P && P <= cum + h) {
@@ -1539,7 +1541,7 @@ constexpr int kLinBins = 2048;
 constexpr int kCutCap = 1536;
 // parent bits held in LDS (dynamic, sized per launch to the words a row
 // reaches): levels of up to 163,840 parents (with the static arrays, at
-// most 68 KiB of the 160 KiB a workgroup may take)
+// most 61 KiB of the 160 KiB a workgroup may take)
 constexpr int kParentWords = 5120;
 constexpr int kSelUnroll = 4;
 
@@ -1561,17 +1563,16 @@ __device__ __forceinline__ float4 row_f4(const float4* row4, int64_t n4, const u
 
 __device__ uint32_t block_minmax_u32(uint32_t v, bool want_max, unsigned long long* red) {
   const int tid = threadIdx.x;
-  red[tid] = v;
-  __syncthreads();
-  for (int off = kSelThreads / 2; off > 0; off >>= 1) {
-    if (tid < off) {
-      const uint32_t a = (uint32_t)red[tid], b = (uint32_t)red[tid + off];
-      red[tid] = want_max ? max(a, b) : min(a, b);
-    }
-    __syncthreads();
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t u = (uint32_t)__shfl_xor((int)v, o);
+    v = want_max ? max(v, u) : min(v, u);
   }
-  const uint32_t r = (uint32_t)red[0];
+  if ((tid & 63) == 0) red[tid >> 6] = v;
   __syncthreads();
+  uint32_t r = (uint32_t)red[0];
+#pragma unroll
+  for (int w = 1; w < kSelThreads / 64; ++w) r = want_max ? max(r, (uint32_t)red[w]) : min(r, (uint32_t)red[w]);
+  __syncthreads();  // red is free again
   return r;
 }
 
@@ -1588,7 +1589,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs A) {
   const int64_t nwords = (n + 31) / 32;
 
   __shared__ unsigned long long hist[2048];
-  __shared__ unsigned long long red[kSelThreads];
+  __shared__ unsigned long long red[kSelThreads / 64];  // per-wave partials of the block reductions
   __shared__ int sh_bin;
   __shared__ unsigned long long sh_above;
   __shared__ uint32_t l_key[kCutCap];
@@ -2319,7 +2320,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_hist(SelectArgs A) {
   const SelState s = *sel_state(A, q);
   if (s.phase != 0) return;
   __shared__ unsigned long long hist[2048];
-  __shared__ unsigned long long red[kSelThreads];
+  __shared__ unsigned long long red[kSelThreads / 64];  // per-wave partials of the block reductions
   const int w = s.lo < 11 ? s.lo : 11;
   const int nb = 1 << w;
   const int64_t n = A.n_nodes;
@@ -2347,7 +2348,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_find(SelectArgs A, int64
   SelState s = *sel_state(A, q);
   if (s.phase != 0) return;
   __shared__ unsigned long long hist[2048];
-  __shared__ unsigned long long red[kSelThreads];
+  __shared__ unsigned long long red[kSelThreads / 64];  // per-wave partials of the block reductions
   __shared__ int sh_bin;
   __shared__ unsigned long long sh_above;
   const int w = s.lo < 11 ? s.lo : 11;
@@ -2408,7 +2409,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_ties(SelectArgs A) {
   const int64_t seg = blockIdx.x, q = blockIdx.y;
   const SelState s = *sel_state(A, q);
   if (s.phase != 1 || s.need_tie == 0ull) return;
-  __shared__ unsigned long long red[kSelThreads];
+  __shared__ unsigned long long red[kSelThreads / 64];  // per-wave partials of the block reductions
   int64_t w0, w1;
   segment_words(A, seg, &w0, &w1);
   const unsigned long long c =
@@ -2419,7 +2420,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_ties(SelectArgs A) {
 __global__ __launch_bounds__(kSelThreads) void k_select_bits(SelectArgs A) {
   const int64_t seg = blockIdx.x, q = blockIdx.y;
   const SelState s = *sel_state(A, q);
-  __shared__ unsigned long long red[kSelThreads];
+  __shared__ unsigned long long red[kSelThreads / 64];  // per-wave partials of the block reductions
   int64_t w0, w1;
   segment_words(A, seg, &w0, &w1);
   uint32_t* srow = A.sel + q * A.words;
