@@ -80,9 +80,9 @@ enum zha_dtype { ZHA_F32 = 0, ZHA_BF16 = 1 };
  *     with at most 4 queries per cache and routing from level 2 or above,
  *     that pass also forms the level-1 scores of its children (the keys of
  *     a candidate are read once) and keeps the logits when the caller
- *     passes the buffer; that pass reads only the keys and the L of the
- *     node and of its children, and recomputes the weights, shares and c
- *     from the reference queries the tree keeps (ref_offset) and the keys,
+ *     passes the buffer; that pass reads only the keys: it recomputes the
+ *     log masses L of the node and of its children, the weights, shares and
+ *     c from the reference queries the tree keeps (ref_offset) and the keys,
  *     to fp32 rounding of the stored ones.  A level-2 node occupies R*(4C+8) bytes instead of
  *     R*(2d+8).  Supported with bf16, chunk 4 and 3..8 levels, with either
  *     g_dtype (ZHA_G_FP8 then stores levels >= 3 in fp8); not with the
@@ -185,7 +185,8 @@ typedef struct zha_tree_layout {
   int64_t ref_offset;     /* ZHA_LEAF_WEIGHTS2: the reference queries the tree was
                              built with, [H][R][d] fp32 (zha_build and zha_append
                              store them; routing recomputes the level-1 and
-                             level-2 weights from them and the stored L); else -1 */
+                             level-2 log masses and weights from them and the
+                             keys); else -1 */
 } zha_tree_layout;
 
 /*

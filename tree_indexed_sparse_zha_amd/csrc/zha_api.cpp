@@ -597,8 +597,6 @@ static int do_route(const zha_config* cfg, const void* tree, int64_t n_tokens, c
       sa.nquads = tl.node_cap[0] * cfg->chunk / 4;
       sa.QW = logits_row(sa.QC);
       if (l == 1) {  // level 2 holding child shares: the level-1 rows it reads (and fills)
-        sa.L = reinterpret_cast<const float*>(static_cast<const char*>(tree) + tl.L_offset[1]);
-        sa.L1 = reinterpret_cast<const float*>(static_cast<const char*>(tree) + tl.L_offset[0]);
         sa.ref = reinterpret_cast<const float*>(static_cast<const char*>(tree) + tl.ref_offset);
         sa.w1 = reinterpret_cast<const float*>(static_cast<const char*>(tree) + tl.g_offset[0]);
         sa.c1 = reinterpret_cast<const float*>(static_cast<const char*>(tree) + tl.c_offset[0]);

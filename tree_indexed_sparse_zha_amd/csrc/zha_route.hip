@@ -478,8 +478,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
   const int b = cache / A.H, h = cache % A.H;
   // MODE 2: the tree's reference queries in bf16 (exact: they hold bf16
   // values) in LDS, read per group as a second B operand (column = plane
-  // j = qn), so that the weights come from z_ji = r_j . k_i / sqrt(d) and
-  // the stored L instead of memory
+  // j = qn), so that the log masses, weights, shares and offsets of both
+  // levels come from z_ji = r_j . k_i / sqrt(d) instead of memory
   // (loaded here, stored to LDS once the tile's key loads are issued)
   constexpr int RPC = D / 8;  // 16-byte bf16 pieces of a reference row
   __shared__ uint4 refs[MODE == 2 ? 16 : 1][RPC + 1];
@@ -560,19 +560,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     cst[r] = bld4f(cr, ok ? (uint32_t)((x * R + j) * 4) : kOffNone);
   }
   }
-  // MODE 2: L of each of the lane's 4 nodes and of chunk kg of each (plane qn)
-  float L1v[MODE == 2 ? GPW : 1], L2v[MODE == 2 ? GPW : 1];
-  if constexpr (MODE == 2) {
-    const rsrc_t l1r = make_rsrc(A.L1 + ((int64_t)cache * A.node_cap1 + c0) * R, (uint32_t)(n1v * R * 4));
-    const rsrc_t l2r = make_rsrc(A.L + ((int64_t)cache * A.node_cap + m0) * R, (uint32_t)(n_valid * R * 4));
-#pragma unroll
-    for (int gi = 0; gi < GPW; ++gi) {
-      const int g = wave * GPW + gi;
-      const bool ok = ((anybits >> g) & 1ull) && qn < R;
-      L1v[gi] = bld4f<0>(l1r, ok ? (uint32_t)(((4 * g + kg) * R + qn) * 4) : kOffNone);
-      L2v[gi] = bld4f<0>(l2r, ok ? (uint32_t)((g * R + qn) * 4) : kOffNone);
-    }
-  }
   uint4 kf[GPW][NS];
   bool live[GPW];
 #pragma unroll
@@ -633,31 +620,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       for (int i = 0; i < 4; ++i) st4_nt(lp + i * A.QW, zz[i]);
     }
     if constexpr (MODE == 2) {
-      // lane (plane j = qn, chunk kg of node g): z of the chunk's 4 keys, its
-      // weights w = exp(z - L(chunk)), offset c = L(chunk) - sum w z, its share
-      // rho = exp(L(chunk) - L(node)); the node's offset is L(node) - sum over
-      // its chunks of rho (L(chunk) - c(chunk))
+      // lane (plane j = qn, chunk kg of node g): z of the chunk's 4 keys; the
+      // chunk's log mass L(chunk) = LSE z (formed as the build forms it), its
+      // weights w = exp(z - L(chunk)), offset c = L(chunk) - sum w z; the
+      // node's log mass L(node) = LSE over its complete chunks of L(chunk)
+      // (4 lanes), each chunk's share rho = exp(L(chunk) - L(node)), and the
+      // node's offset L(node) - sum over its chunks of rho (L(chunk) - c(chunk)).
+      // Nothing of the stored tree is read: both levels come from the keys
+      // and the reference queries alone.
       f32x4 zr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < NS; ++s)
         zr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[gi][s]), as_bf16x8(refs[qn][4 * s + kg]), zr, 0, 0, 0);
       const bool ok = qn < R && c0 + 4 * g + kg < n1;
+      float zi[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zi[i] = zr[i] * A.inv_sqrt_d;
+      const float m1 = fmaxf(fmaxf(zi[0], zi[1]), fmaxf(zi[2], zi[3]));
+      float e[4], s1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        e[i] = __expf(zi[i] - m1);
+        s1 += e[i];
+      }
+      const float L1 = m1 + __logf(s1);
+      const float inv1 = 1.f / s1;
       float w[4], wz = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float zi = zr[i] * A.inv_sqrt_d;
-        w[i] = ok ? __expf(zi - L1v[gi]) : 0.f;
-        wz = fmaf(w[i], zi, wz);
+        w[i] = ok ? e[i] * inv1 : 0.f;
+        wz = fmaf(w[i], zi[i], wz);
       }
-      const float rho = ok ? __expf(L1v[gi] - L2v[gi]) : 0.f;
+      float m2 = ok ? m1 : kNegInf;
+      m2 = fmaxf(m2, __shfl_xor(m2, 16));
+      m2 = fmaxf(m2, __shfl_xor(m2, 32));
+      const float pl = ok ? s1 * __expf(m1 - m2) : 0.f;  // this chunk's mass relative to the node max
+      float ps = pl + __shfl_xor(pl, 16);
+      ps += __shfl_xor(ps, 32);
+      const float L2 = m2 + __logf(ps);
+      const float rho = ok ? pl / ps : 0.f;
       float t = rho * wz;
       t += __shfl_xor(t, 16);
       t += __shfl_xor(t, 32);
       if (qn < R) {
         wl[g][wix(qn, kg)] = make_float4(w[0], w[1], w[2], w[3]);
         rl[g][qn * PARTS + kg] = rho;
-        c1l[4 * g + kg][qn] = L1v[gi] - wz;
-        if (kg == 0) cl[g][qn] = L2v[gi] - t;
+        c1l[4 * g + kg][qn] = L1 - wz;
+        if (kg == 0) cl[g][qn] = L2 - t;
       }
     }
     if constexpr (Q4) {
