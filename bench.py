@@ -264,18 +264,21 @@ def cpu_baseline(w: W.Workload, batch, n0: int, p: float, T: int, cfg: zha.ZhaCo
 
     v_all, used_all, nc_all, nq_all, t_all = run(host_cores)
     v_one, used_one, nc_one, nq_one, t_one = run(1)
+    n_built = len(cache_data)  # full builds, all under the all-cores setting
     return {
         "value": v_all,
         "unit": "queries/s",
         "cores": int(used_all),
         "kind": "oracle",
         "value_1_thread": v_one,
+        "build_tokens_per_s": n_built * n1 / t_build_full if t_build_full > 0 else None,
         "sample": (
             f"caches (sequence, KV head) of the workload's {cfg.n_caches} at {n1} tokens, each one step: build of "
             f"the appended {A}-token top span + route and attend of its {w.q_per_kv * T} queries; fp64 numpy. "
             f"All cores: {nc_all} caches, {nq_all} queries, {t_all:.1f} s timed, BLAS threads {used_all}. "
             f"One thread: {nc_one} caches, {nq_one} queries, {t_one:.1f} s timed, BLAS threads {used_one}. "
-            f"The oracle's initial full tree builds ({t_build_full:.1f} s) are not counted; other numpy work is "
+            f"The oracle's initial full tree builds ({n_built} caches x {n1} tokens, {t_build_full:.1f} s, "
+            f"BLAS threads {used_all}: build_tokens_per_s) are not counted in value; other numpy work is "
             f"single-threaded. Host {platform.processor() or platform.machine()}, {host_cores} usable cores"
         ),
     }
@@ -547,7 +550,8 @@ def frame(res, args, steps, warmup, metric=METRIC):
 
 def sweep_main(args):
     """One JSON line per point: the crossover curve of the deep tree (the 1M
-    workload's recipe at other context lengths) and of the lightweight
+    workload's recipe at other context lengths, and the 10M workload's
+    shape at 2M and 4M tokens) and of the lightweight
     geometry, the other p of the 1M workload, and the other configurations
     (32K deep with 64 queries per head, 256K wide, 10M deep with its full
     build timed).  Each point: 2 warm-up + 4 timed steps, the flushed
@@ -556,8 +560,10 @@ def sweep_main(args):
     import dataclasses
 
     points = []
-    for n in (32768, 65536, 131072, 262144, 524288, 1048576, 2097152):
+    for n in (8192, 16384, 32768, 65536, 131072, 262144, 524288, 1048576, 2097152):
         points.append(("deep-crossover", "deep1m", n, None))
+    for n in (2097152, 4194304):  # the 10M workload's shape (4 caches) at shorter contexts
+        points.append(("deep10m-crossover", "deep10m", n, None))
     for n in (16384, 32768, 49152, 65536, 131072, 262144, 1048576, 4194304):
         points.append(("light-crossover", "light1m", n, None))
     points.append(("deep1m-p", "deep1m", None, 0.9))
