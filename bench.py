@@ -592,8 +592,11 @@ def probe_main(args):
     n = 8 << 30
     src = torch.empty(n // 4, dtype=torch.int32, device="cuda").random_()
     ev = zha.HipEvents(1)
-    for mode in ("read", "read_nt", "read_slab", "read_slab_nt", "copy", "copy_nt", "mix", "mix_nt"):
-        if mode.startswith("copy"):
+    for mode in ("read", "read_nt", "read_slab", "read_slab_nt", "copy", "copy_nt", "mix", "mix_nt", "tile_mix"):
+        if mode == "tile_mix":
+            dst = torch.empty(n // 64, dtype=torch.int32, device="cuda")
+            moved = n + n // 16
+        elif mode.startswith("copy"):
             dst = torch.empty(n // 4, dtype=torch.int32, device="cuda")
             moved = 2 * n
         elif mode.startswith("mix"):
@@ -620,7 +623,10 @@ def probe_main(args):
                      "copy": "read + write of the same bytes",
                      "copy_nt": "as copy, nontemporal loads and stores",
                      "mix": "4 bytes read per byte written (key-reading score passes)",
-                     "mix_nt": "as mix, nontemporal stores"}[mode],
+                     "mix_nt": "as mix, nontemporal stores",
+                     "tile_mix": "64 KiB tiles of 256 rows x 256 B, one per workgroup, loaded 16 rows x 64 B per "
+                                 "instruction (the key-reading passes' operand layout), 1 byte written per 16 read "
+                                 "(nontemporal): the fused level-2 pass's shape and mix"}[mode],
         }), flush=True)
         del dst
     del src

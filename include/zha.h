@@ -515,7 +515,14 @@ int zha_dense_decode(const zha_config* cfg, const void* Q, const int64_t q_strid
  *                          per byte
  *                          written (plain / nontemporal stores), the mix of
  *                          the scoring passes that read keys and write
- *                          logits.
+ *                          logits;
+ *   ZHA_PROBE_TILE_MIX     one 64 KiB tile of src per workgroup (256 rows of
+ *                          256 bytes), each load instruction covering 16 rows
+ *                          x 64 bytes (the matrix-core operand layout of the
+ *                          key-reading passes), then one 16-byte piece per
+ *                          256 bytes read written to dst[0, n_bytes / 16)
+ *                          (nontemporal): the tile shape and 16:1
+ *                          read/write mix of the fused level-2 pass.
  *   src, dst  device, 16-byte aligned, not overlapping; dst_bytes its size.
  *   n_bytes   a positive multiple of 64.
  * Errors: ZHA_ERR_ARG (mode, n_bytes), ZHA_ERR_NULL, ZHA_ERR_ALIGN,
@@ -529,7 +536,8 @@ enum zha_probe_mode {
   ZHA_PROBE_MIX = 4,
   ZHA_PROBE_MIX_NT = 5,
   ZHA_PROBE_READ_SLAB = 6,
-  ZHA_PROBE_READ_SLAB_NT = 7
+  ZHA_PROBE_READ_SLAB_NT = 7,
+  ZHA_PROBE_TILE_MIX = 8
 };
 int zha_stream_probe(int32_t mode, const void* src, void* dst, int64_t n_bytes, int64_t dst_bytes,
                      zha_profile* prof, void* stream);

@@ -381,6 +381,9 @@ def test_stream_probe_rejects_bad_arguments(lib):
     with pytest.raises(zha.ZhaError) as ei:  # read-only probes write one word per workgroup
         zha.stream_probe("read", src, dst, 4096)
     assert ei.value.code == zha.ZHA_ERR_CAPACITY
+    with pytest.raises(zha.ZhaError) as ei:  # the tile mix writes 16 bytes per 256 read
+        zha.stream_probe("tile_mix", src, dst[:60], 4096)
+    assert ei.value.code == zha.ZHA_ERR_CAPACITY
     with pytest.raises(zha.ZhaError) as ei:
         zha.stream_probe("mix", src, src, 4096)
     assert ei.value.code == zha.ZHA_ERR_ARG

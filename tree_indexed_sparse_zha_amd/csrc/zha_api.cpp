@@ -827,12 +827,15 @@ int zha_stream_probe(int32_t mode, const void* src, void* dst, int64_t n_bytes, 
                      zha_profile* prof, void* stream) {
   int rc = check_prof(prof);
   if (rc) return rc;
-  if (mode < ZHA_PROBE_READ || mode > ZHA_PROBE_READ_SLAB_NT) return fail(ZHA_ERR_ARG, "probe mode %d unknown", mode);
+  if (mode < ZHA_PROBE_READ || mode > ZHA_PROBE_TILE_MIX) return fail(ZHA_ERR_ARG, "probe mode %d unknown", mode);
   if (n_bytes < 64 || n_bytes % 64) return fail(ZHA_ERR_ARG, "n_bytes must be a positive multiple of 64");
   if ((rc = check_ptr16(src, "src"))) return rc;
   if ((rc = check_ptr16(dst, "dst"))) return rc;
-  const bool read_only = mode <= ZHA_PROBE_READ_NT || mode >= ZHA_PROBE_READ_SLAB;
-  const int64_t need = read_only ? 16384 : mode <= ZHA_PROBE_COPY_NT ? n_bytes : n_bytes / 4;
+  const bool read_only = mode <= ZHA_PROBE_READ_NT || mode == ZHA_PROBE_READ_SLAB || mode == ZHA_PROBE_READ_SLAB_NT;
+  const int64_t need = read_only                    ? 16384
+                       : mode <= ZHA_PROBE_COPY_NT  ? n_bytes
+                       : mode == ZHA_PROBE_TILE_MIX ? (n_bytes / 16 + 15) / 16 * 16
+                                                    : n_bytes / 4;
   if (dst_bytes < need)
     return fail(ZHA_ERR_CAPACITY, "dst holds %lld bytes, the probe writes up to %lld", (long long)dst_bytes,
                 (long long)need);

@@ -129,6 +129,32 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_mix(const u32x4* __rest
   }
 }
 
+// Tiles of 256 rows x 256 bytes (64 KiB), one per workgroup, loaded in the
+// operand layout of the key-reading score passes (each load instruction
+// covers 16 rows x 64 bytes; 16 pieces in flight per lane), folded, and one
+// 16-byte piece written per 256 bytes read (nontemporal): the read/write
+// mix and tile shape of the fused level-2 pass (4 KiB written per 64 KiB
+// tile of keys).  Pieces past n16 read as zero.
+__global__ __launch_bounds__(kProbeThreads) void k_probe_tile_mix(const u32x4* __restrict__ src, int64_t n16,
+                                                                  u32x4* __restrict__ dst) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qn = lane & 15, kg = lane >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * 4096;  // first piece of the tile
+  u32x4 v[16];
+#pragma unroll
+  for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int64_t i = t0 + (int64_t)(64 * wave + 16 * gi + qn) * 16 + 4 * s + kg;
+      v[4 * gi + s] = i < n16 ? src[i] : u32x4{0u, 0u, 0u, 0u};
+    }
+  u32x4 x = v[0];
+#pragma unroll
+  for (int t = 1; t < 16; ++t) x ^= v[t];
+  const int64_t o = (int64_t)blockIdx.x * kProbeThreads + tid;  // stands for pieces [16 o, 16 o + 16)
+  if (16 * o < n16) __builtin_nontemporal_store(x, dst + o);
+}
+
 }  // namespace
 
 hipError_t launch_probe(int mode, const void* src, void* dst, int64_t n_bytes, Prof& prof) {
@@ -171,6 +197,13 @@ hipError_t launch_probe(int mode, const void* src, void* dst, int64_t n_bytes, P
       hipLaunchKernelGGL(k_probe_mix<true>, dim3((unsigned)slabs), dim3(kProbeThreads), 0, s, in, n16,
                          static_cast<u32x4*>(dst));
       break;
+    case ZHA_PROBE_TILE_MIX: {
+      const int64_t tiles = (n16 + 4095) / 4096;
+      if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+      hipLaunchKernelGGL(k_probe_tile_mix, dim3((unsigned)tiles), dim3(kProbeThreads), 0, s, in, n16,
+                         static_cast<u32x4*>(dst));
+      break;
+    }
     default:
       return hipErrorInvalidValue;
   }

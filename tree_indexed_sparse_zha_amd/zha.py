@@ -116,7 +116,7 @@ K_BUILD, K_SCORE, K_SELECT, K_ATTEND, K_COMBINE, K_PROBE = 1, 2, 3, 4, 5, 6
 KERNEL_NAMES = {K_BUILD: "build", K_SCORE: "score", K_SELECT: "select", K_ATTEND: "attend", K_COMBINE: "combine",
                 K_PROBE: "probe"}
 PROBE_MODES = {"read": 0, "read_nt": 1, "copy": 2, "copy_nt": 3, "mix": 4, "mix_nt": 5, "read_slab": 6,
-               "read_slab_nt": 7}
+               "read_slab_nt": 7, "tile_mix": 8}
 
 
 class Profile(ct.Structure):
