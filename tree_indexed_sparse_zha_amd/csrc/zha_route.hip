@@ -1835,8 +1835,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs A) {
 }
 
 // Wave form: one wave per query for rows of at most kWaveRow candidates
-// (lane l holds candidates 32l .. 32l + 31 in registers, and later writes
-// bitset word l).  Same fixed-point masses and the same cut as k_select;
+// (register i of lane l holds candidate 64i + l, so that the steps past the
+// row's end, i >= ceil(n / 64), are skipped by the whole wave; step i's
+// ballot is bitset words 2i and 2i + 1).  Same fixed-point masses and the
+// same cut as k_select;
 // the radix digits are 8 bits wide (a 256-bin histogram per wave in LDS),
 // which changes the number of passes, not the key found: each pass narrows
 // to the one bin whose mass interval holds P, and the last pass ends at the
@@ -1853,25 +1855,18 @@ __global__ __launch_bounds__(256) void k_select_wave(SelectArgs A, int64_t n_que
   __shared__ unsigned long long hist_all[4][256];
   unsigned long long* hist = hist_all[wave];
   const int64_t n = A.n_nodes;
-  const int64_t n4 = (n + 3) / 4;
-  const float4* row4 = reinterpret_cast<const float4*>(A.score + q * A.score_stride);
+  const int nit = (int)((n + 63) / 64);  // steps holding candidates (<= 32; the same in every lane)
+  const float* row = A.score + q * A.score_stride;
   uint32_t* srow = A.sel + q * A.words;
   SelStats* st = reinterpret_cast<SelStats*>(A.stats) + q;
   const int64_t nwords = (n + 31) / 32;
 
   float v[32];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int64_t b4 = 8 * (int64_t)lane + c;
-    const float4 f = b4 < n4 ? row4[b4] : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
-    v[4 * c] = f.x;
-    v[4 * c + 1] = f.y;
-    v[4 * c + 2] = f.z;
-    v[4 * c + 3] = f.w;
+  for (int i = 0; i < 32; ++i) {
+    const int64_t e = 64 * (int64_t)i + lane;
+    v[i] = (i < nit && e < n) ? row[e] : kNegInf;
   }
-#pragma unroll
-  for (int i = 0; i < 32; ++i)
-    if (32 * (int64_t)lane + i >= n) v[i] = kNegInf;
 
   // candidate key range and count from the score tiles' slots
   uint32_t kmax = 0u, kmin = 0xffffffffu;
@@ -1920,7 +1915,7 @@ __global__ __launch_bounds__(256) void k_select_wave(SelectArgs A, int64_t n_que
     unsigned long long part = 0;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      const float s = v[i];
+      const float s = i < nit ? v[i] : kNegInf;
       if (s > kNegInf) {
         const uint32_t k = order_key(s);
         const bool match = top >= 32 || (k >> top) == want;
@@ -1984,49 +1979,48 @@ __global__ __launch_bounds__(256) void k_select_wave(SelectArgs A, int64_t n_que
     tau = want;
     const unsigned long long need = ties_needed(tau, P, above, h_tau, mx, scale);
     if (need) {
-      // the need-th tie in id order: lanes hold consecutive ids
-      uint32_t tb = 0u;
-#pragma unroll
-      for (int i = 0; i < 32; ++i)
-        if (v[i] > kNegInf && order_key(v[i]) == tau) tb |= 1u << i;
-      const unsigned long long c = __popc(tb);
-      unsigned long long pre = c;
-      for (int o = 1; o < 64; o <<= 1) {
-        const unsigned long long t = __shfl_up(pre, o);
-        if (lane >= o) pre += t;
-      }
-      const unsigned long long before = pre - c;
+      // the need-th tie in id order: step i holds ids 64i .. 64i + 63 in
+      // lane order, so its ballot lists them in id order
+      unsigned long long before = 0;
       int cut = -1;
-      if (before < need && need <= before + c) {
-        uint32_t left = (uint32_t)(need - before);
-        for (int i = 0; i < 32; ++i)
-          if ((tb >> i) & 1u) {
-            if (--left == 0u) {
-              cut = 32 * lane + i + 1;
-              break;
-            }
+      unsigned long long cut_b = 0ull;  // ballot of the step holding the cut, lower ties dropped
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if (i < nit) {
+          const unsigned long long b = __ballot(v[i] > kNegInf && order_key(v[i]) == tau);
+          const unsigned long long c = (unsigned long long)__popcll(b);
+          if (cut < 0 && before < need && need <= before + c) {
+            cut = i;
+            cut_b = b;
           }
+          if (cut < 0) before += c;
+        }
       }
-      const unsigned long long ball = __ballot(cut >= 0);
-      if (ball) cut_id = __shfl(cut, __ffsll((long long)ball) - 1);
+      if (cut >= 0) {
+        for (unsigned long long left = need - before; left > 1ull; --left) cut_b &= cut_b - 1ull;
+        cut_id = 64 * cut + (__ffsll((long long)cut_b) - 1) + 1;
+      }
     }
   }
 
-  uint32_t bits = 0u;
-  unsigned long long kmass = 0;
+  unsigned long long kmass = 0, nk = 0;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    const float s = v[i];
-    if (s > kNegInf) {
-      const uint32_t k = order_key(s);
-      if (k > tau || (k == tau && 32 * lane + i < cut_id)) {
-        bits |= 1u << i;
-        kmass += fixed_mass(s, mx, scale);
+    if (i < nit) {
+      const float s = v[i];
+      bool keep = false;
+      if (s > kNegInf) {
+        const uint32_t k = order_key(s);
+        if (k > tau || (k == tau && 64 * i + lane < cut_id)) {
+          keep = true;
+          kmass += fixed_mass(s, mx, scale);
+        }
       }
+      const unsigned long long b = __ballot(keep);  // words 2i (ids 64i ..) and 2i + 1
+      nk += (unsigned long long)__popcll(b);
+      if (lane < 2 && 2 * i + lane < nwords) srow[2 * i + lane] = lane == 0 ? (uint32_t)b : (uint32_t)(b >> 32);
     }
   }
-  if (lane < nwords) srow[lane] = bits;
-  const unsigned long long nk = wsum((unsigned long long)__popc(bits));
   const unsigned long long km = wsum(kmass);
   if (lane == 0) {
     SelStats s1;
