@@ -2037,8 +2037,9 @@ __global__ __launch_bounds__(256) void k_select_wave(SelectArgs A, int64_t n_que
 }
 
 // Row form: one 256-thread workgroup per query for rows of at most
-// kRowsRow candidates, thread t holding candidates 32t .. 32t + 31 in
-// registers (and later writing bitset word t).  The steps of the wave form
+// kRowsRow candidates, register i of thread t holding candidate 256i + t
+// (steps past the row's end skipped by the whole workgroup; step i's ballot
+// in wave w is bitset words 8i + 2w and 8i + 2w + 1).  The steps of the wave form
 // with workgroup-wide sums and scans: 8-bit digits over one LDS histogram,
 // each thread owning one bin in the scan.
 constexpr int kRowsRow = 8192;
@@ -2051,9 +2052,10 @@ __global__ __launch_bounds__(256) void k_select_rows(SelectArgs A) {
   __shared__ uint32_t wmax[4], wmin[4];
   __shared__ int sh_i[2];
   __shared__ unsigned long long sh_u[2];
+  __shared__ uint32_t tcnt[4][32];  // ties at the cut key per wave and step
   const int64_t n = A.n_nodes;
-  const int64_t n4 = (n + 3) / 4;
-  const float4* row4 = reinterpret_cast<const float4*>(A.score + q * A.score_stride);
+  const int nit = (int)((n + 255) / 256);  // steps holding candidates (<= 32)
+  const float* row = A.score + q * A.score_stride;
   uint32_t* srow = A.sel + q * A.words;
   SelStats* st = reinterpret_cast<SelStats*>(A.stats) + q;
   const int64_t nwords = (n + 31) / 32;
@@ -2070,17 +2072,10 @@ __global__ __launch_bounds__(256) void k_select_rows(SelectArgs A) {
 
   float v[32];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int64_t b4 = 8 * (int64_t)tid + c;
-    const float4 f = b4 < n4 ? row4[b4] : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
-    v[4 * c] = f.x;
-    v[4 * c + 1] = f.y;
-    v[4 * c + 2] = f.z;
-    v[4 * c + 3] = f.w;
+  for (int i = 0; i < 32; ++i) {
+    const int64_t e = 256 * (int64_t)i + tid;
+    v[i] = (i < nit && e < n) ? row[e] : kNegInf;
   }
-#pragma unroll
-  for (int i = 0; i < 32; ++i)
-    if (32 * (int64_t)tid + i >= n) v[i] = kNegInf;
 
   uint32_t kmax = 0u, kmin = 0xffffffffu;
   unsigned long long ncand = 0ull;
@@ -2131,7 +2126,7 @@ __global__ __launch_bounds__(256) void k_select_rows(SelectArgs A) {
     unsigned long long part = 0;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      const float s = v[i];
+      const float s = i < nit ? v[i] : kNegInf;
       if (s > kNegInf) {
         const uint32_t k = order_key(s);
         const bool match = top >= 32 || (k >> top) == want;
@@ -2188,53 +2183,65 @@ __global__ __launch_bounds__(256) void k_select_rows(SelectArgs A) {
     tau = want;
     const unsigned long long need = ties_needed(tau, P, above, h_tau, mx, scale);
     if (need) {
-      uint32_t tb = 0u;
+      // the need-th tie in id order (step, then wave, then lane): the ties
+      // per wave and step through LDS, then the wave holding the cut finds
+      // its bit in that step's ballot
 #pragma unroll
-      for (int i = 0; i < 32; ++i)
-        if (v[i] > kNegInf && order_key(v[i]) == tau) tb |= 1u << i;
-      const unsigned long long c = __popc(tb);
-      unsigned long long pre = c;
-      for (int o = 1; o < 64; o <<= 1) {
-        const unsigned long long t = __shfl_up(pre, o);
-        if (lane >= o) pre += t;
+      for (int i = 0; i < 32; ++i) {
+        if (i < nit) {
+          const unsigned long long b = __ballot(v[i] > kNegInf && order_key(v[i]) == tau);
+          if (lane == 0) tcnt[wave][i] = (uint32_t)__popcll(b);
+        }
       }
-      if (lane == 63) wred[wave] = pre;
-      __syncthreads();
-      unsigned long long lo_waves = 0;
-      for (int w2 = 0; w2 < wave; ++w2) lo_waves += wred[w2];
-      const unsigned long long before = lo_waves + pre - c;
       if (tid == 0) sh_i[1] = INT_MAX;
       __syncthreads();
-      if (before < need && need <= before + c) {
-        uint32_t left = (uint32_t)(need - before);
-        for (int i = 0; i < 32; ++i)
-          if ((tb >> i) & 1u) {
-            if (--left == 0u) {
-              sh_i[1] = 32 * tid + i + 1;
-              break;
-            }
+      unsigned long long before = 0;
+      int istar = -1, wstar = -1;
+      for (int i = 0; i < nit && istar < 0; ++i)
+        for (int w2 = 0; w2 < 4 && istar < 0; ++w2) {
+          const unsigned long long c = tcnt[w2][i];
+          if (before < need && need <= before + c) {
+            istar = i;
+            wstar = w2;
+          } else {
+            before += c;
           }
+        }
+      if (istar >= 0 && wave == wstar) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          if (i == istar) {
+            unsigned long long b = __ballot(v[i] > kNegInf && order_key(v[i]) == tau);
+            for (unsigned long long left = need - before; left > 1ull; --left) b &= b - 1ull;  // drop lower ties
+            if (lane == 0) sh_i[1] = 256 * i + 64 * wave + (__ffsll((long long)b) - 1) + 1;
+          }
+        }
       }
       __syncthreads();
       cut_id = sh_i[1];
     }
   }
 
-  uint32_t bits = 0u;
-  unsigned long long kmass = 0;
+  unsigned long long kmass = 0, nkeep = 0;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    const float s = v[i];
-    if (s > kNegInf) {
-      const uint32_t k = order_key(s);
-      if (k > tau || (k == tau && 32 * tid + i < cut_id)) {
-        bits |= 1u << i;
-        kmass += fixed_mass(s, mx, scale);
+    if (i < nit) {
+      const float s = v[i];
+      bool keep = false;
+      if (s > kNegInf) {
+        const uint32_t k = order_key(s);
+        if (k > tau || (k == tau && 256 * i + tid < cut_id)) {
+          keep = true;
+          kmass += fixed_mass(s, mx, scale);
+        }
       }
+      nkeep += keep ? 1ull : 0ull;
+      const unsigned long long b = __ballot(keep);  // words 8i + 2 wave and 8i + 2 wave + 1
+      const int64_t wd = 8 * (int64_t)i + 2 * wave + lane;
+      if (lane < 2 && wd < nwords) srow[wd] = lane == 0 ? (uint32_t)b : (uint32_t)(b >> 32);
     }
   }
-  if (tid < nwords) srow[tid] = bits;
-  const unsigned long long nk = bsum((unsigned long long)__popc(bits));
+  const unsigned long long nk = bsum(nkeep);
   const unsigned long long km = bsum(kmass);
   if (tid == 0) {
     SelStats s1;
