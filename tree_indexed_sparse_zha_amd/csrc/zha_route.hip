@@ -1671,6 +1671,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs A) {
     M = block_sum_u64(part, red);
     P = p_target(A.p, M);
     const int bcut = find_bin(hist, kLinBins, P, &above, red, &sh_bin, &sh_above);
+    // the kept mass of the bins above the cut bin is their histogram mass
+    // (the same integer masses; every candidate when no bin is cut, M = 0)
+    const unsigned long long above_bins = bcut >= 0 ? above : M;
     // pass 2: bits of the bins above the cut bin; the cut bin's candidates to
     // LDS.  Eight consecutive lanes hold one bitset word's 32 candidates.
     for (int64_t b0 = 0; b0 < n4; b0 += (int64_t)kSelThreads * kSelUnroll) {
@@ -1689,7 +1692,6 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs A) {
             const int bin = lin_bin(a[e], lo, inv_w);
             if (bin > bcut) {
               nib |= 1u << e;
-              kmass += fixed_mass(a[e], mx, scale);
             } else if (bin == bcut) {
               const int j = atomicAdd(&l_n, 1);
               if (j < A.cut_cap) {
@@ -1769,6 +1771,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs A) {
           ++kept;
         }
       }
+      if (tid == 0) kmass += above_bins;
       done = true;
     } else {
       kept = 0ull;
