@@ -1481,10 +1481,10 @@ __device__ int tie_find(const float* row, int64_t i0, int64_t i1, uint32_t tau, 
 
 // Bitset words [w0, w1) of the kept candidates (key above tau, or at tau
 // with id below cut_id): one word (8 float4 loads) per thread step; adds this
-// thread's kept count and kept mass.
+// thread's kept count.  (The kept mass follows from the cut itself, see
+// kept_mass.)
 __device__ void write_bits(const float4* row4, int64_t n, int64_t w0, int64_t w1, uint32_t tau, int cut_id,
-                           float mx, double scale, uint32_t* srow, unsigned long long* kept,
-                           unsigned long long* kmass) {
+                           uint32_t* srow, unsigned long long* kept) {
   const int64_t n4 = (n + 3) / 4;
   for (int64_t w = w0 + threadIdx.x; w < w1; w += kSelThreads) {
     uint32_t bits = 0u;
@@ -1504,16 +1504,25 @@ __device__ void write_bits(const float4* row4, int64_t n, int64_t w0, int64_t w1
         const float s = a[e];
         if (i < n && s > kNegInf) {
           const uint32_t k = order_key(s);
-          if (k > tau || (k == tau && i < (int64_t)cut_id)) {
-            bits |= 1u << bb;
-            *kmass += fixed_mass(s, mx, scale);
-          }
+          if (k > tau || (k == tau && i < (int64_t)cut_id)) bits |= 1u << bb;
         }
       }
     }
     srow[w] = bits;
     *kept += __popc(bits);
   }
+}
+
+// Kept fixed-point mass of a selection with cut key tau: every candidate
+// when all are kept (M), else the mass strictly above tau plus the kept ties
+// at tau, which all carry one mass (need of them, or all h_tau of them when
+// need is 0).  Integer sums: equal to adding the kept candidates' masses.
+__device__ __forceinline__ unsigned long long kept_mass(bool keep_all, unsigned long long M,
+                                                         unsigned long long above, unsigned long long h_tau,
+                                                         unsigned long long need, uint32_t tau, float mx,
+                                                         double scale) {
+  if (keep_all) return M;
+  return above + (need ? need * fixed_mass(key_to_float(tau), mx, scale) : h_tau);
 }
 
 __device__ __forceinline__ unsigned long long p_target(float p, unsigned long long M) {
@@ -1814,12 +1823,14 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs A) {
       found = lo == 0;
     } while (!found);
 
+    unsigned long long need = 0;
     if (!A.keep_all) {
       tau = want;
-      const unsigned long long need = ties_needed(tau, P, above, h_tau, mx, scale);
+      need = ties_needed(tau, P, above, h_tau, mx, scale);
       if (need) cut_id = tie_find(row, 0, n, tau, need);
     }
-    write_bits(row4, n, 0, nwords, tau, cut_id, mx, scale, srow, &kept, &kmass);
+    write_bits(row4, n, 0, nwords, tau, cut_id, srow, &kept);
+    kmass = tid == 0 ? kept_mass(A.keep_all, M, above, h_tau, need, tau, mx, scale) : 0ull;
   }
   const unsigned long long nk = block_sum_u64(kept, red);
   const unsigned long long km = block_sum_u64(kmass, red);
@@ -2283,9 +2294,9 @@ __device__ __forceinline__ SelState* sel_state(const SelectArgs& A, int64_t q) {
   return reinterpret_cast<SelState*>(static_cast<char*>(A.split) + q * kSelStateBytes);
 }
 // Segment slot of (query, segment): histogram bins, then the first pass's
-// mass, the kept count, the kept mass, the ties at the cut key and the
+// mass, the kept count, one unused word, the ties at the cut key and the
 // segment's cut id.
-constexpr int kSlotM = 2048, kSlotKept = 2049, kSlotKMass = 2050, kSlotTies = 2051, kSlotCut = 2052;
+constexpr int kSlotM = 2048, kSlotKept = 2049, kSlotTies = 2051, kSlotCut = 2052;
 __device__ __forceinline__ unsigned long long* sel_slot(const SelectArgs& A, int64_t n_queries, int64_t q,
                                                          int64_t s) {
   return reinterpret_cast<unsigned long long*>(static_cast<char*>(A.split) + n_queries * kSelStateBytes) +
@@ -2459,14 +2470,11 @@ __global__ __launch_bounds__(kSelThreads) void k_select_bits(SelectArgs A) {
       cut_rec = cut;
     }
   }
-  unsigned long long kept = 0, kmass = 0;
-  write_bits(reinterpret_cast<const float4*>(row), A.n_nodes, w0, w1, A.keep_all ? 0u : s.tau, cut, s.mx, s.scale,
-             srow, &kept, &kmass);
+  unsigned long long kept = 0;
+  write_bits(reinterpret_cast<const float4*>(row), A.n_nodes, w0, w1, A.keep_all ? 0u : s.tau, cut, srow, &kept);
   const unsigned long long nk = block_sum_u64(kept, red);
-  const unsigned long long km = block_sum_u64(kmass, red);
   if (threadIdx.x == 0) {
     out[kSlotKept] = nk;
-    out[kSlotKMass] = km;
     out[kSlotCut] = (unsigned long long)(uint32_t)cut_rec;
   }
 }
@@ -2482,18 +2490,17 @@ __global__ __launch_bounds__(64) void k_select_stats(SelectArgs A, int64_t n_que
     }
     return;
   }
-  unsigned long long nk = 0, km = 0, cut = INT_MAX;
+  unsigned long long nk = 0, cut = INT_MAX;
   for (int64_t g = threadIdx.x; g < A.split_S; g += 64) {
     const unsigned long long* slot = sel_slot(A, n_queries, q, g);
     nk += slot[kSlotKept];
-    km += slot[kSlotKMass];
     cut = min(cut, slot[kSlotCut]);  // at most one segment cuts inside its ties
   }
   for (int o = 1; o < 64; o <<= 1) {
     nk += __shfl_xor(nk, o);
-    km += __shfl_xor(km, o);
     cut = min(cut, (unsigned long long)__shfl_xor(cut, o));
   }
+  const unsigned long long km = kept_mass(A.keep_all, s.M, s.above, s.h_tau, s.need_tie, s.tau, s.mx, s.scale);
   if (threadIdx.x == 0) {
     SelStats s1;
     s1.max_score = s.mx;
